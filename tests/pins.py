@@ -1,0 +1,342 @@
+"""Checks that tie the fp64 oracle to what the pages and the mathematics fix.
+
+Each function takes an ``oracle.Oracle`` instance and raises AssertionError on
+a mismatch. test_oracle_pins.py runs them against oracle.c. The mutation test
+runs them against deliberately broken copies of oracle.c, so each plausible
+mistake has to fail at least one pin.
+
+Independent anchors used here, none of them the oracle's own code:
+  * scipy's multivariate normal log-density and logsumexp (textbook GMM
+    posterior) for the responsibilities;
+  * the materialised N x N affinity written with numpy for the associative
+    GMA form;
+  * closed forms: K = 1 (running mean of V up to eps), identical components
+    (rows of Gamma equal the priors);
+  * hand-derived tiny examples (tests/golden/*.json);
+  * numpy brute force with explicit decay products for gated linear attention;
+  * numpy.cov(bias=True) for the running key covariance, itself checked to be
+    the Hessian of the softmax log-partition at q = 0 (which fixes the 1/t);
+  * reductions: lambda = 0 or constant keys turn CCQ into plain gated linear
+    attention; a query orthogonal to the keys' span is not changed.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+from scipy.special import logsumexp
+from scipy.stats import multivariate_normal
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _gma_params(rng, H, K, d, spread=1.0):
+    mu = rng.standard_normal((H, K, d)) * spread
+    lv = np.logaddexp(0.0, rng.standard_normal((H, K, d)) * np.sqrt(0.5))
+    lp = rng.standard_normal((H, K))
+    return mu, lv, lp
+
+
+def scipy_gamma(x, mu, lv, lp):
+    """Textbook GMM posterior with scipy: log pi_k + log N(x; mu_k, diag(exp lv_k))."""
+    K = mu.shape[0]
+    logpi = lp - logsumexp(lp)
+    cols = [multivariate_normal(mean=mu[c], cov=np.diag(np.exp(lv[c]))).logpdf(x) + logpi[c]
+            for c in range(K)]
+    lj = np.stack(cols, axis=-1).reshape(x.shape[0], K)
+    return np.exp(lj - logsumexp(lj, axis=1, keepdims=True))
+
+
+def numpy_gma_brute(q, k, v, mu, lv, lp, causal, eps):
+    """Materialised affinity Gamma_Q Gamma_K^T (masked when causal), O = A V / (A 1 + eps)."""
+    B, H, N, _ = q.shape
+    out = np.empty(v.shape[:3] + (v.shape[-1],))
+    for b in range(B):
+        for h in range(H):
+            gq = scipy_gamma(q[b, h], mu[h], lv[h], lp[h])
+            gk = scipy_gamma(k[b, h], mu[h], lv[h], lp[h])
+            a = gq @ gk.T
+            if causal:
+                a = np.tril(a)
+            out[b, h] = (a @ v[b, h]) / (a.sum(1, keepdims=True) + eps)
+    return out
+
+
+def relerr(x, r):
+    return float(np.max(np.abs(x - r)) / max(np.max(np.abs(r)), 1e-300))
+
+
+# ---------------------------------------------------------------- GMA pins
+
+
+def pin_gamma_scipy(orc):
+    rng = _rng(101)
+    for d, K in ((1, 1), (3, 5), (8, 16)):
+        mu, lv, lp = _gma_params(rng, 1, K, d)
+        x = rng.standard_normal((20, d)) * 1.5
+        g = orc.responsibilities(x, mu[0], lv[0], lp[0])
+        assert np.all(g >= 0)
+        assert np.allclose(g.sum(1), 1.0, atol=1e-13, rtol=0)
+        ref = scipy_gamma(x, mu[0], lv[0], lp[0])
+        assert np.max(np.abs(g - ref)) < 1e-12, np.max(np.abs(g - ref))
+
+
+def pin_gma_brute_numpy(orc):
+    rng = _rng(102)
+    B, H, N, d, K, dv = 2, 2, 33, 4, 5, 3
+    mu, lv, lp = _gma_params(rng, H, K, d)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, dv))
+    for causal in (True, False):
+        for eps in (1e-6, 0.3):
+            ref = numpy_gma_brute(q, k, v, mu, lv, lp, causal, eps)
+            got = orc.gma_forward(q, k, v, mu, lv, lp, causal=causal, eps=eps)
+            assert relerr(got, ref) < 1e-12, (causal, eps, relerr(got, ref))
+            got2 = orc.gma_brute(q, k, v, mu, lv, lp, causal=causal, eps=eps)
+            assert relerr(got2, ref) < 1e-12, (causal, eps, relerr(got2, ref))
+
+
+def pin_gma_k1_closed_form(orc):
+    rng = _rng(103)
+    B, H, N, d, dv = 1, 2, 40, 3, 4
+    mu, lv, lp = _gma_params(rng, H, 1, d)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, dv))
+    eps = 0.25
+    cnt = np.arange(1, N + 1)[:, None]
+    got = orc.gma_forward(q, k, v, mu, lv, lp, causal=True, eps=eps)
+    ref = np.cumsum(v, axis=2) / (cnt + eps)
+    assert relerr(got, ref) < 1e-13
+    got = orc.gma_forward(q, k, v, mu, lv, lp, causal=False, eps=eps)
+    ref = np.broadcast_to(v.sum(2, keepdims=True) / (N + eps), v.shape)
+    assert relerr(got, ref) < 1e-13
+
+
+def pin_gma_identical_components(orc):
+    rng = _rng(104)
+    B, H, N, d, K, dv = 1, 1, 30, 3, 4, 2
+    mu = np.broadcast_to(rng.standard_normal((1, 1, d)), (H, K, d)).copy()
+    lv = np.broadcast_to(rng.standard_normal((1, 1, d)), (H, K, d)).copy()
+    lp = rng.standard_normal((H, K))
+    pi = np.exp(lp - logsumexp(lp, axis=1, keepdims=True))
+    s = float((pi[0] ** 2).sum())
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, dv))
+    eps = 0.1
+    cnt = np.arange(1, N + 1)[:, None]
+    got = orc.gma_forward(q, k, v, mu, lv, lp, causal=True, eps=eps)
+    ref = s * np.cumsum(v, axis=2) / (s * cnt + eps)
+    assert relerr(got, ref) < 1e-12
+
+
+def pin_gma_permutation(orc):
+    rng = _rng(105)
+    B, H, N, d, K, dv = 1, 1, 25, 3, 6, 2
+    mu, lv, lp = _gma_params(rng, H, K, d)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, dv))
+    perm = rng.permutation(K)
+    a = orc.gma_forward(q, k, v, mu, lv, lp)
+    b = orc.gma_forward(q, k, v, mu[:, perm], lv[:, perm], lp[:, perm])
+    assert relerr(a, b) < 1e-13
+
+
+def pin_gma_prefix(orc):
+    rng = _rng(106)
+    B, H, N, d, K, dv = 1, 1, 40, 3, 5, 2
+    mu, lv, lp = _gma_params(rng, H, K, d)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, dv))
+    full = orc.gma_forward(q, k, v, mu, lv, lp, causal=True)
+    for i in (1, 7, 23):
+        part = orc.gma_forward(q[:, :, :i], k[:, :, :i], v[:, :, :i], mu, lv, lp, causal=True)
+        assert relerr(part, full[:, :, :i]) < 1e-14
+    # the current token takes part in its own output (j <= i)
+    v2 = v.copy()
+    v2[:, :, 10] += 1.0
+    changed = orc.gma_forward(q, k, v2, mu, lv, lp, causal=True)
+    assert np.all(np.abs(changed[:, :, 10] - full[:, :, 10]) > 1e-9)
+    assert relerr(changed[:, :, :10], full[:, :, :10]) < 1e-14
+
+
+def pin_gma_affinity_structure(orc):
+    rng = _rng(107)
+    B, H, N, d, K, dv = 1, 1, 24, 3, 4, 2
+    mu, lv, lp = _gma_params(rng, H, K, d)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, dv))
+    _, a = orc.gma_brute(q, k, v, mu, lv, lp, causal=False, return_affinity=True)
+    assert np.all(a >= 0)
+    assert np.linalg.matrix_rank(a, tol=1e-10) <= K
+    # the masked causal affinity is the lower triangle of the same matrix
+    _, ac = orc.gma_brute(q, k, v, mu, lv, lp, causal=True, return_affinity=True)
+    assert np.max(np.abs(ac - np.tril(a))) < 1e-15
+
+
+def pin_gma_golden(orc):
+    with open(os.path.join(GOLDEN, "gma_two_components.json")) as f:
+        case = json.load(f)
+    got = orc.gma_forward(np.array(case["q"]), np.array(case["k"]), np.array(case["v"]),
+                          np.array(case["mu"]), np.array(case["log_var"]),
+                          np.array(case["logit_pi"]), causal=case["causal"], eps=case["eps"])
+    ref = np.array(case["expected_out"])
+    assert relerr(got, ref) < 1e-12, (got, ref)
+
+
+# ---------------------------------------------------------------- GLA pins
+
+
+def numpy_gla_brute(q, k, v, g):
+    """o_t = sum_{j<=t} (prod_{s=j+1..t} g_s) (q_t . k_j) v_j, explicit products."""
+    B, H, N, _ = q.shape
+    out = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            for t in range(N):
+                for j in range(t + 1):
+                    dec = np.prod(g[b, h, j + 1:t + 1])
+                    out[b, h, t] += dec * (q[b, h, t] @ k[b, h, j]) * v[b, h, j]
+    return out
+
+
+def pin_gla_brute(orc):
+    rng = _rng(201)
+    B, H, N, dk, dv = 1, 2, 37, 5, 3
+    q = rng.standard_normal((B, H, N, dk))
+    k = rng.standard_normal((B, H, N, dk))
+    v = rng.standard_normal((B, H, N, dv))
+    g = rng.uniform(0.2, 1.0, (B, H, N))
+    got = orc.gla_forward(q, k, v, g)
+    assert relerr(got, numpy_gla_brute(q, k, v, g)) < 1e-12
+    ones = np.ones((B, H, N))
+    got = orc.gla_forward(q, k, v, ones)
+    ref = np.tril(q @ np.swapaxes(k, -1, -2)) @ v
+    assert relerr(got, ref) < 1e-12
+
+
+def pin_gla_chunkwise(orc):
+    rng = _rng(202)
+    B, H, N, dk, dv = 2, 1, 70, 4, 6
+    q = rng.standard_normal((B, H, N, dk))
+    k = rng.standard_normal((B, H, N, dk))
+    v = rng.standard_normal((B, H, N, dv))
+    g = rng.uniform(0.3, 1.0, (B, H, N))
+    rec = orc.gla_forward(q, k, v, g)
+    for C in (1, 8, 16, 64, 128):
+        assert relerr(orc.gla_chunkwise(q, k, v, g, chunk=C), rec) < 1e-12, C
+    assert relerr(rec, numpy_gla_brute(q, k, v, g)) < 1e-12
+
+
+# ---------------------------------------------------------------- CCQ pins
+
+
+def numpy_ccq_brute(q, k, v, g, w, b):
+    """o_t = S_t^T (q_t - lambda_t Cov_{<=t}[k] q_t) with np.cov(bias=True) and the
+    brute-force state S_t = sum_{j<=t} prod(g_{j+1..t}) k_j v_j^T."""
+    B, H, N, dk = q.shape
+    out = np.zeros(v.shape)
+    for bb in range(B):
+        for h in range(H):
+            for t in range(N):
+                kk = k[bb, h, :t + 1]
+                sig = np.cov(kk.T, bias=True).reshape(dk, dk) if t > 0 else np.zeros((dk, dk))
+                lam = 1.0 / (1.0 + np.exp(-(w[h] @ q[bb, h, t] + b[h])))
+                qc = q[bb, h, t] - lam * sig @ q[bb, h, t]
+                S = np.zeros((dk, v.shape[-1]))
+                for j in range(t + 1):
+                    S += np.prod(g[bb, h, j + 1:t + 1]) * np.outer(kk[j], v[bb, h, j])
+                out[bb, h, t] = S.T @ qc
+    return out
+
+
+def _ccq_case(rng, B=1, H=2, N=30, dk=4, dv=3, bias=1.0, center=0.0):
+    q = rng.standard_normal((B, H, N, dk))
+    k = rng.standard_normal((B, H, N, dk)) + center
+    v = rng.standard_normal((B, H, N, dv))
+    g = rng.uniform(0.3, 1.0, (B, H, N))
+    w = rng.standard_normal((H, dk)) / np.sqrt(dk)
+    b = np.full(H, bias)
+    return q, k, v, g, w, b
+
+
+def pin_ccq_numpy_cov(orc):
+    rng = _rng(301)
+    for center in (0.0, 2.0):
+        q, k, v, g, w, b = _ccq_case(rng, center=center)
+        got = orc.ccq_forward(q, k, v, g, w, b)
+        ref = numpy_ccq_brute(q, k, v, g, w, b)
+        assert relerr(got, ref) < 1e-11, (center, relerr(got, ref))
+        # the correction is not negligible in this case
+        assert relerr(orc.gla_forward(q, k, v, g), ref) > 1e-2
+
+
+def pin_cov_is_logpartition_hessian(orc):
+    """The pages state that the Hessian at q = 0 of log sum_{j<=t} exp(k_j^T q) is
+    the running key covariance; numpy.cov(bias=True), used above, must be it."""
+    rng = _rng(302)
+    dk, t = 4, 9
+    kk = rng.standard_normal((t, dk)) + 0.5
+    f = lambda qq: logsumexp(kk @ qq)
+    h = 1e-4
+    hess = np.empty((dk, dk))
+    for a in range(dk):
+        for c in range(dk):
+            ea = np.eye(dk)[a] * h
+            ec = np.eye(dk)[c] * h
+            hess[a, c] = (f(ea + ec) - f(ea - ec) - f(-ea + ec) + f(-ea - ec)) / (4 * h * h)
+    assert np.max(np.abs(hess - np.cov(kk.T, bias=True))) < 1e-6
+    assert np.max(np.abs(hess - np.cov(kk.T, bias=False))) > 1e-2
+
+
+def pin_ccq_reductions(orc):
+    rng = _rng(303)
+    q, k, v, g, w, b = _ccq_case(rng)
+    gla = orc.gla_forward(q, k, v, g)
+    # gate closed: lambda = sigmoid(-1e4) = 0 exactly
+    assert relerr(orc.ccq_forward(q, k, v, g, w, np.full(2, -1e4)), gla) < 1e-14
+    # constant keys: covariance is zero
+    kc = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    assert relerr(orc.ccq_forward(q, kc, v, g, w, b), orc.gla_forward(q, kc, v, g)) < 1e-12
+    # query orthogonal to the span of the keys: Sigma q = 0, q unchanged
+    k2 = k.copy()
+    k2[..., 2:] = 0.0
+    q2 = q.copy()
+    q2[..., :2] = 0.0
+    assert relerr(orc.ccq_forward(q2, k2, v, g, w, np.full(2, 3.0)),
+                  orc.gla_forward(q2, k2, v, g)) < 1e-12
+
+
+def pin_ccq_chunkwise(orc):
+    rng = _rng(304)
+    q, k, v, g, w, b = _ccq_case(rng, N=45, bias=0.5)
+    rec = orc.ccq_forward(q, k, v, g, w, b)
+    for C in (1, 4, 16, 64):
+        assert relerr(orc.ccq_chunkwise(q, k, v, g, w, b, chunk=C), rec) < 1e-11, C
+
+
+def pin_ccq_golden(orc):
+    with open(os.path.join(GOLDEN, "ccq_two_keys.json")) as f:
+        case = json.load(f)
+    args = [np.array(case[x]) for x in ("q", "k", "v", "g", "w_lambda", "b_lambda")]
+    got = orc.ccq_forward(*args)
+    ref = np.array(case["expected_out"])
+    assert relerr(got, ref) < 1e-14, (got, ref)
+
+
+ALL_PINS = [
+    pin_gamma_scipy, pin_gma_brute_numpy, pin_gma_k1_closed_form, pin_gma_identical_components,
+    pin_gma_permutation, pin_gma_prefix, pin_gma_affinity_structure, pin_gma_golden,
+    pin_gla_brute, pin_gla_chunkwise, pin_ccq_numpy_cov, pin_cov_is_logpartition_hessian,
+    pin_ccq_reductions, pin_ccq_chunkwise, pin_ccq_golden,
+]
