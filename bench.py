@@ -1,0 +1,266 @@
+"""Benchmark: forward head-tokens/s of causal GMA and CCQ at 16K tokens on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--secondary]
+
+One step is one forward of each headline path on its own synthetic batch:
+  * causal Gaussian Mixture Attention, bf16 in / fp32 accumulate:
+    B=4, H=8, N=16384, d=dv=64, K=128 components;
+  * CCQ read over gated linear attention, bf16 in / fp32 accumulate:
+    B=4, H=16, N=16384, dk=dv=128, chunk 64.
+value = (head-tokens of both batches) x steps / wall time of the timed region,
+where a head-token is one (b, h, n) row. Inputs are resident in HBM before
+timing starts. Each path rotates through copies of its inputs totalling more
+than the 256 MB last-level cache, so no step reads a previous step's inputs
+from cache.
+
+The JSON line also holds:
+  * roofline: the entry point that takes longer per step (its kernels measured
+    with HIP events on the stream they run on), as algorithmic HBM bytes per
+    call / average call time, against MI355X's 8 TB/s;
+  * cpu_baseline: the fp64 oracle on a bounded sample of the same workload
+    (a few (b, h) slices at full length) on the host cores;
+  * parts: per-path rates.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+LLC_BYTES = 256 << 20
+METRIC = "fwd tokens/s per head at N=16K (causal GMA, CCQ-GLA) + % MFMA/HBM roofline"
+
+
+def gma_bytes_per_head_token(cfg, esize=2):
+    # q, k, v read + out written
+    return (2 * cfg.d + 2 * cfg.dv) * esize
+
+
+def gma_flops_per_head_token(cfg):
+    # routing of q and k (8 K d), write + read (4 K (dv + 1))
+    return 8 * cfg.K * cfg.d + 4 * cfg.K * (cfg.dv + 1)
+
+
+def ccq_bytes_per_head_token(cfg, esize=2):
+    # q, k, v read + out written + the fp32 decay
+    return (2 * cfg.dk + 2 * cfg.dv) * esize + 4
+
+
+def ccq_flops_per_head_token(cfg):
+    return 4 * cfg.dk * cfg.dv + 4 * cfg.dk * cfg.dk
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", action="store_true", help="also time bidirectional GMA, GLA and long GMA")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(every (b, h) slice is independent; see DESIGN.md on sharding). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_attention_gmm_amd import ccq_forward, gma_forward, inputs, linattn_chunk_forward
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gcfg = inputs.CONFIGS["gma_bf16_n16k"]
+    ccfg = inputs.CONFIGS["ccq_bf16_n16k"]
+
+    t_gen = time.perf_counter()
+    gx = inputs.gma_inputs(gcfg)
+    cx = inputs.linattn_inputs(ccfg, ccq=True)
+    print("inputs generated in %.1f s" % (time.perf_counter() - t_gen), file=sys.stderr, flush=True)
+
+    def copies(x, keys, nbytes):
+        n = max(2, math.ceil(2 * LLC_BYTES / nbytes))
+        base = {k: v.to(dev) for k, v in x.items() if isinstance(v, torch.Tensor)}
+        out = [base]
+        for _ in range(n - 1):
+            out.append({k: (v.clone() if k in keys else v) for k, v in base.items()})
+        return out
+
+    g_in_bytes = sum(gx[k].numel() * gx[k].element_size() for k in ("q", "k", "v"))
+    c_in_bytes = sum(cx[k].numel() * cx[k].element_size() for k in ("q", "k", "v", "g"))
+    gset = copies(gx, ("q", "k", "v"), g_in_bytes)
+    cset = copies(cx, ("q", "k", "v", "g"), c_in_bytes)
+    gout = torch.empty_like(gset[0]["v"])
+    cout = torch.empty_like(cset[0]["v"])
+    gws = torch.empty(max(16, __import__("linear_attention_gmm_amd").gma_workspace_bytes(
+        gcfg.B, gcfg.H, gcfg.N, gcfg.d, gcfg.K, gcfg.dv, True, torch.bfloat16)), dtype=torch.uint8, device=dev)
+    cws = torch.empty(max(16, __import__("linear_attention_gmm_amd").ccq_workspace_bytes(
+        ccfg.B, ccfg.H, ccfg.N, ccfg.dk, ccfg.dv, 64, torch.bfloat16)), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        a = gset[i % len(gset)]
+        b = cset[i % len(cset)]
+        if ev is not None:
+            ev[0].record()
+        gma_forward(a["q"], a["k"], a["v"], a["mu"], a["log_var"], a["logit_pi"], causal=True, eps=gcfg.eps,
+                    out=gout, workspace=gws)
+        if ev is not None:
+            ev[1].record()
+        ccq_forward(b["q"], b["k"], b["v"], b["g"], b["w_lambda"], b["b_lambda"], out=cout, workspace=cws)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+
+    g_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    c_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    g_tok = gcfg.B * gcfg.H * gcfg.N
+    c_tok = ccfg.B * ccfg.H * ccfg.N
+    value = (g_tok + c_tok) * args.steps / wall
+
+    g_bytes = g_tok * gma_bytes_per_head_token(gcfg)
+    c_bytes = c_tok * ccq_bytes_per_head_token(ccfg)
+    parts = {
+        "gma_causal": {"head_tokens_per_s": g_tok / (g_ms * 1e-3), "ms_per_call": g_ms,
+                       "alg_GBps": g_bytes / (g_ms * 1e-3) / 1e9,
+                       "hbm_frac": g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "alg_TFLOPs": g_tok * gma_flops_per_head_token(gcfg) / (g_ms * 1e-3) / 1e12,
+                       "alg_bytes_per_call": g_bytes},
+        "ccq": {"head_tokens_per_s": c_tok / (c_ms * 1e-3), "ms_per_call": c_ms,
+                "alg_GBps": c_bytes / (c_ms * 1e-3) / 1e9,
+                "hbm_frac": c_bytes / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "alg_TFLOPs": c_tok * ccq_flops_per_head_token(ccfg) / (c_ms * 1e-3) / 1e12,
+                "alg_bytes_per_call": c_bytes},
+    }
+    dom = "ccq" if c_ms >= g_ms else "gma_causal"
+    achieved = parts[dom]["alg_GBps"]
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "ccq_forward (segment-state + chunk kernels)" if dom == "ccq"
+                else "gma_forward (prep + segment-state + chunk kernels)",
+                "alg_bytes_per_call": parts[dom]["alg_bytes_per_call"], "avg_call_ms": parts[dom]["ms_per_call"]}
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; distributions of the GMA and CCQ workloads)",
+        "config": {"workload": "causal GMA B4 H8 N16384 d64 K128 dv64 + CCQ-GLA B4 H16 N16384 dk=dv=128, "
+                               "bf16 inputs, fp32 accumulation, chunk 64",
+                   "head_tokens_per_step": g_tok + c_tok},
+        "roofline": roofline,
+        "parts": parts,
+    }
+
+    if args.secondary:
+        sec = {}
+        for name, fn in (("gma_bidir_n16k", "bidir"), ("gla_bf16_n8k", "gla"), ("gma_bf16_n128k", "gma5")):
+            if fn == "bidir":
+                a = gset[0]
+                call = lambda: gma_forward(a["q"], a["k"], a["v"], a["mu"], a["log_var"], a["logit_pi"],
+                                           causal=False, out=gout, workspace=gws)
+                tok, byt = g_tok, g_bytes
+            elif fn == "gla":
+                cfg = inputs.CONFIGS["gla_bf16_n8k"]
+                x = {k: v.to(dev) for k, v in inputs.linattn_inputs(cfg).items()}
+                call = lambda: linattn_chunk_forward(x["q"], x["k"], x["v"], x["g"])
+                tok = cfg.B * cfg.H * cfg.N
+                byt = tok * ccq_bytes_per_head_token(cfg)
+            else:
+                cfg = inputs.CONFIGS["gma_bf16_n128k"]
+                y = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inputs.gma_inputs(cfg).items()}
+                call = lambda: gma_forward(y["q"], y["k"], y["v"], y["mu"], y["log_var"], y["logit_pi"], causal=True)
+                tok = cfg.B * cfg.H * cfg.N
+                byt = tok * gma_bytes_per_head_token(cfg)
+            for _ in range(2):
+                call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            n = 5
+            for _ in range(n):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n
+            sec[name] = {"ms_per_call": ms, "head_tokens_per_s": tok / (ms * 1e-3),
+                         "alg_GBps": byt / (ms * 1e-3) / 1e9, "hbm_frac": byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            if fn == "gma5":
+                sec[name]["alg_TFLOPs"] = tok * gma_flops_per_head_token(cfg) / (ms * 1e-3) / 1e12
+                sec[name]["mfma_frac"] = sec[name]["alg_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
+        result["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(gx, cx, gcfg, ccfg)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(gx, cx, gcfg, ccfg):
+    """The fp64 oracle (as it is) on a bounded sample of the step's workload:
+    the first S (b, h) slices of each path at full length, S = host threads
+    (at most the slice count), so every thread has one slice of each."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.num_threads()
+    sg = min(threads, gcfg.B * gcfg.H)
+    sc = min(threads, ccfg.B * ccfg.H)
+
+    def head_slices(n, H):
+        return [(i // H, i % H) for i in range(n)]
+
+    t0 = time.perf_counter()
+    gidx = head_slices(sg, gcfg.H)
+    gsel = lambda t: np.stack([t[b, h].float().numpy() for b, h in gidx])[None]
+    q, k, v = gsel(gx["q"]), gsel(gx["k"]), gsel(gx["v"])
+    # every slice keeps its own head's parameters: the sample is passed as B = 1, H = slices
+    mu = np.stack([gx["mu"][h].numpy() for _, h in gidx])
+    lv = np.stack([gx["log_var"][h].numpy() for _, h in gidx])
+    lp = np.stack([gx["logit_pi"][h].numpy() for _, h in gidx])
+    tg0 = time.perf_counter()
+    oracle.gma_forward(q, k, v, mu, lv, lp, causal=True, eps=gcfg.eps)
+    tg = time.perf_counter() - tg0
+    cidx = head_slices(sc, ccfg.H)
+    sel = lambda t: np.stack([t[b, h].float().numpy() for b, h in cidx])[None]
+    w = np.stack([cx["w_lambda"][h].numpy() for _, h in cidx])
+    bb = np.stack([cx["b_lambda"][h].numpy() for _, h in cidx])
+    tc0 = time.perf_counter()
+    oracle.ccq_forward(sel(cx["q"]), sel(cx["k"]), sel(cx["v"]), sel(cx["g"]), w, bb)
+    tc = time.perf_counter() - tc0
+    toks = sg * gcfg.N + sc * ccfg.N
+    return {"value": toks / (tg + tc), "unit": "head-tokens/s", "cores": max(sg, sc), "kind": "oracle",
+            "sample": "%d causal-GMA slices + %d CCQ slices at N=16384 (one per thread), fp64; GMA %.1f s, "
+                      "CCQ %.1f s" % (sg, sc, tg, tc),
+            "host_threads": threads, "wall_s": time.perf_counter() - t0}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+"""Thin Python binding of liblinmix.so (the C ABI in include/linmix.h).
+
+Argument marshalling only: tensors are checked for the layout the ABI assumes
+(device, dtype, shape, contiguity), turned into raw pointers and passed with the
+caller's current HIP stream. Every step of the forward pass runs in the HIP
+library. If the library is missing, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinmix.so")
+
+LM_OK, LM_EINVAL, LM_EUNSUPPORTED, LM_EWORKSPACE, LM_EHIP = range(5)
+LM_F32, LM_BF16 = 0, 1
+
+_DT = {torch.float32: LM_F32, torch.bfloat16: LM_BF16}
+
+
+class LinmixError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (fn, _status_name(status), detail))
+
+
+_lock = threading.Lock()
+_lib = None
+
+_I64 = ctypes.c_int64
+_P = ctypes.c_void_p
+_SIGS = {
+    "lm_abi_version": ([], ctypes.c_int),
+    "lm_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "lm_last_error": ([], ctypes.c_char_p),
+    "gma_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, ctypes.c_int, _I64], ctypes.c_size_t),
+    "gma_forward": ([_P] * 7 + [_I64] * 6 + [ctypes.c_int, ctypes.c_float, ctypes.c_int, _I64, _P,
+                                             ctypes.c_size_t, _P], ctypes.c_int),
+    "linattn_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
+    "linattn_chunk_forward": ([_P] * 5 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P],
+                              ctypes.c_int),
+    "ccq_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
+    "ccq_forward": ([_P] * 7 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
+}
+
+
+def lib():
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("HIP library %s is missing; build it with "
+                                   "`python -m linear_attention_gmm_amd.build`" % LIB_PATH)
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in _SIGS.items():
+                f = getattr(L, name)
+                f.argtypes = args
+                f.restype = res
+            _lib = L
+    return _lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return lib().lm_status_string(s).decode()
+    except Exception:  # library unavailable while formatting an error
+        return str(s)
+
+
+def _check(fn: str, status: int):
+    if status != LM_OK:
+        raise LinmixError(fn, status, lib().lm_last_error().decode())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace holds %d bytes, %d needed" % (workspace.numel() * workspace.element_size(), nbytes))
+    return workspace
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError("q must be float32 or bfloat16 (got %s)" % t.dtype)
+    return _DT[t.dtype]
+
+
+def gma_workspace_bytes(B, H, N, d, K, dv, causal=True, dtype=torch.bfloat16, segments=0) -> int:
+    return int(lib().gma_workspace_bytes(B, H, N, d, K, dv, int(bool(causal)), _DT[dtype], segments))
+
+
+def gma_forward(q, k, v, mu, log_var, logit_pi, causal: bool = True, eps: float = 1e-6, segments: int = 0,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gaussian Mixture Attention forward. q, k [B,H,N,d]; v [B,H,N,dv] (float32 or
+    bfloat16, all the same); mu, log_var [H,K,d] and logit_pi [H,K] float32.
+    Returns out [B,H,N,dv] in the input dtype."""
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    dt = _dtype_code(q)
+    pq = _dev(q, "q", q.dtype, (B, H, N, d))
+    pk = _dev(k, "k", q.dtype, (B, H, N, d))
+    pv = _dev(v, "v", q.dtype, (B, H, N, dv))
+    pmu = _dev(mu, "mu", torch.float32, (H, K, d))
+    plv = _dev(log_var, "log_var", torch.float32, (H, K, d))
+    plp = _dev(logit_pi, "logit_pi", torch.float32, (H, K))
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    po = _dev(out, "out", q.dtype, (B, H, N, dv))
+    nbytes = gma_workspace_bytes(B, H, N, d, K, dv, causal, q.dtype, segments)
+    if nbytes == 0:
+        _check("gma_workspace_bytes", lib().gma_forward(None, None, None, None, None, None, None, B, H, N, d, K,
+                                                        dv, int(bool(causal)), float(eps), dt, segments, None,
+                                                        0, None))
+    ws = _workspace(nbytes, q.device, workspace)
+    st = lib().gma_forward(pq, pk, pv, pmu, plv, plp, po, B, H, N, d, K, dv, int(bool(causal)), float(eps), dt,
+                           segments, ws.data_ptr(), nbytes, _stream(q.device))
+    _check("gma_forward", st)
+    return out
+
+
+def linattn_workspace_bytes(B, H, N, dk, dv, chunk=64, dtype=torch.bfloat16, segments=0) -> int:
+    return int(lib().linattn_workspace_bytes(B, H, N, dk, dv, chunk, _DT[dtype], segments))
+
+
+def ccq_workspace_bytes(B, H, N, dk, dv, chunk=64, dtype=torch.bfloat16, segments=0) -> int:
+    return int(lib().ccq_workspace_bytes(B, H, N, dk, dv, chunk, _DT[dtype], segments))
+
+
+def _lin_common(q, k, v, g, out):
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    ptrs = (_dev(q, "q", q.dtype, (B, H, N, dk)), _dev(k, "k", q.dtype, (B, H, N, dk)),
+            _dev(v, "v", q.dtype, (B, H, N, dv)), _dev(g, "g", torch.float32, (B, H, N)))
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    po = _dev(out, "out", q.dtype, (B, H, N, dv))
+    return (B, H, N, dk, dv), ptrs, out, po
+
+
+def linattn_chunk_forward(q, k, v, g, chunk: int = 64, segments: int = 0, out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decayed linear attention S_t = g_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t.
+    q, k [B,H,N,dk], v [B,H,N,dv] (float32 or bfloat16); g [B,H,N] float32."""
+    dt = _dtype_code(q)
+    (B, H, N, dk, dv), (pq, pk, pv, pg), out, po = _lin_common(q, k, v, g, out)
+    nbytes = linattn_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    st = lib().linattn_chunk_forward(pq, pk, pv, pg, po, B, H, N, dk, dv, chunk, dt, segments,
+                                     ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
+    _check("linattn_chunk_forward", st)
+    return out
+
+
+def ccq_forward(q, k, v, g, w_lambda, b_lambda, chunk: int = 64, segments: int = 0,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Curvature-conditioned-query read over decayed linear attention.
+    w_lambda [H,dk], b_lambda [H] float32."""
+    dt = _dtype_code(q)
+    (B, H, N, dk, dv), (pq, pk, pv, pg), out, po = _lin_common(q, k, v, g, out)
+    pw = _dev(w_lambda, "w_lambda", torch.float32, (H, dk))
+    pb = _dev(b_lambda, "b_lambda", torch.float32, (H,))
+    nbytes = ccq_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    st = lib().ccq_forward(pq, pk, pv, pg, pw, pb, po, B, H, N, dk, dv, chunk, dt, segments,
+                           ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
+    _check("ccq_forward", st)
+    return out

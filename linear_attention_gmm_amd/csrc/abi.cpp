@@ -1,0 +1,291 @@
+// abi.cpp -- C ABI of the sequence-mixer library: argument checks, workspace
+// layout, segment plan and dispatch. The kernels live in gma.hip and linattn.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/linmix.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int ok() {
+  g_err.clear();
+  return LM_OK;
+}
+
+constexpr int64_t kChunk = 64;
+// Workgroups the segment plan aims for: one per compute unit of an MI355X.
+constexpr int64_t kTargetGroups = 256;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int64_t P;
+  int64_t seg_len;
+};
+
+// Cuts each sequence into P segments of whole chunks. Depends only on the
+// shapes (and the caller's explicit request), so results are reproducible.
+Plan plan_segments(int64_t BH, int64_t N, int64_t segments) {
+  const int64_t nch = (N + kChunk - 1) / kChunk;
+  int64_t P = segments > 0 ? segments : (kTargetGroups + BH - 1) / BH;
+  if (P < 1) P = 1;
+  if (P > nch) P = nch;
+  const int64_t cps = (nch + P - 1) / P;
+  P = (nch + cps - 1) / cps;
+  return Plan{P, cps * kChunk};
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+size_t esize(int dtype) { return dtype == LM_BF16 ? 2 : 4; }
+
+// ----------------------------------------------------------------------------- GMA
+
+int gma_kp(int64_t K) {
+  if (K <= 32) return 32;
+  if (K <= 64) return 64;
+  if (K <= 128) return 128;
+  return 256;
+}
+
+struct GmaLayout {
+  size_t W, c, agg, aggz, total;
+  Plan plan;
+  int64_t KP;
+};
+
+GmaLayout gma_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int dtype,
+                     int64_t segments) {
+  GmaLayout L;
+  L.KP = gma_kp(K);
+  L.plan = plan_segments(B * H, N, segments);
+  size_t off = 0;
+  L.W = off;
+  off = align_up(off + (size_t)H * L.KP * 2 * d * esize(dtype));
+  L.c = off;
+  off = align_up(off + (size_t)H * L.KP * 4);
+  L.agg = off;
+  off = align_up(off + (size_t)B * H * L.plan.P * L.KP * dv * 4);
+  L.aggz = off;
+  off = align_up(off + (size_t)B * H * L.plan.P * L.KP * 4);
+  L.total = off;
+  return L;
+}
+
+int gma_check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal,
+                    int dtype, int64_t segments) {
+  if (B < 1 || H < 1 || N < 1 || d < 1 || K < 1 || dv < 1)
+    return fail(LM_EINVAL, "sizes must be >= 1 (B=%lld H=%lld N=%lld d=%lld K=%lld dv=%lld)",
+                (long long)B, (long long)H, (long long)N, (long long)d, (long long)K, (long long)dv);
+  if (dtype != LM_F32 && dtype != LM_BF16) return fail(LM_EINVAL, "dtype %d is not LM_F32 or LM_BF16", dtype);
+  if (causal != 0 && causal != 1) return fail(LM_EINVAL, "causal must be 0 or 1 (got %d)", causal);
+  if (segments < 0) return fail(LM_EINVAL, "segments must be >= 0 (got %lld)", (long long)segments);
+  if (!(d == 32 || d == 64 || d == 128) || dv != d)
+    return fail(LM_EUNSUPPORTED, "gma_forward implements d == dv in {32, 64, 128} (got d=%lld dv=%lld)",
+                (long long)d, (long long)dv);
+  if (K > 256) return fail(LM_EUNSUPPORTED, "gma_forward implements K <= 256 (got %lld)", (long long)K);
+  if (dtype == LM_F32 && d == 128 && K > 128)
+    return fail(LM_EUNSUPPORTED, "gma_forward in float32 implements K <= 128 at d = 128 (got %lld)", (long long)K);
+  if (N > (int64_t(1) << 30) || B * H > 65535)
+    return fail(LM_EUNSUPPORTED, "N <= 2^30 and B*H <= 65535 are implemented");
+  return LM_OK;
+}
+
+// ----------------------------------------------------------------------------- linear attention
+
+struct LinLayout {
+  size_t agg, total;
+  Plan plan;
+};
+
+LinLayout lin_layout(int64_t B, int64_t H, int64_t N, int64_t dk, bool ccq, int64_t segments) {
+  LinLayout L;
+  L.plan = plan_segments(B * H, N, segments);
+  L.agg = 0;
+  L.total = align_up((size_t)B * H * L.plan.P * lm::lin_state_floats(dk, ccq) * 4);
+  return L;
+}
+
+int lin_check_shape(const char* fn, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                    int dtype, int64_t segments) {
+  if (B < 1 || H < 1 || N < 1 || dk < 1 || dv < 1 || chunk < 1)
+    return fail(LM_EINVAL, "%s: sizes must be >= 1", fn);
+  if (dtype != LM_F32 && dtype != LM_BF16) return fail(LM_EINVAL, "%s: dtype %d is not LM_F32 or LM_BF16", fn, dtype);
+  if (segments < 0) return fail(LM_EINVAL, "%s: segments must be >= 0", fn);
+  if (chunk != kChunk) return fail(LM_EUNSUPPORTED, "%s: chunk %lld; 64 is implemented", fn, (long long)chunk);
+  if (!(dk == 32 || dk == 64 || dk == 128) || dv != dk)
+    return fail(LM_EUNSUPPORTED, "%s implements dk == dv in {32, 64, 128} (got dk=%lld dv=%lld)", fn,
+                (long long)dk, (long long)dv);
+  if (N > (int64_t(1) << 30) || B * H > 65535)
+    return fail(LM_EUNSUPPORTED, "%s: N <= 2^30 and B*H <= 65535 are implemented", fn);
+  return LM_OK;
+}
+
+int lin_forward(const char* fn, bool ccq, const void* q, const void* k, const void* v, const float* g,
+                const float* w_lambda, const float* b_lambda, void* out, int64_t B, int64_t H, int64_t N,
+                int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int st = lin_check_shape(fn, B, H, N, dk, dv, chunk, dtype, segments);
+  if (st != LM_OK) return st;
+  if (!q || !k || !v || !g || !out || !workspace || (ccq && (!w_lambda || !b_lambda)))
+    return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+      !aligned(g, 4) || (ccq && (!aligned(w_lambda, 4) || !aligned(b_lambda, 4))))
+    return fail(LM_EINVAL, "%s: misaligned pointer (tensors need 16 bytes, parameters 4)", fn);
+  const size_t es = esize(dtype);
+  const size_t nq = (size_t)B * H * N * dk * es, nv = (size_t)B * H * N * dv * es;
+  const LinLayout L = lin_layout(B, H, N, dk, ccq, segments);
+  if (workspace_bytes < L.total)
+    return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
+  if (overlap(out, nv, q, nq) || overlap(out, nv, k, nq) || overlap(out, nv, v, nv) ||
+      overlap(out, nv, g, (size_t)B * H * N * 4) || overlap(out, nv, workspace, L.total))
+    return fail(LM_EINVAL, "%s: out overlaps an input or the workspace", fn);
+  lm::LinLaunch La;
+  La.q = q;
+  La.k = k;
+  La.v = v;
+  La.g = g;
+  La.w_lambda = w_lambda;
+  La.b_lambda = b_lambda;
+  La.out = out;
+  La.agg = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.agg);
+  La.B = B;
+  La.H = H;
+  La.N = N;
+  La.D = dk;
+  La.P = L.plan.P;
+  La.seg_len = L.plan.seg_len;
+  La.bf16 = dtype == LM_BF16;
+  La.ccq = ccq;
+  hipError_t e = lm::linattn_launch(La, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int lm_abi_version(void) { return LM_ABI_VERSION; }
+
+const char* lm_status_string(int status) {
+  switch (status) {
+    case LM_OK: return "LM_OK";
+    case LM_EINVAL: return "LM_EINVAL";
+    case LM_EUNSUPPORTED: return "LM_EUNSUPPORTED";
+    case LM_EWORKSPACE: return "LM_EWORKSPACE";
+    case LM_EHIP: return "LM_EHIP";
+    default: return "LM_UNKNOWN";
+  }
+}
+
+const char* lm_last_error(void) { return g_err.c_str(); }
+
+size_t gma_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal,
+                           int dtype, int64_t segments) {
+  if (gma_check_shape(B, H, N, d, K, dv, causal, dtype, segments) != LM_OK) return 0;
+  return gma_layout(B, H, N, d, K, dv, dtype, segments).total;
+}
+
+int gma_forward(const void* q, const void* k, const void* v, const float* mu, const float* log_var,
+                const float* logit_pi, void* out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t K,
+                int64_t dv, int causal, float eps, int dtype, int64_t segments, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int st = gma_check_shape(B, H, N, d, K, dv, causal, dtype, segments);
+  if (st != LM_OK) return st;
+  if (!(eps >= 0.f) || std::isinf(eps)) return fail(LM_EINVAL, "gma_forward: eps must be finite and >= 0");
+  if (!q || !k || !v || !mu || !log_var || !logit_pi || !out || !workspace)
+    return fail(LM_EINVAL, "gma_forward: null pointer argument");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+      !aligned(mu, 4) || !aligned(log_var, 4) || !aligned(logit_pi, 4))
+    return fail(LM_EINVAL, "gma_forward: misaligned pointer (tensors need 16 bytes, parameters 4)");
+  const GmaLayout L = gma_layout(B, H, N, d, K, dv, dtype, segments);
+  if (workspace_bytes < L.total)
+    return fail(LM_EWORKSPACE, "gma_forward: workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  const size_t es = esize(dtype);
+  const size_t nq = (size_t)B * H * N * d * es, nv = (size_t)B * H * N * dv * es;
+  if (overlap(out, nv, q, nq) || overlap(out, nv, k, nq) || overlap(out, nv, v, nv) ||
+      overlap(out, nv, workspace, L.total) || overlap(out, nv, mu, (size_t)H * K * d * 4) ||
+      overlap(out, nv, log_var, (size_t)H * K * d * 4) || overlap(out, nv, logit_pi, (size_t)H * K * 4))
+    return fail(LM_EINVAL, "gma_forward: out overlaps an input or the workspace");
+  lm::GmaLaunch La;
+  char* ws = static_cast<char*>(workspace);
+  La.q = q;
+  La.k = k;
+  La.v = v;
+  La.out = out;
+  La.mu = mu;
+  La.log_var = log_var;
+  La.logit_pi = logit_pi;
+  La.W = ws + L.W;
+  La.c = reinterpret_cast<float*>(ws + L.c);
+  La.agg = reinterpret_cast<float*>(ws + L.agg);
+  La.aggz = reinterpret_cast<float*>(ws + L.aggz);
+  La.B = B;
+  La.H = H;
+  La.N = N;
+  La.D = d;
+  La.K = K;
+  La.KP = L.KP;
+  La.P = L.plan.P;
+  La.seg_len = L.plan.seg_len;
+  La.causal = causal;
+  La.bf16 = dtype == LM_BF16;
+  La.eps = eps;
+  hipError_t e = lm::gma_launch(La, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_EHIP, "gma_forward: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t linattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
+                               int64_t segments) {
+  if (lin_check_shape("linattn_chunk_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
+  return lin_layout(B, H, N, dk, false, segments).total;
+}
+
+int linattn_chunk_forward(const void* q, const void* k, const void* v, const float* g, void* out, int64_t B,
+                          int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return lin_forward("linattn_chunk_forward", false, q, k, v, g, nullptr, nullptr, out, B, H, N, dk, dv, chunk,
+                     dtype, segments, workspace, workspace_bytes, stream);
+}
+
+size_t ccq_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
+                           int64_t segments) {
+  if (lin_check_shape("ccq_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
+  return lin_layout(B, H, N, dk, true, segments).total;
+}
+
+int ccq_forward(const void* q, const void* k, const void* v, const float* g, const float* w_lambda,
+                const float* b_lambda, void* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                int64_t chunk, int dtype, int64_t segments, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  return lin_forward("ccq_forward", true, q, k, v, g, w_lambda, b_lambda, out, B, H, N, dk, dv, chunk, dtype,
+                     segments, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

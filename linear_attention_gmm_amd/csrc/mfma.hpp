@@ -1,0 +1,198 @@
+// mfma.hpp -- CDNA4 (gfx950) matrix-core and wavefront helpers shared by the
+// mixer kernels.
+//
+// Matrix products use 16x16 output tiles:
+//   bf16: v_mfma_f32_16x16x32_bf16  (k-step 32, 8 bf16 per lane per operand)
+//   f32 : v_mfma_f32_16x16x4_f32    (k-step 4, 1 float per lane per operand)
+// Lane layouts (verified on gfx950):
+//   A (16 x k): lane l holds row l%16; its k-values come from lane group g = l/16.
+//   B (k x 16): lane l holds column l%16; k-values from group g.
+//   D (16 x 16, fp32): lane l holds column l%16, rows 4g..4g+3 (one f32x4).
+//
+// Which k-values a group holds within one k-step is a free choice, so long as
+// A and B agree. Two orders are used:
+//   NATURAL: bf16 k = 8g..8g+7 ; f32 k = g.
+//   CHAIN  : the order in which a D tile's rows sit in registers. This lets an
+//            accumulator feed the next product straight from registers.
+//            bf16 (32 rows = tiles t0, t1): k = {4g..4g+3} U {16+4g..16+4g+3};
+//            f32 (step s of a 16-row tile): k = 4g + s.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lm {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define LM_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+  static constexpr int KS = 32;
+  typedef bf16x8 frag;
+  __device__ static __forceinline__ f32x4 mma(const frag& a, const frag& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ frag zero() {
+    frag z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (bf16)0.f;
+    return z;
+  }
+  // CHAIN fragment of k-step s from D tiles stacked along k (tiles[2s], tiles[2s+1]).
+  __device__ static __forceinline__ frag chain(const f32x4* tiles, int s) {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = (bf16)tiles[2 * s][i];
+      f[4 + i] = (bf16)tiles[2 * s + 1][i];
+    }
+    return f;
+  }
+  // Same from two explicit tiles.
+  __device__ static __forceinline__ frag chain2(const f32x4& t0, const f32x4& t1) {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = (bf16)t0[i];
+      f[4 + i] = (bf16)t1[i];
+    }
+    return f;
+  }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int KS = 4;
+  typedef float frag;
+  __device__ static __forceinline__ f32x4 mma(frag a, frag b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ frag zero() { return 0.f; }
+  __device__ static __forceinline__ frag chain(const f32x4* tiles, int s) { return tiles[s >> 2][s & 3]; }
+};
+
+// Number of 16-row D tiles one k-step spans in CHAIN order.
+template <typename T>
+struct ChainTiles {
+  static constexpr int value = 2;  // bf16: 32 rows
+};
+template <>
+struct ChainTiles<float> {
+  static constexpr int value = 0;  // f32: 4 steps share one tile (use Mma<float>::chain)
+};
+
+// ---------------------------------------------------------------------------
+// LDS fragment loads. `base` points at element (row 0, col 0) of a row-major
+// LDS tile with `pitch` elements per row.
+
+// k contiguous in memory: operand row/column index `rc` (the lane's row of A or
+// column of B) is a memory row, k runs along the row. NATURAL order.
+__device__ __forceinline__ bf16x8 ld_kc_nat(const bf16* base, int pitch, int rc, int kstep) {
+  const int g = lane_id() >> 4;
+  return *reinterpret_cast<const bf16x8*>(base + rc * pitch + kstep * 32 + 8 * g);
+}
+__device__ __forceinline__ float ld_kc_nat(const float* base, int pitch, int rc, int kstep) {
+  const int g = lane_id() >> 4;
+  return base[rc * pitch + kstep * 4 + g];
+}
+// CHAIN order, k contiguous.
+__device__ __forceinline__ bf16x8 ld_kc_chain(const bf16* base, int pitch, int rc, int kstep) {
+  const int g = lane_id() >> 4;
+  const bf16* p = base + rc * pitch + kstep * 32 + 4 * g;
+  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ float ld_kc_chain(const float* base, int pitch, int rc, int kstep) {
+  const int g = lane_id() >> 4;
+  return base[rc * pitch + 16 * (kstep >> 2) + 4 * g + (kstep & 3)];
+}
+
+// k-major in memory: k is the memory row, the operand's row/column index is the
+// memory column. `c0` is the first column of the 16-wide tile. CHAIN order.
+// bf16 uses the gfx950 LDS transpose read: each 16-lane group reads a 4 x 16
+// block (lane j of the group supplies row k0 + j/4, columns c0 + 4(j%4)..+3)
+// and lane p of the group receives column c0 + p of the four rows.
+__device__ __forceinline__ bf16x4 tr16(const bf16* base, int pitch, int c0, int k0) {
+  const int j = lane_id() & 15;
+  const bf16* p = base + (k0 + (j >> 2)) * pitch + c0 + 4 * (j & 3);
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LM_LDS*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+__device__ __forceinline__ bf16x8 ld_km_chain(const bf16* base, int pitch, int c0, int kstep) {
+  const int g = lane_id() >> 4;
+  bf16x4 lo = tr16(base, pitch, c0, kstep * 32 + 4 * g);
+  bf16x4 hi = tr16(base, pitch, c0, kstep * 32 + 16 + 4 * g);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ float ld_km_chain(const float* base, int pitch, int c0, int kstep) {
+  const int g = lane_id() >> 4;
+  const int k = 16 * (kstep >> 2) + 4 * g + (kstep & 3);
+  return base[k * pitch + c0 + (lane_id() & 15)];
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions.
+
+// Across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Sum over the 16 lanes of a row (DPP row rotations); every lane gets the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Element conversion.
+template <typename T>
+__device__ __forceinline__ float to_f32(T x) {
+  return (float)x;
+}
+template <typename T>
+__device__ __forceinline__ T from_f32(float x) {
+  return (T)x;
+}
+
+// 16-byte vector of T.
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<bf16> {
+  static constexpr int n = 8;
+  typedef bf16x8 type;
+};
+template <>
+struct Vec16<float> {
+  static constexpr int n = 4;
+  typedef f32x4 type;
+};
+
+}  // namespace lm

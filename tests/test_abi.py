@@ -1,0 +1,143 @@
+"""The C ABI library on the host: it loads without a GPU, exports every function
+include/linmix.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_gmm_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linmix.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH), reason="liblinmix.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) - {"if", "sizeof"})
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gma_forward", "linattn_chunk_forward", "ccq_forward", "gma_workspace_bytes",
+              "linattn_workspace_bytes", "ccq_workspace_bytes", "lm_abi_version", "lm_status_string",
+              "lm_last_error"):
+        assert n in names
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@needs_lib
+def test_version_and_status_strings():
+    L = binding.lib()
+    assert L.lm_abi_version() == 1
+    for code, name in enumerate(["LM_OK", "LM_EINVAL", "LM_EUNSUPPORTED", "LM_EWORKSPACE", "LM_EHIP"]):
+        assert L.lm_status_string(code).decode() == name
+    assert L.lm_status_string(99).decode() == "LM_UNKNOWN"
+
+
+FAKE = 1 << 40  # an aligned address that is never dereferenced (calls fail before any HIP call)
+
+
+def _gma(L, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), mu=FAKE + (3 << 30), lv=FAKE + (4 << 30),
+             lp=FAKE + (5 << 30), out=FAKE + (6 << 30), B=1, H=2, N=100, d=64, K=16, dv=64, causal=1,
+             eps=1e-6, dt=binding.LM_BF16, seg=0, ws=FAKE + (7 << 30), wsb=0)
+    a.update(kw)
+    if a["wsb"] == 0 and "wsb" not in kw:
+        a["wsb"] = L.gma_workspace_bytes(a["B"], a["H"], a["N"], a["d"], a["K"], a["dv"], a["causal"], a["dt"], a["seg"])
+    st = L.gma_forward(a["q"], a["k"], a["v"], a["mu"], a["lv"], a["lp"], a["out"], a["B"], a["H"], a["N"], a["d"],
+                       a["K"], a["dv"], a["causal"], a["eps"], a["dt"], a["seg"], a["ws"], a["wsb"], None)
+    return st, L.lm_last_error().decode()
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), binding.LM_EINVAL),
+    (dict(out=FAKE + (6 << 30) + 2), binding.LM_EINVAL),  # misaligned
+    (dict(N=0), binding.LM_EINVAL),
+    (dict(eps=-1.0), binding.LM_EINVAL),
+    (dict(eps=float("nan")), binding.LM_EINVAL),
+    (dict(causal=2), binding.LM_EINVAL),
+    (dict(dt=7), binding.LM_EINVAL),
+    (dict(seg=-1), binding.LM_EINVAL),
+    (dict(d=48, dv=48), binding.LM_EUNSUPPORTED),
+    (dict(d=64, dv=32), binding.LM_EUNSUPPORTED),
+    (dict(K=257), binding.LM_EUNSUPPORTED),
+    (dict(d=128, dv=128, K=200, dt=binding.LM_F32), binding.LM_EUNSUPPORTED),
+    (dict(wsb=16), binding.LM_EWORKSPACE),
+    (dict(out=FAKE + 16), binding.LM_EINVAL),  # overlaps q
+])
+def test_gma_errors(kw, code):
+    st, msg = _gma(binding.lib(), **kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def _lin(L, fn, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30), w=FAKE + (4 << 30),
+             b=FAKE + (5 << 30), out=FAKE + (6 << 30), B=1, H=2, N=100, dk=64, dv=64, chunk=64,
+             dt=binding.LM_BF16, seg=0, ws=FAKE + (7 << 30), wsb=None)
+    a.update(kw)
+    ccq = fn == "ccq_forward"
+    if a["wsb"] is None:
+        wsf = L.ccq_workspace_bytes if ccq else L.linattn_workspace_bytes
+        a["wsb"] = wsf(a["B"], a["H"], a["N"], a["dk"], a["dv"], a["chunk"], a["dt"], a["seg"])
+    if ccq:
+        st = L.ccq_forward(a["q"], a["k"], a["v"], a["g"], a["w"], a["b"], a["out"], a["B"], a["H"], a["N"], a["dk"],
+                           a["dv"], a["chunk"], a["dt"], a["seg"], a["ws"], a["wsb"], None)
+    else:
+        st = L.linattn_chunk_forward(a["q"], a["k"], a["v"], a["g"], a["out"], a["B"], a["H"], a["N"], a["dk"],
+                                     a["dv"], a["chunk"], a["dt"], a["seg"], a["ws"], a["wsb"], None)
+    return st, L.lm_last_error().decode()
+
+
+@needs_lib
+@pytest.mark.parametrize("fn", ["linattn_chunk_forward", "ccq_forward"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), binding.LM_EINVAL),
+    (dict(g=FAKE + (3 << 30) + 2), binding.LM_EINVAL),
+    (dict(H=0), binding.LM_EINVAL),
+    (dict(chunk=32), binding.LM_EUNSUPPORTED),
+    (dict(dk=96, dv=96), binding.LM_EUNSUPPORTED),
+    (dict(dk=64, dv=128), binding.LM_EUNSUPPORTED),
+    (dict(wsb=8), binding.LM_EWORKSPACE),
+    (dict(out=FAKE + (2 << 30) + 64), binding.LM_EINVAL),  # overlaps v
+])
+def test_linattn_errors(fn, kw, code):
+    st, msg = _lin(binding.lib(), fn, **kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+@needs_lib
+def test_ccq_needs_gate_parameters():
+    st, _ = _lin(binding.lib(), "ccq_forward", w=None)
+    assert st == binding.LM_EINVAL
+
+
+@needs_lib
+def test_workspace_sizes_are_deterministic_and_grow_with_segments():
+    L = binding.lib()
+    a = L.gma_workspace_bytes(4, 8, 16384, 64, 128, 64, 1, binding.LM_BF16, 0)
+    assert a == L.gma_workspace_bytes(4, 8, 16384, 64, 128, 64, 1, binding.LM_BF16, 0) and a > 0
+    assert L.gma_workspace_bytes(4, 8, 16384, 64, 128, 64, 1, binding.LM_BF16, 16) > \
+        L.gma_workspace_bytes(4, 8, 16384, 64, 128, 64, 1, binding.LM_BF16, 2)
+    assert L.gma_workspace_bytes(4, 8, 16384, 48, 128, 48, 1, binding.LM_BF16, 0) == 0
+    assert L.ccq_workspace_bytes(4, 16, 16384, 128, 128, 64, binding.LM_BF16, 0) > \
+        L.linattn_workspace_bytes(4, 16, 16384, 128, 128, 64, binding.LM_BF16, 0)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 32)
+    with pytest.raises((ValueError, RuntimeError)):
+        binding.gma_forward(q, q, q, torch.zeros(1, 4, 32), torch.zeros(1, 4, 32), torch.zeros(1, 4))
