@@ -23,10 +23,13 @@ LIB = os.path.join(PKG, "liblinmix.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
-# Packed fp32 VALU forms are kept out of the generated code; the host pass warns
-# that it does not know the feature, which is harmless.
+# Packed fp32 VALU forms are kept out of the generated code (the host pass warns
+# that it does not know the feature, which is harmless). MFMA accumulators are
+# kept in VGPRs where possible, which avoids AGPR<->VGPR copies around the VALU
+# work on accumulators.
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I" + os.path.join(ROOT, "include")]
 
 
@@ -57,8 +60,18 @@ def build(jobs: int = 0) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
+    _check_symbols(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_symbols(path: str) -> None:
+    """Fails the build when the library references its own code it does not define
+    (e.g. a kernel stub that was never instantiated)."""
+    r = subprocess.run(["nm", "-D", "--undefined-only", path], capture_output=True, text=True)
+    bad = [l.split()[-1] for l in r.stdout.splitlines() if "_ZN2lm" in l]
+    if bad:
+        raise RuntimeError("undefined library symbols: " + ", ".join(bad))
 
 
 if __name__ == "__main__":

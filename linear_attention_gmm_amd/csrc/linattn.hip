@@ -23,21 +23,28 @@
 //           = -alpha_i M_prev q_i + sum_{j<=i} k_j (beta_i - alpha_i P_ij) + beta_i m_prev
 //   alpha_i = lambda_i / t,  beta_i = lambda_i (m_prev . q_i + sum_{j<=i} P_ij) / t^2.
 // The read then uses q + delta. delta is formed in fp32 and rounded once, so the
-// correction survives even where it is far below bf16 resolution of q.
+// correction survives even where it is far below the bf16 resolution of q.
 //
-// MI355X design: the transposed formulation (lane = query token) lets every
-// product chain from registers. A workgroup of NW waves owns one (b, h,
-// segment). Wave w owns the value columns [w CW, (w+1) CW) of S (and the same
-// columns of the symmetric M). Q/K/V tiles sit row-major in LDS; k-major
-// operands use the gfx950 transpose read. A segment pass (AGG) and a prefix
-// combine at segment start give enough workgroups for short B*H.
+// MI355X design
+//  * Transposed formulation (lane = query token): products chain from registers.
+//  * A workgroup of NW waves owns one (b, h, segment). Wave w owns the value
+//    columns [w CW, (w+1) CW) of S and the same columns of the symmetric M,
+//    and query tiles {w, w + NW, ...} for the per-query work (raw scores, gate,
+//    mean terms, decay mask), which is done once per workgroup and handed to
+//    the other waves through LDS.
+//  * Q/K/V/g tiles arrive by direct global->LDS DMA into XOR-swizzled,
+//    double-buffered tiles; the next chunk is in flight while this one is
+//    computed. k-major operands use the gfx950 LDS transpose read.
+//  * A segment pass (AGG) and a prefix combine at segment start give enough
+//    workgroups for short B*H.
 #include "mfma.hpp"
 #include "launch.hpp"
 
 namespace lm {
 namespace lin {
 
-constexpr int kChunk = 64;
+constexpr int kC = 64;
+constexpr int kLds = 160 * 1024;
 
 struct Args {
   const void* q;
@@ -60,54 +67,54 @@ struct Waves {
   static constexpr int NW = D / 16 < 4 ? D / 16 : 4;
   static constexpr int CW = D / NW;  // value (and M) columns per wave
   static constexpr int CT = CW / 16;
+  static constexpr int QPW = 4 / NW;  // query tiles per wave
 };
 
 template <typename T, int D, bool CCQ, bool AGG>
 struct Cfg {
   typedef Waves<D> Wv;
-  static constexpr int NW = Wv::NW, CW = Wv::CW, CT = Wv::CT;
+  static constexpr int NW = Wv::NW, CW = Wv::CW, CT = Wv::CT, QPW = Wv::QPW;
   static constexpr int KS = Mma<T>::KS;
-  static constexpr int NKD = D / KS;      // k-steps over features
-  static constexpr int NKT = kChunk / KS; // k-steps over tokens
-  static constexpr int DT = D / 16;       // feature tiles
-  static constexpr int PAD = 16 / (int)sizeof(T);
-  static constexpr int PQ = D + PAD;
-  static constexpr int tile = kChunk * PQ * (int)sizeof(T);
-  static constexpr int o_q = 0;
-  static constexpr int o_k = o_q + (AGG ? 0 : tile);
-  static constexpr int o_v = o_k + tile;
-  static constexpr int o_d = o_v + tile;                      // delta (CCQ)
-  static constexpr int o_o = o_d + ((CCQ && !AGG) ? tile : 0); // output staging
-  // rest of the layout without the staging tile, to decide whether it fits
-  static constexpr int rest = ((CCQ && !AGG) ? 16 * PQ * (int)sizeof(T) : 0) + kChunk * 4 + (CCQ ? D * 4 : 0);
-  static constexpr bool STAGE_O = !AGG && o_o + tile + rest <= 160 * 1024;
-  static constexpr int o_dot = o_o + (STAGE_O ? tile : 0);    // [16][PQ] gate/mean rows (CCQ)
-  static constexpr int o_l = o_dot + ((CCQ && !AGG) ? 16 * PQ * (int)sizeof(T) : 0);
-  static constexpr int o_m = o_l + kChunk * 4;
-  static constexpr int lds = o_m + (CCQ ? D * 4 : 0);
-  static_assert(lds <= 160 * 1024, "LDS budget");
+  static constexpr int NKD = D / KS;   // k-steps over features
+  static constexpr int NKT = kC / KS;  // k-steps over tokens
+  static constexpr int DT = D / 16;    // feature tiles
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int CPR = D * ES / 16;
+  static constexpr int TB = kC * D * ES;  // one swizzled tile
+  static constexpr int PADE = 16 / ES;    // padding of register-written tiles
+  static constexpr int PD = D + PADE;     // delta / output tile pitch (elements)
+  static constexpr int PP = kC + PADE;    // score tile pitch (elements)
+  static constexpr int NTILE = AGG ? 2 : 3;                 // (Q), K, V
+  static constexpr int BUF = NTILE * TB + 256;              // + g
+  static constexpr int o_d = 0;                             // delta [64][PD]
+  static constexpr int d_bytes = (CCQ && !AGG) ? kC * PD * ES : 0;
+  static constexpr int o_p = o_d + d_bytes;                 // scores / Bmat [64 q][PP]
+  static constexpr int p_bytes = AGG ? 0 : kC * PP * ES;
+  static constexpr int o_dot = o_p + p_bytes;               // [16][PD] gate and mean rows
+  static constexpr int dot_bytes = (CCQ && !AGG) ? 16 * PD * ES : 0;
+  static constexpr int o_small = o_dot + dot_bytes;         // sL [NW][64], sAB [64] float2, sMv [D]
+  static constexpr int small_bytes = NW * kC * 4 + kC * 8 + D * 4;
+  static constexpr int o_o = o_small + small_bytes;         // output staging [64][PD]
+  static constexpr int o_bytes = AGG ? 0 : kC * PD * ES;
+  static constexpr bool STAGE_O = !AGG && o_o + o_bytes + BUF <= kLds;
+  static constexpr int o_buf = (o_o + (STAGE_O ? o_bytes : 0) + 15) / 16 * 16;
+  static constexpr int NBUF = o_buf + 2 * BUF <= kLds ? 2 : 1;
+  static constexpr int lds = o_buf + NBUF * BUF;
+  static_assert(lds <= kLds, "LDS budget");
 };
 
 template <typename T, int D, int NT>
-__device__ __forceinline__ void load_tile(T* s, int pq, const T* __restrict__ src, int nvalid) {
+__device__ __forceinline__ void store_rows(T* __restrict__ dst, const T* s, int pitch, int nrows) {
   typedef typename Vec16<T>::type vec;
   constexpr int VN = Vec16<T>::n;
   constexpr int PER_ROW = D / VN;
-  for (int i = threadIdx.x; i < kChunk * PER_ROW; i += NT) {
+  for (int i = threadIdx.x; i < nrows * PER_ROW; i += NT) {
     const int row = i / PER_ROW, cv = i - (i / PER_ROW) * PER_ROW;
-    vec x;
-    if (row < nvalid) {
-      x = *reinterpret_cast<const vec*>(src + (size_t)row * D + cv * VN);
-    } else {
-#pragma unroll
-      for (int j = 0; j < VN; ++j) x[j] = from_f32<T>(0.f);
-    }
-    *reinterpret_cast<vec*>(s + row * pq + cv * VN) = x;
+    *reinterpret_cast<vec*>(dst + (size_t)row * D + cv * VN) = *reinterpret_cast<const vec*>(s + row * pitch + cv * VN);
   }
 }
 
-// hi/lo split of an fp32 D tile into two CHAIN fragments (bf16), or the value
-// itself (f32; lo = 0).
+// hi/lo split of fp32 D tiles into two CHAIN fragments (bf16), or the value (f32).
 template <typename T>
 struct Split;
 template <>
@@ -130,22 +137,70 @@ struct Split<float> {
   }
 };
 
+// Decay weights 2^(l_last - l_j) applied to the token entries of a CHAIN-order
+// k-major fragment of step s.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag decay_tokens(typename Mma<T>::frag f, const float* sl, float l_last,
+                                                               int s) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (bf16)((float)f[i] * fast_exp2(l_last - sl[chain_k<T>(s, i)]));
+    return f;
+  } else {
+    return f * fast_exp2(l_last - sl[chain_k<T>(s, 0)]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float frag_sum(const typename Mma<T>::frag& f) {
+  if constexpr (sizeof(T) == 2) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += (float)f[i];
+    return s;
+  } else {
+    return f;
+  }
+}
+
+template <typename C, bool AGG>
+__device__ __forceinline__ char* buf_k(char* base, int b) { return base + b * C::BUF + (AGG ? 0 : C::TB); }
+template <typename C, bool AGG>
+__device__ __forceinline__ char* buf_v(char* base, int b) { return base + b * C::BUF + (AGG ? 1 : 2) * C::TB; }
+template <typename C>
+__device__ __forceinline__ float* buf_g(char* base, int b) {
+  return reinterpret_cast<float*>(base + b * C::BUF + C::NTILE * C::TB);
+}
+
+// Issues the DMA of one chunk (Q unless AGG, K, V, and the decays) into buffer b.
+template <typename T, int D, typename C, bool AGG>
+__device__ __forceinline__ void issue_chunk(const TileDma<T, D, C::NW>& dma, char* base, int b, const T* Qg,
+                                            const T* Kg, const T* Vg, const float* Gg, int64_t c0, int64_t N) {
+  const int nv = (int)((N - c0) < kC ? (N - c0) : kC);
+  if constexpr (!AGG) dma.issue(base + b * C::BUF, Qg + (size_t)c0 * D, nv);
+  dma.issue(buf_k<C, AGG>(base, b), Kg + (size_t)c0 * D, nv);
+  dma.issue(buf_v<C, AGG>(base, b), Vg + (size_t)c0 * D, nv);
+  if (wave_id() == 0) {
+    const rsrc_t rg = make_rsrc(Gg + c0, (uint32_t)(nv * 4));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (LM_LDS void*)(buf_g<C>(base, b)), 4, lane_id() * 4, 0, 0, 0);
+  }
+}
+
 template <typename T, int D, bool CCQ, bool AGG>
 __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
   typedef Cfg<T, D, CCQ, AGG> C;
   typedef Mma<T> M;
   typedef typename M::frag frag;
-  constexpr int NW = C::NW, NT = NW * 64, CT = C::CT, DT = C::DT;
+  constexpr int NW = C::NW, NT = NW * 64, CT = C::CT, DT = C::DT, CPR = C::CPR;
 
   __shared__ __attribute__((aligned(16))) char smem[C::lds];
-  T* sQ = reinterpret_cast<T*>(smem + C::o_q);
-  T* sK = reinterpret_cast<T*>(smem + C::o_k);
-  T* sV = reinterpret_cast<T*>(smem + C::o_v);
-  T* sDl = reinterpret_cast<T*>(smem + C::o_d);
-  T* sO = reinterpret_cast<T*>(smem + C::o_o);
+  T* sD = reinterpret_cast<T*>(smem + C::o_d);
+  T* sP = reinterpret_cast<T*>(smem + C::o_p);
   T* sDot = reinterpret_cast<T*>(smem + C::o_dot);
-  float* sL = reinterpret_cast<float*>(smem + C::o_l);
-  float* sMv = reinterpret_cast<float*>(smem + C::o_m);
+  float* sL = reinterpret_cast<float*>(smem + C::o_small);
+  float2* sAB = reinterpret_cast<float2*>(smem + C::o_small + NW * kC * 4);
+  float* sMv = reinterpret_cast<float*>(smem + C::o_small + NW * kC * 4 + kC * 8);
+  T* sO = reinterpret_cast<T*>(smem + C::o_o);
 
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int bh = blockIdx.y, p = blockIdx.x;
@@ -159,12 +214,17 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
   const float* __restrict__ Gg = a.g + (size_t)bh * N;
   T* __restrict__ Og = reinterpret_cast<T*>(a.out) + (size_t)bh * N * D;
   const int cbase = w * C::CW;
+  float* sLw = sL + w * kC;
+
+  char* const bufbase = smem + C::o_buf;
+  TileDma<T, D, NW> dma;
+  dma.init();
 
   // S[kt][ct]: rows = key features 16 kt + 4 g + r, cols = value dims cbase + 16 ct + c16.
   // M[kt][ct]: rows = features 16 kt + 4 g + r, cols = features cbase + 16 ct + c16.
   f32x4 S[DT][CT];
   f32x4 Mst[CCQ ? DT : 1][CCQ ? CT : 1];
-  float mreg[CT];  // running key sum for column cbase + 16 ct + c16
+  float mreg[CT];  // running key sum of column cbase + 16 ct + c16
 #pragma unroll
   for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
@@ -175,6 +235,10 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) mreg[ct] = 0.f;
   float lseg = 0.f;  // AGG: log2 of the segment's decay product
+
+  if constexpr (C::NBUF == 2) {
+    if (t_begin < t_end) issue_chunk<T, D, C, AGG>(dma, bufbase, 0, Qg, Kg, Vg, Gg, t_begin, N);
+  }
 
   if constexpr (!AGG) {
     for (int pp = 0; pp < p; ++pp) {
@@ -197,302 +261,318 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
     }
   }
   if constexpr (CCQ && !AGG) {
-    // gate rows of the dot tile: row 0 = w (hi), row 1 = w (lo); rows 2, 3 = running key sum (per chunk)
-    for (int i = threadIdx.x; i < 16 * C::PQ; i += NT) {
-      const int row = i / C::PQ, col = i - (i / C::PQ) * C::PQ;
+    // rows 0/1: gate weights (hi/lo); rows 2/3: running key sum (hi/lo); others 0
+    for (int i = threadIdx.x; i < 16 * C::PD; i += NT) {
+      const int row = i / C::PD, col = i - (i / C::PD) * C::PD;
       float x = 0.f;
       if (col < D && row < 2) {
         const float wv = a.wl[(size_t)h * D + col];
         const T hi = from_f32<T>(wv);
         x = row == 0 ? to_f32(hi) : wv - to_f32(hi);
       }
-      sDot[i] = from_f32<T>(x);
+      if (row < 2 || row >= 4 || col >= D) sDot[i] = from_f32<T>(x);
     }
     if (g == 0) {
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) sMv[cbase + 16 * ct + c16] = mreg[ct];
+      for (int ct = 0; ct < CT; ++ct) {
+        const int col = cbase + 16 * ct + c16;
+        const T hi = from_f32<T>(mreg[ct]);
+        sMv[col] = mreg[ct];
+        sDot[2 * C::PD + col] = hi;
+        sDot[3 * C::PD + col] = from_f32<T>(mreg[ct] - to_f32(hi));
+      }
     }
   }
   const float gate_b = CCQ ? a.bl[h] : 0.f;
 
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    const int nvalid = (int)((N - t0) < kChunk ? (N - t0) : kChunk);
-    __syncthreads();  // previous chunk done with the tiles; sMv complete
+  int it = 0;
+  int64_t t_prev = -1;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kC, ++it) {
+    const int nvalid = (int)((N - t0) < kC ? (N - t0) : kC);
+    const int b = C::NBUF == 2 ? (it & 1) : 0;
+    if constexpr (C::NBUF == 1) {
+      __syncthreads();  // previous chunk done with the single buffer
+      issue_chunk<T, D, C, AGG>(dma, bufbase, 0, Qg, Kg, Vg, Gg, t0, N);
+    }
+    wait_vmem();
+    __syncthreads();  // this chunk's tiles landed; the previous chunk is finished everywhere
+    if constexpr (C::STAGE_O) {
+      if (t_prev >= 0) store_rows<T, D, NT>(Og + (size_t)t_prev * D, sO, C::PD, kC);
+    }
+    if constexpr (C::NBUF == 2) {
+      if (t0 + kC < t_end) issue_chunk<T, D, C, AGG>(dma, bufbase, b ^ 1, Qg, Kg, Vg, Gg, t0 + kC, N);
+    }
+    const char* Kt = buf_k<C, AGG>(bufbase, b);
+    const char* Vt = buf_v<C, AGG>(bufbase, b);
 
-    // ---- 1. tiles, cumulative log2 decay, running-mean rows
-    if constexpr (!AGG) load_tile<T, D, NT>(sQ, C::PQ, Qg + (size_t)t0 * D, nvalid);
-    load_tile<T, D, NT>(sK, C::PQ, Kg + (size_t)t0 * D, nvalid);
-    load_tile<T, D, NT>(sV, C::PQ, Vg + (size_t)t0 * D, nvalid);
-    if (w == 0) {
-      float x = l < nvalid ? fmaxf(log2f(Gg[t0 + l]), -200.f) : 0.f;
+    // cumulative log2 decay of this chunk (each wave keeps a private copy)
+    {
+      float x = l < nvalid ? fmaxf(log2f(buf_g<C>(bufbase, b)[l]), -200.f) : 0.f;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const float y = __shfl_up(x, o);
         if (l >= o) x += y;
       }
-      sL[l] = x;
+      sLw[l] = x;
     }
-    if constexpr (CCQ && !AGG) {
-      for (int i = threadIdx.x; i < D; i += NT) {
-        const float mv = sMv[i];
-        const T hi = from_f32<T>(mv);
-        sDot[2 * C::PQ + i] = hi;
-        sDot[3 * C::PQ + i] = from_f32<T>(mv - to_f32(hi));
-      }
-    }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+    const float l_last = sLw[kC - 1];
 
-    const float l_last = sL[kChunk - 1];
+    frag KTc[CCQ ? CT : 1][CCQ ? C::NKT : 1];  // K^T of this wave's columns (CCQ)
+    if constexpr (CCQ) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int s = 0; s < C::NKT; ++s) KTc[ct][s] = tl_kmaj_t<CPR, T>(Kt, s, cbase + 16 * ct);
+    }
 
     if constexpr (!AGG) {
-      float lq[4], bq[4];
+      const char* Qt = bufbase + b * C::BUF;
+      // ---- phase 1: per owned query tile: raw scores, gate/mean terms, Bmat or decayed scores
+      f32x4 Pr[C::QPW][4];
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        lq[qt] = sL[16 * qt + c16];
-        bq[qt] = fast_exp2(lq[qt]);
-      }
-
-      // ---- 2. raw scores P^T[kt][qt] = K Q^T (keys x queries), keys <= query
-      f32x4 Pt[4][4];
+      for (int qi = 0; qi < C::QPW; ++qi) {
+        const int qt = w + NW * qi;
+        frag QF[C::NKD];
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
+        for (int ks = 0; ks < C::NKD; ++ks) QF[ks] = tl_nat_t<CPR, T>(Qt, 16 * qt + c16, ks);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          Pt[kt][qt] = zero4();
+          Pr[qi][kt] = zero4();
           if (kt <= qt) {
 #pragma unroll
             for (int ks = 0; ks < C::NKD; ++ks)
-              Pt[kt][qt] = M::mma(ld_kc_chain(sK, C::PQ, 16 * kt + c16, ks),
-                                  ld_kc_chain(sQ, C::PQ, 16 * qt + c16, ks), Pt[kt][qt]);
+              Pr[qi][kt] = M::mma(tl_nat_t<CPR, T>(Kt, 16 * kt + c16, ks), QF[ks], Pr[qi][kt]);
             if (kt == qt) {
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                if (4 * g + r > c16) Pt[kt][qt][r] = 0.f;
+                if (4 * g + r > c16) Pr[qi][kt][r] = 0.f;
             }
           }
         }
-
-      if constexpr (CCQ) {
-        // ---- 3. per-query gate and mean terms
-        float alpha[4], beta[4];
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
+        const int q = 16 * qt + c16;
+        T* prow = sP + q * C::PP;
+        if constexpr (CCQ) {
           f32x4 dq = zero4();
 #pragma unroll
-          for (int ks = 0; ks < C::NKD; ++ks)
-            dq = M::mma(ld_kc_chain(sDot, C::PQ, c16, ks), ld_kc_chain(sQ, C::PQ, 16 * qt + c16, ks), dq);
-          // rows 0..3 live in group 0: w.q = row0 + row1, m.q = row2 + row3
+          for (int ks = 0; ks < C::NKD; ++ks) dq = M::mma(ld_kc_nat(sDot, C::PD, c16, ks), QF[ks], dq);
           const float wq = __shfl(dq[0] + dq[1], c16);
           const float mq = __shfl(dq[2] + dq[3], c16);
           float rs = 0.f;
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) rs += Pt[kt][qt][r];
+            for (int r = 0; r < 4; ++r) rs += Pr[qi][kt][r];
           rs = group_sum(rs);
-          const float cnt = (float)(t0 + 16 * qt + c16 + 1);
+          const float cnt = (float)(t0 + q + 1);
           const float lam = 1.f / (1.f + expf(-(wq + gate_b)));
-          alpha[qt] = lam / cnt;
-          beta[qt] = lam * ((mq + rs) / cnt) / cnt;
-        }
-        // ---- 4. delta^T for this wave's feature columns
-        float mprev[CT][4];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mprev[ct][r] = sMv[cbase + 16 * ct + 4 * g + r];
-        frag Bf[4][C::NKT];
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-          f32x4 Bt[4];
+          const float alpha = lam / cnt;
+          const float beta = lam * ((mq + rs) / cnt) / cnt;
+          if (g == 0) sAB[q] = make_float2(alpha, beta);
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
+            T* dst = prow + 16 * kt + 4 * g;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const bool in = kt < qt || (kt == qt && 4 * g + r <= c16);
-              Bt[kt][r] = in ? beta[qt] - alpha[qt] * Pt[kt][qt][r] : 0.f;
+              dst[r] = from_f32<T>(in ? beta - alpha * Pr[qi][kt][r] : 0.f);
             }
           }
+        } else {
+          const float lq = sLw[q];
 #pragma unroll
-          for (int s = 0; s < C::NKT; ++s) Bf[qt][s] = M::chain(Bt, s);
+          for (int kt = 0; kt < 4; ++kt) {
+            T* dst = prow + 16 * kt + 4 * g;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float dec = fast_exp2(lq - sLw[16 * kt + 4 * g + r]);
+              dst[r] = from_f32<T>(kt <= qt ? Pr[qi][kt][r] * dec : 0.f);
+            }
+          }
         }
+      }
+      __syncthreads();
+
+
+      if constexpr (CCQ) {
+        // ---- phase 3: delta^T for this wave's feature columns
+        float2 ab[4];
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) ab[qt] = sAB[16 * qt + c16];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
+          const int c0 = cbase + 16 * ct;
           frag Mh[C::NKD], Ml[C::NKD];
-          // A operand rows = features cbase + 16 ct + c16 (symmetric M): column tiles of M
-          f32x4 Mcol[DT];
+          {
+            f32x4 Mcol[DT];
 #pragma unroll
-          for (int kt = 0; kt < DT; ++kt) Mcol[kt] = Mst[kt][ct];
+            for (int kt = 0; kt < DT; ++kt) Mcol[kt] = Mst[kt][ct];
 #pragma unroll
-          for (int s = 0; s < C::NKD; ++s) Split<T>::chain(Mcol, s, Mh[s], Ml[s]);
-          frag KT[C::NKT];
+            for (int s = 0; s < C::NKD; ++s) Split<T>::chain(Mcol, s, Mh[s], Ml[s]);
+          }
+          float mprev[4];
 #pragma unroll
-          for (int s = 0; s < C::NKT; ++s) KT[s] = ld_km_chain(sK, C::PQ, cbase + 16 * ct, s);
+          for (int r = 0; r < 4; ++r) mprev[r] = sMv[c0 + 4 * g + r];
 #pragma unroll
           for (int qt = 0; qt < 4; ++qt) {
             f32x4 mqv = zero4();
 #pragma unroll
             for (int s = 0; s < C::NKD; ++s) {
-              const frag qf = ld_kc_chain(sQ, C::PQ, 16 * qt + c16, s);
+              const frag qf = tl_chain_t<CPR, T>(Qt, 16 * qt + c16, s);
               mqv = M::mma(Mh[s], qf, mqv);
               if constexpr (sizeof(T) == 2) mqv = M::mma(Ml[s], qf, mqv);
             }
             f32x4 kb = zero4();
 #pragma unroll
             for (int s = 0; s < C::NKT; ++s)
-              if ((s * M::KS) / 16 <= qt) kb = M::mma(KT[s], Bf[qt][s], kb);
-            T* dst = sDl + (16 * qt + c16) * C::PQ + cbase + 16 * ct + 4 * g;
+              if ((s * M::KS) / 16 <= qt) kb = M::mma(KTc[ct][s], ld_kc_chain(sP, C::PP, 16 * qt + c16, s), kb);
+            T* dst = sD + (16 * qt + c16) * C::PD + c0 + 4 * g;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              dst[r] = from_f32<T>(-alpha[qt] * mqv[r] + kb[r] + beta[qt] * mprev[ct][r]);
+            for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(-ab[qt].x * mqv[r] + kb[r] + ab[qt].y * mprev[r]);
           }
         }
-        __syncthreads();  // delta complete
-        // ---- 5. scores with the cleaned query: P^T += K delta^T (same mask)
+        __syncthreads();  // delta complete; Bmat consumed
+
+        // ---- phase 4: scores with the cleaned query, decay, for owned query tiles
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt)
+        for (int qi = 0; qi < C::QPW; ++qi) {
+          const int qt = w + NW * qi;
+          const int q = 16 * qt + c16;
+          frag DF[C::NKD];
+#pragma unroll
+          for (int ks = 0; ks < C::NKD; ++ks) DF[ks] = ld_kc_nat(sD, C::PD, q, ks);
+          const float lq = sLw[q];
+          T* prow = sP + q * C::PP;
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
+            f32x4 acc = Pr[qi][kt];
             if (kt <= qt) {
-              f32x4 acc = zero4();
 #pragma unroll
-              for (int ks = 0; ks < C::NKD; ++ks)
-                acc = M::mma(ld_kc_chain(sK, C::PQ, 16 * kt + c16, ks),
-                             ld_kc_chain(sDl, C::PQ, 16 * qt + c16, ks), acc);
+              for (int ks = 0; ks < C::NKD; ++ks) acc = M::mma(tl_nat_t<CPR, T>(Kt, 16 * kt + c16, ks), DF[ks], acc);
+            }
+            T* dst = prow + 16 * kt + 4 * g;
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (kt < qt || 4 * g + r <= c16) Pt[kt][qt][r] += acc[r];
+            for (int r = 0; r < 4; ++r) {
+              const bool in = kt < qt || (kt == qt && 4 * g + r <= c16);
+              const float dec = fast_exp2(lq - sLw[16 * kt + 4 * g + r]);
+              dst[r] = from_f32<T>(in ? acc[r] * dec : 0.f);
             }
           }
+        }
+        __syncthreads();  // decayed scores complete
       }
 
-      // ---- 6. decay mask and read
-      frag Pf[4][C::NKT];
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float lj = sL[16 * kt + 4 * g + r];
-            Pt[kt][qt][r] = kt <= qt ? Pt[kt][qt][r] * fast_exp2(lq[qt] - lj) : 0.f;
-          }
-      }
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        f32x4 col[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) col[kt] = Pt[kt][qt];
-#pragma unroll
-        for (int s = 0; s < C::NKT; ++s) Pf[qt][s] = M::chain(col, s);
-      }
+      // ---- phase 5: outputs of this wave's value columns (query tile outer, so Q and
+      //      delta fragments are read once)
+      frag Sc[CT][C::NKD], Vf[CT][C::NKT];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        frag Sf[C::NKD];
-        {
-          f32x4 Scol[DT];
+        f32x4 Scol[DT];
 #pragma unroll
-          for (int kt = 0; kt < DT; ++kt) Scol[kt] = S[kt][ct];
+        for (int kt = 0; kt < DT; ++kt) Scol[kt] = S[kt][ct];
 #pragma unroll
-          for (int s = 0; s < C::NKD; ++s) Sf[s] = M::chain(Scol, s);
+        for (int s = 0; s < C::NKD; ++s) Sc[ct][s] = M::chain(Scol, s);
+#pragma unroll
+        for (int s = 0; s < C::NKT; ++s) Vf[ct][s] = tl_kmaj_t<CPR, T>(Vt, s, cbase + 16 * ct);
+      }
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        const int q = 16 * qt + c16;
+        f32x4 inter[CT], acc[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          inter[ct] = zero4();
+          acc[ct] = zero4();
         }
-        frag Vf[C::NKT];
 #pragma unroll
-        for (int s = 0; s < C::NKT; ++s) Vf[s] = ld_km_chain(sV, C::PQ, cbase + 16 * ct, s);
+        for (int s = 0; s < C::NKD; ++s) {
+          const frag qf = tl_chain_t<CPR, T>(Qt, 16 * qt + c16, s);
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-          f32x4 inter = zero4();
+          for (int ct = 0; ct < CT; ++ct) inter[ct] = M::mma(Sc[ct][s], qf, inter[ct]);
+          if constexpr (CCQ) {
+            const frag df = ld_kc_chain(sD, C::PD, q, s);
 #pragma unroll
-          for (int s = 0; s < C::NKD; ++s) {
-            inter = M::mma(Sf[s], ld_kc_chain(sQ, C::PQ, 16 * qt + c16, s), inter);
-            if constexpr (CCQ) inter = M::mma(Sf[s], ld_kc_chain(sDl, C::PQ, 16 * qt + c16, s), inter);
+            for (int ct = 0; ct < CT; ++ct) inter[ct] = M::mma(Sc[ct][s], df, inter[ct]);
           }
-          f32x4 acc = zero4();
+        }
 #pragma unroll
-          for (int s = 0; s < C::NKT; ++s)
-            if ((s * M::KS) / 16 <= qt) acc = M::mma(Vf[s], Pf[qt][s], acc);
+        for (int s = 0; s < C::NKT; ++s) {
+          if ((s * M::KS) / 16 <= qt) {
+            const frag pf = ld_kc_chain(sP, C::PP, q, s);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) acc[ct] = M::mma(Vf[ct][s], pf, acc[ct]);
+          }
+        }
+        const float bq = fast_exp2(sLw[q]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int c0 = cbase + 16 * ct;
           if constexpr (C::STAGE_O) {
-            T* dst = sO + (16 * qt + c16) * C::PQ + cbase + 16 * ct + 4 * g;
+            T* dst = sO + q * C::PD + c0 + 4 * g;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(acc[r] + bq[qt] * inter[r]);
-          } else if (16 * qt + c16 < nvalid) {
-            T* dst = Og + (size_t)(t0 + 16 * qt + c16) * D + cbase + 16 * ct + 4 * g;
+            for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(acc[ct][r] + bq * inter[ct][r]);
+          } else if (q < nvalid) {
+            T* dst = Og + (size_t)(t0 + q) * D + c0 + 4 * g;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(acc[r] + bq[qt] * inter[r]);
+            for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(acc[ct][r] + bq * inter[ct][r]);
           }
         }
       }
-      if constexpr (C::STAGE_O) {
-        __syncthreads();
-        typedef typename Vec16<T>::type vec;
-        constexpr int VN = Vec16<T>::n;
-        constexpr int PER_ROW = D / VN;
-        for (int i = threadIdx.x; i < nvalid * PER_ROW; i += NT) {
-          const int row = i / PER_ROW, cv = i - (i / PER_ROW) * PER_ROW;
-          *reinterpret_cast<vec*>(Og + (size_t)(t0 + row) * D + cv * VN) =
-              *reinterpret_cast<const vec*>(sO + row * C::PQ + cv * VN);
-        }
-      }
+      t_prev = t0;
     }
 
-    // ---- 7. state updates
+    // ---- state updates: S <- 2^l_last S + K^T (w V), M += K^T K, m += sum K
     {
       const float b_last = fast_exp2(l_last);
 #pragma unroll
       for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) S[kt][ct] *= b_last;
+      frag Vw[CT][C::NKT];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        frag Vw[C::NKT], Kc[C::NKT];
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int s = 0; s < C::NKT; ++s)
+          Vw[ct][s] = decay_tokens<T>(tl_kmaj_t<CPR, T>(Vt, s, cbase + 16 * ct), sLw, l_last, s);
+#pragma unroll
+      for (int kt = 0; kt < DT; ++kt) {
 #pragma unroll
         for (int s = 0; s < C::NKT; ++s) {
-          frag vf = ld_km_chain(sV, C::PQ, cbase + 16 * ct, s);
-          // scale by 2^(l_last - l_j)
-          if constexpr (sizeof(T) == 2) {
+          const frag kf = tl_kmaj_t<CPR, T>(Kt, s, 16 * kt);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int tok = 32 * s + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
-              vf[i] = (bf16)((float)vf[i] * fast_exp2(l_last - sL[tok]));
-            }
-          } else {
-            const int tok = 16 * (s >> 2) + 4 * g + (s & 3);
-            vf = vf * fast_exp2(l_last - sL[tok]);
-          }
-          Vw[s] = vf;
-          if constexpr (CCQ) Kc[s] = ld_km_chain(sK, C::PQ, cbase + 16 * ct, s);
-        }
-        if constexpr (CCQ) {
-          // running key sum of this wave's columns
-          float cs = 0.f;
-#pragma unroll
-          for (int s = 0; s < C::NKT; ++s) {
-            if constexpr (sizeof(T) == 2) {
-#pragma unroll
-              for (int i = 0; i < 8; ++i) cs += (float)Kc[s][i];
-            } else {
-              cs += Kc[s];
-            }
-          }
-          mreg[ct] += group_sum(cs);
-        }
-#pragma unroll
-        for (int kt = 0; kt < DT; ++kt) {
-#pragma unroll
-          for (int s = 0; s < C::NKT; ++s) {
-            const frag kf = ld_km_chain(sK, C::PQ, 16 * kt, s);
-            S[kt][ct] = M::mma(kf, Vw[s], S[kt][ct]);
-            if constexpr (CCQ) Mst[kt][ct] = M::mma(kf, Kc[s], Mst[kt][ct]);
+          for (int ct = 0; ct < CT; ++ct) {
+            S[kt][ct] = M::mma(kf, Vw[ct][s], S[kt][ct]);
+            if constexpr (CCQ) Mst[kt][ct] = M::mma(kf, KTc[ct][s], Mst[kt][ct]);
           }
         }
       }
-      if constexpr (CCQ && !AGG) {
-        if (g == 0) {
+      if constexpr (CCQ) {
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) sMv[cbase + 16 * ct + c16] = mreg[ct];
+        for (int ct = 0; ct < CT; ++ct) {
+          float cs = 0.f;
+#pragma unroll
+          for (int s = 0; s < C::NKT; ++s) cs += frag_sum<T>(KTc[ct][s]);
+          mreg[ct] += group_sum(cs);
+          if constexpr (!AGG) {
+            if (g == 0) {
+              const int col = cbase + 16 * ct + c16;
+              const T hi = from_f32<T>(mreg[ct]);
+              sMv[col] = mreg[ct];
+              sDot[2 * C::PD + col] = hi;
+              sDot[3 * C::PD + col] = from_f32<T>(mreg[ct] - to_f32(hi));
+            }
+          }
         }
       }
       lseg += l_last;
+    }
+  }
+
+  if constexpr (C::STAGE_O) {
+    __syncthreads();
+    if (t_prev >= 0) {
+      const int nv = (int)((N - t_prev) < kC ? (N - t_prev) : kC);
+      store_rows<T, D, NT>(Og + (size_t)t_prev * D, sO, C::PD, nv);
     }
   }
 
@@ -518,6 +598,13 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
   }
 }
 
+template <typename T, int D, bool CCQ, bool AGG>
+static hipError_t launch_one(const Args& a, unsigned gx, unsigned gy, hipStream_t st) {
+  typedef Cfg<T, D, CCQ, AGG> C;
+  hipLaunchKernelGGL((lin_kernel<T, D, CCQ, AGG>), dim3(gx, gy), dim3(C::NW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool CCQ>
 static hipError_t launch_d(const LinLaunch& L, hipStream_t st) {
   Args a;
@@ -534,12 +621,12 @@ static hipError_t launch_d(const LinLaunch& L, hipStream_t st) {
   a.P = (int)L.P;
   a.seg_len = (int)L.seg_len;
   a.sfl = (int)lin_state_floats(D, CCQ);
-  constexpr int NT = Waves<D>::NW * 64;
   const unsigned BH = (unsigned)(L.B * L.H);
-  if (L.P > 1)
-    hipLaunchKernelGGL((lin_kernel<T, D, CCQ, true>), dim3((unsigned)(L.P - 1), BH), dim3(NT), 0, st, a);
-  hipLaunchKernelGGL((lin_kernel<T, D, CCQ, false>), dim3((unsigned)L.P, BH), dim3(NT), 0, st, a);
-  return hipGetLastError();
+  if (L.P > 1) {
+    hipError_t e = launch_one<T, D, CCQ, true>(a, (unsigned)(L.P - 1), BH, st);
+    if (e != hipSuccess) return e;
+  }
+  return launch_one<T, D, CCQ, false>(a, (unsigned)L.P, BH, st);
 }
 
 template <typename T, bool CCQ>

@@ -145,6 +145,148 @@ __device__ __forceinline__ float ld_km_chain(const float* base, int pitch, int c
 }
 
 // ---------------------------------------------------------------------------
+// Swizzled LDS tiles filled by direct global->LDS DMA.
+//
+// A tile holds 64 rows of RB = D * sizeof(T) bytes, unpadded, cut into 16-byte
+// chunks (CPR = RB / 16 per row). Logical chunk c of row r sits at physical
+// chunk c ^ sw(r). sw is chosen so that the three read shapes used here hit
+// distinct banks (64 banks x 4 bytes):
+//   * 16 consecutive rows, same 16-byte chunk (b128 operand reads);
+//   * 16 consecutive rows, same 8-byte half-chunk (b64 reads, CHAIN order);
+//   * 8 consecutive rows, two adjacent chunks each (the transpose read).
+// The DMA writes 64 consecutive physical chunks per wave instruction, so the
+// swizzle is applied to the global source addresses instead.
+template <int CPR>
+__device__ __forceinline__ int tile_sw(int r) {
+  if constexpr (CPR >= 16) {
+    return ((r & 7) << 1) | ((r >> 3) & 1);
+  } else {
+    constexpr int RPL = 16 / CPR;  // rows per 256-byte bank line
+    const int u = r / RPL;
+    return ((u & (CPR / 2 - 1)) << 1) | ((u / (CPR / 2)) & 1);
+  }
+}
+
+// Byte offset of element `col` of row `r` (element size ES) in a swizzled tile.
+template <int CPR, int ES>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  constexpr int EPC = 16 / ES;  // elements per chunk
+  return r * (CPR * 16) + (((col / EPC) ^ tile_sw<CPR>(r)) * 16) + (col % EPC) * ES;
+}
+
+// Buffer resource over `nbytes` bytes at `base` (raw, stride 0). Loads past
+// nbytes return 0, which is how the tail of a sequence reads as zero rows.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+
+// This wave's share of the DMA of a 64 x D tile into a swizzled LDS tile: each
+// wave moves INSTR blocks of 64 consecutive physical chunks. The per-lane byte
+// offsets in the (row-major, unswizzled) source are fixed, so they are computed
+// once; only the buffer base changes from chunk to chunk.
+template <typename T, int D, int NW>
+struct TileDma {
+  static constexpr int CPR = D * (int)sizeof(T) / 16;
+  static constexpr int INSTR = CPR / NW;
+  static_assert(CPR % NW == 0, "tile split");
+  int voff[INSTR];
+  __device__ __forceinline__ void init() {
+    const int l = lane_id(), w = wave_id();
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      const int p = (w * INSTR + i) * 64 + l;
+      const int r = p / CPR, pc = p - (p / CPR) * CPR;
+      voff[i] = r * CPR * 16 + ((pc ^ tile_sw<CPR>(r)) * 16);
+    }
+  }
+  // src: the tile's first row in global memory; rows: rows of the sequence left from src.
+  __device__ __forceinline__ void issue(char* dst, const T* src, int rows) const {
+    const int w = wave_id();
+    const rsrc_t rs = make_rsrc(src, (uint32_t)((rows < 64 ? rows : 64) * D * (int)sizeof(T)));
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LM_LDS void*)(dst + (w * INSTR + i) * 1024), 16, voff[i], 0, 0, 0);
+  }
+};
+
+// Waits for this wave's outstanding vector memory operations (loads, LDS DMA, stores).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Operand fragments from a swizzled tile.
+// NATURAL order, k contiguous along the row: row `r`, k-step `ks`.
+template <int CPR>
+__device__ __forceinline__ bf16x8 tl_nat(const char* t, int r, int ks) {
+  const int g = lane_id() >> 4;
+  return *reinterpret_cast<const bf16x8*>(t + tile_off<CPR, 2>(r, ks * 32 + 8 * g));
+}
+template <int CPR>
+__device__ __forceinline__ float tl_nat_f(const char* t, int r, int ks) {
+  const int g = lane_id() >> 4;
+  return *reinterpret_cast<const float*>(t + tile_off<CPR, 4>(r, ks * 4 + g));
+}
+// CHAIN order, k contiguous along the row.
+template <int CPR>
+__device__ __forceinline__ bf16x8 tl_chain(const char* t, int r, int ks) {
+  const int g = lane_id() >> 4;
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(t + tile_off<CPR, 2>(r, ks * 32 + 4 * g));
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(t + tile_off<CPR, 2>(r, ks * 32 + 16 + 4 * g));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+template <int CPR>
+__device__ __forceinline__ float tl_chain_f(const char* t, int r, int ks) {
+  const int g = lane_id() >> 4;
+  return *reinterpret_cast<const float*>(t + tile_off<CPR, 4>(r, 16 * (ks >> 2) + 4 * g + (ks & 3)));
+}
+// k-major: k = tile row, the operand's row/column index = tile column c0 + lane%16.
+// CHAIN order over k (group g holds k = 4g..4g+3 and 16+4g..16+4g+3 of the
+// step), read through the transpose read: each 16-lane group reads 4 rows x 16
+// columns, and the two reads of a half-wave cover 8 consecutive rows.
+template <int CPR>
+__device__ __forceinline__ bf16x4 tl_tr16(const char* t, int k0, int c0) {
+  const int j = lane_id() & 15;
+  const int r = k0 + (j >> 2);
+  const char* p = t + tile_off<CPR, 2>(r, c0 + 4 * (j & 3));
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LM_LDS*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+template <int CPR>
+__device__ __forceinline__ bf16x8 tl_kmaj(const char* t, int ks, int c0) {
+  const int g = lane_id() >> 4;
+  const bf16x4 lo = tl_tr16<CPR>(t, ks * 32 + 4 * g, c0);
+  const bf16x4 hi = tl_tr16<CPR>(t, ks * 32 + 16 + 4 * g, c0);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+template <int CPR>
+__device__ __forceinline__ float tl_kmaj_f(const char* t, int ks, int c0) {
+  const int g = lane_id() >> 4;
+  const int k = 16 * (ks >> 2) + 4 * g + (ks & 3);
+  return *reinterpret_cast<const float*>(t + tile_off<CPR, 4>(k, c0 + (lane_id() & 15)));
+}
+
+// Type-generic front ends.
+template <int CPR, typename T>
+__device__ __forceinline__ typename Mma<T>::frag tl_nat_t(const char* t, int r, int ks) {
+  if constexpr (sizeof(T) == 2) return tl_nat<CPR>(t, r, ks); else return tl_nat_f<CPR>(t, r, ks);
+}
+template <int CPR, typename T>
+__device__ __forceinline__ typename Mma<T>::frag tl_chain_t(const char* t, int r, int ks) {
+  if constexpr (sizeof(T) == 2) return tl_chain<CPR>(t, r, ks); else return tl_chain_f<CPR>(t, r, ks);
+}
+template <int CPR, typename T>
+__device__ __forceinline__ typename Mma<T>::frag tl_kmaj_t(const char* t, int ks, int c0) {
+  if constexpr (sizeof(T) == 2) return tl_kmaj<CPR>(t, ks, c0); else return tl_kmaj_f<CPR>(t, ks, c0);
+}
+
+// k index of element i of this lane's fragment for k-step ks, CHAIN order.
+template <typename T>
+__device__ __forceinline__ int chain_k(int ks, int i) {
+  const int g = lane_id() >> 4;
+  if constexpr (sizeof(T) == 2) return ks * 32 + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
+  else return 16 * (ks >> 2) + 4 * g + (ks & 3);
+}
+
+// ---------------------------------------------------------------------------
 // Wave reductions.
 
 // Across the four 16-lane groups (lanes l, l^16, l^32, l^48).
