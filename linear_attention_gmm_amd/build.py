@@ -29,8 +29,11 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 # work on accumulators.
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I" + os.path.join(ROOT, "include")]
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+# The generic GMA kernel file crashes the compiler's AGPR rewrite pass under
+# the VGPR-form option (fp32 d = 128 instantiations), so it is built without it.
+NO_VGPR_FORM = {"gma.hip"}
 
 
 def sources():
@@ -39,7 +42,8 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    extra = [] if os.path.basename(src) in NO_VGPR_FORM else VGPR_FORM
+    cmd = [HIPCC] + FLAGS + extra + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "not a recognized feature" not in l)
     if r.returncode != 0:

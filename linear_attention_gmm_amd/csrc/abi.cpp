@@ -32,7 +32,11 @@ int ok() {
 
 constexpr int64_t kChunk = 64;
 // Workgroups the segment plan aims for: one per compute unit of an MI355X.
+// Workgroups to aim for when a launch is cut into segments: one per CU for the
+// linear-attention kernels, two per CU for the bf16 GMA kernel (it is sized to
+// share a CU).
 constexpr int64_t kTargetGroups = 256;
+constexpr int64_t kTargetGroupsGma = 512;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -44,9 +48,9 @@ struct Plan {
 
 // Cuts each sequence into P segments of whole chunks. Depends only on the
 // shapes (and the caller's explicit request), so results are reproducible.
-Plan plan_segments(int64_t BH, int64_t N, int64_t segments) {
+Plan plan_segments(int64_t BH, int64_t N, int64_t segments, int64_t target = kTargetGroups) {
   const int64_t nch = (N + kChunk - 1) / kChunk;
-  int64_t P = segments > 0 ? segments : (kTargetGroups + BH - 1) / BH;
+  int64_t P = segments > 0 ? segments : (target + BH - 1) / BH;
   if (P < 1) P = 1;
   if (P > nch) P = nch;
   const int64_t cps = (nch + P - 1) / P;
@@ -65,7 +69,12 @@ size_t esize(int dtype) { return dtype == LM_BF16 ? 2 : 4; }
 
 // ----------------------------------------------------------------------------- GMA
 
-int gma_kp(int64_t K) {
+// Components are padded to KP (padding has logit -inf). The bf16 kernel for
+// d <= 64 works on 64 or 128 components.
+bool gma_fast(int64_t d, int64_t K, int dtype) { return dtype == LM_BF16 && d <= 64 && K <= 128; }
+
+int gma_kp(int64_t K, int64_t d, int dtype) {
+  if (gma_fast(d, K, dtype)) return K <= 64 ? 64 : 128;
   if (K <= 32) return 32;
   if (K <= 64) return 64;
   if (K <= 128) return 128;
@@ -81,8 +90,8 @@ struct GmaLayout {
 GmaLayout gma_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int dtype,
                      int64_t segments) {
   GmaLayout L;
-  L.KP = gma_kp(K);
-  L.plan = plan_segments(B * H, N, segments);
+  L.KP = gma_kp(K, d, dtype);
+  L.plan = plan_segments(B * H, N, segments, gma_fast(d, K, dtype) ? kTargetGroupsGma : kTargetGroups);
   size_t off = 0;
   L.W = off;
   off = align_up(off + (size_t)H * L.KP * 2 * d * esize(dtype));

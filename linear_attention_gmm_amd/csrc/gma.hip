@@ -30,69 +30,98 @@
 //    segment's [Vtil | Z]. The CAUSAL launch then starts every segment from
 //    the sum of the earlier aggregates, and BIDIR starts from the total.
 #include "mfma.hpp"
-#include "launch.hpp"
+#include "gma.hpp"
 
 namespace lm {
 namespace gma {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kChunk = 64;
 constexpr int kLdsBudget = 160 * 1024;
 
-enum Mode { AGG = 0, CAUSAL = 1, BIDIR = 2 };
-
 // ---------------------------------------------------------------------------
-// Parameter prep: per head and component, W = [a | b] * log2e (element type T,
-// KP x 2D) and c * log2e (float). Padded components get W = 0, c = -inf, so
-// their responsibility is exactly 0. The constant -(D/2) log 2pi is left out
-// because it cancels in the posterior.
+// Parameter prep, one wave per (head, component): W = [a | b] * log2e
+// (element type T, KP x 2D) and c * log2e (float), with a = mu / sigma^2,
+// b = -1 / (2 sigma^2), c = log pi - (1/2) sum_d (log sigma^2 + mu^2 / sigma^2)
+// and log pi the log-softmax of the mixing logits. Padded components get
+// W = 0, c = kPadLogit, so their responsibility is exactly 0. The constant
+// -(D/2) log 2pi is left out because it cancels in the posterior.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 template <typename T>
-__global__ void prep_kernel(const float* __restrict__ mu, const float* __restrict__ log_var,
-                            const float* __restrict__ logit_pi, T* __restrict__ W,
-                            float* __restrict__ c, int H, int K, int KP, int D) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= H * KP) return;
-  const int h = idx / KP, k = idx - (idx / KP) * KP;
-  T* w = W + (size_t)idx * 2 * D;
+__global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ mu, const float* __restrict__ log_var,
+                                                   const float* __restrict__ logit_pi, T* __restrict__ W,
+                                                   float* __restrict__ c, int K, int KP, int D) {
+  const int h = blockIdx.x, k = blockIdx.y * 4 + wave_id(), l = lane_id();
+  if (k >= KP) return;
+  T* w = W + ((size_t)h * KP + k) * 2 * D;
   if (k >= K) {
-    for (int j = 0; j < 2 * D; ++j) w[j] = from_f32<T>(0.f);
-    c[idx] = -INFINITY;
+    for (int j = l; j < 2 * D; j += 64) w[j] = from_f32<T>(0.f);
+    if (l == 0) c[(size_t)h * KP + k] = kPadLogit;
     return;
   }
   const float* lp = logit_pi + (size_t)h * K;
   float mx = -INFINITY;
-  for (int j = 0; j < K; ++j) mx = fmaxf(mx, lp[j]);
+  for (int j = l; j < K; j += 64) mx = fmaxf(mx, lp[j]);
+  mx = wave_max(mx);
   float s = 0.f;
-  for (int j = 0; j < K; ++j) s += expf(lp[j] - mx);
-  float acc = lp[k] - (mx + logf(s));
+  for (int j = l; j < K; j += 64) s += expf(lp[j] - mx);
+  s = wave_sum(s);
   const float* m = mu + ((size_t)h * K + k) * D;
   const float* lv = log_var + ((size_t)h * K + k) * D;
-  for (int j = 0; j < D; ++j) {
+  float acc = 0.f;
+  for (int j = l; j < D; j += 64) {
     const float prec = expf(-lv[j]);
     w[j] = from_f32<T>(m[j] * prec * kLog2e);
     w[D + j] = from_f32<T>(-0.5f * prec * kLog2e);
-    acc -= 0.5f * (lv[j] + m[j] * m[j] * prec);
+    acc += lv[j] + m[j] * m[j] * prec;
   }
-  c[idx] = acc * kLog2e;
+  acc = wave_sum(acc);
+  if (l == 0) c[(size_t)h * KP + k] = (lp[k] - (mx + logf(s)) - 0.5f * acc) * kLog2e;
 }
 
 // ---------------------------------------------------------------------------
-struct Args {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* out;
-  const void* W;   // [H][KP][2D]
-  const float* c;  // [H][KP]
-  float* agg;      // [B*H][P][KP][DV]
-  float* aggz;     // [B*H][P][KP]
-  int64_t N;
-  int H;
-  int P;          // segments in the workspace layout
-  int seg_len;    // tokens per segment (multiple of 64)
-  int KP;
-  float eps;
-};
+// Segment scan over the per-segment states [Vtil | Z] of every sequence, in a
+// fixed order. Causal: slot p becomes the sum of the segments before p (slots
+// 0 .. P-2 hold the segment states; slot 0 becomes zero). Bidirectional: slot 0
+// becomes the sum of all P segments.
+__global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ agg, float* __restrict__ aggz, int P,
+                                                   int KP, int DV, int causal) {
+  const int bh = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int ns = KP * DV;
+  if (e >= ns + KP) return;
+  float* x;
+  size_t stride;
+  if (e < ns) {
+    x = agg + (size_t)bh * P * ns + e;
+    stride = ns;
+  } else {
+    x = aggz + (size_t)bh * P * KP + (e - ns);
+    stride = KP;
+  }
+  float run = 0.f;
+  if (causal) {
+    for (int p = 0; p < P; ++p) {
+      const float t = p < P - 1 ? x[p * stride] : 0.f;
+      x[p * stride] = run;
+      run += t;
+    }
+  } else {
+    for (int p = 0; p < P; ++p) run += x[p * stride];
+    x[0] = run;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic kernel (float32 inputs, and bf16 shapes outside the bf16 kernel).
 
 template <typename T, int D, int DV, int NW, int KPW, int MODE>
 struct Cfg {
@@ -342,18 +371,18 @@ __global__ __launch_bounds__(NW * 64) void gma_kernel(Args a) {
     for (int r = 0; r < 4; ++r) Z[rt][r] = 0.f;
 
   if constexpr (MODE != AGG) {
-    const int pend = MODE == CAUSAL ? p : a.P;
-    for (int pp = 0; pp < pend; ++pp) {
-      const float* ag = a.agg + ((size_t)bh * a.P + pp) * a.KP * DV;
-      const float* az = a.aggz + ((size_t)bh * a.P + pp) * a.KP;
+    if (a.has_init) {
+      const int slot = MODE == CAUSAL ? p : 0;
+      const float* ag = a.agg + ((size_t)bh * a.P + slot) * a.KP * DV;
+      const float* az = a.aggz + ((size_t)bh * a.P + slot) * a.KP;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int comp = comp0 + 16 * rt + 4 * g + r;
 #pragma unroll
-          for (int dt = 0; dt < C::DT; ++dt) S[dt][rt][r] += ag[(size_t)comp * DV + 16 * dt + c16];
-          Z[rt][r] += az[comp];
+          for (int dt = 0; dt < C::DT; ++dt) S[dt][rt][r] = ag[(size_t)comp * DV + 16 * dt + c16];
+          Z[rt][r] = az[comp];
         }
     }
   }
@@ -632,8 +661,59 @@ __global__ __launch_bounds__(NW * 64) void gma_kernel(Args a) {
 // Host-side launch.
 
 template <typename T, int D, int NW, int KPW>
-static hipError_t launch_all(const GmaLaunch& L, hipStream_t st) {
+static hipError_t launch_mode(const Args& a, int mode, int segments, unsigned BH, hipStream_t st) {
   constexpr int DV = D;
+  const dim3 grid((unsigned)segments, BH), block(NW * 64);
+  switch (mode) {
+    case AGG: hipLaunchKernelGGL((gma_kernel<T, D, DV, NW, KPW, AGG>), grid, block, 0, st, a); break;
+    case CAUSAL: hipLaunchKernelGGL((gma_kernel<T, D, DV, NW, KPW, CAUSAL>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((gma_kernel<T, D, DV, NW, KPW, BIDIR>), grid, block, 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t generic_d(const GmaLaunch& L, const Args& a, int mode, int segments, hipStream_t st) {
+  const unsigned BH = (unsigned)(L.B * L.H);
+  switch (L.KP) {
+    case 32: return launch_mode<T, D, 1, 32>(a, mode, segments, BH, st);
+    case 64: return launch_mode<T, D, 2, 32>(a, mode, segments, BH, st);
+    case 128: return launch_mode<T, D, 4, 32>(a, mode, segments, BH, st);
+    case 256:
+      // fp32 tiles at d = 128 with 256 components do not fit the LDS; the
+      // ABI layer rejects that shape before it gets here.
+      if constexpr (sizeof(T) == 2 || D < 128) return launch_mode<T, D, 4, 64>(a, mode, segments, BH, st);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+static hipError_t generic(const GmaLaunch& L, const Args& a, int mode, int segments, hipStream_t st) {
+  switch (L.D) {
+    case 32: return generic_d<T, 32>(L, a, mode, segments, st);
+    case 64: return generic_d<T, 64>(L, a, mode, segments, st);
+    case 128: return generic_d<T, 128>(L, a, mode, segments, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t run(const GmaLaunch& L, const Args& a, int mode, int segments, hipStream_t st) {
+  if (fast_supported(L)) return fast_launch(L, a, mode, segments, st);
+  return L.bf16 ? generic<bf16>(L, a, mode, segments, st) : generic<float>(L, a, mode, segments, st);
+}
+
+static hipError_t scan(const GmaLaunch& L, int causal, hipStream_t st) {
+  const int E = (int)(L.KP * L.D + L.KP);
+  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((E + 255) / 256), (unsigned)(L.B * L.H)), dim3(256), 0, st,
+                     L.agg, L.aggz, (int)L.P, (int)L.KP, (int)L.D, causal);
+  return hipGetLastError();
+}
+
+}  // namespace gma
+
+hipError_t gma_launch(const GmaLaunch& L, hipStream_t st) {
+  using namespace gma;
   Args a;
   a.q = L.q;
   a.k = L.k;
@@ -649,57 +729,29 @@ static hipError_t launch_all(const GmaLaunch& L, hipStream_t st) {
   a.seg_len = (int)L.seg_len;
   a.KP = (int)L.KP;
   a.eps = L.eps;
-  const int threads = 256;
-  const int nprep = (int)(L.H * L.KP);
-  hipLaunchKernelGGL((prep_kernel<T>), dim3((nprep + threads - 1) / threads), dim3(threads), 0, st,
-                     L.mu, L.log_var, L.logit_pi, (T*)L.W, L.c, (int)L.H, (int)L.K, (int)L.KP, D);
-  const unsigned BH = (unsigned)(L.B * L.H);
+  a.has_init = 0;
+  const dim3 pgrid((unsigned)L.H, (unsigned)((L.KP + 3) / 4));
+  if (L.bf16)
+    hipLaunchKernelGGL((prep_kernel<bf16>), pgrid, dim3(256), 0, st, L.mu, L.log_var, L.logit_pi, (bf16*)L.W, L.c,
+                       (int)L.K, (int)L.KP, (int)L.D);
+  else
+    hipLaunchKernelGGL((prep_kernel<float>), pgrid, dim3(256), 0, st, L.mu, L.log_var, L.logit_pi, (float*)L.W,
+                       L.c, (int)L.K, (int)L.KP, (int)L.D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int P = (int)L.P;
   if (L.causal) {
-    if (L.P > 1)
-      hipLaunchKernelGGL((gma_kernel<T, D, DV, NW, KPW, AGG>), dim3((unsigned)(L.P - 1), BH), dim3(NW * 64), 0,
-                         st, a);
-    hipLaunchKernelGGL((gma_kernel<T, D, DV, NW, KPW, CAUSAL>), dim3((unsigned)L.P, BH), dim3(NW * 64), 0, st,
-                       a);
-  } else {
-    hipLaunchKernelGGL((gma_kernel<T, D, DV, NW, KPW, AGG>), dim3((unsigned)L.P, BH), dim3(NW * 64), 0, st, a);
-    hipLaunchKernelGGL((gma_kernel<T, D, DV, NW, KPW, BIDIR>), dim3((unsigned)L.P, BH), dim3(NW * 64), 0, st,
-                       a);
-  }
-  return hipGetLastError();
-}
-
-template <typename T, int D>
-static hipError_t launch_d(const GmaLaunch& L, hipStream_t st) {
-  switch (L.KP) {
-    case 32: return launch_all<T, D, 1, 32>(L, st);
-    case 64: return launch_all<T, D, 2, 32>(L, st);
-    case 128: return launch_all<T, D, 4, 32>(L, st);
-    case 256:
-      // fp32 tiles at d = 128 with 256 components do not fit the LDS; the
-      // ABI layer rejects that shape before it gets here.
-      if constexpr (sizeof(T) == 2 || D < 128) return launch_all<T, D, 4, 64>(L, st);
-      return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
-  }
-}
-
-}  // namespace gma
-
-hipError_t gma_launch(const GmaLaunch& L, hipStream_t st) {
-  if (L.bf16) {
-    switch (L.D) {
-      case 32: return gma::launch_d<bf16, 32>(L, st);
-      case 64: return gma::launch_d<bf16, 64>(L, st);
-      case 128: return gma::launch_d<bf16, 128>(L, st);
+    if (P > 1) {
+      if ((e = run(L, a, AGG, P - 1, st)) != hipSuccess) return e;
+      if ((e = scan(L, 1, st)) != hipSuccess) return e;
+      a.has_init = 1;
     }
-  } else {
-    switch (L.D) {
-      case 32: return gma::launch_d<float, 32>(L, st);
-      case 64: return gma::launch_d<float, 64>(L, st);
-      case 128: return gma::launch_d<float, 128>(L, st);
-    }
+    return run(L, a, CAUSAL, P, st);
   }
-  return hipErrorInvalidValue;
+  if ((e = run(L, a, AGG, P, st)) != hipSuccess) return e;
+  if ((e = scan(L, 0, st)) != hipSuccess) return e;
+  a.has_init = 1;
+  return run(L, a, BIDIR, P, st);
 }
 
 }  // namespace lm

@@ -60,6 +60,7 @@ struct Args {
   int P;
   int seg_len;
   int sfl;
+  int has_init;  // chunk pass: start from the state block of the segment
 };
 
 template <int D>
@@ -164,159 +165,118 @@ __device__ __forceinline__ float frag_sum(const typename Mma<T>::frag& f) {
 }
 
 template <typename C, bool AGG>
-__device__ __forceinline__ char* buf_k(char* base, int b) { return base + b * C::BUF + (AGG ? 0 : C::TB); }
+__device__ __forceinline__ const char* tile_k(const char* buf) { return buf + (AGG ? 0 : C::TB); }
 template <typename C, bool AGG>
-__device__ __forceinline__ char* buf_v(char* base, int b) { return base + b * C::BUF + (AGG ? 1 : 2) * C::TB; }
+__device__ __forceinline__ const char* tile_v(const char* buf) { return buf + (AGG ? 1 : 2) * C::TB; }
 template <typename C>
-__device__ __forceinline__ float* buf_g(char* base, int b) {
-  return reinterpret_cast<float*>(base + b * C::BUF + C::NTILE * C::TB);
+__device__ __forceinline__ const float* tile_g(const char* buf) {
+  return reinterpret_cast<const float*>(buf + C::NTILE * C::TB);
 }
 
-// Issues the DMA of one chunk (Q unless AGG, K, V, and the decays) into buffer b.
-template <typename T, int D, typename C, bool AGG>
-__device__ __forceinline__ void issue_chunk(const TileDma<T, D, C::NW>& dma, char* base, int b, const T* Qg,
-                                            const T* Kg, const T* Vg, const float* Gg, int64_t c0, int64_t N) {
-  const int nv = (int)((N - c0) < kC ? (N - c0) : kC);
-  if constexpr (!AGG) dma.issue(base + b * C::BUF, Qg + (size_t)c0 * D, nv);
-  dma.issue(buf_k<C, AGG>(base, b), Kg + (size_t)c0 * D, nv);
-  dma.issue(buf_v<C, AGG>(base, b), Vg + (size_t)c0 * D, nv);
-  if (wave_id() == 0) {
-    const rsrc_t rg = make_rsrc(Gg + c0, (uint32_t)(nv * 4));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (LM_LDS void*)(buf_g<C>(base, b)), 4, lane_id() * 4, 0, 0, 0);
-  }
-}
-
+// Per-workgroup constants of the chunk loop.
 template <typename T, int D, bool CCQ, bool AGG>
-__global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
+struct Ctx {
+  typedef Cfg<T, D, CCQ, AGG> C;
+  const T* Qg;
+  const T* Kg;
+  const T* Vg;
+  const float* Gg;
+  T* Og;
+  int64_t N, t_end;
+  float gate_b;
+  int cbase;
+  TileDma<T, D, C::NW> dma;
+
+  // Issues the DMA of the chunk at c0 (Q unless AGG, K, V, and the decays) into `buf`.
+  __device__ __forceinline__ void issue(char* buf, int64_t c0) const {
+    const int nv = (int)((N - c0) < kC ? (N - c0) : kC);
+    if constexpr (!AGG) dma.issue(buf, Qg + (size_t)c0 * D, nv);
+    dma.issue(buf + (AGG ? 0 : C::TB), Kg + (size_t)c0 * D, nv);
+    dma.issue(buf + (AGG ? 1 : 2) * C::TB, Vg + (size_t)c0 * D, nv);
+    if (wave_id() == 0) {
+      const rsrc_t rg = make_rsrc(Gg + c0, (uint32_t)(nv * 4));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (LM_LDS void*)(buf + C::NTILE * C::TB), 4, lane_id() * 4, 0, 0,
+                                               0);
+    }
+  }
+};
+
+// Registers carried from chunk to chunk.
+template <typename T, int D, bool CCQ, bool AGG>
+struct State {
+  typedef Cfg<T, D, CCQ, AGG> C;
+  // S[kt][ct]: rows = key features 16 kt + 4 g + r, cols = value dims cbase + 16 ct + c16.
+  // M[kt][ct]: rows = features 16 kt + 4 g + r, cols = features cbase + 16 ct + c16.
+  f32x4 S[C::DT][C::CT];
+  f32x4 Mst[CCQ ? C::DT : 1][CCQ ? C::CT : 1];
+  float mreg[C::CT];  // running key sum of column cbase + 16 ct + c16
+  float lseg;         // AGG: log2 of the segment's decay product
+  int64_t t_prev;     // chunk whose outputs wait in the staging tile
+};
+
+// One chunk. `cur` holds this chunk's tiles (DMA issued a chunk earlier when
+// double-buffered); `nxt` receives the next chunk's tiles. Instantiated once per
+// buffer parity so that every LDS access names its array statically (the
+// compiler then knows which accesses can overlap an outstanding DMA).
+template <typename T, int D, bool CCQ, bool AGG>
+__device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T, D, CCQ, AGG>& st, char* cur,
+                                           char* nxt, char* work, int64_t t0) {
   typedef Cfg<T, D, CCQ, AGG> C;
   typedef Mma<T> M;
   typedef typename M::frag frag;
   constexpr int NW = C::NW, NT = NW * 64, CT = C::CT, DT = C::DT, CPR = C::CPR;
-
-  __shared__ __attribute__((aligned(16))) char smem[C::lds];
-  T* sD = reinterpret_cast<T*>(smem + C::o_d);
-  T* sP = reinterpret_cast<T*>(smem + C::o_p);
-  T* sDot = reinterpret_cast<T*>(smem + C::o_dot);
-  float* sL = reinterpret_cast<float*>(smem + C::o_small);
-  float2* sAB = reinterpret_cast<float2*>(smem + C::o_small + NW * kC * 4);
-  float* sMv = reinterpret_cast<float*>(smem + C::o_small + NW * kC * 4 + kC * 8);
-  T* sO = reinterpret_cast<T*>(smem + C::o_o);
-
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
-  const int bh = blockIdx.y, p = blockIdx.x;
-  const int h = bh % a.H;
-  const int64_t N = a.N;
-  const int64_t t_begin = (int64_t)p * a.seg_len;
-  const int64_t t_end = N < t_begin + a.seg_len ? N : t_begin + a.seg_len;
-  const T* __restrict__ Qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * N * D;
-  const T* __restrict__ Kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * N * D;
-  const T* __restrict__ Vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * N * D;
-  const float* __restrict__ Gg = a.g + (size_t)bh * N;
-  T* __restrict__ Og = reinterpret_cast<T*>(a.out) + (size_t)bh * N * D;
-  const int cbase = w * C::CW;
-  float* sLw = sL + w * kC;
+  const int64_t N = x.N;
+  const int nvalid = (int)((N - t0) < kC ? (N - t0) : kC);
+  const int cbase = x.cbase;
+  const float gate_b = x.gate_b;
+  T* sD = reinterpret_cast<T*>(work + C::o_d);
+  T* sP = reinterpret_cast<T*>(work + C::o_p);
+  T* sDot = reinterpret_cast<T*>(work + C::o_dot);
+  float* sLw = reinterpret_cast<float*>(work + C::o_small) + w * kC;
+  float2* sAB = reinterpret_cast<float2*>(work + C::o_small + NW * kC * 4);
+  float* sMv = reinterpret_cast<float*>(work + C::o_small + NW * kC * 4 + kC * 8);
+  T* sO = reinterpret_cast<T*>(work + C::o_o);
+  T* __restrict__ Og = x.Og;
+  f32x4 (&S)[DT][CT] = st.S;
+  auto& Mst = st.Mst;
+  float (&mreg)[CT] = st.mreg;
+  float& lseg = st.lseg;
+  int64_t& t_prev = st.t_prev;
+  (void)gate_b;
+  (void)sAB;
+  (void)sO;
+  (void)Og;
+  (void)t_prev;
 
-  char* const bufbase = smem + C::o_buf;
-  TileDma<T, D, NW> dma;
-  dma.init();
-
-  // S[kt][ct]: rows = key features 16 kt + 4 g + r, cols = value dims cbase + 16 ct + c16.
-  // M[kt][ct]: rows = features 16 kt + 4 g + r, cols = features cbase + 16 ct + c16.
-  f32x4 S[DT][CT];
-  f32x4 Mst[CCQ ? DT : 1][CCQ ? CT : 1];
-  float mreg[CT];  // running key sum of column cbase + 16 ct + c16
-#pragma unroll
-  for (int kt = 0; kt < DT; ++kt)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      S[kt][ct] = zero4();
-      if constexpr (CCQ) Mst[kt][ct] = zero4();
-    }
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) mreg[ct] = 0.f;
-  float lseg = 0.f;  // AGG: log2 of the segment's decay product
-
+  if constexpr (C::NBUF == 1) {
+    lds_barrier();  // the previous chunk is done with the single buffer
+    x.issue(cur, t0);
+  }
+  wait_vmem();
+  lds_barrier();  // this chunk's tiles landed; the previous chunk is finished everywhere
+  if constexpr (C::STAGE_O) {
+    if (t_prev >= 0) store_rows<T, D, NT>(Og + (size_t)t_prev * D, sO, C::PD, kC);
+  }
   if constexpr (C::NBUF == 2) {
-    if (t_begin < t_end) issue_chunk<T, D, C, AGG>(dma, bufbase, 0, Qg, Kg, Vg, Gg, t_begin, N);
+    if (t0 + kC < x.t_end) x.issue(nxt, t0 + kC);
   }
-
-  if constexpr (!AGG) {
-    for (int pp = 0; pp < p; ++pp) {
-      const float* blk = a.agg + ((size_t)bh * a.P + pp) * a.sfl;
-      const float G = blk[D * D];
-#pragma unroll
-      for (int kt = 0; kt < DT; ++kt)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 16 * kt + 4 * g + r, col = cbase + 16 * ct + c16;
-            S[kt][ct][r] = G * S[kt][ct][r] + blk[row * D + col];
-            if constexpr (CCQ) Mst[kt][ct][r] += blk[D * D + 1 + row * D + col];
-          }
-      if constexpr (CCQ) {
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) mreg[ct] += blk[2 * D * D + 1 + cbase + 16 * ct + c16];
-      }
-    }
-  }
-  if constexpr (CCQ && !AGG) {
-    // rows 0/1: gate weights (hi/lo); rows 2/3: running key sum (hi/lo); others 0
-    for (int i = threadIdx.x; i < 16 * C::PD; i += NT) {
-      const int row = i / C::PD, col = i - (i / C::PD) * C::PD;
-      float x = 0.f;
-      if (col < D && row < 2) {
-        const float wv = a.wl[(size_t)h * D + col];
-        const T hi = from_f32<T>(wv);
-        x = row == 0 ? to_f32(hi) : wv - to_f32(hi);
-      }
-      if (row < 2 || row >= 4 || col >= D) sDot[i] = from_f32<T>(x);
-    }
-    if (g == 0) {
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int col = cbase + 16 * ct + c16;
-        const T hi = from_f32<T>(mreg[ct]);
-        sMv[col] = mreg[ct];
-        sDot[2 * C::PD + col] = hi;
-        sDot[3 * C::PD + col] = from_f32<T>(mreg[ct] - to_f32(hi));
-      }
-    }
-  }
-  const float gate_b = CCQ ? a.bl[h] : 0.f;
-
-  int it = 0;
-  int64_t t_prev = -1;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kC, ++it) {
-    const int nvalid = (int)((N - t0) < kC ? (N - t0) : kC);
-    const int b = C::NBUF == 2 ? (it & 1) : 0;
-    if constexpr (C::NBUF == 1) {
-      __syncthreads();  // previous chunk done with the single buffer
-      issue_chunk<T, D, C, AGG>(dma, bufbase, 0, Qg, Kg, Vg, Gg, t0, N);
-    }
-    wait_vmem();
-    __syncthreads();  // this chunk's tiles landed; the previous chunk is finished everywhere
-    if constexpr (C::STAGE_O) {
-      if (t_prev >= 0) store_rows<T, D, NT>(Og + (size_t)t_prev * D, sO, C::PD, kC);
-    }
-    if constexpr (C::NBUF == 2) {
-      if (t0 + kC < t_end) issue_chunk<T, D, C, AGG>(dma, bufbase, b ^ 1, Qg, Kg, Vg, Gg, t0 + kC, N);
-    }
-    const char* Kt = buf_k<C, AGG>(bufbase, b);
-    const char* Vt = buf_v<C, AGG>(bufbase, b);
+    const char* Kt = tile_k<C, AGG>(cur);
+    const char* Vt = tile_v<C, AGG>(cur);
 
     // cumulative log2 decay of this chunk (each wave keeps a private copy)
+    float l_last;
     {
-      float x = l < nvalid ? fmaxf(log2f(buf_g<C>(bufbase, b)[l]), -200.f) : 0.f;
+      float x = l < nvalid ? fmaxf(log2f(tile_g<C>(cur)[l]), -200.f) : 0.f;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const float y = __shfl_up(x, o);
         if (l >= o) x += y;
       }
       sLw[l] = x;
+      l_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), kC - 1));
     }
     __builtin_amdgcn_wave_barrier();
-    const float l_last = sLw[kC - 1];
 
     frag KTc[CCQ ? CT : 1][CCQ ? C::NKT : 1];  // K^T of this wave's columns (CCQ)
     if constexpr (CCQ) {
@@ -327,7 +287,7 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
     }
 
     if constexpr (!AGG) {
-      const char* Qt = bufbase + b * C::BUF;
+      const char* Qt = cur;
       // ---- phase 1: per owned query tile: raw scores, gate/mean terms, Bmat or decayed scores
       f32x4 Pr[C::QPW][4];
 #pragma unroll
@@ -391,7 +351,7 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
 
 
       if constexpr (CCQ) {
@@ -431,7 +391,7 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
             for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(-ab[qt].x * mqv[r] + kb[r] + ab[qt].y * mprev[r]);
           }
         }
-        __syncthreads();  // delta complete; Bmat consumed
+        lds_barrier();  // delta complete; Bmat consumed
 
         // ---- phase 4: scores with the cleaned query, decay, for owned query tiles
 #pragma unroll
@@ -459,7 +419,7 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
             }
           }
         }
-        __syncthreads();  // decayed scores complete
+        lds_barrier();  // decayed scores complete
       }
 
       // ---- phase 5: outputs of this wave's value columns (query tile outer, so Q and
@@ -566,13 +526,119 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
       }
       lseg += l_last;
     }
+}
+
+template <typename T, int D, bool CCQ, bool AGG>
+__global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
+  typedef Cfg<T, D, CCQ, AGG> C;
+  constexpr int NW = C::NW, NT = NW * 64, CT = C::CT, DT = C::DT;
+
+  // Separate arrays: the two DMA buffers and the register-written tiles.
+  __shared__ __attribute__((aligned(16))) char sBuf0[C::BUF];
+  __shared__ __attribute__((aligned(16))) char sBuf1[C::NBUF == 2 ? C::BUF : 16];
+  __shared__ __attribute__((aligned(16))) char sWork[C::o_buf];
+
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const int bh = blockIdx.y, p = blockIdx.x;
+  const int h = bh % a.H;
+  const int64_t N = a.N;
+  const int64_t t_begin = (int64_t)p * a.seg_len;
+  const int64_t t_end = N < t_begin + a.seg_len ? N : t_begin + a.seg_len;
+
+  Ctx<T, D, CCQ, AGG> x;
+  x.Qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * N * D;
+  x.Kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * N * D;
+  x.Vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * N * D;
+  x.Gg = a.g + (size_t)bh * N;
+  x.Og = reinterpret_cast<T*>(a.out) + (size_t)bh * N * D;
+  x.N = N;
+  x.t_end = t_end;
+  x.gate_b = CCQ ? a.bl[h] : 0.f;
+  x.cbase = w * C::CW;
+  x.dma.init();
+  const int cbase = x.cbase;
+  T* sDot = reinterpret_cast<T*>(sWork + C::o_dot);
+  float* sMv = reinterpret_cast<float*>(sWork + C::o_small + NW * kC * 4 + kC * 8);
+  T* sO = reinterpret_cast<T*>(sWork + C::o_o);
+  (void)sDot;
+  (void)sMv;
+  (void)sO;
+
+  State<T, D, CCQ, AGG> st;
+#pragma unroll
+  for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      st.S[kt][ct] = zero4();
+      if constexpr (CCQ) st.Mst[kt][ct] = zero4();
+    }
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) st.mreg[ct] = 0.f;
+  st.lseg = 0.f;
+  st.t_prev = -1;
+
+  if constexpr (C::NBUF == 2) {
+    if (t_begin < t_end) x.issue(sBuf0, t_begin);
+  }
+
+  if constexpr (!AGG) {
+    // state at the segment start (exclusive prefix written by the segment scan)
+    if (a.has_init) {
+      const float* blk = a.agg + ((size_t)bh * a.P + p) * a.sfl;
+#pragma unroll
+      for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * kt + 4 * g + r, col = cbase + 16 * ct + c16;
+            st.S[kt][ct][r] = blk[row * D + col];
+            if constexpr (CCQ) st.Mst[kt][ct][r] = blk[D * D + 1 + row * D + col];
+          }
+      if constexpr (CCQ) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) st.mreg[ct] = blk[2 * D * D + 1 + cbase + 16 * ct + c16];
+      }
+    }
+  }
+  if constexpr (CCQ && !AGG) {
+    // rows 0/1: gate weights (hi/lo); rows 2/3: running key sum (hi/lo); others 0
+    for (int i = threadIdx.x; i < 16 * C::PD; i += NT) {
+      const int row = i / C::PD, col = i - (i / C::PD) * C::PD;
+      float v = 0.f;
+      if (col < D && row < 2) {
+        const float wv = a.wl[(size_t)h * D + col];
+        const T hi = from_f32<T>(wv);
+        v = row == 0 ? to_f32(hi) : wv - to_f32(hi);
+      }
+      if (row < 2 || row >= 4 || col >= D) sDot[i] = from_f32<T>(v);
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int col = cbase + 16 * ct + c16;
+        const T hi = from_f32<T>(st.mreg[ct]);
+        sMv[col] = st.mreg[ct];
+        sDot[2 * C::PD + col] = hi;
+        sDot[3 * C::PD + col] = from_f32<T>(st.mreg[ct] - to_f32(hi));
+      }
+    }
+  }
+
+  if constexpr (C::NBUF == 2) {
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * kC) {
+      chunk_step<T, D, CCQ, AGG>(x, st, sBuf0, sBuf1, sWork, t0);
+      if (t0 + kC < t_end) chunk_step<T, D, CCQ, AGG>(x, st, sBuf1, sBuf0, sWork, t0 + kC);
+    }
+  } else {
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kC) chunk_step<T, D, CCQ, AGG>(x, st, sBuf0, sBuf0, sWork, t0);
   }
 
   if constexpr (C::STAGE_O) {
-    __syncthreads();
-    if (t_prev >= 0) {
-      const int nv = (int)((N - t_prev) < kC ? (N - t_prev) : kC);
-      store_rows<T, D, NT>(Og + (size_t)t_prev * D, sO, C::PD, nv);
+    lds_barrier();
+    if (st.t_prev >= 0) {
+      const int nv = (int)((N - st.t_prev) < kC ? (N - st.t_prev) : kC);
+      store_rows<T, D, NT>(x.Og + (size_t)st.t_prev * D, sO, C::PD, nv);
     }
   }
 
@@ -585,16 +651,38 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * kt + 4 * g + r, col = cbase + 16 * ct + c16;
-          blk[row * D + col] = S[kt][ct][r];
-          if constexpr (CCQ) blk[D * D + 1 + row * D + col] = Mst[kt][ct][r];
+          blk[row * D + col] = st.S[kt][ct][r];
+          if constexpr (CCQ) blk[D * D + 1 + row * D + col] = st.Mst[kt][ct][r];
         }
-    if (w == 0 && l == 0) blk[D * D] = exp2f(lseg);
+    if (w == 0 && l == 0) blk[D * D] = exp2f(st.lseg);
     if constexpr (CCQ) {
       if (g == 0) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) blk[2 * D * D + 1 + cbase + 16 * ct + c16] = mreg[ct];
+        for (int ct = 0; ct < CT; ++ct) blk[2 * D * D + 1 + cbase + 16 * ct + c16] = st.mreg[ct];
       }
     }
+  }
+}
+
+// Segment scan over the per-segment state blocks of every sequence, in a fixed
+// order: block p becomes the state at the start of segment p,
+//   S_in(p) = G_{p-1} S_in(p-1) + S_{p-1},   M_in(p) = M_in(p-1) + M_{p-1},
+//   m_in(p) = m_in(p-1) + m_{p-1},           S_in(0) = M_in(0) = m_in(0) = 0,
+// with G_p the decay product of segment p (left in place). Blocks 0 .. P-2 hold
+// the segment states on entry.
+__global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ agg, int P, int sfl, int D, int ccq) {
+  const int bh = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int nS = D * D;
+  const int nTot = ccq ? 2 * D * D + 1 + D : D * D + 1;
+  if (e >= nTot || e == nS) return;
+  float* base = agg + (size_t)bh * P * sfl;
+  float run = 0.f;
+  for (int pp = 0; pp < P; ++pp) {
+    float* xp = base + (size_t)pp * sfl + e;
+    const float t = pp < P - 1 ? *xp : 0.f;
+    *xp = run;
+    if (pp < P - 1) run = e < nS ? base[(size_t)pp * sfl + nS] * run + t : run + t;
   }
 }
 
@@ -621,10 +709,16 @@ static hipError_t launch_d(const LinLaunch& L, hipStream_t st) {
   a.P = (int)L.P;
   a.seg_len = (int)L.seg_len;
   a.sfl = (int)lin_state_floats(D, CCQ);
+  a.has_init = 0;
   const unsigned BH = (unsigned)(L.B * L.H);
   if (L.P > 1) {
     hipError_t e = launch_one<T, D, CCQ, true>(a, (unsigned)(L.P - 1), BH, st);
     if (e != hipSuccess) return e;
+    const int n = CCQ ? 2 * D * D + 1 + D : D * D + 1;
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((n + 255) / 256), BH), dim3(256), 0, st, L.agg, (int)L.P, a.sfl,
+                       D, CCQ ? 1 : 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    a.has_init = 1;
   }
   return launch_one<T, D, CCQ, false>(a, (unsigned)L.P, BH, st);
 }

@@ -212,6 +212,21 @@ struct TileDma {
 
 // Waits for this wave's outstanding vector memory operations (loads, LDS DMA, stores).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Waits until at most n (< 16) of this wave's vector memory operations are
+// outstanding (they complete in order for loads).
+#define LM_WAIT_VMEM(n) __builtin_amdgcn_s_waitcnt(0x0f70 | (n))
+
+// Workgroup barrier for LDS traffic only: this wave's LDS reads and writes are
+// complete, then all waves meet. Unlike __syncthreads() it does not wait for
+// outstanding global loads, stores or LDS DMA (those are waited for
+// explicitly where their data is needed). The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Operand fragments from a swizzled tile.
 // NATURAL order, k contiguous along the row: row `r`, k-step `ks`.
