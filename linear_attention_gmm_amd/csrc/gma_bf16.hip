@@ -155,11 +155,10 @@ __device__ __forceinline__ void dma_init(int (&voff)[INSTR]) {
 }
 template <int D, int INSTR>
 __device__ __forceinline__ void dma_issue(char* dst, const bf16* src, int rows, const int* voff) {
-  const rsrc_t rs = make_rsrc(src, (uint32_t)(rows * D * 2));
-  const int w = wave_id();
+  const u32x4 d = buf_desc(src, (uint32_t)(rows * D * 2));
+  const unsigned base = lds_addr(dst) + (unsigned)(wave_id() * INSTR * 1024);
 #pragma unroll
-  for (int i = 0; i < INSTR; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LM_LDS void*)(dst + (w * INSTR + i) * 1024), 16, voff[i], 0, 0, 0);
+  for (int i = 0; i < INSTR; ++i) lds_dma16(d, voff[i], base + (unsigned)(i * 1024));
 }
 
 // x*x of the 16 rows this wave's DMA wrote (same physical positions).

@@ -63,12 +63,15 @@ struct Args {
   int has_init;  // chunk pass: start from the state block of the segment
 };
 
+// Waves per workgroup: 16 state columns per wave (8 waves, two per SIMD, at
+// D = 128 so that the MFMA work of one wave overlaps the VALU work of the
+// other). Query tiles are owned by waves 0..3 (waves >= 4 own none).
 template <int D>
 struct Waves {
-  static constexpr int NW = D / 16 < 4 ? D / 16 : 4;
+  static constexpr int NW = D / 16;
   static constexpr int CW = D / NW;  // value (and M) columns per wave
   static constexpr int CT = CW / 16;
-  static constexpr int QPW = 4 / NW;  // query tiles per wave
+  static constexpr int QPW = NW >= 4 ? 1 : 4 / NW;  // query tiles per wave
 };
 
 template <typename T, int D, bool CCQ, bool AGG>
@@ -82,17 +85,22 @@ struct Cfg {
   static constexpr int ES = (int)sizeof(T);
   static constexpr int CPR = D * ES / 16;
   static constexpr int TB = kC * D * ES;  // one swizzled tile
-  static constexpr int PADE = 16 / ES;    // padding of register-written tiles
-  static constexpr int PD = D + PADE;     // delta / output tile pitch (elements)
-  static constexpr int PP = kC + PADE;    // score tile pitch (elements)
+  // Pitches (elements) of the register-written tiles. For bf16 the score and
+  // delta rows are 8 bytes past a multiple of 128 bytes: the 8-byte accumulator
+  // writes and the 8-byte operand reads of 16 consecutive rows then hit distinct
+  // LDS banks (measured). The output staging tile keeps 16-byte aligned rows
+  // for its 16-byte row reads.
+  static constexpr int PP = ES == 2 ? kC + 4 : kC + 4;   // scores / Bmat
+  static constexpr int PDD = ES == 2 ? D + 4 : D + 4;    // delta and the gate/mean rows
+  static constexpr int PD = ES == 2 ? D + 8 : D + 4;     // output staging
   static constexpr int NTILE = AGG ? 2 : 3;                 // (Q), K, V
   static constexpr int BUF = NTILE * TB + 256;              // + g
-  static constexpr int o_d = 0;                             // delta [64][PD]
-  static constexpr int d_bytes = (CCQ && !AGG) ? kC * PD * ES : 0;
+  static constexpr int o_d = 0;                             // delta [64][PDD]
+  static constexpr int d_bytes = (CCQ && !AGG) ? kC * PDD * ES : 0;
   static constexpr int o_p = o_d + d_bytes;                 // scores / Bmat [64 q][PP]
   static constexpr int p_bytes = AGG ? 0 : kC * PP * ES;
-  static constexpr int o_dot = o_p + p_bytes;               // [16][PD] gate and mean rows
-  static constexpr int dot_bytes = (CCQ && !AGG) ? 16 * PD * ES : 0;
+  static constexpr int o_dot = o_p + p_bytes;               // [16][PDD] gate and mean rows
+  static constexpr int dot_bytes = (CCQ && !AGG) ? 16 * PDD * ES : 0;
   static constexpr int o_small = o_dot + dot_bytes;         // sL [NW][64], sAB [64] float2, sMv [D]
   static constexpr int small_bytes = NW * kC * 4 + kC * 8 + D * 4;
   static constexpr int o_o = o_small + small_bytes;         // output staging [64][PD]
@@ -115,54 +123,48 @@ __device__ __forceinline__ void store_rows(T* __restrict__ dst, const T* s, int 
   }
 }
 
-// hi/lo split of fp32 D tiles into two CHAIN fragments (bf16), or the value (f32).
+// Four consecutive elements (accumulator rows r = 0..3 of one lane) in one store.
 template <typename T>
-struct Split;
-template <>
-struct Split<bf16> {
-  __device__ static __forceinline__ void chain(const f32x4* tiles, int s, bf16x8& hi, bf16x8& lo) {
+__device__ __forceinline__ void put4v(T* dst, const f32x4& v) {
+  if constexpr (sizeof(T) == 2)
+    *reinterpret_cast<bf16x4*>(dst) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  else
+    *reinterpret_cast<f32x4*>(dst) = v;
+}
+
+// NATURAL fragment (k contiguous along the row) of a padded tile whose rows are
+// only 8-byte aligned: two 8-byte reads for bf16.
+__device__ __forceinline__ bf16x8 ld_nat8(const bf16* base, int pitch, int rc, int kstep) {
+  const int g = lane_id() >> 4;
+  const bf16* p = base + rc * pitch + kstep * 32 + 8 * g;
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 4);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ float ld_nat8(const float* base, int pitch, int rc, int kstep) {
+  return ld_kc_nat(base, pitch, rc, kstep);
+}
+
+// Decay weights 2^(l_last - l_j) of the token entries (CHAIN order, step s)
+// this lane holds in k-major fragments; the same for every column tile.
+template <typename T>
+struct DecayW {
+  static constexpr int NE = sizeof(T) == 2 ? 8 : 1;
+  float w[NE];
+  __device__ __forceinline__ void init(const float* sl, float l_last, int s) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = tiles[2 * s + (i >> 2)][i & 3];
-      const bf16 h = (bf16)x;
-      hi[i] = h;
-      lo[i] = (bf16)(x - (float)h);
+    for (int i = 0; i < NE; ++i) w[i] = fast_exp2(l_last - sl[chain_k<T>(s, i)]);
+  }
+  __device__ __forceinline__ typename Mma<T>::frag apply(typename Mma<T>::frag f) const {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = (bf16)((float)f[i] * w[i]);
+      return f;
+    } else {
+      return f * w[0];
     }
   }
 };
-template <>
-struct Split<float> {
-  __device__ static __forceinline__ void chain(const f32x4* tiles, int s, float& hi, float& lo) {
-    hi = tiles[s >> 2][s & 3];
-    lo = 0.f;
-  }
-};
-
-// Decay weights 2^(l_last - l_j) applied to the token entries of a CHAIN-order
-// k-major fragment of step s.
-template <typename T>
-__device__ __forceinline__ typename Mma<T>::frag decay_tokens(typename Mma<T>::frag f, const float* sl, float l_last,
-                                                               int s) {
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (bf16)((float)f[i] * fast_exp2(l_last - sl[chain_k<T>(s, i)]));
-    return f;
-  } else {
-    return f * fast_exp2(l_last - sl[chain_k<T>(s, 0)]);
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ float frag_sum(const typename Mma<T>::frag& f) {
-  if constexpr (sizeof(T) == 2) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s += (float)f[i];
-    return s;
-  } else {
-    return f;
-  }
-}
 
 template <typename C, bool AGG>
 __device__ __forceinline__ const char* tile_k(const char* buf) { return buf + (AGG ? 0 : C::TB); }
@@ -193,11 +195,7 @@ struct Ctx {
     if constexpr (!AGG) dma.issue(buf, Qg + (size_t)c0 * D, nv);
     dma.issue(buf + (AGG ? 0 : C::TB), Kg + (size_t)c0 * D, nv);
     dma.issue(buf + (AGG ? 1 : 2) * C::TB, Vg + (size_t)c0 * D, nv);
-    if (wave_id() == 0) {
-      const rsrc_t rg = make_rsrc(Gg + c0, (uint32_t)(nv * 4));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (LM_LDS void*)(buf + C::NTILE * C::TB), 4, lane_id() * 4, 0, 0,
-                                               0);
-    }
+    if (wave_id() == 0) lds_dma4(buf_desc(Gg + c0, (uint32_t)(nv * 4)), lane_id() * 4, lds_addr(buf + C::NTILE * C::TB));
   }
 };
 
@@ -267,12 +265,9 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
     // cumulative log2 decay of this chunk (each wave keeps a private copy)
     float l_last;
     {
-      float x = l < nvalid ? fmaxf(log2f(tile_g<C>(cur)[l]), -200.f) : 0.f;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(x, o);
-        if (l >= o) x += y;
-      }
+      // log2 g in hardware (g in (0, 1]; g = 0 gives -inf, clamped)
+      float x = l < nvalid ? fmaxf(__builtin_amdgcn_logf(tile_g<C>(cur)[l]), -200.f) : 0.f;
+      x = wave_scan_incl(x);
       sLw[l] = x;
       l_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), kC - 1));
     }
@@ -293,6 +288,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
       for (int qi = 0; qi < C::QPW; ++qi) {
         const int qt = w + NW * qi;
+        if (qt >= 4) continue;
         frag QF[C::NKD];
 #pragma unroll
         for (int ks = 0; ks < C::NKD; ++ks) QF[ks] = tl_nat_t<CPR, T>(Qt, 16 * qt + c16, ks);
@@ -315,7 +311,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
         if constexpr (CCQ) {
           f32x4 dq = zero4();
 #pragma unroll
-          for (int ks = 0; ks < C::NKD; ++ks) dq = M::mma(ld_kc_nat(sDot, C::PD, c16, ks), QF[ks], dq);
+          for (int ks = 0; ks < C::NKD; ++ks) dq = M::mma(ld_nat8(sDot, C::PDD, c16, ks), QF[ks], dq);
           const float wq = __shfl(dq[0] + dq[1], c16);
           const float mq = __shfl(dq[2] + dq[3], c16);
           float rs = 0.f;
@@ -331,23 +327,25 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
           if (g == 0) sAB[q] = make_float2(alpha, beta);
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
-            T* dst = prow + 16 * kt + 4 * g;
+            f32x4 v;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const bool in = kt < qt || (kt == qt && 4 * g + r <= c16);
-              dst[r] = from_f32<T>(in ? beta - alpha * Pr[qi][kt][r] : 0.f);
+              v[r] = in ? beta - alpha * Pr[qi][kt][r] : 0.f;
             }
+            put4v<T>(prow + 16 * kt + 4 * g, v);
           }
         } else {
           const float lq = sLw[q];
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
-            T* dst = prow + 16 * kt + 4 * g;
+            f32x4 v;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float dec = fast_exp2(lq - sLw[16 * kt + 4 * g + r]);
-              dst[r] = from_f32<T>(kt <= qt ? Pr[qi][kt][r] * dec : 0.f);
+              v[r] = kt <= qt ? Pr[qi][kt][r] * dec : 0.f;
             }
+            put4v<T>(prow + 16 * kt + 4 * g, v);
           }
         }
       }
@@ -362,33 +360,36 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int c0 = cbase + 16 * ct;
-          frag Mh[C::NKD], Ml[C::NKD];
+          // M_prev as the operand precision (bf16 for bf16 inputs): its rounding
+          // perturbs q_clean by at most lambda |k|^2 2^-9 |q|, the size of the
+          // rounding of q itself for unit-norm keys.
+          frag Mh[C::NKD];
           {
             f32x4 Mcol[DT];
 #pragma unroll
             for (int kt = 0; kt < DT; ++kt) Mcol[kt] = Mst[kt][ct];
 #pragma unroll
-            for (int s = 0; s < C::NKD; ++s) Split<T>::chain(Mcol, s, Mh[s], Ml[s]);
+            for (int s = 0; s < C::NKD; ++s) Mh[s] = M::chain(Mcol, s);
           }
           float mprev[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) mprev[r] = sMv[c0 + 4 * g + r];
-#pragma unroll
+#pragma unroll 1
           for (int qt = 0; qt < 4; ++qt) {
             f32x4 mqv = zero4();
 #pragma unroll
             for (int s = 0; s < C::NKD; ++s) {
               const frag qf = tl_chain_t<CPR, T>(Qt, 16 * qt + c16, s);
               mqv = M::mma(Mh[s], qf, mqv);
-              if constexpr (sizeof(T) == 2) mqv = M::mma(Ml[s], qf, mqv);
             }
             f32x4 kb = zero4();
 #pragma unroll
             for (int s = 0; s < C::NKT; ++s)
               if ((s * M::KS) / 16 <= qt) kb = M::mma(KTc[ct][s], ld_kc_chain(sP, C::PP, 16 * qt + c16, s), kb);
-            T* dst = sD + (16 * qt + c16) * C::PD + c0 + 4 * g;
+            f32x4 v;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(-ab[qt].x * mqv[r] + kb[r] + ab[qt].y * mprev[r]);
+            for (int r = 0; r < 4; ++r) v[r] = -ab[qt].x * mqv[r] + kb[r] + ab[qt].y * mprev[r];
+            put4v<T>(sD + (16 * qt + c16) * C::PDD + c0 + 4 * g, v);
           }
         }
         lds_barrier();  // delta complete; Bmat consumed
@@ -397,10 +398,11 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
         for (int qi = 0; qi < C::QPW; ++qi) {
           const int qt = w + NW * qi;
+          if (qt >= 4) continue;
           const int q = 16 * qt + c16;
           frag DF[C::NKD];
 #pragma unroll
-          for (int ks = 0; ks < C::NKD; ++ks) DF[ks] = ld_kc_nat(sD, C::PD, q, ks);
+          for (int ks = 0; ks < C::NKD; ++ks) DF[ks] = ld_nat8(sD, C::PDD, q, ks);
           const float lq = sLw[q];
           T* prow = sP + q * C::PP;
 #pragma unroll
@@ -410,13 +412,14 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
               for (int ks = 0; ks < C::NKD; ++ks) acc = M::mma(tl_nat_t<CPR, T>(Kt, 16 * kt + c16, ks), DF[ks], acc);
             }
-            T* dst = prow + 16 * kt + 4 * g;
+            f32x4 v;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const bool in = kt < qt || (kt == qt && 4 * g + r <= c16);
               const float dec = fast_exp2(lq - sLw[16 * kt + 4 * g + r]);
-              dst[r] = from_f32<T>(in ? acc[r] * dec : 0.f);
+              v[r] = in ? acc[r] * dec : 0.f;
             }
+            put4v<T>(prow + 16 * kt + 4 * g, v);
           }
         }
         lds_barrier();  // decayed scores complete
@@ -435,7 +438,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
         for (int s = 0; s < C::NKT; ++s) Vf[ct][s] = tl_kmaj_t<CPR, T>(Vt, s, cbase + 16 * ct);
       }
-#pragma unroll
+#pragma unroll 1
       for (int qt = 0; qt < 4; ++qt) {
         const int q = 16 * qt + c16;
         f32x4 inter[CT], acc[CT];
@@ -450,7 +453,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) inter[ct] = M::mma(Sc[ct][s], qf, inter[ct]);
           if constexpr (CCQ) {
-            const frag df = ld_kc_chain(sD, C::PD, q, s);
+            const frag df = ld_kc_chain(sD, C::PDD, q, s);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) inter[ct] = M::mma(Sc[ct][s], df, inter[ct]);
           }
@@ -467,14 +470,11 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int c0 = cbase + 16 * ct;
+          const f32x4 o = acc[ct] + bq * inter[ct];
           if constexpr (C::STAGE_O) {
-            T* dst = sO + q * C::PD + c0 + 4 * g;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(acc[ct][r] + bq * inter[ct][r]);
+            put4v<T>(sO + q * C::PD + c0 + 4 * g, o);
           } else if (q < nvalid) {
-            T* dst = Og + (size_t)(t0 + q) * D + c0 + 4 * g;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[r] = from_f32<T>(acc[ct][r] + bq * inter[ct][r]);
+            put4v<T>(Og + (size_t)(t0 + q) * D + c0 + 4 * g, o);
           }
         }
       }
@@ -490,10 +490,12 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
         for (int ct = 0; ct < CT; ++ct) S[kt][ct] *= b_last;
       frag Vw[CT][C::NKT];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+      for (int s = 0; s < C::NKT; ++s) {
+        DecayW<T> dw;
+        dw.init(sLw, l_last, s);
 #pragma unroll
-        for (int s = 0; s < C::NKT; ++s)
-          Vw[ct][s] = decay_tokens<T>(tl_kmaj_t<CPR, T>(Vt, s, cbase + 16 * ct), sLw, l_last, s);
+        for (int ct = 0; ct < CT; ++ct) Vw[ct][s] = dw.apply(tl_kmaj_t<CPR, T>(Vt, s, cbase + 16 * ct));
+      }
 #pragma unroll
       for (int kt = 0; kt < DT; ++kt) {
 #pragma unroll
@@ -507,19 +509,28 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
         }
       }
       if constexpr (CCQ) {
+        // column sums of K: ones^T K on the matrix core (every row of the tile
+        // holds the sum of its column)
+        frag ones;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.f;
+        } else {
+          ones = 1.f;
+        }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          float cs = 0.f;
+          f32x4 cs = zero4();
 #pragma unroll
-          for (int s = 0; s < C::NKT; ++s) cs += frag_sum<T>(KTc[ct][s]);
-          mreg[ct] += group_sum(cs);
+          for (int s = 0; s < C::NKT; ++s) cs = M::mma(ones, KTc[ct][s], cs);
+          mreg[ct] += cs[0];
           if constexpr (!AGG) {
             if (g == 0) {
               const int col = cbase + 16 * ct + c16;
               const T hi = from_f32<T>(mreg[ct]);
               sMv[col] = mreg[ct];
-              sDot[2 * C::PD + col] = hi;
-              sDot[3 * C::PD + col] = from_f32<T>(mreg[ct] - to_f32(hi));
+              sDot[2 * C::PDD + col] = hi;
+              sDot[3 * C::PDD + col] = from_f32<T>(mreg[ct] - to_f32(hi));
             }
           }
         }
@@ -603,8 +614,8 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
   }
   if constexpr (CCQ && !AGG) {
     // rows 0/1: gate weights (hi/lo); rows 2/3: running key sum (hi/lo); others 0
-    for (int i = threadIdx.x; i < 16 * C::PD; i += NT) {
-      const int row = i / C::PD, col = i - (i / C::PD) * C::PD;
+    for (int i = threadIdx.x; i < 16 * C::PDD; i += NT) {
+      const int row = i / C::PDD, col = i - (i / C::PDD) * C::PDD;
       float v = 0.f;
       if (col < D && row < 2) {
         const float wv = a.wl[(size_t)h * D + col];
@@ -619,8 +630,8 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
         const int col = cbase + 16 * ct + c16;
         const T hi = from_f32<T>(st.mreg[ct]);
         sMv[col] = st.mreg[ct];
-        sDot[2 * C::PD + col] = hi;
-        sDot[3 * C::PD + col] = from_f32<T>(st.mreg[ct] - to_f32(hi));
+        sDot[2 * C::PDD + col] = hi;
+        sDot[3 * C::PDD + col] = from_f32<T>(st.mreg[ct] - to_f32(hi));
       }
     }
   }

@@ -181,6 +181,41 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
 }
 
+// Buffer descriptor words over `nbytes` bytes at `base` (raw, stride 0, 32-bit
+// data format), for the inline-asm transfers below.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 buf_desc(const void* base, uint32_t nbytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  u32x4 d;
+  d[0] = (unsigned)a;
+  d[1] = (unsigned)(a >> 32) & 0xffffu;
+  d[2] = nbytes;
+  d[3] = 0x00020000u;
+  return d;
+}
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((unsigned)reinterpret_cast<uintptr_t>((LM_LDS const char*)p));
+}
+
+// Direct global->LDS transfers written as inline asm: LDS[dst + 16 lane] (or
+// 4 lane) = global[desc base + voff], 0 past the descriptor's range. The
+// compiler does not see these as LDS stores, so it inserts no waits for them
+// at unrelated LDS accesses; callers wait for them explicitly (vmcnt) and
+// publish them with a barrier before any LDS read of the destination.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const u32x4& desc, int voff, unsigned lds) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);  // keeps the operand scalar
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(desc), "s"(m)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const u32x4& desc, int voff, unsigned lds) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(desc), "s"(m)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // This wave's share of the DMA of a 64 x D tile into a swizzled LDS tile: each
 // wave moves INSTR blocks of 64 consecutive physical chunks. The per-lane byte
 // offsets in the (row-major, unswizzled) source are fixed, so they are computed
@@ -203,10 +238,10 @@ struct TileDma {
   // src: the tile's first row in global memory; rows: rows of the sequence left from src.
   __device__ __forceinline__ void issue(char* dst, const T* src, int rows) const {
     const int w = wave_id();
-    const rsrc_t rs = make_rsrc(src, (uint32_t)((rows < 64 ? rows : 64) * D * (int)sizeof(T)));
+    const u32x4 d = buf_desc(src, (uint32_t)((rows < 64 ? rows : 64) * D * (int)sizeof(T)));
+    const unsigned base = lds_addr(dst) + (unsigned)(w * INSTR * 1024);
 #pragma unroll
-    for (int i = 0; i < INSTR; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LM_LDS void*)(dst + (w * INSTR + i) * 1024), 16, voff[i], 0, 0, 0);
+    for (int i = 0; i < INSTR; ++i) lds_dma16(d, voff[i], base + (unsigned)(i * 1024));
   }
 };
 
@@ -326,6 +361,25 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within 16-lane rows
+// (DPP, zero fill at the row start), then each row adds the totals of the rows
+// before it (read from lanes 15, 31, 47).
+template <int CTRL>
+__device__ __forceinline__ float dpp_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float wave_scan_incl(float x) {
+  x += dpp_shr<0x111>(x);  // row_shr:1
+  x += dpp_shr<0x112>(x);  // row_shr:2
+  x += dpp_shr<0x114>(x);  // row_shr:4
+  x += dpp_shr<0x118>(x);  // row_shr:8
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+  const int row = lane_id() >> 4;
+  return x + (row == 0 ? 0.f : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
+}
 
 // ---------------------------------------------------------------------------
 // Element conversion.
