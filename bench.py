@@ -16,14 +16,29 @@ from cache.
 The JSON line also holds:
   * roofline: the entry point that takes longer per step (its kernels measured
     with HIP events on the stream they run on), as algorithmic HBM bytes per
-    call / average call time, against MI355X's 8 TB/s;
+    call / average call time, against MI355X's 8 TB/s. traffic is the measured
+    HBM bytes per call of that entry point (rocprofv3 FETCH_SIZE + WRITE_SIZE
+    runs, scaled by the same counters on a copy of known size), read from
+    profiles/traffic.json when it was taken on the current kernel sources,
+    else null;
   * cpu_baseline: the fp64 oracle on a bounded sample of the same workload
-    (a few (b, h) slices at full length) on the host cores;
+    (one (b, h) slice per host thread at full length, repeated until at least
+    10 s of work) on the host cores;
   * parts: per-path rates.
+
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR
+
+turns the counter collections of two runs of this bench under
+`rocprofv3 --pmc FETCH_SIZE` and `rocprofv3 --pmc WRITE_SIZE` (csv output)
+into profiles/traffic.json and prints a summary table. Each run of the bench
+first copies a 384 MiB buffer once; that copy's counters give the scale.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -37,6 +52,25 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 LLC_BYTES = 256 << 20
 METRIC = "fwd tokens/s per head at N=16K (causal GMA, CCQ-GLA) + % MFMA/HBM roofline"
+CALIB_BYTES = 384 << 20  # differs from every input tensor size
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+# kernels launched by each entry point (name fragments as rocprofv3 reports them)
+ENTRY_KERNELS = {
+    "gma_forward": ("gma4fast6kernel", "lm::gma::fast::kernel", "gma_kernel", "prep_kernel", "lm::gma::scan_kernel"),
+    "ccq_forward": ("lin_kernelIDF16bLi128ELb1", "lm::lin::scan_kernel"),
+}
+
+
+def sources_digest():
+    """Hash of the library's kernel and ABI sources (identifies the code the counters were taken on)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "linear_attention_gmm_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "linmix.h"))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def gma_bytes_per_head_token(cfg, esize=2):
@@ -65,7 +99,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", action="store_true", help="also time bidirectional GMA, GLA and long GMA")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two rocprofv3 --pmc runs of this bench into profiles/traffic.json")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
               "(every (b, h) slice is independent; see DESIGN.md on sharding). Use --gpus 1.", file=sys.stderr)
@@ -118,6 +157,13 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    # one copy of known size: its HBM counters scale the kernels' counters
+    calib_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -153,8 +199,15 @@ def main():
     }
     dom = "ccq" if c_ms >= g_ms else "gma_causal"
     achieved = parts[dom]["alg_GBps"]
+    traffic = None
+    if os.path.exists(TRAFFIC_JSON):
+        with open(TRAFFIC_JSON) as fh:
+            tj = json.load(fh)
+        entry = "ccq_forward" if dom == "ccq" else "gma_forward"
+        if tj.get("sources") == sources_digest() and entry in tj.get("bytes_per_call", {}):
+            traffic = tj["bytes_per_call"][entry]
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": "ccq_forward (segment-state + chunk kernels)" if dom == "ccq"
                 else "gma_forward (prep + segment-state + chunk kernels)",
                 "alg_bytes_per_call": parts[dom]["alg_bytes_per_call"], "avg_call_ms": parts[dom]["ms_per_call"]}
@@ -222,10 +275,11 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(gx, cx, gcfg, ccfg):
+def cpu_baseline(gx, cx, gcfg, ccfg, min_seconds=10.0, max_rounds=20):
     """The fp64 oracle (as it is) on a bounded sample of the step's workload:
     the first S (b, h) slices of each path at full length, S = host threads
-    (at most the slice count), so every thread has one slice of each."""
+    (at most the slice count), so every thread has one slice of each; the
+    sample is run again until at least min_seconds of work are timed."""
     import numpy as np
 
     import oracle
@@ -245,21 +299,90 @@ def cpu_baseline(gx, cx, gcfg, ccfg):
     mu = np.stack([gx["mu"][h].numpy() for _, h in gidx])
     lv = np.stack([gx["log_var"][h].numpy() for _, h in gidx])
     lp = np.stack([gx["logit_pi"][h].numpy() for _, h in gidx])
-    tg0 = time.perf_counter()
-    oracle.gma_forward(q, k, v, mu, lv, lp, causal=True, eps=gcfg.eps)
-    tg = time.perf_counter() - tg0
     cidx = head_slices(sc, ccfg.H)
     sel = lambda t: np.stack([t[b, h].float().numpy() for b, h in cidx])[None]
+    cq, ck, cv, cg = sel(cx["q"]), sel(cx["k"]), sel(cx["v"]), sel(cx["g"])
     w = np.stack([cx["w_lambda"][h].numpy() for _, h in cidx])
     bb = np.stack([cx["b_lambda"][h].numpy() for _, h in cidx])
-    tc0 = time.perf_counter()
-    oracle.ccq_forward(sel(cx["q"]), sel(cx["k"]), sel(cx["v"]), sel(cx["g"]), w, bb)
-    tc = time.perf_counter() - tc0
-    toks = sg * gcfg.N + sc * ccfg.N
+    tg = tc = 0.0
+    rounds = 0
+    while rounds < max_rounds and (rounds == 0 or tg + tc < min_seconds):
+        tg0 = time.perf_counter()
+        oracle.gma_forward(q, k, v, mu, lv, lp, causal=True, eps=gcfg.eps)
+        tg += time.perf_counter() - tg0
+        tc0 = time.perf_counter()
+        oracle.ccq_forward(cq, ck, cv, cg, w, bb)
+        tc += time.perf_counter() - tc0
+        rounds += 1
+    toks = rounds * (sg * gcfg.N + sc * ccfg.N)
     return {"value": toks / (tg + tc), "unit": "head-tokens/s", "cores": max(sg, sc), "kind": "oracle",
-            "sample": "%d causal-GMA slices + %d CCQ slices at N=16384 (one per thread), fp64; GMA %.1f s, "
-                      "CCQ %.1f s" % (sg, sc, tg, tc),
+            "sample": "%d round(s) of %d causal-GMA + %d CCQ slices at N=16384 (one slice per thread per path), "
+                      "fp64; GMA %.1f s, CCQ %.1f s" % (rounds, sg, sc, tg, tc),
             "host_threads": threads, "wall_s": time.perf_counter() - t0}
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Per-dispatch HBM bytes of each kernel from two rocprofv3 --pmc runs of
+    this bench (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled so that the
+    calibration copy reads and writes exactly its size. Writes
+    profiles/traffic.json and prints a markdown table."""
+
+    def load(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit("no counter_collection.csv under %s" % d)
+        rows = []
+        with open(f[0]) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0))
+        rows.sort()
+        return [(name, b) for _, name, b in rows]
+
+    fetch = load(fetch_dir, "FETCH_SIZE")
+    write = load(write_dir, "WRITE_SIZE")
+
+    # the calibration copy: the last copy dispatched before the library's first kernel
+    def calib(rows):
+        last = None
+        for name, b in rows:
+            if "lm::" in name or "_ZN2lm" in name:
+                break
+            if "copy" in name.lower():
+                last = b
+        if not last:
+            raise SystemExit("calibration copy not found")
+        return last
+
+    fs, ws = CALIB_BYTES / calib(fetch), CALIB_BYTES / calib(write)
+
+    def per_kernel(rows, scale):
+        acc = {}
+        for name, b in rows:
+            n, t = acc.get(name, (0, 0.0))
+            acc[name] = (n + 1, t + b * scale)
+        return {k: (n, t / n) for k, (n, t) in acc.items()}
+
+    fk, wk = per_kernel(fetch, fs), per_kernel(write, ws)
+    out = {"sources": sources_digest(), "fetch_scale": fs, "write_scale": ws, "kernels": {}, "bytes_per_call": {}}
+    print("| kernel | dispatches | read MB/dispatch | written MB/dispatch |")
+    print("|---|---|---|---|")
+    for k in sorted(fk, key=lambda k: -fk[k][1]):
+        n, fb = fk[k]
+        wb = wk.get(k, (0, 0.0))[1]
+        out["kernels"][k] = {"dispatches": n, "read_bytes": fb, "write_bytes": wb}
+        print("| %s | %d | %.1f | %.1f |" % (k[:70], n, fb / 1e6, wb / 1e6))
+    for entry, frags in ENTRY_KERNELS.items():
+        total = 0.0
+        for k, v in out["kernels"].items():
+            if any(f in k for f in frags):
+                total += v["read_bytes"] + v["write_bytes"]
+        out["bytes_per_call"][entry] = total
+    print("\nscale factors: FETCH_SIZE x %.4f, WRITE_SIZE x %.4f (%d MiB copy)" % (fs, ws, CALIB_BYTES >> 20))
+    for entry, b in out["bytes_per_call"].items():
+        print("%s: %.1f MB of HBM traffic per call" % (entry, b / 1e6))
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(out, fh, indent=1)
 
 
 if __name__ == "__main__":

@@ -213,9 +213,7 @@ struct State {
 };
 
 // One chunk. `cur` holds this chunk's tiles (DMA issued a chunk earlier when
-// double-buffered); `nxt` receives the next chunk's tiles. Instantiated once per
-// buffer parity so that every LDS access names its array statically (the
-// compiler then knows which accesses can overlap an outstanding DMA).
+// double-buffered); `nxt` receives the next chunk's tiles.
 template <typename T, int D, bool CCQ, bool AGG>
 __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T, D, CCQ, AGG>& st, char* cur,
                                            char* nxt, char* work, int64_t t0) {
@@ -354,9 +352,6 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 
       if constexpr (CCQ) {
         // ---- phase 3: delta^T for this wave's feature columns
-        float2 ab[4];
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) ab[qt] = sAB[16 * qt + c16];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int c0 = cbase + 16 * ct;
@@ -386,9 +381,10 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
             for (int s = 0; s < C::NKT; ++s)
               if ((s * M::KS) / 16 <= qt) kb = M::mma(KTc[ct][s], ld_kc_chain(sP, C::PP, 16 * qt + c16, s), kb);
+            const float2 ab = sAB[16 * qt + c16];  // (alpha, beta) of this lane's query
             f32x4 v;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = -ab[qt].x * mqv[r] + kb[r] + ab[qt].y * mprev[r];
+            for (int r = 0; r < 4; ++r) v[r] = -ab.x * mqv[r] + kb[r] + ab.y * mprev[r];
             put4v<T>(sD + (16 * qt + c16) * C::PDD + c0 + 4 * g, v);
           }
         }
@@ -636,13 +632,13 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
     }
   }
 
-  if constexpr (C::NBUF == 2) {
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * kC) {
-      chunk_step<T, D, CCQ, AGG>(x, st, sBuf0, sBuf1, sWork, t0);
-      if (t0 + kC < t_end) chunk_step<T, D, CCQ, AGG>(x, st, sBuf1, sBuf0, sWork, t0 + kC);
-    }
-  } else {
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += kC) chunk_step<T, D, CCQ, AGG>(x, st, sBuf0, sBuf0, sWork, t0);
+  // The tile DMA is invisible to the compiler (inline asm), so the buffer of a
+  // chunk can be chosen at run time without extra waits.
+  int it = 0;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kC, ++it) {
+    char* cur = (C::NBUF == 2 && (it & 1)) ? sBuf1 : sBuf0;
+    char* nxt = (C::NBUF == 2 && !(it & 1)) ? sBuf1 : sBuf0;
+    chunk_step<T, D, CCQ, AGG>(x, st, cur, nxt, sWork, t0);
   }
 
   if constexpr (C::STAGE_O) {
