@@ -45,6 +45,21 @@ namespace lin {
 
 constexpr int kC = 64;
 constexpr int kLds = 160 * 1024;
+constexpr float kLog2eF = 1.4426950408889634f;
+
+// B operand (CHAIN order, token step s) of the lower-triangular ones matrix for
+// query q of the chunk: entry (token j, query q) is 1 where j <= q.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag tri_frag(int s, int q) {
+  typename Mma<T>::frag f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = chain_k<T>(s, i) <= q ? (bf16)1.f : (bf16)0.f;
+  } else {
+    f = chain_k<T>(s, 0) <= q ? 1.f : 0.f;
+  }
+  return f;
+}
 
 struct Args {
   const void* q;
@@ -65,19 +80,33 @@ struct Args {
 
 // Waves per workgroup: 16 state columns per wave (8 waves, two per SIMD, at
 // D = 128 so that the MFMA work of one wave overlaps the VALU work of the
-// other). Query tiles are owned by waves 0..3 (waves >= 4 own none).
+// other).
+// The per-query work (score tiles of query tile qt against key tiles kt <= qt)
+// is shared out by (qt, kt): with 8 waves each query tile has two owners, part 0
+// taking the even key tiles and part 1 the odd ones; part-1 waves take the query
+// tiles in reverse order, so that waves w and w + 4 (one SIMD) get a light and a
+// heavy tile.
 template <int D>
 struct Waves {
   static constexpr int NW = D / 16;
   static constexpr int CW = D / NW;  // value (and M) columns per wave
   static constexpr int CT = CW / 16;
-  static constexpr int QPW = NW >= 4 ? 1 : 4 / NW;  // query tiles per wave
+  static constexpr int SPLIT = NW >= 8 ? 2 : 1;  // owners per query tile
+  static constexpr int QW = NW / SPLIT;           // waves per part
+  static constexpr int QPW = QW >= 4 ? 1 : 4 / QW;  // query tiles per wave
+  static constexpr int KPW = 4 / SPLIT;           // key tiles per owned query tile
+  __device__ static __forceinline__ int part(int w) { return w / QW; }
+  __device__ static __forceinline__ int qtile(int w, int qi) {
+    const int r = w % QW + QW * qi;
+    return part(w) == 0 ? r : 3 - r;
+  }
+  __device__ static __forceinline__ int ktile(int w, int j) { return part(w) + SPLIT * j; }
 };
 
 template <typename T, int D, bool CCQ, bool AGG>
 struct Cfg {
   typedef Waves<D> Wv;
-  static constexpr int NW = Wv::NW, CW = Wv::CW, CT = Wv::CT, QPW = Wv::QPW;
+  static constexpr int NW = Wv::NW, CW = Wv::CW, CT = Wv::CT, QPW = Wv::QPW, KPW = Wv::KPW, SPLIT = Wv::SPLIT;
   static constexpr int KS = Mma<T>::KS;
   static constexpr int NKD = D / KS;   // k-steps over features
   static constexpr int NKT = kC / KS;  // k-steps over tokens
@@ -101,8 +130,10 @@ struct Cfg {
   static constexpr int p_bytes = AGG ? 0 : kC * PP * ES;
   static constexpr int o_dot = o_p + p_bytes;               // [16][PDD] gate and mean rows
   static constexpr int dot_bytes = (CCQ && !AGG) ? 16 * PDD * ES : 0;
-  static constexpr int o_small = o_dot + dot_bytes;         // sL [NW][64], sAB [64] float2, sMv [D]
-  static constexpr int small_bytes = NW * kC * 4 + kC * 8 + D * 4;
+  // sL [NW][64]; sWQ [64] float2 (gate logit w.q, mean term m_prev.q); sMv [D];
+  // sRS [SPLIT][64] (partial row sums of the masked scores)
+  static constexpr int o_small = o_dot + dot_bytes;
+  static constexpr int small_bytes = NW * kC * 4 + kC * 8 + D * 4 + SPLIT * kC * 4;
   static constexpr int o_o = o_small + small_bytes;         // output staging [64][PD]
   static constexpr int o_bytes = AGG ? 0 : kC * PD * ES;
   static constexpr bool STAGE_O = !AGG && o_o + o_bytes + BUF <= kLds;
@@ -189,13 +220,29 @@ struct Ctx {
   int cbase;
   TileDma<T, D, C::NW> dma;
 
-  // Issues the DMA of the chunk at c0 (Q unless AGG, K, V, and the decays) into `buf`.
-  __device__ __forceinline__ void issue(char* buf, int64_t c0) const {
+  // Issues the DMA of one tile of the chunk at c0 into `buf`: TILE 0 = Q (not
+  // in AGG), 1 = K, 2 = V, 3 = the decays.
+  template <int TILE>
+  __device__ __forceinline__ void issue_tile(char* buf, int64_t c0) const {
     const int nv = (int)((N - c0) < kC ? (N - c0) : kC);
-    if constexpr (!AGG) dma.issue(buf, Qg + (size_t)c0 * D, nv);
-    dma.issue(buf + (AGG ? 0 : C::TB), Kg + (size_t)c0 * D, nv);
-    dma.issue(buf + (AGG ? 1 : 2) * C::TB, Vg + (size_t)c0 * D, nv);
-    if (wave_id() == 0) lds_dma4(buf_desc(Gg + c0, (uint32_t)(nv * 4)), lane_id() * 4, lds_addr(buf + C::NTILE * C::TB));
+    if constexpr (TILE == 0) {
+      static_assert(!AGG, "no Q tile in the segment pass");
+      dma.issue(buf, Qg + (size_t)c0 * D, nv);
+    } else if constexpr (TILE == 1) {
+      dma.issue(buf + (AGG ? 0 : C::TB), Kg + (size_t)c0 * D, nv);
+    } else if constexpr (TILE == 2) {
+      dma.issue(buf + (AGG ? 1 : 2) * C::TB, Vg + (size_t)c0 * D, nv);
+    } else {
+      if (wave_id() == 0)
+        lds_dma4(buf_desc(Gg + c0, (uint32_t)(nv * 4)), lane_id() * 4, lds_addr(buf + C::NTILE * C::TB));
+    }
+  }
+  // All tiles of the chunk at c0.
+  __device__ __forceinline__ void issue(char* buf, int64_t c0) const {
+    if constexpr (!AGG) issue_tile<0>(buf, c0);
+    issue_tile<1>(buf, c0);
+    issue_tile<2>(buf, c0);
+    issue_tile<3>(buf, c0);
   }
 };
 
@@ -230,8 +277,9 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
   T* sP = reinterpret_cast<T*>(work + C::o_p);
   T* sDot = reinterpret_cast<T*>(work + C::o_dot);
   float* sLw = reinterpret_cast<float*>(work + C::o_small) + w * kC;
-  float2* sAB = reinterpret_cast<float2*>(work + C::o_small + NW * kC * 4);
+  float2* sWQ = reinterpret_cast<float2*>(work + C::o_small + NW * kC * 4);
   float* sMv = reinterpret_cast<float*>(work + C::o_small + NW * kC * 4 + kC * 8);
+  float* sRS = sMv + D;
   T* sO = reinterpret_cast<T*>(work + C::o_o);
   T* __restrict__ Og = x.Og;
   f32x4 (&S)[DT][CT] = st.S;
@@ -240,7 +288,8 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
   float& lseg = st.lseg;
   int64_t& t_prev = st.t_prev;
   (void)gate_b;
-  (void)sAB;
+  (void)sWQ;
+  (void)sRS;
   (void)sO;
   (void)Og;
   (void)t_prev;
@@ -251,11 +300,26 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
   }
   wait_vmem();
   lds_barrier();  // this chunk's tiles landed; the previous chunk is finished everywhere
-  if constexpr (C::STAGE_O) {
-    if (t_prev >= 0) store_rows<T, D, NT>(Og + (size_t)t_prev * D, sO, C::PD, kC);
-  }
-  if constexpr (C::NBUF == 2) {
-    if (t0 + kC < x.t_end) x.issue(nxt, t0 + kC);
+  // The next chunk's DMA and the previous chunk's output stores are spread over
+  // the phases of this one: issued together, the vector memory instructions of
+  // all waves queue behind each other in the address unit.
+  const bool pre = C::NBUF == 2 && t0 + kC < x.t_end;
+  const int64_t tn = t0 + kC;
+  (void)pre;
+  (void)tn;
+  if constexpr (AGG) {
+    if (pre) {
+      x.template issue_tile<1>(nxt, tn);
+      x.template issue_tile<3>(nxt, tn);
+    }
+  } else if constexpr (!CCQ) {
+    if constexpr (C::STAGE_O) {
+      if (t_prev >= 0) store_rows<T, D, NT>(Og + (size_t)t_prev * D, sO, C::PD, kC);
+    }
+    if (pre) {
+      x.template issue_tile<0>(nxt, tn);
+      x.template issue_tile<3>(nxt, tn);
+    }
   }
     const char* Kt = tile_k<C, AGG>(cur);
     const char* Vt = tile_v<C, AGG>(cur);
@@ -278,80 +342,130 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
         for (int s = 0; s < C::NKT; ++s) KTc[ct][s] = tl_kmaj_t<CPR, T>(Kt, s, cbase + 16 * ct);
     }
+    if constexpr (AGG) {
+      if (pre) x.template issue_tile<2>(nxt, tn);
+    }
 
     if constexpr (!AGG) {
       const char* Qt = cur;
-      // ---- phase 1: per owned query tile: raw scores, gate/mean terms, Bmat or decayed scores
-      f32x4 Pr[C::QPW][4];
+      // ---- phase 1: owned (query tile, key tile) pairs: raw scores; for CCQ the
+      //      masked scores, their partial row sums and the gate/mean terms, for
+      //      the plain read the decayed scores
+      typedef Waves<D> Wv;
+      f32x4 Pr[C::QPW][C::KPW];
 #pragma unroll
       for (int qi = 0; qi < C::QPW; ++qi) {
-        const int qt = w + NW * qi;
-        if (qt >= 4) continue;
+        const int qt = Wv::qtile(w, qi);
+        const int q = 16 * qt + c16;
         frag QF[C::NKD];
 #pragma unroll
-        for (int ks = 0; ks < C::NKD; ++ks) QF[ks] = tl_nat_t<CPR, T>(Qt, 16 * qt + c16, ks);
+        for (int ks = 0; ks < C::NKD; ++ks) QF[ks] = tl_nat_t<CPR, T>(Qt, q, ks);
+        // bf16: all key fragments of the owned tiles are read up front (one LDS
+        // round trip); fp32 fragments are single floats, read where used.
+        constexpr bool HOIST = sizeof(T) == 2;
+        frag KF[HOIST ? C::KPW : 1][HOIST ? C::NKD : 1];
+        if constexpr (HOIST) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          Pr[qi][kt] = zero4();
-          if (kt <= qt) {
+          for (int j = 0; j < C::KPW; ++j) {
+            const int kt = Wv::ktile(w, j);
+            if (kt <= qt) {
 #pragma unroll
-            for (int ks = 0; ks < C::NKD; ++ks)
-              Pr[qi][kt] = M::mma(tl_nat_t<CPR, T>(Kt, 16 * kt + c16, ks), QF[ks], Pr[qi][kt]);
-            if (kt == qt) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (4 * g + r > c16) Pr[qi][kt][r] = 0.f;
+              for (int ks = 0; ks < C::NKD; ++ks) KF[j][ks] = tl_nat_t<CPR, T>(Kt, 16 * kt + c16, ks);
             }
           }
         }
-        const int q = 16 * qt + c16;
+        const bool dq_owner = CCQ && Wv::part(w) == C::SPLIT - 1;
+        frag DQ[CCQ && HOIST ? C::NKD : 1];
+        if constexpr (CCQ && HOIST) {
+          if (dq_owner) {
+#pragma unroll
+            for (int ks = 0; ks < C::NKD; ++ks) DQ[ks] = ld_nat8(sDot, C::PDD, c16, ks);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < C::KPW; ++j) {
+          const int kt = Wv::ktile(w, j);
+          Pr[qi][j] = zero4();
+          if (kt <= qt) {
+#pragma unroll
+            for (int ks = 0; ks < C::NKD; ++ks)
+              Pr[qi][j] = M::mma(HOIST ? KF[HOIST ? j : 0][HOIST ? ks : 0] : tl_nat_t<CPR, T>(Kt, 16 * kt + c16, ks),
+                                 QF[ks], Pr[qi][j]);
+            if (kt == qt) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (4 * g + r > c16) Pr[qi][j][r] = 0.f;
+            }
+          }
+        }
         T* prow = sP + q * C::PP;
         if constexpr (CCQ) {
-          f32x4 dq = zero4();
+          if (dq_owner) {
+            f32x4 dq = zero4();
 #pragma unroll
-          for (int ks = 0; ks < C::NKD; ++ks) dq = M::mma(ld_nat8(sDot, C::PDD, c16, ks), QF[ks], dq);
-          const float wq = __shfl(dq[0] + dq[1], c16);
-          const float mq = __shfl(dq[2] + dq[3], c16);
+            for (int ks = 0; ks < C::NKD; ++ks)
+              dq = M::mma(HOIST ? DQ[HOIST ? ks : 0] : ld_nat8(sDot, C::PDD, c16, ks), QF[ks], dq);
+            const float wq = __shfl(dq[0] + dq[1], c16);
+            const float mq = __shfl(dq[2] + dq[3], c16);
+            if (g == 0) sWQ[q] = make_float2(wq, mq);
+          }
           float rs = 0.f;
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
+          for (int j = 0; j < C::KPW; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) rs += Pr[qi][kt][r];
+            for (int r = 0; r < 4; ++r) rs += Pr[qi][j][r];
           rs = group_sum(rs);
-          const float cnt = (float)(t0 + q + 1);
-          const float lam = 1.f / (1.f + expf(-(wq + gate_b)));
-          const float alpha = lam / cnt;
-          const float beta = lam * ((mq + rs) / cnt) / cnt;
-          if (g == 0) sAB[q] = make_float2(alpha, beta);
+          if (g == 0) sRS[Wv::part(w) * kC + q] = rs;
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
-            f32x4 v;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const bool in = kt < qt || (kt == qt && 4 * g + r <= c16);
-              v[r] = in ? beta - alpha * Pr[qi][kt][r] : 0.f;
-            }
-            put4v<T>(prow + 16 * kt + 4 * g, v);
-          }
+          for (int j = 0; j < C::KPW; ++j) put4v<T>(prow + 16 * Wv::ktile(w, j) + 4 * g, Pr[qi][j]);
         } else {
           const float lq = sLw[q];
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
+          for (int j = 0; j < C::KPW; ++j) {
+            const int kt = Wv::ktile(w, j);
+            const f32x4 lk = *reinterpret_cast<const f32x4*>(sLw + 16 * kt + 4 * g);
             f32x4 v;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float dec = fast_exp2(lq - sLw[16 * kt + 4 * g + r]);
-              v[r] = kt <= qt ? Pr[qi][kt][r] * dec : 0.f;
-            }
+            for (int r = 0; r < 4; ++r) v[r] = kt <= qt ? Pr[qi][j][r] * fast_exp2(lq - lk[r]) : 0.f;
             put4v<T>(prow + 16 * kt + 4 * g, v);
           }
         }
       }
       lds_barrier();
-
+      if constexpr (CCQ) {
+        if constexpr (C::STAGE_O) {
+          if (t_prev >= 0) store_rows<T, D, NT>(Og + (size_t)t_prev * D, sO, C::PD, kC);
+        }
+        if (pre) x.template issue_tile<2>(nxt, tn);
+      } else {
+        if (pre) {
+          x.template issue_tile<1>(nxt, tn);
+          x.template issue_tile<2>(nxt, tn);
+        }
+      }
 
       if constexpr (CCQ) {
-        // ---- phase 3: delta^T for this wave's feature columns
+        // ---- phase 3: delta^T for this wave's feature columns,
+        //   delta_i = -alpha_i (M_prev q_i + sum_j k_j P_ij) + beta_i (sum_{j<=i} k_j + m_prev)
+        // (P masked to j <= i). The prefix sum of keys is a product with the
+        // lower-triangular ones matrix, built in registers.
+        const float gate_bias = gate_b;
+        const float t0f = (float)t0;
+        // bf16 diagonal blocks of the mask (tokens 32 s' .. 32 s' + 31 against
+        // query tile qt with s' = qt / 2): tri0 for even qt, tri1 for odd qt
+        frag ones, tri0, tri1;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int j = chain_k<T>(0, i);
+            ones[i] = (bf16)1.f;
+            tri0[i] = j <= c16 ? (bf16)1.f : (bf16)0.f;
+            tri1[i] = j <= 16 + c16 ? (bf16)1.f : (bf16)0.f;
+          }
+        }
+        (void)ones;
+        (void)tri0;
+        (void)tri1;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int c0 = cbase + 16 * ct;
@@ -371,54 +485,100 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
           for (int r = 0; r < 4; ++r) mprev[r] = sMv[c0 + 4 * g + r];
 #pragma unroll 1
           for (int qt = 0; qt < 4; ++qt) {
+            const int q = 16 * qt + c16;
+            // bf16: every operand of this query tile is requested before the
+            // first product (one LDS round trip); fp32 operands are read where used.
+            constexpr bool HOIST = sizeof(T) == 2;
+            frag qf[HOIST ? C::NKD : 1], pf[HOIST ? C::NKT : 1];
+            if constexpr (HOIST) {
+#pragma unroll
+              for (int s = 0; s < C::NKD; ++s) qf[s] = tl_chain_t<CPR, T>(Qt, q, s);
+#pragma unroll
+              for (int s = 0; s < C::NKT; ++s) pf[s] = ld_kc_chain(sP, C::PP, q, s);
+            }
+            const float2 wm = sWQ[q];
+            float rs = sRS[q];
+            if constexpr (C::SPLIT > 1) rs += sRS[kC + q];
+            if constexpr (HOIST) __builtin_amdgcn_sched_barrier(0);
             f32x4 mqv = zero4();
 #pragma unroll
-            for (int s = 0; s < C::NKD; ++s) {
-              const frag qf = tl_chain_t<CPR, T>(Qt, 16 * qt + c16, s);
-              mqv = M::mma(Mh[s], qf, mqv);
-            }
-            f32x4 kb = zero4();
+            for (int s = 0; s < C::NKD; ++s)
+              mqv = M::mma(Mh[s], HOIST ? qf[HOIST ? s : 0] : tl_chain_t<CPR, T>(Qt, q, s), mqv);
+            f32x4 kp = zero4(), kc = zero4();
 #pragma unroll
             for (int s = 0; s < C::NKT; ++s)
-              if ((s * M::KS) / 16 <= qt) kb = M::mma(KTc[ct][s], ld_kc_chain(sP, C::PP, 16 * qt + c16, s), kb);
-            const float2 ab = sAB[16 * qt + c16];  // (alpha, beta) of this lane's query
+              if ((s * M::KS) / 16 <= qt) {
+                kp = M::mma(KTc[ct][s], HOIST ? pf[HOIST ? s : 0] : ld_kc_chain(sP, C::PP, q, s), kp);
+                frag tri;
+                if constexpr (HOIST) {
+                  // whole 32-token blocks below the diagonal are all ones
+                  tri = (s + 1) * M::KS <= 16 * qt ? ones : ((qt & 1) ? tri1 : tri0);
+                } else {
+                  tri = tri_frag<T>(s, q);
+                }
+                kc = M::mma(KTc[ct][s], tri, kc);
+              }
+            // gate and mean weights of this lane's query (count t = t0 + q + 1)
+            const float lam = __builtin_amdgcn_rcpf(1.f + fast_exp2(-(wm.x + gate_bias) * kLog2eF));
+            const float inv_t = __builtin_amdgcn_rcpf(t0f + (float)(q + 1));
+            const float alpha = lam * inv_t;
+            const float beta = alpha * (wm.y + rs) * inv_t;
             f32x4 v;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = -ab.x * mqv[r] + kb[r] + ab.y * mprev[r];
-            put4v<T>(sD + (16 * qt + c16) * C::PDD + c0 + 4 * g, v);
+            for (int r = 0; r < 4; ++r) v[r] = beta * (kc[r] + mprev[r]) - alpha * (mqv[r] + kp[r]);
+            put4v<T>(sD + q * C::PDD + c0 + 4 * g, v);
           }
         }
-        lds_barrier();  // delta complete; Bmat consumed
+        lds_barrier();  // delta complete; masked scores consumed
+        if (pre) x.template issue_tile<1>(nxt, tn);
 
-        // ---- phase 4: scores with the cleaned query, decay, for owned query tiles
+        // ---- phase 4: owned score tiles with the cleaned query, decayed
 #pragma unroll
         for (int qi = 0; qi < C::QPW; ++qi) {
-          const int qt = w + NW * qi;
-          if (qt >= 4) continue;
+          const int qt = Wv::qtile(w, qi);
           const int q = 16 * qt + c16;
           frag DF[C::NKD];
 #pragma unroll
           for (int ks = 0; ks < C::NKD; ++ks) DF[ks] = ld_nat8(sD, C::PDD, q, ks);
+          constexpr bool HOIST = sizeof(T) == 2;
+          frag KF[HOIST ? C::KPW : 1][HOIST ? C::NKD : 1];
+          if constexpr (HOIST) {
+#pragma unroll
+            for (int j = 0; j < C::KPW; ++j) {
+              const int kt = Wv::ktile(w, j);
+              if (kt <= qt) {
+#pragma unroll
+                for (int ks = 0; ks < C::NKD; ++ks) KF[j][ks] = tl_nat_t<CPR, T>(Kt, 16 * kt + c16, ks);
+              }
+            }
+          }
           const float lq = sLw[q];
           T* prow = sP + q * C::PP;
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
-            f32x4 acc = Pr[qi][kt];
+          for (int j = 0; j < C::KPW; ++j) {
+            const int kt = Wv::ktile(w, j);
+            f32x4 acc = Pr[qi][j];
+            f32x4 v = zero4();
             if (kt <= qt) {
 #pragma unroll
-              for (int ks = 0; ks < C::NKD; ++ks) acc = M::mma(tl_nat_t<CPR, T>(Kt, 16 * kt + c16, ks), DF[ks], acc);
-            }
-            f32x4 v;
+              for (int ks = 0; ks < C::NKD; ++ks)
+                acc = M::mma(HOIST ? KF[HOIST ? j : 0][HOIST ? ks : 0] : tl_nat_t<CPR, T>(Kt, 16 * kt + c16, ks), DF[ks],
+                             acc);
+              const f32x4 lk = *reinterpret_cast<const f32x4*>(sLw + 16 * kt + 4 * g);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const bool in = kt < qt || (kt == qt && 4 * g + r <= c16);
-              const float dec = fast_exp2(lq - sLw[16 * kt + 4 * g + r]);
-              v[r] = in ? acc[r] * dec : 0.f;
+              for (int r = 0; r < 4; ++r) {
+                const bool in = kt < qt || 4 * g + r <= c16;
+                v[r] = in ? acc[r] * fast_exp2(lq - lk[r]) : 0.f;
+              }
             }
             put4v<T>(prow + 16 * kt + 4 * g, v);
           }
         }
         lds_barrier();  // decayed scores complete
+        if (pre) {
+          x.template issue_tile<0>(nxt, tn);
+          x.template issue_tile<3>(nxt, tn);
+        }
       }
 
       // ---- phase 5: outputs of this wave's value columns (query tile outer, so Q and
@@ -492,15 +652,40 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) Vw[ct][s] = dw.apply(tl_kmaj_t<CPR, T>(Vt, s, cbase + 16 * ct));
       }
+      if constexpr (sizeof(T) == 2) {
+        // K^T fragments one feature tile ahead of their products, so the LDS
+        // latency of tile kt+1 overlaps the matrix-core work of tile kt.
+        frag kfb[2][C::NKT];
 #pragma unroll
-      for (int kt = 0; kt < DT; ++kt) {
+        for (int s = 0; s < C::NKT; ++s) kfb[0][s] = tl_kmaj_t<CPR, T>(Kt, s, 0);
 #pragma unroll
-        for (int s = 0; s < C::NKT; ++s) {
-          const frag kf = tl_kmaj_t<CPR, T>(Kt, s, 16 * kt);
+        for (int kt = 0; kt < DT; ++kt) {
+          if (kt + 1 < DT) {
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            S[kt][ct] = M::mma(kf, Vw[ct][s], S[kt][ct]);
-            if constexpr (CCQ) Mst[kt][ct] = M::mma(kf, KTc[ct][s], Mst[kt][ct]);
+            for (int s = 0; s < C::NKT; ++s) kfb[(kt + 1) & 1][s] = tl_kmaj_t<CPR, T>(Kt, s, 16 * (kt + 1));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s = 0; s < C::NKT; ++s) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              S[kt][ct] = M::mma(kfb[kt & 1][s], Vw[ct][s], S[kt][ct]);
+              if constexpr (CCQ) Mst[kt][ct] = M::mma(kfb[kt & 1][s], KTc[ct][s], Mst[kt][ct]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < DT; ++kt) {
+#pragma unroll
+          for (int s = 0; s < C::NKT; ++s) {
+            const frag kf = tl_kmaj_t<CPR, T>(Kt, s, 16 * kt);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              S[kt][ct] = M::mma(kf, Vw[ct][s], S[kt][ct]);
+              if constexpr (CCQ) Mst[kt][ct] = M::mma(kf, KTc[ct][s], Mst[kt][ct]);
+            }
           }
         }
       }
