@@ -46,14 +46,17 @@ struct Plan {
   int64_t seg_len;
 };
 
-// Cuts each sequence into P segments of whole chunks. Depends only on the
-// shapes (and the caller's explicit request), so results are reproducible.
-Plan plan_segments(int64_t BH, int64_t N, int64_t segments, int64_t target = kTargetGroups) {
+// Cuts each sequence into P segments of whole chunks. An automatic plan
+// (segments == 0) makes each segment a multiple of `granule` chunks. Depends
+// only on the shapes (and the caller's explicit request), so results are
+// reproducible.
+Plan plan_segments(int64_t BH, int64_t N, int64_t segments, int64_t target = kTargetGroups, int64_t granule = 1) {
   const int64_t nch = (N + kChunk - 1) / kChunk;
   int64_t P = segments > 0 ? segments : (target + BH - 1) / BH;
   if (P < 1) P = 1;
   if (P > nch) P = nch;
-  const int64_t cps = (nch + P - 1) / P;
+  int64_t cps = (nch + P - 1) / P;
+  if (segments == 0) cps = (cps + granule - 1) / granule * granule;
   P = (nch + cps - 1) / cps;
   return Plan{P, cps * kChunk};
 }
@@ -126,16 +129,22 @@ int gma_check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64
 
 // ----------------------------------------------------------------------------- linear attention
 
+// The segment-state pass runs over kLinSub sub-segments per segment: twice the
+// workgroups of the chunk pass, two of them sharing a CU.
+constexpr int64_t kLinSub = 2;
+
 struct LinLayout {
   size_t agg, total;
   Plan plan;
+  int64_t R;
 };
 
 LinLayout lin_layout(int64_t B, int64_t H, int64_t N, int64_t dk, bool ccq, int64_t segments) {
   LinLayout L;
-  L.plan = plan_segments(B * H, N, segments);
+  L.plan = plan_segments(B * H, N, segments, kTargetGroups, kLinSub);
+  L.R = L.plan.P > 1 && (L.plan.seg_len / kChunk) % kLinSub == 0 ? kLinSub : 1;
   L.agg = 0;
-  L.total = align_up((size_t)B * H * L.plan.P * lm::lin_state_floats(dk, ccq) * 4);
+  L.total = align_up((size_t)B * H * L.R * L.plan.P * lm::lin_state_floats(dk, ccq) * 4);
   return L;
 }
 
@@ -188,6 +197,7 @@ int lin_forward(const char* fn, bool ccq, const void* q, const void* k, const vo
   La.D = dk;
   La.P = L.plan.P;
   La.seg_len = L.plan.seg_len;
+  La.R = L.R;
   La.bf16 = dtype == LM_BF16;
   La.ccq = ccq;
   hipError_t e = lm::linattn_launch(La, static_cast<hipStream_t>(stream));

@@ -32,14 +32,15 @@ struct LinLaunch {
   const float* w_lambda;  // CCQ only
   const float* b_lambda;  // CCQ only
   void* out;
-  float* agg;  // workspace: per (b,h,segment) state block (see linattn.hip)
+  float* agg;  // workspace: R * P state blocks per (b,h) (see linattn.hip)
   int64_t B, H, N, D, P, seg_len;
+  int64_t R;  // sub-segments per segment in the segment-state pass
   bool bf16;
   bool ccq;
 };
 hipError_t linattn_launch(const LinLaunch& L, hipStream_t st);
 
-// Floats per (b,h,segment) state block written by the segment pass.
+// Floats per state block written by the segment-state pass.
 inline int64_t lin_state_floats(int64_t D, bool ccq) {
   // S (D x D), decay product, and for CCQ: M (D x D), m (D); padded to 64 floats
   int64_t n = D * D + 1 + (ccq ? D * D + D : 0);

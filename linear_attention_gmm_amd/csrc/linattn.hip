@@ -69,13 +69,14 @@ struct Args {
   const float* wl;  // [H][D]
   const float* bl;  // [H]
   void* out;
-  float* agg;  // [B*H][P][sfl]
+  float* agg;  // [B*H][P][sfl] state blocks
   int64_t N;
   int H;
-  int P;
-  int seg_len;
+  int P;         // state blocks per (b,h)
+  int seg_len;   // tokens per workgroup (a segment, or a sub-segment in the AGG pass)
   int sfl;
-  int has_init;  // chunk pass: start from the state block of the segment
+  int has_init;  // chunk pass: start from the state block R * (segment index)
+  int R;
 };
 
 // Waves per workgroup: 16 state columns per wave (8 waves, two per SIMD, at
@@ -720,8 +721,10 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
     }
 }
 
+// The bf16 segment-state pass is sized for two workgroups per CU (at D = 128:
+// four waves per SIMD, so at most 128 VGPRs).
 template <typename T, int D, bool CCQ, bool AGG>
-__global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
+__global__ __launch_bounds__(Waves<D>::NW * 64, AGG && sizeof(T) == 2 ? 4 : 1) void lin_kernel(Args a) {
   typedef Cfg<T, D, CCQ, AGG> C;
   constexpr int NW = C::NW, NT = NW * 64, CT = C::CT, DT = C::DT;
 
@@ -776,7 +779,7 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
   if constexpr (!AGG) {
     // state at the segment start (exclusive prefix written by the segment scan)
     if (a.has_init) {
-      const float* blk = a.agg + ((size_t)bh * a.P + p) * a.sfl;
+      const float* blk = a.agg + ((size_t)bh * a.P + (size_t)a.R * p) * a.sfl;
 #pragma unroll
       for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
@@ -856,26 +859,28 @@ __global__ __launch_bounds__(Waves<D>::NW * 64) void lin_kernel(Args a) {
   }
 }
 
-// Segment scan over the per-segment state blocks of every sequence, in a fixed
-// order: block p becomes the state at the start of segment p,
-//   S_in(p) = G_{p-1} S_in(p-1) + S_{p-1},   M_in(p) = M_in(p-1) + M_{p-1},
-//   m_in(p) = m_in(p-1) + m_{p-1},           S_in(0) = M_in(0) = m_in(0) = 0,
-// with G_p the decay product of segment p (left in place). Blocks 0 .. P-2 hold
-// the segment states on entry.
-__global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ agg, int P, int sfl, int D, int ccq) {
+// Scan over the sub-segment state blocks of every sequence, in a fixed order.
+// Blocks 0 .. nsub-1 hold the states of consecutive sub-segments (R per
+// segment) on entry; block R p becomes the state at the start of segment p:
+//   S_run <- G_q S_run + S_q,  M_run <- M_run + M_q,  m_run <- m_run + m_q
+// over sub-segments q (from zero), with G_q the decay product of sub-segment q
+// (left in place).
+__global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ agg, int slots, int nsub, int R, int sfl,
+                                                   int D, int ccq) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int nS = D * D;
   const int nTot = ccq ? 2 * D * D + 1 + D : D * D + 1;
   if (e >= nTot || e == nS) return;
-  float* base = agg + (size_t)bh * P * sfl;
+  float* base = agg + (size_t)bh * slots * sfl;
   float run = 0.f;
-  for (int pp = 0; pp < P; ++pp) {
-    float* xp = base + (size_t)pp * sfl + e;
-    const float t = pp < P - 1 ? *xp : 0.f;
-    *xp = run;
-    if (pp < P - 1) run = e < nS ? base[(size_t)pp * sfl + nS] * run + t : run + t;
+  for (int q = 0; q < nsub; ++q) {
+    float* xp = base + (size_t)q * sfl + e;
+    const float t = *xp;
+    if (q % R == 0) *xp = run;
+    run = e < nS ? base[(size_t)q * sfl + nS] * run + t : run + t;
   }
+  base[(size_t)nsub * sfl + e] = run;
 }
 
 template <typename T, int D, bool CCQ, bool AGG>
@@ -898,20 +903,24 @@ static hipError_t launch_d(const LinLaunch& L, hipStream_t st) {
   a.agg = L.agg;
   a.N = L.N;
   a.H = (int)L.H;
-  a.P = (int)L.P;
-  a.seg_len = (int)L.seg_len;
   a.sfl = (int)lin_state_floats(D, CCQ);
   a.has_init = 0;
+  a.R = (int)L.R;
+  a.P = (int)(L.R * L.P);  // state blocks per (b,h)
   const unsigned BH = (unsigned)(L.B * L.H);
   if (L.P > 1) {
-    hipError_t e = launch_one<T, D, CCQ, true>(a, (unsigned)(L.P - 1), BH, st);
+    // sub-segment states of segments 0 .. P-2, then their prefixes
+    const int nsub = (int)(L.R * (L.P - 1));
+    a.seg_len = (int)(L.seg_len / L.R);
+    hipError_t e = launch_one<T, D, CCQ, true>(a, (unsigned)nsub, BH, st);
     if (e != hipSuccess) return e;
     const int n = CCQ ? 2 * D * D + 1 + D : D * D + 1;
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((n + 255) / 256), BH), dim3(256), 0, st, L.agg, (int)L.P, a.sfl,
-                       D, CCQ ? 1 : 0);
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((n + 255) / 256), BH), dim3(256), 0, st, L.agg, a.P, nsub, a.R,
+                       a.sfl, D, CCQ ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     a.has_init = 1;
   }
+  a.seg_len = (int)L.seg_len;
   return launch_one<T, D, CCQ, false>(a, (unsigned)L.P, BH, st);
 }
 

@@ -123,6 +123,15 @@ def test_ccq_bf16_lowrank_sampled():
     assert_close(got, ref, "bf16", "ccq bf16 low-rank keys sampled slices")
 
 
+@pytest.mark.parametrize("segments", [3, 4])
+def test_ccq_bf16_sub_segments(segments):
+    # N = 768 is 12 chunks: 3 segments of 4 chunks (two sub-segments each in the
+    # segment-state pass) and 4 segments of 3 chunks (one each)
+    cfg = inputs.CONFIGS["ccq_bf16_n16k"].replace(name="ccq_bf16_sub", B=1, H=2, N=768)
+    got, ref = _ccq(cfg, segments=segments)
+    assert_close(got, ref, "bf16", "ccq bf16 N=768 P=%d" % segments)
+
+
 def test_ccq_segment_invariance_fp32():
     cfg = inputs.LinAttnConfig("ccq_seg", 303, B=1, H=2, N=2048, dk=64, dv=64, dtype="f32", lowrank_keys=4,
                                gate_bias=2.0)
