@@ -46,6 +46,7 @@ namespace lin {
 constexpr int kC = 64;
 constexpr int kLds = 160 * 1024;
 constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kLazy = 64.f;
 
 // B operand (CHAIN order, token step s) of the lower-triangular ones matrix for
 // query q of the chunk: entry (token j, query q) is 1 where j <= q.
@@ -177,13 +178,19 @@ __device__ __forceinline__ float ld_nat8(const float* base, int pitch, int rc, i
   return ld_kc_nat(base, pitch, rc, kstep);
 }
 
-// Decay weights 2^(l_last - l_j) of the token entries (CHAIN order, step s)
-// this lane holds in k-major fragments; the same for every column tile.
+// Decay weights of the token entries (CHAIN order, step s) this lane holds in
+// k-major fragments, read from the per-token weights in LDS; the same for
+// every column tile.
 template <typename T>
 struct DecayW {
   static constexpr int NE = sizeof(T) == 2 ? 8 : 1;
   float w[NE];
-  __device__ __forceinline__ void init(const float* sl, float l_last, int s) {
+  __device__ __forceinline__ void init(const float* wt, int s) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) w[i] = wt[chain_k<T>(s, i)];
+  }
+  // From the cumulative decays instead: 2^(l_last - l_j).
+  __device__ __forceinline__ void init_exp(const float* sl, float l_last, int s) {
 #pragma unroll
     for (int i = 0; i < NE; ++i) w[i] = fast_exp2(l_last - sl[chain_k<T>(s, i)]);
   }
@@ -257,6 +264,10 @@ struct State {
   f32x4 Mst[CCQ ? C::DT : 1][CCQ ? C::CT : 1];
   float mreg[C::CT];  // running key sum of column cbase + 16 ct + c16
   float lseg;         // AGG: log2 of the segment's decay product
+  // The decayed state is held lazily: S_true = 2^ls S. The chunk decay is
+  // folded into the weights of the new terms until ls would drop below
+  // -kLazy, and only then multiplied into S (bounded weights, no overflow).
+  float ls;
   int64_t t_prev;     // chunk whose outputs wait in the staging tile
 };
 
@@ -326,13 +337,14 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
     const char* Vt = tile_v<C, AGG>(cur);
 
     // cumulative log2 decay of this chunk (each wave keeps a private copy)
-    float l_last;
+    float l_last, l_mine;  // chunk total; this lane's token (lane = token)
     {
       // log2 g in hardware (g in (0, 1]; g = 0 gives -inf, clamped)
       float x = l < nvalid ? fmaxf(__builtin_amdgcn_logf(tile_g<C>(cur)[l]), -200.f) : 0.f;
       x = wave_scan_incl(x);
-      sLw[l] = x;
+      l_mine = x;
       l_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), kC - 1));
+      sLw[l] = x;
     }
     __builtin_amdgcn_wave_barrier();
 
@@ -450,8 +462,18 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
         //   delta_i = -alpha_i (M_prev q_i + sum_j k_j P_ij) + beta_i (sum_{j<=i} k_j + m_prev)
         // (P masked to j <= i). The prefix sum of keys is a product with the
         // lower-triangular ones matrix, built in registers.
-        const float gate_bias = gate_b;
-        const float t0f = (float)t0;
+        // gate and mean weights, lane = query (count t = t0 + lane + 1); each
+        // query tile picks its own by a lane permute
+        float alpha_l, beta_l;
+        {
+          const float2 wm = sWQ[l];
+          float rs = sRS[l];
+          if constexpr (C::SPLIT > 1) rs += sRS[kC + l];
+          const float lam = __builtin_amdgcn_rcpf(1.f + fast_exp2(-(wm.x + gate_b) * kLog2eF));
+          const float inv_t = __builtin_amdgcn_rcpf((float)t0 + (float)(l + 1));
+          alpha_l = lam * inv_t;
+          beta_l = alpha_l * (wm.y + rs) * inv_t;
+        }
         // bf16 diagonal blocks of the mask (tokens 32 s' .. 32 s' + 31 against
         // query tile qt with s' = qt / 2): tri0 for even qt, tri1 for odd qt
         frag ones, tri0, tri1;
@@ -497,9 +519,8 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
               for (int s = 0; s < C::NKT; ++s) pf[s] = ld_kc_chain(sP, C::PP, q, s);
             }
-            const float2 wm = sWQ[q];
-            float rs = sRS[q];
-            if constexpr (C::SPLIT > 1) rs += sRS[kC + q];
+            const float alpha = __shfl(alpha_l, q);
+            const float beta = __shfl(beta_l, q);
             if constexpr (HOIST) __builtin_amdgcn_sched_barrier(0);
             f32x4 mqv = zero4();
 #pragma unroll
@@ -519,11 +540,6 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
                 }
                 kc = M::mma(KTc[ct][s], tri, kc);
               }
-            // gate and mean weights of this lane's query (count t = t0 + q + 1)
-            const float lam = __builtin_amdgcn_rcpf(1.f + fast_exp2(-(wm.x + gate_bias) * kLog2eF));
-            const float inv_t = __builtin_amdgcn_rcpf(t0f + (float)(q + 1));
-            const float alpha = lam * inv_t;
-            const float beta = alpha * (wm.y + rs) * inv_t;
             f32x4 v;
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = beta * (kc[r] + mprev[r]) - alpha * (mqv[r] + kp[r]);
@@ -623,7 +639,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
             for (int ct = 0; ct < CT; ++ct) acc[ct] = M::mma(Vf[ct][s], pf, acc[ct]);
           }
         }
-        const float bq = fast_exp2(sLw[q]);
+        const float bq = fast_exp2(sLw[q] + st.ls);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int c0 = cbase + 16 * ct;
@@ -638,18 +654,40 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
       t_prev = t0;
     }
 
-    // ---- state updates: S <- 2^l_last S + K^T (w V), M += K^T K, m += sum K
+    // ---- state updates: S <- 2^l_last S + K^T (w V), M += K^T K, m += sum K,
+    //      with S held as 2^ls S:
+    //        lazy : ls <- ls + l_last,  S <- S + K^T (2^(-ls_prev - l_j) V)
+    //        eager: S <- 2^(ls + l_last) S + K^T (2^(l_last - l_j) V),  ls <- 0
+    //      (the lazy weights stay below 2^kLazy)
     {
-      const float b_last = fast_exp2(l_last);
+      const float ls_next = st.ls + l_last;
+      float wb;
+      // (the segment pass, sized for 128 registers, always scales eagerly)
+      if (AGG || ls_next < -kLazy) {
+        const float b = fast_exp2(ls_next);
 #pragma unroll
-      for (int kt = 0; kt < DT; ++kt)
+        for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) S[kt][ct] *= b_last;
+          for (int ct = 0; ct < CT; ++ct) S[kt][ct] *= b;
+        st.ls = 0.f;
+        wb = l_last;
+      } else {
+        wb = -st.ls;
+        st.ls = ls_next;
+      }
+      // per-token weights replace this wave's cumulative decays in LDS
+      if constexpr (!AGG) {
+        sLw[l] = fast_exp2(wb - l_mine);
+        __builtin_amdgcn_wave_barrier();
+      }
       frag Vw[CT][C::NKT];
 #pragma unroll
       for (int s = 0; s < C::NKT; ++s) {
         DecayW<T> dw;
-        dw.init(sLw, l_last, s);
+        if constexpr (AGG)
+          dw.init_exp(sLw, l_last, s);
+        else
+          dw.init(sLw, s);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) Vw[ct][s] = dw.apply(tl_kmaj_t<CPR, T>(Vt, s, cbase + 16 * ct));
       }
@@ -770,6 +808,7 @@ __global__ __launch_bounds__(Waves<D>::NW * 64, AGG && sizeof(T) == 2 ? 4 : 1) v
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) st.mreg[ct] = 0.f;
   st.lseg = 0.f;
+  st.ls = 0.f;
   st.t_prev = -1;
 
   if constexpr (C::NBUF == 2) {
@@ -839,6 +878,7 @@ __global__ __launch_bounds__(Waves<D>::NW * 64, AGG && sizeof(T) == 2 ? 4 : 1) v
 
   if constexpr (AGG) {
     float* blk = a.agg + ((size_t)bh * a.P + p) * a.sfl;
+    const float sfin = exp2f(st.ls);
 #pragma unroll
     for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
@@ -846,7 +886,7 @@ __global__ __launch_bounds__(Waves<D>::NW * 64, AGG && sizeof(T) == 2 ? 4 : 1) v
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * kt + 4 * g + r, col = cbase + 16 * ct + c16;
-          blk[row * D + col] = st.S[kt][ct][r];
+          blk[row * D + col] = st.S[kt][ct][r] * sfin;
           if constexpr (CCQ) blk[D * D + 1 + row * D + col] = st.Mst[kt][ct][r];
         }
     if (w == 0 && l == 0) blk[D * D] = exp2f(st.lseg);
