@@ -73,6 +73,7 @@ class LinAttnConfig:
     dtype: str = "bf16"
     chunk: int = 64
     g_one: bool = False  # decay identically 1
+    g_logit_mean: float = 3.0  # decay g = sigmoid(N(g_logit_mean, 1))
     lowrank_keys: int = 0  # >0: keys = U z + 0.1 n with rank-r U (unnormalised)
     gate_bias: float = -2.0
 
@@ -198,7 +199,7 @@ def linattn_inputs(cfg: LinAttnConfig, N: Optional[int] = None, ccq: bool = Fals
         if cfg.g_one:
             gs = np.ones(N)
         else:
-            gs = 1.0 / (1.0 + np.exp(-(3.0 + _rng(cfg.cfg_id, T_G, b, h).standard_normal(N))))
+            gs = 1.0 / (1.0 + np.exp(-(cfg.g_logit_mean + _rng(cfg.cfg_id, T_G, b, h).standard_normal(N))))
         q[b, h] = _to(qs, cfg.dtype)
         k[b, h] = _to(ks, cfg.dtype)
         v[b, h] = _to(vs, cfg.dtype)
