@@ -178,6 +178,29 @@ __device__ __forceinline__ float ld_nat8(const float* base, int pitch, int rc, i
   return ld_kc_nat(base, pitch, rc, kstep);
 }
 
+// Decay factors 2^(l_i - l_j) of the score tile (query tile qt, key tile
+// kt <= qt) for this lane's query i (cumulative log2 decay lq) and key rows
+// 16 kt + 4 g + r; zero above the diagonal. Off the diagonal the factor splits
+// at the tile's last key p = l_{16 kt + 15} into 2^(l_i - p) 2^(p - l_j), both
+// at most 1 (five exponentials instead of sixteen). On the diagonal the
+// exponent is clamped to <= 0 before the mask, so that masked entries cannot
+// overflow.
+__device__ __forceinline__ f32x4 decay_tile(const float* sl, float lq, int kt, int qt) {
+  const int g = lane_id() >> 4, c16 = lane_id() & 15;
+  const f32x4 lk = *reinterpret_cast<const f32x4*>(sl + 16 * kt + 4 * g);
+  f32x4 d;
+  if (kt < qt) {
+    const float p = sl[16 * kt + 15];
+    const float a = fast_exp2(lq - p);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[r] = a * fast_exp2(p - lk[r]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[r] = 4 * g + r <= c16 ? fast_exp2(fminf(lq - lk[r], 0.f)) : 0.f;
+  }
+  return d;
+}
+
 // Decay weights of the token entries (CHAIN order, step s) this lane holds in
 // k-major fragments, read from the per-token weights in LDS; the same for
 // every column tile.
@@ -436,10 +459,8 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
           for (int j = 0; j < C::KPW; ++j) {
             const int kt = Wv::ktile(w, j);
-            const f32x4 lk = *reinterpret_cast<const f32x4*>(sLw + 16 * kt + 4 * g);
-            f32x4 v;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = kt <= qt ? Pr[qi][j][r] * fast_exp2(lq - lk[r]) : 0.f;
+            f32x4 v = zero4();
+            if (kt <= qt) v = Pr[qi][j] * decay_tile(sLw, lq, kt, qt);
             put4v<T>(prow + 16 * kt + 4 * g, v);
           }
         }
@@ -581,12 +602,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
               for (int ks = 0; ks < C::NKD; ++ks)
                 acc = M::mma(HOIST ? KF[HOIST ? j : 0][HOIST ? ks : 0] : tl_nat_t<CPR, T>(Kt, 16 * kt + c16, ks), DF[ks],
                              acc);
-              const f32x4 lk = *reinterpret_cast<const f32x4*>(sLw + 16 * kt + 4 * g);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const bool in = kt < qt || 4 * g + r <= c16;
-                v[r] = in ? acc[r] * fast_exp2(lq - lk[r]) : 0.f;
-              }
+              v = acc * decay_tile(sLw, lq, kt, qt);
             }
             put4v<T>(prow + 16 * kt + 4 * g, v);
           }

@@ -193,8 +193,11 @@ __device__ __forceinline__ u32x4 buf_desc(const void* base, uint32_t nbytes) {
   d[3] = 0x00020000u;
   return d;
 }
+// LDS byte address of a generic pointer into LDS: its low 32 bits (the high
+// half is the shared aperture). Taken directly rather than by an address-space
+// cast, whose null-pointer check the backend can mis-lower.
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((unsigned)reinterpret_cast<uintptr_t>((LM_LDS const char*)p));
+  return __builtin_amdgcn_readfirstlane((unsigned)reinterpret_cast<uintptr_t>(p));
 }
 
 // Direct global->LDS transfers written as inline asm: LDS[dst + 16 lane] (or

@@ -54,11 +54,12 @@ def test_gla_fp32(dk, segments):
     assert_close(got, ref, "f32", "gla fp32 dk=%d P=%d" % (dk, segments))
 
 
-@pytest.mark.parametrize("g_logit_mean", [1.0, -1.0])
+@pytest.mark.parametrize("g_logit_mean", [1.0, -1.0, -30.0])
 @pytest.mark.parametrize("ccq", [False, True])
 def test_strong_decay_fp32(g_logit_mean, ccq):
     # g ~ 0.7 and g ~ 0.3 per token: the decay of the carried state is applied
-    # both lazily (folded into later weights) and eagerly within a few chunks
+    # both lazily (folded into later weights) and eagerly within a few chunks;
+    # g ~ 1e-13: decay ratios across a chunk far beyond the float range
     cfg = inputs.LinAttnConfig("decay_fp32", 205, B=1, H=2, N=700, dk=64, dv=64, dtype="f32",
                                g_logit_mean=g_logit_mean, lowrank_keys=4 if ccq else 0, gate_bias=2.0)
     got, ref = (_ccq(cfg, segments=3) if ccq else _gla(cfg, segments=3))
