@@ -129,6 +129,10 @@ struct Cfg {
   // targets from the others and does not wait for an outstanding DMA at every
   // LDS access). Unused ones keep a token size.
   static constexpr int b_xk = HK ? XB : 16;
+  // AGG (keys only) double-buffers the key tile: its DMA is issued two chunks
+  // ahead, a whole chunk before it is needed.
+  static constexpr bool XDB = MODE == AGG;
+  static constexpr int b_xk1 = XDB ? XB : 16;
   static constexpr int b_xq = HQ ? XB : 16;
   static constexpr int b_v = HK ? XB : 16;
   static constexpr int b_g = NS * XB > NS * GB ? NS * XB : NS * GB;  // x*x tiles, later Gamma tiles
@@ -137,7 +141,7 @@ struct Cfg {
   static constexpr int b_st = HQ ? SB : 16;            // bf16 state snapshot Vtil^T [D][KP]
   static constexpr int b_sk = HK ? NW * 64 * 8 : 16;   // key stats [NW][64] (max, sum)
   static constexpr int b_sq = HQ ? NW * 64 * 16 : 16;  // query stats [NW][64] (max, sum, Z-dot)
-  static constexpr int lds = b_xk + b_xq + b_v + b_g + b_st + b_sk + b_sq;
+  static constexpr int lds = b_xk + b_xk1 + b_xq + b_v + b_g + b_st + b_sk + b_sq;
   static_assert(lds <= 80 * 1024, "two workgroups per CU");
   static_assert(XC % NW == 0 && KP % 64 == 0 && D % 32 == 0, "shape");
 };
@@ -265,13 +269,14 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
   typedef Mma<bf16> M;
   constexpr int RT = C::RT, DT = C::DT, NKC = C::NKC;
   __shared__ __attribute__((aligned(16))) char sXK[C::b_xk];
+  __shared__ __attribute__((aligned(16))) char sXK1[C::b_xk1];
   __shared__ __attribute__((aligned(16))) char sXQ[C::b_xq];
   __shared__ __attribute__((aligned(16))) char sV[C::b_v];
   __shared__ __attribute__((aligned(16))) char sG[C::b_g];
   __shared__ __attribute__((aligned(16))) char sST[C::b_st];
   __shared__ __attribute__((aligned(16))) float2 stK[C::b_sk / 8];
   __shared__ __attribute__((aligned(16))) f32x4 stQ[C::b_sq / 16];
-  const Tiles tl{sXK, sG + C::o_x2k, sXQ, sG + C::o_x2q};
+  Tiles tl{sXK, sG + C::o_x2k, sXQ, sG + C::o_x2q};
 
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int bh = blockIdx.y, p = blockIdx.x;
@@ -333,7 +338,13 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
       dma_issue<D, C::INSTR>(sV, Vg + (size_t)t_begin * D, rows, voff);
     }
     if constexpr (C::HQ) dma_issue<D, C::INSTR>(sXQ, Qg + (size_t)t_begin * D, rows, voff);
-    wait_vmem();
+    if (C::XDB && t_begin + kChunk < t_end) {
+      const int64_t t1 = t_begin + kChunk;
+      dma_issue<D, C::INSTR>(sXK1, Kg + (size_t)t1 * D, (int)((N - t1) < kChunk ? (N - t1) : kChunk), voff);
+      LM_WAIT_VMEM(C::INSTR);
+    } else {
+      wait_vmem();
+    }
     if constexpr (C::HK) square_rows<D>(sXK, sG + C::o_x2k);
     if constexpr (C::HQ) square_rows<D>(sXQ, sG + C::o_x2q);
     lds_barrier();
@@ -345,10 +356,16 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.f;
 
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kChunk) {
+  int it = 0;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kChunk, ++it) {
     const int nvalid = (int)((N - t0) < kChunk ? (N - t0) : kChunk);
     const bool more = t0 + kChunk < t_end;
     const int rows_next = more ? (int)((N - t0 - kChunk) < kChunk ? (N - t0 - kChunk) : kChunk) : 0;
+    // key tile of this chunk and of the next (double-buffered in AGG)
+    char* xk_cur = (C::XDB && (it & 1)) ? sXK1 : sXK;
+    char* xk_nxt = (C::XDB && !(it & 1)) ? sXK1 : sXK;
+    tl.xk = xk_cur;
+    const bool more2 = C::XDB && t0 + 2 * kChunk < t_end;
 
     // ---- 1. routing and wave-local softmax statistics
     f32x4 Lk[4][RT], Lq[4][RT];
@@ -433,14 +450,21 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
         for (int rt = 0; rt < RT; ++rt)
           put4<C::GC>(sG + C::o_gq, 16 * ct + c16, comp0 + 16 * rt + 4 * g, Lq[ct][rt] * f[ct]);
     }
-    // next chunk's X tiles (their old contents died at the barrier above)
-    if (more) {
+    // next chunk's X tiles (their old contents died at the barrier above); in
+    // AGG the key tile after next, into this chunk's key buffer
+    if constexpr (C::XDB) {
+      if (more2) {
+        const int64_t t2 = t0 + 2 * kChunk;
+        dma_issue<D, C::INSTR>(xk_cur, Kg + (size_t)t2 * D, (int)((N - t2) < kChunk ? (N - t2) : kChunk), voff);
+      }
+    } else if (more) {
       if constexpr (C::HK) dma_issue<D, C::INSTR>(sXK, Kg + (size_t)(t0 + kChunk) * D, rows_next, voff);
       if constexpr (C::HQ) dma_issue<D, C::INSTR>(sXQ, Qg + (size_t)(t0 + kChunk) * D, rows_next, voff);
     }
     if constexpr (C::HK) {
-      // V of this chunk: its DMA was issued before the next chunk's X tiles
-      if (more)
+      // V of this chunk: its DMA was issued before the X tiles just issued (in
+      // AGG also the next key tile, issued a chunk ago, is waited for here)
+      if (C::XDB ? more2 : more)
         LM_WAIT_VMEM(C::INSTR * (C::HQ ? 2 : 1));
       else
         wait_vmem();
@@ -449,8 +473,9 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
 
     // ---- 3. read (query tile w) and update (this wave's components). The W
     // fragments for the next chunk are fetched now; they are waited for with
-    // the next chunk's tiles.
-    if (more) load_w<C>(Wf, wrow);
+    // the next chunk's tiles. AGG keeps them in registers instead: a wait for
+    // loads issued here would also wait for the tile DMA issued after them.
+    if (!C::XDB && more) load_w<C>(Wf, wrow);
     bf16x8 VB[DT][2];
     if constexpr (C::HK) {
 #pragma unroll
@@ -536,12 +561,15 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
     }
     if (more) {
       if constexpr (C::HK) {
+        // Next X tiles and the W fragments first (AGG: the key tile landed
+        // earlier), then the V DMA: issued after the wait, the V tile is not
+        // waited for by the compiler's own wait for W at the next routing.
+        if constexpr (!C::XDB) wait_vmem();
         dma_issue<D, C::INSTR>(sV, Vg + (size_t)(t0 + kChunk) * D, rows_next, voff);
-        LM_WAIT_VMEM(C::INSTR);
       } else {
         wait_vmem();
       }
-      if constexpr (C::HK) square_rows<D>(sXK, sG + C::o_x2k);
+      if constexpr (C::HK) square_rows<D>(xk_nxt, sG + C::o_x2k);
       if constexpr (C::HQ) square_rows<D>(sXQ, sG + C::o_x2q);
     }
     lds_barrier();
