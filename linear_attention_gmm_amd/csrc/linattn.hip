@@ -627,35 +627,9 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
         for (int s = 0; s < C::NKT; ++s) Vf[ct][s] = tl_kmaj_t<CPR, T>(Vt, s, cbase + 16 * ct);
       }
-#pragma unroll 1
-      for (int qt = 0; qt < 4; ++qt) {
-        const int q = 16 * qt + c16;
-        f32x4 inter[CT], acc[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          inter[ct] = zero4();
-          acc[ct] = zero4();
-        }
-#pragma unroll
-        for (int s = 0; s < C::NKD; ++s) {
-          const frag qf = tl_chain_t<CPR, T>(Qt, 16 * qt + c16, s);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) inter[ct] = M::mma(Sc[ct][s], qf, inter[ct]);
-          if constexpr (CCQ) {
-            const frag df = ld_kc_chain(sD, C::PDD, q, s);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) inter[ct] = M::mma(Sc[ct][s], df, inter[ct]);
-          }
-        }
-#pragma unroll
-        for (int s = 0; s < C::NKT; ++s) {
-          if ((s * M::KS) / 16 <= qt) {
-            const frag pf = ld_kc_chain(sP, C::PP, q, s);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) acc[ct] = M::mma(Vf[ct][s], pf, acc[ct]);
-          }
-        }
-        const float bq = fast_exp2(sLw[q] + st.ls);
+      // Output of query q for this wave's column tiles.
+      auto emit = [&](int q, const f32x4 (&acc)[CT], const f32x4 (&inter)[CT], float lq) {
+        const float bq = fast_exp2(lq + st.ls);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int c0 = cbase + 16 * ct;
@@ -665,6 +639,84 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
           } else if (q < nvalid) {
             put4v<T>(Og + (size_t)(t0 + q) * D + c0 + 4 * g, o);
           }
+        }
+      };
+      if constexpr (sizeof(T) == 2 && C::NKD >= 2 && C::NKT == 2) {
+        // Software pipeline over half query tiles (k-steps 0 .. NKD/2-1, then
+        // the rest): the LDS operands of step i+1 are requested before the
+        // products of step i, with the register footprint of one whole tile.
+        constexpr int HS = C::NKD / 2;
+        struct Ops {
+          frag q[HS], d[HS], p;
+          float lq;
+        };
+        auto load = [&](int step, Ops& o) {
+          const int qt = step >> 1, h = step & 1, q = 16 * qt + c16;
+#pragma unroll
+          for (int i = 0; i < HS; ++i) {
+            o.q[i] = tl_chain_t<CPR, T>(Qt, q, HS * h + i);
+            if constexpr (CCQ) o.d[i] = ld_kc_chain(sD, C::PDD, q, HS * h + i);
+          }
+          if ((h * M::KS) / 16 <= qt) o.p = ld_kc_chain(sP, C::PP, q, h);
+          if (h == 1) o.lq = sLw[q];
+        };
+        Ops ops[2];
+        load(0, ops[0]);
+        f32x4 inter[CT], acc[CT];
+#pragma unroll
+        for (int step = 0; step < 8; ++step) {
+          const int qt = step >> 1, h = step & 1;
+          if (step + 1 < 8) load(step + 1, ops[(step + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          const Ops& o = ops[step & 1];
+          if (h == 0) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              inter[ct] = zero4();
+              acc[ct] = zero4();
+            }
+          }
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+            for (int i = 0; i < HS; ++i) {
+              inter[ct] = M::mma(Sc[ct][HS * h + i], o.q[i], inter[ct]);
+              if constexpr (CCQ) inter[ct] = M::mma(Sc[ct][HS * h + i], o.d[i], inter[ct]);
+            }
+            if ((h * M::KS) / 16 <= qt) acc[ct] = M::mma(Vf[ct][h], o.p, acc[ct]);
+          }
+          if (h == 1) emit(16 * qt + c16, acc, inter, o.lq);
+        }
+      } else {
+#pragma unroll 1
+        for (int qt = 0; qt < 4; ++qt) {
+          const int q = 16 * qt + c16;
+          f32x4 inter[CT], acc[CT];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            inter[ct] = zero4();
+            acc[ct] = zero4();
+          }
+#pragma unroll
+          for (int s = 0; s < C::NKD; ++s) {
+            const frag qf = tl_chain_t<CPR, T>(Qt, 16 * qt + c16, s);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) inter[ct] = M::mma(Sc[ct][s], qf, inter[ct]);
+            if constexpr (CCQ) {
+              const frag df = ld_kc_chain(sD, C::PDD, q, s);
+#pragma unroll
+              for (int ct = 0; ct < CT; ++ct) inter[ct] = M::mma(Sc[ct][s], df, inter[ct]);
+            }
+          }
+#pragma unroll
+          for (int s = 0; s < C::NKT; ++s) {
+            if ((s * M::KS) / 16 <= qt) {
+              const frag pf = ld_kc_chain(sP, C::PP, q, s);
+#pragma unroll
+              for (int ct = 0; ct < CT; ++ct) acc[ct] = M::mma(Vf[ct][s], pf, acc[ct]);
+            }
+          }
+          emit(q, acc, inter, sLw[q]);
         }
       }
       t_prev = t0;
