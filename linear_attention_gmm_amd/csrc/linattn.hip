@@ -141,6 +141,9 @@ struct Cfg {
   static constexpr bool STAGE_O = !AGG && o_o + o_bytes + BUF <= kLds;
   static constexpr int o_buf = (o_o + (STAGE_O ? o_bytes : 0) + 15) / 16 * 16;
   static constexpr int NBUF = o_buf + 2 * BUF <= kLds ? 2 : 1;
+  // bf16 CCQ: the S^T q half of the read is formed in phase 3 from the Q
+  // fragments read there (Q is then read once per chunk instead of twice).
+  static constexpr bool IQ = CCQ && !AGG && ES == 2 && NKD >= 2 && CT == 1;
   static constexpr int lds = o_buf + NBUF * BUF;
   static_assert(lds <= kLds, "LDS budget");
 };
@@ -382,6 +385,14 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
       if (pre) x.template issue_tile<2>(nxt, tn);
     }
 
+    // bf16 CCQ (IQ): bf16 snapshot of S and S^T q per query tile, from phase 3
+    // to the read
+    frag Sc_iq[C::IQ ? C::NKD : 1];
+    f32x4 Scol_iq[C::IQ ? DT : 1];
+    f32x4 iq[C::IQ ? 4 : 1];
+    (void)Sc_iq;
+    (void)Scol_iq;
+    (void)iq;
     if constexpr (!AGG) {
       const char* Qt = cur;
       // ---- phase 1: owned (query tile, key tile) pairs: raw scores; for CCQ the
@@ -498,7 +509,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
         // bf16 diagonal blocks of the mask (tokens 32 s' .. 32 s' + 31 against
         // query tile qt with s' = qt / 2): tri0 for even qt, tri1 for odd qt
         frag ones, tri0, tri1;
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (sizeof(T) == 2 && !C::IQ) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int j = chain_k<T>(0, i);
@@ -510,6 +521,13 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
         (void)ones;
         (void)tri0;
         (void)tri1;
+        if constexpr (C::IQ) {
+          // S^T q of the read, with the bf16 snapshot of S (unchanged until the update)
+#pragma unroll
+          for (int kt = 0; kt < DT; ++kt) Scol_iq[kt] = S[kt][0];
+#pragma unroll
+          for (int s2 = 0; s2 < C::NKD; ++s2) Sc_iq[s2] = M::chain(Scol_iq, s2);
+        }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int c0 = cbase + 16 * ct;
@@ -527,8 +545,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
           float mprev[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) mprev[r] = sMv[c0 + 4 * g + r];
-#pragma unroll 1
-          for (int qt = 0; qt < 4; ++qt) {
+          auto delta_tile = [&](const int qt) {
             const int q = 16 * qt + c16;
             // bf16: every operand of this query tile is requested before the
             // first product (one LDS round trip); fp32 operands are read where used.
@@ -547,13 +564,21 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
             for (int s = 0; s < C::NKD; ++s)
               mqv = M::mma(Mh[s], HOIST ? qf[HOIST ? s : 0] : tl_chain_t<CPR, T>(Qt, q, s), mqv);
+            if constexpr (C::IQ) {
+              f32x4 a = zero4();
+#pragma unroll
+              for (int s = 0; s < C::NKD; ++s) a = M::mma(Sc_iq[s], qf[HOIST ? s : 0], a);
+              iq[qt] = a;
+            }
             f32x4 kp = zero4(), kc = zero4();
 #pragma unroll
             for (int s = 0; s < C::NKT; ++s)
               if ((s * M::KS) / 16 <= qt) {
                 kp = M::mma(KTc[ct][s], HOIST ? pf[HOIST ? s : 0] : ld_kc_chain(sP, C::PP, q, s), kp);
                 frag tri;
-                if constexpr (HOIST) {
+                if constexpr (C::IQ) {
+                  tri = tri_frag<T>(s, q);  // (qt is a constant here: unrolled)
+                } else if constexpr (HOIST) {
                   // whole 32-token blocks below the diagonal are all ones
                   tri = (s + 1) * M::KS <= 16 * qt ? ones : ((qt & 1) ? tri1 : tri0);
                 } else {
@@ -565,10 +590,17 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = beta * (kc[r] + mprev[r]) - alpha * (mqv[r] + kp[r]);
             put4v<T>(sD + q * C::PDD + c0 + 4 * g, v);
+            if constexpr (C::IQ) __builtin_amdgcn_sched_barrier(0);  // one query tile at a time
+          };
+          if constexpr (C::IQ) {
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt) delta_tile(qt);
+          } else {
+#pragma unroll 1
+            for (int qt = 0; qt < 4; ++qt) delta_tile(qt);
           }
         }
         lds_barrier();  // delta complete; masked scores consumed
-        if (pre) x.template issue_tile<1>(nxt, tn);
 
         // ---- phase 4: owned score tiles with the cleaned query, decayed
 #pragma unroll
@@ -608,8 +640,10 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
           }
         }
         lds_barrier();  // decayed scores complete
+        // (K after phase 4 as well: a register reload there would also wait for it)
         if (pre) {
           x.template issue_tile<0>(nxt, tn);
+          x.template issue_tile<1>(nxt, tn);
           x.template issue_tile<3>(nxt, tn);
         }
       }
@@ -619,11 +653,16 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
       frag Sc[CT][C::NKD], Vf[CT][C::NKT];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        f32x4 Scol[DT];
+        if constexpr (C::IQ) {
 #pragma unroll
-        for (int kt = 0; kt < DT; ++kt) Scol[kt] = S[kt][ct];
+          for (int s = 0; s < C::NKD; ++s) Sc[ct][s] = Sc_iq[s];
+        } else {
+          f32x4 Scol[DT];
 #pragma unroll
-        for (int s = 0; s < C::NKD; ++s) Sc[ct][s] = M::chain(Scol, s);
+          for (int kt = 0; kt < DT; ++kt) Scol[kt] = S[kt][ct];
+#pragma unroll
+          for (int s = 0; s < C::NKD; ++s) Sc[ct][s] = M::chain(Scol, s);
+        }
 #pragma unroll
         for (int s = 0; s < C::NKT; ++s) Vf[ct][s] = tl_kmaj_t<CPR, T>(Vt, s, cbase + 16 * ct);
       }
@@ -654,7 +693,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
           const int qt = step >> 1, h = step & 1, q = 16 * qt + c16;
 #pragma unroll
           for (int i = 0; i < HS; ++i) {
-            o.q[i] = tl_chain_t<CPR, T>(Qt, q, HS * h + i);
+            if constexpr (!C::IQ) o.q[i] = tl_chain_t<CPR, T>(Qt, q, HS * h + i);
             if constexpr (CCQ) o.d[i] = ld_kc_chain(sD, C::PDD, q, HS * h + i);
           }
           if ((h * M::KS) / 16 <= qt) o.p = ld_kc_chain(sP, C::PP, q, h);
@@ -672,7 +711,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
           if (h == 0) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-              inter[ct] = zero4();
+              inter[ct] = C::IQ ? iq[C::IQ ? qt : 0] : zero4();
               acc[ct] = zero4();
             }
           }
@@ -680,7 +719,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
           for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
             for (int i = 0; i < HS; ++i) {
-              inter[ct] = M::mma(Sc[ct][HS * h + i], o.q[i], inter[ct]);
+              if constexpr (!C::IQ) inter[ct] = M::mma(Sc[ct][HS * h + i], o.q[i], inter[ct]);
               if constexpr (CCQ) inter[ct] = M::mma(Sc[ct][HS * h + i], o.d[i], inter[ct]);
             }
             if ((h * M::KS) / 16 <= qt) acc[ct] = M::mma(Vf[ct][h], o.p, acc[ct]);
