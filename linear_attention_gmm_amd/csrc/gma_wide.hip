@@ -1,0 +1,15 @@
+// gma_wide.hip -- the general GMA kernel instantiated for bf16 inputs with
+// d = dv = 128 and 256 (padded) components. It is built in its own translation
+// unit so that its MFMA accumulators can be kept in VGPRs (the other
+// instantiations are compiled without that option).
+#include "gma_generic.hpp"
+
+namespace lm {
+namespace gma {
+
+hipError_t wide_launch(const Args& a, int mode, int segments, unsigned BH, hipStream_t st) {
+  return launch_mode<bf16, 128, 4, 64>(a, mode, segments, BH, st);
+}
+
+}  // namespace gma
+}  // namespace lm

@@ -101,6 +101,36 @@ def test_gma_bf16_n16k_sampled():
     assert_close(got, ref, "bf16", "gma bf16 N=16384 causal, slices (0,0),(3,7)")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_gma_bf16_d128_k256_ragged(causal):
+    # the long-context shape (d = dv = 128, 256 components, mixture keys) at a
+    # small, ragged N over several segments
+    cfg = inputs.CONFIGS["gma_bf16_n128k"].replace(name="gma_bf16_wide", cfg_id=108, B=1, H=2, N=1000)
+    for seg in (1, 5):
+        got, ref = _run(cfg, causal=causal, segments=seg)
+        assert_close(got, ref, "bf16", "gma bf16 d=128 K=256 N=1000 causal=%d P=%d" % (causal, seg))
+
+
+def test_gma_bf16_n128k_sampled():
+    # the long-context workload at full size (B=1, H=16, N=131072); the oracle
+    # reads 192 sampled rows of one head (every token still writes)
+    cfg = inputs.CONFIGS["gma_bf16_n128k"]
+    x = inputs.gma_inputs(cfg)
+    N, h = cfg.N, 11
+    say("gma: %s N=%d causal=1 head %d, sampled rows" % (cfg.name, N, h))
+    d = cuda(x)
+    out = gma_forward(d["q"], d["k"], d["v"], d["mu"], d["log_var"], d["logit_pi"], causal=True, eps=cfg.eps)
+    torch.cuda.synchronize()
+    got = host(out)[0, h]
+    rows = np.r_[0:64, N // 2 - 32:N // 2 + 32, N - 64:N]
+    mask = np.zeros((1, 1, N), np.uint8)
+    mask[0, 0, rows] = 1
+    sel = lambda t: t[:, h:h + 1]
+    ref = oracle.gma_forward(sel(x["q"]), sel(x["k"]), sel(x["v"]), x["mu"][h:h + 1], x["log_var"][h:h + 1],
+                             x["logit_pi"][h:h + 1], causal=True, eps=cfg.eps, row_mask=mask)[0, 0]
+    assert_close(got[rows], ref[rows], "bf16", "gma bf16 N=131072 causal, head %d, sampled rows" % h)
+
+
 def test_gma_bf16_ragged_multiseg():
     cfg = inputs.GmaConfig("gma_bf16_ragged", 106, B=2, H=2, N=1000, d=64, K=128, dv=64, qk_scale=True)
     for causal in (True, False):
