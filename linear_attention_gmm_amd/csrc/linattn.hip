@@ -528,8 +528,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
 #pragma unroll
           for (int s2 = 0; s2 < C::NKD; ++s2) Sc_iq[s2] = M::chain(Scol_iq, s2);
         }
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
+        for (int ct = 0; ct < CT; ++ct) {  // (one column tile per wave)
           const int c0 = cbase + 16 * ct;
           // M_prev as the operand precision (bf16 for bf16 inputs): its rounding
           // perturbs q_clean by at most lambda |k|^2 2^-9 |q|, the size of the
