@@ -75,6 +75,8 @@ def _gma(L, **kw):
     (dict(d=128, dv=128, K=200, dt=binding.LM_F32), binding.LM_EUNSUPPORTED),
     (dict(wsb=16), binding.LM_EWORKSPACE),
     (dict(out=FAKE + 16), binding.LM_EINVAL),  # overlaps q
+    (dict(N=(1 << 30) + 1), binding.LM_EUNSUPPORTED),  # beyond the largest sequence
+    (dict(B=256, H=256), binding.LM_EUNSUPPORTED),  # beyond the largest B*H
 ])
 def test_gma_errors(kw, code):
     st, msg = _gma(binding.lib(), **kw)
@@ -111,6 +113,8 @@ def _lin(L, fn, **kw):
     (dict(dk=64, dv=128), binding.LM_EUNSUPPORTED),
     (dict(wsb=8), binding.LM_EWORKSPACE),
     (dict(out=FAKE + (2 << 30) + 64), binding.LM_EINVAL),  # overlaps v
+    (dict(N=(1 << 30) + 1), binding.LM_EUNSUPPORTED),  # beyond the largest sequence
+    (dict(B=256, H=256), binding.LM_EUNSUPPORTED),  # beyond the largest B*H
 ])
 def test_linattn_errors(fn, kw, code):
     st, msg = _lin(binding.lib(), fn, **kw)
