@@ -27,16 +27,21 @@
 //
 // MI355X design
 //  * Transposed formulation (lane = query token): products chain from registers.
-//  * A workgroup of NW waves owns one (b, h, segment). Wave w owns the value
-//    columns [w CW, (w+1) CW) of S and the same columns of the symmetric M,
-//    and query tiles {w, w + NW, ...} for the per-query work (raw scores, gate,
-//    mean terms, decay mask), which is done once per workgroup and handed to
-//    the other waves through LDS.
-//  * Q/K/V/g tiles arrive by direct global->LDS DMA into XOR-swizzled,
-//    double-buffered tiles; the next chunk is in flight while this one is
-//    computed. k-major operands use the gfx950 LDS transpose read.
-//  * A segment pass (AGG) and a prefix combine at segment start give enough
-//    workgroups for short B*H.
+//  * A workgroup of NW waves (8 at D = 128, two per SIMD) owns one (b, h,
+//    segment). Wave w owns the value columns [w CW, (w+1) CW) of S and the
+//    same columns of the symmetric M and of m, in fp32 registers. The
+//    per-query work (score tiles, gate and mean terms, decay mask) is shared
+//    out by (query tile, key tile) pairs (see Waves) and handed to the other
+//    waves through LDS; delta and the read are split by columns.
+//  * Q/K/V/g tiles arrive by direct global->LDS DMA (inline asm) into
+//    XOR-swizzled, double-buffered tiles; the next chunk's transfers are spread
+//    over the phases of this one. k-major operands use the gfx950 LDS
+//    transpose read.
+//  * The decay of S is applied lazily (see State::ls), and the decay factors
+//    of the score tiles never have a positive exponent (decay_tile).
+//  * A segment-state pass (AGG, two sub-segments per segment) and a prefix
+//    scan give the state at every segment start, so that B*H too small to
+//    fill the GPU is cut into independent segments.
 #include "mfma.hpp"
 #include "launch.hpp"
 
