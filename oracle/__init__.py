@@ -63,11 +63,12 @@ class Oracle:
         lib.oracle_gma_responsibilities.argtypes = [_D, _I, _I, _I, _D, _D, _D, _D]
         lib.oracle_gma_forward.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I,
                                            ctypes.c_int, ctypes.c_double,
-                                           ctypes.POINTER(ctypes.c_uint8)]
+                                           ctypes.POINTER(ctypes.c_uint8), _D, _D]
         lib.oracle_gma_brute.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I,
                                          ctypes.c_int, ctypes.c_double, _D]
-        lib.oracle_gla_forward.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I]
-        lib.oracle_ccq_forward.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I]
+        lib.oracle_gla_forward.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _D, _D]
+        lib.oracle_ccq_forward.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I, _D,
+                                           _D]
         lib.oracle_gla_chunkwise.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I]
         lib.oracle_ccq_chunkwise.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -87,21 +88,28 @@ class Oracle:
         return out
 
     def gma_forward(self, q, k, v, mu, log_var, logit_pi, causal: bool = True, eps: float = 1e-6,
-                    row_mask=None) -> np.ndarray:
+                    row_mask=None, state_in=None, return_state: bool = False):
         """Associative GMA. q, k [B,H,N,d]; v [B,H,N,dv]; mu, log_var [H,K,d];
-        logit_pi [H,K]. row_mask [B,H,N] (optional): rows to read, others NaN."""
+        logit_pi [H,K]. row_mask [B,H,N] (optional): rows to read, others NaN.
+        Causal only: state_in [B,H,K*dv+K] (optional) is the memory [Vtil | Z]
+        before the first token; return_state also returns the memory after the
+        last one (same layout)."""
         q, k, v, mu, lv, lp = map(_f64, (q, k, v, mu, log_var, logit_pi))
         B, H, N, d = q.shape
         dv = v.shape[-1]
         K = mu.shape[1]
+        if (state_in is not None or return_state) and not causal:
+            raise ValueError("the memory is carried by the causal form only")
         out = np.full((B, H, N, dv), np.nan)
         mask_p = None
         if row_mask is not None:
             rm = np.ascontiguousarray(np.asarray(row_mask, dtype=np.uint8).reshape(B, H, N))
             mask_p = rm.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+        sin = None if state_in is None else _f64(state_in).reshape(B, H, K * dv + K)
+        sout = np.empty((B, H, K * dv + K)) if return_state else None
         self.lib.oracle_gma_forward(_p(q), _p(k), _p(v), _p(mu), _p(lv), _p(lp), _p(out), B, H, N,
-                                    d, K, dv, int(causal), float(eps), mask_p)
-        return out
+                                    d, K, dv, int(causal), float(eps), mask_p, _p(sin), _p(sout))
+        return (out, sout) if return_state else out
 
     def gma_brute(self, q, k, v, mu, log_var, logit_pi, causal: bool = True, eps: float = 1e-6,
                   return_affinity: bool = False):
@@ -117,24 +125,37 @@ class Oracle:
                                   K, dv, int(causal), float(eps), _p(aff))
         return (out, aff) if return_affinity else out
 
-    def gla_forward(self, q, k, v, g) -> np.ndarray:
-        """Recurrent decayed linear attention: q, k [B,H,N,dk], v [B,H,N,dv], g [B,H,N]."""
+    def gla_forward(self, q, k, v, g, state_in=None, return_state: bool = False):
+        """Recurrent decayed linear attention: q, k [B,H,N,dk], v [B,H,N,dv], g [B,H,N].
+        state_in [B,H,dk*dv] (optional): S before the first token; return_state
+        also returns S after the last one."""
         q, k, v, g = map(_f64, (q, k, v, g))
         B, H, N, dk = q.shape
         dv = v.shape[-1]
         out = np.empty((B, H, N, dv))
-        self.lib.oracle_gla_forward(_p(q), _p(k), _p(v), _p(g), _p(out), B, H, N, dk, dv)
-        return out
+        sin = None if state_in is None else _f64(state_in).reshape(B, H, dk * dv)
+        sout = np.empty((B, H, dk * dv)) if return_state else None
+        self.lib.oracle_gla_forward(_p(q), _p(k), _p(v), _p(g), _p(out), B, H, N, dk, dv, _p(sin),
+                                    _p(sout))
+        return (out, sout) if return_state else out
 
-    def ccq_forward(self, q, k, v, g, w_lambda, b_lambda) -> np.ndarray:
-        """Recurrent CCQ read over decayed linear attention; w_lambda [H,dk], b_lambda [H]."""
+    def ccq_forward(self, q, k, v, g, w_lambda, b_lambda, t0: int = 0, state_in=None,
+                    return_state: bool = False):
+        """Recurrent CCQ read over decayed linear attention; w_lambda [H,dk], b_lambda [H].
+        state_in [B,H,dk*dv+dk*dk+dk] (optional): [S | M | m] after t0 earlier
+        tokens; return_state also returns the state after the last token."""
         q, k, v, g, w, b = map(_f64, (q, k, v, g, w_lambda, b_lambda))
         B, H, N, dk = q.shape
         dv = v.shape[-1]
+        ss = dk * dv + dk * dk + dk
+        if state_in is None and t0 != 0:
+            raise ValueError("t0 counts the tokens held by state_in")
         out = np.empty((B, H, N, dv))
+        sin = None if state_in is None else _f64(state_in).reshape(B, H, ss)
+        sout = np.empty((B, H, ss)) if return_state else None
         self.lib.oracle_ccq_forward(_p(q), _p(k), _p(v), _p(g), _p(w), _p(b), _p(out), B, H, N, dk,
-                                    dv)
-        return out
+                                    dv, int(t0), _p(sin), _p(sout))
+        return (out, sout) if return_state else out
 
     def gla_chunkwise(self, q, k, v, g, chunk: int = 64) -> np.ndarray:
         q, k, v, g = map(_f64, (q, k, v, g))

@@ -110,9 +110,14 @@ void oracle_gma_responsibilities(const double* x, int64_t N, int64_t d, int64_t 
 static void gma_slice(const double* q, const double* k, const double* v, const double* mu,
                       const double* log_var, const double* logit_pi, double* out, int64_t N,
                       int64_t d, int64_t K, int64_t dv, int causal, double eps,
-                      const uint8_t* row_mask) {
+                      const uint8_t* row_mask, const double* mem_in, double* mem_out) {
   double* vt = (double*)calloc((size_t)(K * dv), sizeof(double));
   double* zt = (double*)calloc((size_t)K, sizeof(double));
+  /* causal: the memory may start from an earlier prefix (Vtil, Z) */
+  if (mem_in) {
+    memcpy(vt, mem_in, sizeof(double) * (size_t)(K * dv));
+    memcpy(zt, mem_in + K * dv, sizeof(double) * (size_t)K);
+  }
   double* gk = (double*)malloc(sizeof(double) * (size_t)K);
   double* gq = (double*)malloc(sizeof(double) * (size_t)K);
 
@@ -139,23 +144,35 @@ static void gma_slice(const double* q, const double* k, const double* v, const d
       }
     }
   }
+  if (mem_out) {
+    memcpy(mem_out, vt, sizeof(double) * (size_t)(K * dv));
+    memcpy(mem_out + K * dv, zt, sizeof(double) * (size_t)K);
+  }
   free(vt);
   free(zt);
   free(gk);
   free(gq);
 }
 
+/*
+ * mem_in, mem_out (optional, causal only): per (b,h) memory [Vtil (K x dv) | Z (K)]
+ * before the first token and after the last [GMA, variants: the causal form
+ * is a running prefix sum, so a sequence can be continued from its memory].
+ */
 void oracle_gma_forward(const double* q, const double* k, const double* v, const double* mu,
                         const double* log_var, const double* logit_pi, double* out, int64_t B,
                         int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal,
-                        double eps, const uint8_t* row_mask) {
+                        double eps, const uint8_t* row_mask, const double* mem_in,
+                        double* mem_out) {
   int64_t BH = B * H;
+  const int64_t ms = K * dv + K;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t s = 0; s < BH; ++s) {
     const int64_t h = s % H;
     gma_slice(q + s * N * d, k + s * N * d, v + s * N * dv, mu + h * K * d, log_var + h * K * d,
               logit_pi + h * K, out + s * N * dv, N, d, K, dv, causal, eps,
-              row_mask ? row_mask + s * N : NULL);
+              row_mask ? row_mask + s * N : NULL, mem_in ? mem_in + s * ms : NULL,
+              mem_out ? mem_out + s * ms : NULL);
   }
 }
 
@@ -222,10 +239,18 @@ void oracle_gma_brute(const double* q, const double* k, const double* v, const d
  */
 static void linattn_slice(const double* q, const double* k, const double* v, const double* g,
                           const double* w, double bias, double* out, int64_t N, int64_t dk,
-                          int64_t dv, int ccq) {
+                          int64_t dv, int ccq, int64_t t0, const double* st_in, double* st_out) {
   double* S = (double*)calloc((size_t)(dk * dv), sizeof(double));
   double* M = ccq ? (double*)calloc((size_t)(dk * dk), sizeof(double)) : NULL;
   double* m = ccq ? (double*)calloc((size_t)dk, sizeof(double)) : NULL;
+  /* state [S (dk x dv) | M (dk x dk) | m (dk)] after t0 earlier tokens */
+  if (st_in) {
+    memcpy(S, st_in, sizeof(double) * (size_t)(dk * dv));
+    if (ccq) {
+      memcpy(M, st_in + dk * dv, sizeof(double) * (size_t)(dk * dk));
+      memcpy(m, st_in + dk * dv + dk * dk, sizeof(double) * (size_t)dk);
+    }
+  }
   double* mu = ccq ? (double*)malloc(sizeof(double) * (size_t)dk) : NULL;
   double* qc = (double*)malloc(sizeof(double) * (size_t)dk);
 
@@ -239,7 +264,7 @@ static void linattn_slice(const double* q, const double* k, const double* v, con
 
     for (int64_t a = 0; a < dk; ++a) qc[a] = qt[a];
     if (ccq) {
-      const double cnt = (double)(t + 1);
+      const double cnt = (double)(t0 + t + 1);
       for (int64_t a = 0; a < dk; ++a) {
         m[a] += kt[a];
         for (int64_t c = 0; c < dk; ++c) M[a * dk + c] += kt[a] * kt[c];
@@ -260,6 +285,13 @@ static void linattn_slice(const double* q, const double* k, const double* v, con
       out[t * dv + e] = acc;
     }
   }
+  if (st_out) {
+    memcpy(st_out, S, sizeof(double) * (size_t)(dk * dv));
+    if (ccq) {
+      memcpy(st_out + dk * dv, M, sizeof(double) * (size_t)(dk * dk));
+      memcpy(st_out + dk * dv + dk * dk, m, sizeof(double) * (size_t)dk);
+    }
+  }
   free(S);
   free(M);
   free(m);
@@ -267,24 +299,41 @@ static void linattn_slice(const double* q, const double* k, const double* v, con
   free(qc);
 }
 
+/*
+ * st_in, st_out (optional): per (b,h) state [S (dk x dv)] before the first token
+ * and after the last [LIN, recurrent form: the state is all a later token
+ * needs, so a sequence can be continued, one token at a time, from it].
+ */
 void oracle_gla_forward(const double* q, const double* k, const double* v, const double* g,
-                        double* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv) {
+                        double* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                        const double* st_in, double* st_out) {
   int64_t BH = B * H;
+  const int64_t ss = dk * dv;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t s = 0; s < BH; ++s)
     linattn_slice(q + s * N * dk, k + s * N * dk, v + s * N * dv, g + s * N, NULL, 0.0,
-                  out + s * N * dv, N, dk, dv, 0);
+                  out + s * N * dv, N, dk, dv, 0, 0, st_in ? st_in + s * ss : NULL,
+                  st_out ? st_out + s * ss : NULL);
 }
 
+/*
+ * t0, st_in, st_out: the running key statistics belong to the state too
+ * [CCQ, integration: they are kept by the same recurrent machinery], so the
+ * per (b,h) state is [S (dk x dv) | M = sum k k^T (dk x dk) | m = sum k (dk)],
+ * and t0 is the number of tokens it already holds (0 without st_in).
+ */
 void oracle_ccq_forward(const double* q, const double* k, const double* v, const double* g,
                         const double* w, const double* b, double* out, int64_t B, int64_t H,
-                        int64_t N, int64_t dk, int64_t dv) {
+                        int64_t N, int64_t dk, int64_t dv, int64_t t0, const double* st_in,
+                        double* st_out) {
   int64_t BH = B * H;
+  const int64_t ss = dk * dv + dk * dk + dk;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t s = 0; s < BH; ++s) {
     const int64_t h = s % H;
     linattn_slice(q + s * N * dk, k + s * N * dk, v + s * N * dv, g + s * N, w + h * dk, b[h],
-                  out + s * N * dv, N, dk, dv, 1);
+                  out + s * N * dv, N, dk, dv, 1, t0, st_in ? st_in + s * ss : NULL,
+                  st_out ? st_out + s * ss : NULL);
   }
 }
 

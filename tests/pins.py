@@ -334,9 +334,77 @@ def pin_ccq_golden(orc):
     assert relerr(got, ref) < 1e-14, (got, ref)
 
 
+def pin_gma_state(orc):
+    """The causal memory after a prefix is Gamma_K^T [V | 1] over that prefix
+    (scipy posterior), and reading on from it gives the rows of the whole
+    sequence (numpy brute force), one token at a time included."""
+    rng = _rng(401)
+    B, H, N, d, K, dv, eps = 1, 2, 23, 4, 3, 2, 1e-3
+    mu, lv, lp = _gma_params(rng, H, K, d)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, dv))
+    ref = numpy_gma_brute(q, k, v, mu, lv, lp, True, eps)
+    for a in (9, N - 1):
+        o1, st = orc.gma_forward(q[:, :, :a], k[:, :, :a], v[:, :, :a], mu, lv, lp, True, eps,
+                                 return_state=True)
+        for h in range(H):
+            gam = scipy_gamma(k[0, h, :a], mu[h], lv[h], lp[h])
+            want = np.concatenate([(gam.T @ v[0, h, :a]).ravel(), gam.sum(0)])
+            assert relerr(st[0, h], want) < 1e-12
+        o2, st2 = orc.gma_forward(q[:, :, a:], k[:, :, a:], v[:, :, a:], mu, lv, lp, True, eps,
+                                  state_in=st, return_state=True)
+        assert relerr(np.concatenate([o1, o2], 2), ref) < 1e-12
+        # every responsibility row sums to 1: the normaliser mass is the token count
+        assert abs(st2[0, 0, K * dv:].sum() - N) < 1e-12
+
+
+def pin_gla_state(orc):
+    """S after a prefix is sum_j prod(g_{j+1..a}) k_j v_j^T; continuing from it
+    (also one token at a time) gives the brute-force rows of the whole sequence."""
+    rng = _rng(402)
+    B, H, N, dk, dv = 1, 2, 21, 4, 3
+    q = rng.standard_normal((B, H, N, dk))
+    k = rng.standard_normal((B, H, N, dk))
+    v = rng.standard_normal((B, H, N, dv))
+    g = rng.uniform(0.2, 1.0, (B, H, N))
+    ref = numpy_gla_brute(q, k, v, g)
+    for a in (8, N - 1):
+        o1, st = orc.gla_forward(q[:, :, :a], k[:, :, :a], v[:, :, :a], g[:, :, :a], return_state=True)
+        for h in range(H):
+            want = sum(np.prod(g[0, h, j + 1:a]) * np.outer(k[0, h, j], v[0, h, j]) for j in range(a))
+            assert relerr(st[0, h], want.ravel()) < 1e-12
+        o2 = orc.gla_forward(q[:, :, a:], k[:, :, a:], v[:, :, a:], g[:, :, a:], state_in=st)
+        assert relerr(np.concatenate([o1, o2], 2), ref) < 1e-12
+
+
+def pin_ccq_state(orc):
+    """The CCQ state after a prefix holds S (as for plain decay), M = K^T K and
+    m = K^T 1 of that prefix; continuing from it with the token count gives the
+    brute-force rows (np.cov over the whole prefix) of the whole sequence."""
+    rng = _rng(403)
+    q, k, v, g, w, b = _ccq_case(rng, N=19, center=0.7)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    ref = numpy_ccq_brute(q, k, v, g, w, b)
+    for a in (7, N - 1):
+        o1, st = orc.ccq_forward(q[:, :, :a], k[:, :, :a], v[:, :, :a], g[:, :, :a], w, b,
+                                 return_state=True)
+        for h in range(H):
+            kk = k[0, h, :a]
+            S = sum(np.prod(g[0, h, j + 1:a]) * np.outer(kk[j], v[0, h, j]) for j in range(a))
+            want = np.concatenate([S.ravel(), (kk.T @ kk).ravel(), kk.sum(0)])
+            assert relerr(st[0, h], want) < 1e-12
+        o2 = orc.ccq_forward(q[:, :, a:], k[:, :, a:], v[:, :, a:], g[:, :, a:], w, b, t0=a,
+                             state_in=st)
+        assert relerr(np.concatenate([o1, o2], 2), ref) < 1e-12
+    assert dk * dv + dk * dk + dk == st.shape[-1]
+
+
 ALL_PINS = [
     pin_gamma_scipy, pin_gma_brute_numpy, pin_gma_k1_closed_form, pin_gma_identical_components,
     pin_gma_permutation, pin_gma_prefix, pin_gma_affinity_structure, pin_gma_golden,
     pin_gla_brute, pin_gla_chunkwise, pin_ccq_numpy_cov, pin_cov_is_logpartition_hessian,
-    pin_ccq_reductions, pin_ccq_chunkwise, pin_ccq_golden,
+    pin_ccq_reductions, pin_ccq_chunkwise, pin_ccq_golden, pin_gma_state, pin_gla_state,
+    pin_ccq_state,
 ]

@@ -23,8 +23,14 @@ MUTANTS = [
      " zt[c] += gk[c]; } }"),
     ("decay_after_add", "S[a * dv + e] = g[t] * S[a * dv + e] + kt[a] * vt[e];",
      "S[a * dv + e] = g[t] * (S[a * dv + e] + kt[a] * vt[e]);"),
-    ("cov_unbiased", "const double cnt = (double)(t + 1);",
-     "const double cnt = (double)(t > 0 ? t : 1);"),
+    ("cov_unbiased", "const double cnt = (double)(t0 + t + 1);",
+     "const double cnt = (double)(t0 + t > 0 ? t0 + t : 1);"),
+    ("state_count_ignored", "const double cnt = (double)(t0 + t + 1);", "const double cnt = (double)(t + 1);"),
+    ("state_key_sum_not_carried", "memcpy(m, st_in + dk * dv + dk * dk, sizeof(double) * (size_t)dk);", ""),
+    ("state_decay_not_applied", "S[a * dv + e] = g[t] * S[a * dv + e] + kt[a] * vt[e];",
+     "S[a * dv + e] = (t == 0 && st_in ? 1.0 : g[t]) * S[a * dv + e] + kt[a] * vt[e];"),
+    ("gma_state_normaliser_not_carried", "memcpy(zt, mem_in + K * dv, sizeof(double) * (size_t)K);", ""),
+    ("gma_state_out_missing_z", "memcpy(mem_out + K * dv, zt, sizeof(double) * (size_t)K);", ""),
     ("cov_mean_term_dropped", "(M[a * dk + c] / cnt - mu[a] * mu[c]) * qt[c]", "(M[a * dk + c] / cnt) * qt[c]"),
     ("lambda_sign", "qc[a] = qt[a] - lam * sq;", "qc[a] = qt[a] + lam * sq;"),
     ("gate_bias_sign", "double z = bias;\n      for (int64_t a = 0; a < dk; ++a) z += w[a] * qt[a];",
