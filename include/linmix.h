@@ -27,6 +27,34 @@
  *                         Conditioned Query for Linear Attention", section 2
  *                         Method (derivation, mechanism, integration).
  *
+ * Carried state (prefill, then one token at a time). The causal forms need
+ * nothing from the past but a fixed-size state per (b, h), so a sequence can
+ * be continued in a later call:
+ *  gma_forward_state, linattn_chunk_forward_state, ccq_forward_state
+ *                         the forwards above, starting from a caller's state
+ *                         (optional) and writing the state after the last
+ *                         token (optional).
+ *  gma_decode_step, linattn_decode_step, ccq_decode_step
+ *                         one token per (b, h): advance the state in place and
+ *                         read it.
+ *                         Source: "Gaussian Mixture Attention", Method ->
+ *                         variants (causal form as prefix sums of the memory);
+ *                         allinfo.ai.kr linear attention post, "Key messages"
+ *                         (a constant-size state replaces the growing cache);
+ *                         "Don't Read Everything", section 2 Method ->
+ *                         integration (the covariance statistics ride on the
+ *                         same recurrence).
+ * State layouts (float32, dense, one block per (b, h), blocks in b-major order):
+ *    GMA   [Vtil (K x dv) | Z (K)]            K*dv + K floats:
+ *          Vtil = sum_j gamma(k_j) v_j^T, Z = sum_j gamma(k_j)
+ *    GLA   [S (dk x dv)]                      dk*dv floats:
+ *          S = sum_j (prod_{s > j} g_s) k_j v_j^T
+ *    CCQ   [S (dk x dv) | M (dk x dk) | m (dk)]  dk*dv + dk*dk + dk floats:
+ *          M = sum_j k_j k_j^T, m = sum_j k_j (no decay)
+ *    A zero-filled block is the state of an empty prefix. The CCQ state also
+ *    needs the number of tokens it holds, which the caller passes (t_in,
+ *    t_prev); all (b, h) of one call hold the same number.
+ *
  * Conventions common to every entry point
  *  - Pointers named q, k, v, g, mu, ..., out, workspace are DEVICE pointers on
  *    the current HIP device. Tensors are dense and row-major in the layouts given
@@ -61,7 +89,7 @@
 extern "C" {
 #endif
 
-#define LM_ABI_VERSION 1
+#define LM_ABI_VERSION 2
 
 typedef enum {
   LM_OK = 0,
@@ -132,6 +160,67 @@ int ccq_forward(const void* q, const void* k, const void* v, const float* g,
                 const float* w_lambda, const float* b_lambda, void* out, int64_t B, int64_t H,
                 int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forwards on a carried state. Arguments as for the forward of the same name
+ * (gma_forward_state is the causal GMA forward; the workspace is the one
+ * gma_workspace_bytes gives for causal = 1), plus:
+ *   state_in   [B,H,state] device, float32 (layouts above): the state before
+ *              the first token; NULL = empty prefix (zero state).
+ *   state_out  [B,H,state] device, float32: receives the state after the last
+ *              token; NULL = not written. May be the same buffer as state_in
+ *              (updated in place); otherwise the two must not overlap. Neither
+ *              may overlap out or the workspace. 16-byte aligned.
+ *   t_in       (CCQ) tokens already held by state_in: the running statistics
+ *              of token i of this call divide by t_in + i + 1. Must be 0 when
+ *              state_in is NULL.
+ * Cost: state_out of GMA adds the segment pass over the last segment; the
+ * linear-attention forms write it from the registers of the last segment.
+ */
+int gma_forward_state(const void* q, const void* k, const void* v, const float* mu,
+                      const float* log_var, const float* logit_pi, void* out, int64_t B,
+                      int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, float eps,
+                      int dtype, int64_t segments, const float* state_in, float* state_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+int linattn_chunk_forward_state(const void* q, const void* k, const void* v, const float* g,
+                                void* out, int64_t B, int64_t H, int64_t N, int64_t dk,
+                                int64_t dv, int64_t chunk, int dtype, int64_t segments,
+                                const float* state_in, float* state_out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+int ccq_forward_state(const void* q, const void* k, const void* v, const float* g,
+                      const float* w_lambda, const float* b_lambda, void* out, int64_t B,
+                      int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
+                      int64_t segments, int64_t t_in, const float* state_in, float* state_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One-token steps. Per (b, h) one new token: q, k [B,H,d] and v, out [B,H,dv]
+ * (dtype, 16-byte aligned); g [B,H] float32 (linear attention); parameters as
+ * for the forwards. state [B,H,state] (device float32, layouts above, 16-byte
+ * aligned) is read, advanced by the token and written back in place; out is
+ * the read of the advanced state (the token sees itself, as in the causal
+ * forwards). Equal to the matching forward over the prefix plus this token.
+ *   gma_decode_step      Vtil += gamma(k) v^T, Z += gamma(k);
+ *                        out = gamma(q) Vtil / (gamma(q) Z + eps).
+ *   linattn_decode_step  S = g S + k v^T; out = S^T q.
+ *   ccq_decode_step      also M += k k^T, m += k; with t = t_prev + 1 tokens,
+ *                        out = S^T (q - lambda Sigma q), Sigma = M / t - m m^T / t^2.
+ *                        t_prev: tokens held by the state before the step (>= 0).
+ * Implemented: d == dv in {32, 64, 128}, 1 <= K <= 256, B*H <= 2^24. No
+ * workspace. state must not overlap q, k, v or out. Calls that share a state
+ * buffer must be ordered on one stream.
+ */
+int gma_decode_step(const void* q, const void* k, const void* v, const float* mu,
+                    const float* log_var, const float* logit_pi, void* out, float* state,
+                    int64_t B, int64_t H, int64_t d, int64_t K, int64_t dv, float eps, int dtype,
+                    void* stream);
+int linattn_decode_step(const void* q, const void* k, const void* v, const float* g, void* out,
+                        float* state, int64_t B, int64_t H, int64_t dk, int64_t dv, int dtype,
+                        void* stream);
+int ccq_decode_step(const void* q, const void* k, const void* v, const float* g,
+                    const float* w_lambda, const float* b_lambda, void* out, float* state,
+                    int64_t B, int64_t H, int64_t dk, int64_t dv, int64_t t_prev, int dtype,
+                    void* stream);
 
 #ifdef __cplusplus
 }

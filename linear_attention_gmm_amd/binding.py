@@ -45,6 +45,15 @@ _SIGS = {
                               ctypes.c_int),
     "ccq_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
     "ccq_forward": ([_P] * 7 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "gma_forward_state": ([_P] * 7 + [_I64] * 6 + [ctypes.c_float, ctypes.c_int, _I64, _P, _P, _P,
+                                                   ctypes.c_size_t, _P], ctypes.c_int),
+    "linattn_chunk_forward_state": ([_P] * 5 + [_I64] * 6 + [ctypes.c_int, _I64, _P, _P, _P, ctypes.c_size_t, _P],
+                                    ctypes.c_int),
+    "ccq_forward_state": ([_P] * 7 + [_I64] * 6 + [ctypes.c_int, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P],
+                          ctypes.c_int),
+    "gma_decode_step": ([_P] * 8 + [_I64] * 5 + [ctypes.c_float, ctypes.c_int, _P], ctypes.c_int),
+    "linattn_decode_step": ([_P] * 6 + [_I64] * 4 + [ctypes.c_int, _P], ctypes.c_int),
+    "ccq_decode_step": ([_P] * 8 + [_I64] * 5 + [ctypes.c_int, _P], ctypes.c_int),
 }
 
 
@@ -191,4 +200,158 @@ def ccq_forward(q, k, v, g, w_lambda, b_lambda, chunk: int = 64, segments: int =
     st = lib().ccq_forward(pq, pk, pv, pg, pw, pb, po, B, H, N, dk, dv, chunk, dt, segments,
                            ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
     _check("ccq_forward", st)
+    return out
+
+
+# ----------------------------------------------------------------------------- carried state
+
+def gma_state_size(K: int, dv: int) -> int:
+    """Floats per (b,h) of the GMA memory [Vtil (K x dv) | Z (K)]."""
+    return K * dv + K
+
+
+def linattn_state_size(dk: int, dv: int) -> int:
+    """Floats per (b,h) of the decayed state S (dk x dv)."""
+    return dk * dv
+
+
+def ccq_state_size(dk: int, dv: int) -> int:
+    """Floats per (b,h) of the CCQ state [S (dk x dv) | M (dk x dk) | m (dk)]."""
+    return dk * dv + dk * dk + dk
+
+
+def _state(t: Optional[torch.Tensor], name: str, shape, dev) -> int:
+    if t is None:
+        return None
+    if t.device != dev:
+        raise ValueError("%s must be on %s (got %s)" % (name, dev, t.device))
+    return _dev(t, name, torch.float32, shape)
+
+
+def _state_out(state_out, shape, dev):
+    if state_out is None:
+        return torch.empty(shape, dtype=torch.float32, device=dev)
+    return state_out
+
+
+def gma_forward_state(q, k, v, mu, log_var, logit_pi, state_in: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                      segments: int = 0, out: Optional[torch.Tensor] = None,
+                      state_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Causal GMA forward continuing from state_in [B,H,K*dv+K] (None = empty
+    prefix). Returns (out, state_out): the memory after the last token.
+    state_out may be state_in itself (updated in place)."""
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    dt = _dtype_code(q)
+    pq = _dev(q, "q", q.dtype, (B, H, N, d))
+    pk = _dev(k, "k", q.dtype, (B, H, N, d))
+    pv = _dev(v, "v", q.dtype, (B, H, N, dv))
+    pmu = _dev(mu, "mu", torch.float32, (H, K, d))
+    plv = _dev(log_var, "log_var", torch.float32, (H, K, d))
+    plp = _dev(logit_pi, "logit_pi", torch.float32, (H, K))
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    po = _dev(out, "out", q.dtype, (B, H, N, dv))
+    shape = (B, H, gma_state_size(K, dv))
+    psi = _state(state_in, "state_in", shape, q.device)
+    state_out = _state_out(state_out, shape, q.device)
+    pso = _state(state_out, "state_out", shape, q.device)
+    nbytes = gma_workspace_bytes(B, H, N, d, K, dv, True, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    st = lib().gma_forward_state(pq, pk, pv, pmu, plv, plp, po, B, H, N, d, K, dv, float(eps), dt, segments, psi,
+                                 pso, ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
+    _check("gma_forward_state", st)
+    return out, state_out
+
+
+def linattn_chunk_forward_state(q, k, v, g, state_in: Optional[torch.Tensor] = None, chunk: int = 64,
+                                segments: int = 0, out: Optional[torch.Tensor] = None,
+                                state_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Decayed linear attention continuing from state_in [B,H,dk*dv] (None =
+    zero). Returns (out, state_out), the state after the last token."""
+    dt = _dtype_code(q)
+    (B, H, N, dk, dv), (pq, pk, pv, pg), out, po = _lin_common(q, k, v, g, out)
+    shape = (B, H, linattn_state_size(dk, dv))
+    psi = _state(state_in, "state_in", shape, q.device)
+    state_out = _state_out(state_out, shape, q.device)
+    pso = _state(state_out, "state_out", shape, q.device)
+    nbytes = linattn_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    st = lib().linattn_chunk_forward_state(pq, pk, pv, pg, po, B, H, N, dk, dv, chunk, dt, segments, psi, pso,
+                                           ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
+    _check("linattn_chunk_forward_state", st)
+    return out, state_out
+
+
+def ccq_forward_state(q, k, v, g, w_lambda, b_lambda, state_in: Optional[torch.Tensor] = None, t_in: int = 0,
+                      chunk: int = 64, segments: int = 0, out: Optional[torch.Tensor] = None,
+                      state_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """CCQ forward continuing from state_in [B,H,dk*dv+dk*dk+dk] that holds t_in
+    tokens. Returns (out, state_out); the new state holds t_in + N tokens."""
+    dt = _dtype_code(q)
+    (B, H, N, dk, dv), (pq, pk, pv, pg), out, po = _lin_common(q, k, v, g, out)
+    pw = _dev(w_lambda, "w_lambda", torch.float32, (H, dk))
+    pb = _dev(b_lambda, "b_lambda", torch.float32, (H,))
+    shape = (B, H, ccq_state_size(dk, dv))
+    psi = _state(state_in, "state_in", shape, q.device)
+    state_out = _state_out(state_out, shape, q.device)
+    pso = _state(state_out, "state_out", shape, q.device)
+    nbytes = ccq_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    st = lib().ccq_forward_state(pq, pk, pv, pg, pw, pb, po, B, H, N, dk, dv, chunk, dt, segments, int(t_in), psi,
+                                 pso, ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
+    _check("ccq_forward_state", st)
+    return out, state_out
+
+
+def _dec_common(q, k, v, out):
+    B, H, d = q.shape
+    dv = v.shape[-1]
+    ptrs = (_dev(q, "q", q.dtype, (B, H, d)), _dev(k, "k", q.dtype, (B, H, d)), _dev(v, "v", q.dtype, (B, H, dv)))
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    return (B, H, d, dv), ptrs, out, _dev(out, "out", q.dtype, (B, H, dv))
+
+
+def gma_decode_step(q, k, v, mu, log_var, logit_pi, state, eps: float = 1e-6,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One causal GMA token per (b,h): q, k [B,H,d], v [B,H,dv]; state
+    [B,H,K*dv+K] advanced in place. Returns out [B,H,dv]."""
+    dt = _dtype_code(q)
+    (B, H, d, dv), (pq, pk, pv), out, po = _dec_common(q, k, v, out)
+    K = mu.shape[1]
+    pmu = _dev(mu, "mu", torch.float32, (H, K, d))
+    plv = _dev(log_var, "log_var", torch.float32, (H, K, d))
+    plp = _dev(logit_pi, "logit_pi", torch.float32, (H, K))
+    ps = _state(state, "state", (B, H, gma_state_size(K, dv)), q.device)
+    st = lib().gma_decode_step(pq, pk, pv, pmu, plv, plp, po, ps, B, H, d, K, dv, float(eps), dt, _stream(q.device))
+    _check("gma_decode_step", st)
+    return out
+
+
+def linattn_decode_step(q, k, v, g, state, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decayed-linear-attention token per (b,h): g [B,H]; state [B,H,dk*dv]
+    advanced in place. Returns out [B,H,dv]."""
+    dt = _dtype_code(q)
+    (B, H, dk, dv), (pq, pk, pv), out, po = _dec_common(q, k, v, out)
+    pg = _dev(g, "g", torch.float32, (B, H))
+    ps = _state(state, "state", (B, H, linattn_state_size(dk, dv)), q.device)
+    st = lib().linattn_decode_step(pq, pk, pv, pg, po, ps, B, H, dk, dv, dt, _stream(q.device))
+    _check("linattn_decode_step", st)
+    return out
+
+
+def ccq_decode_step(q, k, v, g, w_lambda, b_lambda, state, t_prev: int,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One CCQ token per (b,h); state [B,H,dk*dv+dk*dk+dk] holds t_prev tokens
+    and is advanced in place. Returns out [B,H,dv]."""
+    dt = _dtype_code(q)
+    (B, H, dk, dv), (pq, pk, pv), out, po = _dec_common(q, k, v, out)
+    pg = _dev(g, "g", torch.float32, (B, H))
+    pw = _dev(w_lambda, "w_lambda", torch.float32, (H, dk))
+    pb = _dev(b_lambda, "b_lambda", torch.float32, (H,))
+    ps = _state(state, "state", (B, H, ccq_state_size(dk, dv)), q.device)
+    st = lib().ccq_decode_step(pq, pk, pv, pg, pw, pb, po, ps, B, H, dk, dv, int(t_prev), dt, _stream(q.device))
+    _check("ccq_decode_step", st)
     return out

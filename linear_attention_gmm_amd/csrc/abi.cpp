@@ -70,6 +70,21 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 size_t esize(int dtype) { return dtype == LM_BF16 ? 2 : 4; }
 
+// Carried states: 16-byte aligned, clear of `out` and the workspace, and either
+// the same buffer for input and output or two that do not overlap.
+int check_states(const char* fn, const float* sin, float* sout, size_t nbytes, const void* out, size_t nout,
+                 const void* ws, size_t nws) {
+  for (const float* p : {sin, static_cast<const float*>(sout)}) {
+    if (!p) continue;
+    if (!aligned(p, 16)) return fail(LM_EINVAL, "%s: misaligned state pointer (16 bytes needed)", fn);
+    if (overlap(p, nbytes, out, nout) || overlap(p, nbytes, ws, nws))
+      return fail(LM_EINVAL, "%s: a state buffer overlaps out or the workspace", fn);
+  }
+  if (sin && sout && sin != sout && overlap(sin, nbytes, sout, nbytes))
+    return fail(LM_EINVAL, "%s: state_in and state_out overlap without being the same buffer", fn);
+  return LM_OK;
+}
+
 // ----------------------------------------------------------------------------- GMA
 
 // Components are padded to KP (padding has logit -inf). The bf16 kernel for
@@ -165,8 +180,8 @@ int lin_check_shape(const char* fn, int64_t B, int64_t H, int64_t N, int64_t dk,
 
 int lin_forward(const char* fn, bool ccq, const void* q, const void* k, const void* v, const float* g,
                 const float* w_lambda, const float* b_lambda, void* out, int64_t B, int64_t H, int64_t N,
-                int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments, int64_t t_in,
+                const float* state_in, float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
   int st = lin_check_shape(fn, B, H, N, dk, dv, chunk, dtype, segments);
   if (st != LM_OK) return st;
   if (!q || !k || !v || !g || !out || !workspace || (ccq && (!w_lambda || !b_lambda)))
@@ -182,6 +197,12 @@ int lin_forward(const char* fn, bool ccq, const void* q, const void* k, const vo
   if (overlap(out, nv, q, nq) || overlap(out, nv, k, nq) || overlap(out, nv, v, nv) ||
       overlap(out, nv, g, (size_t)B * H * N * 4) || overlap(out, nv, workspace, L.total))
     return fail(LM_EINVAL, "%s: out overlaps an input or the workspace", fn);
+  if (t_in < 0 || (t_in > 0 && !state_in) || t_in > (int64_t(1) << 40))
+    return fail(LM_EINVAL, "%s: t_in counts the tokens held by state_in (0 without one; got %lld)", fn,
+                (long long)t_in);
+  const size_t sfl = (size_t)dk * dv + (ccq ? (size_t)dk * dk + dk : 0);
+  if ((st = check_states(fn, state_in, state_out, (size_t)B * H * sfl * 4, out, nv, workspace, L.total)) != LM_OK)
+    return st;
   lm::LinLaunch La;
   La.q = q;
   La.k = k;
@@ -200,7 +221,95 @@ int lin_forward(const char* fn, bool ccq, const void* q, const void* k, const vo
   La.R = L.R;
   La.bf16 = dtype == LM_BF16;
   La.ccq = ccq;
+  La.state_in = state_in;
+  La.state_out = state_out;
+  La.t_in = t_in;
   hipError_t e = lm::linattn_launch(La, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+int gma_impl(const char* fn, const void* q, const void* k, const void* v, const float* mu, const float* log_var,
+             const float* logit_pi, void* out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv,
+             int causal, float eps, int dtype, int64_t segments, const float* state_in, float* state_out,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  int st = gma_check_shape(B, H, N, d, K, dv, causal, dtype, segments);
+  if (st != LM_OK) return st;
+  if (!(eps >= 0.f) || std::isinf(eps)) return fail(LM_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (!q || !k || !v || !mu || !log_var || !logit_pi || !out || !workspace)
+    return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+      !aligned(mu, 4) || !aligned(log_var, 4) || !aligned(logit_pi, 4))
+    return fail(LM_EINVAL, "%s: misaligned pointer (tensors need 16 bytes, parameters 4)", fn);
+  const GmaLayout L = gma_layout(B, H, N, d, K, dv, dtype, segments);
+  if (workspace_bytes < L.total)
+    return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
+  const size_t es = esize(dtype);
+  const size_t nq = (size_t)B * H * N * d * es, nv = (size_t)B * H * N * dv * es;
+  if (overlap(out, nv, q, nq) || overlap(out, nv, k, nq) || overlap(out, nv, v, nv) ||
+      overlap(out, nv, workspace, L.total) || overlap(out, nv, mu, (size_t)H * K * d * 4) ||
+      overlap(out, nv, log_var, (size_t)H * K * d * 4) || overlap(out, nv, logit_pi, (size_t)H * K * 4))
+    return fail(LM_EINVAL, "%s: out overlaps an input or the workspace", fn);
+  if ((st = check_states(fn, state_in, state_out, (size_t)B * H * (K * dv + K) * 4, out, nv, workspace,
+                         L.total)) != LM_OK)
+    return st;
+  lm::GmaLaunch La;
+  char* ws = static_cast<char*>(workspace);
+  La.q = q;
+  La.k = k;
+  La.v = v;
+  La.out = out;
+  La.mu = mu;
+  La.log_var = log_var;
+  La.logit_pi = logit_pi;
+  La.W = ws + L.W;
+  La.c = reinterpret_cast<float*>(ws + L.c);
+  La.agg = reinterpret_cast<float*>(ws + L.agg);
+  La.aggz = reinterpret_cast<float*>(ws + L.aggz);
+  La.B = B;
+  La.H = H;
+  La.N = N;
+  La.D = d;
+  La.K = K;
+  La.KP = L.KP;
+  La.P = L.plan.P;
+  La.seg_len = L.plan.seg_len;
+  La.causal = causal;
+  La.bf16 = dtype == LM_BF16;
+  La.eps = eps;
+  La.state_in = state_in;
+  La.state_out = state_out;
+  hipError_t e = lm::gma_launch(La, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+// One-token steps: shapes as the forwards with N = 1, state in place.
+int dec_check(const char* fn, int64_t B, int64_t H, int64_t d, int64_t dv, int dtype) {
+  if (B < 1 || H < 1 || d < 1 || dv < 1) return fail(LM_EINVAL, "%s: sizes must be >= 1", fn);
+  if (dtype != LM_F32 && dtype != LM_BF16) return fail(LM_EINVAL, "%s: dtype %d is not LM_F32 or LM_BF16", fn, dtype);
+  if (!(d == 32 || d == 64 || d == 128) || dv != d)
+    return fail(LM_EUNSUPPORTED, "%s implements d == dv in {32, 64, 128} (got %lld, %lld)", fn, (long long)d,
+                (long long)dv);
+  if (B * H > (int64_t(1) << 24)) return fail(LM_EUNSUPPORTED, "%s: B*H <= 2^24 is implemented", fn);
+  return LM_OK;
+}
+
+int dec_run(const char* fn, bool gma, bool ccq, lm::DecodeLaunch& La, int64_t d, size_t state_floats,
+            void* stream) {
+  const size_t es = La.bf16 ? 2 : 4;
+  const size_t nx = (size_t)La.B * La.H * d * es, ns = (size_t)La.B * La.H * state_floats * 4;
+  if (!La.q || !La.k || !La.v || !La.out || !La.state) return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(La.q, 16) || !aligned(La.k, 16) || !aligned(La.v, 16) || !aligned(La.out, 16) ||
+      !aligned(La.state, 16))
+    return fail(LM_EINVAL, "%s: misaligned pointer (tensors and the state need 16 bytes)", fn);
+  if (overlap(La.out, nx, La.q, nx) || overlap(La.out, nx, La.k, nx) || overlap(La.out, nx, La.v, nx) ||
+      overlap(La.out, nx, La.state, ns))
+    return fail(LM_EINVAL, "%s: out overlaps an input or the state", fn);
+  if (overlap(La.state, ns, La.q, nx) || overlap(La.state, ns, La.k, nx) || overlap(La.state, ns, La.v, nx))
+    return fail(LM_EINVAL, "%s: the state overlaps an input", fn);
+  hipError_t e = gma ? lm::gma_decode_launch(La, static_cast<hipStream_t>(stream))
+                     : lm::lin_decode_launch(La, ccq, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
   return ok();
 }
@@ -234,50 +343,46 @@ int gma_forward(const void* q, const void* k, const void* v, const float* mu, co
                 const float* logit_pi, void* out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t K,
                 int64_t dv, int causal, float eps, int dtype, int64_t segments, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  int st = gma_check_shape(B, H, N, d, K, dv, causal, dtype, segments);
+  return gma_impl("gma_forward", q, k, v, mu, log_var, logit_pi, out, B, H, N, d, K, dv, causal, eps, dtype,
+                  segments, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int gma_forward_state(const void* q, const void* k, const void* v, const float* mu, const float* log_var,
+                      const float* logit_pi, void* out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t K,
+                      int64_t dv, float eps, int dtype, int64_t segments, const float* state_in,
+                      float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return gma_impl("gma_forward_state", q, k, v, mu, log_var, logit_pi, out, B, H, N, d, K, dv, 1, eps, dtype,
+                  segments, state_in, state_out, workspace, workspace_bytes, stream);
+}
+
+int gma_decode_step(const void* q, const void* k, const void* v, const float* mu, const float* log_var,
+                    const float* logit_pi, void* out, float* state, int64_t B, int64_t H, int64_t d, int64_t K,
+                    int64_t dv, float eps, int dtype, void* stream) {
+  const char* fn = "gma_decode_step";
+  int st = dec_check(fn, B, H, d, dv, dtype);
   if (st != LM_OK) return st;
-  if (!(eps >= 0.f) || std::isinf(eps)) return fail(LM_EINVAL, "gma_forward: eps must be finite and >= 0");
-  if (!q || !k || !v || !mu || !log_var || !logit_pi || !out || !workspace)
-    return fail(LM_EINVAL, "gma_forward: null pointer argument");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
-      !aligned(mu, 4) || !aligned(log_var, 4) || !aligned(logit_pi, 4))
-    return fail(LM_EINVAL, "gma_forward: misaligned pointer (tensors need 16 bytes, parameters 4)");
-  const GmaLayout L = gma_layout(B, H, N, d, K, dv, dtype, segments);
-  if (workspace_bytes < L.total)
-    return fail(LM_EWORKSPACE, "gma_forward: workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
-  const size_t es = esize(dtype);
-  const size_t nq = (size_t)B * H * N * d * es, nv = (size_t)B * H * N * dv * es;
-  if (overlap(out, nv, q, nq) || overlap(out, nv, k, nq) || overlap(out, nv, v, nv) ||
-      overlap(out, nv, workspace, L.total) || overlap(out, nv, mu, (size_t)H * K * d * 4) ||
-      overlap(out, nv, log_var, (size_t)H * K * d * 4) || overlap(out, nv, logit_pi, (size_t)H * K * 4))
-    return fail(LM_EINVAL, "gma_forward: out overlaps an input or the workspace");
-  lm::GmaLaunch La;
-  char* ws = static_cast<char*>(workspace);
+  if (K < 1 || K > 256) return fail(K < 1 ? LM_EINVAL : LM_EUNSUPPORTED, "%s: 1 <= K <= 256 (got %lld)", fn,
+                                    (long long)K);
+  if (!(eps >= 0.f) || std::isinf(eps)) return fail(LM_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (!mu || !log_var || !logit_pi) return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(mu, 4) || !aligned(log_var, 4) || !aligned(logit_pi, 4))
+    return fail(LM_EINVAL, "%s: misaligned parameter pointer", fn);
+  lm::DecodeLaunch La{};
   La.q = q;
   La.k = k;
   La.v = v;
-  La.out = out;
   La.mu = mu;
   La.log_var = log_var;
   La.logit_pi = logit_pi;
-  La.W = ws + L.W;
-  La.c = reinterpret_cast<float*>(ws + L.c);
-  La.agg = reinterpret_cast<float*>(ws + L.agg);
-  La.aggz = reinterpret_cast<float*>(ws + L.aggz);
+  La.out = out;
+  La.state = state;
   La.B = B;
   La.H = H;
-  La.N = N;
   La.D = d;
   La.K = K;
-  La.KP = L.KP;
-  La.P = L.plan.P;
-  La.seg_len = L.plan.seg_len;
-  La.causal = causal;
   La.bf16 = dtype == LM_BF16;
   La.eps = eps;
-  hipError_t e = lm::gma_launch(La, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(LM_EHIP, "gma_forward: %s", hipGetErrorString(e));
-  return ok();
+  return dec_run(fn, true, false, La, d, (size_t)K * dv + K, stream);
 }
 
 size_t linattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
@@ -290,7 +395,36 @@ int linattn_chunk_forward(const void* q, const void* k, const void* v, const flo
                           int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
                           void* workspace, size_t workspace_bytes, void* stream) {
   return lin_forward("linattn_chunk_forward", false, q, k, v, g, nullptr, nullptr, out, B, H, N, dk, dv, chunk,
-                     dtype, segments, workspace, workspace_bytes, stream);
+                     dtype, segments, 0, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int linattn_chunk_forward_state(const void* q, const void* k, const void* v, const float* g, void* out, int64_t B,
+                                int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
+                                int64_t segments, const float* state_in, float* state_out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return lin_forward("linattn_chunk_forward_state", false, q, k, v, g, nullptr, nullptr, out, B, H, N, dk, dv,
+                     chunk, dtype, segments, 0, state_in, state_out, workspace, workspace_bytes, stream);
+}
+
+int linattn_decode_step(const void* q, const void* k, const void* v, const float* g, void* out, float* state,
+                        int64_t B, int64_t H, int64_t dk, int64_t dv, int dtype, void* stream) {
+  const char* fn = "linattn_decode_step";
+  int st = dec_check(fn, B, H, dk, dv, dtype);
+  if (st != LM_OK) return st;
+  if (!g) return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(g, 4)) return fail(LM_EINVAL, "%s: misaligned g", fn);
+  lm::DecodeLaunch La{};
+  La.q = q;
+  La.k = k;
+  La.v = v;
+  La.g = g;
+  La.out = out;
+  La.state = state;
+  La.B = B;
+  La.H = H;
+  La.D = dk;
+  La.bf16 = dtype == LM_BF16;
+  return dec_run(fn, false, false, La, dk, (size_t)dk * dv, stream);
 }
 
 size_t ccq_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
@@ -304,7 +438,43 @@ int ccq_forward(const void* q, const void* k, const void* v, const float* g, con
                 int64_t chunk, int dtype, int64_t segments, void* workspace, size_t workspace_bytes,
                 void* stream) {
   return lin_forward("ccq_forward", true, q, k, v, g, w_lambda, b_lambda, out, B, H, N, dk, dv, chunk, dtype,
-                     segments, workspace, workspace_bytes, stream);
+                     segments, 0, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int ccq_forward_state(const void* q, const void* k, const void* v, const float* g, const float* w_lambda,
+                      const float* b_lambda, void* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                      int64_t chunk, int dtype, int64_t segments, int64_t t_in, const float* state_in,
+                      float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return lin_forward("ccq_forward_state", true, q, k, v, g, w_lambda, b_lambda, out, B, H, N, dk, dv, chunk,
+                     dtype, segments, t_in, state_in, state_out, workspace, workspace_bytes, stream);
+}
+
+int ccq_decode_step(const void* q, const void* k, const void* v, const float* g, const float* w_lambda,
+                    const float* b_lambda, void* out, float* state, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                    int64_t t_prev, int dtype, void* stream) {
+  const char* fn = "ccq_decode_step";
+  int st = dec_check(fn, B, H, dk, dv, dtype);
+  if (st != LM_OK) return st;
+  if (!g || !w_lambda || !b_lambda) return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(g, 4) || !aligned(w_lambda, 4) || !aligned(b_lambda, 4))
+    return fail(LM_EINVAL, "%s: misaligned parameter pointer", fn);
+  if (t_prev < 0 || t_prev > (int64_t(1) << 40))
+    return fail(LM_EINVAL, "%s: t_prev must be in [0, 2^40] (got %lld)", fn, (long long)t_prev);
+  lm::DecodeLaunch La{};
+  La.q = q;
+  La.k = k;
+  La.v = v;
+  La.g = g;
+  La.w_lambda = w_lambda;
+  La.b_lambda = b_lambda;
+  La.out = out;
+  La.state = state;
+  La.B = B;
+  La.H = H;
+  La.D = dk;
+  La.t_now = t_prev + 1;
+  La.bf16 = dtype == LM_BF16;
+  return dec_run(fn, false, true, La, dk, (size_t)dk * dv + (size_t)dk * dk + dk, stream);
 }
 
 }  // extern "C"

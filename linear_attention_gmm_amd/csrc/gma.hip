@@ -88,31 +88,42 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ mu,
 
 // ---------------------------------------------------------------------------
 // Segment scan over the per-segment states [Vtil | Z] of every sequence, in a
-// fixed order. Causal: slot p becomes the sum of the segments before p (slots
-// 0 .. P-2 hold the segment states; slot 0 becomes zero). Bidirectional: slot 0
-// becomes the sum of all P segments.
+// fixed order. Causal: slot p becomes the memory before segment p, i.e. the
+// caller's initial memory (zero without one) plus the segments before p; slots
+// 0 .. P-2 hold the segment states, and slot P-1 too when the memory after the
+// last token is asked for (fin). Bidirectional: slot 0 becomes the sum of all P
+// segments. init and fin are [B*H][K*DV + K] without padded components.
 __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ agg, float* __restrict__ aggz, int P,
-                                                   int KP, int DV, int causal) {
+                                                   int KP, int DV, int causal, int K,
+                                                   const float* __restrict__ init, float* __restrict__ fin) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int ns = KP * DV;
   if (e >= ns + KP) return;
   float* x;
   size_t stride;
+  int comp, pub;  // component, and index in the caller's layout
   if (e < ns) {
     x = agg + (size_t)bh * P * ns + e;
     stride = ns;
+    comp = e / DV;
+    pub = comp * DV + (e - comp * DV);
   } else {
     x = aggz + (size_t)bh * P * KP + (e - ns);
     stride = KP;
+    comp = e - ns;
+    pub = K * DV + comp;
   }
+  const size_t pitch = (size_t)K * DV + K;
   float run = 0.f;
   if (causal) {
+    if (init && comp < K) run = init[(size_t)bh * pitch + pub];
     for (int p = 0; p < P; ++p) {
-      const float t = p < P - 1 ? x[p * stride] : 0.f;
+      const float t = (p < P - 1 || fin) ? x[p * stride] : 0.f;
       x[p * stride] = run;
       run += t;
     }
+    if (fin && comp < K) fin[(size_t)bh * pitch + pub] = run;
   } else {
     for (int p = 0; p < P; ++p) run += x[p * stride];
     x[0] = run;
@@ -158,7 +169,8 @@ static hipError_t run(const GmaLaunch& L, const Args& a, int mode, int segments,
 static hipError_t scan(const GmaLaunch& L, int causal, hipStream_t st) {
   const int E = (int)(L.KP * L.D + L.KP);
   hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((E + 255) / 256), (unsigned)(L.B * L.H)), dim3(256), 0, st,
-                     L.agg, L.aggz, (int)L.P, (int)L.KP, (int)L.D, causal);
+                     L.agg, L.aggz, (int)L.P, (int)L.KP, (int)L.D, causal, (int)L.K,
+                     causal ? L.state_in : nullptr, causal ? L.state_out : nullptr);
   return hipGetLastError();
 }
 
@@ -193,8 +205,10 @@ hipError_t gma_launch(const GmaLaunch& L, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int P = (int)L.P;
   if (L.causal) {
-    if (P > 1) {
-      if ((e = run(L, a, AGG, P - 1, st)) != hipSuccess) return e;
+    // the memory after the last token needs the last segment's aggregate too
+    const int nagg = L.state_out ? P : P - 1;
+    if (nagg > 0 || L.state_in) {
+      if (nagg > 0 && (e = run(L, a, AGG, nagg, st)) != hipSuccess) return e;
       if ((e = scan(L, 1, st)) != hipSuccess) return e;
       a.has_init = 1;
     }

@@ -21,6 +21,10 @@ struct GmaLaunch {
   int causal;
   bool bf16;
   float eps;
+  // causal only (optional): memory [Vtil (K x D) | Z (K)] per (b,h) before the
+  // first token and after the last
+  const float* state_in;
+  float* state_out;
 };
 hipError_t gma_launch(const GmaLaunch& L, hipStream_t st);
 
@@ -37,8 +41,35 @@ struct LinLaunch {
   int64_t R;  // sub-segments per segment in the segment-state pass
   bool bf16;
   bool ccq;
+  // optional: state [S (D x D) | M (D x D) | m (D)] per (b,h) before the first
+  // token (holding t_in tokens) and after the last
+  const float* state_in;
+  float* state_out;
+  int64_t t_in;
 };
 hipError_t linattn_launch(const LinLaunch& L, hipStream_t st);
+
+// One-token steps on a carried fp32 state (decode.hip). q, k [B,H,D]; v, out
+// [B,H,D]; state in place.
+struct DecodeLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;         // linear attention
+  const float* w_lambda;  // CCQ
+  const float* b_lambda;  // CCQ
+  const float* mu;        // GMA
+  const float* log_var;   // GMA
+  const float* logit_pi;  // GMA
+  void* out;
+  float* state;
+  int64_t B, H, D, K;
+  int64_t t_now;  // CCQ: tokens in the state after the step
+  bool bf16;
+  float eps;
+};
+hipError_t lin_decode_launch(const DecodeLaunch& L, bool ccq, hipStream_t st);
+hipError_t gma_decode_launch(const DecodeLaunch& L, hipStream_t st);
 
 // Floats per state block written by the segment-state pass.
 inline int64_t lin_state_floats(int64_t D, bool ccq) {

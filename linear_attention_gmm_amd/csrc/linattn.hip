@@ -83,6 +83,8 @@ struct Args {
   int sfl;
   int has_init;  // chunk pass: start from the state block R * (segment index)
   int R;
+  int64_t t_off;   // tokens before the first one (held by a caller's initial state)
+  float* st_out;   // chunk pass (optional): state after the last token, [S | M | m]
 };
 
 // Waves per workgroup: 16 state columns per wave (8 waves, two per SIMD, at
@@ -254,7 +256,7 @@ struct Ctx {
   const T* Vg;
   const float* Gg;
   T* Og;
-  int64_t N, t_end;
+  int64_t N, t_end, t_off;
   float gate_b;
   int cbase;
   TileDma<T, D, C::NW> dma;
@@ -507,7 +509,7 @@ __device__ __forceinline__ void chunk_step(const Ctx<T, D, CCQ, AGG>& x, State<T
           float rs = sRS[l];
           if constexpr (C::SPLIT > 1) rs += sRS[kC + l];
           const float lam = __builtin_amdgcn_rcpf(1.f + fast_exp2(-(wm.x + gate_b) * kLog2eF));
-          const float inv_t = __builtin_amdgcn_rcpf((float)t0 + (float)(l + 1));
+          const float inv_t = __builtin_amdgcn_rcpf((float)(t0 + x.t_off) + (float)(l + 1));
           alpha_l = lam * inv_t;
           beta_l = alpha_l * (wm.y + rs) * inv_t;
         }
@@ -897,6 +899,7 @@ __global__ __launch_bounds__(Waves<D>::NW * 64, AGG && sizeof(T) == 2 ? 4 : 1) v
   x.Og = reinterpret_cast<T*>(a.out) + (size_t)bh * N * D;
   x.N = N;
   x.t_end = t_end;
+  x.t_off = a.t_off;
   x.gate_b = CCQ ? a.bl[h] : 0.f;
   x.cbase = w * C::CW;
   x.dma.init();
@@ -987,6 +990,30 @@ __global__ __launch_bounds__(Waves<D>::NW * 64, AGG && sizeof(T) == 2 ? 4 : 1) v
     }
   }
 
+  if constexpr (!AGG) {
+    // the workgroup of the last segment holds the state after the last token
+    if (a.st_out && p == (int)gridDim.x - 1) {
+      float* so = a.st_out + (size_t)bh * (D * D + (CCQ ? D * D + D : 0));
+      const float sfin = exp2f(st.ls);
+#pragma unroll
+      for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * kt + 4 * g + r, col = cbase + 16 * ct + c16;
+            so[row * D + col] = st.S[kt][ct][r] * sfin;
+            if constexpr (CCQ) so[D * D + row * D + col] = st.Mst[kt][ct][r];
+          }
+      if constexpr (CCQ) {
+        if (g == 0) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) so[2 * D * D + cbase + 16 * ct + c16] = st.mreg[ct];
+        }
+      }
+    }
+  }
+
   if constexpr (AGG) {
     float* blk = a.agg + ((size_t)bh * a.P + p) * a.sfl;
     const float sfin = exp2f(st.ls);
@@ -1014,17 +1041,18 @@ __global__ __launch_bounds__(Waves<D>::NW * 64, AGG && sizeof(T) == 2 ? 4 : 1) v
 // Blocks 0 .. nsub-1 hold the states of consecutive sub-segments (R per
 // segment) on entry; block R p becomes the state at the start of segment p:
 //   S_run <- G_q S_run + S_q,  M_run <- M_run + M_q,  m_run <- m_run + m_q
-// over sub-segments q (from zero), with G_q the decay product of sub-segment q
+// over sub-segments q (from zero, or from the caller's initial state [S | M |
+// m], which has no decay slot), with G_q the decay product of sub-segment q
 // (left in place).
 __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ agg, int slots, int nsub, int R, int sfl,
-                                                   int D, int ccq) {
+                                                   int D, int ccq, const float* __restrict__ init) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int nS = D * D;
   const int nTot = ccq ? 2 * D * D + 1 + D : D * D + 1;
   if (e >= nTot || e == nS) return;
   float* base = agg + (size_t)bh * slots * sfl;
-  float run = 0.f;
+  float run = init ? init[(size_t)bh * (nTot - 1) + (e < nS ? e : e - 1)] : 0.f;
   for (int q = 0; q < nsub; ++q) {
     float* xp = base + (size_t)q * sfl + e;
     const float t = *xp;
@@ -1058,16 +1086,19 @@ static hipError_t launch_d(const LinLaunch& L, hipStream_t st) {
   a.has_init = 0;
   a.R = (int)L.R;
   a.P = (int)(L.R * L.P);  // state blocks per (b,h)
+  a.t_off = L.state_in ? L.t_in : 0;
+  a.st_out = L.state_out;
   const unsigned BH = (unsigned)(L.B * L.H);
-  if (L.P > 1) {
-    // sub-segment states of segments 0 .. P-2, then their prefixes
+  if (L.P > 1 || L.state_in) {
+    // sub-segment states of segments 0 .. P-2, then their prefixes (from the
+    // initial state when there is one)
     const int nsub = (int)(L.R * (L.P - 1));
     a.seg_len = (int)(L.seg_len / L.R);
-    hipError_t e = launch_one<T, D, CCQ, true>(a, (unsigned)nsub, BH, st);
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (nsub > 0 && (e = launch_one<T, D, CCQ, true>(a, (unsigned)nsub, BH, st)) != hipSuccess) return e;
     const int n = CCQ ? 2 * D * D + 1 + D : D * D + 1;
     hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((n + 255) / 256), BH), dim3(256), 0, st, L.agg, a.P, nsub, a.R,
-                       a.sfl, D, CCQ ? 1 : 0);
+                       a.sfl, D, CCQ ? 1 : 0, L.state_in);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     a.has_init = 1;
   }

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_version_and_status_strings():
     L = binding.lib()
-    assert L.lm_abi_version() == 1
+    assert L.lm_abi_version() == 2
     for code, name in enumerate(["LM_OK", "LM_EINVAL", "LM_EUNSUPPORTED", "LM_EWORKSPACE", "LM_EHIP"]):
         assert L.lm_status_string(code).decode() == name
     assert L.lm_status_string(99).decode() == "LM_UNKNOWN"
@@ -145,3 +145,79 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 1, 64, 32)
     with pytest.raises((ValueError, RuntimeError)):
         binding.gma_forward(q, q, q, torch.zeros(1, 4, 32), torch.zeros(1, 4, 32), torch.zeros(1, 4))
+
+
+# ----------------------------------------------------------------------------- carried state and decode steps
+
+def _ccq_state(L, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30), w=FAKE + (4 << 30),
+             b=FAKE + (5 << 30), out=FAKE + (6 << 30), B=1, H=2, N=100, dk=64, dv=64, chunk=64,
+             dt=binding.LM_BF16, seg=0, t_in=0, sin=FAKE + (8 << 30), sout=FAKE + (9 << 30),
+             ws=FAKE + (7 << 30), wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = L.ccq_workspace_bytes(a["B"], a["H"], a["N"], a["dk"], a["dv"], a["chunk"], a["dt"], a["seg"])
+    st = L.ccq_forward_state(a["q"], a["k"], a["v"], a["g"], a["w"], a["b"], a["out"], a["B"], a["H"], a["N"],
+                             a["dk"], a["dv"], a["chunk"], a["dt"], a["seg"], a["t_in"], a["sin"], a["sout"],
+                             a["ws"], a["wsb"], None)
+    return st, L.lm_last_error().decode()
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(sin=None, t_in=5), binding.LM_EINVAL),  # a token count without a state
+    (dict(t_in=-1), binding.LM_EINVAL),
+    (dict(sin=FAKE + (8 << 30) + 4), binding.LM_EINVAL),  # misaligned state
+    (dict(sout=FAKE + (8 << 30) + 256), binding.LM_EINVAL),  # partial overlap of the two states
+    (dict(sout=FAKE + (6 << 30)), binding.LM_EINVAL),  # state_out overlaps out
+    (dict(dk=48, dv=48), binding.LM_EUNSUPPORTED),
+])
+def test_ccq_state_errors(kw, code):
+    st, msg = _ccq_state(binding.lib(), **kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def _gma_state(L, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), mu=FAKE + (3 << 30), lv=FAKE + (4 << 30),
+             lp=FAKE + (5 << 30), out=FAKE + (6 << 30), B=1, H=2, N=100, d=64, K=16, dv=64, eps=1e-6,
+             dt=binding.LM_BF16, seg=0, sin=FAKE + (8 << 30), sout=FAKE + (9 << 30), ws=FAKE + (7 << 30), wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = L.gma_workspace_bytes(a["B"], a["H"], a["N"], a["d"], a["K"], a["dv"], 1, a["dt"], a["seg"])
+    st = L.gma_forward_state(a["q"], a["k"], a["v"], a["mu"], a["lv"], a["lp"], a["out"], a["B"], a["H"], a["N"],
+                             a["d"], a["K"], a["dv"], a["eps"], a["dt"], a["seg"], a["sin"], a["sout"], a["ws"],
+                             a["wsb"], None)
+    return st, L.lm_last_error().decode()
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(sin=FAKE + (8 << 30) + 8), binding.LM_EINVAL),
+    (dict(sout=FAKE + (7 << 30)), binding.LM_EINVAL),  # state_out overlaps the workspace
+    (dict(sout=FAKE + (8 << 30) + 16), binding.LM_EINVAL),  # partial overlap of the two states
+    (dict(K=300), binding.LM_EUNSUPPORTED),
+])
+def test_gma_state_errors(kw, code):
+    st, msg = _gma_state(binding.lib(), **kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+@needs_lib
+def test_decode_step_errors():
+    L = binding.lib()
+    q, k, v, g, w, b, out, s = (FAKE + (i << 30) for i in range(8))
+    bf = binding.LM_BF16
+    assert L.linattn_decode_step(q, k, v, g, out, s, 2, 2, 48, 48, bf, None) == binding.LM_EUNSUPPORTED
+    assert L.linattn_decode_step(q, k, v, g, out, None, 2, 2, 64, 64, bf, None) == binding.LM_EINVAL
+    assert L.linattn_decode_step(q, k, v, g, out + 4, s, 2, 2, 64, 64, bf, None) == binding.LM_EINVAL
+    assert L.linattn_decode_step(q, k, v, g, q, s, 2, 2, 64, 64, bf, None) == binding.LM_EINVAL  # out is q
+    assert L.linattn_decode_step(q, k, v, g, out, s, 0, 2, 64, 64, bf, None) == binding.LM_EINVAL
+    assert L.ccq_decode_step(q, k, v, g, w, b, out, s, 2, 2, 64, 64, -1, bf, None) == binding.LM_EINVAL
+    assert L.ccq_decode_step(q, k, v, g, None, b, out, s, 2, 2, 64, 64, 3, bf, None) == binding.LM_EINVAL
+    assert L.ccq_decode_step(q, k, v, g, w, b, out, k, 2, 2, 64, 64, 3, bf, None) == binding.LM_EINVAL  # state is k
+    assert L.gma_decode_step(q, k, v, g, w, b, out, s, 2, 2, 64, 257, 64, 1e-6, bf, None) == binding.LM_EUNSUPPORTED
+    assert L.gma_decode_step(q, k, v, g, w, b, out, s, 2, 2, 64, 16, 64, -1.0, bf, None) == binding.LM_EINVAL
+    assert L.gma_decode_step(q, k, v, g, w, b, out, s, 2, 2, 64, 16, 32, 1e-6, bf, None) == binding.LM_EUNSUPPORTED
+    assert L.lm_last_error().decode()
