@@ -1,6 +1,6 @@
 """Benchmark: forward head-tokens/s of causal GMA and CCQ at 16K tokens on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--secondary]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--secondary] [--decode]
 
 One step is one forward of each headline path on its own synthetic batch:
   * causal Gaussian Mixture Attention, bf16 in / fp32 accumulate:
@@ -24,7 +24,10 @@ The JSON line also holds:
   * cpu_baseline: the fp64 oracle on a bounded sample of the same workload
     (one (b, h) slice per host thread at full length, repeated until at least
     10 s of work) on the host cores;
-  * parts: per-path rates.
+  * parts: per-path rates;
+  * decode (--decode): the one-token steps at the model shapes of the two
+    workloads, batched so that the states (about 0.5 GB) exceed the cache,
+    against the same 8 TB/s (the state is read and written once per step).
 
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR
 
@@ -99,6 +102,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", action="store_true", help="also time bidirectional GMA, GLA and long GMA")
+    ap.add_argument("--decode", action="store_true",
+                    help="also time the one-token decode steps on states larger than the last-level cache")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 --pmc runs of this bench into profiles/traffic.json")
     args = ap.parse_args()
@@ -270,9 +275,61 @@ def main():
                 sec[name]["mfma_frac"] = sec[name]["alg_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
         result["secondary"] = sec
 
+    if args.decode:
+        result["decode"] = decode_steps(torch, dev)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(gx, cx, gcfg, ccfg)
     print(json.dumps(result), flush=True)
+
+
+def decode_steps(torch, dev, steps=20):
+    """One-token steps of the three mixers at the model shapes of the 16K-token
+    workloads, with batches whose states (about 0.5 GB) exceed the 256 MB
+    last-level cache. Algorithmic bytes per step: the state read and written
+    once, plus q, k, v, out (and g) in bf16."""
+    import numpy as np
+
+    import linear_attention_gmm_amd as lm
+
+    res = {}
+    gen = torch.Generator(device=dev).manual_seed(7)
+    for name, kind, B, H, d, K in (("gma_decode_b2048_h8_d64_k128", "gma", 2048, 8, 64, 128),
+                                   ("gla_decode_b512_h16_d128", "gla", 512, 16, 128, 0),
+                                   ("ccq_decode_b256_h16_d128", "ccq", 256, 16, 128, 0)):
+        rnd = lambda *shape: torch.randn(*shape, generator=gen, device=dev)
+        q, k, v = (rnd(B, H, d).bfloat16() for _ in range(3))
+        out = torch.empty_like(v)
+        if kind == "gma":
+            sf = lm.gma_state_size(K, d)
+            mu, lv, lp = rnd(H, K, d), torch.nn.functional.softplus(rnd(H, K, d)), rnd(H, K)
+            call = lambda st: lm.gma_decode_step(q, k, v, mu, lv, lp, st, out=out)
+        else:
+            sf = lm.ccq_state_size(d, d) if kind == "ccq" else lm.linattn_state_size(d, d)
+            g = torch.sigmoid(rnd(B, H) + 3.0)
+            if kind == "ccq":
+                w, b = rnd(H, d) / d ** 0.5, torch.full((H,), -2.0, device=dev)
+                call = lambda st: lm.ccq_decode_step(q, k, v, g, w, b, st, t_prev=16384, out=out)
+            else:
+                call = lambda st: lm.linattn_decode_step(q, k, v, g, st, out=out)
+        st = rnd(B, H, sf) * 0.01
+        io = B * H * (4 * d * 2 + (4 if kind != "gma" else 0))
+        nbytes = 2 * st.numel() * 4 + io
+        for _ in range(3):
+            call(st)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record()
+        for i in range(steps):
+            call(st)
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]))
+        res[name] = {"ms_per_step": ms, "tokens_per_s": B * H / (ms * 1e-3), "state_MB": st.numel() * 4 / 1e6,
+                     "alg_bytes_per_step": nbytes, "alg_GBps": nbytes / (ms * 1e-3) / 1e9,
+                     "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del st, q, k, v, out
+    return res
 
 
 def cpu_baseline(gx, cx, gcfg, ccfg, min_seconds=10.0, max_rounds=20):

@@ -160,54 +160,65 @@ __global__ __launch_bounds__(NT) void lin_step(const T* __restrict__ q, const T*
 // straight from the Gaussian log-densities, log pi_c - (1/2) sum_i (log var_ci +
 // (x_i - mu_ci)^2 / var_ci); the terms common to all components (the
 // normaliser of the priors, (D/2) log 2 pi) cancel in the posterior.
-template <typename T, int D>
+// One workgroup serves NB batch entries of one head, so the parameters are
+// read and the precisions exp(-log var) formed once for NB tokens.
+template <typename T, int D, int NB>
 __global__ __launch_bounds__(NT) void gma_step(const T* __restrict__ q, const T* __restrict__ k,
                                                const T* __restrict__ v, const float* __restrict__ mu,
                                                const float* __restrict__ lv, const float* __restrict__ lp,
-                                               T* __restrict__ out, float* __restrict__ state, int H, int K,
-                                               float eps) {
+                                               T* __restrict__ out, float* __restrict__ state, int B, int H,
+                                               int K, float eps) {
   typedef Rows<D> R;
   constexpr int BATCH = 8;  // passes whose loads are in flight together
-  __shared__ float sq[D], sk[D], sv[D];
-  __shared__ float sgq[256], sgk[256];
+  __shared__ float sq[NB][D], sk[NB][D], sv[NB][D];
+  __shared__ float sgq[NB][256], sgk[NB][256];
   __shared__ float sred[R::RPP][D];
   __shared__ float sden[NT / 64];
-  const int bh = blockIdx.x, h = bh % H, tid = threadIdx.x, l = lane_id(), w = wave_id();
+  const int h = blockIdx.x % H, b0 = (blockIdx.x / H) * NB;
+  const int nb = B - b0 < NB ? B - b0 : NB;
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
   const int j = tid % R::C4, r0 = tid / R::C4;
-  float* Vt = state + (size_t)bh * ((size_t)K * D + K);
-  float* Z = Vt + (size_t)K * D;
-  if (tid < D) {
-    sq[tid] = to_f32(q[(size_t)bh * D + tid]);
-    sk[tid] = to_f32(k[(size_t)bh * D + tid]);
-    sv[tid] = to_f32(v[(size_t)bh * D + tid]);
+  for (int i = tid; i < NB * D; i += NT) {
+    const int n = i / D, e = i - n * D;
+    const size_t x = ((size_t)(b0 + n) * H + h) * D + e;
+    sq[n][e] = n < nb ? to_f32(q[x]) : 0.f;
+    sk[n][e] = n < nb ? to_f32(k[x]) : 0.f;
+    sv[n][e] = n < nb ? to_f32(v[x]) : 0.f;
   }
   __syncthreads();
 
-  // log joint of q and k under every component: one wave per component, lanes
-  // over features
-  for (int c = w; c < K; c += NT / 64) {
-    const float* mc = mu + ((size_t)h * K + c) * D;
-    const float* lc = lv + ((size_t)h * K + c) * D;
-    float aq = 0.f, ak = 0.f;
-    for (int i = l; i < D; i += 64) {
+  // log joint of the queries and keys under every component: one thread per
+  // component, over the features (q and k are LDS broadcasts)
+  if (tid < K) {
+    const float* mc = mu + ((size_t)h * K + tid) * D;
+    const float* lc = lv + ((size_t)h * K + tid) * D;
+    float aq[NB], ak[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) aq[n] = ak[n] = 0.f;
+    float lsum = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < D; ++i) {
       const float m = mc[i], lvar = lc[i];
       const float prec = expf(-lvar);
-      const float dq = sq[i] - m, dk = sk[i] - m;
-      aq += lvar + dq * dq * prec;
-      ak += lvar + dk * dk * prec;
+      lsum += lvar;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const float dq = sq[n][i] - m, dk = sk[n][i] - m;
+        aq[n] += dq * dq * prec;
+        ak[n] += dk * dk * prec;
+      }
     }
-    aq = wave_sum(aq);
-    ak = wave_sum(ak);
-    if (l == 0) {
-      const float pc = lp[(size_t)h * K + c];
-      sgq[c] = pc - 0.5f * aq;
-      sgk[c] = pc - 0.5f * ak;
+    const float pc = lp[(size_t)h * K + tid];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      sgq[n][tid] = pc - 0.5f * (lsum + aq[n]);
+      sgk[n][tid] = pc - 0.5f * (lsum + ak[n]);
     }
   }
   __syncthreads();
-  // posterior: softmax over components (wave 0: q, wave 1: k)
-  if (w < 2) {
-    float* s = w == 0 ? sgq : sgk;
+  // posteriors: softmax over components, one wave per (entry, q or k)
+  for (int sidx = w; sidx < 2 * nb; sidx += NT / 64) {
+    float* s = (sidx & 1) ? sgk[sidx >> 1] : sgq[sidx >> 1];
     float mx = -INFINITY;
     for (int c = l; c < K; c += 64) mx = fmaxf(mx, s[c]);
     mx = wave_max(mx);
@@ -223,42 +234,48 @@ __global__ __launch_bounds__(NT) void gma_step(const T* __restrict__ q, const T*
   }
   __syncthreads();
 
-  // memory rows: Vtil <- Vtil + gamma_k v^T, numerator gamma_q^T Vtil
-  const float4 vc = ld4(&sv[4 * j]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const int npass = (K + R::RPP - 1) / R::RPP;
-  for (int p0 = 0; p0 < npass; p0 += BATCH) {
-    float4 x[BATCH];
+  for (int n = 0; n < nb; ++n) {
+    const size_t bh = (size_t)(b0 + n) * H + h;
+    float* Vt = state + bh * ((size_t)K * D + K);
+    float* Z = Vt + (size_t)K * D;
+    // memory rows: Vtil <- Vtil + gamma_k v^T, numerator gamma_q^T Vtil
+    const float4 vc = ld4(&sv[n][4 * j]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p0 = 0; p0 < npass; p0 += BATCH) {
+      float4 x[BATCH];
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int c = r0 + (p0 + b) * R::RPP;
-      if (c < K) x[b] = ld4(Vt + (size_t)c * D + 4 * j);
-    }
+      for (int bb = 0; bb < BATCH; ++bb) {
+        const int c = r0 + (p0 + bb) * R::RPP;
+        if (c < K) x[bb] = ld4(Vt + (size_t)c * D + 4 * j);
+      }
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int c = r0 + (p0 + b) * R::RPP;
-      if (c < K) {
-        const float4 s = fma4(sgk[c], vc, x[b]);
-        st4(Vt + (size_t)c * D + 4 * j, s);
-        acc = fma4(sgq[c], s, acc);
+      for (int bb = 0; bb < BATCH; ++bb) {
+        const int c = r0 + (p0 + bb) * R::RPP;
+        if (c < K) {
+          const float4 s = fma4(sgk[n][c], vc, x[bb]);
+          st4(Vt + (size_t)c * D + 4 * j, s);
+          acc = fma4(sgq[n][c], s, acc);
+        }
       }
     }
-  }
-  // normaliser: Z <- Z + gamma_k, denominator gamma_q . Z
-  float den = 0.f;
-  for (int c = tid; c < K; c += NT) {
-    const float z = Z[c] + sgk[c];
-    Z[c] = z;
-    den += sgq[c] * z;
-  }
-  den = wave_sum(den);
-  if (l == 0) sden[w] = den;
-  const float num = column_sum<D>(acc, sred);  // (contains the barrier that publishes sden)
-  if (tid < D) {
-    float d = 0.f;
+    // normaliser: Z <- Z + gamma_k, denominator gamma_q . Z
+    float den = 0.f;
+    for (int c = tid; c < K; c += NT) {
+      const float z = Z[c] + sgk[n][c];
+      Z[c] = z;
+      den += sgq[n][c] * z;
+    }
+    den = wave_sum(den);
+    if (l == 0) sden[w] = den;
+    const float num = column_sum<D>(acc, sred);  // (its barrier publishes sden)
+    if (tid < D) {
+      float dsum = 0.f;
 #pragma unroll
-    for (int i = 0; i < NT / 64; ++i) d += sden[i];
-    out[(size_t)bh * D + tid] = from_f32<T>(num / (d + eps));
+      for (int i = 0; i < NT / 64; ++i) dsum += sden[i];
+      out[bh * D + tid] = from_f32<T>(num / (dsum + eps));
+    }
+    __syncthreads();  // sred and sden are reused by the next entry
   }
 }
 
@@ -279,12 +296,13 @@ static hipError_t lin_t(const DecodeLaunch& L, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t gma_t(const DecodeLaunch& L, hipStream_t st) {
-  const unsigned BH = (unsigned)(L.B * L.H);
+template <typename T, int NB>
+static hipError_t gma_nb(const DecodeLaunch& L, hipStream_t st) {
+  const unsigned grid = (unsigned)(((L.B + NB - 1) / NB) * L.H);
 #define LM_GMA_STEP(DD)                                                                                        \
-  hipLaunchKernelGGL((gma_step<T, DD>), dim3(BH), dim3(NT), 0, st, (const T*)L.q, (const T*)L.k,             \
-                     (const T*)L.v, L.mu, L.log_var, L.logit_pi, (T*)L.out, L.state, (int)L.H, (int)L.K, L.eps)
+  hipLaunchKernelGGL((gma_step<T, DD, NB>), dim3(grid), dim3(NT), 0, st, (const T*)L.q, (const T*)L.k,       \
+                     (const T*)L.v, L.mu, L.log_var, L.logit_pi, (T*)L.out, L.state, (int)L.B, (int)L.H,      \
+                     (int)L.K, L.eps)
   switch (L.D) {
     case 32: LM_GMA_STEP(32); break;
     case 64: LM_GMA_STEP(64); break;
@@ -293,6 +311,15 @@ static hipError_t gma_t(const DecodeLaunch& L, hipStream_t st) {
   }
 #undef LM_GMA_STEP
   return hipGetLastError();
+}
+
+// Batch entries per workgroup: as many as fill a group without idle entries
+// for small batches.
+template <typename T>
+static hipError_t gma_t(const DecodeLaunch& L, hipStream_t st) {
+  if (L.B >= 8) return gma_nb<T, 8>(L, st);
+  if (L.B >= 4) return gma_nb<T, 4>(L, st);
+  return gma_nb<T, 1>(L, st);
 }
 
 }  // namespace dec

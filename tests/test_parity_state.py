@@ -203,3 +203,19 @@ def test_ccq_full_size_prefill_then_decode():
                                      x["b_lambda"][h:h + 1], return_state=True)
         assert_close(np.stack([o[b, h] for o in outs]), ref[0, 0, N:], "bf16", "decode out (%d,%d)" % (b, h))
         cmp_state(stg[b, h], rs[0, 0], "ccq", 128, "bf16", "state after decode (%d,%d)" % (b, h))
+
+
+@pytest.mark.parametrize("B", [2, 5, 11])
+def test_gma_decode_from_empty_state(B):
+    # the decode kernel serves 1, 4 or 8 batch entries of one head per
+    # workgroup; 5 and 11 leave the last group partly filled
+    cfg = inputs.GmaConfig("state_gma_empty", 304, B=B, H=3, N=7, d=32, K=20, dv=32, dtype="f32", eps=1e-6)
+    x = inputs.gma_inputs(cfg)
+    dd = cuda(x)
+    st = torch.zeros((B, 3, binding.gma_state_size(20, 32)), dtype=torch.float32, device="cuda")
+    outs = [host(binding.gma_decode_step(*[_tok(dd[n], i) for n in "qkv"], dd["mu"], dd["log_var"], dd["logit_pi"],
+                                         st, eps=cfg.eps)) for i in range(cfg.N)]
+    ref, rs = oracle.gma_forward(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"], True, cfg.eps,
+                                 return_state=True)
+    assert_close(np.stack(outs, axis=2), ref, "f32", "decode-only out")
+    cmp_state(host(st), rs, "gma", (32, 20), "f32", "decode-only memory")
