@@ -69,6 +69,7 @@ class Oracle:
         lib.oracle_gla_forward.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _D, _D]
         lib.oracle_ccq_forward.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I, _D,
                                            _D]
+        lib.oracle_glv_forward.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I]
         lib.oracle_gla_chunkwise.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I]
         lib.oracle_ccq_chunkwise.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -157,6 +158,15 @@ class Oracle:
                                     dv, int(t0), _p(sin), _p(sout))
         return (out, sout) if return_state else out
 
+    def glv_forward(self, q, k, v, g) -> np.ndarray:
+        """Recurrent linear attention with a decay per key feature: g [B,H,N,dk]."""
+        q, k, v, g = map(_f64, (q, k, v, g))
+        B, H, N, dk = q.shape
+        dv = v.shape[-1]
+        out = np.empty((B, H, N, dv))
+        self.lib.oracle_glv_forward(_p(q), _p(k), _p(v), _p(g), _p(out), B, H, N, dk, dv)
+        return out
+
     def gla_chunkwise(self, q, k, v, g, chunk: int = 64) -> np.ndarray:
         q, k, v, g = map(_f64, (q, k, v, g))
         B, H, N, dk = q.shape
@@ -211,6 +221,10 @@ def gla_forward(*a, **kw):
 
 def ccq_forward(*a, **kw):
     return get().ccq_forward(*a, **kw)
+
+
+def glv_forward(*a, **kw):
+    return get().glv_forward(*a, **kw)
 
 
 def gla_chunkwise(*a, **kw):

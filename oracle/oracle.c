@@ -337,6 +337,37 @@ void oracle_ccq_forward(const double* q, const double* k, const double* v, const
   }
 }
 
+/*
+ * Decayed linear attention with a decay gate per key feature [LIN, decay gates:
+ * the forget rate may be set per channel]:
+ *     S_t[a][e] = g_t[a] S_{t-1}[a][e] + k_t[a] v_t[e],   o_t = S_t^T q_t
+ * g [B,H,N,dk]. With g_t[a] the same for every a this is oracle_gla_forward.
+ */
+void oracle_glv_forward(const double* q, const double* k, const double* v, const double* g,
+                        double* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv) {
+  int64_t BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t s = 0; s < BH; ++s) {
+    const double* qs = q + s * N * dk;
+    const double* ks = k + s * N * dk;
+    const double* vs = v + s * N * dv;
+    const double* gs = g + s * N * dk;
+    double* os = out + s * N * dv;
+    double* S = (double*)calloc((size_t)(dk * dv), sizeof(double));
+    for (int64_t t = 0; t < N; ++t) {
+      for (int64_t a = 0; a < dk; ++a)
+        for (int64_t e = 0; e < dv; ++e)
+          S[a * dv + e] = gs[t * dk + a] * S[a * dv + e] + ks[t * dk + a] * vs[t * dv + e];
+      for (int64_t e = 0; e < dv; ++e) {
+        double acc = 0.0;
+        for (int64_t a = 0; a < dk; ++a) acc += S[a * dv + e] * qs[t * dk + a];
+        os[t * dv + e] = acc;
+      }
+    }
+    free(S);
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Chunkwise-parallel forms                                                  */
 /* ------------------------------------------------------------------------ */

@@ -401,10 +401,49 @@ def pin_ccq_state(orc):
     assert dk * dv + dk * dk + dk == st.shape[-1]
 
 
+def numpy_glv_brute(q, k, v, g):
+    """o_t = sum_{j<=t} sum_a q_ta k_ja (prod_{s=j+1..t} g_sa) v_j, explicit products."""
+    B, H, N, _ = q.shape
+    out = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            for t in range(N):
+                for j in range(t + 1):
+                    dec = np.prod(g[b, h, j + 1:t + 1], axis=0)  # per key feature
+                    out[b, h, t] += np.sum(q[b, h, t] * k[b, h, j] * dec) * v[b, h, j]
+    return out
+
+
+def pin_glv(orc):
+    """Per-feature decay: explicit products; a decay equal across features is the
+    scalar form (numpy brute force); g = 1 is tril(Q K^T) V; a feature with
+    g = 0 forgets all earlier keys in that feature only."""
+    rng = _rng(501)
+    B, H, N, dk, dv = 1, 2, 23, 4, 3
+    q = rng.standard_normal((B, H, N, dk))
+    k = rng.standard_normal((B, H, N, dk))
+    v = rng.standard_normal((B, H, N, dv))
+    g = rng.uniform(0.2, 1.0, (B, H, N, dk))
+    assert relerr(orc.glv_forward(q, k, v, g), numpy_glv_brute(q, k, v, g)) < 1e-12
+    gs = rng.uniform(0.2, 1.0, (B, H, N))
+    got = orc.glv_forward(q, k, v, np.repeat(gs[..., None], dk, axis=-1))
+    assert relerr(got, numpy_gla_brute(q, k, v, gs)) < 1e-12
+    got = orc.glv_forward(q, k, v, np.ones((B, H, N, dk)))
+    assert relerr(got, np.tril(q @ np.swapaxes(k, -1, -2)) @ v) < 1e-12
+    g0 = np.ones((B, H, N, dk))
+    g0[..., 1] = 0.0  # feature 1 keeps only the current key
+    got = orc.glv_forward(q, k, v, g0)
+    keep = np.ones(dk, dtype=bool)
+    keep[1] = False
+    ref = np.tril(q[..., keep] @ np.swapaxes(k[..., keep], -1, -2)) @ v
+    ref += (q[..., 1] * k[..., 1])[..., None] * v
+    assert relerr(got, ref) < 1e-12
+
+
 ALL_PINS = [
     pin_gamma_scipy, pin_gma_brute_numpy, pin_gma_k1_closed_form, pin_gma_identical_components,
     pin_gma_permutation, pin_gma_prefix, pin_gma_affinity_structure, pin_gma_golden,
     pin_gla_brute, pin_gla_chunkwise, pin_ccq_numpy_cov, pin_cov_is_logpartition_hessian,
     pin_ccq_reductions, pin_ccq_chunkwise, pin_ccq_golden, pin_gma_state, pin_gla_state,
-    pin_ccq_state,
+    pin_ccq_state, pin_glv,
 ]

@@ -30,6 +30,10 @@ MUTANTS = [
     ("state_decay_not_applied", "S[a * dv + e] = g[t] * S[a * dv + e] + kt[a] * vt[e];",
      "S[a * dv + e] = (t == 0 && st_in ? 1.0 : g[t]) * S[a * dv + e] + kt[a] * vt[e];"),
     ("gma_state_normaliser_not_carried", "memcpy(zt, mem_in + K * dv, sizeof(double) * (size_t)K);", ""),
+    ("glv_decay_by_value_feature", "S[a * dv + e] = gs[t * dk + a] * S[a * dv + e]",
+     "S[a * dv + e] = gs[t * dk + (e % dk)] * S[a * dv + e]"),
+    ("glv_decay_of_previous_token", "S[a * dv + e] = gs[t * dk + a] * S[a * dv + e]",
+     "S[a * dv + e] = (t > 0 ? gs[(t - 1) * dk + a] : 1.0) * S[a * dv + e]"),
     ("gma_state_out_missing_z", "memcpy(mem_out + K * dv, zt, sizeof(double) * (size_t)K);", ""),
     ("cov_mean_term_dropped", "(M[a * dk + c] / cnt - mu[a] * mu[c]) * qt[c]", "(M[a * dk + c] / cnt) * qt[c]"),
     ("lambda_sign", "qc[a] = qt[a] - lam * sq;", "qc[a] = qt[a] + lam * sq;"),
