@@ -18,6 +18,8 @@
  *                         Source: allinfo.ai.kr post on linear attention, "Key
  *                         messages" and "Easy explanation" (matrix state,
  *                         decay gates, chunkwise-parallel form).
+ *  linattn_vec_forward    The same with one decay per key feature,
+ *                         S_t = diag(g_t) S_{t-1} + k_t v_t^T.
  *  ccq_forward            The same state read with the curvature-conditioned
  *                         query q_clean = (I - lambda_t Sigma_t) q_t, with
  *                         Sigma_t the running key covariance (weights 1/t,
@@ -160,6 +162,25 @@ int ccq_forward(const void* q, const void* k, const void* v, const float* g,
                 const float* w_lambda, const float* b_lambda, void* out, int64_t B, int64_t H,
                 int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decayed linear attention with one decay per key feature (chunkwise).
+ *   q, k, v, out, chunk as for linattn_chunk_forward
+ *   g     [B,H,N,dk] float32, expected in (0, 1]: S_t = diag(g_t) S_{t-1} + k_t v_t^T,
+ *         o_t = S_t^T q_t, S_0 = 0. Decays below 2^-15 act as 2^-15 (per token
+ *         and feature), which bounds the scaled operands of the intra-chunk
+ *         products.
+ *   g must be 16-byte aligned (it is read in 16-byte transfers).
+ * Source: allinfo.ai.kr post on linear attention, "Key messages" (decay gates,
+ * forgetting rates that can differ per channel).
+ * Implemented shapes: dk == dv in {32, 64, 128}, chunk 64, any N >= 1.
+ */
+size_t linattn_vec_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                                   int64_t chunk, int dtype, int64_t segments);
+int linattn_vec_forward(const void* q, const void* k, const void* v, const float* g, void* out,
+                        int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                        int dtype, int64_t segments, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * Forwards on a carried state. Arguments as for the forward of the same name

@@ -54,6 +54,8 @@ _SIGS = {
     "gma_decode_step": ([_P] * 8 + [_I64] * 5 + [ctypes.c_float, ctypes.c_int, _P], ctypes.c_int),
     "linattn_decode_step": ([_P] * 6 + [_I64] * 4 + [ctypes.c_int, _P], ctypes.c_int),
     "ccq_decode_step": ([_P] * 8 + [_I64] * 5 + [ctypes.c_int, _P], ctypes.c_int),
+    "linattn_vec_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
+    "linattn_vec_forward": ([_P] * 5 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
 }
 
 
@@ -354,4 +356,33 @@ def ccq_decode_step(q, k, v, g, w_lambda, b_lambda, state, t_prev: int,
     ps = _state(state, "state", (B, H, ccq_state_size(dk, dv)), q.device)
     st = lib().ccq_decode_step(pq, pk, pv, pg, pw, pb, po, ps, B, H, dk, dv, int(t_prev), dt, _stream(q.device))
     _check("ccq_decode_step", st)
+    return out
+
+
+# ----------------------------------------------------------------------------- per-feature decay
+
+def linattn_vec_workspace_bytes(B, H, N, dk, dv, chunk=64, dtype=torch.bfloat16, segments=0) -> int:
+    return int(lib().linattn_vec_workspace_bytes(B, H, N, dk, dv, chunk, _DT[dtype], segments))
+
+
+def linattn_vec_forward(q, k, v, g, chunk: int = 64, segments: int = 0, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decayed linear attention with one decay per key feature:
+    S_t = diag(g_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t. q, k [B,H,N,dk],
+    v [B,H,N,dv] (float32 or bfloat16); g [B,H,N,dk] float32."""
+    dt = _dtype_code(q)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    pq = _dev(q, "q", q.dtype, (B, H, N, dk))
+    pk = _dev(k, "k", q.dtype, (B, H, N, dk))
+    pv = _dev(v, "v", q.dtype, (B, H, N, dv))
+    pg = _dev(g, "g", torch.float32, (B, H, N, dk))
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    po = _dev(out, "out", q.dtype, (B, H, N, dv))
+    nbytes = linattn_vec_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    st = lib().linattn_vec_forward(pq, pk, pv, pg, po, B, H, N, dk, dv, chunk, dt, segments,
+                                   ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
+    _check("linattn_vec_forward", st)
     return out

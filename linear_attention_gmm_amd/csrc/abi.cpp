@@ -229,6 +229,18 @@ int lin_forward(const char* fn, bool ccq, const void* q, const void* k, const vo
   return ok();
 }
 
+struct VecLayout {
+  size_t total;
+  Plan plan;
+};
+
+VecLayout vec_layout(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t segments) {
+  VecLayout L;
+  L.plan = plan_segments(B * H, N, segments, kTargetGroups);
+  L.total = align_up((size_t)B * H * L.plan.P * lm::vec_state_floats(dk) * 4);
+  return L;
+}
+
 int gma_impl(const char* fn, const void* q, const void* k, const void* v, const float* mu, const float* log_var,
              const float* logit_pi, void* out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv,
              int causal, float eps, int dtype, int64_t segments, const float* state_in, float* state_out,
@@ -475,6 +487,49 @@ int ccq_decode_step(const void* q, const void* k, const void* v, const float* g,
   La.t_now = t_prev + 1;
   La.bf16 = dtype == LM_BF16;
   return dec_run(fn, false, true, La, dk, (size_t)dk * dv + (size_t)dk * dk + dk, stream);
+}
+
+size_t linattn_vec_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                                   int dtype, int64_t segments) {
+  if (lin_check_shape("linattn_vec_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
+  return vec_layout(B, H, N, dk, segments).total;
+}
+
+int linattn_vec_forward(const void* q, const void* k, const void* v, const float* g, void* out, int64_t B, int64_t H,
+                        int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "linattn_vec_forward";
+  int st = lin_check_shape(fn, B, H, N, dk, dv, chunk, dtype, segments);
+  if (st != LM_OK) return st;
+  if (!q || !k || !v || !g || !out || !workspace) return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 16))
+    return fail(LM_EINVAL, "%s: misaligned pointer (16 bytes needed)", fn);
+  const size_t es = esize(dtype);
+  const size_t nq = (size_t)B * H * N * dk * es, nv = (size_t)B * H * N * dv * es, ng = (size_t)B * H * N * dk * 4;
+  const VecLayout L = vec_layout(B, H, N, dk, segments);
+  if (workspace_bytes < L.total)
+    return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
+  if (overlap(out, nv, q, nq) || overlap(out, nv, k, nq) || overlap(out, nv, v, nv) || overlap(out, nv, g, ng) ||
+      overlap(out, nv, workspace, L.total))
+    return fail(LM_EINVAL, "%s: out overlaps an input or the workspace", fn);
+  lm::VecLaunch La;
+  La.q = q;
+  La.k = k;
+  La.v = v;
+  La.g = g;
+  La.out = out;
+  La.agg = static_cast<float*>(workspace);
+  La.B = B;
+  La.H = H;
+  La.N = N;
+  La.D = dk;
+  La.P = L.plan.P;
+  La.seg_len = L.plan.seg_len;
+  La.bf16 = dtype == LM_BF16;
+  hipError_t e = lm::linattn_vec_launch(La, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
 }
 
 }  // extern "C"

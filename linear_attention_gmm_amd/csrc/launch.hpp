@@ -49,6 +49,23 @@ struct LinLaunch {
 };
 hipError_t linattn_launch(const LinLaunch& L, hipStream_t st);
 
+// Decayed linear attention with a decay per key feature (linattn_vec.hip).
+struct VecLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;  // [B,H,N,D]
+  void* out;
+  float* agg;  // workspace: P state blocks per (b,h)
+  int64_t B, H, N, D, P, seg_len;
+  bool bf16;
+};
+hipError_t linattn_vec_launch(const VecLaunch& L, hipStream_t st);
+
+// Floats per segment block of the per-feature form: S (D x D), then the
+// segment's decay per feature (D); padded to 64 floats.
+inline int64_t vec_state_floats(int64_t D) { return (D * D + D + 63) / 64 * 64; }
+
 // One-token steps on a carried fp32 state (decode.hip). q, k [B,H,D]; v, out
 // [B,H,D]; state in place.
 struct DecodeLaunch {

@@ -75,6 +75,7 @@ class LinAttnConfig:
     g_one: bool = False  # decay identically 1
     g_logit_mean: float = 3.0  # decay g = sigmoid(N(g_logit_mean, 1))
     lowrank_keys: int = 0  # >0: keys = U z + 0.1 n with rank-r U (unnormalised)
+    vector_gates: bool = False  # g [B,H,N,dk]: one decay per token and key feature
     gate_bias: float = -2.0
 
     def replace(self, **kw) -> "LinAttnConfig":
@@ -93,6 +94,7 @@ CONFIGS = {
     "gma_bf16_n16k": GmaConfig("gma_bf16_n16k", 6, B=4, H=8, N=16384, d=64, K=128, dv=64, qk_scale=True),
     "ccq_fp32_lowrank": LinAttnConfig("ccq_fp32_lowrank", 7, B=1, H=2, N=300, dk=32, dv=32, dtype="f32",
                                       lowrank_keys=4, gate_bias=2.0),
+    "glv_bf16_n8k": LinAttnConfig("glv_bf16_n8k", 9, B=8, H=16, N=8192, dk=128, dv=128, vector_gates=True),
     "ccq_bf16_lowrank": LinAttnConfig("ccq_bf16_lowrank", 8, B=4, H=16, N=16384, dk=128, dv=128,
                                       lowrank_keys=4, gate_bias=2.0),
 }
@@ -173,7 +175,8 @@ def gma_inputs(cfg: GmaConfig, N: Optional[int] = None) -> Dict[str, torch.Tenso
 
 
 def linattn_inputs(cfg: LinAttnConfig, N: Optional[int] = None, ccq: bool = False) -> Dict[str, torch.Tensor]:
-    """q, k [B,H,N,dk], v [B,H,N,dv] in cfg.dtype; g [B,H,N] float32; for CCQ also
+    """q, k [B,H,N,dk], v [B,H,N,dv] in cfg.dtype; g [B,H,N] float32 ([B,H,N,dk]
+    with cfg.vector_gates, each entry drawn the same way); for CCQ also
     w_lambda [H,dk] and b_lambda [H] float32."""
     N = cfg.N if N is None else N
     B, H, dk, dv = cfg.B, cfg.H, cfg.dk, cfg.dv
@@ -181,7 +184,8 @@ def linattn_inputs(cfg: LinAttnConfig, N: Optional[int] = None, ccq: bool = Fals
     q = torch.empty((B, H, N, dk), dtype=dt)
     k = torch.empty((B, H, N, dk), dtype=dt)
     v = torch.empty((B, H, N, dv), dtype=dt)
-    g = torch.empty((B, H, N), dtype=torch.float32)
+    gshape = (N, dk) if cfg.vector_gates else (N,)
+    g = torch.empty((B, H) + gshape, dtype=torch.float32)
     basis = None
     if cfg.lowrank_keys:
         r = cfg.lowrank_keys
@@ -197,9 +201,9 @@ def linattn_inputs(cfg: LinAttnConfig, N: Optional[int] = None, ccq: bool = Fals
             ks = z / np.linalg.norm(z, axis=1, keepdims=True)
         vs = _rng(cfg.cfg_id, T_V, b, h).standard_normal((N, dv))
         if cfg.g_one:
-            gs = np.ones(N)
+            gs = np.ones(gshape)
         else:
-            gs = 1.0 / (1.0 + np.exp(-(cfg.g_logit_mean + _rng(cfg.cfg_id, T_G, b, h).standard_normal(N))))
+            gs = 1.0 / (1.0 + np.exp(-(cfg.g_logit_mean + _rng(cfg.cfg_id, T_G, b, h).standard_normal(gshape))))
         q[b, h] = _to(qs, cfg.dtype)
         k[b, h] = _to(ks, cfg.dtype)
         v[b, h] = _to(vs, cfg.dtype)

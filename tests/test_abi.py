@@ -221,3 +221,23 @@ def test_decode_step_errors():
     assert L.gma_decode_step(q, k, v, g, w, b, out, s, 2, 2, 64, 16, 64, -1.0, bf, None) == binding.LM_EINVAL
     assert L.gma_decode_step(q, k, v, g, w, b, out, s, 2, 2, 64, 16, 32, 1e-6, bf, None) == binding.LM_EUNSUPPORTED
     assert L.lm_last_error().decode()
+
+
+@needs_lib
+def test_vec_forward_errors():
+    L = binding.lib()
+    q, k, v, g, out, ws = (FAKE + (i << 30) for i in range(6))
+    bf = binding.LM_BF16
+    wsb = L.linattn_vec_workspace_bytes(1, 2, 100, 64, 64, 64, bf, 0)
+    assert wsb > 0
+    call = lambda **kw: L.linattn_vec_forward(kw.get("q", q), k, v, kw.get("g", g), kw.get("out", out), 1, 2,
+                                              kw.get("N", 100), kw.get("dk", 64), kw.get("dv", 64), kw.get("ch", 64),
+                                              bf, 0, ws, kw.get("wsb", wsb), None)
+    assert call(g=g + 4) == binding.LM_EINVAL  # g is read in 16-byte transfers
+    assert call(q=None) == binding.LM_EINVAL
+    assert call(out=g + 64) == binding.LM_EINVAL  # out overlaps g
+    assert call(wsb=16) == binding.LM_EWORKSPACE
+    assert call(dk=48, dv=48) == binding.LM_EUNSUPPORTED
+    assert call(ch=32) == binding.LM_EUNSUPPORTED
+    assert call(N=0) == binding.LM_EINVAL
+    assert L.lm_last_error().decode()

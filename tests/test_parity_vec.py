@@ -1,0 +1,89 @@
+"""Decayed linear attention with one decay per key feature, on the GPU against
+the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_gmm_amd import binding, inputs
+from parity import assert_close, cuda, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(cfg, segments=0, N=None, sl=None):
+    x = inputs.linattn_inputs(cfg, N=N)
+    say("glv: %s N=%d dk=%d dtype=%s segments=%d g_mean=%s g_one=%s" % (
+        cfg.name, x["q"].shape[2], cfg.dk, cfg.dtype, segments, cfg.g_logit_mean, cfg.g_one))
+    d = cuda(x)
+    got = host(binding.linattn_vec_forward(d["q"], d["k"], d["v"], d["g"], segments=segments))
+    if sl is None:
+        return got, oracle.glv_forward(x["q"], x["k"], x["v"], x["g"])
+    gs, rs = [], []
+    for b, h in sl:
+        sel = lambda t: t[b:b + 1, h:h + 1]
+        rs.append(oracle.glv_forward(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["g"]))[0, 0])
+        gs.append(got[b, h])
+    return np.stack(gs), np.stack(rs)
+
+
+def _cfg(dk, dtype, **kw):
+    return inputs.LinAttnConfig("glv_small", 401, B=2, H=2, N=300, dk=dk, dv=dk, dtype=dtype, vector_gates=True,
+                                **kw)
+
+
+@pytest.mark.parametrize("dk", [32, 64, 128])
+@pytest.mark.parametrize("segments", [1, 3])
+def test_glv_fp32(dk, segments):
+    got, ref = _run(_cfg(dk, "f32"), segments)
+    assert_close(got, ref, "f32", "glv fp32 dk=%d P=%d" % (dk, segments))
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_glv_bf16(dk):
+    got, ref = _run(_cfg(dk, "bf16"), 3)
+    assert_close(got, ref, "bf16", "glv bf16 dk=%d" % dk)
+
+
+@pytest.mark.parametrize("g_logit_mean", [-1.0, -6.0])
+def test_glv_strong_decay_fp32(g_logit_mean):
+    # g ~ 0.27 and g ~ 0.0025 per token and feature: whole sub-chunks decay by
+    # many powers of two, which the scaled operands of the diagonal products
+    # and the carried state must survive
+    got, ref = _run(_cfg(64, "f32", g_logit_mean=g_logit_mean), 2)
+    assert_close(got, ref, "f32", "glv fp32 strong decay %.0f" % g_logit_mean)
+
+
+def test_glv_no_decay_fp32():
+    cfg = _cfg(64, "f32", g_one=True)
+    x = inputs.linattn_inputs(cfg)
+    d = cuda(x)
+    got = host(binding.linattn_vec_forward(d["q"], d["k"], d["v"], d["g"], segments=2))
+    q, k, v = (x[n].double().numpy() for n in "qkv")
+    assert_close(got, np.tril(q @ np.swapaxes(k, -1, -2)) @ v, "f32", "glv g=1 vs tril(QK^T)V")
+
+
+@pytest.mark.parametrize("N", [1, 17, 64, 65])
+def test_glv_short_and_ragged(N):
+    got, ref = _run(_cfg(32, "f32"), 0, N=N)
+    assert_close(got, ref, "f32", "glv fp32 N=%d" % N)
+
+
+def test_glv_equal_gates_match_the_scalar_kernel():
+    # a decay equal across features is the scalar form: both kernels against the
+    # same oracle rows
+    cfg = inputs.LinAttnConfig("glv_eq", 402, B=1, H=2, N=200, dk=64, dv=64, dtype="f32")
+    x = inputs.linattn_inputs(cfg)
+    d = cuda(x)
+    gv = d["g"][..., None].expand(-1, -1, -1, 64).contiguous()
+    got_v = host(binding.linattn_vec_forward(d["q"], d["k"], d["v"], gv))
+    got_s = host(binding.linattn_chunk_forward(d["q"], d["k"], d["v"], d["g"]))
+    ref = oracle.gla_forward(x["q"], x["k"], x["v"], x["g"])
+    assert_close(got_v, ref, "f32", "glv with equal gates")
+    assert_close(got_s, ref, "f32", "scalar kernel")
+
+
+def test_glv_full_size_sampled():
+    cfg = inputs.CONFIGS["glv_bf16_n8k"]
+    got, ref = _run(cfg, sl=[(0, 0), (7, 15)])
+    assert_close(got, ref, "bf16", "glv bf16 8K workload, slices (0,0) and (7,15)")
