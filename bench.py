@@ -239,7 +239,8 @@ def main():
 
     if args.secondary:
         sec = {}
-        for name, fn in (("gma_bidir_n16k", "bidir"), ("gla_bf16_n8k", "gla"), ("gma_bf16_n128k", "gma5")):
+        for name, fn in (("gma_bidir_n16k", "bidir"), ("gla_bf16_n8k", "gla"), ("glv_bf16_n8k", "glv"),
+                         ("gma_bf16_n128k", "gma5")):
             if fn == "bidir":
                 a = gset[0]
                 call = lambda: gma_forward(a["q"], a["k"], a["v"], a["mu"], a["log_var"], a["logit_pi"],
@@ -251,6 +252,14 @@ def main():
                 call = lambda: linattn_chunk_forward(x["q"], x["k"], x["v"], x["g"])
                 tok = cfg.B * cfg.H * cfg.N
                 byt = tok * ccq_bytes_per_head_token(cfg)
+            elif fn == "glv":
+                from linear_attention_gmm_amd import linattn_vec_forward
+                cfg = inputs.CONFIGS["glv_bf16_n8k"]
+                xv = {k: v.to(dev) for k, v in inputs.linattn_inputs(cfg).items()}
+                call = lambda: linattn_vec_forward(xv["q"], xv["k"], xv["v"], xv["g"])
+                tok = cfg.B * cfg.H * cfg.N
+                # Q, K, V, O in bf16 plus one fp32 decay per key feature
+                byt = tok * (4 * cfg.dk * 2 + 4 * cfg.dk)
             else:
                 cfg = inputs.CONFIGS["gma_bf16_n128k"]
                 y = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inputs.gma_inputs(cfg).items()}

@@ -232,12 +232,17 @@ int lin_forward(const char* fn, bool ccq, const void* q, const void* k, const vo
 struct VecLayout {
   size_t total;
   Plan plan;
+  int64_t R;
 };
 
+// Same plan as the scalar-gate form: segments of whole chunks, the segment pass
+// over two sub-segments per segment when the segment length is an even number
+// of chunks.
 VecLayout vec_layout(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t segments) {
   VecLayout L;
-  L.plan = plan_segments(B * H, N, segments, kTargetGroups);
-  L.total = align_up((size_t)B * H * L.plan.P * lm::vec_state_floats(dk) * 4);
+  L.plan = plan_segments(B * H, N, segments, kTargetGroups, kLinSub);
+  L.R = L.plan.P > 1 && (L.plan.seg_len / kChunk) % kLinSub == 0 ? kLinSub : 1;
+  L.total = align_up((size_t)B * H * L.R * L.plan.P * lm::vec_state_floats(dk) * 4);
   return L;
 }
 
@@ -526,6 +531,7 @@ int linattn_vec_forward(const void* q, const void* k, const void* v, const float
   La.D = dk;
   La.P = L.plan.P;
   La.seg_len = L.plan.seg_len;
+  La.R = L.R;
   La.bf16 = dtype == LM_BF16;
   hipError_t e = lm::linattn_vec_launch(La, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));

@@ -58,6 +58,7 @@ struct VecLaunch {
   void* out;
   float* agg;  // workspace: P state blocks per (b,h)
   int64_t B, H, N, D, P, seg_len;
+  int64_t R;  // sub-segments per segment in the segment pass
   bool bf16;
 };
 hipError_t linattn_vec_launch(const VecLaunch& L, hipStream_t st);

@@ -20,9 +20,10 @@
 //    scaled about the sub-chunk's middle token; with log2 g clamped at -15 per
 //    token and feature, no scaled operand exceeds 2^120, so the product stays
 //    finite where it is kept (j <= i).
-//  * Long sequences are cut into segments: a segment pass computes each
-//    segment's S and decay (per feature), a fixed-order scan leaves the state
-//    at every segment start, and the chunk pass starts from it.
+//  * Long sequences are cut into segments: a segment pass computes the S and
+//    the decay (per feature) of every sub-segment (two per segment when the
+//    segment length allows), a fixed-order scan leaves the state at every
+//    segment start, and the chunk pass starts from it.
 #include "mfma.hpp"
 #include "launch.hpp"
 
@@ -43,7 +44,8 @@ struct Args {
   int P;
   int seg_len;
   int sfl;
-  int has_init;
+  int has_init;  // chunk pass: start from the state block R * (segment index)
+  int R;         // sub-segments per segment in the segment pass
 };
 
 template <typename T, int D, bool AGG>
@@ -60,12 +62,26 @@ struct Cfg {
   static constexpr int BUFB = NTL * TB;
   static constexpr int NBUF = (2 * BUFB + GB + 16 * 1024 <= 150 * 1024) ? 2 : 1;
   static constexpr int AP = sizeof(T) == 2 ? 24 : 20;  // pitch of the diagonal score tiles
+  static constexpr int UNR = sizeof(T) == 2 ? 4 : 1;    // unrolled sub-chunks
+  static constexpr int H2 = NW >= 8 ? 2 : 1;  // feature halves of the diagonal products (one per wave)
 };
 
 // L (fp32, swizzled like a DMA tile) at token row r, feature f.
 template <int CPRG>
 __device__ __forceinline__ float& Lat(char* sL, int r, int f) {
   return *reinterpret_cast<float*>(sL + tile_off<CPRG, 4>(r, f));
+}
+
+// L at row r for the N4 * 4 features f0 .. (f0 a multiple of 4): whole 16-byte
+// chunks of the swizzled tile.
+template <int CPRG, int N4>
+__device__ __forceinline__ void load_l(const char* sL, int r, int f0, float* x) {
+#pragma unroll
+  for (int u = 0; u < N4; ++u) {
+    const f32x4 c = *reinterpret_cast<const f32x4*>(sL + r * CPRG * 16 + (((f0 >> 2) + u) ^ tile_sw<CPRG>(r)) * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[4 * u + i] = c[i];
+  }
 }
 
 // NATURAL-order operand fragment of row `row` of a tile (k = features of k-step
@@ -77,10 +93,12 @@ __device__ __forceinline__ typename Mma<T>::frag scaled_nat(const char* tile, ch
   if constexpr (sizeof(T) == 2) {
     const int f0 = ks * 32 + 8 * g;
     const bf16x8 x = tl_nat<CPR>(tile, row, ks);
+    float lr[8], lf[8];
+    load_l<CPRG, 2>(sL, row, f0, lr);
+    load_l<CPRG, 2>(sL, ref, f0, lf);
     bf16x8 y;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      y[i] = (bf16)((float)x[i] * fast_exp2(sign * (Lat<CPRG>(sL, row, f0 + i) - Lat<CPRG>(sL, ref, f0 + i))));
+    for (int i = 0; i < 8; ++i) y[i] = (bf16)((float)x[i] * fast_exp2(sign * (lr[i] - lf[i])));
     return y;
   } else {
     const int f = ks * 4 + g;
@@ -98,7 +116,7 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char sBuf[C::NBUF][C::BUFB];
   __shared__ __attribute__((aligned(16))) char sG[C::GB];
   __shared__ __attribute__((aligned(16))) float sF[AGG ? 1 : 4][D];
-  __shared__ __attribute__((aligned(16))) T sA[AGG ? 1 : 4][16][C::AP];
+  __shared__ __attribute__((aligned(16))) T sA[AGG ? 1 : C::H2][4][16][C::AP];
   __shared__ float sTot[NW][D];
   __shared__ float sLseg[D];
 
@@ -116,14 +134,27 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
 
   TileDma<T, D, NW> dt;
   dt.init();
-  TileDma<float, D, NW> dg;
-  dg.init();
   auto issue = [&](char* buf, int64_t t0) {
     const int rows = (int)(N - t0 < kC ? N - t0 : kC);
     if constexpr (!AGG) dt.issue(buf, Qg + (size_t)t0 * D, rows);
     dt.issue(buf + (AGG ? 0 : C::TB), Kg + (size_t)t0 * D, rows);
     dt.issue(buf + (AGG ? C::TB : 2 * C::TB), Vg + (size_t)t0 * D, rows);
-    dg.issue(sG, Gg + (size_t)t0 * D, rows);
+  };
+  // The decays reach the L pass through registers: wave w owns rows
+  // w TPW .. w TPW + TPW - 1, lane l features l + 64 i. They are loaded one
+  // chunk ahead (rows past the end read as 1, i.e. no decay).
+  constexpr int TPW = kC / NW;
+  constexpr int FPL = (D + 63) / 64;
+  constexpr int GR = TPW * FPL;
+  auto load_g = [&](float* gd, int64_t t0) {
+#pragma unroll
+    for (int rr = 0; rr < TPW; ++rr)
+#pragma unroll
+      for (int i = 0; i < FPL; ++i) {
+        const int f = l + 64 * i;
+        const int64_t row = t0 + w * TPW + rr;
+        gd[rr * FPL + i] = (f < D && row < N) ? Gg[(size_t)row * D + f] : 1.f;
+      }
   };
 
   f32x4 S[DT];
@@ -131,7 +162,7 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
   for (int kt = 0; kt < DT; ++kt) S[kt] = zero4();
   if constexpr (!AGG) {
     if (a.has_init) {
-      const float* blk = a.agg + ((size_t)bh * a.P + p) * a.sfl;
+      const float* blk = a.agg + ((size_t)bh * a.P + (size_t)a.R * p) * a.sfl;
 #pragma unroll
       for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
@@ -140,11 +171,15 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
   }
   if (tid < D) sLseg[tid] = 0.f;
 
+  float gA[GR], gB[C::NBUF == 2 ? GR : 1];
   if constexpr (C::NBUF == 2) {
-    if (t_begin < t_end) issue(sBuf[0], t_begin);
+    if (t_begin < t_end) {
+      issue(sBuf[0], t_begin);
+      load_g(gA, t_begin);
+    }
   }
-  int it = 0;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kC, ++it) {
+  // One chunk; gc holds its decays, gn receives the next chunk's.
+  auto body = [&](int64_t t0, int it, float* gc, float* gn) {
     char* buf = sBuf[C::NBUF == 2 ? (it & 1) : 0];
     if constexpr (C::NBUF == 1) {
       lds_barrier();  // the previous chunk is done with every tile
@@ -153,45 +188,44 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
     char* Qt = buf;
     char* Kt = buf + (AGG ? 0 : C::TB);
     char* Vt = Kt + C::TB;
-    const int nvalid = (int)(N - t0 < kC ? N - t0 : kC);
     wait_vmem();
     lds_barrier();
-
-    // ---- 1. L: cumulative log2 decay per feature, in place of G. Each wave
-    //      scans its block of rows sequentially (lanes = features), then adds
-    //      the totals of the blocks before it.
-    {
-      constexpr int TPW = kC / NW;
-      constexpr int FPL = (D + 63) / 64;
-      float run[FPL];
-#pragma unroll
-      for (int i = 0; i < FPL; ++i) run[i] = 0.f;
-#pragma unroll 4
-      for (int rr = 0; rr < TPW; ++rr) {
-        const int r = w * TPW + rr;
-#pragma unroll
-        for (int i = 0; i < FPL; ++i) {
-          const int f = l + 64 * i;
-          if (f < D) {
-            float& x = Lat<CPRG>(sG, r, f);
-            run[i] += r < nvalid ? fmaxf(__builtin_amdgcn_logf(x), kMinLog2G) : 0.f;
-            x = run[i];
-          }
-        }
+    // the next chunk's tiles and decays load during this whole chunk (the other
+    // buffer was released by the barrier above)
+    if constexpr (C::NBUF == 2) {
+      if (t0 + kC < t_end) {
+        issue(sBuf[(it + 1) & 1], t0 + kC);
+        load_g(gn, t0 + kC);
       }
+    }
+
+    // ---- 1. L: cumulative log2 decay per feature. Each wave scans its block of
+    //      rows sequentially (lanes = features), then adds the totals of the
+    //      blocks before it.
+    {
+      // the block's prefix stays in registers (gc is reused for it) until the
+      // offset of the earlier blocks is known
 #pragma unroll
-      for (int i = 0; i < FPL; ++i)
-        if (l + 64 * i < D) sTot[w][l + 64 * i] = run[i];
+      for (int i = 0; i < FPL; ++i) {
+        float run = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < TPW; ++rr) {
+          run += fmaxf(__builtin_amdgcn_logf(gc[rr * FPL + i]), kMinLog2G);
+          gc[rr * FPL + i] = run;
+        }
+        if (l + 64 * i < D) sTot[w][l + 64 * i] = run;
+      }
       lds_barrier();
-      if (w > 0) {
 #pragma unroll
-        for (int i = 0; i < FPL; ++i) {
-          const int f = l + 64 * i;
-          if (f < D) {
-            float off = 0.f;
-            for (int u = 0; u < w; ++u) off += sTot[u][f];
-            for (int rr = 0; rr < TPW; ++rr) Lat<CPRG>(sG, w * TPW + rr, f) += off;
-          }
+      for (int i = 0; i < FPL; ++i) {
+        const int f = l + 64 * i;
+        if (f < D) {
+          float off = 0.f;
+#pragma unroll
+          for (int u = 0; u < NW - 1; ++u)
+            if (u < w) off += sTot[u][f];
+#pragma unroll
+          for (int rr = 0; rr < TPW; ++rr) Lat<CPRG>(sG, w * TPW + rr, f) = gc[rr * FPL + i] + off;
         }
       }
       lds_barrier();
@@ -199,11 +233,16 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
 
     // ---- 2a. diagonal scores of the four sub-chunks, scaled about token 16t + 8
     if constexpr (!AGG) {
-      for (int t = w; t < 4; t += NW) {
+      // (with eight waves each sub-chunk's product is split in two halves of
+      // the features, one per wave; the read adds both)
+      constexpr int KSN = D / M::KS / C::H2;
+      for (int job = w; job < 4 * C::H2; job += NW) {
+        const int t = job & 3, h = job >> 2;
         const int mid = 16 * t + 8;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int ks = 0; ks < D / M::KS; ++ks) {
+        for (int kk = 0; kk < KSN; ++kk) {
+          const int ks = h * KSN + kk;
           const frag qa = scaled_nat<T, CPR, CPRG>(Qt, sG, 16 * t + c16, ks, mid, 1.f);
           const frag kb = scaled_nat<T, CPR, CPRG>(Kt, sG, 16 * t + c16, ks, mid, -1.f);
           acc = M::mma(qa, kb, acc);
@@ -211,7 +250,7 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
         // lane: key j = c16, queries i = 4g + r; keep j <= i (a select, so the
         // unused entries may be anything)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sA[t][4 * g + r][c16] = from_f32<T>(c16 <= 4 * g + r ? acc[r] : 0.f);
+        for (int r = 0; r < 4; ++r) sA[h][t][4 * g + r][c16] = from_f32<T>(c16 <= 4 * g + r ? acc[r] : 0.f);
       }
       lds_barrier();
     }
@@ -219,24 +258,33 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
     // ---- 2b. Q -> q * 2^(L - P_t), K -> k * 2^(E - L) in place (E = E_t, or
     //      the chunk's last token in the segment pass); row decays F
     for (int idx = tid; idx < kC * CPR; idx += NT) {
+      typedef typename Vec16<T>::type vec;
+      constexpr int EPC = C::EPC;
       const int r = idx / CPR, pc = idx - (idx / CPR) * CPR;
-      const int f0 = (pc ^ tile_sw<CPR>(r)) * C::EPC;
+      const int f0 = (pc ^ tile_sw<CPR>(r)) * EPC;
       const int t = r >> 4;
       const int re = AGG ? kC - 1 : 16 * t + 15;
-      T* pk = reinterpret_cast<T*>(Kt + r * CPR * 16 + pc * 16);
+      float lr[EPC], le[EPC];
+      load_l<CPRG, EPC / 4>(sG, r, f0, lr);
+      load_l<CPRG, EPC / 4>(sG, re, f0, le);
+      vec* pk = reinterpret_cast<vec*>(Kt + r * CPR * 16 + pc * 16);
+      vec kv = *pk;
 #pragma unroll
-      for (int e = 0; e < C::EPC; ++e) {
-        const float lr = Lat<CPRG>(sG, r, f0 + e);
-        pk[e] = from_f32<T>(to_f32(pk[e]) * fast_exp2(Lat<CPRG>(sG, re, f0 + e) - lr));
-      }
+      for (int e = 0; e < EPC; ++e) kv[e] = from_f32<T>(to_f32(kv[e]) * fast_exp2(le[e] - lr[e]));
+      *pk = kv;
       if constexpr (!AGG) {
-        T* pq = reinterpret_cast<T*>(Qt + r * CPR * 16 + pc * 16);
+        float lp[EPC];
+        if (t > 0) {
+          load_l<CPRG, EPC / 4>(sG, 16 * t - 1, f0, lp);
+        } else {
 #pragma unroll
-        for (int e = 0; e < C::EPC; ++e) {
-          const float lr = Lat<CPRG>(sG, r, f0 + e);
-          const float pt = t > 0 ? Lat<CPRG>(sG, 16 * t - 1, f0 + e) : 0.f;
-          pq[e] = from_f32<T>(to_f32(pq[e]) * fast_exp2(lr - pt));
+          for (int e = 0; e < EPC; ++e) lp[e] = 0.f;
         }
+        vec* pq = reinterpret_cast<vec*>(Qt + r * CPR * 16 + pc * 16);
+        vec qv = *pq;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) qv[e] = from_f32<T>(to_f32(qv[e]) * fast_exp2(lr[e] - lp[e]));
+        *pq = qv;
       }
     }
     if constexpr (AGG) {
@@ -254,14 +302,11 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
     }
     lds_barrier();
 
-    // the next chunk's tiles: L is no longer needed, the other buffer is free
-    if constexpr (C::NBUF == 2) {
-      if (t0 + kC < t_end) issue(sBuf[(it + 1) & 1], t0 + kC);
-    }
 
     if constexpr (!AGG) {
       // ---- 3. four sub-chunks: read with the state before them, then update
-#pragma unroll 1
+      // (unrolled where the registers allow, so that tile addresses fold)
+#pragma unroll C::UNR
       for (int t = 0; t < 4; ++t) {
         const int r0 = 16 * t;
         f32x4 o = zero4();
@@ -277,12 +322,14 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
         }
         // intra-sub-chunk: scores (rows = queries, k = keys) times V
         if constexpr (sizeof(T) == 2) {
-          const bf16x4 alo = *reinterpret_cast<const bf16x4*>(&sA[t][c16][4 * g]);
           const bf16x4 vlo = tl_tr16<CPR>(Vt, r0 + 4 * g, cbase);
           const bf16 z = (bf16)0.f;
-          const frag aa = bf16x8{alo[0], alo[1], alo[2], alo[3], z, z, z, z};
           const frag vb = bf16x8{vlo[0], vlo[1], vlo[2], vlo[3], z, z, z, z};
-          o = M::mma(aa, vb, o);
+#pragma unroll
+          for (int h = 0; h < C::H2; ++h) {
+            const bf16x4 alo = *reinterpret_cast<const bf16x4*>(&sA[h][t][c16][4 * g]);
+            o = M::mma(bf16x8{alo[0], alo[1], alo[2], alo[3], z, z, z, z}, vb, o);
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int64_t row = t0 + r0 + 4 * g + r;
@@ -302,7 +349,8 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             vb[s] = *reinterpret_cast<const float*>(Vt + tile_off<CPR, 4>(r0 + 4 * g + s, cbase + c16));
-            o = M::mma(sA[t][c16][4 * g + s], vb[s], o);
+#pragma unroll
+            for (int h = 0; h < C::H2; ++h) o = M::mma(sA[h][t][c16][4 * g + s], vb[s], o);
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -334,6 +382,23 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
         for (int kt = 0; kt < DT; ++kt) S[kt] = M::mma(tl_kmaj_t<CPR, T>(Kt, ks, 16 * kt), vb, S[kt]);
       }
     }
+  };
+
+  if constexpr (C::NBUF == 2) {
+    // two chunks per trip, so that the two decay register sets swap roles
+    // without copies (a copy would wait for the loads in flight)
+    int it = 0;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * kC, it += 2) {
+      body(t0, it, gA, gB);
+      if (t0 + kC < t_end) body(t0 + kC, it + 1, gB, gA);
+    }
+  } else {
+    // one buffer (large fp32 tiles): the chunk's decays load with its tiles
+    int it = 0;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kC, ++it) {
+      load_g(gA, t0);
+      body(t0, it, gA, gB);
+    }
   }
 
   if constexpr (AGG) {
@@ -346,23 +411,26 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
   }
 }
 
-// Scan over the segment states of every sequence, in a fixed order: slot q
-// becomes the state at the start of segment q, run <- diag(G_q) run + S_q over
-// the segments before it (slots 0 .. P-2 hold the segment states on entry).
-__global__ __launch_bounds__(256) void vec_scan(float* __restrict__ agg, int P, int sfl, int D) {
+// Scan over the sub-segment states of every sequence, in a fixed order. Blocks
+// 0 .. nsub-1 hold the states of consecutive sub-segments (R per segment) on
+// entry; block R p becomes the state at the start of segment p:
+// run <- diag(G_q) run + S_q over the sub-segments q before it, with G_q the
+// sub-segment's decay per feature (left in place).
+__global__ __launch_bounds__(256) void vec_scan(float* __restrict__ agg, int slots, int nsub, int R, int sfl, int D) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= D * D) return;
   const int row = e / D;
-  float* base = agg + (size_t)bh * P * sfl;
+  float* base = agg + (size_t)bh * slots * sfl;
   float run = 0.f;
-  for (int q = 0; q < P; ++q) {
+  for (int q = 0; q < nsub; ++q) {
     float* x = base + (size_t)q * sfl + e;
-    const float s = q < P - 1 ? *x : 0.f;
-    const float gq = q < P - 1 ? base[(size_t)q * sfl + D * D + row] : 1.f;
-    *x = run;
+    const float s = *x;
+    const float gq = base[(size_t)q * sfl + D * D + row];
+    if (q % R == 0) *x = run;
     run = gq * run + s;
   }
+  base[(size_t)nsub * sfl + e] = run;
 }
 
 template <typename T, int D>
@@ -375,20 +443,24 @@ static hipError_t launch_d(const VecLaunch& L, hipStream_t st) {
   a.out = L.out;
   a.agg = L.agg;
   a.N = L.N;
-  a.P = (int)L.P;
-  a.seg_len = (int)L.seg_len;
   a.sfl = (int)vec_state_floats(D);
   a.has_init = 0;
+  a.R = (int)L.R;
+  a.P = (int)(L.R * L.P);  // state blocks per (b,h)
   const unsigned BH = (unsigned)(L.B * L.H);
   if (L.P > 1) {
-    hipLaunchKernelGGL((vec_kernel<T, D, true>), dim3((unsigned)(L.P - 1), BH), dim3(Cfg<T, D, true>::NT), 0, st,
-                       a);
+    // sub-segment states of segments 0 .. P-2, then their prefixes
+    const int nsub = (int)(L.R * (L.P - 1));
+    a.seg_len = (int)(L.seg_len / L.R);
+    hipLaunchKernelGGL((vec_kernel<T, D, true>), dim3((unsigned)nsub, BH), dim3(Cfg<T, D, true>::NT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(vec_scan, dim3((unsigned)((D * D + 255) / 256), BH), dim3(256), 0, st, L.agg, a.P, a.sfl, D);
+    hipLaunchKernelGGL(vec_scan, dim3((unsigned)((D * D + 255) / 256), BH), dim3(256), 0, st, L.agg, a.P, nsub, a.R,
+                       a.sfl, D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     a.has_init = 1;
   }
+  a.seg_len = (int)L.seg_len;
   hipLaunchKernelGGL((vec_kernel<T, D, false>), dim3((unsigned)L.P, BH), dim3(Cfg<T, D, false>::NT), 0, st, a);
   return hipGetLastError();
 }
