@@ -64,11 +64,17 @@ ENTRY_KERNELS = {
 }
 
 
+# Sources of the two measured entry points (their kernels, launchers and the
+# ABI layer that plans their segments). The one-token steps and the
+# per-feature-decay kernel are not part of the measured step.
+DIGEST_SOURCES = ("abi.cpp", "launch.hpp", "mfma.hpp", "gma.hip", "gma.hpp", "gma_bf16.hip", "gma_generic.hpp",
+                  "gma_wide.hip", "linattn.hip")
+
+
 def sources_digest():
-    """Hash of the library's kernel and ABI sources (identifies the code the counters were taken on)."""
+    """Hash of the measured entry points' sources (identifies the code the counters were taken on)."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "linear_attention_gmm_amd", "csrc", "*")))
-    files.append(os.path.join(ROOT, "include", "linmix.h"))
+    files = [os.path.join(ROOT, "linear_attention_gmm_amd", "csrc", f) for f in DIGEST_SOURCES]
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
