@@ -193,10 +193,7 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
     // the next chunk's tiles and decays load during this whole chunk (the other
     // buffer was released by the barrier above)
     if constexpr (C::NBUF == 2) {
-      if (t0 + kC < t_end) {
-        issue(sBuf[(it + 1) & 1], t0 + kC);
-        load_g(gn, t0 + kC);
-      }
+      if (t0 + kC < t_end) issue(sBuf[(it + 1) & 1], t0 + kC);
     }
 
     // ---- 1. L: cumulative log2 decay per feature. Each wave scans its block of
@@ -301,6 +298,12 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
       }
     }
     lds_barrier();
+    // the next chunk's decays load during the sub-chunk recurrence (issued here
+    // rather than with the tiles, so that the first phases do not queue behind
+    // them in the address unit)
+    if constexpr (C::NBUF == 2) {
+      if (t0 + kC < t_end) load_g(gn, t0 + kC);
+    }
 
 
     if constexpr (!AGG) {
