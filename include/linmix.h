@@ -181,6 +181,21 @@ int linattn_vec_forward(const void* q, const void* k, const void* v, const float
                         int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
                         int dtype, int64_t segments, void* workspace, size_t workspace_bytes,
                         void* stream);
+/*
+ * The same on a carried state S [B,H,dk*dv] (float32, the GLA layout below):
+ * state_in / state_out as for linattn_chunk_forward_state (workspace from
+ * linattn_vec_workspace_bytes), and the one-token step: q, k [B,H,dk], v, out
+ * [B,H,dv], g [B,H,dk] float32; S = diag(g) S + k v^T in place, out = S^T q.
+ * The step takes g as given (no clamp).
+ */
+int linattn_vec_forward_state(const void* q, const void* k, const void* v, const float* g,
+                              void* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                              int64_t chunk, int dtype, int64_t segments, const float* state_in,
+                              float* state_out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+int linattn_vec_decode_step(const void* q, const void* k, const void* v, const float* g,
+                            void* out, float* state, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                            int dtype, void* stream);
 
 /*
  * Forwards on a carried state. Arguments as for the forward of the same name

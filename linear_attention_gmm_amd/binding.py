@@ -56,6 +56,9 @@ _SIGS = {
     "ccq_decode_step": ([_P] * 8 + [_I64] * 5 + [ctypes.c_int, _P], ctypes.c_int),
     "linattn_vec_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
     "linattn_vec_forward": ([_P] * 5 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "linattn_vec_forward_state": ([_P] * 5 + [_I64] * 6 + [ctypes.c_int, _I64, _P, _P, _P, ctypes.c_size_t, _P],
+                                  ctypes.c_int),
+    "linattn_vec_decode_step": ([_P] * 6 + [_I64] * 4 + [ctypes.c_int, _P], ctypes.c_int),
 }
 
 
@@ -385,4 +388,43 @@ def linattn_vec_forward(q, k, v, g, chunk: int = 64, segments: int = 0, out: Opt
     st = lib().linattn_vec_forward(pq, pk, pv, pg, po, B, H, N, dk, dv, chunk, dt, segments,
                                    ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
     _check("linattn_vec_forward", st)
+    return out
+
+
+def linattn_vec_forward_state(q, k, v, g, state_in: Optional[torch.Tensor] = None, chunk: int = 64,
+                              segments: int = 0, out: Optional[torch.Tensor] = None,
+                              state_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Per-feature decay continuing from state_in [B,H,dk*dv] (None = zero).
+    Returns (out, state_out), the state after the last token."""
+    dt = _dtype_code(q)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    pq = _dev(q, "q", q.dtype, (B, H, N, dk))
+    pk = _dev(k, "k", q.dtype, (B, H, N, dk))
+    pv = _dev(v, "v", q.dtype, (B, H, N, dv))
+    pg = _dev(g, "g", torch.float32, (B, H, N, dk))
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    po = _dev(out, "out", q.dtype, (B, H, N, dv))
+    shape = (B, H, linattn_state_size(dk, dv))
+    psi = _state(state_in, "state_in", shape, q.device)
+    state_out = _state_out(state_out, shape, q.device)
+    pso = _state(state_out, "state_out", shape, q.device)
+    nbytes = linattn_vec_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    st = lib().linattn_vec_forward_state(pq, pk, pv, pg, po, B, H, N, dk, dv, chunk, dt, segments, psi, pso,
+                                         ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
+    _check("linattn_vec_forward_state", st)
+    return out, state_out
+
+
+def linattn_vec_decode_step(q, k, v, g, state, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token per (b,h) with one decay per key feature: g [B,H,dk]; state
+    [B,H,dk*dv] advanced in place. Returns out [B,H,dv]."""
+    dt = _dtype_code(q)
+    (B, H, dk, dv), (pq, pk, pv), out, po = _dec_common(q, k, v, out)
+    pg = _dev(g, "g", torch.float32, (B, H, dk))
+    ps = _state(state, "state", (B, H, linattn_state_size(dk, dv)), q.device)
+    st = lib().linattn_vec_decode_step(pq, pk, pv, pg, po, ps, B, H, dk, dv, dt, _stream(q.device))
+    _check("linattn_vec_decode_step", st)
     return out

@@ -331,6 +331,47 @@ int dec_run(const char* fn, bool gma, bool ccq, lm::DecodeLaunch& La, int64_t d,
   return ok();
 }
 
+int vec_forward(const char* fn, const void* q, const void* k, const void* v, const float* g, void* out, int64_t B,
+                int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
+                const float* state_in, float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = lin_check_shape(fn, B, H, N, dk, dv, chunk, dtype, segments);
+  if (st != LM_OK) return st;
+  if (!q || !k || !v || !g || !out || !workspace) return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 16))
+    return fail(LM_EINVAL, "%s: misaligned pointer (16 bytes needed)", fn);
+  const size_t es = esize(dtype);
+  const size_t nq = (size_t)B * H * N * dk * es, nv = (size_t)B * H * N * dv * es, ng = (size_t)B * H * N * dk * 4;
+  const VecLayout L = vec_layout(B, H, N, dk, segments);
+  if (workspace_bytes < L.total)
+    return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
+  if (overlap(out, nv, q, nq) || overlap(out, nv, k, nq) || overlap(out, nv, v, nv) || overlap(out, nv, g, ng) ||
+      overlap(out, nv, workspace, L.total))
+    return fail(LM_EINVAL, "%s: out overlaps an input or the workspace", fn);
+  if ((st = check_states(fn, state_in, state_out, (size_t)B * H * dk * dv * 4, out, nv, workspace, L.total)) != LM_OK)
+    return st;
+  lm::VecLaunch La;
+  La.q = q;
+  La.k = k;
+  La.v = v;
+  La.g = g;
+  La.out = out;
+  La.agg = static_cast<float*>(workspace);
+  La.B = B;
+  La.H = H;
+  La.N = N;
+  La.D = dk;
+  La.P = L.plan.P;
+  La.seg_len = L.plan.seg_len;
+  La.R = L.R;
+  La.bf16 = dtype == LM_BF16;
+  La.state_in = state_in;
+  La.state_out = state_out;
+  hipError_t e = lm::linattn_vec_launch(La, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -500,42 +541,42 @@ size_t linattn_vec_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, 
   return vec_layout(B, H, N, dk, segments).total;
 }
 
+
 int linattn_vec_forward(const void* q, const void* k, const void* v, const float* g, void* out, int64_t B, int64_t H,
                         int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "linattn_vec_forward";
-  int st = lin_check_shape(fn, B, H, N, dk, dv, chunk, dtype, segments);
+  return vec_forward("linattn_vec_forward", q, k, v, g, out, B, H, N, dk, dv, chunk, dtype, segments, nullptr,
+                     nullptr, workspace, workspace_bytes, stream);
+}
+
+int linattn_vec_forward_state(const void* q, const void* k, const void* v, const float* g, void* out, int64_t B,
+                              int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
+                              int64_t segments, const float* state_in, float* state_out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return vec_forward("linattn_vec_forward_state", q, k, v, g, out, B, H, N, dk, dv, chunk, dtype, segments,
+                     state_in, state_out, workspace, workspace_bytes, stream);
+}
+
+int linattn_vec_decode_step(const void* q, const void* k, const void* v, const float* g, void* out, float* state,
+                            int64_t B, int64_t H, int64_t dk, int64_t dv, int dtype, void* stream) {
+  const char* fn = "linattn_vec_decode_step";
+  int st = dec_check(fn, B, H, dk, dv, dtype);
   if (st != LM_OK) return st;
-  if (!q || !k || !v || !g || !out || !workspace) return fail(LM_EINVAL, "%s: null pointer argument", fn);
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(out, 16) ||
-      !aligned(workspace, 16))
-    return fail(LM_EINVAL, "%s: misaligned pointer (16 bytes needed)", fn);
-  const size_t es = esize(dtype);
-  const size_t nq = (size_t)B * H * N * dk * es, nv = (size_t)B * H * N * dv * es, ng = (size_t)B * H * N * dk * 4;
-  const VecLayout L = vec_layout(B, H, N, dk, segments);
-  if (workspace_bytes < L.total)
-    return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
-  if (overlap(out, nv, q, nq) || overlap(out, nv, k, nq) || overlap(out, nv, v, nv) || overlap(out, nv, g, ng) ||
-      overlap(out, nv, workspace, L.total))
-    return fail(LM_EINVAL, "%s: out overlaps an input or the workspace", fn);
-  lm::VecLaunch La;
+  if (!g) return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(g, 4)) return fail(LM_EINVAL, "%s: misaligned g", fn);
+  lm::DecodeLaunch La{};
   La.q = q;
   La.k = k;
   La.v = v;
   La.g = g;
+  La.vector_gates = true;
   La.out = out;
-  La.agg = static_cast<float*>(workspace);
+  La.state = state;
   La.B = B;
   La.H = H;
-  La.N = N;
   La.D = dk;
-  La.P = L.plan.P;
-  La.seg_len = L.plan.seg_len;
-  La.R = L.R;
   La.bf16 = dtype == LM_BF16;
-  hipError_t e = lm::linattn_vec_launch(La, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
-  return ok();
+  return dec_run(fn, false, false, La, dk, (size_t)dk * dv, stream);
 }
 
 }  // extern "C"

@@ -6,7 +6,8 @@
 //    variant): route q and k to the K components, add gamma(k) v^T and
 //    gamma(k) to the memory [Vtil | Z], read gamma(q) Vtil / (gamma(q) Z + eps).
 //  * Decayed linear attention (allinfo.ai.kr linear attention post, "Key
-//    messages": decay gates on the matrix state): S <- g S + k v^T, o = S^T q.
+//    messages": decay gates on the matrix state): S <- g S + k v^T, o = S^T q,
+//    with one g per (b, h) or one per key feature (row of S).
 //  * CCQ ("Don't Read Everything", section 2 Method): the key sums M += k k^T,
 //    m += k and the count t advance with every token; the read uses
 //    q_clean = q - lambda (M q / t - m (m . q) / t^2), lambda = sigmoid(w . q + b).
@@ -68,8 +69,9 @@ __device__ __forceinline__ float column_sum(float4 acc, float (*sred)[D]) {
 
 // ---------------------------------------------------------------------------
 // Decayed linear attention and CCQ. State per (b,h): [S (D x D) | M (D x D) |
-// m (D)] (M, m for CCQ only). t_now: tokens in the state after this step.
-template <typename T, int D, bool CCQ>
+// m (D)] (M, m for CCQ only). t_now: tokens in the state after this step. VG:
+// one decay per key feature (row of S), g [B,H,D].
+template <typename T, int D, bool CCQ, bool VG>
 __global__ __launch_bounds__(NT) void lin_step(const T* __restrict__ q, const T* __restrict__ k,
                                                const T* __restrict__ v, const float* __restrict__ g,
                                                const float* __restrict__ wl, const float* __restrict__ bl,
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(NT) void lin_step(const T* __restrict__ q, const T*
   typedef Rows<D> R;
   constexpr int NP = D / R::RPP;  // passes over D rows
   constexpr size_t SF = (size_t)D * D + (CCQ ? (size_t)D * D + D : 0);
-  __shared__ float sq[D], sk[D], sv[D], sqc[D], sm[D], sMq[D];
+  __shared__ float sq[D], sk[D], sv[D], sqc[D], sm[D], sMq[D], sg[VG ? D : 1];
   __shared__ float sred[R::RPP][D];
   __shared__ float sdot[2];
   const int bh = blockIdx.x, h = bh % H, tid = threadIdx.x;
@@ -88,8 +90,9 @@ __global__ __launch_bounds__(NT) void lin_step(const T* __restrict__ q, const T*
     sq[tid] = to_f32(q[(size_t)bh * D + tid]);
     sk[tid] = to_f32(k[(size_t)bh * D + tid]);
     sv[tid] = to_f32(v[(size_t)bh * D + tid]);
+    if constexpr (VG) sg[tid] = g[(size_t)bh * D + tid];
   }
-  const float gt = g[bh];
+  const float gt = VG ? 0.f : g[bh];
   __syncthreads();
 
   if constexpr (CCQ) {
@@ -146,7 +149,8 @@ __global__ __launch_bounds__(NT) void lin_step(const T* __restrict__ q, const T*
   for (int p = 0; p < NP; ++p) {
     const int a = r0 + p * R::RPP;
     float4 s = sv4[p];
-    s = make_float4(gt * s.x, gt * s.y, gt * s.z, gt * s.w);
+    const float ga = VG ? sg[a] : gt;
+    s = make_float4(ga * s.x, ga * s.y, ga * s.z, ga * s.w);
     s = fma4(sk[a], vc, s);
     st4(S + (size_t)a * D + 4 * j, s);
     acc = fma4(qr[a], s, acc);
@@ -279,12 +283,12 @@ __global__ __launch_bounds__(NT) void gma_step(const T* __restrict__ q, const T*
   }
 }
 
-template <typename T, bool CCQ>
+template <typename T, bool CCQ, bool VG>
 static hipError_t lin_t(const DecodeLaunch& L, hipStream_t st) {
   const unsigned BH = (unsigned)(L.B * L.H);
   const float t_now = (float)L.t_now;
 #define LM_LIN_STEP(DD)                                                                                        \
-  hipLaunchKernelGGL((lin_step<T, DD, CCQ>), dim3(BH), dim3(NT), 0, st, (const T*)L.q, (const T*)L.k,        \
+  hipLaunchKernelGGL((lin_step<T, DD, CCQ, VG>), dim3(BH), dim3(NT), 0, st, (const T*)L.q, (const T*)L.k,    \
                      (const T*)L.v, L.g, L.w_lambda, L.b_lambda, (T*)L.out, L.state, (int)L.H, t_now)
   switch (L.D) {
     case 32: LM_LIN_STEP(32); break;
@@ -325,8 +329,9 @@ static hipError_t gma_t(const DecodeLaunch& L, hipStream_t st) {
 }  // namespace dec
 
 hipError_t lin_decode_launch(const DecodeLaunch& L, bool ccq, hipStream_t st) {
-  if (L.bf16) return ccq ? dec::lin_t<bf16, true>(L, st) : dec::lin_t<bf16, false>(L, st);
-  return ccq ? dec::lin_t<float, true>(L, st) : dec::lin_t<float, false>(L, st);
+  if (L.vector_gates) return L.bf16 ? dec::lin_t<bf16, false, true>(L, st) : dec::lin_t<float, false, true>(L, st);
+  if (L.bf16) return ccq ? dec::lin_t<bf16, true, false>(L, st) : dec::lin_t<bf16, false, false>(L, st);
+  return ccq ? dec::lin_t<float, true, false>(L, st) : dec::lin_t<float, false, false>(L, st);
 }
 
 hipError_t gma_decode_launch(const DecodeLaunch& L, hipStream_t st) {

@@ -60,6 +60,8 @@ struct VecLaunch {
   int64_t B, H, N, D, P, seg_len;
   int64_t R;  // sub-segments per segment in the segment pass
   bool bf16;
+  const float* state_in;  // optional: S [B*H][D][D] before the first token
+  float* state_out;       // optional: S after the last token
 };
 hipError_t linattn_vec_launch(const VecLaunch& L, hipStream_t st);
 
@@ -73,7 +75,8 @@ struct DecodeLaunch {
   const void* q;
   const void* k;
   const void* v;
-  const float* g;         // linear attention
+  const float* g;         // linear attention: [B,H], or [B,H,D] with vector_gates
+  bool vector_gates;
   const float* w_lambda;  // CCQ
   const float* b_lambda;  // CCQ
   const float* mu;        // GMA

@@ -46,6 +46,7 @@ struct Args {
   int sfl;
   int has_init;  // chunk pass: start from the state block R * (segment index)
   int R;         // sub-segments per segment in the segment pass
+  float* st_out;  // chunk pass (optional): S after the last token, [B*H][D][D]
 };
 
 template <typename T, int D, bool AGG>
@@ -404,6 +405,16 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
     }
   }
 
+  if constexpr (!AGG) {
+    // the workgroup of the last segment holds the state after the last token
+    if (a.st_out && p == (int)gridDim.x - 1) {
+      float* so = a.st_out + (size_t)bh * D * D;
+#pragma unroll
+      for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) so[(16 * kt + 4 * g + r) * D + cbase + c16] = S[kt][r];
+    }
+  }
   if constexpr (AGG) {
     float* blk = a.agg + ((size_t)bh * a.P + p) * a.sfl;
 #pragma unroll
@@ -418,14 +429,16 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
 // 0 .. nsub-1 hold the states of consecutive sub-segments (R per segment) on
 // entry; block R p becomes the state at the start of segment p:
 // run <- diag(G_q) run + S_q over the sub-segments q before it, with G_q the
-// sub-segment's decay per feature (left in place).
-__global__ __launch_bounds__(256) void vec_scan(float* __restrict__ agg, int slots, int nsub, int R, int sfl, int D) {
+// sub-segment's decay per feature (left in place). run starts from the caller's
+// state S (D x D) when there is one, else from zero.
+__global__ __launch_bounds__(256) void vec_scan(float* __restrict__ agg, int slots, int nsub, int R, int sfl, int D,
+                                                const float* __restrict__ init) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= D * D) return;
   const int row = e / D;
   float* base = agg + (size_t)bh * slots * sfl;
-  float run = 0.f;
+  float run = init ? init[(size_t)bh * D * D + e] : 0.f;
   for (int q = 0; q < nsub; ++q) {
     float* x = base + (size_t)q * sfl + e;
     const float s = *x;
@@ -450,16 +463,20 @@ static hipError_t launch_d(const VecLaunch& L, hipStream_t st) {
   a.has_init = 0;
   a.R = (int)L.R;
   a.P = (int)(L.R * L.P);  // state blocks per (b,h)
+  a.st_out = L.state_out;
   const unsigned BH = (unsigned)(L.B * L.H);
-  if (L.P > 1) {
-    // sub-segment states of segments 0 .. P-2, then their prefixes
+  if (L.P > 1 || L.state_in) {
+    // sub-segment states of segments 0 .. P-2, then their prefixes (from the
+    // caller's state when there is one)
     const int nsub = (int)(L.R * (L.P - 1));
     a.seg_len = (int)(L.seg_len / L.R);
-    hipLaunchKernelGGL((vec_kernel<T, D, true>), dim3((unsigned)nsub, BH), dim3(Cfg<T, D, true>::NT), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (nsub > 0) {
+      hipLaunchKernelGGL((vec_kernel<T, D, true>), dim3((unsigned)nsub, BH), dim3(Cfg<T, D, true>::NT), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(vec_scan, dim3((unsigned)((D * D + 255) / 256), BH), dim3(256), 0, st, L.agg, a.P, nsub, a.R,
-                       a.sfl, D);
+                       a.sfl, D, L.state_in);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     a.has_init = 1;
   }

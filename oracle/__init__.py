@@ -69,7 +69,7 @@ class Oracle:
         lib.oracle_gla_forward.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _D, _D]
         lib.oracle_ccq_forward.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I, _D,
                                            _D]
-        lib.oracle_glv_forward.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I]
+        lib.oracle_glv_forward.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _D, _D]
         lib.oracle_gla_chunkwise.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I]
         lib.oracle_ccq_chunkwise.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -158,14 +158,19 @@ class Oracle:
                                     dv, int(t0), _p(sin), _p(sout))
         return (out, sout) if return_state else out
 
-    def glv_forward(self, q, k, v, g) -> np.ndarray:
-        """Recurrent linear attention with a decay per key feature: g [B,H,N,dk]."""
+    def glv_forward(self, q, k, v, g, state_in=None, return_state: bool = False):
+        """Recurrent linear attention with a decay per key feature: g [B,H,N,dk].
+        state_in [B,H,dk*dv] (optional): S before the first token; return_state
+        also returns S after the last one."""
         q, k, v, g = map(_f64, (q, k, v, g))
         B, H, N, dk = q.shape
         dv = v.shape[-1]
         out = np.empty((B, H, N, dv))
-        self.lib.oracle_glv_forward(_p(q), _p(k), _p(v), _p(g), _p(out), B, H, N, dk, dv)
-        return out
+        sin = None if state_in is None else _f64(state_in).reshape(B, H, dk * dv)
+        sout = np.empty((B, H, dk * dv)) if return_state else None
+        self.lib.oracle_glv_forward(_p(q), _p(k), _p(v), _p(g), _p(out), B, H, N, dk, dv, _p(sin),
+                                    _p(sout))
+        return (out, sout) if return_state else out
 
     def gla_chunkwise(self, q, k, v, g, chunk: int = 64) -> np.ndarray:
         q, k, v, g = map(_f64, (q, k, v, g))

@@ -344,7 +344,8 @@ void oracle_ccq_forward(const double* q, const double* k, const double* v, const
  * g [B,H,N,dk]. With g_t[a] the same for every a this is oracle_gla_forward.
  */
 void oracle_glv_forward(const double* q, const double* k, const double* v, const double* g,
-                        double* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv) {
+                        double* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                        const double* st_in, double* st_out) {
   int64_t BH = B * H;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t s = 0; s < BH; ++s) {
@@ -354,6 +355,8 @@ void oracle_glv_forward(const double* q, const double* k, const double* v, const
     const double* gs = g + s * N * dk;
     double* os = out + s * N * dv;
     double* S = (double*)calloc((size_t)(dk * dv), sizeof(double));
+    /* optional state S (dk x dv) before the first token */
+    if (st_in) memcpy(S, st_in + s * dk * dv, sizeof(double) * (size_t)(dk * dv));
     for (int64_t t = 0; t < N; ++t) {
       for (int64_t a = 0; a < dk; ++a)
         for (int64_t e = 0; e < dv; ++e)
@@ -364,6 +367,7 @@ void oracle_glv_forward(const double* q, const double* k, const double* v, const
         os[t * dv + e] = acc;
       }
     }
+    if (st_out) memcpy(st_out + s * dk * dv, S, sizeof(double) * (size_t)(dk * dv));
     free(S);
   }
 }

@@ -438,6 +438,17 @@ def pin_glv(orc):
     ref = np.tril(q[..., keep] @ np.swapaxes(k[..., keep], -1, -2)) @ v
     ref += (q[..., 1] * k[..., 1])[..., None] * v
     assert relerr(got, ref) < 1e-12
+    # carried state: S after a prefix is sum_j diag(prod g) k_j v_j^T, and
+    # continuing from it (also one token at a time) gives the brute-force rows
+    ref = numpy_glv_brute(q, k, v, g)
+    for a in (9, N - 1):
+        o1, st = orc.glv_forward(q[:, :, :a], k[:, :, :a], v[:, :, :a], g[:, :, :a], return_state=True)
+        for h in range(H):
+            want = sum(np.prod(g[0, h, j + 1:a], axis=0)[:, None] * np.outer(k[0, h, j], v[0, h, j])
+                       for j in range(a))
+            assert relerr(st[0, h], want.ravel()) < 1e-12
+        o2 = orc.glv_forward(q[:, :, a:], k[:, :, a:], v[:, :, a:], g[:, :, a:], state_in=st)
+        assert relerr(np.concatenate([o1, o2], 2), ref) < 1e-12
 
 
 ALL_PINS = [

@@ -241,3 +241,19 @@ def test_vec_forward_errors():
     assert call(ch=32) == binding.LM_EUNSUPPORTED
     assert call(N=0) == binding.LM_EINVAL
     assert L.lm_last_error().decode()
+
+
+@needs_lib
+def test_vec_state_and_decode_errors():
+    L = binding.lib()
+    q, k, v, g, out, ws, s0, s1 = (FAKE + (i << 30) for i in range(8))
+    bf = binding.LM_BF16
+    wsb = L.linattn_vec_workspace_bytes(1, 2, 100, 64, 64, 64, bf, 0)
+    fwd = lambda sin, sout: L.linattn_vec_forward_state(q, k, v, g, out, 1, 2, 100, 64, 64, 64, bf, 0, sin, sout, ws,
+                                                        wsb, None)
+    assert fwd(s0 + 8, None) == binding.LM_EINVAL  # misaligned state
+    assert fwd(s0, s0 + 64) == binding.LM_EINVAL  # partial overlap of the two states
+    assert fwd(None, out) == binding.LM_EINVAL  # state_out overlaps out
+    assert L.linattn_vec_decode_step(q, k, v, None, out, s0, 2, 2, 64, 64, bf, None) == binding.LM_EINVAL
+    assert L.linattn_vec_decode_step(q, k, v, g, out, s0, 2, 2, 48, 48, bf, None) == binding.LM_EUNSUPPORTED
+    assert L.linattn_vec_decode_step(q, k, v, g, out, q, 2, 2, 64, 64, bf, None) == binding.LM_EINVAL  # state is q

@@ -34,6 +34,7 @@ MUTANTS = [
      "S[a * dv + e] = gs[t * dk + (e % dk)] * S[a * dv + e]"),
     ("glv_decay_of_previous_token", "S[a * dv + e] = gs[t * dk + a] * S[a * dv + e]",
      "S[a * dv + e] = (t > 0 ? gs[(t - 1) * dk + a] : 1.0) * S[a * dv + e]"),
+    ("glv_state_not_carried", "if (st_in) memcpy(S, st_in + s * dk * dv, sizeof(double) * (size_t)(dk * dv));", ""),
     ("gma_state_out_missing_z", "memcpy(mem_out + K * dv, zt, sizeof(double) * (size_t)K);", ""),
     ("cov_mean_term_dropped", "(M[a * dk + c] / cnt - mu[a] * mu[c]) * qt[c]", "(M[a * dk + c] / cnt) * qt[c]"),
     ("lambda_sign", "qc[a] = qt[a] - lam * sq;", "qc[a] = qt[a] + lam * sq;"),

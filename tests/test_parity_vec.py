@@ -87,3 +87,31 @@ def test_glv_full_size_sampled():
     cfg = inputs.CONFIGS["glv_bf16_n8k"]
     got, ref = _run(cfg, sl=[(0, 0), (7, 15)])
     assert_close(got, ref, "bf16", "glv bf16 8K workload, slices (0,0) and (7,15)")
+
+
+@pytest.mark.parametrize("dtype,dk,segments", [("f32", 64, 1), ("f32", 128, 3), ("bf16", 128, 3), ("f32", 32, 2)])
+def test_glv_state_prefill_continue_decode(dtype, dk, segments):
+    # prefill 300 tokens with the state handed back, continue for 77 from it,
+    # then decode 5 one at a time; every row against the oracle's rows of the
+    # whole sequence, the state against the oracle's state
+    from test_parity_state import cmp_state
+    c1, c2, n = 300, 377, 382
+    cfg = inputs.LinAttnConfig("glv_state", 403, B=2, H=2, N=n, dk=dk, dv=dk, dtype=dtype, vector_gates=True)
+    x = inputs.linattn_inputs(cfg)
+    say("glv state: dk=%d dtype=%s segments=%d" % (dk, dtype, segments))
+    d = cuda(x)
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    ref = oracle.glv_forward(x["q"], x["k"], x["v"], x["g"])
+    _, rs1 = oracle.glv_forward(*[sl(x[m], 0, c1) for m in "qkvg"], return_state=True)
+    _, rs3 = oracle.glv_forward(x["q"], x["k"], x["v"], x["g"], return_state=True)
+    o1, s1 = binding.linattn_vec_forward_state(*[sl(d[m], 0, c1) for m in "qkvg"], segments=segments)
+    assert_close(host(o1), ref[:, :, :c1], dtype, "prefill out")
+    cmp_state(host(s1), rs1, "gla", dk, dtype, "prefill state")
+    o2, s2 = binding.linattn_vec_forward_state(*[sl(d[m], c1, c2) for m in "qkvg"], state_in=s1, state_out=s1,
+                                               segments=segments)
+    assert s2.data_ptr() == s1.data_ptr()
+    assert_close(host(o2), ref[:, :, c1:c2], dtype, "continuation out")
+    outs = [host(binding.linattn_vec_decode_step(*[d[m][:, :, i].contiguous() for m in "qkvg"], s2))
+            for i in range(c2, n)]
+    assert_close(np.stack(outs, axis=2), ref[:, :, c2:], dtype, "decode out")
+    cmp_state(host(s2), rs3, "gla", dk, dtype, "state after decode")
