@@ -299,7 +299,7 @@ def main():
 
 
 def decode_steps(torch, dev, steps=20):
-    """One-token steps of the three mixers at the model shapes of the 16K-token
+    """One-token steps of the mixers at the model shapes of the 8K- and 16K-token
     workloads, with batches whose states (about 0.5 GB) exceed the 256 MB
     last-level cache. Algorithmic bytes per step: the state read and written
     once, plus q, k, v, out (and g) in bf16."""
@@ -311,6 +311,7 @@ def decode_steps(torch, dev, steps=20):
     gen = torch.Generator(device=dev).manual_seed(7)
     for name, kind, B, H, d, K in (("gma_decode_b2048_h8_d64_k128", "gma", 2048, 8, 64, 128),
                                    ("gla_decode_b512_h16_d128", "gla", 512, 16, 128, 0),
+                                   ("glv_decode_b512_h16_d128", "glv", 512, 16, 128, 0),
                                    ("ccq_decode_b256_h16_d128", "ccq", 256, 16, 128, 0)):
         rnd = lambda *shape: torch.randn(*shape, generator=gen, device=dev)
         q, k, v = (rnd(B, H, d).bfloat16() for _ in range(3))
@@ -321,14 +322,16 @@ def decode_steps(torch, dev, steps=20):
             call = lambda st: lm.gma_decode_step(q, k, v, mu, lv, lp, st, out=out)
         else:
             sf = lm.ccq_state_size(d, d) if kind == "ccq" else lm.linattn_state_size(d, d)
-            g = torch.sigmoid(rnd(B, H) + 3.0)
-            if kind == "ccq":
+            g = torch.sigmoid(rnd(B, H, d) + 3.0) if kind == "glv" else torch.sigmoid(rnd(B, H) + 3.0)
+            if kind == "glv":
+                call = lambda st: lm.linattn_vec_decode_step(q, k, v, g, st, out=out)
+            elif kind == "ccq":
                 w, b = rnd(H, d) / d ** 0.5, torch.full((H,), -2.0, device=dev)
                 call = lambda st: lm.ccq_decode_step(q, k, v, g, w, b, st, t_prev=16384, out=out)
             else:
                 call = lambda st: lm.linattn_decode_step(q, k, v, g, st, out=out)
         st = rnd(B, H, sf) * 0.01
-        io = B * H * (4 * d * 2 + (4 if kind != "gma" else 0))
+        io = B * H * (4 * d * 2 + {"gma": 0, "glv": 4 * d}.get(kind, 4))
         nbytes = 2 * st.numel() * 4 + io
         for _ in range(3):
             call(st)
