@@ -219,3 +219,54 @@ def test_gma_decode_from_empty_state(B):
                                  return_state=True)
     assert_close(np.stack(outs, axis=2), ref, "f32", "decode-only out")
     cmp_state(host(st), rs, "gma", (32, 20), "f32", "decode-only memory")
+
+
+@pytest.mark.parametrize("kind", ["gla", "ccq", "gma"])
+@pytest.mark.parametrize("n2", [1, 64])
+def test_continuation_lengths_and_no_state_out(kind, n2):
+    # a continuation of one token and of exactly one chunk, through the raw ABI
+    # with state_out = NULL (the binding always asks for the state)
+    n1 = 130
+    if kind == "gma":
+        cfg = inputs.GmaConfig("state_len", 305, B=1, H=3, N=n1 + n2, d=32, K=12, dv=32, dtype="f32", eps=1e-6)
+        x = inputs.gma_inputs(cfg)
+    else:
+        cfg = inputs.LinAttnConfig("state_len", 305, B=1, H=3, N=n1 + n2, dk=32, dv=32, dtype="f32")
+        x = inputs.linattn_inputs(cfg, ccq=kind == "ccq")
+    d = cuda(x)
+    say("continuation %s n1=%d n2=%d" % (kind, n1, n2))
+    pre = {m: _sl(d[m], 0, n1) for m in ("qkvg" if kind != "gma" else "qkv")}
+    post = {m: _sl(d[m], n1, n1 + n2) for m in ("qkvg" if kind != "gma" else "qkv")}
+    L = binding.lib()
+    out = torch.empty_like(post["v"])
+    if kind == "gma":
+        _, st = binding.gma_forward_state(pre["q"], pre["k"], pre["v"], d["mu"], d["log_var"], d["logit_pi"],
+                                          eps=cfg.eps, segments=2)
+        nb = binding.gma_workspace_bytes(1, 3, n2, 32, 12, 32, True, torch.float32, 0)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        rc = L.gma_forward_state(post["q"].data_ptr(), post["k"].data_ptr(), post["v"].data_ptr(),
+                                 d["mu"].data_ptr(), d["log_var"].data_ptr(), d["logit_pi"].data_ptr(),
+                                 out.data_ptr(), 1, 3, n2, 32, 12, 32, cfg.eps, binding.LM_F32, 0, st.data_ptr(),
+                                 None, ws.data_ptr(), nb, torch.cuda.current_stream().cuda_stream)
+        ref = oracle.gma_forward(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"], True, cfg.eps)
+    elif kind == "gla":
+        _, st = binding.linattn_chunk_forward_state(pre["q"], pre["k"], pre["v"], pre["g"], segments=2)
+        nb = binding.linattn_workspace_bytes(1, 3, n2, 32, 32, 64, torch.float32, 0)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        rc = L.linattn_chunk_forward_state(post["q"].data_ptr(), post["k"].data_ptr(), post["v"].data_ptr(),
+                                           post["g"].data_ptr(), out.data_ptr(), 1, 3, n2, 32, 32, 64,
+                                           binding.LM_F32, 0, st.data_ptr(), None, ws.data_ptr(), nb,
+                                           torch.cuda.current_stream().cuda_stream)
+        ref = oracle.gla_forward(x["q"], x["k"], x["v"], x["g"])
+    else:
+        _, st = binding.ccq_forward_state(pre["q"], pre["k"], pre["v"], pre["g"], d["w_lambda"], d["b_lambda"],
+                                          segments=2)
+        nb = binding.ccq_workspace_bytes(1, 3, n2, 32, 32, 64, torch.float32, 0)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        rc = L.ccq_forward_state(post["q"].data_ptr(), post["k"].data_ptr(), post["v"].data_ptr(),
+                                 post["g"].data_ptr(), d["w_lambda"].data_ptr(), d["b_lambda"].data_ptr(),
+                                 out.data_ptr(), 1, 3, n2, 32, 32, 64, binding.LM_F32, 0, n1, st.data_ptr(), None,
+                                 ws.data_ptr(), nb, torch.cuda.current_stream().cuda_stream)
+        ref = oracle.ccq_forward(x["q"], x["k"], x["v"], x["g"], x["w_lambda"], x["b_lambda"])
+    assert rc == binding.LM_OK, L.lm_last_error().decode()
+    assert_close(host(out), ref[:, :, n1:], "f32", "continuation of %d token(s)" % n2)
