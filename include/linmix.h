@@ -1,7 +1,7 @@
 /*
  * linmix.h -- C ABI of the MI355X (gfx950) sequence-mixer forward library.
  *
- * Three forward passes, each a drop-in replacement for an attention layer:
+ * Four forward passes, each a drop-in replacement for an attention layer:
  *
  *  gma_forward            Gaussian Mixture Attention. Rows of Q and K are routed
  *                         to K diagonal-Gaussian components; keys write a K-slot
@@ -32,11 +32,13 @@
  * Carried state (prefill, then one token at a time). The causal forms need
  * nothing from the past but a fixed-size state per (b, h), so a sequence can
  * be continued in a later call:
- *  gma_forward_state, linattn_chunk_forward_state, ccq_forward_state
+ *  gma_forward_state, linattn_chunk_forward_state, ccq_forward_state,
+ *  linattn_vec_forward_state
  *                         the forwards above, starting from a caller's state
  *                         (optional) and writing the state after the last
  *                         token (optional).
- *  gma_decode_step, linattn_decode_step, ccq_decode_step
+ *  gma_decode_step, linattn_decode_step, ccq_decode_step,
+ *  linattn_vec_decode_step
  *                         one token per (b, h): advance the state in place and
  *                         read it.
  *                         Source: "Gaussian Mixture Attention", Method ->
@@ -50,7 +52,8 @@
  *    GMA   [Vtil (K x dv) | Z (K)]            K*dv + K floats:
  *          Vtil = sum_j gamma(k_j) v_j^T, Z = sum_j gamma(k_j)
  *    GLA   [S (dk x dv)]                      dk*dv floats:
- *          S = sum_j (prod_{s > j} g_s) k_j v_j^T
+ *          S = sum_j (prod_{s > j} g_s) k_j v_j^T (per-feature decay: the
+ *          product scales row a of k_j v_j^T by prod_{s > j} g_s[a])
  *    CCQ   [S (dk x dv) | M (dk x dk) | m (dk)]  dk*dv + dk*dk + dk floats:
  *          M = sum_j k_j k_j^T, m = sum_j k_j (no decay)
  *    A zero-filled block is the state of an empty prefix. The CCQ state also
