@@ -68,8 +68,9 @@
  *    LM_BF16 (bfloat16). Parameters (mu, log_var, logit_pi, g, w_lambda,
  *    b_lambda) are always float32. Accumulation is float32.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
- *    stream). Inputs are read-only. On LM_OK, out is fully overwritten once
- *    the stream reaches the call. out must not overlap any input or the
+ *    stream). Inputs are read-only (the decode steps' state is the one
+ *    argument that is both read and written). On LM_OK, out (and state_out)
+ *    is fully overwritten once the stream reaches the call. out must not overlap any input or the
  *    workspace.
  *  - The library allocates no device memory on these calls. Scratch space
  *    comes from the caller's `workspace` of at least the size returned by the
