@@ -451,10 +451,38 @@ def pin_glv(orc):
         assert relerr(np.concatenate([o1, o2], 2), ref) < 1e-12
 
 
+def pin_gla_backward(orc):
+    """Gradients of the decayed linear attention: the autograd oracle's forward
+    equals oracle.c's recurrence, and every gradient (q, k, v and the gates)
+    equals central finite differences of oracle.c's forward."""
+    from oracle import grad
+    rng = _rng(601)
+    B, H, N, dk, dv = 1, 2, 6, 3, 2
+    q = rng.standard_normal((B, H, N, dk))
+    k = rng.standard_normal((B, H, N, dk))
+    v = rng.standard_normal((B, H, N, dv))
+    g = rng.uniform(0.3, 1.0, (B, H, N))
+    do = rng.standard_normal((B, H, N, dv))
+    fw = grad.gla_forward_torch(*[grad._t(x) for x in (q, k, v, g)]).numpy()
+    assert relerr(fw, orc.gla_forward(q, k, v, g)) < 1e-12
+    dq, dk_, dv_, dg = grad.gla_backward(q, k, v, g, do)
+    loss = lambda q_, k_, v_, g_: float(np.sum(orc.gla_forward(q_, k_, v_, g_) * do))
+    h = 1e-6
+    for idx, (x, gx) in enumerate(((q, dq), (k, dk_), (v, dv_), (g, dg))):
+        num = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp = x.copy(); xp[pos] += h
+            xm = x.copy(); xm[pos] -= h
+            args_p = [q, k, v, g]; args_p[idx] = xp
+            args_m = [q, k, v, g]; args_m[idx] = xm
+            num[pos] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert relerr(gx, num) < 1e-7, ("gradient", idx, relerr(gx, num))
+
+
 ALL_PINS = [
     pin_gamma_scipy, pin_gma_brute_numpy, pin_gma_k1_closed_form, pin_gma_identical_components,
     pin_gma_permutation, pin_gma_prefix, pin_gma_affinity_structure, pin_gma_golden,
     pin_gla_brute, pin_gla_chunkwise, pin_ccq_numpy_cov, pin_cov_is_logpartition_hessian,
     pin_ccq_reductions, pin_ccq_chunkwise, pin_ccq_golden, pin_gma_state, pin_gla_state,
-    pin_ccq_state, pin_glv,
+    pin_ccq_state, pin_glv, pin_gla_backward,
 ]
