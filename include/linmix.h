@@ -202,6 +202,26 @@ int linattn_vec_decode_step(const void* q, const void* k, const void* v, const f
                             int dtype, void* stream);
 
 /*
+ * Backward pass of decayed linear attention (scalar gate): given the output
+ * gradient dout [B,H,N,dv] of linattn_chunk_forward(q, k, v, g), writes
+ *   dq, dk [B,H,N,dk], dv [B,H,N,dv] (dtype) and dg [B,H,N] (float32),
+ * the gradients of sum(out * dout). Computed as three chunkwise passes of the
+ * forward kernel (dq = S_t dout_t; dk, dv from the state gradient
+ * U_t = q_t dout_t^T + g_{t+1} U_{t+1}, run on the time-reversed sequence) and
+ * dg_t = (1/g_t) sum_{m >= t} (q_m . dq_m - k_m . dk_m).
+ * Source: allinfo.ai.kr post on linear attention, "Key messages" (matrix state
+ * with decay gates; the chunkwise form is what makes training parallel).
+ * Outputs must not overlap each other, the inputs or the workspace (of at least
+ * linattn_backward_workspace_bytes). Shapes as for linattn_chunk_forward.
+ */
+size_t linattn_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                                        int64_t chunk, int dtype, int64_t segments);
+int linattn_chunk_backward(const void* q, const void* k, const void* v, const float* g,
+                           const void* dout, void* dq, void* dk, void* dv, float* dg, int64_t B,
+                           int64_t H, int64_t N, int64_t dkk, int64_t dvv, int64_t chunk, int dtype,
+                           int64_t segments, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forwards on a carried state. Arguments as for the forward of the same name
  * (gma_forward_state is the causal GMA forward; the workspace is the one
  * gma_workspace_bytes gives for causal = 1), plus:

@@ -59,6 +59,8 @@ _SIGS = {
     "linattn_vec_forward_state": ([_P] * 5 + [_I64] * 6 + [ctypes.c_int, _I64, _P, _P, _P, ctypes.c_size_t, _P],
                                   ctypes.c_int),
     "linattn_vec_decode_step": ([_P] * 6 + [_I64] * 4 + [ctypes.c_int, _P], ctypes.c_int),
+    "linattn_backward_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
+    "linattn_chunk_backward": ([_P] * 9 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
 }
 
 
@@ -428,3 +430,27 @@ def linattn_vec_decode_step(q, k, v, g, state, out: Optional[torch.Tensor] = Non
     st = lib().linattn_vec_decode_step(pq, pk, pv, pg, po, ps, B, H, dk, dv, dt, _stream(q.device))
     _check("linattn_vec_decode_step", st)
     return out
+
+
+# ----------------------------------------------------------------------------- backward
+
+def linattn_backward_workspace_bytes(B, H, N, dk, dv, chunk=64, dtype=torch.bfloat16, segments=0) -> int:
+    return int(lib().linattn_backward_workspace_bytes(B, H, N, dk, dv, chunk, _DT[dtype], segments))
+
+
+def linattn_chunk_backward(q, k, v, g, dout, chunk: int = 64, segments: int = 0,
+                           workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv, dg) of sum(out * dout) for
+    out = linattn_chunk_forward(q, k, v, g); dq, dk, dv in the input dtype, dg float32."""
+    dt = _dtype_code(q)
+    (B, H, N, dk, dv), (pq, pk, pv, pg), _, _ = _lin_common(q, k, v, g, torch.empty_like(v))
+    pdo = _dev(dout, "dout", q.dtype, (B, H, N, dv))
+    dq, dkt, dvt = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    nbytes = linattn_backward_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    st = lib().linattn_chunk_backward(pq, pk, pv, pg, pdo, dq.data_ptr(), dkt.data_ptr(), dvt.data_ptr(),
+                                      dg.data_ptr(), B, H, N, dk, dv, chunk, dt, segments,
+                                      ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
+    _check("linattn_chunk_backward", st)
+    return dq, dkt, dvt, dg

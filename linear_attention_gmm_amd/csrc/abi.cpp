@@ -579,4 +579,94 @@ int linattn_vec_decode_step(const void* q, const void* k, const void* v, const f
   return dec_run(fn, false, false, La, dk, (size_t)dk * dv, stream);
 }
 
+size_t linattn_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                                        int dtype, int64_t segments) {
+  if (lin_check_shape("linattn_chunk_backward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
+  // float32 tensors: 5 for the reversed passes, and for bf16 inputs 7 more
+  // (float32 copies of q, k, v, do and the gradients before rounding)
+  const size_t t = align_up((size_t)B * H * N * dk * 4);
+  return (dtype == LM_BF16 ? 12 : 5) * t + align_up((size_t)B * H * N * 4) +
+         lin_layout(B, H, N, dk, false, segments).total;
+}
+
+int linattn_chunk_backward(const void* q, const void* k, const void* v, const float* g, const void* dout, void* dq,
+                           void* dk, void* dv, float* dg, int64_t B, int64_t H, int64_t N, int64_t dkk, int64_t dvv,
+                           int64_t chunk, int dtype, int64_t segments, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const char* fn = "linattn_chunk_backward";
+  int st = lin_check_shape(fn, B, H, N, dkk, dvv, chunk, dtype, segments);
+  if (st != LM_OK) return st;
+  if (!q || !k || !v || !g || !dout || !dq || !dk || !dv || !dg || !workspace)
+    return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  const void* ptrs16[] = {q, k, v, dout, dq, dk, dv, workspace};
+  for (const void* p : ptrs16)
+    if (!aligned(p, 16)) return fail(LM_EINVAL, "%s: misaligned pointer (tensors need 16 bytes)", fn);
+  if (!aligned(g, 4) || !aligned(dg, 4)) return fail(LM_EINVAL, "%s: misaligned g or dg", fn);
+  const size_t es = esize(dtype), nt = (size_t)B * H * N * dkk * es, ng = (size_t)B * H * N * 4;
+  const size_t t = align_up((size_t)B * H * N * dkk * 4);
+  const size_t need = linattn_backward_workspace_bytes(B, H, N, dkk, dvv, chunk, dtype, segments);
+  if (workspace_bytes < need)
+    return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+  // outputs must not overlap each other, the inputs or the workspace
+  const void* outs[] = {dq, dk, dv, dg};
+  const size_t nout[] = {nt, nt, nt, ng};
+  const void* ins[] = {q, k, v, dout, g, workspace};
+  const size_t nin[] = {nt, nt, nt, nt, ng, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], nout[i], ins[j], nin[j]))
+        return fail(LM_EINVAL, "%s: an output overlaps an input or the workspace", fn);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], nout[i], outs[j], nout[j])) return fail(LM_EINVAL, "%s: outputs overlap", fn);
+  }
+  char* ws = static_cast<char*>(workspace);
+  const LinLayout LL = lin_layout(B, H, N, dkk, false, segments);
+  lm::BwdLaunch La;
+  const int nten = dtype == LM_BF16 ? 12 : 5;
+  La.fwd.agg = reinterpret_cast<float*>(ws + nten * t + align_up(ng) + LL.agg);
+  La.fwd.w_lambda = nullptr;
+  La.fwd.b_lambda = nullptr;
+  La.fwd.B = B;
+  La.fwd.H = H;
+  La.fwd.N = N;
+  La.fwd.D = dkk;
+  La.fwd.P = LL.plan.P;
+  La.fwd.seg_len = LL.plan.seg_len;
+  La.fwd.R = LL.R;
+  La.fwd.bf16 = dtype == LM_BF16;
+  La.q = q;
+  La.k = k;
+  La.v = v;
+  La.g = g;
+  La.dout = dout;
+  La.dq = dq;
+  La.dk = dk;
+  La.dv = dv;
+  La.dg = dg;
+  float* f[12];
+  for (int i = 0; i < nten; ++i) f[i] = reinterpret_cast<float*>(ws + i * t);
+  for (int i = nten; i < 12; ++i) f[i] = nullptr;
+  La.rq = f[0];
+  La.rk = f[1];
+  La.rv = f[2];
+  La.rdo = f[3];
+  La.rout = f[4];
+  La.uq = f[5];
+  La.uk = f[6];
+  La.uv = f[7];
+  La.udo = f[8];
+  La.udq = f[9];
+  La.udk = f[10];
+  La.udv = f[11];
+  La.rg = reinterpret_cast<float*>(ws + nten * t);
+  La.B = B;
+  La.H = H;
+  La.N = N;
+  La.D = dkk;
+  La.bf16 = dtype == LM_BF16;
+  hipError_t e = lm::linattn_backward_launch(La, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

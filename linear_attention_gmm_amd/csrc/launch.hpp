@@ -92,6 +92,40 @@ struct DecodeLaunch {
 hipError_t lin_decode_launch(const DecodeLaunch& L, bool ccq, hipStream_t st);
 hipError_t gma_decode_launch(const DecodeLaunch& L, hipStream_t st);
 
+// Backward pass of decayed linear attention (linattn_bwd.hip): three chunk-
+// kernel passes on reordered inputs plus the gate gradient.
+struct BwdLaunch {
+  LinLaunch fwd;  // shapes, segment plan and workspace of the chunk passes
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  // workspace (float32): time-reversed q, k, v, do, one reversed output,
+  // shifted gates; for bf16 inputs also float32 copies of q, k, v, do and the
+  // float32 gradients dq, dk, dv before rounding
+  float* rq;
+  float* rk;
+  float* rv;
+  float* rdo;
+  float* rout;
+  float* rg;
+  float* uq;
+  float* uk;
+  float* uv;
+  float* udo;
+  float* udq;
+  float* udk;
+  float* udv;
+  int64_t B, H, N, D;
+  bool bf16;
+};
+hipError_t linattn_backward_launch(const BwdLaunch& L, hipStream_t st);
+
 // Floats per state block written by the segment-state pass.
 inline int64_t lin_state_floats(int64_t D, bool ccq) {
   // S (D x D), decay product, and for CCQ: M (D x D), m (D); padded to 64 floats

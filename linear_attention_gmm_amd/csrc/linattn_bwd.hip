@@ -1,0 +1,194 @@
+// linattn_bwd.hip -- helper kernels of the backward pass of decayed linear
+// attention (allinfo.ai.kr linear attention post, "Key messages": the matrix
+// state with decay gates; the gradients follow from the recurrence).
+//
+// With S_t = g_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t and the output gradient
+// do_t, the gradients are again decayed linear attentions, so the chunk kernel
+// computes them:
+//   dq_t = S_t do_t                         forward(q = do, k = v, v = k, g)
+//   U_t  = q_t do_t^T + g_{t+1} U_{t+1}     (gradient of the state)
+//   dk_t = U_t v_t, dv_t = U_t^T k_t        forward on the time-reversed
+//                                           sequence with the gates shifted by
+//                                           one token
+//   dg_t = (1 / g_t) sum_{m >= t} (q_m . dq_m - k_m . dk_m)
+// (the last line: the loss depends on the gates through the decays
+// exp(L_i - L_j), L the cumulative log gate; the derivative with respect to L_m
+// is q_m . dq_m - k_m . dk_m, and L_m sums the log gates up to m).
+// The kernels below reverse sequences in time, shift the gates and form dg.
+// For bf16 inputs every pass runs in float32 on float32 copies and the
+// gradients are rounded once at the end: dg is a difference of two dot products
+// that nearly cancel, which bf16-rounded dq and dk would not resolve.
+#include "mfma.hpp"
+#include "launch.hpp"
+
+namespace lm {
+namespace bwd {
+
+// out[bh][t][:] = in[bh][N - 1 - t][:], in 16-byte pieces (D * es a multiple of 16).
+__global__ __launch_bounds__(256) void reverse_time(const char* __restrict__ in, char* __restrict__ out, int64_t N,
+                                                    int row_bytes, int64_t total16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total16) return;
+  const int per_row = row_bytes / 16;
+  const int64_t row = i / per_row;  // bh * N + t
+  const int c = (int)(i - row * per_row);
+  const int64_t bh = row / N, t = row - bh * N;
+  const int64_t src = bh * N + (N - 1 - t);
+  *reinterpret_cast<uint4*>(out + row * row_bytes + (int64_t)c * 16) =
+      *reinterpret_cast<const uint4*>(in + src * row_bytes + (int64_t)c * 16);
+}
+
+// Gates of the reversed recurrence: gr[bh][t'] = g[bh][N - t'] for t' >= 1; the
+// first reversed token has no successor, so its gate multiplies zero (1 here).
+__global__ __launch_bounds__(256) void shift_gates(const float* __restrict__ g, float* __restrict__ gr, int64_t N,
+                                                   int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t bh = i / N, t = i - bh * N;
+  gr[i] = t == 0 ? 1.f : g[bh * N + (N - t)];
+}
+
+// dg for one (b, h) per workgroup: x_m = q_m . dq_m - k_m . dk_m (fp32), then
+// the suffix sums over m, divided by g_m. Thread i owns tokens [i len, (i+1) len);
+// x is parked in dg between the two passes.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gate_grad(const T* __restrict__ q, const T* __restrict__ dq,
+                                                 const T* __restrict__ k, const T* __restrict__ dk,
+                                                 const float* __restrict__ g, float* __restrict__ dg, int64_t N) {
+  typedef typename Vec16<T>::type vec;
+  constexpr int EV = Vec16<T>::n;
+  __shared__ float stot[256];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int64_t len = (N + 255) / 256;
+  const int64_t t0 = (int64_t)tid * len, t1 = t0 + len < N ? t0 + len : N;
+  const size_t base = (size_t)bh * N;
+  float tot = 0.f;
+  for (int64_t m = t0; m < t1; ++m) {
+    const vec* pq = reinterpret_cast<const vec*>(q + (base + m) * D);
+    const vec* pdq = reinterpret_cast<const vec*>(dq + (base + m) * D);
+    const vec* pk = reinterpret_cast<const vec*>(k + (base + m) * D);
+    const vec* pdk = reinterpret_cast<const vec*>(dk + (base + m) * D);
+    float x = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < D / EV; ++c) {
+      const vec a = pq[c], b = pdq[c], e = pk[c], f = pdk[c];
+#pragma unroll
+      for (int i = 0; i < EV; ++i) x += to_f32(a[i]) * to_f32(b[i]) - to_f32(e[i]) * to_f32(f[i]);
+    }
+    dg[base + m] = x;
+    tot += x;
+  }
+  stot[tid] = tot;
+  __syncthreads();
+  float run = 0.f;  // sum over the ranges after this thread's
+  for (int u = tid + 1; u < 256; ++u) run += stot[u];
+  for (int64_t m = t1 - 1; m >= t0; --m) {
+    run += dg[base + m];
+    dg[base + m] = run / g[base + m];
+  }
+}
+
+// Element-wise conversion (float32 <-> bf16), n elements (a multiple of 4).
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void convert(const TI* __restrict__ in, TO* __restrict__ out, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[4 * i + j] = from_f32<TO>(to_f32(in[4 * i + j]));
+}
+
+template <typename TI, typename TO>
+static hipError_t convert_n(const void* in, void* out, int64_t n, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL((convert<TI, TO>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const TI*>(in), static_cast<TO*>(out), n4);
+  return hipGetLastError();
+}
+
+static hipError_t gate_grad_f32(const BwdLaunch& L, const float* q, const float* dq, const float* k, const float* dk,
+                                hipStream_t st) {
+  const unsigned BH = (unsigned)(L.B * L.H);
+#define LM_GG(DD)                                                                                              \
+  hipLaunchKernelGGL((gate_grad<float, DD>), dim3(BH), dim3(256), 0, st, q, dq, k, dk, L.g, L.dg, L.N)
+  switch (L.D) {
+    case 32: LM_GG(32); break;
+    case 64: LM_GG(64); break;
+    case 128: LM_GG(128); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef LM_GG
+  return hipGetLastError();
+}
+
+static hipError_t reverse(const void* in, void* out, const BwdLaunch& L, hipStream_t st) {
+  const int row_bytes = (int)(L.D * 4);
+  const int64_t total16 = L.B * L.H * L.N * (row_bytes / 16);
+  hipLaunchKernelGGL(reverse_time, dim3((unsigned)((total16 + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const char*>(in), static_cast<char*>(out), L.N, row_bytes, total16);
+  return hipGetLastError();
+}
+
+// The whole backward in float32: three chunk-kernel passes (dq; dk and dv on
+// the reversed sequence), the reversals around them and the gate gradient.
+static hipError_t run_f32(const BwdLaunch& L, const float* q, const float* k, const float* v, const float* dout,
+                          float* dq, float* dk, float* dv, hipStream_t st) {
+  hipError_t e;
+  LinLaunch F = L.fwd;  // shapes, segment plan, workspace; pointers set per pass
+  F.bf16 = false;
+  F.ccq = false;
+  F.state_in = nullptr;
+  F.state_out = nullptr;
+  F.t_in = 0;
+  // dq = forward(q = do, k = v, v = k, g)
+  F.q = dout;
+  F.k = v;
+  F.v = k;
+  F.g = L.g;
+  F.out = dq;
+  if ((e = linattn_launch(F, st)) != hipSuccess) return e;
+  // reversed inputs and shifted gates
+  if ((e = reverse(q, L.rq, L, st)) != hipSuccess) return e;
+  if ((e = reverse(k, L.rk, L, st)) != hipSuccess) return e;
+  if ((e = reverse(v, L.rv, L, st)) != hipSuccess) return e;
+  if ((e = reverse(dout, L.rdo, L, st)) != hipSuccess) return e;
+  const int64_t tot = L.B * L.H * L.N;
+  hipLaunchKernelGGL(shift_gates, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, L.g, L.rg, L.N, tot);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // dk (reversed) = forward(q = rev v, k = rev do, v = rev q, shifted gates)
+  F.q = L.rv;
+  F.k = L.rdo;
+  F.v = L.rq;
+  F.g = L.rg;
+  F.out = L.rout;
+  if ((e = linattn_launch(F, st)) != hipSuccess) return e;
+  if ((e = reverse(L.rout, dk, L, st)) != hipSuccess) return e;
+  // dv (reversed) = forward(q = rev k, k = rev q, v = rev do, shifted gates)
+  F.q = L.rk;
+  F.k = L.rq;
+  F.v = L.rdo;
+  F.out = L.rout;
+  if ((e = linattn_launch(F, st)) != hipSuccess) return e;
+  if ((e = reverse(L.rout, dv, L, st)) != hipSuccess) return e;
+  return gate_grad_f32(L, q, dq, k, dk, st);
+}
+
+}  // namespace bwd
+
+hipError_t linattn_backward_launch(const BwdLaunch& L, hipStream_t st) {
+  using namespace bwd;
+  if (!L.bf16)
+    return run_f32(L, (const float*)L.q, (const float*)L.k, (const float*)L.v, (const float*)L.dout, (float*)L.dq,
+                   (float*)L.dk, (float*)L.dv, st);
+  const int64_t n = L.B * L.H * L.N * L.D;
+  hipError_t e;
+  if ((e = convert_n<bf16, float>(L.q, L.uq, n, st)) != hipSuccess) return e;
+  if ((e = convert_n<bf16, float>(L.k, L.uk, n, st)) != hipSuccess) return e;
+  if ((e = convert_n<bf16, float>(L.v, L.uv, n, st)) != hipSuccess) return e;
+  if ((e = convert_n<bf16, float>(L.dout, L.udo, n, st)) != hipSuccess) return e;
+  if ((e = run_f32(L, L.uq, L.uk, L.uv, L.udo, L.udq, L.udk, L.udv, st)) != hipSuccess) return e;
+  if ((e = convert_n<float, bf16>(L.udq, L.dq, n, st)) != hipSuccess) return e;
+  if ((e = convert_n<float, bf16>(L.udk, L.dk, n, st)) != hipSuccess) return e;
+  return convert_n<float, bf16>(L.udv, L.dv, n, st);
+}
+
+}  // namespace lm

@@ -257,3 +257,22 @@ def test_vec_state_and_decode_errors():
     assert L.linattn_vec_decode_step(q, k, v, None, out, s0, 2, 2, 64, 64, bf, None) == binding.LM_EINVAL
     assert L.linattn_vec_decode_step(q, k, v, g, out, s0, 2, 2, 48, 48, bf, None) == binding.LM_EUNSUPPORTED
     assert L.linattn_vec_decode_step(q, k, v, g, out, q, 2, 2, 64, 64, bf, None) == binding.LM_EINVAL  # state is q
+
+
+@needs_lib
+def test_backward_errors():
+    L = binding.lib()
+    q, k, v, g, do, dq, dk, dv, dg, ws = (FAKE + (i << 30) for i in range(10))
+    bf = binding.LM_BF16
+    wsb = L.linattn_backward_workspace_bytes(1, 2, 100, 64, 64, 64, bf, 0)
+    assert wsb > L.linattn_workspace_bytes(1, 2, 100, 64, 64, 64, bf, 0)
+    call = lambda **kw: L.linattn_chunk_backward(q, k, v, g, do, kw.get("dq", dq), dk, dv, kw.get("dg", dg), 1, 2,
+                                                 100, kw.get("d", 64), kw.get("d", 64), 64, bf, 0, ws,
+                                                 kw.get("wsb", wsb), None)
+    assert call(wsb=wsb - 1) == binding.LM_EWORKSPACE
+    assert call(dq=dk) == binding.LM_EINVAL  # two outputs in one buffer
+    assert call(dq=q + 64) == binding.LM_EINVAL  # output overlaps an input
+    assert call(dg=dg + 2) == binding.LM_EINVAL  # misaligned
+    assert call(dq=None) == binding.LM_EINVAL
+    assert call(d=48) == binding.LM_EUNSUPPORTED
+    assert L.lm_last_error().decode()
