@@ -107,7 +107,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--secondary", action="store_true", help="also time bidirectional GMA, GLA and long GMA")
+    ap.add_argument("--secondary", action="store_true",
+                    help="also time bidirectional GMA, GLA (forward and backward), per-feature decay and long GMA")
     ap.add_argument("--decode", action="store_true",
                     help="also time the one-token decode steps on states larger than the last-level cache")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -245,8 +246,8 @@ def main():
 
     if args.secondary:
         sec = {}
-        for name, fn in (("gma_bidir_n16k", "bidir"), ("gla_bf16_n8k", "gla"), ("glv_bf16_n8k", "glv"),
-                         ("gma_bf16_n128k", "gma5")):
+        for name, fn in (("gma_bidir_n16k", "bidir"), ("gla_bf16_n8k", "gla"), ("gla_backward_bf16_n8k", "glab"),
+                         ("glv_bf16_n8k", "glv"), ("gma_bf16_n128k", "gma5")):
             if fn == "bidir":
                 a = gset[0]
                 call = lambda: gma_forward(a["q"], a["k"], a["v"], a["mu"], a["log_var"], a["logit_pi"],
@@ -258,6 +259,17 @@ def main():
                 call = lambda: linattn_chunk_forward(x["q"], x["k"], x["v"], x["g"])
                 tok = cfg.B * cfg.H * cfg.N
                 byt = tok * ccq_bytes_per_head_token(cfg)
+            elif fn == "glab":
+                from linear_attention_gmm_amd import linattn_backward_workspace_bytes, linattn_chunk_backward
+                cfg = inputs.CONFIGS["gla_bf16_n8k"]
+                xb = {k: v.to(dev) for k, v in inputs.linattn_inputs(cfg).items()}
+                dout = torch.randn_like(xb["v"])
+                wsb = torch.empty(linattn_backward_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.dk, cfg.dv, 64,
+                                                                   torch.bfloat16), dtype=torch.uint8, device=dev)
+                call = lambda: linattn_chunk_backward(xb["q"], xb["k"], xb["v"], xb["g"], dout, workspace=wsb)
+                tok = cfg.B * cfg.H * cfg.N
+                # read Q, K, V, dO (bf16) and g; write dQ, dK, dV (bf16) and dg (fp32)
+                byt = tok * (7 * cfg.dk * 2 + 8)
             elif fn == "glv":
                 from linear_attention_gmm_amd import linattn_vec_forward
                 cfg = inputs.CONFIGS["glv_bf16_n8k"]

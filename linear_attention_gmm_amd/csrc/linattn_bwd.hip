@@ -48,39 +48,42 @@ __global__ __launch_bounds__(256) void shift_gates(const float* __restrict__ g, 
   gr[i] = t == 0 ? 1.f : g[bh * N + (N - t)];
 }
 
-// dg for one (b, h) per workgroup: x_m = q_m . dq_m - k_m . dk_m (fp32), then
-// the suffix sums over m, divided by g_m. Thread i owns tokens [i len, (i+1) len);
-// x is parked in dg between the two passes.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void gate_grad(const T* __restrict__ q, const T* __restrict__ dq,
-                                                 const T* __restrict__ k, const T* __restrict__ dk,
-                                                 const float* __restrict__ g, float* __restrict__ dg, int64_t N) {
-  typedef typename Vec16<T>::type vec;
-  constexpr int EV = Vec16<T>::n;
+// x_m = q_m . dq_m - k_m . dk_m for every token (float32), one wave per token:
+// lanes over the features, a wave sum. Written into dg.
+template <int D>
+__global__ __launch_bounds__(256) void gate_dots(const float* __restrict__ q, const float* __restrict__ dq,
+                                                 const float* __restrict__ k, const float* __restrict__ dk,
+                                                 float* __restrict__ x, int64_t rows) {
+  const int l = lane_id();
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave_id()) * 16;
+  for (int rr = 0; rr < 16; ++rr) {
+    const int64_t row = row0 + rr;
+    if (row >= rows) break;
+    float s = 0.f;
+#pragma unroll
+    for (int i = l; i < D; i += 64) {
+      const size_t o = (size_t)row * D + i;
+      s += q[o] * dq[o] - k[o] * dk[o];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (l == 0) x[row] = s;
+  }
+}
+
+// dg_t = (1 / g_t) sum_{m >= t} x_m for one (b, h) per workgroup: thread i owns
+// tokens [i len, (i+1) len); the sums of the ranges after it come from LDS.
+__global__ __launch_bounds__(256) void gate_suffix(const float* __restrict__ g, float* __restrict__ dg, int64_t N) {
   __shared__ float stot[256];
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int64_t len = (N + 255) / 256;
   const int64_t t0 = (int64_t)tid * len, t1 = t0 + len < N ? t0 + len : N;
   const size_t base = (size_t)bh * N;
   float tot = 0.f;
-  for (int64_t m = t0; m < t1; ++m) {
-    const vec* pq = reinterpret_cast<const vec*>(q + (base + m) * D);
-    const vec* pdq = reinterpret_cast<const vec*>(dq + (base + m) * D);
-    const vec* pk = reinterpret_cast<const vec*>(k + (base + m) * D);
-    const vec* pdk = reinterpret_cast<const vec*>(dk + (base + m) * D);
-    float x = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < D / EV; ++c) {
-      const vec a = pq[c], b = pdq[c], e = pk[c], f = pdk[c];
-#pragma unroll
-      for (int i = 0; i < EV; ++i) x += to_f32(a[i]) * to_f32(b[i]) - to_f32(e[i]) * to_f32(f[i]);
-    }
-    dg[base + m] = x;
-    tot += x;
-  }
+  for (int64_t m = t0; m < t1; ++m) tot += dg[base + m];
   stot[tid] = tot;
   __syncthreads();
-  float run = 0.f;  // sum over the ranges after this thread's
+  float run = 0.f;
   for (int u = tid + 1; u < 256; ++u) run += stot[u];
   for (int64_t m = t1 - 1; m >= t0; --m) {
     run += dg[base + m];
@@ -107,16 +110,19 @@ static hipError_t convert_n(const void* in, void* out, int64_t n, hipStream_t st
 
 static hipError_t gate_grad_f32(const BwdLaunch& L, const float* q, const float* dq, const float* k, const float* dk,
                                 hipStream_t st) {
-  const unsigned BH = (unsigned)(L.B * L.H);
-#define LM_GG(DD)                                                                                              \
-  hipLaunchKernelGGL((gate_grad<float, DD>), dim3(BH), dim3(256), 0, st, q, dq, k, dk, L.g, L.dg, L.N)
+  const int64_t rows = L.B * L.H * L.N;
+  const unsigned nb = (unsigned)((rows + 63) / 64);
+#define LM_GD(DD) hipLaunchKernelGGL((gate_dots<DD>), dim3(nb), dim3(256), 0, st, q, dq, k, dk, L.dg, rows)
   switch (L.D) {
-    case 32: LM_GG(32); break;
-    case 64: LM_GG(64); break;
-    case 128: LM_GG(128); break;
+    case 32: LM_GD(32); break;
+    case 64: LM_GD(64); break;
+    case 128: LM_GD(128); break;
     default: return hipErrorInvalidValue;
   }
-#undef LM_GG
+#undef LM_GD
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gate_suffix, dim3((unsigned)(L.B * L.H)), dim3(256), 0, st, L.g, L.dg, L.N);
   return hipGetLastError();
 }
 
