@@ -24,7 +24,9 @@ struct Cfg {
   static constexpr int DT = DV / 16;
   static constexpr int PAD = 16 / (int)sizeof(T);
   static constexpr int W_VGPR = RT * (2 * D) * (int)sizeof(T) / 4 / 4;  // per lane
-  static constexpr bool W_RES = W_VGPR <= 64;
+  // W fragments kept in registers when they are few; with eight waves (two per
+  // SIMD, 256 VGPRs each) only up to 32 registers.
+  static constexpr bool W_RES = W_VGPR <= (NW >= 8 ? 32 : 64);
   static constexpr int PV = DV + PAD;
   static constexpr int PE = KPW + PAD;
   static constexpr bool HAS_K = MODE != BIDIR;

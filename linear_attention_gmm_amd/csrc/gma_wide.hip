@@ -7,8 +7,13 @@
 namespace lm {
 namespace gma {
 
+// The segment pass and the bidirectional read run eight waves of 32 components
+// (two waves per SIMD: the routing latency of one wave hides behind the other);
+// the causal pass keeps four waves of 64 components, since its per-wave read
+// partials and state do not fit 256 registers at eight waves.
 hipError_t wide_launch(const Args& a, int mode, int segments, unsigned BH, hipStream_t st) {
-  return launch_mode<bf16, 128, 4, 64>(a, mode, segments, BH, st);
+  if (mode == CAUSAL) return launch_mode<bf16, 128, 4, 64>(a, mode, segments, BH, st);
+  return launch_mode<bf16, 128, 8, 32>(a, mode, segments, BH, st);
 }
 
 }  // namespace gma
