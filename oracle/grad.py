@@ -43,3 +43,52 @@ def gla_backward(q, k, v, g, do):
     o = gla_forward_torch(q, k, v, g)
     o.backward(do)
     return tuple(x.grad.numpy() for x in (q, k, v, g))
+
+
+def gma_forward_torch(q, k, v, mu, log_var, logit_pi, eps, causal=True) -> torch.Tensor:
+    """O [B,H,N,dv] of Gaussian Mixture Attention ("Gaussian Mixture Attention:
+    Linear-Time Sequence Mixing via Probabilistic Latent Routing", method: core
+    mechanism and latent memory routing), differentiable. Responsibilities are
+    the diagonal-Gaussian posteriors p(z = k | x) with priors softmax(logit_pi)
+    and variances exp(log_var), written directly (log 2 pi included); the causal
+    form accumulates the memory token by token and reads it after the write of
+    the same token."""
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    var = torch.exp(log_var)                                        # [H,K,d]
+    log_pi = logit_pi - torch.logsumexp(logit_pi, dim=-1, keepdim=True)
+
+    def resp(x):                                                    # x [B,H,N,d] -> [B,H,N,K]
+        diff = x[:, :, :, None, :] - mu[None, :, None, :, :]
+        ll = log_pi[None, :, None, :] - 0.5 * (np.log(2 * np.pi) + log_var[None, :, None] + diff * diff
+                                              / var[None, :, None]).sum(dim=-1)
+        return torch.softmax(ll, dim=-1)
+
+    gq, gk = resp(q), resp(k)
+    if not causal:
+        vt = torch.einsum("bhnk,bhnd->bhkd", gk, v)
+        z = gk.sum(dim=2)
+        return torch.einsum("bhnk,bhkd->bhnd", gq, vt) / (torch.einsum("bhnk,bhk->bhn", gq, z)[..., None] + eps)
+    K = mu.shape[1]
+    vt = torch.zeros(B, H, K, dv, dtype=q.dtype)
+    z = torch.zeros(B, H, K, dtype=q.dtype)
+    outs = []
+    for t in range(N):
+        vt = vt + gk[:, :, t, :, None] * v[:, :, t, None, :]
+        z = z + gk[:, :, t]
+        num = (gq[:, :, t, :, None] * vt).sum(dim=2)
+        den = (gq[:, :, t] * z).sum(dim=-1, keepdim=True) + eps
+        outs.append(num / den)
+    return torch.stack(outs, dim=2)
+
+
+def gma_backward(q, k, v, mu, log_var, logit_pi, do, eps, causal=True):
+    """Gradients (dq, dk, dv, dmu, dlog_var, dlogit_pi) of sum(O * do) with
+    O = gma_forward_torch(...); returns numpy float64."""
+    q, k, v, mu, log_var, logit_pi, do = map(_t, (q, k, v, mu, log_var, logit_pi, do))
+    xs = (q, k, v, mu, log_var, logit_pi)
+    for x in xs:
+        x.requires_grad_(True)
+    o = gma_forward_torch(q, k, v, mu, log_var, logit_pi, eps, causal)
+    o.backward(do)
+    return tuple(x.grad.numpy() for x in xs)

@@ -479,10 +479,43 @@ def pin_gla_backward(orc):
         assert relerr(gx, num) < 1e-7, ("gradient", idx, relerr(gx, num))
 
 
+def pin_gma_backward(orc):
+    """Gradients of GMA (causal and bidirectional): the autograd oracle's forward
+    equals oracle.c's, and every gradient (q, k, v, mu, log_var, logit_pi)
+    equals central finite differences of oracle.c's forward."""
+    from oracle import grad
+    rng = _rng(602)
+    B, H, N, d, K, dv, eps = 1, 2, 5, 3, 4, 2, 1e-3
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, dv))
+    mu = rng.standard_normal((H, K, d))
+    lv = rng.normal(0.0, 0.5, (H, K, d))
+    lp = rng.standard_normal((H, K))
+    do = rng.standard_normal((B, H, N, dv))
+    for causal in (True, False):
+        fw = grad.gma_forward_torch(*[grad._t(x) for x in (q, k, v, mu, lv, lp)], eps, causal).numpy()
+        assert relerr(fw, orc.gma_forward(q, k, v, mu, lv, lp, causal=causal, eps=eps)) < 1e-12
+        gs = grad.gma_backward(q, k, v, mu, lv, lp, do, eps, causal)
+        base = [q, k, v, mu, lv, lp]
+        loss = lambda a: float(np.sum(orc.gma_forward(*a, causal=causal, eps=eps) * do))
+        h = 1e-6
+        for idx, gx in enumerate(gs):
+            x = base[idx]
+            num = np.zeros_like(x)
+            for pos in np.ndindex(x.shape):
+                xp = x.copy(); xp[pos] += h
+                xm = x.copy(); xm[pos] -= h
+                ap = list(base); ap[idx] = xp
+                am = list(base); am[idx] = xm
+                num[pos] = (loss(ap) - loss(am)) / (2 * h)
+            assert relerr(gx, num) < 1e-7, ("gradient", causal, idx, relerr(gx, num))
+
+
 ALL_PINS = [
     pin_gamma_scipy, pin_gma_brute_numpy, pin_gma_k1_closed_form, pin_gma_identical_components,
     pin_gma_permutation, pin_gma_prefix, pin_gma_affinity_structure, pin_gma_golden,
     pin_gla_brute, pin_gla_chunkwise, pin_ccq_numpy_cov, pin_cov_is_logpartition_hessian,
     pin_ccq_reductions, pin_ccq_chunkwise, pin_ccq_golden, pin_gma_state, pin_gla_state,
-    pin_ccq_state, pin_glv, pin_gla_backward,
+    pin_ccq_state, pin_glv, pin_gla_backward, pin_gma_backward,
 ]
