@@ -222,6 +222,35 @@ int linattn_chunk_backward(const void* q, const void* k, const void* v, const fl
                            int64_t segments, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward pass of causal GMA: given the output gradient dout [B,H,N,dv] of
+ * gma_forward(q, k, v, mu, log_var, logit_pi, causal = 1, eps), writes the
+ * gradients of sum(out * dout):
+ *   dq, dk [B,H,N,d], dv [B,H,N,dv]                 (dtype, 16-byte aligned)
+ *   dmu, dlog_var [H,K,d], dlogit_pi [H,K]          (float32, 4-byte aligned)
+ * The causal output is a linear attention with the responsibilities as
+ * features and [v | 1] as values (numerator and normaliser), so the float32
+ * backward of that linear attention gives the gradients of the features and of
+ * v; the chain rule through the softmax over components and the Gaussian log
+ * joint gives dq, dk and the parameter gradients (summed over the batch and
+ * over both the query and the key tokens, in a fixed order). Everything is
+ * computed in float32; bf16 gradients are rounded once.
+ * Source: "Gaussian Mixture Attention", Method -> core mechanism (posterior
+ * responsibilities), latent memory routing (write and read phases), variants
+ * and training (trained end to end; softplus variances, softmax priors).
+ * Implemented: causal = 1 (0 gives LM_EUNSUPPORTED), d == dv in {32, 64},
+ * 1 <= K <= 128. Outputs must not overlap each other, the inputs or the
+ * workspace (of at least gma_backward_workspace_bytes; float32 rows of
+ * 64 or 128 entries per token: about 14 such tensors).
+ */
+size_t gma_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K,
+                                    int64_t dv, int causal, int dtype);
+int gma_backward(const void* q, const void* k, const void* v, const float* mu,
+                 const float* log_var, const float* logit_pi, const void* dout, void* dq,
+                 void* dk, void* dv, float* dmu, float* dlog_var, float* dlogit_pi, int64_t B,
+                 int64_t H, int64_t N, int64_t d, int64_t K, int64_t dvv, int causal, float eps,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forwards on a carried state. Arguments as for the forward of the same name
  * (gma_forward_state is the causal GMA forward; the workspace is the one
  * gma_workspace_bytes gives for causal = 1), plus:

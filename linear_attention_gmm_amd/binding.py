@@ -61,6 +61,9 @@ _SIGS = {
     "linattn_vec_decode_step": ([_P] * 6 + [_I64] * 4 + [ctypes.c_int, _P], ctypes.c_int),
     "linattn_backward_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
     "linattn_chunk_backward": ([_P] * 9 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "gma_backward_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
+    "gma_backward": ([_P] * 13 + [_I64] * 6 + [ctypes.c_int, ctypes.c_float, ctypes.c_int, _P, ctypes.c_size_t, _P],
+                     ctypes.c_int),
 }
 
 
@@ -454,3 +457,34 @@ def linattn_chunk_backward(q, k, v, g, dout, chunk: int = 64, segments: int = 0,
                                       ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
     _check("linattn_chunk_backward", st)
     return dq, dkt, dvt, dg
+
+
+def gma_backward_workspace_bytes(B, H, N, d, K, dv, causal=True, dtype=torch.bfloat16) -> int:
+    return int(lib().gma_backward_workspace_bytes(B, H, N, d, K, dv, int(bool(causal)), _DT[dtype]))
+
+
+def gma_backward(q, k, v, mu, log_var, logit_pi, dout, eps: float = 1e-6, causal: bool = True,
+                 workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv, dmu, dlog_var, dlogit_pi) of sum(out * dout) for
+    out = gma_forward(q, k, v, mu, log_var, logit_pi, causal, eps); dq, dk, dv in
+    the input dtype, the parameter gradients float32."""
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    dt = _dtype_code(q)
+    pq = _dev(q, "q", q.dtype, (B, H, N, d))
+    pk = _dev(k, "k", q.dtype, (B, H, N, d))
+    pv = _dev(v, "v", q.dtype, (B, H, N, dv))
+    pdo = _dev(dout, "dout", q.dtype, (B, H, N, dv))
+    pmu = _dev(mu, "mu", torch.float32, (H, K, d))
+    plv = _dev(log_var, "log_var", torch.float32, (H, K, d))
+    plp = _dev(logit_pi, "logit_pi", torch.float32, (H, K))
+    dq, dk, dvt = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dmu, dlv, dlp = torch.empty_like(mu), torch.empty_like(log_var), torch.empty_like(logit_pi)
+    nbytes = gma_backward_workspace_bytes(B, H, N, d, K, dv, causal, q.dtype)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    st = lib().gma_backward(pq, pk, pv, pmu, plv, plp, pdo, dq.data_ptr(), dk.data_ptr(), dvt.data_ptr(),
+                            dmu.data_ptr(), dlv.data_ptr(), dlp.data_ptr(), B, H, N, d, K, dv, int(bool(causal)),
+                            float(eps), dt, ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
+    _check("gma_backward", st)
+    return dq, dk, dvt, dmu, dlv, dlp

@@ -372,6 +372,72 @@ int vec_forward(const char* fn, const void* q, const void* k, const void* v, con
   return ok();
 }
 
+// ----------------------------------------------------------------------------- GMA backward
+
+// Width of the inner linear attention of the GMA backward: features are the K
+// responsibilities, values [v | 1].
+int64_t gma_bwd_width(int64_t K, int64_t dv) {
+  const int64_t need = K > dv + 1 ? K : dv + 1;
+  return need <= 32 ? 32 : need <= 64 ? 64 : 128;
+}
+
+struct GmaBwdLayout {
+  size_t iv, cst, rows[8], ones, inner[5], rg, agg, part, total;
+  LinLayout lin;
+  int64_t DL, nseg, seg_len;
+};
+
+GmaBwdLayout gma_bwd_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv) {
+  GmaBwdLayout L;
+  L.DL = gma_bwd_width(K, dv);
+  // token ranges of the routing and chain-rule kernels: about 1024 workgroups
+  const int64_t want = (1024 + 2 * B * H - 1) / (2 * B * H);
+  int64_t len = (N + want - 1) / want;
+  len = (len + 15) / 16 * 16;
+  L.seg_len = len;
+  L.nseg = (N + len - 1) / len;
+  L.lin = lin_layout(B, H, N, L.DL, false, 0);
+  const size_t rowt = align_up((size_t)B * H * N * L.DL * 4), colt = align_up((size_t)B * H * N * 4);
+  size_t off = 0;
+  L.iv = off;
+  off = align_up(off + (size_t)H * K * d * 4);
+  L.cst = off;
+  off = align_up(off + (size_t)H * K * 4);
+  for (int i = 0; i < 8; ++i) {
+    L.rows[i] = off;
+    off += rowt;
+  }
+  L.ones = off;
+  off += colt;
+  for (int i = 0; i < 5; ++i) {
+    L.inner[i] = off;
+    off += rowt;
+  }
+  L.rg = off;
+  off += colt;
+  L.agg = off;
+  off += L.lin.total;
+  L.part = off;
+  off = align_up(off + (size_t)H * 2 * B * L.nseg * K * (2 * d + 1) * 4);
+  L.total = off;
+  return L;
+}
+
+int gma_bwd_check(const char* fn, int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal,
+                  float eps, int dtype) {
+  if (B < 1 || H < 1 || N < 1 || d < 1 || K < 1 || dv < 1) return fail(LM_EINVAL, "%s: sizes must be >= 1", fn);
+  if (dtype != LM_F32 && dtype != LM_BF16) return fail(LM_EINVAL, "%s: dtype %d is not LM_F32 or LM_BF16", fn, dtype);
+  if (causal != 0 && causal != 1) return fail(LM_EINVAL, "%s: causal must be 0 or 1 (got %d)", fn, causal);
+  if (!(eps >= 0.f) || std::isinf(eps)) return fail(LM_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (!causal) return fail(LM_EUNSUPPORTED, "%s implements the causal form", fn);
+  if (!(d == 32 || d == 64) || dv != d)
+    return fail(LM_EUNSUPPORTED, "%s implements d == dv in {32, 64} (got d=%lld dv=%lld)", fn, (long long)d,
+                (long long)dv);
+  if (K > 128) return fail(LM_EUNSUPPORTED, "%s implements K <= 128 (got %lld)", fn, (long long)K);
+  if (N > (int64_t(1) << 30) || B * H > 65535) return fail(LM_EUNSUPPORTED, "%s: N <= 2^30 and B*H <= 65535", fn);
+  return LM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -665,6 +731,112 @@ int linattn_chunk_backward(const void* q, const void* k, const void* v, const fl
   La.D = dkk;
   La.bf16 = dtype == LM_BF16;
   hipError_t e = lm::linattn_backward_launch(La, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+size_t gma_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal,
+                                    int dtype) {
+  if (gma_bwd_check("gma_backward", B, H, N, d, K, dv, causal, 0.f, dtype) != LM_OK) return 0;
+  return gma_bwd_layout(B, H, N, d, K, dv).total;
+}
+
+int gma_backward(const void* q, const void* k, const void* v, const float* mu, const float* log_var,
+                 const float* logit_pi, const void* dout, void* dq, void* dk, void* dv, float* dmu, float* dlog_var,
+                 float* dlogit_pi, int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dvv, int causal,
+                 float eps, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gma_backward";
+  int st = gma_bwd_check(fn, B, H, N, d, K, dvv, causal, eps, dtype);
+  if (st != LM_OK) return st;
+  if (!q || !k || !v || !mu || !log_var || !logit_pi || !dout || !dq || !dk || !dv || !dmu || !dlog_var ||
+      !dlogit_pi || !workspace)
+    return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  const void* p16[] = {q, k, v, dout, dq, dk, dv, workspace};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return fail(LM_EINVAL, "%s: misaligned pointer (tensors need 16 bytes)", fn);
+  const void* p4[] = {mu, log_var, logit_pi, dmu, dlog_var, dlogit_pi};
+  for (const void* p : p4)
+    if (!aligned(p, 4)) return fail(LM_EINVAL, "%s: misaligned parameter pointer", fn);
+  const GmaBwdLayout L = gma_bwd_layout(B, H, N, d, K, dvv);
+  if (workspace_bytes < L.total)
+    return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
+  // outputs must not overlap each other, the inputs or the workspace
+  const size_t nt = (size_t)B * H * N * d * esize(dtype), np = (size_t)H * K * d * 4, nl = (size_t)H * K * 4;
+  const void* outs[] = {dq, dk, dv, dmu, dlog_var, dlogit_pi};
+  const size_t nout[] = {nt, nt, nt, np, np, nl};
+  const void* ins[] = {q, k, v, dout, mu, log_var, logit_pi, workspace};
+  const size_t nin[] = {nt, nt, nt, nt, np, np, nl, L.total};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlap(outs[i], nout[i], ins[j], nin[j]))
+        return fail(LM_EINVAL, "%s: an output overlaps an input or the workspace", fn);
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(outs[i], nout[i], outs[j], nout[j])) return fail(LM_EINVAL, "%s: outputs overlap", fn);
+  }
+  char* ws = static_cast<char*>(workspace);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  lm::GmaBwdLaunch La{};
+  lm::BwdLaunch& Bw = La.bwd;
+  Bw.fwd.agg = F(L.agg);
+  Bw.fwd.w_lambda = nullptr;
+  Bw.fwd.b_lambda = nullptr;
+  Bw.fwd.B = B;
+  Bw.fwd.H = H;
+  Bw.fwd.N = N;
+  Bw.fwd.D = L.DL;
+  Bw.fwd.P = L.lin.plan.P;
+  Bw.fwd.seg_len = L.lin.plan.seg_len;
+  Bw.fwd.R = L.lin.R;
+  Bw.fwd.bf16 = false;
+  Bw.fwd.ccq = false;
+  Bw.rq = F(L.inner[0]);
+  Bw.rk = F(L.inner[1]);
+  Bw.rv = F(L.inner[2]);
+  Bw.rdo = F(L.inner[3]);
+  Bw.rout = F(L.inner[4]);
+  Bw.rg = F(L.rg);
+  Bw.dg = nullptr;
+  Bw.B = B;
+  Bw.H = H;
+  Bw.N = N;
+  Bw.D = L.DL;
+  Bw.bf16 = false;
+  La.q = q;
+  La.k = k;
+  La.v = v;
+  La.dout = dout;
+  La.mu = mu;
+  La.log_var = log_var;
+  La.logit_pi = logit_pi;
+  La.dq = dq;
+  La.dk = dk;
+  La.dv = dv;
+  La.dmu = dmu;
+  La.dlog_var = dlog_var;
+  La.dlogit_pi = dlogit_pi;
+  La.iv = F(L.iv);
+  La.cst = F(L.cst);
+  La.gq = F(L.rows[0]);
+  La.gk = F(L.rows[1]);
+  La.vx = F(L.rows[2]);
+  La.y = F(L.rows[3]);
+  La.dy = F(L.rows[4]);
+  La.dgq = F(L.rows[5]);
+  La.dgk = F(L.rows[6]);
+  La.dvx = F(L.rows[7]);
+  La.ones = F(L.ones);
+  La.part = F(L.part);
+  La.B = B;
+  La.H = H;
+  La.N = N;
+  La.D = d;
+  La.K = K;
+  La.DL = L.DL;
+  La.nseg = L.nseg;
+  La.seg_len = L.seg_len;
+  La.eps = eps;
+  La.bf16 = dtype == LM_BF16;
+  hipError_t e = lm::gma_backward_launch(La, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
   return ok();
 }

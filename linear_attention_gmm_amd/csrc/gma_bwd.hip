@@ -1,0 +1,427 @@
+// gma_bwd.hip -- backward pass of causal Gaussian Mixture Attention ("Gaussian
+// Mixture Attention: Linear-Time Sequence Mixing via Probabilistic Latent
+// Routing", method: core mechanism, latent memory routing, variants and
+// training: the mixer is trained end to end, the variances through softplus and
+// the priors through a softmax).
+//
+// The causal output is a linear attention whose features are the
+// responsibilities: with A_ij = gamma(q_i) . gamma(k_j),
+//   N_i = sum_{j<=i} A_ij v_j,  D_i = sum_{j<=i} A_ij + eps,  O_i = N_i / D_i,
+// i.e. one linear attention (no decay) with keys gamma(k), queries gamma(q) and
+// values [v | 1]. Its gradients with respect to the features and the values
+// are those of that linear attention for the output gradient [dN | dD] with
+// dN_i = dO_i / D_i and dD_i = -(dO_i . O_i) / D_i, so the float32 backward of
+// decayed linear attention (gates = 1) computes them. What is left is the chain
+// rule through the softmax and the Gaussian log joint
+//   l_k(x) = log pi_k - 1/2 sum_d (log var_kd + (x_d - mu_kd)^2 / var_kd):
+//   dl_k   = gamma_k (dgamma_k - sum_k' gamma_k' dgamma_k')
+//   dx_d   = sum_k dl_k (mu_kd - x_d) / var_kd
+//   dmu_kd = sum_tokens dl_k (x_d - mu_kd) / var_kd
+//   dlog var_kd = sum_tokens dl_k (-1/2 + 1/2 (x_d - mu_kd)^2 / var_kd)
+//   dlogit pi_k = G_k - pi_k sum_k' G_k',  G_k = sum_tokens dl_k
+// with the parameter sums running over the query and the key tokens of every
+// batch entry. Everything is float32; the inputs and dq, dk, dv are in the
+// input dtype. The constant -d/2 log 2 pi of the log density cancels in the
+// softmax and is left out.
+//
+// Kernels: prep (per head: 1/var and the constant part of the log joint),
+// route (responsibilities, one thread per component, 16 tokens per step),
+// pack (values [v | 1 | 0], unit gates), out_grad (dN, dD from the forward),
+// chain (softmax and log-joint chain rule per token, parameter partial sums
+// per token range), params (fixed-order sum of the partials), take_dv.
+#include "mfma.hpp"
+#include "launch.hpp"
+
+namespace lm {
+namespace gbwd {
+
+constexpr int kTT = 16;   // tokens per step of route and chain
+constexpr int kThr = 128; // threads per workgroup: one per component (K <= 128)
+
+// Per head: iv[k][d] = exp(-log_var), cst[k] = log pi_k - 1/2 sum_d log_var_kd
+// (log pi = log-softmax of the mixing logits).
+__global__ __launch_bounds__(kThr) void prep_kernel(const float* __restrict__ log_var,
+                                                    const float* __restrict__ logit_pi, float* __restrict__ iv,
+                                                    float* __restrict__ cst, int K, int D) {
+  __shared__ float red[kThr];
+  const int h = blockIdx.x, k = threadIdx.x;
+  const float lp = k < K ? logit_pi[(size_t)h * K + k] : -INFINITY;
+  red[k] = lp;
+  __syncthreads();
+  for (int s = kThr / 2; s > 0; s >>= 1) {
+    if (k < s) red[k] = fmaxf(red[k], red[k + s]);
+    __syncthreads();
+  }
+  const float mx = red[0];
+  __syncthreads();
+  red[k] = k < K ? expf(lp - mx) : 0.f;
+  __syncthreads();
+  for (int s = kThr / 2; s > 0; s >>= 1) {
+    if (k < s) red[k] += red[k + s];
+    __syncthreads();
+  }
+  const float lse = mx + logf(red[0]);
+  if (k >= K) return;
+  float sl = 0.f;
+  for (int d = 0; d < D; ++d) {
+    const float l = log_var[((size_t)h * K + k) * D + d];
+    sl += l;
+    iv[((size_t)h * K + k) * D + d] = expf(-l);
+  }
+  cst[(size_t)h * K + k] = lp - lse - 0.5f * sl;
+}
+
+// Sum over the 128 threads of the workgroup of one value per thread, for kTT
+// values at once; `red` holds 2 x kTT floats.
+__device__ __forceinline__ void block_sum16(float (&x)[kTT], float* red) {
+#pragma unroll
+  for (int t = 0; t < kTT; ++t) {
+    float s = x[t];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    x[t] = s;
+  }
+  if (lane_id() == 0) {
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) red[wave_id() * kTT + t] = x[t];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < kTT; ++t) x[t] = red[t] + red[kTT + t];
+  __syncthreads();
+}
+__device__ __forceinline__ void block_max16(float (&x)[kTT], float* red) {
+#pragma unroll
+  for (int t = 0; t < kTT; ++t) {
+    float s = x[t];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s = fmaxf(s, __shfl_xor(s, off));
+    x[t] = s;
+  }
+  if (lane_id() == 0) {
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) red[wave_id() * kTT + t] = x[t];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < kTT; ++t) x[t] = fmaxf(red[t], red[kTT + t]);
+  __syncthreads();
+}
+
+// Responsibilities of the tokens of x (q for blockIdx.z = 0, k for 1) as
+// float32 rows of DL entries (components >= K are 0). Workgroup: one (b, h),
+// kTT tokens per step over a range of `len` tokens; thread = component.
+template <typename T, int D>
+__global__ __launch_bounds__(kThr) void route_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                     const float* __restrict__ mu, const float* __restrict__ iv,
+                                                     const float* __restrict__ cst, float* __restrict__ gq,
+                                                     float* __restrict__ gk, int64_t N, int H, int K, int DL,
+                                                     int64_t len) {
+  __shared__ float sx[kTT][D];
+  __shared__ float red[2 * kTT];
+  const int bh = blockIdx.y, h = bh % H, c = threadIdx.x;
+  const T* __restrict__ x = (blockIdx.z == 0 ? q : k) + (size_t)bh * N * D;
+  float* __restrict__ out = (blockIdx.z == 0 ? gq : gk) + (size_t)bh * N * DL;
+  const float* __restrict__ muk = mu + ((size_t)h * K + (c < K ? c : 0)) * D;
+  const float* __restrict__ ivk = iv + ((size_t)h * K + (c < K ? c : 0)) * D;
+  const float ck = c < K ? cst[(size_t)h * K + c] : 0.f;
+  const int64_t t_begin = (int64_t)blockIdx.x * len;
+  const int64_t t_end = N < t_begin + len ? N : t_begin + len;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT) {
+    const int nv = (int)(t_end - t0 < kTT ? t_end - t0 : kTT);
+    for (int i = c; i < kTT * D; i += kThr) {
+      const int t = i / D, dd = i - t * D;
+      sx[t][dd] = t < nv ? to_f32(x[(size_t)(t0 + t) * D + dd]) : 0.f;
+    }
+    __syncthreads();
+    float acc[kTT];
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) acc[t] = 0.f;
+    if (c < K) {
+      for (int dd = 0; dd < D; ++dd) {
+        const float m = muk[dd], w = ivk[dd];
+#pragma unroll
+        for (int t = 0; t < kTT; ++t) {
+          const float e = sx[t][dd] - m;
+          acc[t] += e * e * w;
+        }
+      }
+    }
+    float l[kTT], mx[kTT];
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) mx[t] = l[t] = c < K ? ck - 0.5f * acc[t] : -INFINITY;
+    block_max16(mx, red);
+    float e[kTT];
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) e[t] = c < K ? expf(l[t] - mx[t]) : 0.f;
+    float s[kTT];
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) s[t] = e[t];
+    block_sum16(s, red);
+    if (c < DL) {
+      for (int t = 0; t < nv; ++t) out[(size_t)(t0 + t) * DL + c] = e[t] / s[t];
+    }
+  }
+}
+
+// Values of the inner linear attention [v | 1 | 0 ...] (DL columns) and unit
+// gates.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ v, float* __restrict__ vx,
+                                                   float* __restrict__ ones, int64_t rows, int DV, int DL) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * DL) return;
+  const int64_t r = i / DL;
+  const int c = (int)(i - r * DL);
+  vx[i] = c < DV ? to_f32(v[r * DV + c]) : (c == DV ? 1.f : 0.f);
+  if (c == 0) ones[r] = 1.f;
+}
+
+// From the inner forward y = [N | D - eps | ...] and dO: the output gradient of
+// the inner linear attention [dN | dD | 0 ...], one wave per token (DV <= 64).
+template <typename T>
+__global__ __launch_bounds__(256) void out_grad_kernel(const float* __restrict__ y, const T* __restrict__ dout,
+                                                       float* __restrict__ dy, int64_t rows, int DV, int DL,
+                                                       float eps) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave_id();
+  if (r >= rows) return;
+  const int l = lane_id();
+  const float den = y[r * DL + DV] + eps;
+  const float inv = 1.f / den;
+  const float gd = l < DV ? to_f32(dout[r * DV + l]) : 0.f;
+  const float o = l < DV ? y[r * DL + l] * inv : 0.f;
+  float s = gd * o;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  for (int c = l; c < DL; c += 64) dy[r * DL + c] = c < DV ? gd * inv : (c == DV ? -s * inv : 0.f);
+}
+
+// Chain rule through the softmax and the log joint for the tokens of one side
+// (blockIdx.z = 0: queries, 1: keys) of one (b, h), over a range of `len`
+// tokens. Writes dx in the input dtype, and this range's parameter partial sums
+//   part[h][slot][k] = [sum dl (x - mu) (D) | sum dl (x - mu)^2 (D) | sum dl]
+// with slot = (side * B + b) * nseg + blockIdx.x. Thread = component for the
+// partial sums; thread = (feature, token group) for dx.
+template <typename T, int D>
+__global__ __launch_bounds__(kThr) void chain_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                     const float* __restrict__ gq, const float* __restrict__ gk,
+                                                     const float* __restrict__ dgq, const float* __restrict__ dgk,
+                                                     const float* __restrict__ mu, const float* __restrict__ iv,
+                                                     T* __restrict__ dq, T* __restrict__ dk, float* __restrict__ part,
+                                                     int64_t N, int B, int H, int K, int DL, int64_t len, int nseg) {
+  __shared__ float sx[kTT][D];
+  __shared__ float sdl[kTT][kThr];
+  __shared__ float red[2 * kTT];
+  const int bh = blockIdx.y, b = bh / H, h = bh % H, c = threadIdx.x, side = blockIdx.z;
+  const T* __restrict__ x = (side == 0 ? q : k) + (size_t)bh * N * D;
+  T* __restrict__ dx = (side == 0 ? dq : dk) + (size_t)bh * N * D;
+  const float* __restrict__ gx = (side == 0 ? gq : gk) + (size_t)bh * N * DL;
+  const float* __restrict__ dgx = (side == 0 ? dgq : dgk) + (size_t)bh * N * DL;
+  const float* __restrict__ muh = mu + (size_t)h * K * D;
+  const float* __restrict__ ivh = iv + (size_t)h * K * D;
+  const float* __restrict__ muk = muh + (size_t)(c < K ? c : 0) * D;
+  // dx mapping: feature fd = c % D, tokens t = c / D + j * (kThr / D)
+  constexpr int TG = kThr / D;      // token groups
+  constexpr int TPT = kTT / TG;     // tokens per thread
+  const int fd = c % D, tg = c / D;
+
+  float p1[D], p2[D], p0 = 0.f;
+#pragma unroll
+  for (int i = 0; i < D; ++i) p1[i] = p2[i] = 0.f;
+
+  const int64_t t_begin = (int64_t)blockIdx.x * len;
+  const int64_t t_end = N < t_begin + len ? N : t_begin + len;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT) {
+    const int nv = (int)(t_end - t0 < kTT ? t_end - t0 : kTT);
+    for (int i = c; i < kTT * D; i += kThr) {
+      const int t = i / D, dd = i - t * D;
+      sx[t][dd] = t < nv ? to_f32(x[(size_t)(t0 + t) * D + dd]) : 0.f;
+    }
+    float ga[kTT], dga[kTT], r[kTT];
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) {
+      const bool ok = c < K && t < nv;
+      ga[t] = ok ? gx[(size_t)(t0 + t) * DL + c] : 0.f;
+      dga[t] = ok ? dgx[(size_t)(t0 + t) * DL + c] : 0.f;
+      r[t] = ga[t] * dga[t];
+    }
+    block_sum16(r, red);  // also orders the sx writes before the reads below
+    float dl[kTT];
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) {
+      dl[t] = ga[t] * (dga[t] - r[t]);
+      sdl[t][c] = dl[t];
+      p0 += dl[t];
+    }
+    if (c < K) {
+#pragma unroll
+      for (int dd = 0; dd < D; ++dd) {
+        const float m = muk[dd];
+#pragma unroll
+        for (int t = 0; t < kTT; ++t) {
+          const float e = sx[t][dd] - m;
+          const float a = dl[t] * e;
+          p1[dd] += a;
+          p2[dd] += a * e;
+        }
+      }
+    }
+    __syncthreads();
+    // dx_d = sum_k dl_k mu_kd iv_kd - x_d sum_k dl_k iv_kd
+    float s1[TPT], s2[TPT];
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) s1[j] = s2[j] = 0.f;
+    for (int kk = 0; kk < K; ++kk) {
+      const float w = ivh[(size_t)kk * D + fd];
+      const float a = muh[(size_t)kk * D + fd] * w;
+#pragma unroll
+      for (int j = 0; j < TPT; ++j) {
+        const float d_ = sdl[tg + j * TG][kk];
+        s1[j] += d_ * a;
+        s2[j] += d_ * w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const int t = tg + j * TG;
+      if (t < nv) dx[(size_t)(t0 + t) * D + fd] = from_f32<T>(s1[j] - sx[t][fd] * s2[j]);
+    }
+    __syncthreads();
+  }
+  if (c < K) {
+    const int slot = (side * B + b) * nseg + (int)blockIdx.x;
+    float* dst = part + (((size_t)h * 2 * B * nseg + slot) * K + c) * (2 * D + 1);
+#pragma unroll
+    for (int dd = 0; dd < D; ++dd) {
+      dst[dd] = p1[dd];
+      dst[D + dd] = p2[dd];
+    }
+    dst[2 * D] = p0;
+  }
+}
+
+// Parameter gradients per head from the partial sums, summed over the slots in
+// a fixed order: dmu = iv * S1, dlog_var = -1/2 S0 + 1/2 iv * S2, dlogit_pi =
+// S0 - pi * sum S0.
+__global__ __launch_bounds__(kThr) void params_kernel(const float* __restrict__ part, const float* __restrict__ iv,
+                                                      const float* __restrict__ logit_pi, float* __restrict__ dmu,
+                                                      float* __restrict__ dlv, float* __restrict__ dlp, int K, int D,
+                                                      int nslot) {
+  __shared__ float red[kThr];
+  const int h = blockIdx.x, c = threadIdx.x;
+  const int F = 2 * D + 1;
+  float g0 = 0.f;
+  if (c < K) {
+    const float* base = part + (size_t)h * nslot * K * F + (size_t)c * F;
+    for (int s = 0; s < nslot; ++s) g0 += base[(size_t)s * K * F + 2 * D];
+    for (int dd = 0; dd < D; ++dd) {
+      float s1 = 0.f, s2 = 0.f;
+      for (int s = 0; s < nslot; ++s) {
+        s1 += base[(size_t)s * K * F + dd];
+        s2 += base[(size_t)s * K * F + D + dd];
+      }
+      const float w = iv[((size_t)h * K + c) * D + dd];
+      dmu[((size_t)h * K + c) * D + dd] = w * s1;
+      dlv[((size_t)h * K + c) * D + dd] = -0.5f * g0 + 0.5f * w * s2;
+    }
+  }
+  // pi and the total of G over the components
+  const float lp = c < K ? logit_pi[(size_t)h * K + c] : -INFINITY;
+  red[c] = lp;
+  __syncthreads();
+  for (int s = kThr / 2; s > 0; s >>= 1) {
+    if (c < s) red[c] = fmaxf(red[c], red[c + s]);
+    __syncthreads();
+  }
+  const float mx = red[0];
+  __syncthreads();
+  const float e = c < K ? expf(lp - mx) : 0.f;
+  red[c] = e;
+  __syncthreads();
+  for (int s = kThr / 2; s > 0; s >>= 1) {
+    if (c < s) red[c] += red[c + s];
+    __syncthreads();
+  }
+  const float pi = e / red[0];
+  __syncthreads();
+  red[c] = g0;
+  __syncthreads();
+  for (int s = kThr / 2; s > 0; s >>= 1) {
+    if (c < s) red[c] += red[c + s];
+    __syncthreads();
+  }
+  if (c < K) dlp[(size_t)h * K + c] = g0 - pi * red[0];
+}
+
+// dv = the first DV columns of the inner value gradient, in the input dtype.
+template <typename T>
+__global__ __launch_bounds__(256) void take_dv_kernel(const float* __restrict__ dvx, T* __restrict__ dv, int64_t rows,
+                                                      int DV, int DL) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * DV) return;
+  const int64_t r = i / DV;
+  const int c = (int)(i - r * DV);
+  dv[i] = from_f32<T>(dvx[r * DL + c]);
+}
+
+template <typename T, int D>
+static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
+  const int64_t BH = L.B * L.H, rows = BH * L.N;
+  const int K = (int)L.K, DL = (int)L.DL, H = (int)L.H;
+  hipError_t e;
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)H), dim3(kThr), 0, st, L.log_var, L.logit_pi, L.iv, L.cst, K, D);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 grid((unsigned)L.nseg, (unsigned)BH, 2);
+  hipLaunchKernelGGL((route_kernel<T, D>), grid, dim3(kThr), 0, st, static_cast<const T*>(L.q),
+                     static_cast<const T*>(L.k), L.mu, L.iv, L.cst, L.gq, L.gk, L.N, H, K, DL, L.seg_len);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((pack_kernel<T>), dim3((unsigned)((rows * DL + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const T*>(L.v), L.vx, L.ones, rows, D, DL);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // inner forward: y = [N | D - eps | 0 ...]
+  LinLaunch F = L.bwd.fwd;
+  F.q = L.gq;
+  F.k = L.gk;
+  F.v = L.vx;
+  F.g = L.ones;
+  F.out = L.y;
+  F.bf16 = false;
+  F.ccq = false;
+  F.state_in = nullptr;
+  F.state_out = nullptr;
+  F.t_in = 0;
+  if ((e = linattn_launch(F, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((out_grad_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, L.y,
+                     static_cast<const T*>(L.dout), L.dy, rows, D, DL, L.eps);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // gradients of the inner linear attention: features (dgq, dgk) and values
+  BwdLaunch Bw = L.bwd;
+  Bw.g = L.ones;
+  if ((e = linattn_backward_f32(Bw, L.gq, L.gk, L.vx, L.dy, L.dgq, L.dgk, L.dvx, false, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((chain_kernel<T, D>), grid, dim3(kThr), 0, st, static_cast<const T*>(L.q),
+                     static_cast<const T*>(L.k), L.gq, L.gk, L.dgq, L.dgk, L.mu, L.iv, static_cast<T*>(L.dq),
+                     static_cast<T*>(L.dk), L.part, L.N, (int)L.B, H, K, DL, L.seg_len, (int)L.nseg);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(params_kernel, dim3((unsigned)H), dim3(kThr), 0, st, L.part, L.iv, L.logit_pi, L.dmu,
+                     L.dlog_var, L.dlogit_pi, K, D, (int)(2 * L.B * L.nseg));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((take_dv_kernel<T>), dim3((unsigned)((rows * D + 255) / 256)), dim3(256), 0, st, L.dvx,
+                     static_cast<T*>(L.dv), rows, D, DL);
+  return hipGetLastError();
+}
+
+}  // namespace gbwd
+
+hipError_t gma_backward_launch(const GmaBwdLaunch& L, hipStream_t st) {
+  using namespace gbwd;
+  if (L.bf16) {
+    if (L.D == 32) return run<bf16, 32>(L, st);
+    if (L.D == 64) return run<bf16, 64>(L, st);
+  } else {
+    if (L.D == 32) return run<float, 32>(L, st);
+    if (L.D == 64) return run<float, 64>(L, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lm

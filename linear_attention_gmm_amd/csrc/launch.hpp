@@ -125,6 +125,49 @@ struct BwdLaunch {
   bool bf16;
 };
 hipError_t linattn_backward_launch(const BwdLaunch& L, hipStream_t st);
+// The float32 passes of that backward on float32 tensors (gates: also dg).
+hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float* k, const float* v,
+                                const float* dout, float* dq, float* dk, float* dv, bool gates, hipStream_t st);
+
+// Backward pass of causal GMA (gma_bwd.hip): the float32 backward of the
+// linear attention with responsibilities as features and [v | 1] as values,
+// then the chain rule through the softmax and the Gaussian log joint.
+struct GmaBwdLaunch {
+  BwdLaunch bwd;  // inner linear attention: D = DL, float32, its workspace
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* mu;
+  const float* log_var;
+  const float* logit_pi;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dmu;
+  float* dlog_var;
+  float* dlogit_pi;
+  // workspace (float32): per head 1/var [H][K][D] and the constant part of the
+  // log joint [H][K]; rows of DL entries: responsibilities of q and k, values
+  // [v | 1], inner output, its gradient, feature and value gradients; unit
+  // gates; parameter partial sums [H][2 B nseg][K][2 D + 1]
+  float* iv;
+  float* cst;
+  float* gq;
+  float* gk;
+  float* vx;
+  float* y;
+  float* dy;
+  float* dgq;
+  float* dgk;
+  float* dvx;
+  float* ones;
+  float* part;
+  int64_t B, H, N, D, K, DL, nseg, seg_len;
+  float eps;
+  bool bf16;
+};
+hipError_t gma_backward_launch(const GmaBwdLaunch& L, hipStream_t st);
 
 // Floats per state block written by the segment-state pass.
 inline int64_t lin_state_floats(int64_t D, bool ccq) {

@@ -134,10 +134,14 @@ static hipError_t reverse(const void* in, void* out, const BwdLaunch& L, hipStre
   return hipGetLastError();
 }
 
+}  // namespace bwd
+
 // The whole backward in float32: three chunk-kernel passes (dq; dk and dv on
-// the reversed sequence), the reversals around them and the gate gradient.
-static hipError_t run_f32(const BwdLaunch& L, const float* q, const float* k, const float* v, const float* dout,
-                          float* dq, float* dk, float* dv, hipStream_t st) {
+// the reversed sequence), the reversals around them and (gates) the gate
+// gradient.
+hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float* k, const float* v,
+                                const float* dout, float* dq, float* dk, float* dv, bool gates, hipStream_t st) {
+  using namespace bwd;
   hipError_t e;
   LinLaunch F = L.fwd;  // shapes, segment plan, workspace; pointers set per pass
   F.bf16 = false;
@@ -175,23 +179,22 @@ static hipError_t run_f32(const BwdLaunch& L, const float* q, const float* k, co
   F.out = L.rout;
   if ((e = linattn_launch(F, st)) != hipSuccess) return e;
   if ((e = reverse(L.rout, dv, L, st)) != hipSuccess) return e;
-  return gate_grad_f32(L, q, dq, k, dk, st);
+  return gates ? gate_grad_f32(L, q, dq, k, dk, st) : hipSuccess;
 }
-
-}  // namespace bwd
 
 hipError_t linattn_backward_launch(const BwdLaunch& L, hipStream_t st) {
   using namespace bwd;
   if (!L.bf16)
-    return run_f32(L, (const float*)L.q, (const float*)L.k, (const float*)L.v, (const float*)L.dout, (float*)L.dq,
-                   (float*)L.dk, (float*)L.dv, st);
+    return linattn_backward_f32(L, (const float*)L.q, (const float*)L.k, (const float*)L.v, (const float*)L.dout,
+                                (float*)L.dq, (float*)L.dk, (float*)L.dv, true, st);
   const int64_t n = L.B * L.H * L.N * L.D;
   hipError_t e;
   if ((e = convert_n<bf16, float>(L.q, L.uq, n, st)) != hipSuccess) return e;
   if ((e = convert_n<bf16, float>(L.k, L.uk, n, st)) != hipSuccess) return e;
   if ((e = convert_n<bf16, float>(L.v, L.uv, n, st)) != hipSuccess) return e;
   if ((e = convert_n<bf16, float>(L.dout, L.udo, n, st)) != hipSuccess) return e;
-  if ((e = run_f32(L, L.uq, L.uk, L.uv, L.udo, L.udq, L.udk, L.udv, st)) != hipSuccess) return e;
+  if ((e = linattn_backward_f32(L, L.uq, L.uk, L.uv, L.udo, L.udq, L.udk, L.udv, true, st)) != hipSuccess)
+    return e;
   if ((e = convert_n<float, bf16>(L.udq, L.dq, n, st)) != hipSuccess) return e;
   if ((e = convert_n<float, bf16>(L.udk, L.dk, n, st)) != hipSuccess) return e;
   return convert_n<float, bf16>(L.udv, L.dv, n, st);

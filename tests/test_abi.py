@@ -276,3 +276,33 @@ def test_backward_errors():
     assert call(dq=None) == binding.LM_EINVAL
     assert call(d=48) == binding.LM_EUNSUPPORTED
     assert L.lm_last_error().decode()
+
+
+@needs_lib
+def test_gma_backward_errors():
+    L = binding.lib()
+    (q, k, v, mu, lv, lp, do, dq, dk, dv, dmu, dlv, dlp, ws) = (FAKE + (i << 30) for i in range(14))
+    bf, f32 = binding.LM_BF16, binding.LM_F32
+    wsb = L.gma_backward_workspace_bytes(2, 2, 300, 64, 128, 64, 1, bf)
+    assert wsb > 0
+    assert L.gma_backward_workspace_bytes(2, 2, 300, 64, 128, 64, 0, bf) == 0  # bidirectional: not implemented
+    assert L.gma_backward_workspace_bytes(2, 2, 300, 128, 128, 128, 1, bf) == 0  # d = 128: not implemented
+    assert L.gma_backward_workspace_bytes(2, 2, 300, 64, 129, 64, 1, f32) == 0  # K > 128: not implemented
+    assert L.gma_backward_workspace_bytes(2, 2, 300, 32, 16, 32, 1, f32) > 0
+
+    def call(**kw):
+        a = dict(dq=dq, dk=dk, dmu=dmu, d=64, K=128, causal=1, eps=1e-6, wsb=wsb)
+        a.update(kw)
+        return L.gma_backward(q, k, v, mu, lv, lp, do, a["dq"], a["dk"], dv, a["dmu"], dlv, dlp, 2, 2, 300, a["d"],
+                              a["K"], a["d"], a["causal"], a["eps"], bf, ws, a["wsb"], None)
+
+    assert call(wsb=wsb - 1) == binding.LM_EWORKSPACE
+    assert call(dq=dk) == binding.LM_EINVAL  # two outputs in one buffer
+    assert call(dq=q + 64) == binding.LM_EINVAL  # output overlaps an input
+    assert call(dmu=dmu + 2) == binding.LM_EINVAL  # misaligned
+    assert call(dq=None) == binding.LM_EINVAL
+    assert call(eps=-1.0) == binding.LM_EINVAL
+    assert call(causal=0) == binding.LM_EUNSUPPORTED
+    assert call(d=128) == binding.LM_EUNSUPPORTED
+    assert call(K=200) == binding.LM_EUNSUPPORTED
+    assert L.lm_last_error().decode()
