@@ -25,6 +25,10 @@ The JSON line also holds:
     (one (b, h) slice per host thread at full length, repeated until at least
     10 s of work) on the host cores;
   * parts: per-path rates;
+  * secondary (--secondary): the bidirectional 16K GMA, the 8K-token GLA
+    forward and backward, the per-feature-decay forward, the long-context GMA
+    and the causal GMA backward at the 16K GMA shapes, each against 8 TB/s of
+    its algorithmic bytes (and, for the long-context GMA, the bf16 MFMA peak);
   * decode (--decode): the one-token steps at the model shapes of the two
     workloads, batched so that the states (about 0.5 GB) exceed the cache,
     against the same 8 TB/s (the state is read and written once per step).
@@ -247,7 +251,7 @@ def main():
     if args.secondary:
         sec = {}
         for name, fn in (("gma_bidir_n16k", "bidir"), ("gla_bf16_n8k", "gla"), ("gla_backward_bf16_n8k", "glab"),
-                         ("glv_bf16_n8k", "glv"), ("gma_bf16_n128k", "gma5")):
+                         ("glv_bf16_n8k", "glv"), ("gma_bf16_n128k", "gma5"), ("gma_backward_bf16_n16k", "gmab")):
             if fn == "bidir":
                 a = gset[0]
                 call = lambda: gma_forward(a["q"], a["k"], a["v"], a["mu"], a["log_var"], a["logit_pi"],
@@ -278,6 +282,17 @@ def main():
                 tok = cfg.B * cfg.H * cfg.N
                 # Q, K, V, O in bf16 plus one fp32 decay per key feature
                 byt = tok * (4 * cfg.dk * 2 + 4 * cfg.dk)
+            elif fn == "gmab":
+                from linear_attention_gmm_amd import gma_backward, gma_backward_workspace_bytes
+                a = gset[0]
+                gdo = torch.randn_like(a["v"])
+                wsg = torch.empty(gma_backward_workspace_bytes(gcfg.B, gcfg.H, gcfg.N, gcfg.d, gcfg.K, gcfg.dv),
+                                  dtype=torch.uint8, device=dev)
+                call = lambda: gma_backward(a["q"], a["k"], a["v"], a["mu"], a["log_var"], a["logit_pi"], gdo,
+                                            eps=gcfg.eps, workspace=wsg)
+                tok = g_tok
+                # read Q, K, V, dO and write dQ, dK, dV (bf16); parameters are negligible
+                byt = tok * 7 * gcfg.d * 2
             else:
                 cfg = inputs.CONFIGS["gma_bf16_n128k"]
                 y = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inputs.gma_inputs(cfg).items()}

@@ -382,7 +382,7 @@ int64_t gma_bwd_width(int64_t K, int64_t dv) {
 }
 
 struct GmaBwdLayout {
-  size_t iv, cst, rows[8], ones, inner[5], rg, agg, part, total;
+  size_t iv, cst, rows[8], ones, inner[5], rg, agg, part, sums, total;
   LinLayout lin;
   int64_t DL, nseg, seg_len;
 };
@@ -419,6 +419,8 @@ GmaBwdLayout gma_bwd_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t 
   off += L.lin.total;
   L.part = off;
   off = align_up(off + (size_t)H * 2 * B * L.nseg * K * (2 * d + 1) * 4);
+  L.sums = off;
+  off = align_up(off + (size_t)H * K * (2 * d + 1) * 4);
   L.total = off;
   return L;
 }
@@ -826,6 +828,7 @@ int gma_backward(const void* q, const void* k, const void* v, const float* mu, c
   La.dvx = F(L.rows[7]);
   La.ones = F(L.ones);
   La.part = F(L.part);
+  La.sums = F(L.sums);
   La.B = B;
   La.H = H;
   La.N = N;

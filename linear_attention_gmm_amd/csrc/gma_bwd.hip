@@ -28,7 +28,8 @@
 // route (responsibilities, one thread per component, 16 tokens per step),
 // pack (values [v | 1 | 0], unit gates), out_grad (dN, dD from the forward),
 // chain (softmax and log-joint chain rule per token, parameter partial sums
-// per token range), params (fixed-order sum of the partials), take_dv.
+// per token range), reduce (fixed-order sum of the partials), params,
+// take_dv.
 #include "mfma.hpp"
 #include "launch.hpp"
 
@@ -108,6 +109,18 @@ __device__ __forceinline__ void block_max16(float (&x)[kTT], float* red) {
   __syncthreads();
 }
 
+// The head's mu and 1/var as [kThr][D + 1] tables in LDS (zero rows beyond K).
+template <int D>
+__device__ __forceinline__ void load_tables(float (*smu)[D + 1], float (*siv)[D + 1], const float* __restrict__ mu,
+                                            const float* __restrict__ iv, int h, int K) {
+  for (int i = threadIdx.x; i < kThr * D; i += kThr) {
+    const int r = i / D, cc = i - r * D;
+    const bool ok = r < K;
+    smu[r][cc] = ok ? mu[((size_t)h * K + r) * D + cc] : 0.f;
+    siv[r][cc] = ok ? iv[((size_t)h * K + r) * D + cc] : 0.f;
+  }
+}
+
 // Responsibilities of the tokens of x (q for blockIdx.z = 0, k for 1) as
 // float32 rows of DL entries (components >= K are 0). Workgroup: one (b, h),
 // kTT tokens per step over a range of `len` tokens; thread = component.
@@ -122,6 +135,8 @@ __global__ __launch_bounds__(kThr) void route_kernel(const T* __restrict__ q, co
   const int bh = blockIdx.y, h = bh % H, c = threadIdx.x;
   const T* __restrict__ x = (blockIdx.z == 0 ? q : k) + (size_t)bh * N * D;
   float* __restrict__ out = (blockIdx.z == 0 ? gq : gk) + (size_t)bh * N * DL;
+  // this thread's component row of mu and 1/var, read through the cache (small
+  // LDS keeps many workgroups per CU, which measured faster than LDS tables)
   const float* __restrict__ muk = mu + ((size_t)h * K + (c < K ? c : 0)) * D;
   const float* __restrict__ ivk = iv + ((size_t)h * K + (c < K ? c : 0)) * D;
   const float ck = c < K ? cst[(size_t)h * K + c] : 0.f;
@@ -212,14 +227,14 @@ __global__ __launch_bounds__(kThr) void chain_kernel(const T* __restrict__ q, co
   __shared__ float sx[kTT][D];
   __shared__ float sdl[kTT][kThr];
   __shared__ float red[2 * kTT];
+  __shared__ float smu[kThr][D + 1];
+  __shared__ float siv[kThr][D + 1];
   const int bh = blockIdx.y, b = bh / H, h = bh % H, c = threadIdx.x, side = blockIdx.z;
   const T* __restrict__ x = (side == 0 ? q : k) + (size_t)bh * N * D;
   T* __restrict__ dx = (side == 0 ? dq : dk) + (size_t)bh * N * D;
   const float* __restrict__ gx = (side == 0 ? gq : gk) + (size_t)bh * N * DL;
   const float* __restrict__ dgx = (side == 0 ? dgq : dgk) + (size_t)bh * N * DL;
-  const float* __restrict__ muh = mu + (size_t)h * K * D;
-  const float* __restrict__ ivh = iv + (size_t)h * K * D;
-  const float* __restrict__ muk = muh + (size_t)(c < K ? c : 0) * D;
+  load_tables<D>(smu, siv, mu, iv, h, K);
   // dx mapping: feature fd = c % D, tokens t = c / D + j * (kThr / D)
   constexpr int TG = kThr / D;      // token groups
   constexpr int TPT = kTT / TG;     // tokens per thread
@@ -256,7 +271,7 @@ __global__ __launch_bounds__(kThr) void chain_kernel(const T* __restrict__ q, co
     if (c < K) {
 #pragma unroll
       for (int dd = 0; dd < D; ++dd) {
-        const float m = muk[dd];
+        const float m = smu[c][dd];
 #pragma unroll
         for (int t = 0; t < kTT; ++t) {
           const float e = sx[t][dd] - m;
@@ -272,8 +287,8 @@ __global__ __launch_bounds__(kThr) void chain_kernel(const T* __restrict__ q, co
 #pragma unroll
     for (int j = 0; j < TPT; ++j) s1[j] = s2[j] = 0.f;
     for (int kk = 0; kk < K; ++kk) {
-      const float w = ivh[(size_t)kk * D + fd];
-      const float a = muh[(size_t)kk * D + fd] * w;
+      const float w = siv[kk][fd];
+      const float a = smu[kk][fd] * w;
 #pragma unroll
       for (int j = 0; j < TPT; ++j) {
         const float d_ = sdl[tg + j * TG][kk];
@@ -300,29 +315,35 @@ __global__ __launch_bounds__(kThr) void chain_kernel(const T* __restrict__ q, co
   }
 }
 
-// Parameter gradients per head from the partial sums, summed over the slots in
-// a fixed order: dmu = iv * S1, dlog_var = -1/2 S0 + 1/2 iv * S2, dlogit_pi =
-// S0 - pi * sum S0.
-__global__ __launch_bounds__(kThr) void params_kernel(const float* __restrict__ part, const float* __restrict__ iv,
+// Sum of the partial sums over the slots, in a fixed order: one thread per
+// (head, component, entry); red[h][k][F] with F = 2 D + 1.
+__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, float* __restrict__ red,
+                                                     int64_t n, int K, int F, int nslot) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t h = i / ((int64_t)K * F), e = i - h * K * F;  // e = k * F + f
+  const float* src = part + (size_t)h * nslot * K * F + e;
+  float s = 0.f;
+  for (int sl = 0; sl < nslot; ++sl) s += src[(size_t)sl * K * F];
+  red[i] = s;
+}
+
+// Parameter gradients per head from the summed partials S1, S2, S0:
+// dmu = iv * S1, dlog_var = -1/2 S0 + 1/2 iv * S2, dlogit_pi = S0 - pi * sum S0.
+__global__ __launch_bounds__(kThr) void params_kernel(const float* __restrict__ sums, const float* __restrict__ iv,
                                                       const float* __restrict__ logit_pi, float* __restrict__ dmu,
-                                                      float* __restrict__ dlv, float* __restrict__ dlp, int K, int D,
-                                                      int nslot) {
+                                                      float* __restrict__ dlv, float* __restrict__ dlp, int K,
+                                                      int D) {
   __shared__ float red[kThr];
   const int h = blockIdx.x, c = threadIdx.x;
   const int F = 2 * D + 1;
-  float g0 = 0.f;
+  const float* base = sums + ((size_t)h * K + (c < K ? c : 0)) * F;
+  const float g0 = c < K ? base[2 * D] : 0.f;
   if (c < K) {
-    const float* base = part + (size_t)h * nslot * K * F + (size_t)c * F;
-    for (int s = 0; s < nslot; ++s) g0 += base[(size_t)s * K * F + 2 * D];
     for (int dd = 0; dd < D; ++dd) {
-      float s1 = 0.f, s2 = 0.f;
-      for (int s = 0; s < nslot; ++s) {
-        s1 += base[(size_t)s * K * F + dd];
-        s2 += base[(size_t)s * K * F + D + dd];
-      }
       const float w = iv[((size_t)h * K + c) * D + dd];
-      dmu[((size_t)h * K + c) * D + dd] = w * s1;
-      dlv[((size_t)h * K + c) * D + dd] = -0.5f * g0 + 0.5f * w * s2;
+      dmu[((size_t)h * K + c) * D + dd] = w * base[dd];
+      dlv[((size_t)h * K + c) * D + dd] = -0.5f * g0 + 0.5f * w * base[D + dd];
     }
   }
   // pi and the total of G over the components
@@ -402,8 +423,13 @@ static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
                      static_cast<const T*>(L.k), L.gq, L.gk, L.dgq, L.dgk, L.mu, L.iv, static_cast<T*>(L.dq),
                      static_cast<T*>(L.dk), L.part, L.N, (int)L.B, H, K, DL, L.seg_len, (int)L.nseg);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(params_kernel, dim3((unsigned)H), dim3(kThr), 0, st, L.part, L.iv, L.logit_pi, L.dmu,
-                     L.dlog_var, L.dlogit_pi, K, D, (int)(2 * L.B * L.nseg));
+  const int NF = 2 * D + 1;
+  const int64_t nred = (int64_t)H * K * NF;
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((nred + 255) / 256)), dim3(256), 0, st, L.part, L.sums, nred, K,
+                     NF, (int)(2 * L.B * L.nseg));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(params_kernel, dim3((unsigned)H), dim3(kThr), 0, st, L.sums, L.iv, L.logit_pi, L.dmu,
+                     L.dlog_var, L.dlogit_pi, K, D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((take_dv_kernel<T>), dim3((unsigned)((rows * D + 255) / 256)), dim3(256), 0, st, L.dvx,
                      static_cast<T*>(L.dv), rows, D, DL);

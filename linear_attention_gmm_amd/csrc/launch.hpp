@@ -163,6 +163,7 @@ struct GmaBwdLaunch {
   float* dvx;
   float* ones;
   float* part;
+  float* sums;  // the partials summed over the slots [H][K][2 D + 1]
   int64_t B, H, N, D, K, DL, nseg, seg_len;
   float eps;
   bool bf16;
