@@ -222,8 +222,8 @@ int linattn_chunk_backward(const void* q, const void* k, const void* v, const fl
                            int64_t segments, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Backward pass of causal GMA: given the output gradient dout [B,H,N,dv] of
- * gma_forward(q, k, v, mu, log_var, logit_pi, causal = 1, eps), writes the
+ * Backward pass of GMA: given the output gradient dout [B,H,N,dv] of
+ * gma_forward(q, k, v, mu, log_var, logit_pi, causal, eps), writes the
  * gradients of sum(out * dout):
  *   dq, dk [B,H,N,d], dv [B,H,N,dv]                 (dtype, 16-byte aligned)
  *   dmu, dlog_var [H,K,d], dlogit_pi [H,K]          (float32, 4-byte aligned)
@@ -232,15 +232,18 @@ int linattn_chunk_backward(const void* q, const void* k, const void* v, const fl
  * backward of that linear attention gives the gradients of the features and of
  * v; the chain rule through the softmax over components and the Gaussian log
  * joint gives dq, dk and the parameter gradients (summed over the batch and
- * over both the query and the key tokens, in a fixed order). Everything is
- * computed in float32; bf16 gradients are rounded once.
+ * over both the query and the key tokens, in a fixed order). The
+ * bidirectional form is the same inner linear attention over 2N rows, keys and
+ * values first, then the queries. Everything is computed in float32; bf16
+ * gradients are rounded once.
  * Source: "Gaussian Mixture Attention", Method -> core mechanism (posterior
  * responsibilities), latent memory routing (write and read phases), variants
  * and training (trained end to end; softplus variances, softmax priors).
- * Implemented: causal = 1 (0 gives LM_EUNSUPPORTED), d == dv in {32, 64},
- * 1 <= K <= 128. Outputs must not overlap each other, the inputs or the
- * workspace (of at least gma_backward_workspace_bytes; float32 rows of
- * 64 or 128 entries per token: about 14 such tensors).
+ * Implemented: causal 0 or 1, d == dv in {32, 64}, 1 <= K <= 128,
+ * N <= 2^29. Outputs must not overlap each other, the inputs or the workspace
+ * (of at least gma_backward_workspace_bytes; float32 rows of 64 or 128
+ * entries per token, about 14 such tensors, twice as many rows when
+ * bidirectional).
  */
 size_t gma_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K,
                                     int64_t dv, int causal, int dtype);

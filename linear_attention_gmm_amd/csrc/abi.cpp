@@ -384,20 +384,21 @@ int64_t gma_bwd_width(int64_t K, int64_t dv) {
 struct GmaBwdLayout {
   size_t iv, cst, rows[8], ones, inner[5], rg, agg, part, sums, total;
   LinLayout lin;
-  int64_t DL, nseg, seg_len;
+  int64_t DL, nseg, seg_len, NN;
 };
 
-GmaBwdLayout gma_bwd_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv) {
+GmaBwdLayout gma_bwd_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal) {
   GmaBwdLayout L;
   L.DL = gma_bwd_width(K, dv);
+  L.NN = causal ? N : 2 * N;  // bidirectional: keys in rows [0, N), queries in [N, 2N)
   // token ranges of the routing and chain-rule kernels: about 1024 workgroups
   const int64_t want = (1024 + 2 * B * H - 1) / (2 * B * H);
   int64_t len = (N + want - 1) / want;
   len = (len + 15) / 16 * 16;
   L.seg_len = len;
   L.nseg = (N + len - 1) / len;
-  L.lin = lin_layout(B, H, N, L.DL, false, 0);
-  const size_t rowt = align_up((size_t)B * H * N * L.DL * 4), colt = align_up((size_t)B * H * N * 4);
+  L.lin = lin_layout(B, H, L.NN, L.DL, false, 0);
+  const size_t rowt = align_up((size_t)B * H * L.NN * L.DL * 4), colt = align_up((size_t)B * H * L.NN * 4);
   size_t off = 0;
   L.iv = off;
   off = align_up(off + (size_t)H * K * d * 4);
@@ -431,12 +432,11 @@ int gma_bwd_check(const char* fn, int64_t B, int64_t H, int64_t N, int64_t d, in
   if (dtype != LM_F32 && dtype != LM_BF16) return fail(LM_EINVAL, "%s: dtype %d is not LM_F32 or LM_BF16", fn, dtype);
   if (causal != 0 && causal != 1) return fail(LM_EINVAL, "%s: causal must be 0 or 1 (got %d)", fn, causal);
   if (!(eps >= 0.f) || std::isinf(eps)) return fail(LM_EINVAL, "%s: eps must be finite and >= 0", fn);
-  if (!causal) return fail(LM_EUNSUPPORTED, "%s implements the causal form", fn);
   if (!(d == 32 || d == 64) || dv != d)
     return fail(LM_EUNSUPPORTED, "%s implements d == dv in {32, 64} (got d=%lld dv=%lld)", fn, (long long)d,
                 (long long)dv);
   if (K > 128) return fail(LM_EUNSUPPORTED, "%s implements K <= 128 (got %lld)", fn, (long long)K);
-  if (N > (int64_t(1) << 30) || B * H > 65535) return fail(LM_EUNSUPPORTED, "%s: N <= 2^30 and B*H <= 65535", fn);
+  if (N > (int64_t(1) << 29) || B * H > 65535) return fail(LM_EUNSUPPORTED, "%s: N <= 2^29 and B*H <= 65535", fn);
   return LM_OK;
 }
 
@@ -740,7 +740,7 @@ int linattn_chunk_backward(const void* q, const void* k, const void* v, const fl
 size_t gma_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal,
                                     int dtype) {
   if (gma_bwd_check("gma_backward", B, H, N, d, K, dv, causal, 0.f, dtype) != LM_OK) return 0;
-  return gma_bwd_layout(B, H, N, d, K, dv).total;
+  return gma_bwd_layout(B, H, N, d, K, dv, causal).total;
 }
 
 int gma_backward(const void* q, const void* k, const void* v, const float* mu, const float* log_var,
@@ -759,7 +759,7 @@ int gma_backward(const void* q, const void* k, const void* v, const float* mu, c
   const void* p4[] = {mu, log_var, logit_pi, dmu, dlog_var, dlogit_pi};
   for (const void* p : p4)
     if (!aligned(p, 4)) return fail(LM_EINVAL, "%s: misaligned parameter pointer", fn);
-  const GmaBwdLayout L = gma_bwd_layout(B, H, N, d, K, dvv);
+  const GmaBwdLayout L = gma_bwd_layout(B, H, N, d, K, dvv, causal);
   if (workspace_bytes < L.total)
     return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
   // outputs must not overlap each other, the inputs or the workspace
@@ -784,7 +784,7 @@ int gma_backward(const void* q, const void* k, const void* v, const float* mu, c
   Bw.fwd.b_lambda = nullptr;
   Bw.fwd.B = B;
   Bw.fwd.H = H;
-  Bw.fwd.N = N;
+  Bw.fwd.N = L.NN;
   Bw.fwd.D = L.DL;
   Bw.fwd.P = L.lin.plan.P;
   Bw.fwd.seg_len = L.lin.plan.seg_len;
@@ -800,7 +800,7 @@ int gma_backward(const void* q, const void* k, const void* v, const float* mu, c
   Bw.dg = nullptr;
   Bw.B = B;
   Bw.H = H;
-  Bw.N = N;
+  Bw.N = L.NN;
   Bw.D = L.DL;
   Bw.bf16 = false;
   La.q = q;
@@ -837,6 +837,8 @@ int gma_backward(const void* q, const void* k, const void* v, const float* mu, c
   La.DL = L.DL;
   La.nseg = L.nseg;
   La.seg_len = L.seg_len;
+  La.NN = L.NN;
+  La.causal = causal;
   La.eps = eps;
   La.bf16 = dtype == LM_BF16;
   hipError_t e = lm::gma_backward_launch(La, static_cast<hipStream_t>(stream));

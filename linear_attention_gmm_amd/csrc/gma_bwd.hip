@@ -24,6 +24,11 @@
 // input dtype. The constant -d/2 log 2 pi of the log density cancels in the
 // softmax and is left out.
 //
+// Bidirectional: every query reads the memory of the whole sequence, which is
+// the causal linear attention over a sequence of 2N rows with the keys and
+// values in rows [0, N) and the queries in rows [N, 2N) (zero rows elsewhere):
+// the same inner forward and backward then give the gradients.
+//
 // Kernels: prep (per head: 1/var and the constant part of the log joint),
 // route (responsibilities, one thread per component, 16 tokens per step),
 // pack (values [v | 1 | 0], unit gates), out_grad (dN, dD from the forward),
@@ -128,13 +133,13 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThr) void route_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                      const float* __restrict__ mu, const float* __restrict__ iv,
                                                      const float* __restrict__ cst, float* __restrict__ gq,
-                                                     float* __restrict__ gk, int64_t N, int H, int K, int DL,
-                                                     int64_t len) {
+                                                     float* __restrict__ gk, int64_t N, int64_t NN, int64_t qoff,
+                                                     int H, int K, int DL, int64_t len) {
   __shared__ float sx[kTT][D];
   __shared__ float red[2 * kTT];
   const int bh = blockIdx.y, h = bh % H, c = threadIdx.x;
   const T* __restrict__ x = (blockIdx.z == 0 ? q : k) + (size_t)bh * N * D;
-  float* __restrict__ out = (blockIdx.z == 0 ? gq : gk) + (size_t)bh * N * DL;
+  float* __restrict__ out = blockIdx.z == 0 ? gq + ((size_t)bh * NN + qoff) * DL : gk + (size_t)bh * NN * DL;
   // this thread's component row of mu and 1/var, read through the cache (small
   // LDS keeps many workgroups per CU, which measured faster than LDS tables)
   const float* __restrict__ muk = mu + ((size_t)h * K + (c < K ? c : 0)) * D;
@@ -179,36 +184,48 @@ __global__ __launch_bounds__(kThr) void route_kernel(const T* __restrict__ q, co
   }
 }
 
-// Values of the inner linear attention [v | 1 | 0 ...] (DL columns) and unit
-// gates.
+// Values of the inner linear attention [v | 1 | 0 ...] (DL columns) in rows
+// [0, N) of each sequence's NN inner rows.
 template <typename T>
-__global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ v, float* __restrict__ vx,
-                                                   float* __restrict__ ones, int64_t rows, int DV, int DL) {
+__global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ v, float* __restrict__ vx, int64_t N,
+                                                   int64_t NN, int64_t total, int DV, int DL) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * DL) return;
-  const int64_t r = i / DL;
+  if (i >= total) return;
+  const int64_t r = i / DL;  // bh * N + t
   const int c = (int)(i - r * DL);
-  vx[i] = c < DV ? to_f32(v[r * DV + c]) : (c == DV ? 1.f : 0.f);
-  if (c == 0) ones[r] = 1.f;
+  const int64_t bh = r / N, t = r - bh * N;
+  vx[((size_t)bh * NN + t) * DL + c] = c < DV ? to_f32(v[r * DV + c]) : (c == DV ? 1.f : 0.f);
+}
+
+// rows [r0, r0 + nr) of every sequence of a [BH][NN][DL] tensor set to x
+// (also the unit gates: DL = 1).
+__global__ __launch_bounds__(256) void fill_rows_kernel(float* __restrict__ p, int64_t NN, int64_t r0, int64_t nr,
+                                                        int DL, float x, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t per = nr * DL;
+  const int64_t bh = i / per, e = i - bh * per;
+  p[((size_t)bh * NN + r0) * DL + e] = x;
 }
 
 // From the inner forward y = [N | D - eps | ...] and dO: the output gradient of
 // the inner linear attention [dN | dD | 0 ...], one wave per token (DV <= 64).
 template <typename T>
 __global__ __launch_bounds__(256) void out_grad_kernel(const float* __restrict__ y, const T* __restrict__ dout,
-                                                       float* __restrict__ dy, int64_t rows, int DV, int DL,
-                                                       float eps) {
-  const int64_t r = (int64_t)blockIdx.x * 4 + wave_id();
+                                                       float* __restrict__ dy, int64_t N, int64_t NN, int64_t qoff,
+                                                       int64_t rows, int DV, int DL, float eps) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave_id();  // bh * N + t
   if (r >= rows) return;
+  const int64_t bh = r / N, yr = bh * NN + qoff + (r - bh * N);  // the query's inner row
   const int l = lane_id();
-  const float den = y[r * DL + DV] + eps;
+  const float den = y[yr * DL + DV] + eps;
   const float inv = 1.f / den;
   const float gd = l < DV ? to_f32(dout[r * DV + l]) : 0.f;
-  const float o = l < DV ? y[r * DL + l] * inv : 0.f;
+  const float o = l < DV ? y[yr * DL + l] * inv : 0.f;
   float s = gd * o;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  for (int c = l; c < DL; c += 64) dy[r * DL + c] = c < DV ? gd * inv : (c == DV ? -s * inv : 0.f);
+  for (int c = l; c < DL; c += 64) dy[yr * DL + c] = c < DV ? gd * inv : (c == DV ? -s * inv : 0.f);
 }
 
 // Chain rule through the softmax and the log joint for the tokens of one side
@@ -223,7 +240,8 @@ __global__ __launch_bounds__(kThr) void chain_kernel(const T* __restrict__ q, co
                                                      const float* __restrict__ dgq, const float* __restrict__ dgk,
                                                      const float* __restrict__ mu, const float* __restrict__ iv,
                                                      T* __restrict__ dq, T* __restrict__ dk, float* __restrict__ part,
-                                                     int64_t N, int B, int H, int K, int DL, int64_t len, int nseg) {
+                                                     int64_t N, int64_t NN, int64_t qoff, int B, int H, int K, int DL,
+                                                     int64_t len, int nseg) {
   __shared__ float sx[kTT][D];
   __shared__ float sdl[kTT][kThr];
   __shared__ float red[2 * kTT];
@@ -232,8 +250,9 @@ __global__ __launch_bounds__(kThr) void chain_kernel(const T* __restrict__ q, co
   const int bh = blockIdx.y, b = bh / H, h = bh % H, c = threadIdx.x, side = blockIdx.z;
   const T* __restrict__ x = (side == 0 ? q : k) + (size_t)bh * N * D;
   T* __restrict__ dx = (side == 0 ? dq : dk) + (size_t)bh * N * D;
-  const float* __restrict__ gx = (side == 0 ? gq : gk) + (size_t)bh * N * DL;
-  const float* __restrict__ dgx = (side == 0 ? dgq : dgk) + (size_t)bh * N * DL;
+  const size_t row0 = (size_t)bh * NN + (side == 0 ? qoff : 0);  // inner row of this side's token 0
+  const float* __restrict__ gx = (side == 0 ? gq : gk) + row0 * DL;
+  const float* __restrict__ dgx = (side == 0 ? dgq : dgk) + row0 * DL;
   load_tables<D>(smu, siv, mu, iv, h, K);
   // dx mapping: feature fd = c % D, tokens t = c / D + j * (kThr / D)
   constexpr int TG = kThr / D;      // token groups
@@ -376,30 +395,48 @@ __global__ __launch_bounds__(kThr) void params_kernel(const float* __restrict__ 
 
 // dv = the first DV columns of the inner value gradient, in the input dtype.
 template <typename T>
-__global__ __launch_bounds__(256) void take_dv_kernel(const float* __restrict__ dvx, T* __restrict__ dv, int64_t rows,
-                                                      int DV, int DL) {
+__global__ __launch_bounds__(256) void take_dv_kernel(const float* __restrict__ dvx, T* __restrict__ dv, int64_t N,
+                                                      int64_t NN, int64_t rows, int DV, int DL) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= rows * DV) return;
-  const int64_t r = i / DV;
+  const int64_t r = i / DV;  // bh * N + t
   const int c = (int)(i - r * DV);
-  dv[i] = from_f32<T>(dvx[r * DL + c]);
+  const int64_t bh = r / N;
+  dv[i] = from_f32<T>(dvx[((size_t)bh * NN + (r - bh * N)) * DL + c]);
+}
+
+static hipError_t fill_rows(float* p, const GmaBwdLaunch& L, int64_t r0, int64_t nr, int DL, float x,
+                            hipStream_t st) {
+  const int64_t total = L.B * L.H * nr * DL;
+  hipLaunchKernelGGL(fill_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, p, L.NN, r0, nr, DL, x,
+                     total);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
   const int64_t BH = L.B * L.H, rows = BH * L.N;
   const int K = (int)L.K, DL = (int)L.DL, H = (int)L.H;
+  const int64_t N = L.N, NN = L.NN, qoff = L.causal ? 0 : N;
   hipError_t e;
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)H), dim3(kThr), 0, st, L.log_var, L.logit_pi, L.iv, L.cst, K, D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!L.causal) {
+    // bidirectional: queries in rows [N, 2N), keys and values in [0, N)
+    if ((e = fill_rows(L.gq, L, 0, N, DL, 0.f, st)) != hipSuccess) return e;
+    if ((e = fill_rows(L.gk, L, N, N, DL, 0.f, st)) != hipSuccess) return e;
+    if ((e = fill_rows(L.vx, L, N, N, DL, 0.f, st)) != hipSuccess) return e;
+    if ((e = fill_rows(L.dy, L, 0, N, DL, 0.f, st)) != hipSuccess) return e;
+  }
+  if ((e = fill_rows(L.ones, L, 0, NN, 1, 1.f, st)) != hipSuccess) return e;
   const dim3 grid((unsigned)L.nseg, (unsigned)BH, 2);
   hipLaunchKernelGGL((route_kernel<T, D>), grid, dim3(kThr), 0, st, static_cast<const T*>(L.q),
-                     static_cast<const T*>(L.k), L.mu, L.iv, L.cst, L.gq, L.gk, L.N, H, K, DL, L.seg_len);
+                     static_cast<const T*>(L.k), L.mu, L.iv, L.cst, L.gq, L.gk, N, NN, qoff, H, K, DL, L.seg_len);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((pack_kernel<T>), dim3((unsigned)((rows * DL + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const T*>(L.v), L.vx, L.ones, rows, D, DL);
+                     static_cast<const T*>(L.v), L.vx, N, NN, rows * DL, D, DL);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // inner forward: y = [N | D - eps | 0 ...]
+  // inner forward: y = [N | D - eps | 0 ...] at the query rows
   LinLaunch F = L.bwd.fwd;
   F.q = L.gq;
   F.k = L.gk;
@@ -413,7 +450,7 @@ static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
   F.t_in = 0;
   if ((e = linattn_launch(F, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((out_grad_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, L.y,
-                     static_cast<const T*>(L.dout), L.dy, rows, D, DL, L.eps);
+                     static_cast<const T*>(L.dout), L.dy, N, NN, qoff, rows, D, DL, L.eps);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // gradients of the inner linear attention: features (dgq, dgk) and values
   BwdLaunch Bw = L.bwd;
@@ -421,7 +458,7 @@ static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
   if ((e = linattn_backward_f32(Bw, L.gq, L.gk, L.vx, L.dy, L.dgq, L.dgk, L.dvx, false, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((chain_kernel<T, D>), grid, dim3(kThr), 0, st, static_cast<const T*>(L.q),
                      static_cast<const T*>(L.k), L.gq, L.gk, L.dgq, L.dgk, L.mu, L.iv, static_cast<T*>(L.dq),
-                     static_cast<T*>(L.dk), L.part, L.N, (int)L.B, H, K, DL, L.seg_len, (int)L.nseg);
+                     static_cast<T*>(L.dk), L.part, N, NN, qoff, (int)L.B, H, K, DL, L.seg_len, (int)L.nseg);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int NF = 2 * D + 1;
   const int64_t nred = (int64_t)H * K * NF;
@@ -432,7 +469,7 @@ static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
                      L.dlog_var, L.dlogit_pi, K, D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((take_dv_kernel<T>), dim3((unsigned)((rows * D + 255) / 256)), dim3(256), 0, st, L.dvx,
-                     static_cast<T*>(L.dv), rows, D, DL);
+                     static_cast<T*>(L.dv), N, NN, rows, D, DL);
   return hipGetLastError();
 }
 

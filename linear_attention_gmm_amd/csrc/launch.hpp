@@ -129,9 +129,10 @@ hipError_t linattn_backward_launch(const BwdLaunch& L, hipStream_t st);
 hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float* k, const float* v,
                                 const float* dout, float* dq, float* dk, float* dv, bool gates, hipStream_t st);
 
-// Backward pass of causal GMA (gma_bwd.hip): the float32 backward of the
-// linear attention with responsibilities as features and [v | 1] as values,
-// then the chain rule through the softmax and the Gaussian log joint.
+// Backward pass of GMA (gma_bwd.hip): the float32 backward of the linear
+// attention with responsibilities as features and [v | 1] as values (over 2N
+// rows for the bidirectional form), then the chain rule through the softmax and
+// the Gaussian log joint.
 struct GmaBwdLaunch {
   BwdLaunch bwd;  // inner linear attention: D = DL, float32, its workspace
   const void* q;
@@ -148,9 +149,10 @@ struct GmaBwdLaunch {
   float* dlog_var;
   float* dlogit_pi;
   // workspace (float32): per head 1/var [H][K][D] and the constant part of the
-  // log joint [H][K]; rows of DL entries: responsibilities of q and k, values
-  // [v | 1], inner output, its gradient, feature and value gradients; unit
-  // gates; parameter partial sums [H][2 B nseg][K][2 D + 1]
+  // log joint [H][K]; [B*H][NN] rows of DL entries: responsibilities of q and
+  // k, values [v | 1], inner output, its gradient, feature and value
+  // gradients; unit gates [B*H][NN]; parameter partial sums
+  // [H][2 B nseg][K][2 D + 1]
   float* iv;
   float* cst;
   float* gq;
@@ -165,6 +167,8 @@ struct GmaBwdLaunch {
   float* part;
   float* sums;  // the partials summed over the slots [H][K][2 D + 1]
   int64_t B, H, N, D, K, DL, nseg, seg_len;
+  int64_t NN;  // inner rows per sequence: N (causal) or 2N (bidirectional)
+  int causal;
   float eps;
   bool bf16;
 };

@@ -285,7 +285,7 @@ def test_gma_backward_errors():
     bf, f32 = binding.LM_BF16, binding.LM_F32
     wsb = L.gma_backward_workspace_bytes(2, 2, 300, 64, 128, 64, 1, bf)
     assert wsb > 0
-    assert L.gma_backward_workspace_bytes(2, 2, 300, 64, 128, 64, 0, bf) == 0  # bidirectional: not implemented
+    assert L.gma_backward_workspace_bytes(2, 2, 300, 64, 128, 64, 0, bf) > wsb  # bidirectional: 2N inner rows
     assert L.gma_backward_workspace_bytes(2, 2, 300, 128, 128, 128, 1, bf) == 0  # d = 128: not implemented
     assert L.gma_backward_workspace_bytes(2, 2, 300, 64, 129, 64, 1, f32) == 0  # K > 128: not implemented
     assert L.gma_backward_workspace_bytes(2, 2, 300, 32, 16, 32, 1, f32) > 0
@@ -302,7 +302,7 @@ def test_gma_backward_errors():
     assert call(dmu=dmu + 2) == binding.LM_EINVAL  # misaligned
     assert call(dq=None) == binding.LM_EINVAL
     assert call(eps=-1.0) == binding.LM_EINVAL
-    assert call(causal=0) == binding.LM_EUNSUPPORTED
+    assert call(causal=2) == binding.LM_EINVAL
     assert call(d=128) == binding.LM_EUNSUPPORTED
     assert call(K=200) == binding.LM_EUNSUPPORTED
     assert L.lm_last_error().decode()

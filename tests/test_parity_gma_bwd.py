@@ -1,5 +1,5 @@
-"""Backward pass of causal GMA on the GPU against the fp64 reverse-mode oracle
-(oracle/grad.py) on the same seeded inputs."""
+"""Backward pass of GMA (causal and bidirectional) on the GPU against the fp64
+reverse-mode oracle (oracle/grad.py) on the same seeded inputs."""
 import numpy as np
 import pytest
 import torch
@@ -13,16 +13,17 @@ pytestmark = pytest.mark.gpu
 NAMES = ("dq", "dk", "dv", "dmu", "dlog_var", "dlogit_pi")
 
 
-def _case(cfg, N=None, heads=None, eps=None):
+def _case(cfg, N=None, heads=None, eps=None, causal=True):
     """GPU gradients of the whole config and the oracle's for the heads listed
     (all batch entries of a head: the parameter gradients sum over them)."""
     x = inputs.gma_inputs(cfg, N=N)
     eps = cfg.eps if eps is None else eps
     n = x["q"].shape[2]
     do = torch.from_numpy(np.random.default_rng([cfg.cfg_id, 98]).standard_normal(x["v"].shape)).to(x["v"].dtype)
-    say("gma backward: %s N=%d d=%d K=%d dtype=%s" % (cfg.name, n, cfg.d, cfg.K, cfg.dtype))
+    say("gma backward: %s N=%d d=%d K=%d dtype=%s causal=%d" % (cfg.name, n, cfg.d, cfg.K, cfg.dtype, causal))
     d = cuda(x)
-    got = binding.gma_backward(d["q"], d["k"], d["v"], d["mu"], d["log_var"], d["logit_pi"], do.cuda(), eps=eps)
+    got = binding.gma_backward(d["q"], d["k"], d["v"], d["mu"], d["log_var"], d["logit_pi"], do.cuda(), eps=eps,
+                               causal=causal)
     torch.cuda.synchronize()
     got = [host(t) for t in got]
     heads = list(range(cfg.H)) if heads is None else heads
@@ -31,7 +32,7 @@ def _case(cfg, N=None, heads=None, eps=None):
     for h in heads:
         hs = slice(h, h + 1)
         ref = grad.gma_backward(x["q"][:, hs], x["k"][:, hs], x["v"][:, hs], x["mu"][hs], x["log_var"][hs],
-                                x["logit_pi"][hs], do[:, hs], eps)
+                                x["logit_pi"][hs], do[:, hs], eps, causal)
         for i in range(3):
             gs[i].append(got[i][:, h])
             rs[i].append(ref[i][:, 0])
@@ -81,7 +82,25 @@ def test_gma_backward_full_size_sampled():
         assert_close(a, r, "bf16", "%s bf16 4K workload, head 5" % name)
 
 
-def test_gma_backward_rejects_bidirectional():
-    x = cuda(inputs.gma_inputs(inputs.GmaConfig("gma_bwd_rej", 704, B=1, H=1, N=8, d=32, K=4, dv=32, dtype="f32")))
-    with pytest.raises(binding.LinmixError):
-        binding.gma_backward(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"], x["v"], causal=False)
+@pytest.mark.parametrize("d,K,N", [(32, 16, 200), (64, 63, 300)])
+def test_gma_backward_bidirectional_fp32(d, K, N):
+    cfg = inputs.GmaConfig("gma_bwd_bidir", 704, B=2, H=2, N=N, d=d, K=K, dv=d, dtype="f32")
+    got, ref = _case(cfg, causal=False)
+    for name, a, r in zip(NAMES, got, ref):
+        assert_close(a, r, "f32", "%s fp32 bidirectional d=%d K=%d N=%d" % (name, d, K, N))
+
+
+@pytest.mark.parametrize("N", [1, 17])
+def test_gma_backward_bidirectional_short(N):
+    # eps as in the causal short test: a one-token sequence is the same function
+    cfg = inputs.GmaConfig("gma_bwd_bidir_short", 705, B=1, H=2, N=N, d=32, K=16, dv=32, dtype="f32", eps=0.25)
+    got, ref = _case(cfg, causal=False)
+    for name, a, r in zip(NAMES, got, ref):
+        assert_close(a, r, "f32", "%s fp32 bidirectional N=%d" % (name, N))
+
+
+def test_gma_backward_bidirectional_bf16():
+    cfg = inputs.CONFIGS["gma_bf16_n4k"].replace(name="gma_bwd_bidir_bf16", cfg_id=706, B=2, H=2, N=300)
+    got, ref = _case(cfg, causal=False)
+    for name, a, r in zip(NAMES, got, ref):
+        assert_close(a, r, "bf16", "%s bf16 bidirectional N=300" % name)
