@@ -92,3 +92,41 @@ def gma_backward(q, k, v, mu, log_var, logit_pi, do, eps, causal=True):
     o = gma_forward_torch(q, k, v, mu, log_var, logit_pi, eps, causal)
     o.backward(do)
     return tuple(x.grad.numpy() for x in xs)
+
+
+def ccq_forward_torch(q, k, v, g, w, b) -> torch.Tensor:
+    """o [B,H,N,dv] of the curvature-conditioned read over decayed linear
+    attention ("Don't Read Everything: A Curvature-Conditioned Query for Linear
+    Attention", section 2 Method), token by token (differentiable): running key
+    sums M = sum k k^T and m = sum k, covariance Sigma_t = M/t - (m/t)(m/t)^T,
+    lambda_t = sigmoid(w . q_t + b), q_clean = q_t - lambda_t Sigma_t q_t, state
+    S_t = g_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_clean."""
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    S = torch.zeros(B, H, dk, dv, dtype=q.dtype)
+    M = torch.zeros(B, H, dk, dk, dtype=q.dtype)
+    m = torch.zeros(B, H, dk, dtype=q.dtype)
+    outs = []
+    for t in range(N):
+        kt, qt = k[:, :, t], q[:, :, t]
+        M = M + kt[..., :, None] * kt[..., None, :]
+        m = m + kt
+        mu = m / (t + 1)
+        sigma = M / (t + 1) - mu[..., :, None] * mu[..., None, :]
+        lam = torch.sigmoid((w[None] * qt).sum(-1) + b[None])
+        qc = qt - lam[..., None] * (sigma * qt[..., None, :]).sum(-1)
+        S = g[:, :, t, None, None] * S + kt[..., :, None] * v[:, :, t, None, :]
+        outs.append((S * qc[..., :, None]).sum(dim=2))
+    return torch.stack(outs, dim=2)
+
+
+def ccq_backward(q, k, v, g, w, b, do):
+    """Gradients (dq, dk, dv, dg, dw, db) of sum(o * do) with
+    o = ccq_forward_torch(q, k, v, g, w, b); returns numpy float64."""
+    q, k, v, g, w, b, do = map(_t, (q, k, v, g, w, b, do))
+    xs = (q, k, v, g, w, b)
+    for x in xs:
+        x.requires_grad_(True)
+    o = ccq_forward_torch(q, k, v, g, w, b)
+    o.backward(do)
+    return tuple(x.grad.numpy() for x in xs)

@@ -512,10 +512,43 @@ def pin_gma_backward(orc):
             assert relerr(gx, num) < 1e-7, ("gradient", causal, idx, relerr(gx, num))
 
 
+def pin_ccq_backward(orc):
+    """Gradients of the CCQ read: the autograd oracle's forward equals oracle.c's
+    recurrence, and every gradient (q, k, v, g, w, b) equals central finite
+    differences of oracle.c's forward (keys with a common offset and a strong
+    gate, so that the covariance term carries weight)."""
+    from oracle import grad
+    rng = _rng(603)
+    B, H, N, dk = 1, 2, 6, 3
+    q = rng.standard_normal((B, H, N, dk))
+    k = rng.standard_normal((B, H, N, dk)) + 0.5
+    v = rng.standard_normal((B, H, N, dk))
+    g = rng.uniform(0.3, 1.0, (B, H, N))
+    w = rng.standard_normal((H, dk))
+    b = np.array([1.0, -0.5])
+    do = rng.standard_normal((B, H, N, dk))
+    fw = grad.ccq_forward_torch(*[grad._t(x) for x in (q, k, v, g, w, b)]).numpy()
+    assert relerr(fw, orc.ccq_forward(q, k, v, g, w, b)) < 1e-12
+    gs = grad.ccq_backward(q, k, v, g, w, b, do)
+    base = [q, k, v, g, w, b]
+    loss = lambda a: float(np.sum(orc.ccq_forward(*a) * do))
+    h = 1e-6
+    for idx, gx in enumerate(gs):
+        x = base[idx]
+        num = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp = x.copy(); xp[pos] += h
+            xm = x.copy(); xm[pos] -= h
+            ap = list(base); ap[idx] = xp
+            am = list(base); am[idx] = xm
+            num[pos] = (loss(ap) - loss(am)) / (2 * h)
+        assert relerr(gx, num) < 1e-7, ("gradient", idx, relerr(gx, num))
+
+
 ALL_PINS = [
     pin_gamma_scipy, pin_gma_brute_numpy, pin_gma_k1_closed_form, pin_gma_identical_components,
     pin_gma_permutation, pin_gma_prefix, pin_gma_affinity_structure, pin_gma_golden,
     pin_gla_brute, pin_gla_chunkwise, pin_ccq_numpy_cov, pin_cov_is_logpartition_hessian,
     pin_ccq_reductions, pin_ccq_chunkwise, pin_ccq_golden, pin_gma_state, pin_gla_state,
-    pin_ccq_state, pin_glv, pin_gla_backward, pin_gma_backward,
+    pin_ccq_state, pin_glv, pin_gla_backward, pin_gma_backward, pin_ccq_backward,
 ]
