@@ -26,8 +26,9 @@ The JSON line also holds:
     10 s of work) on the host cores;
   * parts: per-path rates;
   * secondary (--secondary): the bidirectional 16K GMA, the 8K-token GLA
-    forward and backward, the per-feature-decay forward, the long-context GMA
-    and the causal GMA backward at the 16K GMA shapes, each against 8 TB/s of
+    forward and backward, the per-feature-decay forward, the long-context GMA,
+    the causal GMA backward at the 16K GMA shapes and the CCQ backward at the
+    CCQ workload, each against 8 TB/s of
     its algorithmic bytes (and, for the long-context GMA, the bf16 MFMA peak);
   * decode (--decode): the one-token steps at the model shapes of the two
     workloads, batched so that the states (about 0.5 GB) exceed the cache,
@@ -251,7 +252,8 @@ def main():
     if args.secondary:
         sec = {}
         for name, fn in (("gma_bidir_n16k", "bidir"), ("gla_bf16_n8k", "gla"), ("gla_backward_bf16_n8k", "glab"),
-                         ("glv_bf16_n8k", "glv"), ("gma_bf16_n128k", "gma5"), ("gma_backward_bf16_n16k", "gmab")):
+                         ("glv_bf16_n8k", "glv"), ("gma_bf16_n128k", "gma5"), ("gma_backward_bf16_n16k", "gmab"),
+                         ("ccq_backward_bf16_n16k", "ccqb")):
             if fn == "bidir":
                 a = gset[0]
                 call = lambda: gma_forward(a["q"], a["k"], a["v"], a["mu"], a["log_var"], a["logit_pi"],
@@ -293,6 +295,17 @@ def main():
                 tok = g_tok
                 # read Q, K, V, dO and write dQ, dK, dV (bf16); parameters are negligible
                 byt = tok * 7 * gcfg.d * 2
+            elif fn == "ccqb":
+                from linear_attention_gmm_amd import ccq_backward, ccq_backward_workspace_bytes
+                b_ = cset[0]
+                cdo = torch.randn_like(b_["v"])
+                wsc = torch.empty(ccq_backward_workspace_bytes(ccfg.B, ccfg.H, ccfg.N, ccfg.dk, ccfg.dv),
+                                  dtype=torch.uint8, device=dev)
+                call = lambda: ccq_backward(b_["q"], b_["k"], b_["v"], b_["g"], b_["w_lambda"], b_["b_lambda"], cdo,
+                                            workspace=wsc)
+                tok = c_tok
+                # read Q, K, V, dO (bf16) and g; write dQ, dK, dV (bf16) and dg (fp32)
+                byt = tok * (7 * ccfg.dk * 2 + 8)
             else:
                 cfg = inputs.CONFIGS["gma_bf16_n128k"]
                 y = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inputs.gma_inputs(cfg).items()}

@@ -222,6 +222,36 @@ int linattn_chunk_backward(const void* q, const void* k, const void* v, const fl
                            int64_t segments, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward pass of the CCQ read: given the output gradient dout [B,H,N,dv] of
+ * ccq_forward(q, k, v, g, w_lambda, b_lambda), writes the gradients of
+ * sum(out * dout):
+ *   dq, dk [B,H,N,dk], dv [B,H,N,dv]                 (dtype, 16-byte aligned)
+ *   dg [B,H,N], dw_lambda [H,dk], db_lambda [H]       (float32, 4-byte aligned)
+ * With u the gradient of q_clean (from the backward of the decayed linear
+ * attention read with q_clean, which also gives dv, dg and the direct part of
+ * dk): dq = u - lambda Sigma u - (u . Sigma q) lambda (1 - lambda) w; the
+ * covariance adds -sum_{t>=j} (lambda_t/t) [u_t (q_t . k_j) + q_t (u_t . k_j)]
+ * plus the suffix sum of (lambda_t/t^2) [u_t (q_t . m_t) + q_t (u_t . m_t)]
+ * to dk_j (m_t the running key sum); dw, db sum -(u . Sigma q) lambda
+ * (1 - lambda) q and its scalar over the batch and the tokens. Computed in
+ * float32 with the chunk kernel (decayed and undecayed passes, some on the
+ * time-reversed sequence); bf16 gradients are rounded once.
+ * Source: "Don't Read Everything: A Curvature-Conditioned Query for Linear
+ * Attention", section 2 Method (derivation, mechanism, integration).
+ * Shapes as for ccq_forward (chunk 64, dk == dv in {32, 64, 128}); no carried
+ * state. Outputs must not overlap each other, the inputs or the workspace (of
+ * at least ccq_backward_workspace_bytes: about 18 float32 tensors of the
+ * size of q, 23 for bf16 inputs).
+ */
+size_t ccq_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                                    int64_t chunk, int dtype);
+int ccq_backward(const void* q, const void* k, const void* v, const float* g,
+                 const float* w_lambda, const float* b_lambda, const void* dout, void* dq,
+                 void* dk, void* dv, float* dg, float* dw_lambda, float* db_lambda, int64_t B,
+                 int64_t H, int64_t N, int64_t dkk, int64_t dvv, int64_t chunk, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward pass of GMA: given the output gradient dout [B,H,N,dv] of
  * gma_forward(q, k, v, mu, log_var, logit_pi, causal, eps), writes the
  * gradients of sum(out * dout):

@@ -62,6 +62,8 @@ _SIGS = {
     "linattn_backward_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
     "linattn_chunk_backward": ([_P] * 9 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "gma_backward_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
+    "ccq_backward_workspace_bytes": ([_I64] * 6 + [ctypes.c_int], ctypes.c_size_t),
+    "ccq_backward": ([_P] * 13 + [_I64] * 6 + [ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "gma_backward": ([_P] * 13 + [_I64] * 6 + [ctypes.c_int, ctypes.c_float, ctypes.c_int, _P, ctypes.c_size_t, _P],
                      ctypes.c_int),
 }
@@ -488,3 +490,28 @@ def gma_backward(q, k, v, mu, log_var, logit_pi, dout, eps: float = 1e-6, causal
                             float(eps), dt, ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
     _check("gma_backward", st)
     return dq, dk, dvt, dmu, dlv, dlp
+
+
+def ccq_backward_workspace_bytes(B, H, N, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
+    return int(lib().ccq_backward_workspace_bytes(B, H, N, dk, dv, chunk, _DT[dtype]))
+
+
+def ccq_backward(q, k, v, g, w_lambda, b_lambda, dout, chunk: int = 64, workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv, dg, dw_lambda, db_lambda) of sum(out * dout) for
+    out = ccq_forward(q, k, v, g, w_lambda, b_lambda); dq, dk, dv in the input
+    dtype, the rest float32."""
+    dt = _dtype_code(q)
+    (B, H, N, dk, dv), (pq, pk, pv, pg), _, _ = _lin_common(q, k, v, g, torch.empty_like(v))
+    pw = _dev(w_lambda, "w_lambda", torch.float32, (H, dk))
+    pb = _dev(b_lambda, "b_lambda", torch.float32, (H,))
+    pdo = _dev(dout, "dout", q.dtype, (B, H, N, dv))
+    dq, dkt, dvt = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dw, db = torch.empty_like(w_lambda), torch.empty_like(b_lambda)
+    nbytes = ccq_backward_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    st = lib().ccq_backward(pq, pk, pv, pg, pw, pb, pdo, dq.data_ptr(), dkt.data_ptr(), dvt.data_ptr(),
+                            dg.data_ptr(), dw.data_ptr(), db.data_ptr(), B, H, N, dk, dv, chunk, dt,
+                            ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
+    _check("ccq_backward", st)
+    return dq, dkt, dvt, dg, dw, db

@@ -440,6 +440,47 @@ int gma_bwd_check(const char* fn, int64_t B, int64_t H, int64_t N, int64_t d, in
   return LM_OK;
 }
 
+// ----------------------------------------------------------------------------- CCQ backward
+
+struct CcqBwdLayout {
+  size_t rows[24], cols[3], csum, part, agg, total;
+  int nrows;
+  LinLayout lin;
+  int64_t nch, clen, nblk, blen;
+};
+
+CcqBwdLayout ccq_bwd_layout(int64_t B, int64_t H, int64_t N, int64_t D, int dtype) {
+  CcqBwdLayout L;
+  L.lin = lin_layout(B, H, N, D, false, 0);
+  L.nch = N < 64 ? N : 64;
+  L.clen = (N + L.nch - 1) / L.nch;
+  L.nch = (N + L.clen - 1) / L.clen;
+  int64_t blen = (N * B * H + 1023) / 1024;
+  blen = blen < 4 ? 4 : (blen + 3) / 4 * 4;
+  L.blen = blen;
+  L.nblk = (N + blen - 1) / blen;
+  // 13 rows always, 4 input copies and dv for bf16, 5 reversal buffers
+  L.nrows = 13 + 5 + (dtype == LM_BF16 ? 5 : 0);
+  const size_t rowt = align_up((size_t)B * H * N * D * 4), colt = align_up((size_t)B * H * N * 4);
+  size_t off = 0;
+  for (int i = 0; i < L.nrows; ++i) {
+    L.rows[i] = off;
+    off += rowt;
+  }
+  for (int i = 0; i < 3; ++i) {
+    L.cols[i] = off;
+    off += colt;
+  }
+  L.csum = off;
+  off = align_up(off + (size_t)B * H * L.nch * D * 4);
+  L.part = off;
+  off = align_up(off + (size_t)H * B * L.nblk * (D + 1) * 4);
+  L.agg = off;
+  off += L.lin.total;
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -842,6 +883,108 @@ int gma_backward(const void* q, const void* k, const void* v, const float* mu, c
   La.eps = eps;
   La.bf16 = dtype == LM_BF16;
   hipError_t e = lm::gma_backward_launch(La, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+size_t ccq_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                                    int dtype) {
+  if (lin_check_shape("ccq_backward", B, H, N, dk, dv, chunk, dtype, 0) != LM_OK) return 0;
+  return ccq_bwd_layout(B, H, N, dk, dtype).total;
+}
+
+int ccq_backward(const void* q, const void* k, const void* v, const float* g, const float* w_lambda,
+                 const float* b_lambda, const void* dout, void* dq, void* dk, void* dv, float* dg, float* dw_lambda,
+                 float* db_lambda, int64_t B, int64_t H, int64_t N, int64_t dkk, int64_t dvv, int64_t chunk,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "ccq_backward";
+  int st = lin_check_shape(fn, B, H, N, dkk, dvv, chunk, dtype, 0);
+  if (st != LM_OK) return st;
+  if (!q || !k || !v || !g || !w_lambda || !b_lambda || !dout || !dq || !dk || !dv || !dg || !dw_lambda ||
+      !db_lambda || !workspace)
+    return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  const void* p16[] = {q, k, v, dout, dq, dk, dv, workspace};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return fail(LM_EINVAL, "%s: misaligned pointer (tensors need 16 bytes)", fn);
+  const void* p4[] = {g, w_lambda, b_lambda, dg, dw_lambda, db_lambda};
+  for (const void* p : p4)
+    if (!aligned(p, 4)) return fail(LM_EINVAL, "%s: misaligned float pointer", fn);
+  const CcqBwdLayout L = ccq_bwd_layout(B, H, N, dkk, dtype);
+  if (workspace_bytes < L.total)
+    return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
+  const size_t nt = (size_t)B * H * N * dkk * esize(dtype), ng = (size_t)B * H * N * 4,
+               nw = (size_t)H * dkk * 4, nb = (size_t)H * 4;
+  const void* outs[] = {dq, dk, dv, dg, dw_lambda, db_lambda};
+  const size_t nout[] = {nt, nt, nt, ng, nw, nb};
+  const void* ins[] = {q, k, v, dout, g, w_lambda, b_lambda, workspace};
+  const size_t nin[] = {nt, nt, nt, nt, ng, nw, nb, L.total};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlap(outs[i], nout[i], ins[j], nin[j]))
+        return fail(LM_EINVAL, "%s: an output overlaps an input or the workspace", fn);
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(outs[i], nout[i], outs[j], nout[j])) return fail(LM_EINVAL, "%s: outputs overlap", fn);
+  }
+  char* ws = static_cast<char*>(workspace);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  lm::CcqBwdLaunch La{};
+  lm::BwdLaunch& Bw = La.bwd;
+  Bw.fwd.agg = F(L.agg);
+  Bw.fwd.w_lambda = nullptr;
+  Bw.fwd.b_lambda = nullptr;
+  Bw.fwd.B = B;
+  Bw.fwd.H = H;
+  Bw.fwd.N = N;
+  Bw.fwd.D = dkk;
+  Bw.fwd.P = L.lin.plan.P;
+  Bw.fwd.seg_len = L.lin.plan.seg_len;
+  Bw.fwd.R = L.lin.R;
+  Bw.fwd.bf16 = false;
+  Bw.fwd.ccq = false;
+  Bw.g = g;
+  Bw.dg = dg;
+  Bw.B = B;
+  Bw.H = H;
+  Bw.N = N;
+  Bw.D = dkk;
+  Bw.bf16 = false;
+  int r = 0;
+  float** rowp[] = {&La.m, &La.mq, &La.s, &La.qc, &La.u, &La.dkg, &La.mu, &La.vr1, &La.vr2, &La.dm, &La.sdm, &La.r1,
+                    &La.r2, &Bw.rq, &Bw.rk, &Bw.rv, &Bw.rdo, &Bw.rout};
+  for (float** p : rowp) *p = F(L.rows[r++]);
+  if (dtype == LM_BF16) {
+    La.fq = F(L.rows[r++]);
+    La.fk = F(L.rows[r++]);
+    La.fv = F(L.rows[r++]);
+    La.fdo = F(L.rows[r++]);
+    La.dvg = F(L.rows[r++]);
+  }
+  La.lam = F(L.cols[0]);
+  La.ones = F(L.cols[1]);
+  Bw.rg = F(L.cols[2]);
+  La.csum = F(L.csum);
+  La.part = F(L.part);
+  La.q = q;
+  La.k = k;
+  La.v = v;
+  La.dout = dout;
+  La.w = w_lambda;
+  La.b = b_lambda;
+  La.dq = dq;
+  La.dk = dk;
+  La.dv = dv;
+  La.dw = dw_lambda;
+  La.db = db_lambda;
+  La.B = B;
+  La.H = H;
+  La.N = N;
+  La.D = dkk;
+  La.nch = L.nch;
+  La.clen = L.clen;
+  La.nblk = L.nblk;
+  La.blen = L.blen;
+  La.bf16 = dtype == LM_BF16;
+  hipError_t e = lm::ccq_backward_launch(La, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
   return ok();
 }

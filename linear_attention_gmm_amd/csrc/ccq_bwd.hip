@@ -1,0 +1,332 @@
+// ccq_bwd.hip -- backward pass of the curvature-conditioned-query read over
+// decayed linear attention ("Don't Read Everything: A Curvature-Conditioned
+// Query for Linear Attention", section 2 Method: derivation, mechanism,
+// integration; the read is trained with the rest of the layer).
+//
+// Forward (token t, count t = index + 1): m_t = sum_{j<=t} k_j,
+// Mq_t = sum_{j<=t} k_j (k_j . q_t), s_t = Sigma_t q_t = (Mq_t - m_t (m_t . q_t) / t) / t,
+// lambda_t = sigmoid(w . q_t + b), qc_t = q_t - lambda_t s_t, and
+// o = GLA(qc, k, v, g) (S_t = g_t S_{t-1} + k_t v_t^T, o_t = S_t^T qc_t).
+// With u = dL/dqc (from the backward of the decayed linear attention, which
+// also gives dv, dg and the direct part of dk):
+//   a_t   = u_t . s_t,  lambda'_t = lambda_t (1 - lambda_t)
+//   dq_t  = u_t - lambda_t Sigma_t u_t - a_t lambda'_t w
+//   dw    = -sum_t a_t lambda'_t q_t,  db = -sum_t a_t lambda'_t
+//   dk_j += -sum_{t>=j} (lambda_t / t) [u_t (q_t . k_j) + q_t (u_t . k_j)] + sum_{t>=j} dm_t,
+//   dm_t  = (lambda_t / t^2) [u_t (q_t . m_t) + q_t (u_t . m_t)]
+// (dL/dSigma_t = -lambda_t u_t q_t^T, through M_t / t and m_t m_t^T / t^2).
+// Mq and Sigma u are linear attentions without decay (key k, value k); the two
+// sums over t >= j are linear attentions on the time-reversed sequence. All of
+// them run on the float32 chunk kernel with unit gates. Everything is float32;
+// bf16 gradients are rounded once.
+#include "mfma.hpp"
+#include "launch.hpp"
+
+namespace lm {
+namespace cbwd {
+
+// Per (b, h, token range) feature sums: csum[bh][c][f] = sum_{t in range c} x[t][f].
+__global__ __launch_bounds__(128) void chunk_sum_kernel(const float* __restrict__ x, float* __restrict__ csum,
+                                                        int64_t N, int D, int64_t clen, int nch) {
+  const int c = blockIdx.x, bh = blockIdx.y, f = threadIdx.x;
+  if (f >= D) return;
+  const int64_t t0 = (int64_t)c * clen, t1 = N < t0 + clen ? N : t0 + clen;
+  const float* p = x + (size_t)bh * N * D + f;
+  float s = 0.f;
+  for (int64_t t = t0; t < t1; ++t) s += p[(size_t)t * D];
+  csum[((size_t)bh * nch + c) * D + f] = s;
+}
+
+// Inclusive prefix (rev = 0) or suffix (rev = 1) sums over tokens of x, per
+// feature: the ranges before (after) this one from csum, then a running sum.
+__global__ __launch_bounds__(128) void scan_apply_kernel(const float* __restrict__ x, const float* __restrict__ csum,
+                                                         float* __restrict__ y, int64_t N, int D, int64_t clen,
+                                                         int nch, int rev) {
+  const int c = blockIdx.x, bh = blockIdx.y, f = threadIdx.x;
+  if (f >= D) return;
+  float off = 0.f;
+  const float* cs = csum + (size_t)bh * nch * D + f;
+  if (!rev) {
+    for (int cc = 0; cc < c; ++cc) off += cs[(size_t)cc * D];
+  } else {
+    for (int cc = nch - 1; cc > c; --cc) off += cs[(size_t)cc * D];
+  }
+  const int64_t t0 = (int64_t)c * clen, t1 = N < t0 + clen ? N : t0 + clen;
+  const float* p = x + (size_t)bh * N * D + f;
+  float* o = y + (size_t)bh * N * D + f;
+  if (!rev) {
+    for (int64_t t = t0; t < t1; ++t) {
+      off += p[(size_t)t * D];
+      o[(size_t)t * D] = off;
+    }
+  } else {
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+      off += p[(size_t)t * D];
+      o[(size_t)t * D] = off;
+    }
+  }
+}
+
+// Sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wsum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Per token (one wave): lambda, s = Sigma q and q_clean.
+template <int D>
+__global__ __launch_bounds__(256) void pre_kernel(const float* __restrict__ q, const float* __restrict__ m,
+                                                  const float* __restrict__ mq, const float* __restrict__ w,
+                                                  const float* __restrict__ b, float* __restrict__ s,
+                                                  float* __restrict__ qc, float* __restrict__ lam, int64_t N, int H,
+                                                  int64_t rows) {
+  constexpr int PL = (D + 63) / 64;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave_id();
+  if (r >= rows) return;
+  const int l = lane_id();
+  const int64_t bh = r / N, tok = r - bh * N;
+  const int h = (int)(bh % H);
+  const float t = (float)(tok + 1);
+  float qv[PL], mv[PL], wv[PL];
+  float wq = 0.f, mqd = 0.f;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int f = l + 64 * i;
+    const bool ok = f < D;
+    qv[i] = ok ? q[(size_t)r * D + f] : 0.f;
+    mv[i] = ok ? m[(size_t)r * D + f] : 0.f;
+    wv[i] = ok ? w[(size_t)h * D + f] : 0.f;
+    wq += wv[i] * qv[i];
+    mqd += mv[i] * qv[i];
+  }
+  wq = wsum(wq);
+  mqd = wsum(mqd);
+  const float la = 1.f / (1.f + expf(-(wq + b[h])));
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int f = l + 64 * i;
+    if (f < D) {
+      const float sv = (mq[(size_t)r * D + f] - mv[i] * mqd / t) / t;
+      s[(size_t)r * D + f] = sv;
+      qc[(size_t)r * D + f] = qv[i] - la * sv;
+    }
+  }
+  if (l == 0) lam[r] = la;
+}
+
+// Per token (one wave, a block of four waves over `blen` tokens of one (b, h)):
+// dq, the values of the two reversed passes, dm, and this block's partial sums
+// of dw and db, part[h][b * nblk + block][0 .. D) = dw, [D] = db.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void post_kernel(const float* __restrict__ q, const float* __restrict__ m,
+                                                   const float* __restrict__ s, const float* __restrict__ u,
+                                                   const float* __restrict__ mu, const float* __restrict__ lam,
+                                                   const float* __restrict__ w, T* __restrict__ dq,
+                                                   float* __restrict__ vr1, float* __restrict__ vr2,
+                                                   float* __restrict__ dm, float* __restrict__ part, int64_t N, int B,
+                                                   int H, int64_t blen, int nblk) {
+  constexpr int PL = (D + 63) / 64;
+  __shared__ float sp[4][D + 1];
+  const int l = lane_id(), wv_ = wave_id();
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  float pw[PL], pb = 0.f, wl[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    pw[i] = 0.f;
+    const int f = l + 64 * i;
+    wl[i] = f < D ? w[(size_t)h * D + f] : 0.f;
+  }
+  const int64_t t_begin = (int64_t)blockIdx.x * blen;
+  const int64_t t_end = N < t_begin + blen ? N : t_begin + blen;
+  for (int64_t tok = t_begin + wv_; tok < t_end; tok += 4) {
+    const size_t r = (size_t)bh * N + tok;
+    const float t = (float)(tok + 1);
+    float qv[PL], mv[PL], uv[PL];
+    float a = 0.f, um = 0.f, qm = 0.f;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int f = l + 64 * i;
+      const bool ok = f < D;
+      qv[i] = ok ? q[r * D + f] : 0.f;
+      mv[i] = ok ? m[r * D + f] : 0.f;
+      uv[i] = ok ? u[r * D + f] : 0.f;
+      const float sv = ok ? s[r * D + f] : 0.f;
+      a += uv[i] * sv;
+      um += uv[i] * mv[i];
+      qm += qv[i] * mv[i];
+    }
+    a = wsum(a);
+    um = wsum(um);
+    qm = wsum(qm);
+    const float la = lam[r];
+    const float lp = la * (1.f - la);
+    const float c1 = la / t;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int f = l + 64 * i;
+      if (f < D) {
+        const float su = (mu[r * D + f] - mv[i] * um / t) / t;  // Sigma u
+        dq[r * D + f] = from_f32<T>(uv[i] - la * su - a * lp * wl[i]);
+        vr1[r * D + f] = c1 * uv[i];
+        vr2[r * D + f] = c1 * qv[i];
+        dm[r * D + f] = c1 / t * (uv[i] * qm + qv[i] * um);
+      }
+      pw[i] -= a * lp * qv[i];
+    }
+    pb -= a * lp;
+  }
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int f = l + 64 * i;
+    if (f < D) sp[wv_][f] = pw[i];
+  }
+  if (l == 0) sp[wv_][D] = pb;
+  __syncthreads();
+  float* dst = part + ((size_t)h * B * nblk + (size_t)b * nblk + blockIdx.x) * (D + 1);
+  for (int f = threadIdx.x; f <= D; f += 256) dst[f] = sp[0][f] + sp[1][f] + sp[2][f] + sp[3][f];
+}
+
+// dk = (direct part) - R1 - R2 + suffix(dm); R1 and R2 come time-reversed.
+template <typename T>
+__global__ __launch_bounds__(256) void dk_kernel(const float* __restrict__ dkg, const float* __restrict__ r1,
+                                                 const float* __restrict__ r2, const float* __restrict__ sdm,
+                                                 T* __restrict__ dk, int64_t N, int D, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t row = i / D;
+  const int f = (int)(i - row * D);
+  const int64_t bh = row / N, t = row - bh * N;
+  const size_t rr = ((size_t)bh * N + (N - 1 - t)) * D + f;
+  dk[i] = from_f32<T>(dkg[i] - r1[rr] - r2[rr] + sdm[i]);
+}
+
+// dw, db per head: the block partials summed over (b, block) in a fixed order.
+__global__ __launch_bounds__(256) void param_kernel(const float* __restrict__ part, float* __restrict__ dw,
+                                                    float* __restrict__ db, int D, int nslot) {
+  const int h = blockIdx.x;
+  for (int f = threadIdx.x; f <= D; f += 256) {
+    float s = 0.f;
+    for (int sl = 0; sl < nslot; ++sl) s += part[((size_t)h * nslot + sl) * (D + 1) + f];
+    if (f < D)
+      dw[(size_t)h * D + f] = s;
+    else
+      db[h] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, float x, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = x;
+}
+
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void cvt_kernel(const TI* __restrict__ in, TO* __restrict__ out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = from_f32<TO>(to_f32(in[i]));
+}
+
+static unsigned nblocks(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+// Causal linear attention without decay on float32 rows: out = LA(q, k, v).
+static hipError_t la(const CcqBwdLaunch& L, const float* q, const float* k, const float* v, float* out,
+                     hipStream_t st) {
+  LinLaunch F = L.bwd.fwd;
+  F.q = q;
+  F.k = k;
+  F.v = v;
+  F.g = L.ones;
+  F.out = out;
+  F.bf16 = false;
+  F.ccq = false;
+  F.state_in = nullptr;
+  F.state_out = nullptr;
+  F.t_in = 0;
+  return linattn_launch(F, st);
+}
+
+static hipError_t scan(const CcqBwdLaunch& L, const float* x, float* y, int rev, hipStream_t st) {
+  const dim3 grid((unsigned)L.nch, (unsigned)(L.B * L.H));
+  hipLaunchKernelGGL(chunk_sum_kernel, grid, dim3(128), 0, st, x, L.csum, L.N, (int)L.D, L.clen, (int)L.nch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_apply_kernel, grid, dim3(128), 0, st, x, L.csum, y, L.N, (int)L.D, L.clen, (int)L.nch, rev);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
+  const int64_t BH = L.B * L.H, rows = BH * L.N, n = rows * D;
+  const int H = (int)L.H;
+  hipError_t e;
+  const float *fq, *fk, *fv, *fdo;
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n)), dim3(256), 0, st, static_cast<const T*>(L.q), L.fq, n);
+    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n)), dim3(256), 0, st, static_cast<const T*>(L.k), L.fk, n);
+    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n)), dim3(256), 0, st, static_cast<const T*>(L.v), L.fv, n);
+    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n)), dim3(256), 0, st, static_cast<const T*>(L.dout),
+                       L.fdo, n);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    fq = L.fq;
+    fk = L.fk;
+    fv = L.fv;
+    fdo = L.fdo;
+  } else {
+    fq = static_cast<const float*>(L.q);
+    fk = static_cast<const float*>(L.k);
+    fv = static_cast<const float*>(L.v);
+    fdo = static_cast<const float*>(L.dout);
+  }
+  hipLaunchKernelGGL(fill_kernel, dim3(nblocks(rows)), dim3(256), 0, st, L.ones, 1.f, rows);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // forward quantities: m = prefix sum of k, Mq, then lambda, s = Sigma q, q_clean
+  if ((e = scan(L, fk, L.m, 0, st)) != hipSuccess) return e;
+  if ((e = la(L, fq, fk, fk, L.mq, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((pre_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, fq, L.m, L.mq, L.w, L.b,
+                     L.s, L.qc, L.lam, L.N, H, rows);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // backward of the decayed linear attention read with q_clean: u = dq_clean,
+  // the direct part of dk, dv and dg
+  float* dvg = sizeof(T) == 2 ? L.dvg : static_cast<float*>(L.dv);
+  if ((e = linattn_backward_f32(L.bwd, L.qc, fk, fv, fdo, L.u, L.dkg, dvg, true, st)) != hipSuccess) return e;
+  // Sigma u needs M u
+  if ((e = la(L, L.u, fk, fk, L.mu, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((post_kernel<T, D>), dim3((unsigned)L.nblk, (unsigned)BH), dim3(256), 0, st, fq, L.m, L.s, L.u,
+                     L.mu, L.lam, L.w, static_cast<T*>(L.dq), L.vr1, L.vr2, L.dm, L.part, L.N, (int)L.B, H, L.blen,
+                     (int)L.nblk);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // sum_{t>=j} (lambda_t/t) u_t (q_t . k_j) and (lambda_t/t) q_t (u_t . k_j): causal
+  // passes over the reversed sequence (query rev k, keys rev q / rev u)
+  if ((e = reverse_rows_f32(fk, L.bwd.rk, BH, L.N, D, st)) != hipSuccess) return e;
+  if ((e = reverse_rows_f32(fq, L.bwd.rq, BH, L.N, D, st)) != hipSuccess) return e;
+  if ((e = reverse_rows_f32(L.u, L.bwd.rv, BH, L.N, D, st)) != hipSuccess) return e;
+  if ((e = reverse_rows_f32(L.vr1, L.bwd.rdo, BH, L.N, D, st)) != hipSuccess) return e;
+  if ((e = reverse_rows_f32(L.vr2, L.bwd.rout, BH, L.N, D, st)) != hipSuccess) return e;
+  if ((e = la(L, L.bwd.rk, L.bwd.rq, L.bwd.rdo, L.r1, st)) != hipSuccess) return e;
+  if ((e = la(L, L.bwd.rk, L.bwd.rv, L.bwd.rout, L.r2, st)) != hipSuccess) return e;
+  if ((e = scan(L, L.dm, L.sdm, 1, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((dk_kernel<T>), dim3(nblocks(n)), dim3(256), 0, st, L.dkg, L.r1, L.r2, L.sdm,
+                     static_cast<T*>(L.dk), L.N, D, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((cvt_kernel<float, T>), dim3(nblocks(n)), dim3(256), 0, st, L.dvg, static_cast<T*>(L.dv), n);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(param_kernel, dim3((unsigned)H), dim3(256), 0, st, L.part, L.dw, L.db, D,
+                     (int)(L.B * L.nblk));
+  return hipGetLastError();
+}
+
+}  // namespace cbwd
+
+hipError_t ccq_backward_launch(const CcqBwdLaunch& L, hipStream_t st) {
+  using namespace cbwd;
+  switch (L.D) {
+    case 32: return L.bf16 ? run<bf16, 32>(L, st) : run<float, 32>(L, st);
+    case 64: return L.bf16 ? run<bf16, 64>(L, st) : run<float, 64>(L, st);
+    case 128: return L.bf16 ? run<bf16, 128>(L, st) : run<float, 128>(L, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lm

@@ -129,6 +129,40 @@ hipError_t linattn_backward_launch(const BwdLaunch& L, hipStream_t st);
 hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float* k, const float* v,
                                 const float* dout, float* dq, float* dk, float* dv, bool gates, hipStream_t st);
 
+// Time reversal of float32 rows: out[bh][t] = in[bh][N - 1 - t] (D floats per row).
+hipError_t reverse_rows_f32(const float* in, float* out, int64_t BH, int64_t N, int64_t D, hipStream_t st);
+
+// Backward pass of the CCQ read (ccq_bwd.hip): the float32 backward of the
+// decayed linear attention read with q_clean, no-decay passes for M q and M u,
+// two passes on the reversed sequence for the covariance term of dk, scans of
+// the key sum.
+struct CcqBwdLaunch {
+  BwdLaunch bwd;  // inner backward (float32, real gates, dg = the output dg); its
+                  // plan, segment workspace and reversal buffers also serve the
+                  // no-decay passes
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* w;  // [H][D]
+  const float* b;  // [H]
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dw;
+  float* db;
+  // workspace (float32 rows [B*H][N][D]): copies of q, k, v, dout (bf16 inputs),
+  // m, M q, Sigma q, q_clean, u = dq_clean, the direct dk, dv (bf16), M u, the
+  // values of the reversed passes, dm, its suffix sums, the two reversed sums;
+  // [B*H][N]: lambda, unit gates; scan range sums [B*H][nch][D]; dw/db partials
+  // [H][B*nblk][D + 1]
+  float *fq, *fk, *fv, *fdo, *m, *mq, *s, *qc, *u, *dkg, *dvg, *mu, *vr1, *vr2, *dm, *sdm, *r1, *r2;
+  float *lam, *ones, *csum, *part;
+  int64_t B, H, N, D, nch, clen, nblk, blen;
+  bool bf16;
+};
+hipError_t ccq_backward_launch(const CcqBwdLaunch& L, hipStream_t st);
+
 // Backward pass of GMA (gma_bwd.hip): the float32 backward of the linear
 // attention with responsibilities as features and [v | 1] as values (over 2N
 // rows for the bidirectional form), then the chain rule through the softmax and

@@ -182,6 +182,14 @@ hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float*
   return gates ? gate_grad_f32(L, q, dq, k, dk, st) : hipSuccess;
 }
 
+hipError_t reverse_rows_f32(const float* in, float* out, int64_t BH, int64_t N, int64_t D, hipStream_t st) {
+  const int row_bytes = (int)(D * 4);
+  const int64_t total16 = BH * N * (row_bytes / 16);
+  hipLaunchKernelGGL(bwd::reverse_time, dim3((unsigned)((total16 + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const char*>(in), reinterpret_cast<char*>(out), N, row_bytes, total16);
+  return hipGetLastError();
+}
+
 hipError_t linattn_backward_launch(const BwdLaunch& L, hipStream_t st) {
   using namespace bwd;
   if (!L.bf16)

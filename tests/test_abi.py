@@ -306,3 +306,29 @@ def test_gma_backward_errors():
     assert call(d=128) == binding.LM_EUNSUPPORTED
     assert call(K=200) == binding.LM_EUNSUPPORTED
     assert L.lm_last_error().decode()
+
+
+@needs_lib
+def test_ccq_backward_errors():
+    L = binding.lib()
+    (q, k, v, g, w, b, do, dq, dk, dv, dg, dw, db, ws) = (FAKE + (i << 30) for i in range(14))
+    bf = binding.LM_BF16
+    wsb = L.ccq_backward_workspace_bytes(1, 2, 100, 64, 64, 64, bf)
+    assert wsb > L.linattn_backward_workspace_bytes(1, 2, 100, 64, 64, 64, bf, 0)
+    assert L.ccq_backward_workspace_bytes(1, 2, 100, 48, 48, 64, bf) == 0
+    assert L.ccq_backward_workspace_bytes(1, 2, 100, 64, 64, 32, bf) == 0
+
+    def call(**kw):
+        a = dict(dq=dq, dg=dg, db=db, d=64, chunk=64, wsb=wsb)
+        a.update(kw)
+        return L.ccq_backward(q, k, v, g, w, b, do, a["dq"], dk, dv, a["dg"], dw, a["db"], 1, 2, 100, a["d"],
+                              a["d"], a["chunk"], bf, ws, a["wsb"], None)
+
+    assert call(wsb=wsb - 1) == binding.LM_EWORKSPACE
+    assert call(dq=dk) == binding.LM_EINVAL  # two outputs in one buffer
+    assert call(dq=q + 64) == binding.LM_EINVAL  # output overlaps an input
+    assert call(db=db + 2) == binding.LM_EINVAL  # misaligned
+    assert call(dg=None) == binding.LM_EINVAL
+    assert call(d=48) == binding.LM_EUNSUPPORTED
+    assert call(chunk=32) == binding.LM_EUNSUPPORTED
+    assert L.lm_last_error().decode()
