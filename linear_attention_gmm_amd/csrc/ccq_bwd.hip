@@ -220,10 +220,14 @@ __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, float 
   if (i < n) p[i] = x;
 }
 
+// Element-wise conversion, four elements per thread (n a multiple of 4: rows
+// of 32, 64 or 128 entries).
 template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void cvt_kernel(const TI* __restrict__ in, TO* __restrict__ out, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) out[i] = from_f32<TO>(to_f32(in[i]));
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[i + j] = from_f32<TO>(to_f32(in[i + j]));
 }
 
 static unsigned nblocks(int64_t n) { return (unsigned)((n + 255) / 256); }
@@ -261,10 +265,10 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   hipError_t e;
   const float *fq, *fk, *fv, *fdo;
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n)), dim3(256), 0, st, static_cast<const T*>(L.q), L.fq, n);
-    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n)), dim3(256), 0, st, static_cast<const T*>(L.k), L.fk, n);
-    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n)), dim3(256), 0, st, static_cast<const T*>(L.v), L.fv, n);
-    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n)), dim3(256), 0, st, static_cast<const T*>(L.dout),
+    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.q), L.fq, n);
+    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.k), L.fk, n);
+    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.v), L.fv, n);
+    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.dout),
                        L.fdo, n);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     fq = L.fq;
@@ -309,7 +313,7 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
                      static_cast<T*>(L.dk), L.N, D, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((cvt_kernel<float, T>), dim3(nblocks(n)), dim3(256), 0, st, L.dvg, static_cast<T*>(L.dv), n);
+    hipLaunchKernelGGL((cvt_kernel<float, T>), dim3(nblocks(n / 4)), dim3(256), 0, st, L.dvg, static_cast<T*>(L.dv), n);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(param_kernel, dim3((unsigned)H), dim3(256), 0, st, L.part, L.dw, L.db, D,
