@@ -124,7 +124,8 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
-              "(every (b, h) slice is independent; see DESIGN.md on sharding). Use --gpus 1.", file=sys.stderr)
+              "(every (b, h) slice is independent, so data or head parallelism would need no exchange). "
+              "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
