@@ -98,3 +98,14 @@ def test_ccq_backward_workload_shape_sampled():
     cfg = inputs.CONFIGS["ccq_bf16_n16k"]
     got, ref = _case(cfg, N=2048, heads=[9])
     _check(got, ref, "bf16", "bf16 CCQ workload shape N=2048, head 9")
+
+
+def test_ccq_backward_deterministic():
+    # fixed-order reductions: two calls give bit-identical gradients
+    cfg = inputs.CONFIGS["ccq_bf16_lowrank"].replace(name="ccq_bwd_det", cfg_id=805, B=2, H=2, N=777)
+    x = cuda(inputs.linattn_inputs(cfg, ccq=True))
+    do = torch.randn_like(x["v"])
+    a = binding.ccq_backward(x["q"], x["k"], x["v"], x["g"], x["w_lambda"], x["b_lambda"], do)
+    b = binding.ccq_backward(x["q"], x["k"], x["v"], x["g"], x["w_lambda"], x["b_lambda"], do)
+    for name, u, w in zip(NAMES, a, b):
+        assert torch.equal(u, w), name

@@ -104,3 +104,14 @@ def test_gma_backward_bidirectional_bf16():
     got, ref = _case(cfg, causal=False)
     for name, a, r in zip(NAMES, got, ref):
         assert_close(a, r, "bf16", "%s bf16 bidirectional N=300" % name)
+
+
+def test_gma_backward_deterministic():
+    # fixed-order reductions: two calls give bit-identical gradients
+    cfg = inputs.CONFIGS["gma_bf16_n4k"].replace(name="gma_bwd_det", cfg_id=707, B=2, H=2, N=777)
+    x = cuda(inputs.gma_inputs(cfg))
+    do = torch.randn_like(x["v"])
+    a = binding.gma_backward(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"], do)
+    b = binding.gma_backward(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"], do)
+    for name, u, w in zip(NAMES, a, b):
+        assert torch.equal(u, w), name
