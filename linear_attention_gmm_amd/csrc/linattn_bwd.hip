@@ -15,9 +15,10 @@
 // exp(L_i - L_j), L the cumulative log gate; the derivative with respect to L_m
 // is q_m . dq_m - k_m . dk_m, and L_m sums the log gates up to m).
 // The kernels below reverse sequences in time, shift the gates and form dg.
-// For bf16 inputs every pass runs in float32 on float32 copies and the
-// gradients are rounded once at the end: dg is a difference of two dot products
-// that nearly cancel, which bf16-rounded dq and dk would not resolve.
+// For bf16 inputs the dq and dk passes run in float32 on float32 copies and
+// those gradients are rounded once at the end: dg is a difference of two dot
+// products that nearly cancel, which bf16-rounded dq and dk would not resolve.
+// The dv pass, which dg does not use, runs on the bf16 inputs directly.
 #include "mfma.hpp"
 #include "launch.hpp"
 
@@ -126,22 +127,30 @@ static hipError_t gate_grad_f32(const BwdLaunch& L, const float* q, const float*
   return hipGetLastError();
 }
 
-static hipError_t reverse(const void* in, void* out, const BwdLaunch& L, hipStream_t st) {
-  const int row_bytes = (int)(L.D * 4);
+static hipError_t reverse(const void* in, void* out, const BwdLaunch& L, hipStream_t st, int elem_bytes = 4) {
+  const int row_bytes = (int)(L.D * elem_bytes);
   const int64_t total16 = L.B * L.H * L.N * (row_bytes / 16);
   hipLaunchKernelGGL(reverse_time, dim3((unsigned)((total16 + 255) / 256)), dim3(256), 0, st,
                      static_cast<const char*>(in), static_cast<char*>(out), L.N, row_bytes, total16);
   return hipGetLastError();
 }
 
-}  // namespace bwd
+// bf16 operands of the dv pass (for bf16 inputs): the time-reversed bf16 k, q
+// and dout, a reversed output buffer, and dv itself.
+struct DvBf16 {
+  const bf16* rk;
+  const bf16* rq;
+  const bf16* rdo;
+  bf16* rout;
+  bf16* dv;
+};
 
-// The whole backward in float32: three chunk-kernel passes (dq; dk and dv on
-// the reversed sequence), the reversals around them and (gates) the gate
-// gradient.
-hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float* k, const float* v,
-                                const float* dout, float* dq, float* dk, float* dv, bool gates, hipStream_t st) {
-  using namespace bwd;
+// Three chunk-kernel passes (dq; dk and dv on the reversed sequence), the
+// reversals around them and (gates) the gate gradient, in float32. With h,
+// the dv pass runs on the bf16 chunk kernel instead: dv does not enter the
+// gate gradient, whose q . dq - k . dk cancellation is what needs float32.
+static hipError_t backward(const BwdLaunch& L, const float* q, const float* k, const float* v, const float* dout,
+                           float* dq, float* dk, float* dv, bool gates, const DvBf16* h, hipStream_t st) {
   hipError_t e;
   LinLaunch F = L.fwd;  // shapes, segment plan, workspace; pointers set per pass
   F.bf16 = false;
@@ -158,7 +167,7 @@ hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float*
   if ((e = linattn_launch(F, st)) != hipSuccess) return e;
   // reversed inputs and shifted gates
   if ((e = reverse(q, L.rq, L, st)) != hipSuccess) return e;
-  if ((e = reverse(k, L.rk, L, st)) != hipSuccess) return e;
+  if (!h && (e = reverse(k, L.rk, L, st)) != hipSuccess) return e;
   if ((e = reverse(v, L.rv, L, st)) != hipSuccess) return e;
   if ((e = reverse(dout, L.rdo, L, st)) != hipSuccess) return e;
   const int64_t tot = L.B * L.H * L.N;
@@ -173,13 +182,30 @@ hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float*
   if ((e = linattn_launch(F, st)) != hipSuccess) return e;
   if ((e = reverse(L.rout, dk, L, st)) != hipSuccess) return e;
   // dv (reversed) = forward(q = rev k, k = rev q, v = rev do, shifted gates)
-  F.q = L.rk;
-  F.k = L.rq;
-  F.v = L.rdo;
-  F.out = L.rout;
-  if ((e = linattn_launch(F, st)) != hipSuccess) return e;
-  if ((e = reverse(L.rout, dv, L, st)) != hipSuccess) return e;
+  if (h) {
+    F.bf16 = true;
+    F.q = h->rk;
+    F.k = h->rq;
+    F.v = h->rdo;
+    F.out = h->rout;
+    if ((e = linattn_launch(F, st)) != hipSuccess) return e;
+    if ((e = reverse(h->rout, h->dv, L, st, 2)) != hipSuccess) return e;
+  } else {
+    F.q = L.rk;
+    F.k = L.rq;
+    F.v = L.rdo;
+    F.out = L.rout;
+    if ((e = linattn_launch(F, st)) != hipSuccess) return e;
+    if ((e = reverse(L.rout, dv, L, st)) != hipSuccess) return e;
+  }
   return gates ? gate_grad_f32(L, q, dq, k, dk, st) : hipSuccess;
+}
+
+}  // namespace bwd
+
+hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float* k, const float* v,
+                                const float* dout, float* dq, float* dk, float* dv, bool gates, hipStream_t st) {
+  return bwd::backward(L, q, k, v, dout, dq, dk, dv, gates, nullptr, st);
 }
 
 hipError_t reverse_rows_f32(const float* in, float* out, int64_t BH, int64_t N, int64_t D, hipStream_t st) {
@@ -201,11 +227,18 @@ hipError_t linattn_backward_launch(const BwdLaunch& L, hipStream_t st) {
   if ((e = convert_n<bf16, float>(L.k, L.uk, n, st)) != hipSuccess) return e;
   if ((e = convert_n<bf16, float>(L.v, L.uv, n, st)) != hipSuccess) return e;
   if ((e = convert_n<bf16, float>(L.dout, L.udo, n, st)) != hipSuccess) return e;
-  if ((e = linattn_backward_f32(L, L.uq, L.uk, L.uv, L.udo, L.udq, L.udk, L.udv, true, st)) != hipSuccess)
-    return e;
+  // the dv pass on bf16 operands: the reversed bf16 k and q share the float32
+  // slot that would hold the reversed float32 k, the reversed bf16 dout and its
+  // output share the slot of the float32 dv (neither is used on this path)
+  bf16* rk16 = reinterpret_cast<bf16*>(L.rk);
+  bf16* rdo16 = reinterpret_cast<bf16*>(L.udv);
+  const DvBf16 h{rk16, rk16 + n, rdo16, rdo16 + n, static_cast<bf16*>(L.dv)};
+  if ((e = reverse(L.k, rk16, L, st, 2)) != hipSuccess) return e;
+  if ((e = reverse(L.q, rk16 + n, L, st, 2)) != hipSuccess) return e;
+  if ((e = reverse(L.dout, rdo16, L, st, 2)) != hipSuccess) return e;
+  if ((e = backward(L, L.uq, L.uk, L.uv, L.udo, L.udq, L.udk, nullptr, true, &h, st)) != hipSuccess) return e;
   if ((e = convert_n<float, bf16>(L.udq, L.dq, n, st)) != hipSuccess) return e;
-  if ((e = convert_n<float, bf16>(L.udk, L.dk, n, st)) != hipSuccess) return e;
-  return convert_n<float, bf16>(L.udv, L.dv, n, st);
+  return convert_n<float, bf16>(L.udk, L.dk, n, st);
 }
 
 }  // namespace lm
