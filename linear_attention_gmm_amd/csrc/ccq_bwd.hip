@@ -17,10 +17,12 @@
 // (dL/dSigma_t = -lambda_t u_t q_t^T, through M_t / t and m_t m_t^T / t^2).
 // Mq and Sigma u are linear attentions without decay (key k, value k); the two
 // sums over t >= j are linear attentions on the time-reversed sequence. All of
-// them run on the float32 chunk kernel with unit gates. Everything is float32;
-// bf16 gradients are rounded once.
+// them run on the float32 chunk kernel with unit gates. Everything is float32
+// and bf16 gradients are rounded once, except the dv pass for bf16 inputs,
+// which runs on the bf16 chunk kernel (dv does not enter any other gradient).
 #include "mfma.hpp"
 #include "launch.hpp"
+#include "bwd.hpp"
 
 namespace lm {
 namespace cbwd {
@@ -291,8 +293,22 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // backward of the decayed linear attention read with q_clean: u = dq_clean,
   // the direct part of dk, dv and dg
-  float* dvg = sizeof(T) == 2 ? L.dvg : static_cast<float*>(L.dv);
-  if ((e = linattn_backward_f32(L.bwd, L.qc, fk, fv, fdo, L.u, L.dkg, dvg, true, st)) != hipSuccess) return e;
+  if constexpr (sizeof(T) == 2) {
+    // dv (which dg does not use) on bf16 operands: reversed k, q_clean and
+    // dout in the slots of the float32 dv and of the inner reversed k
+    bf16* a16 = reinterpret_cast<bf16*>(L.dvg);
+    bf16* b16 = reinterpret_cast<bf16*>(L.bwd.rk);
+    if ((e = reverse_to_bf16<bf16>(static_cast<const bf16*>(L.k), a16, BH, L.N, D, st)) != hipSuccess) return e;
+    if ((e = reverse_to_bf16<float>(L.qc, a16 + n, BH, L.N, D, st)) != hipSuccess) return e;
+    if ((e = reverse_to_bf16<bf16>(static_cast<const bf16*>(L.dout), b16, BH, L.N, D, st)) != hipSuccess) return e;
+    if ((e = linattn_backward_mixed(L.bwd, L.qc, fk, fv, fdo, L.u, L.dkg, true, a16, a16 + n, b16, b16 + n,
+                                    static_cast<bf16*>(L.dv), st)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = linattn_backward_f32(L.bwd, L.qc, fk, fv, fdo, L.u, L.dkg, static_cast<float*>(L.dv), true, st)) !=
+        hipSuccess)
+      return e;
+  }
   // Sigma u needs M u
   if ((e = la(L, L.u, fk, fk, L.mu, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((post_kernel<T, D>), dim3((unsigned)L.nblk, (unsigned)BH), dim3(256), 0, st, fq, L.m, L.s, L.u,
@@ -312,10 +328,6 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   hipLaunchKernelGGL((dk_kernel<T>), dim3(nblocks(n)), dim3(256), 0, st, L.dkg, L.r1, L.r2, L.sdm,
                      static_cast<T*>(L.dk), L.N, D, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((cvt_kernel<float, T>), dim3(nblocks(n / 4)), dim3(256), 0, st, L.dvg, static_cast<T*>(L.dv), n);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   hipLaunchKernelGGL(param_kernel, dim3((unsigned)H), dim3(256), 0, st, L.part, L.dw, L.db, D,
                      (int)(L.B * L.nblk));
   return hipGetLastError();

@@ -20,7 +20,8 @@
 //   dlog var_kd = sum_tokens dl_k (-1/2 + 1/2 (x_d - mu_kd)^2 / var_kd)
 //   dlogit pi_k = G_k - pi_k sum_k' G_k',  G_k = sum_tokens dl_k
 // with the parameter sums running over the query and the key tokens of every
-// batch entry. Everything is float32; the inputs and dq, dk, dv are in the
+// batch entry. Everything is float32 (for bf16 inputs the value gradient's
+// pass runs on the bf16 chunk kernel); the inputs and dq, dk, dv are in the
 // input dtype. The constant -d/2 log 2 pi of the log density cancels in the
 // softmax and is left out.
 //
@@ -37,6 +38,7 @@
 // take_dv.
 #include "mfma.hpp"
 #include "launch.hpp"
+#include "bwd.hpp"
 
 namespace lm {
 namespace gbwd {
@@ -394,15 +396,15 @@ __global__ __launch_bounds__(kThr) void params_kernel(const float* __restrict__ 
 }
 
 // dv = the first DV columns of the inner value gradient, in the input dtype.
-template <typename T>
-__global__ __launch_bounds__(256) void take_dv_kernel(const float* __restrict__ dvx, T* __restrict__ dv, int64_t N,
+template <typename T, typename TI>
+__global__ __launch_bounds__(256) void take_dv_kernel(const TI* __restrict__ dvx, T* __restrict__ dv, int64_t N,
                                                       int64_t NN, int64_t rows, int DV, int DL) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= rows * DV) return;
   const int64_t r = i / DV;  // bh * N + t
   const int c = (int)(i - r * DV);
   const int64_t bh = r / N;
-  dv[i] = from_f32<T>(dvx[((size_t)bh * NN + (r - bh * N)) * DL + c]);
+  dv[i] = from_f32<T>(to_f32(dvx[((size_t)bh * NN + (r - bh * N)) * DL + c]));
 }
 
 static hipError_t fill_rows(float* p, const GmaBwdLaunch& L, int64_t r0, int64_t nr, int DL, float x,
@@ -455,7 +457,24 @@ static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
   // gradients of the inner linear attention: features (dgq, dgk) and values
   BwdLaunch Bw = L.bwd;
   Bw.g = L.ones;
-  if ((e = linattn_backward_f32(Bw, L.gq, L.gk, L.vx, L.dy, L.dgq, L.dgk, L.dvx, false, st)) != hipSuccess) return e;
+  bf16* dv16 = reinterpret_cast<bf16*>(L.dvx);
+  if constexpr (sizeof(T) == 2) {
+    // the value gradient (which nothing else uses) on bf16 operands: reversed
+    // responsibilities of k and q and output gradient, in the slots of the
+    // (now dead) inner output and of the inner reversed k
+    const int64_t ni = BH * NN * DL;
+    bf16* a16 = reinterpret_cast<bf16*>(L.y);
+    bf16* b16 = reinterpret_cast<bf16*>(Bw.rk);
+    if ((e = reverse_to_bf16<float>(L.gk, a16, BH, NN, DL, st)) != hipSuccess) return e;
+    if ((e = reverse_to_bf16<float>(L.gq, a16 + ni, BH, NN, DL, st)) != hipSuccess) return e;
+    if ((e = reverse_to_bf16<float>(L.dy, b16, BH, NN, DL, st)) != hipSuccess) return e;
+    if ((e = linattn_backward_mixed(Bw, L.gq, L.gk, L.vx, L.dy, L.dgq, L.dgk, false, a16, a16 + ni, b16, b16 + ni,
+                                    dv16, st)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = linattn_backward_f32(Bw, L.gq, L.gk, L.vx, L.dy, L.dgq, L.dgk, L.dvx, false, st)) != hipSuccess)
+      return e;
+  }
   hipLaunchKernelGGL((chain_kernel<T, D>), grid, dim3(kThr), 0, st, static_cast<const T*>(L.q),
                      static_cast<const T*>(L.k), L.gq, L.gk, L.dgq, L.dgk, L.mu, L.iv, static_cast<T*>(L.dq),
                      static_cast<T*>(L.dk), L.part, N, NN, qoff, (int)L.B, H, K, DL, L.seg_len, (int)L.nseg);
@@ -468,8 +487,12 @@ static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
   hipLaunchKernelGGL(params_kernel, dim3((unsigned)H), dim3(kThr), 0, st, L.sums, L.iv, L.logit_pi, L.dmu,
                      L.dlog_var, L.dlogit_pi, K, D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((take_dv_kernel<T>), dim3((unsigned)((rows * D + 255) / 256)), dim3(256), 0, st, L.dvx,
-                     static_cast<T*>(L.dv), N, NN, rows, D, DL);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((take_dv_kernel<T, bf16>), dim3((unsigned)((rows * D + 255) / 256)), dim3(256), 0, st, dv16,
+                       static_cast<T*>(L.dv), N, NN, rows, D, DL);
+  else
+    hipLaunchKernelGGL((take_dv_kernel<T, float>), dim3((unsigned)((rows * D + 255) / 256)), dim3(256), 0, st,
+                       L.dvx, static_cast<T*>(L.dv), N, NN, rows, D, DL);
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@
 // The dv pass, which dg does not use, runs on the bf16 inputs directly.
 #include "mfma.hpp"
 #include "launch.hpp"
+#include "bwd.hpp"
 
 namespace lm {
 namespace bwd {
@@ -207,6 +208,36 @@ hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float*
                                 const float* dout, float* dq, float* dk, float* dv, bool gates, hipStream_t st) {
   return bwd::backward(L, q, k, v, dout, dq, dk, dv, gates, nullptr, st);
 }
+
+hipError_t linattn_backward_mixed(const BwdLaunch& L, const float* q, const float* k, const float* v,
+                                  const float* dout, float* dq, float* dk, bool gates, const bf16* rk16,
+                                  const bf16* rq16, const bf16* rdo16, bf16* rout16, bf16* dv16, hipStream_t st) {
+  const bwd::DvBf16 h{rk16, rq16, rdo16, rout16, dv16};
+  return bwd::backward(L, q, k, v, dout, dq, dk, nullptr, gates, &h, st);
+}
+
+namespace bwd {
+template <typename TI>
+__global__ __launch_bounds__(256) void reverse_to_bf16_kernel(const TI* __restrict__ in, bf16* __restrict__ out,
+                                                              int64_t N, int D, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t row = i / D;  // bh * N + t
+  const int c = (int)(i - row * D);
+  const int64_t bh = row / N, t = row - bh * N;
+  out[i] = from_f32<bf16>(to_f32(in[(bh * N + (N - 1 - t)) * D + c]));
+}
+}  // namespace bwd
+
+template <typename TI>
+hipError_t reverse_to_bf16(const TI* in, bf16* out, int64_t BH, int64_t N, int64_t D, hipStream_t st) {
+  const int64_t total = BH * N * D;
+  hipLaunchKernelGGL((bwd::reverse_to_bf16_kernel<TI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, in,
+                     out, N, (int)D, total);
+  return hipGetLastError();
+}
+template hipError_t reverse_to_bf16<float>(const float*, bf16*, int64_t, int64_t, int64_t, hipStream_t);
+template hipError_t reverse_to_bf16<bf16>(const bf16*, bf16*, int64_t, int64_t, int64_t, hipStream_t);
 
 hipError_t reverse_rows_f32(const float* in, float* out, int64_t BH, int64_t N, int64_t D, hipStream_t st) {
   const int row_bytes = (int)(D * 4);
