@@ -101,6 +101,14 @@ def test_gma_bf16_n16k_sampled():
     assert_close(got, ref, "bf16", "gma bf16 N=16384 causal, slices (0,0),(3,7)")
 
 
+def test_gma_bf16_n16k_bidir_sampled():
+    # the 16K-token GMA workload read bidirectionally, in the launch the bench
+    # times, checked on two slices
+    cfg = inputs.CONFIGS["gma_bf16_n16k"]
+    got, ref = _run(cfg, causal=False, sl=[(1, 2), (2, 5)])
+    assert_close(got, ref, "bf16", "gma bf16 N=16384 bidirectional, slices (1,2),(2,5)")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_gma_bf16_d128_k256_ragged(causal):
     # the long-context shape (d = dv = 128, 256 components, mixture keys) at a
