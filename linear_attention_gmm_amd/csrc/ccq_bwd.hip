@@ -17,9 +17,11 @@
 // (dL/dSigma_t = -lambda_t u_t q_t^T, through M_t / t and m_t m_t^T / t^2).
 // Mq and Sigma u are linear attentions without decay (key k, value k); the two
 // sums over t >= j are linear attentions on the time-reversed sequence. All of
-// them run on the float32 chunk kernel with unit gates. Everything is float32
-// and bf16 gradients are rounded once, except the dv pass for bf16 inputs,
-// which runs on the bf16 chunk kernel (dv does not enter any other gradient).
+// them run on the chunk kernel with unit gates. Everything is float32 and bf16
+// gradients are rounded once, except for bf16 inputs: there the undecayed
+// passes and the dv pass run on the bf16 chunk kernel (their results enter the
+// gradients as perturbations of the size of the bf16 rounding; the gradients
+// of the decayed read, whose gate gradient cancels, stay in float32).
 #include "mfma.hpp"
 #include "launch.hpp"
 #include "bwd.hpp"
@@ -77,9 +79,9 @@ __device__ __forceinline__ float wsum(float x) {
 }
 
 // Per token (one wave): lambda, s = Sigma q and q_clean.
-template <int D>
+template <int D, typename TM>
 __global__ __launch_bounds__(256) void pre_kernel(const float* __restrict__ q, const float* __restrict__ m,
-                                                  const float* __restrict__ mq, const float* __restrict__ w,
+                                                  const TM* __restrict__ mq, const float* __restrict__ w,
                                                   const float* __restrict__ b, float* __restrict__ s,
                                                   float* __restrict__ qc, float* __restrict__ lam, int64_t N, int H,
                                                   int64_t rows) {
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(256) void pre_kernel(const float* __restrict__ q, c
   for (int i = 0; i < PL; ++i) {
     const int f = l + 64 * i;
     if (f < D) {
-      const float sv = (mq[(size_t)r * D + f] - mv[i] * mqd / t) / t;
+      const float sv = (to_f32(mq[(size_t)r * D + f]) - mv[i] * mqd / t) / t;
       s[(size_t)r * D + f] = sv;
       qc[(size_t)r * D + f] = qv[i] - la * sv;
     }
@@ -119,13 +121,16 @@ __global__ __launch_bounds__(256) void pre_kernel(const float* __restrict__ q, c
 
 // Per token (one wave, a block of four waves over `blen` tokens of one (b, h)):
 // dq, the values of the two reversed passes, dm, and this block's partial sums
-// of dw and db, part[h][b * nblk + block][0 .. D) = dw, [D] = db.
+// of dw and db, part[h][b * nblk + block][0 .. D) = dw, [D] = db. float32
+// inputs: M u and the values in float32, in time order. bf16 inputs: M u in
+// bf16, and the values and u written in bf16 at the time-reversed positions
+// (the operands of the reversed passes; ru receives u).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void post_kernel(const float* __restrict__ q, const float* __restrict__ m,
                                                    const float* __restrict__ s, const float* __restrict__ u,
-                                                   const float* __restrict__ mu, const float* __restrict__ lam,
+                                                   const T* __restrict__ mu, const float* __restrict__ lam,
                                                    const float* __restrict__ w, T* __restrict__ dq,
-                                                   float* __restrict__ vr1, float* __restrict__ vr2,
+                                                   T* __restrict__ vr1, T* __restrict__ vr2, T* __restrict__ ru,
                                                    float* __restrict__ dm, float* __restrict__ part, int64_t N, int B,
                                                    int H, int64_t blen, int nblk) {
   constexpr int PL = (D + 63) / 64;
@@ -168,10 +173,17 @@ __global__ __launch_bounds__(256) void post_kernel(const float* __restrict__ q, 
     for (int i = 0; i < PL; ++i) {
       const int f = l + 64 * i;
       if (f < D) {
-        const float su = (mu[r * D + f] - mv[i] * um / t) / t;  // Sigma u
+        const float su = (to_f32(mu[r * D + f]) - mv[i] * um / t) / t;  // Sigma u
         dq[r * D + f] = from_f32<T>(uv[i] - la * su - a * lp * wl[i]);
-        vr1[r * D + f] = c1 * uv[i];
-        vr2[r * D + f] = c1 * qv[i];
+        if constexpr (sizeof(T) == 2) {
+          const size_t rr = ((size_t)bh * N + (N - 1 - tok)) * D + f;
+          vr1[rr] = from_f32<T>(c1 * uv[i]);
+          vr2[rr] = from_f32<T>(c1 * qv[i]);
+          ru[rr] = from_f32<T>(uv[i]);
+        } else {
+          vr1[r * D + f] = c1 * uv[i];
+          vr2[r * D + f] = c1 * qv[i];
+        }
         dm[r * D + f] = c1 / t * (uv[i] * qm + qv[i] * um);
       }
       pw[i] -= a * lp * qv[i];
@@ -191,8 +203,8 @@ __global__ __launch_bounds__(256) void post_kernel(const float* __restrict__ q, 
 
 // dk = (direct part) - R1 - R2 + suffix(dm); R1 and R2 come time-reversed.
 template <typename T>
-__global__ __launch_bounds__(256) void dk_kernel(const float* __restrict__ dkg, const float* __restrict__ r1,
-                                                 const float* __restrict__ r2, const float* __restrict__ sdm,
+__global__ __launch_bounds__(256) void dk_kernel(const float* __restrict__ dkg, const T* __restrict__ r1,
+                                                 const T* __restrict__ r2, const float* __restrict__ sdm,
                                                  T* __restrict__ dk, int64_t N, int D, int64_t total) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
@@ -200,7 +212,7 @@ __global__ __launch_bounds__(256) void dk_kernel(const float* __restrict__ dkg, 
   const int f = (int)(i - row * D);
   const int64_t bh = row / N, t = row - bh * N;
   const size_t rr = ((size_t)bh * N + (N - 1 - t)) * D + f;
-  dk[i] = from_f32<T>(dkg[i] - r1[rr] - r2[rr] + sdm[i]);
+  dk[i] = from_f32<T>(dkg[i] - to_f32(r1[rr]) - to_f32(r2[rr]) + sdm[i]);
 }
 
 // dw, db per head: the block partials summed over (b, block) in a fixed order.
@@ -234,16 +246,17 @@ __global__ __launch_bounds__(256) void cvt_kernel(const TI* __restrict__ in, TO*
 
 static unsigned nblocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 
-// Causal linear attention without decay on float32 rows: out = LA(q, k, v).
-static hipError_t la(const CcqBwdLaunch& L, const float* q, const float* k, const float* v, float* out,
-                     hipStream_t st) {
+// Causal linear attention without decay: out = LA(q, k, v), on the float32 or
+// the bf16 chunk kernel.
+template <typename T>
+static hipError_t la(const CcqBwdLaunch& L, const T* q, const T* k, const T* v, T* out, hipStream_t st) {
   LinLaunch F = L.bwd.fwd;
   F.q = q;
   F.k = k;
   F.v = v;
   F.g = L.ones;
   F.out = out;
-  F.bf16 = false;
+  F.bf16 = sizeof(T) == 2;
   F.ccq = false;
   F.state_in = nullptr;
   F.state_out = nullptr;
@@ -285,11 +298,22 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   }
   hipLaunchKernelGGL(fill_kernel, dim3(nblocks(rows)), dim3(256), 0, st, L.ones, 1.f, rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // forward quantities: m = prefix sum of k, Mq, then lambda, s = Sigma q, q_clean
+  // forward quantities: m = prefix sum of k, Mq, then lambda, s = Sigma q, q_clean.
+  // For bf16 inputs the undecayed passes (M q, M u and the two reversed ones)
+  // run on the bf16 chunk kernel: their results enter q_clean, dq and dk as
+  // perturbations of the size of the bf16 rounding, while the gradients of the
+  // decayed read (with the gate gradient's cancellation) stay in float32.
   if ((e = scan(L, fk, L.m, 0, st)) != hipSuccess) return e;
-  if ((e = la(L, fq, fk, fk, L.mq, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((pre_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, fq, L.m, L.mq, L.w, L.b,
-                     L.s, L.qc, L.lam, L.N, H, rows);
+  T* mq16 = reinterpret_cast<T*>(L.mq);  // the M q result in the input dtype
+  if constexpr (sizeof(T) == 2) {
+    if ((e = la<T>(L, static_cast<const T*>(L.q), static_cast<const T*>(L.k), static_cast<const T*>(L.k), mq16,
+                   st)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = la<float>(L, fq, fk, fk, L.mq, st)) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((pre_kernel<D, T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, fq, L.m, mq16, L.w,
+                     L.b, L.s, L.qc, L.lam, L.N, H, rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // backward of the decayed linear attention read with q_clean: u = dq_clean,
   // the direct part of dk, dv and dg
@@ -309,23 +333,46 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
         hipSuccess)
       return e;
   }
-  // Sigma u needs M u
-  if ((e = la(L, L.u, fk, fk, L.mu, st)) != hipSuccess) return e;
+  // Sigma u needs M u; then dq, the values of the reversed passes, dm, dw/db
+  T* mu16 = reinterpret_cast<T*>(L.mu);
+  T* vr1 = reinterpret_cast<T*>(L.vr1);
+  T* vr2 = reinterpret_cast<T*>(L.vr2);
+  T* ru16 = sizeof(T) == 2 ? reinterpret_cast<T*>(L.vr1) + n : nullptr;  // bf16: second half of the vr1 slot
+  if constexpr (sizeof(T) == 2) {
+    T* u16 = mu16 + n;  // second half of the M u slot
+    hipLaunchKernelGGL((cvt_kernel<float, T>), dim3(nblocks(n / 4)), dim3(256), 0, st, L.u, u16, n);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = la<T>(L, u16, static_cast<const T*>(L.k), static_cast<const T*>(L.k), mu16, st)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = la<float>(L, L.u, fk, fk, L.mu, st)) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((post_kernel<T, D>), dim3((unsigned)L.nblk, (unsigned)BH), dim3(256), 0, st, fq, L.m, L.s, L.u,
-                     L.mu, L.lam, L.w, static_cast<T*>(L.dq), L.vr1, L.vr2, L.dm, L.part, L.N, (int)L.B, H, L.blen,
+                     mu16, L.lam, L.w, static_cast<T*>(L.dq), vr1, vr2, ru16, L.dm, L.part, L.N, (int)L.B, H, L.blen,
                      (int)L.nblk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // sum_{t>=j} (lambda_t/t) u_t (q_t . k_j) and (lambda_t/t) q_t (u_t . k_j): causal
   // passes over the reversed sequence (query rev k, keys rev q / rev u)
-  if ((e = reverse_rows_f32(fk, L.bwd.rk, BH, L.N, D, st)) != hipSuccess) return e;
-  if ((e = reverse_rows_f32(fq, L.bwd.rq, BH, L.N, D, st)) != hipSuccess) return e;
-  if ((e = reverse_rows_f32(L.u, L.bwd.rv, BH, L.N, D, st)) != hipSuccess) return e;
-  if ((e = reverse_rows_f32(L.vr1, L.bwd.rdo, BH, L.N, D, st)) != hipSuccess) return e;
-  if ((e = reverse_rows_f32(L.vr2, L.bwd.rout, BH, L.N, D, st)) != hipSuccess) return e;
-  if ((e = la(L, L.bwd.rk, L.bwd.rq, L.bwd.rdo, L.r1, st)) != hipSuccess) return e;
-  if ((e = la(L, L.bwd.rk, L.bwd.rv, L.bwd.rout, L.r2, st)) != hipSuccess) return e;
+  T* r1 = reinterpret_cast<T*>(L.r1);
+  T* r2 = reinterpret_cast<T*>(L.r2);
+  if constexpr (sizeof(T) == 2) {
+    T* rk16 = reinterpret_cast<T*>(L.bwd.rk);
+    T* rq16 = rk16 + n;
+    if ((e = reverse_to_bf16<bf16>(static_cast<const bf16*>(L.k), rk16, BH, L.N, D, st)) != hipSuccess) return e;
+    if ((e = reverse_to_bf16<bf16>(static_cast<const bf16*>(L.q), rq16, BH, L.N, D, st)) != hipSuccess) return e;
+    if ((e = la<T>(L, rk16, rq16, vr1, r1, st)) != hipSuccess) return e;
+    if ((e = la<T>(L, rk16, ru16, vr2, r2, st)) != hipSuccess) return e;
+  } else {
+    if ((e = reverse_rows_f32(fk, L.bwd.rk, BH, L.N, D, st)) != hipSuccess) return e;
+    if ((e = reverse_rows_f32(fq, L.bwd.rq, BH, L.N, D, st)) != hipSuccess) return e;
+    if ((e = reverse_rows_f32(L.u, L.bwd.rv, BH, L.N, D, st)) != hipSuccess) return e;
+    if ((e = reverse_rows_f32(L.vr1, L.bwd.rdo, BH, L.N, D, st)) != hipSuccess) return e;
+    if ((e = reverse_rows_f32(L.vr2, L.bwd.rout, BH, L.N, D, st)) != hipSuccess) return e;
+    if ((e = la<float>(L, L.bwd.rk, L.bwd.rq, L.bwd.rdo, L.r1, st)) != hipSuccess) return e;
+    if ((e = la<float>(L, L.bwd.rk, L.bwd.rv, L.bwd.rout, L.r2, st)) != hipSuccess) return e;
+  }
   if ((e = scan(L, L.dm, L.sdm, 1, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((dk_kernel<T>), dim3(nblocks(n)), dim3(256), 0, st, L.dkg, L.r1, L.r2, L.sdm,
+  hipLaunchKernelGGL((dk_kernel<T>), dim3(nblocks(n)), dim3(256), 0, st, L.dkg, r1, r2, L.sdm,
                      static_cast<T*>(L.dk), L.N, D, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(param_kernel, dim3((unsigned)H), dim3(256), 0, st, L.part, L.dw, L.db, D,
