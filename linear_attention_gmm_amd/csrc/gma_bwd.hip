@@ -234,42 +234,73 @@ __global__ __launch_bounds__(256) void out_grad_kernel(const float* __restrict__
 // (blockIdx.z = 0: queries, 1: keys) of one (b, h), over a range of `len`
 // tokens. Writes dx in the input dtype, and this range's parameter partial sums
 //   part[h][slot][k] = [sum dl (x - mu) (D) | sum dl (x - mu)^2 (D) | sum dl]
-// with slot = (side * B + b) * nseg + blockIdx.x. Thread = component for the
-// partial sums; thread = (feature, token group) for dx.
+// with slot = (side * B + b) * nseg + blockIdx.x. kCT = 256 threads: for the
+// partial sums thread (half hh, component c) owns features [hh D/2, (hh+1) D/2)
+// of component c (half the accumulators per thread, two waves per SIMD); for
+// dx thread = (feature, token group).
+constexpr int kCT = 2 * kThr;
+
+__device__ __forceinline__ void block_sum16_4(float (&x)[kTT], float* red) {
+#pragma unroll
+  for (int t = 0; t < kTT; ++t) {
+    float s = x[t];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    x[t] = s;
+  }
+  if (lane_id() == 0) {
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) red[wave_id() * kTT + t] = x[t];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < kTT; ++t) x[t] = (red[t] + red[kTT + t]) + (red[2 * kTT + t] + red[3 * kTT + t]);
+  __syncthreads();
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(kThr) void chain_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                     const float* __restrict__ gq, const float* __restrict__ gk,
-                                                     const float* __restrict__ dgq, const float* __restrict__ dgk,
-                                                     const float* __restrict__ mu, const float* __restrict__ iv,
-                                                     T* __restrict__ dq, T* __restrict__ dk, float* __restrict__ part,
-                                                     int64_t N, int64_t NN, int64_t qoff, int B, int H, int K, int DL,
-                                                     int64_t len, int nseg) {
+__global__ __launch_bounds__(kCT) void chain_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                    const float* __restrict__ gq, const float* __restrict__ gk,
+                                                    const float* __restrict__ dgq, const float* __restrict__ dgk,
+                                                    const float* __restrict__ mu, const float* __restrict__ iv,
+                                                    T* __restrict__ dq, T* __restrict__ dk, float* __restrict__ part,
+                                                    int64_t N, int64_t NN, int64_t qoff, int B, int H, int K, int DL,
+                                                    int64_t len, int nseg) {
+  constexpr int DH = D / 2;  // features per thread in the partial sums
   __shared__ float sx[kTT][D];
   __shared__ float sdl[kTT][kThr];
-  __shared__ float red[2 * kTT];
+  __shared__ float red[4 * kTT];
   __shared__ float smu[kThr][D + 1];
   __shared__ float siv[kThr][D + 1];
-  const int bh = blockIdx.y, b = bh / H, h = bh % H, c = threadIdx.x, side = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int c = tid % kThr, hh = tid / kThr;  // component, feature half
+  const int bh = blockIdx.y, b = bh / H, h = bh % H, side = blockIdx.z;
   const T* __restrict__ x = (side == 0 ? q : k) + (size_t)bh * N * D;
   T* __restrict__ dx = (side == 0 ? dq : dk) + (size_t)bh * N * D;
   const size_t row0 = (size_t)bh * NN + (side == 0 ? qoff : 0);  // inner row of this side's token 0
   const float* __restrict__ gx = (side == 0 ? gq : gk) + row0 * DL;
   const float* __restrict__ dgx = (side == 0 ? dgq : dgk) + row0 * DL;
-  load_tables<D>(smu, siv, mu, iv, h, K);
-  // dx mapping: feature fd = c % D, tokens t = c / D + j * (kThr / D)
-  constexpr int TG = kThr / D;      // token groups
-  constexpr int TPT = kTT / TG;     // tokens per thread
-  const int fd = c % D, tg = c / D;
+  for (int i = tid; i < kThr * D; i += kCT) {
+    const int rr = i / D, cc = i - rr * D;
+    const bool ok = rr < K;
+    smu[rr][cc] = ok ? mu[((size_t)h * K + rr) * D + cc] : 0.f;
+    siv[rr][cc] = ok ? iv[((size_t)h * K + rr) * D + cc] : 0.f;
+  }
+  // dx mapping: feature fd = tid % D, tokens t = tid / D + j * (kCT / D)
+  constexpr int TG = kCT / D;   // token groups
+  constexpr int TPT = kTT / TG; // tokens per thread
+  const int fd = tid % D, tg = tid / D;
+  const int d0 = hh * DH;
 
-  float p1[D], p2[D], p0 = 0.f;
+  float p1[DH], p2[DH], p0 = 0.f;
 #pragma unroll
-  for (int i = 0; i < D; ++i) p1[i] = p2[i] = 0.f;
+  for (int i = 0; i < DH; ++i) p1[i] = p2[i] = 0.f;
 
   const int64_t t_begin = (int64_t)blockIdx.x * len;
   const int64_t t_end = N < t_begin + len ? N : t_begin + len;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT) {
     const int nv = (int)(t_end - t0 < kTT ? t_end - t0 : kTT);
-    for (int i = c; i < kTT * D; i += kThr) {
+    for (int i = tid; i < kTT * D; i += kCT) {
       const int t = i / D, dd = i - t * D;
       sx[t][dd] = t < nv ? to_f32(x[(size_t)(t0 + t) * D + dd]) : 0.f;
     }
@@ -279,26 +310,29 @@ __global__ __launch_bounds__(kThr) void chain_kernel(const T* __restrict__ q, co
       const bool ok = c < K && t < nv;
       ga[t] = ok ? gx[(size_t)(t0 + t) * DL + c] : 0.f;
       dga[t] = ok ? dgx[(size_t)(t0 + t) * DL + c] : 0.f;
-      r[t] = ga[t] * dga[t];
+      r[t] = hh == 0 ? ga[t] * dga[t] : 0.f;  // each component counted once
     }
-    block_sum16(r, red);  // also orders the sx writes before the reads below
+    block_sum16_4(r, red);  // also orders the sx writes (and the tables) before the reads below
     float dl[kTT];
 #pragma unroll
     for (int t = 0; t < kTT; ++t) {
       dl[t] = ga[t] * (dga[t] - r[t]);
-      sdl[t][c] = dl[t];
       p0 += dl[t];
+    }
+    if (hh == 0) {
+#pragma unroll
+      for (int t = 0; t < kTT; ++t) sdl[t][c] = dl[t];
     }
     if (c < K) {
 #pragma unroll
-      for (int dd = 0; dd < D; ++dd) {
-        const float m = smu[c][dd];
+      for (int i = 0; i < DH; ++i) {
+        const float m = smu[c][d0 + i];
 #pragma unroll
         for (int t = 0; t < kTT; ++t) {
-          const float e = sx[t][dd] - m;
+          const float e = sx[t][d0 + i] - m;
           const float a = dl[t] * e;
-          p1[dd] += a;
-          p2[dd] += a * e;
+          p1[i] += a;
+          p2[i] += a * e;
         }
       }
     }
@@ -328,11 +362,11 @@ __global__ __launch_bounds__(kThr) void chain_kernel(const T* __restrict__ q, co
     const int slot = (side * B + b) * nseg + (int)blockIdx.x;
     float* dst = part + (((size_t)h * 2 * B * nseg + slot) * K + c) * (2 * D + 1);
 #pragma unroll
-    for (int dd = 0; dd < D; ++dd) {
-      dst[dd] = p1[dd];
-      dst[D + dd] = p2[dd];
+    for (int i = 0; i < DH; ++i) {
+      dst[d0 + i] = p1[i];
+      dst[D + d0 + i] = p2[i];
     }
-    dst[2 * D] = p0;
+    if (hh == 0) dst[2 * D] = p0;
   }
 }
 
@@ -475,7 +509,7 @@ static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
     if ((e = linattn_backward_f32(Bw, L.gq, L.gk, L.vx, L.dy, L.dgq, L.dgk, L.dvx, false, st)) != hipSuccess)
       return e;
   }
-  hipLaunchKernelGGL((chain_kernel<T, D>), grid, dim3(kThr), 0, st, static_cast<const T*>(L.q),
+  hipLaunchKernelGGL((chain_kernel<T, D>), grid, dim3(kCT), 0, st, static_cast<const T*>(L.q),
                      static_cast<const T*>(L.k), L.gq, L.gk, L.dgq, L.dgk, L.mu, L.iv, static_cast<T*>(L.dq),
                      static_cast<T*>(L.dk), L.part, N, NN, qoff, (int)L.B, H, K, DL, L.seg_len, (int)L.nseg);
   if ((e = hipGetLastError()) != hipSuccess) return e;
