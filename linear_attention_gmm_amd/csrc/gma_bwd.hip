@@ -142,10 +142,17 @@ __global__ __launch_bounds__(kThr) void route_kernel(const T* __restrict__ q, co
   const int bh = blockIdx.y, h = bh % H, c = threadIdx.x;
   const T* __restrict__ x = (blockIdx.z == 0 ? q : k) + (size_t)bh * N * D;
   float* __restrict__ out = blockIdx.z == 0 ? gq + ((size_t)bh * NN + qoff) * DL : gk + (size_t)bh * NN * DL;
-  // this thread's component row of mu and 1/var, read through the cache (small
-  // LDS keeps many workgroups per CU, which measured faster than LDS tables)
-  const float* __restrict__ muk = mu + ((size_t)h * K + (c < K ? c : 0)) * D;
-  const float* __restrict__ ivk = iv + ((size_t)h * K + (c < K ? c : 0)) * D;
+  // this thread's component row of mu and 1/var, in registers
+  float muk[D], ivk[D];
+  {
+    const float* __restrict__ mr = mu + ((size_t)h * K + (c < K ? c : 0)) * D;
+    const float* __restrict__ ir = iv + ((size_t)h * K + (c < K ? c : 0)) * D;
+#pragma unroll
+    for (int dd = 0; dd < D; ++dd) {
+      muk[dd] = mr[dd];
+      ivk[dd] = ir[dd];
+    }
+  }
   const float ck = c < K ? cst[(size_t)h * K + c] : 0.f;
   const int64_t t_begin = (int64_t)blockIdx.x * len;
   const int64_t t_end = N < t_begin + len ? N : t_begin + len;
@@ -160,6 +167,7 @@ __global__ __launch_bounds__(kThr) void route_kernel(const T* __restrict__ q, co
 #pragma unroll
     for (int t = 0; t < kTT; ++t) acc[t] = 0.f;
     if (c < K) {
+#pragma unroll
       for (int dd = 0; dd < D; ++dd) {
         const float m = muk[dd], w = ivk[dd];
 #pragma unroll
