@@ -217,23 +217,32 @@ hipError_t linattn_backward_mixed(const BwdLaunch& L, const float* q, const floa
 }
 
 namespace bwd {
-template <typename TI>
-__global__ __launch_bounds__(256) void reverse_to_bf16_kernel(const TI* __restrict__ in, bf16* __restrict__ out,
-                                                              int64_t N, int D, int64_t total) {
+// float32 rows to reversed bf16 rows, four entries per thread (D a multiple of 4).
+__global__ __launch_bounds__(256) void reverse_to_bf16_kernel(const float* __restrict__ in, bf16* __restrict__ out,
+                                                              int64_t N, int D4, int64_t total4) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const int64_t row = i / D;  // bh * N + t
-  const int c = (int)(i - row * D);
+  if (i >= total4) return;
+  const int64_t row = i / D4;  // bh * N + t
+  const int c = (int)(i - row * D4);
   const int64_t bh = row / N, t = row - bh * N;
-  out[i] = from_f32<bf16>(to_f32(in[(bh * N + (N - 1 - t)) * D + c]));
+  const f32x4 v = *reinterpret_cast<const f32x4*>(in + ((bh * N + (N - 1 - t)) * D4 + c) * 4);
+  *reinterpret_cast<bf16x4*>(out + i * 4) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
 }
 }  // namespace bwd
 
 template <typename TI>
 hipError_t reverse_to_bf16(const TI* in, bf16* out, int64_t BH, int64_t N, int64_t D, hipStream_t st) {
-  const int64_t total = BH * N * D;
-  hipLaunchKernelGGL((bwd::reverse_to_bf16_kernel<TI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, in,
-                     out, N, (int)D, total);
+  if constexpr (sizeof(TI) == 2) {
+    // a plain reversal: 16-byte pieces of the rows
+    const int row_bytes = (int)(D * 2);
+    const int64_t total16 = BH * N * (row_bytes / 16);
+    hipLaunchKernelGGL(bwd::reverse_time, dim3((unsigned)((total16 + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<const char*>(in), reinterpret_cast<char*>(out), N, row_bytes, total16);
+  } else {
+    const int64_t total4 = BH * N * (D / 4);
+    hipLaunchKernelGGL(bwd::reverse_to_bf16_kernel, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0, st, in, out,
+                       N, (int)(D / 4), total4);
+  }
   return hipGetLastError();
 }
 template hipError_t reverse_to_bf16<float>(const float*, bf16*, int64_t, int64_t, int64_t, hipStream_t);
