@@ -48,6 +48,13 @@
  *                         "Don't Read Everything", section 2 Method ->
  *                         integration (the covariance statistics ride on the
  *                         same recurrence).
+ * Backward passes (training): the gradients of sum(out * dout) for a given
+ * output gradient dout, for the forwards without a carried state:
+ *  linattn_chunk_backward dq, dk, dv, dg of decayed linear attention.
+ *  gma_backward           dq, dk, dv, dmu, dlog_var, dlogit_pi of GMA (causal
+ *                         and bidirectional).
+ *  ccq_backward           dq, dk, dv, dg, dw_lambda, db_lambda of the CCQ read.
+ *                         Each with a *_workspace_bytes function.
  * State layouts (float32, dense, one block per (b, h), blocks in b-major order):
  *    GMA   [Vtil (K x dv) | Z (K)]            K*dv + K floats:
  *          Vtil = sum_j gamma(k_j) v_j^T, Z = sum_j gamma(k_j)
@@ -95,7 +102,7 @@
 extern "C" {
 #endif
 
-#define LM_ABI_VERSION 2
+#define LM_ABI_VERSION 3
 
 typedef enum {
   LM_OK = 0,
