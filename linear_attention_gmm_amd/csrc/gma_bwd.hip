@@ -1,8 +1,8 @@
-// gma_bwd.hip -- backward pass of causal Gaussian Mixture Attention ("Gaussian
-// Mixture Attention: Linear-Time Sequence Mixing via Probabilistic Latent
-// Routing", method: core mechanism, latent memory routing, variants and
-// training: the mixer is trained end to end, the variances through softplus and
-// the priors through a softmax).
+// gma_bwd.hip -- backward pass of Gaussian Mixture Attention, causal and
+// bidirectional ("Gaussian Mixture Attention: Linear-Time Sequence Mixing via
+// Probabilistic Latent Routing", method: core mechanism, latent memory routing,
+// variants and training: the mixer is trained end to end, the variances
+// through softplus and the priors through a softmax).
 //
 // The causal output is a linear attention whose features are the
 // responsibilities: with A_ij = gamma(q_i) . gamma(k_j),
@@ -33,8 +33,8 @@
 // Kernels: prep (per head: 1/var and the constant part of the log joint),
 // route (responsibilities, one thread per component, 16 tokens per step),
 // pack (values [v | 1 | 0], unit gates), out_grad (dN, dD from the forward),
-// chain (softmax and log-joint chain rule per token, parameter partial sums
-// per token range), reduce (fixed-order sum of the partials), params,
+// chain (softmax and log-joint chain rule per token, two threads per
+// component; parameter partial sums per token range), reduce (fixed-order sum of the partials), params,
 // take_dv.
 #include "mfma.hpp"
 #include "launch.hpp"
