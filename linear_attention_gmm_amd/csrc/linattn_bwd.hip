@@ -51,11 +51,14 @@ __global__ __launch_bounds__(256) void shift_gates(const float* __restrict__ g, 
 }
 
 // x_m = q_m . dq_m - k_m . dk_m for every token (float32), one wave per token:
-// lanes over the features, a wave sum. Written into dg.
+// lanes over the features, a wave sum. Written into dg. With dq16 / dk16 the
+// gradients are also written rounded to bf16 (the final outputs for bf16
+// inputs, saving a separate conversion pass over dq and dk).
 template <int D>
 __global__ __launch_bounds__(256) void gate_dots(const float* __restrict__ q, const float* __restrict__ dq,
                                                  const float* __restrict__ k, const float* __restrict__ dk,
-                                                 float* __restrict__ x, int64_t rows) {
+                                                 float* __restrict__ x, int64_t rows, bf16* __restrict__ dq16,
+                                                 bf16* __restrict__ dk16) {
   const int l = lane_id();
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave_id()) * 16;
   for (int rr = 0; rr < 16; ++rr) {
@@ -65,7 +68,12 @@ __global__ __launch_bounds__(256) void gate_dots(const float* __restrict__ q, co
 #pragma unroll
     for (int i = l; i < D; i += 64) {
       const size_t o = (size_t)row * D + i;
-      s += q[o] * dq[o] - k[o] * dk[o];
+      const float a = dq[o], b = dk[o];
+      s += q[o] * a - k[o] * b;
+      if (dq16) {
+        dq16[o] = from_f32<bf16>(a);
+        dk16[o] = from_f32<bf16>(b);
+      }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
@@ -111,10 +119,11 @@ static hipError_t convert_n(const void* in, void* out, int64_t n, hipStream_t st
 }
 
 static hipError_t gate_grad_f32(const BwdLaunch& L, const float* q, const float* dq, const float* k, const float* dk,
-                                hipStream_t st) {
+                                hipStream_t st, bf16* dq16 = nullptr, bf16* dk16 = nullptr) {
   const int64_t rows = L.B * L.H * L.N;
   const unsigned nb = (unsigned)((rows + 63) / 64);
-#define LM_GD(DD) hipLaunchKernelGGL((gate_dots<DD>), dim3(nb), dim3(256), 0, st, q, dq, k, dk, L.dg, rows)
+#define LM_GD(DD) \
+  hipLaunchKernelGGL((gate_dots<DD>), dim3(nb), dim3(256), 0, st, q, dq, k, dk, L.dg, rows, dq16, dk16)
   switch (L.D) {
     case 32: LM_GD(32); break;
     case 64: LM_GD(64); break;
@@ -144,6 +153,8 @@ struct DvBf16 {
   const bf16* rdo;
   bf16* rout;
   bf16* dv;
+  bf16* dq16;  // optional: dq and dk rounded to bf16 by the gate-gradient pass
+  bf16* dk16;
 };
 
 // Three chunk-kernel passes (dq; dk and dv on the reversed sequence), the
@@ -199,7 +210,7 @@ static hipError_t backward(const BwdLaunch& L, const float* q, const float* k, c
     if ((e = linattn_launch(F, st)) != hipSuccess) return e;
     if ((e = reverse(L.rout, dv, L, st)) != hipSuccess) return e;
   }
-  return gates ? gate_grad_f32(L, q, dq, k, dk, st) : hipSuccess;
+  return gates ? gate_grad_f32(L, q, dq, k, dk, st, h ? h->dq16 : nullptr, h ? h->dk16 : nullptr) : hipSuccess;
 }
 
 }  // namespace bwd
@@ -212,7 +223,7 @@ hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float*
 hipError_t linattn_backward_mixed(const BwdLaunch& L, const float* q, const float* k, const float* v,
                                   const float* dout, float* dq, float* dk, bool gates, const bf16* rk16,
                                   const bf16* rq16, const bf16* rdo16, bf16* rout16, bf16* dv16, hipStream_t st) {
-  const bwd::DvBf16 h{rk16, rq16, rdo16, rout16, dv16};
+  const bwd::DvBf16 h{rk16, rq16, rdo16, rout16, dv16, nullptr, nullptr};
   return bwd::backward(L, q, k, v, dout, dq, dk, nullptr, gates, &h, st);
 }
 
@@ -272,13 +283,13 @@ hipError_t linattn_backward_launch(const BwdLaunch& L, hipStream_t st) {
   // output share the slot of the float32 dv (neither is used on this path)
   bf16* rk16 = reinterpret_cast<bf16*>(L.rk);
   bf16* rdo16 = reinterpret_cast<bf16*>(L.udv);
-  const DvBf16 h{rk16, rk16 + n, rdo16, rdo16 + n, static_cast<bf16*>(L.dv)};
+  const DvBf16 h{rk16, rk16 + n, rdo16, rdo16 + n, static_cast<bf16*>(L.dv), static_cast<bf16*>(L.dq),
+                 static_cast<bf16*>(L.dk)};
   if ((e = reverse(L.k, rk16, L, st, 2)) != hipSuccess) return e;
   if ((e = reverse(L.q, rk16 + n, L, st, 2)) != hipSuccess) return e;
   if ((e = reverse(L.dout, rdo16, L, st, 2)) != hipSuccess) return e;
-  if ((e = backward(L, L.uq, L.uk, L.uv, L.udo, L.udq, L.udk, nullptr, true, &h, st)) != hipSuccess) return e;
-  if ((e = convert_n<float, bf16>(L.udq, L.dq, n, st)) != hipSuccess) return e;
-  return convert_n<float, bf16>(L.udk, L.dk, n, st);
+  // dq, dk in bf16 come from the gate-gradient pass
+  return backward(L, L.uq, L.uk, L.uv, L.udo, L.udq, L.udk, nullptr, true, &h, st);
 }
 
 }  // namespace lm
