@@ -116,16 +116,35 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ agg, floa
   }
   const size_t pitch = (size_t)K * DV + K;
   float run = 0.f;
+  // the loads of a batch of segments are issued together, then combined in order
+  constexpr int kBatch = 8;
   if (causal) {
     if (init && comp < K) run = init[(size_t)bh * pitch + pub];
-    for (int p = 0; p < P; ++p) {
-      const float t = (p < P - 1 || fin) ? x[p * stride] : 0.f;
-      x[p * stride] = run;
-      run += t;
+    for (int p0 = 0; p0 < P; p0 += kBatch) {
+      float t[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int p = p0 + i;
+        t[i] = p < P && (p < P - 1 || fin) ? x[p * stride] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (p0 + i < P) {
+          x[(p0 + i) * stride] = run;
+          run += t[i];
+        }
+      }
     }
     if (fin && comp < K) fin[(size_t)bh * pitch + pub] = run;
   } else {
-    for (int p = 0; p < P; ++p) run += x[p * stride];
+    for (int p0 = 0; p0 < P; p0 += kBatch) {
+      float t[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) t[i] = p0 + i < P ? x[(p0 + i) * stride] : 0.f;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (p0 + i < P) run += t[i];
+    }
     x[0] = run;
   }
 }
