@@ -100,13 +100,13 @@ int gma_kp(int64_t K, int64_t d, int dtype) {
 }
 
 struct GmaLayout {
-  size_t W, c, agg, aggz, total;
+  size_t W, c, agg, aggz, gk, total;  // gk == 0: no key-responsibility buffer
   Plan plan;
   int64_t KP;
 };
 
 GmaLayout gma_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int dtype,
-                     int64_t segments) {
+                     int64_t segments, int causal) {
   GmaLayout L;
   L.KP = gma_kp(K, d, dtype);
   L.plan = plan_segments(B * H, N, segments, gma_fast(d, K, dtype) ? kTargetGroupsGma : kTargetGroups);
@@ -119,6 +119,13 @@ GmaLayout gma_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int6
   off = align_up(off + (size_t)B * H * L.plan.P * L.KP * dv * 4);
   L.aggz = off;
   off = align_up(off + (size_t)B * H * L.plan.P * L.KP * 4);
+  // causal bf16 kernel over several segments: the segment pass stores each
+  // chunk's key responsibilities (64 x KP bf16) for the causal pass
+  L.gk = 0;
+  if (causal && gma_fast(d, K, dtype) && L.plan.P > 1) {
+    L.gk = off;
+    off = align_up(off + (size_t)B * H * ((N + kChunk - 1) / kChunk) * kChunk * L.KP * 2);
+  }
   L.total = off;
   return L;
 }
@@ -258,7 +265,7 @@ int gma_impl(const char* fn, const void* q, const void* k, const void* v, const 
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
       !aligned(mu, 4) || !aligned(log_var, 4) || !aligned(logit_pi, 4))
     return fail(LM_EINVAL, "%s: misaligned pointer (tensors need 16 bytes, parameters 4)", fn);
-  const GmaLayout L = gma_layout(B, H, N, d, K, dv, dtype, segments);
+  const GmaLayout L = gma_layout(B, H, N, d, K, dv, dtype, segments, causal);
   if (workspace_bytes < L.total)
     return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
   const size_t es = esize(dtype);
@@ -283,6 +290,7 @@ int gma_impl(const char* fn, const void* q, const void* k, const void* v, const 
   La.c = reinterpret_cast<float*>(ws + L.c);
   La.agg = reinterpret_cast<float*>(ws + L.agg);
   La.aggz = reinterpret_cast<float*>(ws + L.aggz);
+  La.gk = L.gk ? ws + L.gk : nullptr;
   La.B = B;
   La.H = H;
   La.N = N;
@@ -503,7 +511,7 @@ const char* lm_last_error(void) { return g_err.c_str(); }
 size_t gma_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal,
                            int dtype, int64_t segments) {
   if (gma_check_shape(B, H, N, d, K, dv, causal, dtype, segments) != LM_OK) return 0;
-  return gma_layout(B, H, N, d, K, dv, dtype, segments).total;
+  return gma_layout(B, H, N, d, K, dv, dtype, segments, causal).total;
 }
 
 int gma_forward(const void* q, const void* k, const void* v, const float* mu, const float* log_var,

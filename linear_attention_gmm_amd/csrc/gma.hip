@@ -29,6 +29,9 @@
 //  * Long sequences are cut into segments. An AGG launch computes each
 //    segment's [Vtil | Z]. The CAUSAL launch then starts every segment from
 //    the sum of the earlier aggregates, and BIDIR starts from the total.
+//    In the causal bf16 kernel the AGG launch also stores every chunk's key
+//    responsibilities, which the CAUSAL launch loads instead of routing the
+//    keys a second time.
 #include "mfma.hpp"
 #include "gma.hpp"
 #include "gma_generic.hpp"
@@ -213,6 +216,7 @@ hipError_t gma_launch(const GmaLaunch& L, hipStream_t st) {
   a.KP = (int)L.KP;
   a.eps = L.eps;
   a.has_init = 0;
+  a.gk = L.gk;
   const dim3 pgrid((unsigned)L.H, (unsigned)((L.KP + 3) / 4));
   if (L.bf16)
     hipLaunchKernelGGL((prep_kernel<bf16>), pgrid, dim3(256), 0, st, L.mu, L.log_var, L.logit_pi, (bf16*)L.W, L.c,
@@ -224,14 +228,18 @@ hipError_t gma_launch(const GmaLaunch& L, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int P = (int)L.P;
   if (L.causal) {
+    // With a key-responsibility buffer (bf16 kernel, several segments) the
+    // segment pass covers every segment and stores Gamma_K of each chunk; the
+    // causal pass loads it instead of routing the keys a second time.
+    const bool reuse = L.gk != nullptr && fast_supported(L) && P > 1;
     // the memory after the last token needs the last segment's aggregate too
-    const int nagg = L.state_out ? P : P - 1;
+    const int nagg = reuse || L.state_out ? P : P - 1;
     if (nagg > 0 || L.state_in) {
-      if (nagg > 0 && (e = run(L, a, AGG, nagg, st)) != hipSuccess) return e;
+      if (nagg > 0 && (e = run(L, a, reuse ? AGG_G : AGG, nagg, st)) != hipSuccess) return e;
       if ((e = scan(L, 1, st)) != hipSuccess) return e;
       a.has_init = 1;
     }
-    return run(L, a, CAUSAL, P, st);
+    return run(L, a, reuse ? CAUSAL_G : CAUSAL, P, st);
   }
   if ((e = run(L, a, AGG, P, st)) != hipSuccess) return e;
   if ((e = scan(L, 0, st)) != hipSuccess) return e;

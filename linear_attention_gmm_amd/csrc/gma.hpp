@@ -19,7 +19,10 @@ constexpr float kPadLogit = -1.0e30f;
 
 // AGG: per-segment state [Vtil | Z] only. CAUSAL: outputs, starting from the
 // exclusive prefix of the earlier segments. BIDIR: outputs against the total.
-enum Mode { AGG = 0, CAUSAL = 1, BIDIR = 2 };
+// AGG_G and CAUSAL_G (bf16 kernel only): AGG that also stores each chunk's key
+// responsibilities (the bf16 tile as it sits in LDS), and CAUSAL that loads
+// them instead of routing the keys again.
+enum Mode { AGG = 0, CAUSAL = 1, BIDIR = 2, AGG_G = 3, CAUSAL_G = 4 };
 
 struct Args {
   const void* q;
@@ -37,6 +40,7 @@ struct Args {
   int KP;
   int has_init;  // CAUSAL/BIDIR: start from agg slot (p, or 0 for BIDIR) instead of zero
   float eps;
+  void* gk;      // AGG_G / CAUSAL_G: [B*H][ceil(N/64)] key-responsibility tiles (64 x KP bf16 each)
 };
 
 // General kernel for bf16, d = dv = 128, KP = 256 (gma_wide.hip).

@@ -24,7 +24,10 @@
 //     features are formed once per token (each wave squares the rows its own
 //     DMA brought in).
 // Q/K/V tiles arrive by direct global->LDS DMA into XOR-swizzled tiles, issued
-// a phase ahead of their use.
+// a phase ahead of their use. In the causal form over several segments, the
+// segment pass (AGG_G) stores each chunk's Gamma_K tile as it sits in LDS and
+// the causal pass (CAUSAL_G) brings it back by the same DMA in place of K:
+// steps 1 and 2 then route the queries only.
 #include "mfma.hpp"
 #include "gma.hpp"
 
@@ -121,8 +124,13 @@ struct Cfg {
   static constexpr int XB = 64 * D * 2;
   static constexpr int GB = 64 * KP * 2;
   static constexpr int SB = D * KP * 2;
-  static constexpr bool HK = MODE != BIDIR;
-  static constexpr bool HQ = MODE != AGG;
+  static constexpr bool IS_AGG = MODE == AGG || MODE == AGG_G;
+  static constexpr bool IS_CAUSAL = MODE == CAUSAL || MODE == CAUSAL_G;
+  static constexpr bool GSTORE = MODE == AGG_G;    // store the key responsibilities
+  static constexpr bool GLOAD = MODE == CAUSAL_G;  // load them instead of routing the keys
+  static constexpr bool HK = MODE != BIDIR;        // keys update the state
+  static constexpr bool RK = HK && !GLOAD;         // keys are routed here
+  static constexpr bool HQ = !IS_AGG;
   static constexpr int NS = (HK ? 1 : 0) + (HQ ? 1 : 0);
   static constexpr int INSTR = XC / NW;  // DMA instructions per wave per tile
   // Separate LDS arrays (so that the compiler can tell accesses to the DMA
@@ -131,15 +139,16 @@ struct Cfg {
   static constexpr int b_xk = HK ? XB : 16;
   // AGG (keys only) double-buffers the key tile: its DMA is issued two chunks
   // ahead, a whole chunk before it is needed.
-  static constexpr bool XDB = MODE == AGG;
+  static constexpr bool XDB = IS_AGG;
   static constexpr int b_xk1 = XDB ? XB : 16;
   static constexpr int b_xq = HQ ? XB : 16;
   static constexpr int b_v = HK ? XB : 16;
   static constexpr int b_g = NS * XB > NS * GB ? NS * XB : NS * GB;  // x*x tiles, later Gamma tiles
-  static constexpr int o_x2k = 0, o_x2q = HK ? XB : 0;
+  static constexpr int o_x2k = 0, o_x2q = HK ? XB : 0;  // (GLOAD: queries' x*x in the key tile buffer)
   static constexpr int o_gk = 0, o_gq = HK ? GB : 0;
   static constexpr int b_st = HQ ? SB : 16;            // bf16 state snapshot Vtil^T [D][KP]
-  static constexpr int b_sk = HK ? NW * 64 * 8 : 16;   // key stats [NW][64] (max, sum)
+  static constexpr int b_sk = RK ? NW * 64 * 8 : 16;   // key stats [NW][64] (max, sum)
+  static constexpr int GDMA = GB / (NW * 1024);        // DMA instructions per wave for a key-responsibility tile
   static constexpr int b_sq = HQ ? NW * 64 * 16 : 16;  // query stats [NW][64] (max, sum, Z-dot)
   static constexpr int lds = b_xk + b_xk1 + b_xq + b_v + b_g + b_st + b_sk + b_sq;
   static_assert(lds <= 80 * 1024, "two workgroups per CU");
@@ -163,6 +172,17 @@ __device__ __forceinline__ void dma_issue(char* dst, const bf16* src, int rows, 
   const unsigned base = lds_addr(dst) + (unsigned)(wave_id() * INSTR * 1024);
 #pragma unroll
   for (int i = 0; i < INSTR; ++i) lds_dma16(d, voff[i], base + (unsigned)(i * 1024));
+}
+
+// Linear DMA of one key-responsibility tile (GB bytes, stored as it sat in
+// LDS) into LDS: each wave moves GDMA 1 KB pieces.
+template <int GDMA>
+__device__ __forceinline__ void gdma_issue(char* dst, const char* src, int bytes) {
+  const u32x4 d = buf_desc(src, (uint32_t)bytes);
+  const unsigned base = lds_addr(dst) + (unsigned)(wave_id() * GDMA * 1024);
+#pragma unroll
+  for (int i = 0; i < GDMA; ++i)
+    lds_dma16(d, (wave_id() * GDMA + i) * 1024 + lane_id() * 16, base + (unsigned)(i * 1024));
 }
 
 // x*x of the 16 rows this wave's DMA wrote (same physical positions).
@@ -198,7 +218,7 @@ __device__ __forceinline__ void feat(const Tiles& t, int ct, bf16x8 (&fk)[C::NKF
 #pragma unroll
   for (int ks = 0; ks < C::NKF; ++ks) {
     const int kk = ks < C::NKX ? ks : ks - C::NKX;
-    if constexpr (C::HK) fk[ks] = gat<C::XC>(ks < C::NKX ? t.xk : t.x2k, row, kk);
+    if constexpr (C::RK) fk[ks] = gat<C::XC>(ks < C::NKX ? t.xk : t.x2k, row, kk);
     if constexpr (C::HQ) fq[ks] = gat<C::XC>(ks < C::NKX ? t.xq : t.x2q, row, kk);
   }
 }
@@ -217,10 +237,10 @@ __device__ __forceinline__ void route(f32x4 (&Lk)[4][C::RT], f32x4 (&Lq)[4][C::R
       f32x4 ak = c, aq = c;
 #pragma unroll
       for (int ks = 0; ks < C::NKF; ++ks) {
-        if constexpr (C::HK) ak = Mma<bf16>::mma(Wf[rt][ks], fk[ks], ak);
+        if constexpr (C::RK) ak = Mma<bf16>::mma(Wf[rt][ks], fk[ks], ak);
         if constexpr (C::HQ) aq = Mma<bf16>::mma(Wf[rt][ks], fq[ks], aq);
       }
-      if constexpr (C::HK) Lk[ct][rt] = ak;
+      if constexpr (C::RK) Lk[ct][rt] = ak;
       if constexpr (C::HQ) Lq[ct][rt] = aq;
     }
 #pragma unroll
@@ -276,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char sST[C::b_st];
   __shared__ __attribute__((aligned(16))) float2 stK[C::b_sk / 8];
   __shared__ __attribute__((aligned(16))) f32x4 stQ[C::b_sq / 16];
-  Tiles tl{sXK, sG + C::o_x2k, sXQ, sG + C::o_x2q};
+  Tiles tl{sXK, sG + C::o_x2k, sXQ, C::GLOAD ? sXK : sG + C::o_x2q};
 
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int bh = blockIdx.y, p = blockIdx.x;
@@ -291,6 +311,8 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
   const bf16* __restrict__ Wh = reinterpret_cast<const bf16*>(a.W) + (size_t)h * KP * 2 * D;
   const float* __restrict__ ch = a.c + (size_t)h * KP;
   const int comp0 = w * C::KPW;
+  const int64_t nch = (N + kChunk - 1) / kChunk;
+  char* const gkh = C::GSTORE || C::GLOAD ? static_cast<char*>(a.gk) + (size_t)bh * nch * C::GB : nullptr;
 
   const bf16* __restrict__ wrow = Wh + (size_t)(comp0 + c16) * 2 * D + 8 * g;
   float cb[RT][4];
@@ -308,9 +330,9 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) S[dt][rt] = zero4();
   }
-  if constexpr (MODE != AGG) {
+  if constexpr (!C::IS_AGG) {
     if (a.has_init) {
-      const int slot = MODE == CAUSAL ? p : 0;
+      const int slot = C::IS_CAUSAL ? p : 0;
       const float* ag = a.agg + ((size_t)bh * a.P + slot) * KP * D;
       const float* az = a.aggz + ((size_t)bh * a.P + slot) * KP;
 #pragma unroll
@@ -333,10 +355,9 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
   dma_init<C::XC, C::INSTR>(voff);
   {
     const int rows = (int)((N - t_begin) < kChunk ? (N - t_begin) : kChunk);
-    if constexpr (C::HK) {
-      dma_issue<D, C::INSTR>(sXK, Kg + (size_t)t_begin * D, rows, voff);
-      dma_issue<D, C::INSTR>(sV, Vg + (size_t)t_begin * D, rows, voff);
-    }
+    if constexpr (C::RK) dma_issue<D, C::INSTR>(sXK, Kg + (size_t)t_begin * D, rows, voff);
+    if constexpr (C::GLOAD) gdma_issue<C::GDMA>(sG + C::o_gk, gkh + (size_t)(t_begin / kChunk) * C::GB, C::GB);
+    if constexpr (C::HK) dma_issue<D, C::INSTR>(sV, Vg + (size_t)t_begin * D, rows, voff);
     if constexpr (C::HQ) dma_issue<D, C::INSTR>(sXQ, Qg + (size_t)t_begin * D, rows, voff);
     if (C::XDB && t_begin + kChunk < t_end) {
       const int64_t t1 = t_begin + kChunk;
@@ -345,8 +366,8 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
     } else {
       wait_vmem();
     }
-    if constexpr (C::HK) square_rows<D>(sXK, sG + C::o_x2k);
-    if constexpr (C::HQ) square_rows<D>(sXQ, sG + C::o_x2q);
+    if constexpr (C::RK) square_rows<D>(sXK, sG + C::o_x2k);
+    if constexpr (C::HQ) square_rows<D>(sXQ, const_cast<char*>(tl.x2q));
     lds_barrier();
   }
 
@@ -375,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
     // row of the product is sum_k e_k; for queries the odd rows of A hold Z
     // (state before the chunk), so element 1 of each lane's tile is
     // sum_k e_k Z_k. The sums use the exponentials rounded to bf16.
-    if constexpr (C::HK) {
+    if constexpr (C::RK) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const bf16x8 e = local_exp<RT>(Lk[ct], mk[ct]);
@@ -397,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
       }
     }
     // lane (g, c16) publishes token 16 g + c16 (every row holds every tile's stats)
-    if constexpr (C::HK) stK[w * 64 + l] = make_float2(pick(mk, g), pick(sk, g));
+    if constexpr (C::RK) stK[w * 64 + l] = make_float2(pick(mk, g), pick(sk, g));
     if constexpr (C::HQ) stQ[w * 64 + l] = f32x4{pick(mq, g), pick(sq, g), pick(dq, g), 0.f};
     lds_barrier();  // X tiles and x*x tiles are dead from here
 
@@ -406,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
     // waves' statistics of token 16 g + c16; the factors are then broadcast to
     // the rows that hold that token tile.
     float den_inter = 0.f;
-    if constexpr (C::HK) {
+    if constexpr (C::RK) {
       float2 st[4];
 #pragma unroll
       for (int ww = 0; ww < 4; ++ww) st[ww] = stK[ww * 64 + l];
@@ -458,14 +479,14 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
         dma_issue<D, C::INSTR>(xk_cur, Kg + (size_t)t2 * D, (int)((N - t2) < kChunk ? (N - t2) : kChunk), voff);
       }
     } else if (more) {
-      if constexpr (C::HK) dma_issue<D, C::INSTR>(sXK, Kg + (size_t)(t0 + kChunk) * D, rows_next, voff);
+      if constexpr (C::RK) dma_issue<D, C::INSTR>(sXK, Kg + (size_t)(t0 + kChunk) * D, rows_next, voff);
       if constexpr (C::HQ) dma_issue<D, C::INSTR>(sXQ, Qg + (size_t)(t0 + kChunk) * D, rows_next, voff);
     }
     if constexpr (C::HK) {
       // V of this chunk: its DMA was issued before the X tiles just issued (in
       // AGG also the next key tile, issued a chunk ago, is waited for here)
       if (C::XDB ? more2 : more)
-        LM_WAIT_VMEM(C::INSTR * (C::HQ ? 2 : 1));
+        LM_WAIT_VMEM(C::INSTR * ((C::RK ? 1 : 0) + (C::HQ ? 1 : 0)));
       else
         wait_vmem();
     }
@@ -476,6 +497,12 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
     // the next chunk's tiles. AGG keeps them in registers instead: a wait for
     // loads issued here would also wait for the tile DMA issued after them.
     if (!C::XDB && more) load_w<C>(Wf, wrow);
+    if constexpr (C::GSTORE) {
+      // the key-responsibility tile of this chunk, as it sits in LDS
+      char* gdst = gkh + (size_t)(t0 / kChunk) * C::GB;
+      for (int i = threadIdx.x; i < C::GB / 16; i += 256)
+        *reinterpret_cast<u32x4*>(gdst + 16 * i) = *reinterpret_cast<const u32x4*>(sG + C::o_gk + 16 * i);
+    }
     bf16x8 VB[DT][2];
     if constexpr (C::HK) {
 #pragma unroll
@@ -496,7 +523,7 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
         for (int ks = 0; ks < NKC; ++ks) O[dt] = M::mma(gat<C::GC>(sST, 16 * dt + c16, ks), GQ[ks], O[dt]);
       }
       float den = den_inter + a.eps;
-      if constexpr (MODE == CAUSAL) {
+      if constexpr (C::IS_CAUSAL) {
         const char* gk = sG + C::o_gk;
         f32x4 At[4];
 #pragma unroll
@@ -553,7 +580,7 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
     lds_barrier();  // Gamma tiles, the state snapshot and V are dead from here
 
     // ---- 4. state snapshot, next V, next x*x
-    if constexpr (MODE == CAUSAL) {
+    if constexpr (C::IS_CAUSAL) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -565,17 +592,19 @@ __global__ __launch_bounds__(256, 2) void kernel(Args a) {
         // earlier), then the V DMA: issued after the wait, the V tile is not
         // waited for by the compiler's own wait for W at the next routing.
         if constexpr (!C::XDB) wait_vmem();
+        if constexpr (C::GLOAD)
+          gdma_issue<C::GDMA>(sG + C::o_gk, gkh + (size_t)(t0 / kChunk + 1) * C::GB, C::GB);
         dma_issue<D, C::INSTR>(sV, Vg + (size_t)(t0 + kChunk) * D, rows_next, voff);
       } else {
         wait_vmem();
       }
-      if constexpr (C::HK) square_rows<D>(xk_nxt, sG + C::o_x2k);
-      if constexpr (C::HQ) square_rows<D>(sXQ, sG + C::o_x2q);
+      if constexpr (C::RK) square_rows<D>(xk_nxt, sG + C::o_x2k);
+      if constexpr (C::HQ) square_rows<D>(sXQ, const_cast<char*>(tl.x2q));
     }
     lds_barrier();
   }
 
-  if constexpr (MODE == AGG) {
+  if constexpr (C::IS_AGG) {
     float* ag = a.agg + ((size_t)bh * a.P + p) * KP * D;
     float* az = a.aggz + ((size_t)bh * a.P + p) * KP;
 #pragma unroll
@@ -596,6 +625,8 @@ static hipError_t launch_mode(const Args& a, int mode, int segments, unsigned BH
   switch (mode) {
     case AGG: hipLaunchKernelGGL((kernel<D, KP, AGG>), grid, block, 0, st, a); break;
     case CAUSAL: hipLaunchKernelGGL((kernel<D, KP, CAUSAL>), grid, block, 0, st, a); break;
+    case AGG_G: hipLaunchKernelGGL((kernel<D, KP, AGG_G>), grid, block, 0, st, a); break;
+    case CAUSAL_G: hipLaunchKernelGGL((kernel<D, KP, CAUSAL_G>), grid, block, 0, st, a); break;
     default: hipLaunchKernelGGL((kernel<D, KP, BIDIR>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();

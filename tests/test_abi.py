@@ -136,6 +136,15 @@ def test_workspace_sizes_are_deterministic_and_grow_with_segments():
     assert L.gma_workspace_bytes(4, 8, 16384, 64, 128, 64, 1, binding.LM_BF16, 16) > \
         L.gma_workspace_bytes(4, 8, 16384, 64, 128, 64, 1, binding.LM_BF16, 2)
     assert L.gma_workspace_bytes(4, 8, 16384, 48, 128, 48, 1, binding.LM_BF16, 0) == 0
+    # the causal bf16 kernel over several segments also keeps every chunk's key
+    # responsibilities (64 x 128 bf16 per chunk); one segment, float32 and the
+    # bidirectional form do not
+    tiles = 4 * 8 * (16384 // 64) * 64 * 128 * 2
+    assert a - L.gma_workspace_bytes(4, 8, 16384, 64, 128, 64, 0, binding.LM_BF16, 0) == tiles
+    assert L.gma_workspace_bytes(4, 8, 16384, 64, 128, 64, 1, binding.LM_BF16, 1) == \
+        L.gma_workspace_bytes(4, 8, 16384, 64, 128, 64, 0, binding.LM_BF16, 1)
+    assert L.gma_workspace_bytes(4, 8, 16384, 64, 128, 64, 1, binding.LM_F32, 0) == \
+        L.gma_workspace_bytes(4, 8, 16384, 64, 128, 64, 0, binding.LM_F32, 0)
     assert L.ccq_workspace_bytes(4, 16, 16384, 128, 128, 64, binding.LM_BF16, 0) > \
         L.linattn_workspace_bytes(4, 16, 16384, 128, 128, 64, binding.LM_BF16, 0)
 
