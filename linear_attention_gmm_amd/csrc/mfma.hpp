@@ -31,7 +31,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LM_LDS __attribute__((address_space(3)))
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
-__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+// Uniform across the wave (one-dimensional workgroups of whole waves), so it is
+// moved to a scalar register: offsets derived from it then take no VGPRs.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
