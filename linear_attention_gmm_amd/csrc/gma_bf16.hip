@@ -153,6 +153,7 @@ struct Cfg {
   static constexpr int lds = b_xk + b_xk1 + b_xq + b_v + b_g + b_st + b_sk + b_sq;
   static_assert(lds <= 80 * 1024, "two workgroups per CU");
   static_assert(XC % NW == 0 && KP % 64 == 0 && D % 32 == 0, "shape");
+  static_assert(GDMA * NW * 1024 == GB, "a key-responsibility tile is whole 1 KB DMA pieces");
 };
 
 // Per-lane source offsets of this wave's share of a 64-row tile DMA.
