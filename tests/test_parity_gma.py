@@ -147,6 +147,17 @@ def test_gma_bf16_ragged_multiseg():
             assert_close(got, ref, "bf16", "gma bf16 N=1000 causal=%d P=%d" % (causal, seg))
 
 
+@pytest.mark.parametrize("d,K", [(32, 40), (64, 64), (32, 128)])
+def test_gma_bf16_causal_stored_key_responsibilities(d, K):
+    # the causal bf16 kernel over several segments, where the segment pass
+    # stores every chunk's key responsibilities and the causal pass loads them:
+    # both padded widths (64 and 128 components) and a ragged last chunk
+    cfg = inputs.GmaConfig("gma_bf16_gk", 108, B=2, H=2, N=777, d=d, K=K, dv=d, qk_scale=d == 64)
+    for seg in (2, 7):
+        got, ref = _run(cfg, causal=True, segments=seg)
+        assert_close(got, ref, "bf16", "gma bf16 d=%d K=%d N=777 causal P=%d" % (d, K, seg))
+
+
 def test_gma_segment_invariance_fp32():
     cfg = inputs.GmaConfig("gma_seg", 107, B=1, H=2, N=1024, d=64, K=128, dv=64, dtype="f32", qk_scale=True)
     x = cuda(inputs.gma_inputs(cfg))
