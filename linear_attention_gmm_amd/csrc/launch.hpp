@@ -17,7 +17,7 @@ struct GmaLaunch {
   float* c;     // workspace: [H][KP]
   float* agg;   // workspace: [B*H][P][KP][DV]
   float* aggz;  // workspace: [B*H][P][KP]
-  void* gk;     // workspace (bf16 causal kernel, P > 1): key responsibilities per chunk
+  void* gk = nullptr;  // workspace (bf16 causal kernel, P > 1): key responsibilities per chunk
   int64_t B, H, N, D, K, KP, P, seg_len;
   int causal;
   bool bf16;
