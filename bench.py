@@ -77,17 +77,39 @@ DIGEST_SOURCES = ("abi.cpp", "launch.hpp", "mfma.hpp", "gma.hip", "gma.hpp", "gm
 
 
 def sources_digest():
-    """Hash of the measured entry points' sources (identifies the code the counters were taken on).
-    Lines that hold only a // comment are left out, so that editing such a comment keeps the digest."""
+    """Hash of the measured entry points' sources and of the build script that
+    sets their compile flags (identifies the code the counters were taken on).
+    Lines that hold only a comment (// in C++, # in Python) are left out, so
+    that editing such a comment keeps the digest. Only --summarize-pmc, which
+    reads fresh counters, records it in profiles/traffic.json."""
     h = hashlib.sha256()
     files = [os.path.join(ROOT, "linear_attention_gmm_amd", "csrc", f) for f in DIGEST_SOURCES]
+    files.append(os.path.join(ROOT, "linear_attention_gmm_amd", "build.py"))
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             for line in fh.read().splitlines(keepends=True):
-                if not line.lstrip().startswith(b"//"):
+                if not line.lstrip().startswith((b"//", b"#")):
                     h.update(line)
     return h.hexdigest()[:16]
+
+
+def host_cpu():
+    """(model name, logical CPUs this process may run on, logical CPUs of the host)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 0
+    return model, avail, os.cpu_count() or 0
 
 
 def gma_bytes_per_head_token(cfg, esize=2):
@@ -434,10 +456,13 @@ def cpu_baseline(gx, cx, gcfg, ccfg, min_seconds=10.0, max_rounds=20):
         tc += time.perf_counter() - tc0
         rounds += 1
     toks = rounds * (sg * gcfg.N + sc * ccfg.N)
+    model, avail, ncpu = host_cpu()
+    # cores: the OpenMP threads that had work (one (b, h) slice each)
     return {"value": toks / (tg + tc), "unit": "head-tokens/s", "cores": max(sg, sc), "kind": "oracle",
             "sample": "%d round(s) of %d causal-GMA + %d CCQ slices at N=16384 (one slice per thread per path), "
                       "fp64; GMA %.1f s, CCQ %.1f s" % (rounds, sg, sc, tg, tc),
-            "host_threads": threads, "wall_s": time.perf_counter() - t0}
+            "host_threads": threads, "cpu_model": model, "nproc": avail, "host_cpus": ncpu,
+            "wall_s": time.perf_counter() - t0}
 
 
 def summarize_pmc(fetch_dir, write_dir):

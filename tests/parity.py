@@ -9,6 +9,8 @@ Metrics (the tolerances come with the method's precision targets):
 """
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -35,6 +37,19 @@ def rel_l2(x, r) -> float:
     return float(np.linalg.norm((x - r).ravel()) / max(np.linalg.norm(r.ravel()), 1e-300))
 
 
+def record(what: str, metric: str, value: float, tol: float, **extra):
+    """Appends one comparison to the JSON-lines file named by LM_PARITY_RECORD
+    (when set), so that a test run leaves every error value and its margin."""
+    path = os.environ.get("LM_PARITY_RECORD")
+    if not path:
+        return
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    row = dict(test=test, what=what, metric=metric, value=float(value), tol=float(tol))
+    row.update(extra)
+    with open(path, "a") as f:
+        f.write(json.dumps(row) + "\n")
+
+
 def assert_close(x, r, dtype: str, what: str):
     """dtype 'f32' -> max-rel <= 1e-4; 'bf16' -> rel-L2 <= 2e-2. Both finite."""
     x = np.asarray(x, dtype=np.float64)
@@ -42,10 +57,13 @@ def assert_close(x, r, dtype: str, what: str):
     if dtype == "f32":
         e = max_rel(x, r)
         say("  %s: max-rel %.3e (tol %.0e)" % (what, e, TOL_F32_MAXREL))
+        record(what, "max-rel", e, TOL_F32_MAXREL, elements=int(x.size))
         assert e <= TOL_F32_MAXREL, "%s: max-rel %.3e > %.0e" % (what, e, TOL_F32_MAXREL)
     else:
         e = rel_l2(x, r)
-        say("  %s: rel-L2 %.3e (tol %.0e), max-rel %.3e" % (what, e, TOL_BF16_RELL2, max_rel(x, r)))
+        mr = max_rel(x, r)
+        say("  %s: rel-L2 %.3e (tol %.0e), max-rel %.3e" % (what, e, TOL_BF16_RELL2, mr))
+        record(what, "rel-L2", e, TOL_BF16_RELL2, max_rel=mr, elements=int(x.size))
         assert e <= TOL_BF16_RELL2, "%s: rel-L2 %.3e > %.0e" % (what, e, TOL_BF16_RELL2)
     return e
 

@@ -23,6 +23,7 @@ def test_digest_ignores_comment_lines_and_tracks_code(tmp_path, monkeypatch):
     csrc.mkdir(parents=True)
     for f in bench.DIGEST_SOURCES:
         shutil.copy(os.path.join(ROOT, "linear_attention_gmm_amd", "csrc", f), csrc / f)
+    shutil.copy(os.path.join(ROOT, "linear_attention_gmm_amd", "build.py"), csrc.parent / "build.py")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     base = bench.sources_digest()
     assert base == bench.sources_digest()
@@ -32,3 +33,16 @@ def test_digest_ignores_comment_lines_and_tracks_code(tmp_path, monkeypatch):
     assert bench.sources_digest() == base
     p.write_text(text + "\nstatic int added_code_line;\n")
     assert bench.sources_digest() != base
+    p.write_text(text)
+    assert bench.sources_digest() == base
+    # a change of compile flags in the build script also changes the digest
+    b = csrc.parent / "build.py"
+    btext = b.read_text()
+    b.write_text(btext.replace('"-O3"', '"-O2"'))
+    assert bench.sources_digest() != base
+
+
+def test_host_cpu_reports_model_and_counts():
+    model, avail, ncpu = bench.host_cpu()
+    assert isinstance(model, str) and model
+    assert 1 <= avail <= ncpu

@@ -50,7 +50,10 @@ def cmp_state(got, ref, kind, d, dtype, what):
 
 
 def _lin_case(dk, dtype, ccq, segments, inplace=False, cfg_id=301):
-    cfg = inputs.LinAttnConfig("state_lin", cfg_id, B=2, H=2, N=NTOT, dk=dk, dv=dk, dtype=dtype)
+    # CCQ on low-rank keys with gate bias +2, where the covariance correction is
+    # a large part of q_clean: a state with a wrong count or key sum shows
+    cfg = inputs.LinAttnConfig("state_lin", cfg_id, B=2, H=2, N=NTOT, dk=dk, dv=dk, dtype=dtype,
+                               lowrank_keys=4 if ccq else 0, gate_bias=2.0 if ccq else -2.0)
     x = inputs.linattn_inputs(cfg, ccq=ccq)
     say("state %s: dk=%d dtype=%s segments=%d inplace=%s" % ("ccq" if ccq else "gla", dk, dtype, segments, inplace))
     d = cuda(x)
@@ -185,24 +188,23 @@ def test_gma_state_in_place():
     _gma_case(64, 32, "f32", 2, inplace=True)
 
 
-def test_ccq_full_size_prefill_then_decode():
-    # the 16K-token CCQ workload (B=4, H=16, d=128, bf16) as a prefill, then two
-    # decode steps; checked on two (b,h) slices
-    cfg = inputs.CONFIGS["ccq_bf16_n16k"]
+@pytest.mark.parametrize("name", ["ccq_bf16_n16k", "ccq_bf16_lowrank"])
+def test_ccq_full_size_prefill_then_decode(name):
+    # the 16K-token CCQ workload (B=4, H=16, d=128, bf16; also with low-rank
+    # keys and gate bias +2) as a prefill, then two decode steps; every slice
+    cfg = inputs.CONFIGS[name]
     N = cfg.N
     x = inputs.linattn_inputs(cfg, N=N + 2, ccq=True)
-    say("state ccq full size: N=%d + 2 steps" % N)
+    say("state ccq full size (%s): N=%d + 2 steps" % (name, N))
     d = cuda(x)
     out, st = binding.ccq_forward_state(*[_sl(d[n], 0, N) for n in "qkvg"], d["w_lambda"], d["b_lambda"])
     outs = [host(binding.ccq_decode_step(*[_tok(d[n], i) for n in "qkvg"], d["w_lambda"], d["b_lambda"], st,
                                          t_prev=i)) for i in (N, N + 1)]
     stg = host(st)
-    for b, h in [(0, 0), (3, 15)]:
-        sel = lambda t: t[b:b + 1, h:h + 1]
-        ref, rs = oracle.ccq_forward(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["g"]), x["w_lambda"][h:h + 1],
-                                     x["b_lambda"][h:h + 1], return_state=True)
-        assert_close(np.stack([o[b, h] for o in outs]), ref[0, 0, N:], "bf16", "decode out (%d,%d)" % (b, h))
-        cmp_state(stg[b, h], rs[0, 0], "ccq", 128, "bf16", "state after decode (%d,%d)" % (b, h))
+    ref, rs = oracle.ccq_forward(x["q"], x["k"], x["v"], x["g"], x["w_lambda"], x["b_lambda"], return_state=True)
+    assert_close(host(out), ref[:, :, :N], "bf16", "prefill out (%s)" % name)
+    assert_close(np.stack(outs, axis=2), ref[:, :, N:], "bf16", "decode out (%s)" % name)
+    cmp_state(stg, rs, "ccq", 128, "bf16", "state after decode (%s)" % name)
 
 
 @pytest.mark.parametrize("B", [2, 5, 11])
