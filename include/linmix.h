@@ -102,7 +102,7 @@
 extern "C" {
 #endif
 
-#define LM_ABI_VERSION 3
+#define LM_ABI_VERSION 4
 
 typedef enum {
   LM_OK = 0,
@@ -321,6 +321,28 @@ int ccq_forward_state(const void* q, const void* k, const void* v, const float* 
                       int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
                       int64_t segments, int64_t t_in, const float* state_in, float* state_out,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gma_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Arguments, shapes and results as for gma_forward.
+ * Scratch comes from a fixed device array of LM_NOALLOC_SCRATCH_BYTES inside
+ * the library, one per GPU, held from the library's load until the process
+ * ends; its address is looked up on the first call on each device. The call
+ * allocates nothing and calls no allocating routine. The causal form does not
+ * store the key responsibilities in this scratch (it routes the keys in both
+ * of its passes), so it needs about 4 (K dv + K) bytes per (b, h) and segment
+ * plus the prepared parameters (8 d K + 4 K bytes per head for bf16).
+ * Errors: LM_EWORKSPACE when the shape needs more scratch than the array
+ * holds (fewer segments need less); otherwise as for gma_forward.
+ * Every call on one GPU uses the same scratch: calls that overlap in time on
+ * one GPU (two streams, two threads) race and must not be issued.
+ */
+#define LM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int gma_forward_noalloc(const void* q, const void* k, const void* v, const float* mu,
+                        const float* log_var, const float* logit_pi, void* out, int64_t B,
+                        int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal,
+                        float eps, int dtype, int64_t segments, void* stream);
 
 /*
  * One-token steps. Per (b, h) one new token: q, k [B,H,d] and v, out [B,H,dv]

@@ -45,6 +45,8 @@ _SIGS = {
                               ctypes.c_int),
     "ccq_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
     "ccq_forward": ([_P] * 7 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "gma_forward_noalloc": ([_P] * 7 + [_I64] * 6 + [ctypes.c_int, ctypes.c_float, ctypes.c_int, _I64, _P],
+                            ctypes.c_int),
     "gma_forward_state": ([_P] * 7 + [_I64] * 6 + [ctypes.c_float, ctypes.c_int, _I64, _P, _P, _P,
                                                    ctypes.c_size_t, _P], ctypes.c_int),
     "linattn_chunk_forward_state": ([_P] * 5 + [_I64] * 6 + [ctypes.c_int, _I64, _P, _P, _P, ctypes.c_size_t, _P],
@@ -163,6 +165,30 @@ def gma_forward(q, k, v, mu, log_var, logit_pi, causal: bool = True, eps: float 
     st = lib().gma_forward(pq, pk, pv, pmu, plv, plp, po, B, H, N, d, K, dv, int(bool(causal)), float(eps), dt,
                            segments, ws.data_ptr(), nbytes, _stream(q.device))
     _check("gma_forward", st)
+    return out
+
+
+def gma_forward_noalloc(q, k, v, mu, log_var, logit_pi, causal: bool = True, eps: float = 1e-6,
+                        segments: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gma_forward on the library's fixed device scratch: no workspace is
+    allocated (only `out`, when the caller passes none). Calls that overlap in
+    time on one GPU share that scratch and must not be issued."""
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    dt = _dtype_code(q)
+    pq = _dev(q, "q", q.dtype, (B, H, N, d))
+    pk = _dev(k, "k", q.dtype, (B, H, N, d))
+    pv = _dev(v, "v", q.dtype, (B, H, N, dv))
+    pmu = _dev(mu, "mu", torch.float32, (H, K, d))
+    plv = _dev(log_var, "log_var", torch.float32, (H, K, d))
+    plp = _dev(logit_pi, "logit_pi", torch.float32, (H, K))
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    po = _dev(out, "out", q.dtype, (B, H, N, dv))
+    st = lib().gma_forward_noalloc(pq, pk, pv, pmu, plv, plp, po, B, H, N, d, K, dv, int(bool(causal)), float(eps),
+                                   dt, segments, _stream(q.device))
+    _check("gma_forward_noalloc", st)
     return out
 
 

@@ -31,6 +31,7 @@ int ok() {
 }
 
 constexpr int64_t kChunk = 64;
+static_assert(lm::kNoallocScratchBytes == LM_NOALLOC_SCRATCH_BYTES, "scratch size of the header and the library");
 // Workgroups the segment plan aims for: one per compute unit of an MI355X.
 // Workgroups to aim for when a launch is cut into segments: one per CU for the
 // linear-attention kernels, two per CU for the bf16 GMA kernel (it is sized to
@@ -106,7 +107,7 @@ struct GmaLayout {
 };
 
 GmaLayout gma_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int dtype,
-                     int64_t segments, int causal) {
+                     int64_t segments, int causal, bool store_gk = true) {
   GmaLayout L;
   L.KP = gma_kp(K, d, dtype);
   L.plan = plan_segments(B * H, N, segments, gma_fast(d, K, dtype) ? kTargetGroupsGma : kTargetGroups);
@@ -122,7 +123,7 @@ GmaLayout gma_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int6
   // causal bf16 kernel over several segments: the segment pass stores each
   // chunk's key responsibilities (64 x KP bf16) for the causal pass
   L.gk = 0;
-  if (causal && gma_fast(d, K, dtype) && L.plan.P > 1) {
+  if (store_gk && causal && gma_fast(d, K, dtype) && L.plan.P > 1) {
     L.gk = off;
     off = align_up(off + (size_t)B * H * ((N + kChunk - 1) / kChunk) * kChunk * L.KP * 2);
   }
@@ -256,7 +257,7 @@ VecLayout vec_layout(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t segmen
 int gma_impl(const char* fn, const void* q, const void* k, const void* v, const float* mu, const float* log_var,
              const float* logit_pi, void* out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv,
              int causal, float eps, int dtype, int64_t segments, const float* state_in, float* state_out,
-             void* workspace, size_t workspace_bytes, void* stream) {
+             void* workspace, size_t workspace_bytes, void* stream, bool store_gk = true) {
   int st = gma_check_shape(B, H, N, d, K, dv, causal, dtype, segments);
   if (st != LM_OK) return st;
   if (!(eps >= 0.f) || std::isinf(eps)) return fail(LM_EINVAL, "%s: eps must be finite and >= 0", fn);
@@ -265,7 +266,7 @@ int gma_impl(const char* fn, const void* q, const void* k, const void* v, const 
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
       !aligned(mu, 4) || !aligned(log_var, 4) || !aligned(logit_pi, 4))
     return fail(LM_EINVAL, "%s: misaligned pointer (tensors need 16 bytes, parameters 4)", fn);
-  const GmaLayout L = gma_layout(B, H, N, d, K, dv, dtype, segments, causal);
+  const GmaLayout L = gma_layout(B, H, N, d, K, dv, dtype, segments, causal, store_gk);
   if (workspace_bytes < L.total)
     return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
   const size_t es = esize(dtype);
@@ -520,6 +521,30 @@ int gma_forward(const void* q, const void* k, const void* v, const float* mu, co
                 size_t workspace_bytes, void* stream) {
   return gma_impl("gma_forward", q, k, v, mu, log_var, logit_pi, out, B, H, N, d, K, dv, causal, eps, dtype,
                   segments, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int gma_forward_noalloc(const void* q, const void* k, const void* v, const float* mu, const float* log_var,
+                        const float* logit_pi, void* out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t K,
+                        int64_t dv, int causal, float eps, int dtype, int64_t segments, void* stream) {
+  const char* fn = "gma_forward_noalloc";
+  int st = gma_check_shape(B, H, N, d, K, dv, causal, dtype, segments);
+  if (st != LM_OK) return st;
+  // (every argument is checked before the first HIP call, as for gma_forward)
+  if (!(eps >= 0.f) || std::isinf(eps)) return fail(LM_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (!q || !k || !v || !mu || !log_var || !logit_pi || !out) return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(mu, 4) ||
+      !aligned(log_var, 4) || !aligned(logit_pi, 4))
+    return fail(LM_EINVAL, "%s: misaligned pointer (tensors need 16 bytes, parameters 4)", fn);
+  // the fixed scratch never holds the stored key responsibilities
+  const size_t need = gma_layout(B, H, N, d, K, dv, dtype, segments, causal, false).total;
+  if (need > lm::kNoallocScratchBytes)
+    return fail(LM_EWORKSPACE, "%s: %zu bytes of scratch needed, the fixed scratch holds %zu", fn, need,
+                lm::kNoallocScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = lm::noalloc_scratch(&ws);
+  if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return gma_impl(fn, q, k, v, mu, log_var, logit_pi, out, B, H, N, d, K, dv, causal, eps, dtype, segments,
+                  nullptr, nullptr, ws, lm::kNoallocScratchBytes, stream, false);
 }
 
 int gma_forward_state(const void* q, const void* k, const void* v, const float* mu, const float* log_var,

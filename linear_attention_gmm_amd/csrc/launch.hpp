@@ -209,6 +209,11 @@ struct GmaBwdLaunch {
 };
 hipError_t gma_backward_launch(const GmaBwdLaunch& L, hipStream_t st);
 
+// Fixed device scratch of the entry point that allocates nothing (noalloc.hip):
+// its size, and its address on the current device (looked up once per device).
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Floats per state block written by the segment-state pass.
 inline int64_t lin_state_floats(int64_t D, bool ccq) {
   // S (D x D), decay product, and for CCQ: M (D x D), m (D); padded to 64 floats

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_version_and_status_strings():
     L = binding.lib()
-    assert L.lm_abi_version() == 3
+    assert L.lm_abi_version() == 4
     for code, name in enumerate(["LM_OK", "LM_EINVAL", "LM_EUNSUPPORTED", "LM_EWORKSPACE", "LM_EHIP"]):
         assert L.lm_status_string(code).decode() == name
     assert L.lm_status_string(99).decode() == "LM_UNKNOWN"
@@ -341,3 +341,24 @@ def test_ccq_backward_errors():
     assert call(d=48) == binding.LM_EUNSUPPORTED
     assert call(chunk=32) == binding.LM_EUNSUPPORTED
     assert L.lm_last_error().decode()
+
+
+@needs_lib
+def test_noalloc_checks_before_any_hip_call():
+    # gma_forward_noalloc: argument errors and a shape beyond its fixed scratch
+    # are reported before the scratch is looked up (no GPU needed)
+    L = binding.lib()
+    G = 1 << 30
+    p = [FAKE + i * G for i in range(7)]
+
+    def call(ptrs, B=1, H=16, N=131072, d=128, K=256, seg=64, eps=1e-6):
+        st = L.gma_forward_noalloc(*ptrs, B, H, N, d, K, d, 1, eps, binding.LM_BF16, seg, None)
+        return st, L.lm_last_error().decode()
+
+    # 64 segments of the long-context shapes: 16 * 64 * 256 * 129 * 4 bytes > 64 MiB
+    st, msg = call(p)
+    assert st == binding.LM_EWORKSPACE and "scratch" in msg, msg
+    assert call([None] + p[1:], seg=1)[0] == binding.LM_EINVAL
+    assert call(p[:6] + [p[6] + 2], seg=1)[0] == binding.LM_EINVAL  # misaligned out
+    assert call(p, seg=1, eps=-1.0)[0] == binding.LM_EINVAL
+    assert call(p, d=48, seg=1)[0] == binding.LM_EUNSUPPORTED
