@@ -50,6 +50,23 @@ struct LinLaunch {
 };
 hipError_t linattn_launch(const LinLaunch& L, hipStream_t st);
 
+// Chunk pass of the CCQ read for bf16 inputs at dk = dv = 128 (ccq_pipe.hip):
+// one workgroup per (b, h, segment), starting from the segment's state block
+// (agg, R * segment, blocks per (b, h)) or from zero when agg is null.
+struct CcqPipeLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* w_lambda;
+  const float* b_lambda;
+  void* out;
+  const float* agg;
+  int64_t B, H, N, P, seg_len, blocks, R, sfl, t_off;
+  float* state_out;
+};
+hipError_t ccq_pipe_launch(const CcqPipeLaunch& L, hipStream_t st);
+
 // Decayed linear attention with a decay per key feature (linattn_vec.hip).
 struct VecLaunch {
   const void* q;

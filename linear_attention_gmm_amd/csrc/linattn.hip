@@ -1103,6 +1103,28 @@ static hipError_t launch_d(const LinLaunch& L, hipStream_t st) {
     a.has_init = 1;
   }
   a.seg_len = (int)L.seg_len;
+  if constexpr (sizeof(T) == 2 && D == 128 && CCQ) {
+    CcqPipeLaunch cp;
+    cp.q = L.q;
+    cp.k = L.k;
+    cp.v = L.v;
+    cp.g = L.g;
+    cp.w_lambda = L.w_lambda;
+    cp.b_lambda = L.b_lambda;
+    cp.out = L.out;
+    cp.agg = a.has_init ? L.agg : nullptr;
+    cp.B = L.B;
+    cp.H = L.H;
+    cp.N = L.N;
+    cp.P = L.P;
+    cp.seg_len = L.seg_len;
+    cp.blocks = a.P;
+    cp.R = a.R;
+    cp.sfl = a.sfl;
+    cp.t_off = a.t_off;
+    cp.state_out = L.state_out;
+    return ccq_pipe_launch(cp, st);
+  }
   return launch_one<T, D, CCQ, false>(a, (unsigned)L.P, BH, st);
 }
 

@@ -159,6 +159,16 @@ def test_ccq_bf16_lowrank():
     assert _worst_slice(got, ref) <= 2e-2
 
 
+@pytest.mark.parametrize("N,segments", [(1, 0), (63, 0), (65, 0), (1000, 1), (1000, 3), (777, 2)])
+@pytest.mark.parametrize("lowrank", [False, True])
+def test_ccq_bf16_d128_ragged(N, segments, lowrank):
+    # the bf16 dk = 128 chunk pass at ragged lengths, one and several segments
+    name = "ccq_bf16_lowrank" if lowrank else "ccq_bf16_n16k"
+    cfg = inputs.CONFIGS[name].replace(name=name + "_ragged", cfg_id=304, B=2, H=2, N=N)
+    got, ref = _ccq(cfg, segments=segments, with_gla=True)
+    assert_close(got, ref, "bf16", "ccq bf16 dk=128 N=%d P=%d lowrank=%d" % (N, segments, lowrank))
+
+
 @pytest.mark.parametrize("segments", [3, 4])
 def test_ccq_bf16_sub_segments(segments):
     # N = 768 is 12 chunks: 3 segments of 4 chunks (two sub-segments each in the
