@@ -70,6 +70,10 @@ class Oracle:
         lib.oracle_ccq_forward.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I, _D,
                                            _D]
         lib.oracle_glv_forward.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _D, _D]
+        lib.oracle_deltanet_forward.argtypes = [_D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _D,
+                                                _D]
+        lib.oracle_ccq_deltanet_forward.argtypes = [_D, _D, _D, _D, _D, _D, _D, _D, _I, _I, _I,
+                                                    _I, _I, _I, _D, _D]
         lib.oracle_gla_chunkwise.argtypes = [_D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I]
         lib.oracle_ccq_chunkwise.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I, _I, _I]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -172,6 +176,37 @@ class Oracle:
                                     _p(sout))
         return (out, sout) if return_state else out
 
+    def deltanet_forward(self, q, k, v, g, beta, state_in=None, return_state: bool = False):
+        """Gated delta write rule, plain read: beta [B,H,N] step sizes; other
+        arguments as for gla_forward (state S [B,H,dk*dv])."""
+        q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+        B, H, N, dk = q.shape
+        dv = v.shape[-1]
+        out = np.empty((B, H, N, dv))
+        sin = None if state_in is None else _f64(state_in).reshape(B, H, dk * dv)
+        sout = np.empty((B, H, dk * dv)) if return_state else None
+        self.lib.oracle_deltanet_forward(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(out), B, H, N,
+                                         dk, dv, _p(sin), _p(sout))
+        return (out, sout) if return_state else out
+
+    def ccq_deltanet_forward(self, q, k, v, g, beta, w_lambda, b_lambda, t0: int = 0,
+                             state_in=None, return_state: bool = False):
+        """CCQ read over the gated delta write rule; state [S | M | m] and t0 as
+        for ccq_forward."""
+        q, k, v, g, beta, w, b = map(_f64, (q, k, v, g, beta, w_lambda, b_lambda))
+        B, H, N, dk = q.shape
+        dv = v.shape[-1]
+        ss = dk * dv + dk * dk + dk
+        if state_in is None and t0 != 0:
+            raise ValueError("t0 counts the tokens held by state_in")
+        out = np.empty((B, H, N, dv))
+        sin = None if state_in is None else _f64(state_in).reshape(B, H, ss)
+        sout = np.empty((B, H, ss)) if return_state else None
+        self.lib.oracle_ccq_deltanet_forward(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(w), _p(b),
+                                             _p(out), B, H, N, dk, dv, int(t0), _p(sin),
+                                             _p(sout))
+        return (out, sout) if return_state else out
+
     def gla_chunkwise(self, q, k, v, g, chunk: int = 64) -> np.ndarray:
         q, k, v, g = map(_f64, (q, k, v, g))
         B, H, N, dk = q.shape
@@ -230,6 +265,14 @@ def ccq_forward(*a, **kw):
 
 def glv_forward(*a, **kw):
     return get().glv_forward(*a, **kw)
+
+
+def deltanet_forward(*a, **kw):
+    return get().deltanet_forward(*a, **kw)
+
+
+def ccq_deltanet_forward(*a, **kw):
+    return get().ccq_deltanet_forward(*a, **kw)
 
 
 def gla_chunkwise(*a, **kw):

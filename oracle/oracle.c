@@ -26,7 +26,10 @@
  *        accumulates key-value outer products, decay gates in (0,1), and
  *        the chunkwise-parallel form (intra-chunk matrix products + state
  *        handed over at chunk boundaries), which gives the same result as
- *        the recurrence.
+ *        the recurrence. The same sections read the state update as one
+ *        step of gradient descent on a squared-error regression from keys
+ *        to values, and name the delta rule (erase the value bound to the
+ *        current key, write the new one) as the companion of the decay gate.
  *
  * Layouts: q, k [B,H,N,d]; v, out [B,H,N,dv]; per-head parameters [H,...];
  * decays g [B,H,N]. All arrays are row-major float64. Nothing is allocated
@@ -236,10 +239,20 @@ void oracle_gma_brute(const double* q, const double* k, const double* v, const d
  *       lambda_t = sigmoid(w . q_t + b),  q_clean = q_t - lambda_t Sigma_t q_t
  *   read [CCQ, integration]: o_t = S_t^T q_clean  (plain linear attention
  *   reads with q_t itself).
+ *   gated delta write (beta != NULL) [LIN, key messages + easy explanation:
+ *   the update is one gradient step on the squared error of predicting v_t
+ *   from k_t, and the delta rule overwrites the value bound to k_t; the
+ *   decay gate forgets first]:
+ *       S' = g_t S_{t-1},  r_t = S'^T k_t - v_t  (prediction error),
+ *       S_t = S' - beta_t k_t r_t^T
+ *   i.e. S' minus beta_t times the gradient of 1/2 ||S^T k_t - v_t||^2 at S'.
+ *   The CCQ read is unchanged on this write rule [CCQ, integration: the read
+ *   does not depend on the write rule].
  */
 static void linattn_slice(const double* q, const double* k, const double* v, const double* g,
-                          const double* w, double bias, double* out, int64_t N, int64_t dk,
-                          int64_t dv, int ccq, int64_t t0, const double* st_in, double* st_out) {
+                          const double* beta, const double* w, double bias, double* out, int64_t N,
+                          int64_t dk, int64_t dv, int ccq, int64_t t0, const double* st_in,
+                          double* st_out) {
   double* S = (double*)calloc((size_t)(dk * dv), sizeof(double));
   double* M = ccq ? (double*)calloc((size_t)(dk * dk), sizeof(double)) : NULL;
   double* m = ccq ? (double*)calloc((size_t)dk, sizeof(double)) : NULL;
@@ -253,14 +266,28 @@ static void linattn_slice(const double* q, const double* k, const double* v, con
   }
   double* mu = ccq ? (double*)malloc(sizeof(double) * (size_t)dk) : NULL;
   double* qc = (double*)malloc(sizeof(double) * (size_t)dk);
+  double* r = beta ? (double*)malloc(sizeof(double) * (size_t)dv) : NULL;
 
   for (int64_t t = 0; t < N; ++t) {
     const double* qt = q + t * dk;
     const double* kt = k + t * dk;
     const double* vt = v + t * dv;
-    /* state: decay, then add the current outer product */
-    for (int64_t a = 0; a < dk; ++a)
-      for (int64_t e = 0; e < dv; ++e) S[a * dv + e] = g[t] * S[a * dv + e] + kt[a] * vt[e];
+    if (beta) {
+      /* state: decay, then one gradient step of size beta_t on the error */
+      for (int64_t a = 0; a < dk; ++a)
+        for (int64_t e = 0; e < dv; ++e) S[a * dv + e] *= g[t];
+      for (int64_t e = 0; e < dv; ++e) {
+        double pred = 0.0;
+        for (int64_t a = 0; a < dk; ++a) pred += S[a * dv + e] * kt[a];
+        r[e] = pred - vt[e];
+      }
+      for (int64_t a = 0; a < dk; ++a)
+        for (int64_t e = 0; e < dv; ++e) S[a * dv + e] -= beta[t] * kt[a] * r[e];
+    } else {
+      /* state: decay, then add the current outer product */
+      for (int64_t a = 0; a < dk; ++a)
+        for (int64_t e = 0; e < dv; ++e) S[a * dv + e] = g[t] * S[a * dv + e] + kt[a] * vt[e];
+    }
 
     for (int64_t a = 0; a < dk; ++a) qc[a] = qt[a];
     if (ccq) {
@@ -297,6 +324,7 @@ static void linattn_slice(const double* q, const double* k, const double* v, con
   free(m);
   free(mu);
   free(qc);
+  free(r);
 }
 
 /*
@@ -311,7 +339,7 @@ void oracle_gla_forward(const double* q, const double* k, const double* v, const
   const int64_t ss = dk * dv;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t s = 0; s < BH; ++s)
-    linattn_slice(q + s * N * dk, k + s * N * dk, v + s * N * dv, g + s * N, NULL, 0.0,
+    linattn_slice(q + s * N * dk, k + s * N * dk, v + s * N * dv, g + s * N, NULL, NULL, 0.0,
                   out + s * N * dv, N, dk, dv, 0, 0, st_in ? st_in + s * ss : NULL,
                   st_out ? st_out + s * ss : NULL);
 }
@@ -331,9 +359,47 @@ void oracle_ccq_forward(const double* q, const double* k, const double* v, const
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t s = 0; s < BH; ++s) {
     const int64_t h = s % H;
-    linattn_slice(q + s * N * dk, k + s * N * dk, v + s * N * dv, g + s * N, w + h * dk, b[h],
-                  out + s * N * dv, N, dk, dv, 1, t0, st_in ? st_in + s * ss : NULL,
+    linattn_slice(q + s * N * dk, k + s * N * dk, v + s * N * dv, g + s * N, NULL, w + h * dk,
+                  b[h], out + s * N * dv, N, dk, dv, 1, t0, st_in ? st_in + s * ss : NULL,
                   st_out ? st_out + s * ss : NULL);
+  }
+}
+
+/*
+ * Gated delta write rule with the plain read [LIN, key messages + easy
+ * explanation]: beta [B,H,N] is the step size of each token's gradient step.
+ * st_in / st_out as for oracle_gla_forward (S, dk x dv).
+ */
+void oracle_deltanet_forward(const double* q, const double* k, const double* v, const double* g,
+                             const double* beta, double* out, int64_t B, int64_t H, int64_t N,
+                             int64_t dk, int64_t dv, const double* st_in, double* st_out) {
+  int64_t BH = B * H;
+  const int64_t ss = dk * dv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t s = 0; s < BH; ++s)
+    linattn_slice(q + s * N * dk, k + s * N * dk, v + s * N * dv, g + s * N, beta + s * N, NULL,
+                  0.0, out + s * N * dv, N, dk, dv, 0, 0, st_in ? st_in + s * ss : NULL,
+                  st_out ? st_out + s * ss : NULL);
+}
+
+/*
+ * The CCQ read over the gated delta write rule [CCQ, integration: the read
+ * attaches to any write rule; Gated DeltaNet is the second backbone the page
+ * names]. State [S | M | m] and t0 as for oracle_ccq_forward.
+ */
+void oracle_ccq_deltanet_forward(const double* q, const double* k, const double* v,
+                                 const double* g, const double* beta, const double* w,
+                                 const double* b, double* out, int64_t B, int64_t H, int64_t N,
+                                 int64_t dk, int64_t dv, int64_t t0, const double* st_in,
+                                 double* st_out) {
+  int64_t BH = B * H;
+  const int64_t ss = dk * dv + dk * dk + dk;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t s = 0; s < BH; ++s) {
+    const int64_t h = s % H;
+    linattn_slice(q + s * N * dk, k + s * N * dk, v + s * N * dv, g + s * N, beta + s * N,
+                  w + h * dk, b[h], out + s * N * dv, N, dk, dv, 1, t0,
+                  st_in ? st_in + s * ss : NULL, st_out ? st_out + s * ss : NULL);
   }
 }
 

@@ -545,10 +545,203 @@ def pin_ccq_backward(orc):
         assert relerr(gx, num) < 1e-7, ("gradient", idx, relerr(gx, num))
 
 
+# ---------------------------------------------------------- gated delta rule
+
+
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _deltanet_case(rng, B=1, H=2, N=30, dk=5, dv=3, unit=True):
+    q = rng.standard_normal((B, H, N, dk))
+    k = rng.standard_normal((B, H, N, dk))
+    k = _unit(k) if unit else k
+    v = rng.standard_normal((B, H, N, dv))
+    g = rng.uniform(0.3, 1.0, (B, H, N))
+    beta = rng.uniform(0.0, 1.0, (B, H, N))
+    return q, k, v, g, beta
+
+
+def pin_deltanet_gradient_step(orc):
+    """One token from a random state: the new state is the decayed state minus
+    beta times the gradient of 1/2 ||S^T k - v||^2 there. The gradient is
+    taken by central differences of that loss (exact for a quadratic up to
+    rounding), with dk != dv and a key of arbitrary norm."""
+    rng = _rng(401)
+    dk, dv = 5, 3
+    for trial in range(3):
+        s_in = rng.standard_normal((1, 1, dk * dv))
+        q = rng.standard_normal((1, 1, 1, dk))
+        k = rng.standard_normal((1, 1, 1, dk)) * (0.5 + trial)
+        v = rng.standard_normal((1, 1, 1, dv))
+        g = rng.uniform(0.2, 1.0, (1, 1, 1))
+        beta = rng.uniform(0.1, 1.0, (1, 1, 1))
+        out, s_out = orc.deltanet_forward(q, k, v, g, beta, state_in=s_in, return_state=True)
+        kk, vv = k[0, 0, 0], v[0, 0, 0]
+        loss = lambda S: 0.5 * np.sum((S.T @ kk - vv) ** 2)
+        S1 = g[0, 0, 0] * s_in.reshape(dk, dv)
+        grad = np.empty((dk, dv))
+        h = 1e-3
+        for a in range(dk):
+            for e in range(dv):
+                E = np.zeros((dk, dv))
+                E[a, e] = h
+                grad[a, e] = (loss(S1 + E) - loss(S1 - E)) / (2 * h)
+        expect = S1 - beta[0, 0, 0] * grad
+        assert relerr(s_out.reshape(dk, dv), expect) < 1e-9, trial
+        assert relerr(out[0, 0, 0], expect.T @ q[0, 0, 0]) < 1e-9, trial
+
+
+def pin_deltanet_orthogonal_keys(orc):
+    """Orthonormal keys never interfere: the error term S^T k_t is zero, so the
+    delta rule writes beta_t v_t, which is gated linear attention with values
+    beta v. CCQ on it likewise equals CCQ on gated linear attention."""
+    rng = _rng(402)
+    B, H, N, dk, dv = 1, 2, 6, 8, 3
+    q, _, v, g, beta = _deltanet_case(rng, B, H, N, dk, dv)
+    k = np.empty((B, H, N, dk))
+    for h in range(H):
+        basis, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+        k[0, h] = basis[:N]
+    bv = beta[..., None] * v
+    assert relerr(orc.deltanet_forward(q, k, v, g, beta), orc.gla_forward(q, k, bv, g)) < 1e-12
+    w = rng.standard_normal((H, dk)) / np.sqrt(dk)
+    b = np.array([1.0, -0.5])
+    assert relerr(orc.ccq_deltanet_forward(q, k, v, g, beta, w, b),
+                  orc.ccq_forward(q, k, bv, g, w, b)) < 1e-12
+    # non-orthogonal keys: the two differ
+    q, k, v, g, beta = _deltanet_case(rng, B, H, N, dk, dv)
+    assert relerr(orc.deltanet_forward(q, k, v, g, beta),
+                  orc.gla_forward(q, k, beta[..., None] * v, g)) > 1e-2
+
+
+def pin_deltanet_exact_recall(orc):
+    """With a unit key and beta = 1 the step overwrites exactly: right after the
+    write, reading with q = k returns v, whatever the history and decay."""
+    rng = _rng(403)
+    B, H, N, dk, dv = 1, 1, 40, 6, 4
+    q, k, v, g, beta = _deltanet_case(rng, B, H, N, dk, dv)
+    s_in = rng.standard_normal((B, H, dk * dv))
+    sel = [3, 17, 18, 39]
+    for t in sel:
+        beta[0, 0, t] = 1.0
+        q[0, 0, t] = k[0, 0, t]
+    out = orc.deltanet_forward(q, k, v, g, beta, state_in=s_in)
+    for t in sel:
+        assert np.max(np.abs(out[0, 0, t] - v[0, 0, t])) < 1e-12, t
+    # and with beta < 1 the recall is only partial
+    beta[0, 0, sel] = 0.5
+    out = orc.deltanet_forward(q, k, v, g, beta, state_in=s_in)
+    assert np.max(np.abs(out[0, 0, sel] - v[0, 0, sel])) > 1e-2
+
+
+def pin_deltanet_beta_zero(orc):
+    """beta = 0 writes nothing: the state only decays, o_t = (prod_{s<=t} g_s) S_0^T q_t."""
+    rng = _rng(404)
+    B, H, N, dk, dv = 1, 2, 12, 4, 5
+    q, k, v, g, _ = _deltanet_case(rng, B, H, N, dk, dv)
+    s_in = rng.standard_normal((B, H, dk * dv))
+    out, s_out = orc.deltanet_forward(q, k, v, g, np.zeros((B, H, N)), state_in=s_in, return_state=True)
+    for h in range(H):
+        S0 = s_in[0, h].reshape(dk, dv)
+        dec = np.cumprod(g[0, h])
+        assert relerr(out[0, h], dec[:, None] * (q[0, h] @ S0)) < 1e-13
+        assert relerr(s_out[0, h], dec[-1] * s_in[0, h]) < 1e-13
+    assert np.all(orc.deltanet_forward(q, k, v, g, np.zeros((B, H, N))) == 0.0)
+
+
+def numpy_deltanet_chunkwise(q, k, v, g, beta, C):
+    """The chunk form used by the GPU kernel, derived from the recurrence. The
+    step is S_r = g_r S_{r-1} + k_r u_r^T with the pseudo-value u_r = beta_r (v_r
+    - g_r S_{r-1}^T k_r), so a chunk is decayed linear attention with values U;
+    unrolling g_r S_{r-1} inside the chunk gives (I + A) U = diag(beta) V
+    - diag(beta gamma) K S_0, A_rj = beta_r (gamma_r / gamma_j) (k_r . k_j) for
+    j < r, gamma the running product of g inside the chunk, S_0 the state at the
+    chunk start."""
+    N, dk = k.shape
+    S = np.zeros((dk, v.shape[1]))
+    out = np.zeros(v.shape)
+    for c0 in range(0, N, C):
+        sl = slice(c0, min(c0 + C, N))
+        Q, K, V, bb = q[sl], k[sl], v[sl], beta[sl]
+        gam = np.cumprod(g[sl])
+        ratio = gam[:, None] / gam[None, :]
+        L = len(gam)
+        A = np.tril(bb[:, None] * ratio * (K @ K.T), -1)
+        T = np.linalg.inv(np.eye(L) + A)
+        W = T @ ((bb * gam)[:, None] * K)
+        U = T @ (bb[:, None] * V) - W @ S
+        P = np.tril(ratio * (Q @ K.T))
+        out[sl] = gam[:, None] * (Q @ S) + P @ U
+        S = gam[-1] * S + K.T @ ((gam[-1] / gam)[:, None] * U)
+    return out
+
+
+def pin_deltanet_chunkwise(orc):
+    rng = _rng(405)
+    q, k, v, g, beta = _deltanet_case(rng, 1, 2, 70, 6, 4)
+    rec = orc.deltanet_forward(q, k, v, g, beta)
+    for h in range(2):
+        for C in (1, 7, 16, 64):
+            got = numpy_deltanet_chunkwise(q[0, h], k[0, h], v[0, h], g[0, h], beta[0, h], C)
+            assert relerr(got, rec[0, h]) < 1e-11, (h, C)
+
+
+def pin_deltanet_state(orc):
+    """Continuing from the state after a prefix gives the rows of the whole
+    sequence (plain and CCQ read; the CCQ count t0 carried)."""
+    rng = _rng(406)
+    B, H, N, dk, dv, n1 = 1, 2, 33, 4, 3, 14
+    q, k, v, g, beta = _deltanet_case(rng, B, H, N, dk, dv)
+    full = orc.deltanet_forward(q, k, v, g, beta)
+    a, st = orc.deltanet_forward(q[:, :, :n1], k[:, :, :n1], v[:, :, :n1], g[:, :, :n1], beta[:, :, :n1],
+                                 return_state=True)
+    b = orc.deltanet_forward(q[:, :, n1:], k[:, :, n1:], v[:, :, n1:], g[:, :, n1:], beta[:, :, n1:],
+                             state_in=st)
+    assert relerr(np.concatenate([a, b], axis=2), full) < 1e-12
+    w = rng.standard_normal((H, dk)) / np.sqrt(dk)
+    bl = np.array([0.5, 2.0])
+    full = orc.ccq_deltanet_forward(q, k, v, g, beta, w, bl)
+    a, st = orc.ccq_deltanet_forward(q[:, :, :n1], k[:, :, :n1], v[:, :, :n1], g[:, :, :n1],
+                                     beta[:, :, :n1], w, bl, return_state=True)
+    b = orc.ccq_deltanet_forward(q[:, :, n1:], k[:, :, n1:], v[:, :, n1:], g[:, :, n1:], beta[:, :, n1:],
+                                 w, bl, t0=n1, state_in=st)
+    assert relerr(np.concatenate([a, b], axis=2), full) < 1e-12
+
+
+def pin_ccq_deltanet_reductions(orc):
+    """Gate closed (lambda = 0): CCQ over the delta rule is the plain delta
+    rule. The read's correction is the CCQ one: with the delta rule's state
+    S_t taken from the oracle's own plain run, o_t = S_t^T (q_t - lambda_t
+    Cov_{<=t}[k] q_t) with numpy.cov(bias=True)."""
+    rng = _rng(407)
+    B, H, N, dk, dv = 1, 2, 20, 4, 3
+    q, k, v, g, beta = _deltanet_case(rng, B, H, N, dk, dv, unit=False)
+    k = k * 0.5 + 0.3
+    w = rng.standard_normal((H, dk)) / np.sqrt(dk)
+    plain = orc.deltanet_forward(q, k, v, g, beta)
+    assert relerr(orc.ccq_deltanet_forward(q, k, v, g, beta, w, np.full(H, -1e4)), plain) < 1e-14
+    bl = np.array([1.0, 2.5])
+    got = orc.ccq_deltanet_forward(q, k, v, g, beta, w, bl)
+    for h in range(H):
+        for t in range(N):
+            _, st = orc.deltanet_forward(q[:, h:h + 1, :t + 1], k[:, h:h + 1, :t + 1], v[:, h:h + 1, :t + 1],
+                                         g[:, h:h + 1, :t + 1], beta[:, h:h + 1, :t + 1], return_state=True)
+            S = st.reshape(dk, dv)
+            kk = k[0, h, :t + 1]
+            sig = np.cov(kk.T, bias=True).reshape(dk, dk) if t > 0 else np.zeros((dk, dk))
+            lam = 1.0 / (1.0 + np.exp(-(w[h] @ q[0, h, t] + bl[h])))
+            ref = S.T @ (q[0, h, t] - lam * sig @ q[0, h, t])
+            assert relerr(got[0, h, t], ref) < 1e-11, (h, t)
+    assert relerr(got, plain) > 1e-2
+
+
 ALL_PINS = [
     pin_gamma_scipy, pin_gma_brute_numpy, pin_gma_k1_closed_form, pin_gma_identical_components,
     pin_gma_permutation, pin_gma_prefix, pin_gma_affinity_structure, pin_gma_golden,
     pin_gla_brute, pin_gla_chunkwise, pin_ccq_numpy_cov, pin_cov_is_logpartition_hessian,
     pin_ccq_reductions, pin_ccq_chunkwise, pin_ccq_golden, pin_gma_state, pin_gla_state,
     pin_ccq_state, pin_glv, pin_gla_backward, pin_gma_backward, pin_ccq_backward,
+    pin_deltanet_gradient_step, pin_deltanet_orthogonal_keys, pin_deltanet_exact_recall,
+    pin_deltanet_beta_zero, pin_deltanet_chunkwise, pin_deltanet_state, pin_ccq_deltanet_reductions,
 ]

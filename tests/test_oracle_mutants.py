@@ -44,6 +44,16 @@ MUTANTS = [
     ("chunk_intra_decay_off_by_one", "for (int64_t s = j + 1; s <= i; ++s) dec *= g[s];",
      "for (int64_t s = j; s <= i; ++s) dec *= g[s];"),
     ("chunk_inter_decay_missing", "out[i * dv + e] = decay_in * acc;", "out[i * dv + e] = acc;"),
+    ("delta_error_sign", "r[e] = pred - vt[e];", "r[e] = vt[e] - pred;"),
+    ("delta_no_decay", "for (int64_t e = 0; e < dv; ++e) S[a * dv + e] *= g[t];", ""),
+    ("delta_error_from_undecayed_state", "pred += S[a * dv + e] * kt[a];", "pred += S[a * dv + e] / g[t] * kt[a];"),
+    ("delta_transposed_prediction", "pred += S[a * dv + e] * kt[a];", "pred += S[e * dv + a % dv] * kt[a];"),
+    ("delta_beta_on_value_only", "S[a * dv + e] -= beta[t] * kt[a] * r[e];",
+     "S[a * dv + e] -= kt[a] * (r[e] + (1.0 - beta[t]) * vt[e]);"),
+    ("delta_beta_squared", "S[a * dv + e] -= beta[t] * kt[a] * r[e];",
+     "S[a * dv + e] -= beta[t] * beta[t] * kt[a] * r[e];"),
+    ("delta_plain_write", "  if (beta) {\n      /* state: decay, then one gradient step",
+     "  if (0) {\n      /* state: decay, then one gradient step"),
 ]
 
 
