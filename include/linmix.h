@@ -20,6 +20,16 @@
  *                         decay gates, chunkwise-parallel form).
  *  linattn_vec_forward    The same with one decay per key feature,
  *                         S_t = diag(g_t) S_{t-1} + k_t v_t^T.
+ *  deltanet_chunk_forward The gated delta write rule: S_t = g_t S_{t-1} -
+ *                         beta_t k_t (g_t S_{t-1}^T k_t - v_t)^T, o_t = S_t^T q_t.
+ *                         Source: allinfo.ai.kr linear attention post, "Key
+ *                         messages" and "Easy explanation" (the update as one
+ *                         gradient step on a squared key-to-value error; the
+ *                         delta rule overwrites the value bound to a key; decay
+ *                         gates forget).
+ *  ccq_deltanet_forward   The CCQ read below over that write rule ("Don't Read
+ *                         Everything", section 2 Method, integration: the read
+ *                         does not depend on the write rule).
  *  ccq_forward            The same state read with the curvature-conditioned
  *                         query q_clean = (I - lambda_t Sigma_t) q_t, with
  *                         Sigma_t the running key covariance (weights 1/t,
@@ -33,7 +43,8 @@
  * nothing from the past but a fixed-size state per (b, h), so a sequence can
  * be continued in a later call:
  *  gma_forward_state, linattn_chunk_forward_state, ccq_forward_state,
- *  linattn_vec_forward_state
+ *  linattn_vec_forward_state, deltanet_forward_state,
+ *  ccq_deltanet_forward_state
  *                         the forwards above, starting from a caller's state
  *                         (optional) and writing the state after the last
  *                         token (optional).
@@ -102,7 +113,7 @@
 extern "C" {
 #endif
 
-#define LM_ABI_VERSION 4
+#define LM_ABI_VERSION 5
 
 typedef enum {
   LM_OK = 0,
@@ -173,6 +184,48 @@ int ccq_forward(const void* q, const void* k, const void* v, const float* g,
                 const float* w_lambda, const float* b_lambda, void* out, int64_t B, int64_t H,
                 int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gated delta rule (chunkwise), plain read.
+ *   q, k  [B,H,N,dk] (dtype);  v [B,H,N,dv] (dtype)
+ *   g     [B,H,N] per-token decay (float32), expected in (0, 1]; decays below
+ *         2^-126 act as 2^-126
+ *   beta  [B,H,N] per-token step size (float32), expected in [0, 1]; with keys
+ *         of unit norm the step never amplifies the state
+ *   out   [B,H,N,dv] o_t = S_t^T q_t, S_t = g_t S_{t-1} - beta_t k_t (g_t
+ *         S_{t-1}^T k_t - v_t)^T, S_0 = 0 (one gradient step of size beta_t on
+ *         1/2 ||S^T k_t - v_t||^2 after the decay)
+ *   chunk 64 is implemented
+ *   segments is accepted and has no effect: the state passes through every
+ *         chunk of a sequence in order (the columns of S are what is split
+ *         across workgroups: B*H*dv/32 of them).
+ * Workspace: deltanet_workspace_bytes returns 0 (workspace may be NULL).
+ * Implemented shapes: dk == dv in {32, 64, 128} for bf16, {32, 64} for
+ * float32; any N >= 1.
+ */
+size_t deltanet_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                                int64_t chunk, int dtype, int64_t segments);
+int deltanet_chunk_forward(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, void* out, int64_t B, int64_t H, int64_t N,
+                           int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The CCQ read over the gated delta rule: o_t = S_t^T (q_t - lambda_t Sigma_t
+ * q_t), with S_t as for deltanet_chunk_forward and lambda_t, Sigma_t as for
+ * ccq_forward (w_lambda [H,dk], b_lambda [H], float32).
+ * Workspace (ccq_deltanet_workspace_bytes): the clean queries (B*H*N*dk
+ * elements of dtype) plus the running key sums of each segment of the
+ * clean-query pass; segments (0 = automatic) splits that pass only.
+ * Implemented shapes: as for deltanet_chunk_forward.
+ */
+size_t ccq_deltanet_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                                    int64_t chunk, int dtype, int64_t segments);
+int ccq_deltanet_forward(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* w_lambda, const float* b_lambda,
+                         void* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                         int64_t chunk, int dtype, int64_t segments, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * Decayed linear attention with one decay per key feature (chunkwise).
@@ -321,6 +374,20 @@ int ccq_forward_state(const void* q, const void* k, const void* v, const float* 
                       int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
                       int64_t segments, int64_t t_in, const float* state_in, float* state_out,
                       void* workspace, size_t workspace_bytes, void* stream);
+/* Gated delta rule on a carried state: S [B,H,dk*dv] (the GLA layout), plain
+ * read; and the CCQ read on it with the CCQ layout [S | M | m] and t_in.
+ * Workspaces from deltanet_workspace_bytes / ccq_deltanet_workspace_bytes. */
+int deltanet_forward_state(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, void* out, int64_t B, int64_t H, int64_t N,
+                           int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
+                           const float* state_in, float* state_out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+int ccq_deltanet_forward_state(const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* w_lambda, const float* b_lambda,
+                               void* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                               int64_t chunk, int dtype, int64_t segments, int64_t t_in,
+                               const float* state_in, float* state_out, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * gma_forward without a workspace argument, for callers that cannot allocate

@@ -68,6 +68,14 @@ _SIGS = {
     "ccq_backward": ([_P] * 13 + [_I64] * 6 + [ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "gma_backward": ([_P] * 13 + [_I64] * 6 + [ctypes.c_int, ctypes.c_float, ctypes.c_int, _P, ctypes.c_size_t, _P],
                      ctypes.c_int),
+    "deltanet_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
+    "deltanet_chunk_forward": ([_P] * 6 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "deltanet_forward_state": ([_P] * 6 + [_I64] * 6 + [ctypes.c_int, _I64, _P, _P, _P, ctypes.c_size_t, _P],
+                               ctypes.c_int),
+    "ccq_deltanet_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
+    "ccq_deltanet_forward": ([_P] * 8 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "ccq_deltanet_forward_state": ([_P] * 8 + [_I64] * 6 + [ctypes.c_int, _I64, _I64, _P, _P, _P, ctypes.c_size_t,
+                                                           _P], ctypes.c_int),
 }
 
 
@@ -239,6 +247,87 @@ def ccq_forward(q, k, v, g, w_lambda, b_lambda, chunk: int = 64, segments: int =
                            ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
     _check("ccq_forward", st)
     return out
+
+
+# ----------------------------------------------------------------------------- gated delta rule
+
+def deltanet_workspace_bytes(B, H, N, dk, dv, chunk=64, dtype=torch.bfloat16, segments=0) -> int:
+    return int(lib().deltanet_workspace_bytes(B, H, N, dk, dv, chunk, _DT[dtype], segments))
+
+
+def ccq_deltanet_workspace_bytes(B, H, N, dk, dv, chunk=64, dtype=torch.bfloat16, segments=0) -> int:
+    return int(lib().ccq_deltanet_workspace_bytes(B, H, N, dk, dv, chunk, _DT[dtype], segments))
+
+
+def _beta(beta, shape) -> int:
+    return _dev(beta, "beta", torch.float32, shape)
+
+
+def deltanet_chunk_forward(q, k, v, g, beta, chunk: int = 64, segments: int = 0,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gated delta rule, plain read. beta [B,H,N] float32 step sizes."""
+    dt = _dtype_code(q)
+    (B, H, N, dk, dv), (pq, pk, pv, pg), out, po = _lin_common(q, k, v, g, out)
+    pb = _beta(beta, (B, H, N))
+    st = lib().deltanet_chunk_forward(pq, pk, pv, pg, pb, po, B, H, N, dk, dv, chunk, dt, segments, None, 0,
+                                      _stream(q.device))
+    _check("deltanet_chunk_forward", st)
+    return out
+
+
+def deltanet_forward_state(q, k, v, g, beta, state_in: Optional[torch.Tensor] = None, chunk: int = 64,
+                           segments: int = 0, out: Optional[torch.Tensor] = None,
+                           state_out: Optional[torch.Tensor] = None):
+    """Gated delta rule continuing from state_in [B,H,dk*dv]. Returns (out, state_out)."""
+    dt = _dtype_code(q)
+    (B, H, N, dk, dv), (pq, pk, pv, pg), out, po = _lin_common(q, k, v, g, out)
+    pb = _beta(beta, (B, H, N))
+    shape = (B, H, linattn_state_size(dk, dv))
+    psi = _state(state_in, "state_in", shape, q.device)
+    state_out = _state_out(state_out, shape, q.device)
+    pso = _state(state_out, "state_out", shape, q.device)
+    st = lib().deltanet_forward_state(pq, pk, pv, pg, pb, po, B, H, N, dk, dv, chunk, dt, segments, psi, pso,
+                                      None, 0, _stream(q.device))
+    _check("deltanet_forward_state", st)
+    return out, state_out
+
+
+def ccq_deltanet_forward(q, k, v, g, beta, w_lambda, b_lambda, chunk: int = 64, segments: int = 0,
+                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """CCQ read over the gated delta rule."""
+    dt = _dtype_code(q)
+    (B, H, N, dk, dv), (pq, pk, pv, pg), out, po = _lin_common(q, k, v, g, out)
+    pb = _beta(beta, (B, H, N))
+    pw = _dev(w_lambda, "w_lambda", torch.float32, (H, dk))
+    pbl = _dev(b_lambda, "b_lambda", torch.float32, (H,))
+    nbytes = ccq_deltanet_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace)
+    st = lib().ccq_deltanet_forward(pq, pk, pv, pg, pb, pw, pbl, po, B, H, N, dk, dv, chunk, dt, segments,
+                                    ws.data_ptr(), nbytes, _stream(q.device))
+    _check("ccq_deltanet_forward", st)
+    return out
+
+
+def ccq_deltanet_forward_state(q, k, v, g, beta, w_lambda, b_lambda, state_in: Optional[torch.Tensor] = None,
+                               t_in: int = 0, chunk: int = 64, segments: int = 0, out: Optional[torch.Tensor] = None,
+                               state_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """CCQ over the gated delta rule continuing from state_in [B,H,dk*dv+dk*dk+dk]
+    that holds t_in tokens. Returns (out, state_out)."""
+    dt = _dtype_code(q)
+    (B, H, N, dk, dv), (pq, pk, pv, pg), out, po = _lin_common(q, k, v, g, out)
+    pb = _beta(beta, (B, H, N))
+    pw = _dev(w_lambda, "w_lambda", torch.float32, (H, dk))
+    pbl = _dev(b_lambda, "b_lambda", torch.float32, (H,))
+    shape = (B, H, ccq_state_size(dk, dv))
+    psi = _state(state_in, "state_in", shape, q.device)
+    state_out = _state_out(state_out, shape, q.device)
+    pso = _state(state_out, "state_out", shape, q.device)
+    nbytes = ccq_deltanet_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace)
+    st = lib().ccq_deltanet_forward_state(pq, pk, pv, pg, pb, pw, pbl, po, B, H, N, dk, dv, chunk, dt, segments,
+                                          int(t_in), psi, pso, ws.data_ptr(), nbytes, _stream(q.device))
+    _check("ccq_deltanet_forward_state", st)
+    return out, state_out
 
 
 # ----------------------------------------------------------------------------- carried state

@@ -237,6 +237,87 @@ int lin_forward(const char* fn, bool ccq, const void* q, const void* k, const vo
   return ok();
 }
 
+// ----------------------------------------------------------------------------- gated delta rule
+
+struct DeltaLayout {
+  size_t qc, agg, total;  // total == 0: no workspace (plain read)
+  Plan plan;
+};
+
+// CCQ: the clean queries (input dtype) and the clean-query pass's segment blocks.
+DeltaLayout delta_layout(int64_t B, int64_t H, int64_t N, int64_t dk, int dtype, bool ccq, int64_t segments) {
+  DeltaLayout L{};
+  L.plan = plan_segments(B * H, N, segments);
+  if (!ccq) return L;
+  L.qc = 0;
+  L.agg = align_up((size_t)B * H * N * dk * esize(dtype));
+  L.total = align_up(L.agg + (size_t)B * H * L.plan.P * lm::cq_state_floats(dk) * 4);
+  return L;
+}
+
+int delta_check_shape(const char* fn, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                      int dtype, int64_t segments) {
+  int st = lin_check_shape(fn, B, H, N, dk, dv, chunk, dtype, segments);
+  if (st != LM_OK) return st;
+  if (dtype == LM_F32 && dk > 64)
+    return fail(LM_EUNSUPPORTED, "%s implements float32 at dk == dv in {32, 64} (got %lld)", fn, (long long)dk);
+  return LM_OK;
+}
+
+int delta_forward(const char* fn, bool ccq, const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, const float* w_lambda, const float* b_lambda, void* out, int64_t B, int64_t H,
+                  int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments, int64_t t_in,
+                  const float* state_in, float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = delta_check_shape(fn, B, H, N, dk, dv, chunk, dtype, segments);
+  if (st != LM_OK) return st;
+  const DeltaLayout L = delta_layout(B, H, N, dk, dtype, ccq, segments);
+  if (!q || !k || !v || !g || !beta || !out || (L.total && !workspace) || (ccq && (!w_lambda || !b_lambda)))
+    return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+      !aligned(g, 4) || !aligned(beta, 4) || (ccq && (!aligned(w_lambda, 4) || !aligned(b_lambda, 4))))
+    return fail(LM_EINVAL, "%s: misaligned pointer (tensors need 16 bytes, parameters 4)", fn);
+  if (workspace_bytes < L.total)
+    return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
+  const size_t es = esize(dtype);
+  const size_t nq = (size_t)B * H * N * dk * es, nv = (size_t)B * H * N * dv * es, nt = (size_t)B * H * N * 4;
+  if (overlap(out, nv, q, nq) || overlap(out, nv, k, nq) || overlap(out, nv, v, nv) || overlap(out, nv, g, nt) ||
+      overlap(out, nv, beta, nt) || overlap(out, nv, workspace, L.total))
+    return fail(LM_EINVAL, "%s: out overlaps an input or the workspace", fn);
+  if (t_in < 0 || (t_in > 0 && !state_in) || t_in > (int64_t(1) << 40))
+    return fail(LM_EINVAL, "%s: t_in counts the tokens held by state_in (0 without one; got %lld)", fn,
+                (long long)t_in);
+  const size_t sfl = (size_t)dk * dv + (ccq ? (size_t)dk * dk + dk : 0);
+  if ((st = check_states(fn, state_in, state_out, (size_t)B * H * sfl * 4, out, nv, workspace, L.total)) != LM_OK)
+    return st;
+  lm::DeltaLaunch La{};
+  La.q = q;
+  La.k = k;
+  La.v = v;
+  La.g = g;
+  La.beta = beta;
+  La.w_lambda = w_lambda;
+  La.b_lambda = b_lambda;
+  La.out = out;
+  La.qc = ccq ? static_cast<char*>(workspace) + L.qc : nullptr;
+  La.agg = ccq ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.agg) : nullptr;
+  La.B = B;
+  La.H = H;
+  La.N = N;
+  La.D = dk;
+  La.dv = dv;
+  La.P = L.plan.P;
+  La.seg_len = L.plan.seg_len;
+  La.bf16 = dtype == LM_BF16;
+  La.ccq = ccq;
+  La.state_in = state_in;
+  La.state_out = state_out;
+  La.sstride = (int64_t)sfl;
+  La.t_in = t_in;
+  hipError_t e = lm::deltanet_launch(La, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 struct VecLayout {
   size_t total;
   Plan plan;
@@ -675,6 +756,50 @@ int ccq_decode_step(const void* q, const void* k, const void* v, const float* g,
   La.t_now = t_prev + 1;
   La.bf16 = dtype == LM_BF16;
   return dec_run(fn, false, true, La, dk, (size_t)dk * dv + (size_t)dk * dk + dk, stream);
+}
+
+size_t deltanet_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
+                                int64_t segments) {
+  if (delta_check_shape("deltanet_chunk_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
+  return delta_layout(B, H, N, dk, dtype, false, segments).total;
+}
+
+int deltanet_chunk_forward(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           void* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                           int dtype, int64_t segments, void* workspace, size_t workspace_bytes, void* stream) {
+  return delta_forward("deltanet_chunk_forward", false, q, k, v, g, beta, nullptr, nullptr, out, B, H, N, dk, dv,
+                       chunk, dtype, segments, 0, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int deltanet_forward_state(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           void* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                           int dtype, int64_t segments, const float* state_in, float* state_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return delta_forward("deltanet_forward_state", false, q, k, v, g, beta, nullptr, nullptr, out, B, H, N, dk, dv,
+                       chunk, dtype, segments, 0, state_in, state_out, workspace, workspace_bytes, stream);
+}
+
+size_t ccq_deltanet_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                                    int dtype, int64_t segments) {
+  if (delta_check_shape("ccq_deltanet_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
+  return delta_layout(B, H, N, dk, dtype, true, segments).total;
+}
+
+int ccq_deltanet_forward(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* w_lambda, const float* b_lambda, void* out, int64_t B, int64_t H, int64_t N,
+                         int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return delta_forward("ccq_deltanet_forward", true, q, k, v, g, beta, w_lambda, b_lambda, out, B, H, N, dk, dv,
+                       chunk, dtype, segments, 0, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int ccq_deltanet_forward_state(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               const float* w_lambda, const float* b_lambda, void* out, int64_t B, int64_t H,
+                               int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
+                               int64_t t_in, const float* state_in, float* state_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return delta_forward("ccq_deltanet_forward_state", true, q, k, v, g, beta, w_lambda, b_lambda, out, B, H, N, dk,
+                       dv, chunk, dtype, segments, t_in, state_in, state_out, workspace, workspace_bytes, stream);
 }
 
 size_t linattn_vec_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,

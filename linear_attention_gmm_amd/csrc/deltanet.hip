@@ -1,0 +1,848 @@
+// deltanet.hip -- chunkwise gated delta rule with the plain or the CCQ read,
+// forward, for gfx950.
+//
+// Method
+//  * Write rule (allinfo.ai.kr post on linear attention, "Key messages" and
+//    "Easy explanation"): the state update is one gradient-descent step on
+//    the squared error of predicting v_t from k_t, the delta rule erases the
+//    value bound to the current key and writes the new one, and a decay gate
+//    forgets. With S (dk x dv), decay g_t in (0, 1] and step size beta_t:
+//        S_t = g_t S_{t-1} - beta_t k_t (g_t S_{t-1}^T k_t - v_t)^T,
+//    read o_t = S_t^T q_t.
+//  * CCQ read ("Don't Read Everything: A Curvature-Conditioned Query for
+//    Linear Attention", section 2 Method, integration): the read uses
+//    q_clean = q_t - lambda_t Sigma_t q_t, which depends on the queries and
+//    keys only, whatever the write rule. The clean-query passes below form it
+//    (running key sums M = sum k k^T, m = sum k, count t), and the chunk pass
+//    then reads with it.
+//
+// Chunk algebra (our own derivation; the pages give no chunk form for this
+// rule). Write the step as S_r = g_r S_{r-1} + k_r u_r^T with the pseudo-value
+// u_r = beta_r (v_r - g_r S_{r-1}^T k_r). Inside a chunk with start state S_0
+// and gamma_r = prod_{s<=r} g_s:
+//   (I + A) U = diag(beta) V - diag(beta gamma) K S_0,
+//   A_rj = beta_r (gamma_r / gamma_j) (k_r . k_j)  for j < r (strictly lower).
+// With T = (I + A)^{-1}, W = T diag(beta gamma) K and Ut = T diag(beta) V
+// (neither depends on S_0):
+//   U   = Ut - W S_0
+//   O   = diag(gamma) Q S_0 + (mask_{j<=r}(gamma_r / gamma_j) o Q K^T) U
+//   S_C = gamma_C S_0 + K^T diag(gamma_C / gamma_j) U.
+// T is formed in fp32: the four 16 x 16 diagonal blocks by forward
+// substitution, then T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj for i - j = 1, 2, 3.
+// Decay ratios are powers of two of differences of the running log2-decay
+// with a non-positive exponent; gamma itself may underflow to 0, which only
+// drops terms of that (negligible) size.
+//
+// MI355X design
+//  * The rule acts on S from the key side only, so the value columns of S
+//    evolve independently: a workgroup of 8 waves owns 32 value columns of
+//    one (b, h) and walks every chunk in order. That is B*H*dv/32 workgroups
+//    (256 at B=4, H=16, dv=128) with no segment pass; the products that do
+//    not depend on S (K K^T, Q K^T, T, W) are recomputed by each column group
+//    (a segment pass for this rule would carry a dense dk x dk transition).
+//    The column groups of one (b, h) are launched gridDim/groups apart, which
+//    for B*H a multiple of 8 puts them on one XCD, sharing its L2 for Q, K.
+//  * Products are 16x16 MFMA tiles (bf16 operands, fp32 accumulation; or
+//    fp32), T in fp32 MFMA. S stays in fp32 registers and is rounded to the
+//    operand type once per chunk for the products that read it.
+//  * The next chunk's Q, K, V, g, beta are loaded into registers while the
+//    current chunk is computed.
+#include "mfma.hpp"
+#include "launch.hpp"
+
+namespace lm {
+namespace gdn {
+
+constexpr int kC = 64;
+constexpr int kNW = 8;
+constexpr int kNT = kNW * 64;
+constexpr int kCG = 32;  // value columns per workgroup
+constexpr float kMinLog2 = -126.f;  // decays below 2^-126 act as 2^-126
+
+// Tiles of the lower triangle of a 4 x 4 tile grid, row by row.
+__device__ __forceinline__ void tri_tile(int u, int& it, int& jt) {
+  it = u >= 6 ? 3 : u >= 3 ? 2 : u >= 1 ? 1 : 0;
+  jt = u - it * (it + 1) / 2;
+}
+
+// k-steps over tokens 0 .. 16 r + 15 (row tile r of a lower-triangular operand).
+template <typename T>
+__device__ __forceinline__ constexpr int tok_steps(int r) {
+  return sizeof(T) == 2 ? r / 2 + 1 : 4 * (r + 1);
+}
+
+template <typename T>
+__device__ __forceinline__ T cvt(float x) {
+  return (T)x;
+}
+
+// A operand, CHAIN order, of a fp32 row-major matrix (row `row`, k-step ks)
+// scaled per k by sc[k], converted to T.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag scaled_row(const float* m, int pitch, int row, int ks,
+                                                            const float* sc) {
+  const int g = lane_id() >> 4;
+  if constexpr (sizeof(T) == 2) {
+    const int k0 = ks * 32 + 4 * g;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(m + row * pitch + k0);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(m + row * pitch + k0 + 16);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sc + k0);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(sc + k0 + 16);
+    bf16x8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = (bf16)(a0[i] * s0[i]);
+      f[4 + i] = (bf16)(a1[i] * s1[i]);
+    }
+    return f;
+  } else {
+    const int k = 16 * (ks >> 2) + 4 * g + (ks & 3);
+    return m[row * pitch + k] * sc[k];
+  }
+}
+
+// A operand of the lower-triangular ones matrix (row i of a 64-row chunk, token
+// k-step ks): 1 where token <= i.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag tri_ones(int ks, int i) {
+  typename Mma<T>::frag f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = chain_k<T>(ks, e) <= i ? (bf16)1.f : (bf16)0.f;
+  } else {
+    f = chain_k<T>(ks, 0) <= i ? 1.f : 0.f;
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag ones_frag() {
+  typename Mma<T>::frag f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)1.f;
+  } else {
+    f = 1.f;
+  }
+  return f;
+}
+
+template <typename T, int D>
+struct Cfg {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int KS = Mma<T>::KS;
+  static constexpr int NKD = D / KS;  // k-steps over features
+  static constexpr int NKC = kC / KS;  // k-steps over a chunk's tokens
+  static constexpr int PAD = ES == 2 ? 8 : 4;
+  // pitches (elements)
+  static constexpr int PQ = D + PAD;    // Q, K, W rows
+  static constexpr int PV = kCG + PAD;  // V, S, U rows
+  static constexpr int PP = kC + PAD;   // P rows
+  static constexpr int PA = kC + 4;     // A, T rows (fp32)
+  // byte offsets
+  static constexpr int o_q = 0;
+  static constexpr int o_k = o_q + kC * PQ * ES;
+  static constexpr int o_w = o_k + kC * PQ * ES;
+  static constexpr int o_v = o_w + kC * PQ * ES;
+  static constexpr int o_s = o_v + kC * PV * ES;
+  static constexpr int o_u = o_s + D * PV * ES;
+  static constexpr int o_ud = o_u + kC * PV * ES;
+  static constexpr int o_p = o_ud + kC * PV * ES;
+  static constexpr int o_a = o_p + kC * PP * ES;
+  static constexpr int o_t = o_a + kC * PA * 4;
+  static constexpr int o_row = o_t + kC * PA * 4;  // [5][64] f32 per-token scalars
+  static constexpr int bytes = o_row + 5 * kC * 4;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static_assert(o_k % 16 == 0 && o_w % 16 == 0 && o_v % 16 == 0 && o_s % 16 == 0 && o_u % 16 == 0 &&
+                    o_ud % 16 == 0 && o_p % 16 == 0 && o_a % 16 == 0 && o_t % 16 == 0 && o_row % 16 == 0,
+                "16-byte aligned regions");
+  // 16-byte vectors per chunk of Q (or K), and per thread
+  static constexpr int VR = D * ES / 16;
+  static constexpr int NQ = (kC * VR + kNT - 1) / kNT;
+  static constexpr int VRV = kCG * ES / 16;
+  static constexpr int NVV = kC * VRV;  // V vectors per chunk (<= kNT)
+  static_assert(NVV <= kNT, "one V vector per thread");
+  // S tiles (16 x 16) of the column group and per wave
+  static constexpr int NST = 2 * D / 16;
+  static constexpr int SPW = (NST + kNW - 1) / kNW;
+};
+
+struct Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  void* out;
+  const float* state_in;  // optional: S at state_in + bh * sstride
+  float* state_out;
+  int64_t sstride;
+  const float* mfinal;  // CCQ with state_out: running sums after the last token,
+                        // block P - 1 of the clean-query pass's workspace
+  int P, sfl;
+  int64_t N;
+  int BH;
+  int dv;
+};
+
+// Registers holding one chunk's inputs between their load and their LDS store.
+template <typename T, int D>
+struct Pref {
+  typedef Cfg<T, D> C;
+  uint4 q[C::NQ], k[C::NQ], v;
+  float g, b;
+  __device__ __forceinline__ void load(const Args& a, int bh, int cg, int64_t c0) {
+    const int tid = threadIdx.x;
+    const char* qb = static_cast<const char*>(a.q) + (size_t)bh * a.N * D * C::ES;
+    const char* kb = static_cast<const char*>(a.k) + (size_t)bh * a.N * D * C::ES;
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) {
+      const int p = tid + i * kNT;
+      const int row = p / C::VR, cv = p % C::VR;
+      const bool ok = p < kC * C::VR && c0 + row < a.N;
+      const size_t off = (size_t)(c0 + row) * D * C::ES + (size_t)cv * 16;
+      q[i] = ok ? *reinterpret_cast<const uint4*>(qb + off) : make_uint4(0, 0, 0, 0);
+      k[i] = ok ? *reinterpret_cast<const uint4*>(kb + off) : make_uint4(0, 0, 0, 0);
+    }
+    {
+      const int row = tid / C::VRV, cv = tid % C::VRV;
+      const bool ok = tid < C::NVV && c0 + row < a.N;
+      const char* vb = static_cast<const char*>(a.v) + ((size_t)bh * a.N + c0 + row) * a.dv * C::ES +
+                       (size_t)cg * kCG * C::ES + (size_t)cv * 16;
+      v = ok ? *reinterpret_cast<const uint4*>(vb) : make_uint4(0, 0, 0, 0);
+    }
+    const bool okt = tid < kC && c0 + tid < a.N;
+    g = okt ? a.g[(size_t)bh * a.N + c0 + tid] : 1.f;
+    b = okt ? a.beta[(size_t)bh * a.N + c0 + tid] : 0.f;
+  }
+  __device__ __forceinline__ void store(char* sm) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) {
+      const int p = tid + i * kNT;
+      if (p < kC * C::VR) {
+        const int row = p / C::VR, cv = p % C::VR;
+        *reinterpret_cast<uint4*>(sm + C::o_q + row * C::PQ * C::ES + cv * 16) = q[i];
+        *reinterpret_cast<uint4*>(sm + C::o_k + row * C::PQ * C::ES + cv * 16) = k[i];
+      }
+    }
+    if (tid < C::NVV) {
+      const int row = tid / C::VRV, cv = tid % C::VRV;
+      *reinterpret_cast<uint4*>(sm + C::o_v + row * C::PV * C::ES + cv * 16) = v;
+    }
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kNT) void gdn_kernel(Args a) {
+  typedef Cfg<T, D> C;
+  typedef Mma<T> M;
+  __shared__ __attribute__((aligned(16))) char sm[C::bytes];
+  T* sQ = reinterpret_cast<T*>(sm + C::o_q);
+  T* sK = reinterpret_cast<T*>(sm + C::o_k);
+  T* sW = reinterpret_cast<T*>(sm + C::o_w);
+  T* sV = reinterpret_cast<T*>(sm + C::o_v);
+  T* sS = reinterpret_cast<T*>(sm + C::o_s);
+  T* sU = reinterpret_cast<T*>(sm + C::o_u);
+  T* sUd = reinterpret_cast<T*>(sm + C::o_ud);
+  T* sP = reinterpret_cast<T*>(sm + C::o_p);
+  float* sA = reinterpret_cast<float*>(sm + C::o_a);
+  float* sT = reinterpret_cast<float*>(sm + C::o_t);
+  float* sL = reinterpret_cast<float*>(sm + C::o_row);  // running log2 decay
+  float* sBt = sL + kC;                                  // beta
+  float* sSw = sL + 2 * kC;                              // beta_j gamma_j
+  float* sDc = sL + 3 * kC;                              // gamma_C / gamma_j
+  float* sGm = sL + 4 * kC;                              // gamma_j
+
+  const int bh = blockIdx.x % a.BH, cg = blockIdx.x / a.BH;
+  const int w = wave_id(), l = lane_id(), g = l >> 4, l16 = l & 15;
+  const int tid = threadIdx.x;
+
+  // upper tiles of P and T stay zero (read by the k-steps that straddle the diagonal)
+  for (int i = tid; i < kC * kC; i += kNT) {
+    const int r = i / kC, c = i % kC;
+    if ((c >> 4) > (r >> 4)) {
+      sP[r * C::PP + c] = cvt<T>(0.f);
+      sT[r * C::PA + c] = 0.f;
+    }
+  }
+
+  // this wave's S tiles: t = w + kNW j, tile (a, c) = (t / 2, t % 2)
+  f32x4 St[C::SPW];
+#pragma unroll
+  for (int j = 0; j < C::SPW; ++j) {
+    St[j] = zero4();
+    const int t = w + kNW * j;
+    if (t < C::NST && a.state_in) {
+      const float* src = a.state_in + (size_t)bh * a.sstride;
+      const int ra = 16 * (t >> 1), col = cg * kCG + 16 * (t & 1) + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) St[j][e] = src[(size_t)(ra + 4 * g + e) * a.dv + col];
+    }
+  }
+
+  Pref<T, D> pf;
+  pf.load(a, bh, cg, 0);
+  const int64_t nch = (a.N + kC - 1) / kC;
+  const int r_own = w >> 1, c_own = w & 1;  // the (row tile, column tile) of U and O this wave owns
+  T* outp = static_cast<T*>(a.out);
+
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    const int64_t c0 = ch * kC;
+    // ---- inputs to LDS, the state to its operand copy, next chunk's loads
+    pf.store(sm);
+#pragma unroll
+    for (int j = 0; j < C::SPW; ++j) {
+      const int t = w + kNW * j;
+      if (t < C::NST) {
+        const int ra = 16 * (t >> 1), col = 16 * (t & 1) + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sS[(ra + 4 * g + e) * C::PV + col] = cvt<T>(St[j][e]);
+      }
+    }
+    if (w == 0) {
+      const float lg = fmaxf(__builtin_amdgcn_logf(pf.g), kMinLog2);  // log2
+      const float lr = wave_scan_incl(lg);
+      const float lc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lr), 63));
+      const float gm = fast_exp2(lr);
+      sL[l] = lr;
+      sBt[l] = pf.b;
+      sSw[l] = pf.b * gm;
+      sDc[l] = fast_exp2(lc - lr);
+      sGm[l] = gm;
+    }
+    if (ch + 1 < nch) pf.load(a, bh, cg, c0 + kC);
+    __syncthreads();
+
+    // ---- score tiles: A = strictly lower beta-scaled decayed K K^T (fp32),
+    //      P = lower decayed Q K^T (operand type)
+    for (int t = w; t < 20; t += kNW) {
+      const bool kk = t < 10;
+      int it, jt;
+      tri_tile(kk ? t : t - 10, it, jt);
+      const T* lhs = kk ? sK : sQ;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < C::NKD; ++ks)
+        acc = M::mma(ld_kc_chain(lhs, C::PQ, 16 * it + l16, ks), ld_kc_chain(sK, C::PQ, 16 * jt + l16, ks), acc);
+      const int j = 16 * jt + l16;
+      const float lj = sL[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * it + 4 * g + e;
+        const float f = fast_exp2(fminf(sL[i] - lj, 0.f));
+        if (kk)
+          sA[i * C::PA + j] = j < i ? sBt[i] * f * acc[e] : 0.f;
+        else
+          sP[i * C::PP + j] = cvt<T>(j <= i ? f * acc[e] : 0.f);
+      }
+    }
+    __syncthreads();
+
+    // ---- T: diagonal blocks by forward substitution (wave 0, lane group =
+    //      block, lane = column)
+    if (w == 0) {
+      const int b0 = 16 * g, c = l16;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc = r == c ? 1.f : 0.f;
+        const float* arow = sA + (b0 + r) * C::PA + b0;
+#pragma unroll
+        for (int i = 0; i < r; ++i) acc -= arow[i] * x[i];
+        x[r] = acc;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[(b0 + r) * C::PA + b0 + c] = x[r];
+    }
+    __syncthreads();
+    // ---- T: off-diagonal blocks, T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+      if (w < 4 - d) {
+        const int bi = w + d, bj = w;
+        f32x4 X = zero4();
+        for (int m = bj; m < bi; ++m) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            X = Mma<float>::mma(ld_kc_chain(sA + 16 * m, C::PA, 16 * bi + l16, ks),
+                                ld_km_chain(sT + 16 * m * C::PA, C::PA, 16 * bj, ks), X);
+        }
+        f32x4 Y = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) Y = Mma<float>::mma(ld_kc_chain(sT + 16 * bi, C::PA, 16 * bi + l16, ks), X[ks], Y);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sT[(16 * bi + 4 * g + e) * C::PA + 16 * bj + l16] = -Y[e];
+      }
+      __syncthreads();
+    }
+
+    // ---- W = T diag(beta gamma) K (all columns, shared out) and Ut = T
+    //      diag(beta) V (this wave's tile, kept in registers)
+    f32x4 ut = zero4();
+    {
+      const int r = r_own;
+      constexpr int NKT = tok_steps<T>(3);
+      typename M::frag aw[NKT], au[NKT];
+      const int nk = tok_steps<T>(r);
+#pragma unroll
+      for (int ks = 0; ks < NKT; ++ks)
+        if (ks < nk) {
+          aw[ks] = scaled_row<T>(sT, C::PA, 16 * r + l16, ks, sSw);
+          au[ks] = scaled_row<T>(sT, C::PA, 16 * r + l16, ks, sBt);
+        }
+      constexpr int FPW = D / 32;  // W column tiles per wave
+#pragma unroll
+      for (int fi = 0; fi < FPW; ++fi) {
+        const int f = c_own * FPW + fi;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKT; ++ks)
+          if (ks < nk) acc = M::mma(aw[ks], ld_km_chain(sK, C::PQ, 16 * f, ks), acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sW[(16 * r + 4 * g + e) * C::PQ + 16 * f + l16] = cvt<T>(acc[e]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKT; ++ks)
+        if (ks < nk) ut = M::mma(au[ks], ld_km_chain(sV, C::PV, 16 * c_own, ks), ut);
+    }
+    __syncthreads();
+
+    // ---- U = Ut - W S_0 (this wave's tile), to LDS plainly and scaled by
+    //      gamma_C / gamma_j for the state update
+    {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < C::NKD; ++ks)
+        acc = M::mma(ld_kc_chain(sW, C::PQ, 16 * r_own + l16, ks), ld_km_chain(sS, C::PV, 16 * c_own, ks), acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * r_own + 4 * g + e;
+        const float u = ut[e] - acc[e];
+        sU[i * C::PV + 16 * c_own + l16] = cvt<T>(u);
+        sUd[i * C::PV + 16 * c_own + l16] = cvt<T>(u * sDc[i]);
+      }
+    }
+    __syncthreads();
+
+    // ---- O = diag(gamma) Q S_0 + P U (this wave's tile)
+    {
+      f32x4 acc = zero4(), acc2 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < C::NKD; ++ks)
+        acc = M::mma(ld_kc_chain(sQ, C::PQ, 16 * r_own + l16, ks), ld_km_chain(sS, C::PV, 16 * c_own, ks), acc);
+      const int nk = tok_steps<T>(r_own);
+      for (int ks = 0; ks < nk; ++ks)
+        acc2 = M::mma(ld_kc_chain(sP, C::PP, 16 * r_own + l16, ks), ld_km_chain(sU, C::PV, 16 * c_own, ks), acc2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * r_own + 4 * g + e;
+        if (c0 + i < a.N)
+          outp[((size_t)bh * a.N + c0 + i) * a.dv + cg * kCG + 16 * c_own + l16] = cvt<T>(acc[e] * sGm[i] + acc2[e]);
+      }
+    }
+    // ---- S_C = gamma_C S_0 + K^T diag(gamma_C / gamma_j) U (this wave's tiles)
+    {
+      const float gc = sGm[kC - 1];
+#pragma unroll
+      for (int j = 0; j < C::SPW; ++j) {
+        const int t = w + kNW * j;
+        if (t < C::NST) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int ks = 0; ks < C::NKC; ++ks)
+            acc = M::mma(ld_km_chain(sK, C::PQ, 16 * (t >> 1), ks), ld_km_chain(sUd, C::PV, 16 * (t & 1), ks), acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) St[j][e] = gc * St[j][e] + acc[e];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (a.state_out) {
+    float* dst = a.state_out + (size_t)bh * a.sstride;
+    if (a.mfinal && cg == 0) {
+      const float* src = a.mfinal + ((size_t)bh * a.P + a.P - 1) * a.sfl;
+      for (int i = tid; i < D * D + D; i += kNT) dst[D * a.dv + i] = src[i];
+    }
+#pragma unroll
+    for (int j = 0; j < C::SPW; ++j) {
+      const int t = w + kNW * j;
+      if (t < C::NST) {
+        const int ra = 16 * (t >> 1), col = cg * kCG + 16 * (t & 1) + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(size_t)(ra + 4 * g + e) * a.dv + col] = St[j][e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Clean query of the CCQ read: q' = q - lambda_t Sigma_t q_t in the chunk form
+//   delta_i = -alpha_i (M_prev q_i + sum_{j<=i} P_ij k_j)
+//             + beta_i (m_prev + sum_{j<=i} k_j),
+//   alpha_i = lambda_i / t,  beta_i = lambda_i (m_prev . q_i + sum_{j<=i} P_ij) / t^2,
+// P_ij = q_i . k_j rounded once to the operand type (row sums from the rounded
+// values, so that the t = 1 case cancels). M_prev, m_prev are the running sums
+// of k k^T and k before the chunk; t counts tokens from the sequence start.
+// A segment pass sums k k^T and k over each segment; the chunk pass of segment
+// s starts from the sums of the segments before it.
+
+template <typename T, int D>
+struct QCfg {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int KS = Mma<T>::KS;
+  static constexpr int NKD = D / KS;
+  static constexpr int NKC = kC / KS;
+  static constexpr int PAD = ES == 2 ? 8 : 4;
+  static constexpr int PQ = D + PAD;
+  static constexpr int PP = kC + PAD;
+  static constexpr int NCT = D / 16;  // feature tiles
+  static constexpr int o_q = 0;
+  static constexpr int o_k = o_q + kC * PQ * ES;
+  static constexpr int o_dot = o_k + kC * PQ * ES;  // [16][PQ]: w hi, w lo, m hi, m lo, zeros
+  static constexpr int o_p = o_dot + 16 * PQ * ES;
+  static constexpr int o_rd = o_p + kC * PP * ES;    // [64][4] f32 dot results
+  static constexpr int o_ab = o_rd + kC * 4 * 4;     // [2][64] f32 alpha, beta
+  static constexpr int bytes = o_ab + 2 * kC * 4;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static constexpr int VR = D * ES / 16;
+  static constexpr int NQ = (kC * VR + kNT - 1) / kNT;
+  static constexpr int NMT = NCT * NCT;  // M tiles (segment pass: shared out over waves)
+  static constexpr int MPW = (NMT + kNW - 1) / kNW;
+};
+
+struct QArgs {
+  const void* q;
+  const void* k;
+  const float* w_lambda;
+  const float* b_lambda;
+  void* qc;
+  float* agg;  // [BH][P][sfl]: sum k k^T (D x D), sum k (D)
+  const float* state_in;  // optional: [M | m] at state_in + bh * sstride
+  int64_t sstride;
+  bool keep_final;  // the last segment stores its final sums in block P - 1 of agg
+  int64_t N, seg_len, t_in;
+  int H, BH, P, sfl;
+};
+
+// Loads rows [c0, c0 + 64) of X [BH][N][D] into an LDS tile.
+// Rows at or past `limit` read as zero.
+template <typename T, int D>
+__device__ __forceinline__ void load_tile(char* dst, const void* src, int bh, int64_t N, int64_t c0, int64_t limit) {
+  typedef QCfg<T, D> C;
+  const char* base = static_cast<const char*>(src) + (size_t)bh * N * D * C::ES;
+#pragma unroll
+  for (int i = 0; i < C::NQ; ++i) {
+    const int p = threadIdx.x + i * kNT;
+    if (p < kC * C::VR) {
+      const int row = p / C::VR, cv = p % C::VR;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (c0 + row < limit) x = *reinterpret_cast<const uint4*>(base + (size_t)(c0 + row) * D * C::ES + (size_t)cv * 16);
+      *reinterpret_cast<uint4*>(dst + row * C::PQ * C::ES + cv * 16) = x;
+    }
+  }
+}
+
+// Segment pass: sums of k k^T and k over segment blockIdx.x of (b, h) blockIdx.y.
+template <typename T, int D>
+__global__ __launch_bounds__(kNT) void cq_agg_kernel(QArgs a) {
+  typedef QCfg<T, D> C;
+  typedef Mma<T> M;
+  __shared__ __attribute__((aligned(16))) char sm[C::o_dot];
+  T* sK = reinterpret_cast<T*>(sm + C::o_k);
+  const int s = blockIdx.x, bh = blockIdx.y;
+  const int w = wave_id(), l = lane_id(), g = l >> 4, l16 = l & 15, tid = threadIdx.x;
+  const int64_t t0 = (int64_t)s * a.seg_len;
+  const int64_t t1 = t0 + a.seg_len < a.N ? t0 + a.seg_len : a.N;
+  f32x4 acc[C::MPW];
+#pragma unroll
+  for (int j = 0; j < C::MPW; ++j) acc[j] = zero4();
+  float msum = 0.f;
+  for (int64_t c0 = t0; c0 < t1; c0 += kC) {
+    load_tile<T, D>(sm + C::o_k, a.k, bh, a.N, c0, t1);  // rows past the segment end read as zero
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < C::MPW; ++j) {
+      const int t = w + kNW * j;
+      if (t < C::NMT) {
+        const int ra = t % C::NCT, cb = t / C::NCT;
+#pragma unroll
+        for (int ks = 0; ks < C::NKC; ++ks)
+          acc[j] = M::mma(ld_km_chain(sK, C::PQ, 16 * ra, ks), ld_km_chain(sK, C::PQ, 16 * cb, ks), acc[j]);
+      }
+    }
+    if (tid < D)
+      for (int r = 0; r < kC; ++r) msum += to_f32(sK[r * C::PQ + tid]);
+    __syncthreads();
+  }
+  float* dst = a.agg + ((size_t)bh * a.P + s) * a.sfl;
+#pragma unroll
+  for (int j = 0; j < C::MPW; ++j) {
+    const int t = w + kNW * j;
+    if (t < C::NMT) {
+      const int ra = t % C::NCT, cb = t / C::NCT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(16 * ra + 4 * g + e) * D + 16 * cb + l16] = acc[j][e];
+    }
+  }
+  if (tid < D) dst[D * D + tid] = msum;
+}
+
+// Chunk pass: clean queries of segment blockIdx.x of (b, h) blockIdx.y.
+template <typename T, int D>
+__global__ __launch_bounds__(kNT) void cq_kernel(QArgs a) {
+  typedef QCfg<T, D> C;
+  typedef Mma<T> M;
+  __shared__ __attribute__((aligned(16))) char sm[C::bytes];
+  T* sQ = reinterpret_cast<T*>(sm + C::o_q);
+  T* sK = reinterpret_cast<T*>(sm + C::o_k);
+  T* sDot = reinterpret_cast<T*>(sm + C::o_dot);
+  T* sP = reinterpret_cast<T*>(sm + C::o_p);
+  float* sRd = reinterpret_cast<float*>(sm + C::o_rd);
+  float* sAl = reinterpret_cast<float*>(sm + C::o_ab);
+  float* sBe = sAl + kC;
+  const int s = blockIdx.x, bh = blockIdx.y, h = bh % a.H;
+  const int w = wave_id(), l = lane_id(), g = l >> 4, l16 = l & 15, tid = threadIdx.x;
+  const int64_t t0 = (int64_t)s * a.seg_len;
+  const int64_t t1 = t0 + a.seg_len < a.N ? t0 + a.seg_len : a.N;
+  const bool owner = w < C::NCT;  // owns feature tile cw = w of delta, M's columns and m
+  const int cw = w;
+
+  // running sums before the segment: the caller's state plus the segments before it
+  f32x4 Mt[C::NCT];
+  float mv = 0.f;
+#pragma unroll
+  for (int at = 0; at < C::NCT; ++at) Mt[at] = zero4();
+  if (owner) {
+    const int col = 16 * cw + l16;
+    if (a.state_in) {
+      const float* src = a.state_in + (size_t)bh * a.sstride;
+#pragma unroll
+      for (int at = 0; at < C::NCT; ++at)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Mt[at][e] = src[(16 * at + 4 * g + e) * D + col];
+      mv = src[D * D + col];
+    }
+    for (int sp = 0; sp < s; ++sp) {
+      const float* src = a.agg + ((size_t)bh * a.P + sp) * a.sfl;
+#pragma unroll
+      for (int at = 0; at < C::NCT; ++at)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Mt[at][e] += src[(16 * at + 4 * g + e) * D + col];
+      mv += src[D * D + col];
+    }
+  }
+  // gate weights (split into two operand-type terms for bf16) and the key sum
+  for (int i = tid; i < 16 * D; i += kNT) {
+    const int r = i / D, f = i % D;
+    float x = 0.f;
+    if (r == 0 || r == 1) {
+      const float wv = a.w_lambda[(size_t)h * D + f];
+      x = r == 0 ? to_f32(cvt<T>(wv)) : wv - to_f32(cvt<T>(wv));
+    }
+    sDot[r * C::PQ + f] = cvt<T>(x);
+  }
+  for (int i = tid; i < kC * kC; i += kNT) {
+    const int r = i / kC, c = i % kC;
+    if ((c >> 4) > (r >> 4)) sP[r * C::PP + c] = cvt<T>(0.f);
+  }
+  __syncthreads();
+  if (owner && g == 0) {
+    const T hi = cvt<T>(mv);
+    sDot[2 * C::PQ + 16 * cw + l16] = hi;
+    sDot[3 * C::PQ + 16 * cw + l16] = cvt<T>(mv - to_f32(hi));
+  }
+  const float bias = a.b_lambda[h];
+  T* qcp = static_cast<T*>(a.qc);
+
+  for (int64_t c0 = t0; c0 < t1; c0 += kC) {
+    load_tile<T, D>(sm + C::o_q, a.q, bh, a.N, c0, t1);
+    load_tile<T, D>(sm + C::o_k, a.k, bh, a.N, c0, t1);
+    __syncthreads();
+    // ---- raw scores (lower, rounded once) and the gate / key-sum dots
+    for (int t = w; t < 14; t += kNW) {
+      if (t < 10) {
+        int it, jt;
+        tri_tile(t, it, jt);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < C::NKD; ++ks)
+          acc = M::mma(ld_kc_chain(sQ, C::PQ, 16 * it + l16, ks), ld_kc_chain(sK, C::PQ, 16 * jt + l16, ks), acc);
+        const int j = 16 * jt + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * it + 4 * g + e;
+          sP[i * C::PP + j] = cvt<T>(j <= i ? acc[e] : 0.f);
+        }
+      } else {
+        const int r = t - 10;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < C::NKD; ++ks)
+          acc = M::mma(ld_kc_chain(sQ, C::PQ, 16 * r + l16, ks), ld_kc_chain(sDot, C::PQ, l16, ks), acc);
+        if (l16 < 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sRd[(16 * r + 4 * g + e) * 4 + l16] = acc[e];
+        }
+      }
+    }
+    __syncthreads();
+    // ---- per-row gate and coefficients
+    if (w == 0) {
+      const int i = l;
+      float rs = 0.f;
+      for (int j = 0; j < kC; ++j) rs += to_f32(sP[i * C::PP + j]);
+      const float wq = sRd[i * 4 + 0] + sRd[i * 4 + 1];
+      const float mq = sRd[i * 4 + 2] + sRd[i * 4 + 3];
+      const float lam = 1.f / (1.f + __expf(-(wq + bias)));
+      const float tc = (float)(a.t_in + c0 + i + 1);
+      const bool ok = c0 + i < t1;
+      const float al = ok ? lam / tc : 0.f;
+      sAl[i] = al;
+      sBe[i] = ok ? al * (mq + rs) / tc : 0.f;
+    }
+    __syncthreads();
+    // ---- delta for this wave's feature tile, the clean query, the running sums
+    if (owner) {
+      typename M::frag mh[C::NKD], ml[C::NKD];
+#pragma unroll
+      for (int ks = 0; ks < C::NKD; ++ks) {
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = Mt[2 * ks][e], x1 = Mt[2 * ks + 1][e];
+            mh[ks][e] = (bf16)x0;
+            mh[ks][4 + e] = (bf16)x1;
+            ml[ks][e] = (bf16)(x0 - (float)mh[ks][e]);
+            ml[ks][4 + e] = (bf16)(x1 - (float)mh[ks][4 + e]);
+          }
+        } else {
+          mh[ks] = Mt[ks >> 2][ks & 3];
+        }
+      }
+      const int f = 16 * cw + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f32x4 acc = zero4(), z = zero4();
+#pragma unroll
+        for (int ks = 0; ks < C::NKD; ++ks) {
+          const typename M::frag aq = ld_kc_chain(sQ, C::PQ, 16 * r + l16, ks);
+          acc = M::mma(aq, mh[ks], acc);
+          if constexpr (sizeof(T) == 2) acc = M::mma(aq, ml[ks], acc);
+        }
+        const int nk = tok_steps<T>(r);
+        for (int ks = 0; ks < nk; ++ks) {
+          const typename M::frag bk = ld_km_chain(sK, C::PQ, 16 * cw, ks);
+          acc = M::mma(ld_kc_chain(sP, C::PP, 16 * r + l16, ks), bk, acc);
+          z = M::mma(tri_ones<T>(ks, 16 * r + l16), bk, z);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * r + 4 * g + e;
+          if (c0 + i < t1) {
+            const float d = -sAl[i] * acc[e] + sBe[i] * (z[e] + mv);
+            qcp[((size_t)bh * a.N + c0 + i) * D + f] = cvt<T>(to_f32(sQ[i * C::PQ + f]) + d);
+          }
+        }
+      }
+      // running sums over the chunk's keys
+      f32x4 cs = zero4();
+#pragma unroll
+      for (int ks = 0; ks < C::NKC; ++ks) {
+        const typename M::frag bk = ld_km_chain(sK, C::PQ, 16 * cw, ks);
+        cs = M::mma(ones_frag<T>(), bk, cs);
+#pragma unroll
+        for (int at = 0; at < C::NCT; ++at) Mt[at] = M::mma(ld_km_chain(sK, C::PQ, 16 * at, ks), bk, Mt[at]);
+      }
+      mv += cs[0];
+    }
+    __syncthreads();  // all reads of sQ, sK, sP and the key-sum row are done
+    if (owner && g == 0) {
+      const T hi = cvt<T>(mv);
+      sDot[2 * C::PQ + 16 * cw + l16] = hi;
+      sDot[3 * C::PQ + 16 * cw + l16] = cvt<T>(mv - to_f32(hi));
+    }
+  }
+  if (a.keep_final && s == a.P - 1 && owner) {
+    float* dst = a.agg + ((size_t)bh * a.P + s) * a.sfl;  // block P - 1 is not a segment sum
+    const int col = 16 * cw + l16;
+#pragma unroll
+    for (int at = 0; at < C::NCT; ++at)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(16 * at + 4 * g + e) * D + col] = Mt[at][e];
+    if (g == 0) dst[D * D + col] = mv;
+  }
+}
+
+template <typename T, int D>
+hipError_t run(const DeltaLaunch& L, hipStream_t st) {
+  const int BH = (int)(L.B * L.H);
+  if (L.ccq) {
+    QArgs q;
+    q.q = L.q;
+    q.k = L.k;
+    q.w_lambda = L.w_lambda;
+    q.b_lambda = L.b_lambda;
+    q.qc = L.qc;
+    q.agg = L.agg;
+    q.state_in = L.state_in ? L.state_in + L.D * L.dv : nullptr;
+    q.sstride = L.sstride;
+    q.keep_final = L.state_out != nullptr;
+    q.N = L.N;
+    q.seg_len = L.seg_len;
+    q.t_in = L.t_in;
+    q.H = (int)L.H;
+    q.BH = BH;
+    q.P = (int)L.P;
+    q.sfl = (int)cq_state_floats(L.D);
+    if (L.P > 1) {
+      hipLaunchKernelGGL((cq_agg_kernel<T, D>), dim3((unsigned)(L.P - 1), (unsigned)BH), dim3(kNT), 0, st, q);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((cq_kernel<T, D>), dim3((unsigned)L.P, (unsigned)BH), dim3(kNT), 0, st, q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  Args a;
+  a.q = L.ccq ? L.qc : L.q;
+  a.k = L.k;
+  a.v = L.v;
+  a.g = L.g;
+  a.beta = L.beta;
+  a.out = L.out;
+  a.state_in = L.state_in;
+  a.state_out = L.state_out;
+  a.sstride = L.sstride;
+  a.mfinal = L.ccq ? L.agg : nullptr;
+  a.P = (int)L.P;
+  a.sfl = (int)cq_state_floats(L.D);
+  a.N = L.N;
+  a.BH = BH;
+  a.dv = (int)L.dv;
+  const unsigned groups = (unsigned)(BH * (L.dv / kCG));
+  hipLaunchKernelGGL((gdn_kernel<T, D>), dim3(groups), dim3(kNT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdn
+
+hipError_t deltanet_launch(const DeltaLaunch& L, hipStream_t st) {
+  if (L.bf16) {
+    switch (L.D) {
+      case 32: return gdn::run<bf16, 32>(L, st);
+      case 64: return gdn::run<bf16, 64>(L, st);
+      case 128: return gdn::run<bf16, 128>(L, st);
+    }
+  } else {
+    switch (L.D) {
+      case 32: return gdn::run<float, 32>(L, st);
+      case 64: return gdn::run<float, 64>(L, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lm

@@ -67,6 +67,38 @@ struct CcqPipeLaunch {
 };
 hipError_t ccq_pipe_launch(const CcqPipeLaunch& L, hipStream_t st);
 
+// Gated delta rule with the plain or the CCQ read (deltanet.hip). For CCQ a
+// clean-query pass (segment sums, then one chunk pass per segment) writes q'
+// to qc, and the chunk pass reads with it.
+struct DeltaLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* w_lambda;  // CCQ only
+  const float* b_lambda;  // CCQ only
+  void* out;
+  void* qc;    // CCQ: workspace [B,H,N,D] of the input dtype
+  float* agg;  // CCQ: workspace [B*H][P][cq_state_floats(D)]
+  int64_t B, H, N, D, dv;
+  int64_t P, seg_len;  // CCQ: segments of the clean-query pass
+  bool bf16;
+  bool ccq;
+  // optional: state [S (D x dv) | M (D x D) | m (D)] (CCQ) or [S] per (b,h),
+  // sstride floats apart, before the first token (holding t_in tokens) and
+  // after the last
+  const float* state_in;
+  float* state_out;
+  int64_t sstride;
+  int64_t t_in;
+};
+hipError_t deltanet_launch(const DeltaLaunch& L, hipStream_t st);
+
+// Floats per block of the clean-query segment pass: sum k k^T (D x D), sum k
+// (D); padded to 64 floats.
+inline int64_t cq_state_floats(int64_t D) { return (D * D + D + 63) / 64 * 64; }
+
 // Decayed linear attention with a decay per key feature (linattn_vec.hip).
 struct VecLaunch {
   const void* q;

@@ -24,6 +24,10 @@ on. ``N(m, s2)`` there names a mean and a *variance*.
   per-token scalar decay g = sigmoid(N(3, 1)) in float32.
 * CCQ: as above, plus a query gate with w ~ N(0, 1/d_k) per head and bias
   b = -2.
+* Gated delta rule: as gated linear attention, plus a per-token step size
+  beta = sigmoid(N(0, 1)) in float32; keys always have unit norm (low-rank
+  keys are normalised after they are drawn), so that the gradient step
+  beta_t k_t k_t^T never amplifies the state.
 """
 from __future__ import annotations
 
@@ -36,7 +40,7 @@ import numpy as np
 import torch
 
 # tensor ids of the seeded streams
-T_Q, T_K, T_V, T_MU, T_LOGVAR, T_LOGITPI, T_G, T_W, T_CENTRES, T_ASSIGN, T_BASIS, T_COEF = range(12)
+T_Q, T_K, T_V, T_MU, T_LOGVAR, T_LOGITPI, T_G, T_W, T_CENTRES, T_ASSIGN, T_BASIS, T_COEF, T_BETA = range(13)
 
 _DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -77,6 +81,7 @@ class LinAttnConfig:
     lowrank_keys: int = 0  # >0: keys = U z + 0.1 n with rank-r U (unnormalised)
     vector_gates: bool = False  # g [B,H,N,dk]: one decay per token and key feature
     gate_bias: float = -2.0
+    delta: bool = False  # gated delta rule: beta [B,H,N], unit-norm keys
 
     def replace(self, **kw) -> "LinAttnConfig":
         return dataclasses.replace(self, **kw)
@@ -97,6 +102,12 @@ CONFIGS = {
     "glv_bf16_n8k": LinAttnConfig("glv_bf16_n8k", 9, B=8, H=16, N=8192, dk=128, dv=128, vector_gates=True),
     "ccq_bf16_lowrank": LinAttnConfig("ccq_bf16_lowrank", 8, B=4, H=16, N=16384, dk=128, dv=128,
                                       lowrank_keys=4, gate_bias=2.0),
+    # the gated delta rule on the 8K and 16K linear-attention shapes
+    "deltanet_bf16_n8k": LinAttnConfig("deltanet_bf16_n8k", 10, B=8, H=16, N=8192, dk=128, dv=128, delta=True),
+    "ccq_deltanet_bf16_n16k": LinAttnConfig("ccq_deltanet_bf16_n16k", 11, B=4, H=16, N=16384, dk=128, dv=128,
+                                            delta=True),
+    "ccq_deltanet_bf16_lowrank": LinAttnConfig("ccq_deltanet_bf16_lowrank", 12, B=4, H=16, N=16384, dk=128,
+                                               dv=128, delta=True, lowrank_keys=4, gate_bias=2.0),
 }
 
 
@@ -177,7 +188,8 @@ def gma_inputs(cfg: GmaConfig, N: Optional[int] = None) -> Dict[str, torch.Tenso
 def linattn_inputs(cfg: LinAttnConfig, N: Optional[int] = None, ccq: bool = False) -> Dict[str, torch.Tensor]:
     """q, k [B,H,N,dk], v [B,H,N,dv] in cfg.dtype; g [B,H,N] float32 ([B,H,N,dk]
     with cfg.vector_gates, each entry drawn the same way); for CCQ also
-    w_lambda [H,dk] and b_lambda [H] float32."""
+    w_lambda [H,dk] and b_lambda [H] float32; with cfg.delta also beta [B,H,N]
+    float32."""
     N = cfg.N if N is None else N
     B, H, dk, dv = cfg.B, cfg.H, cfg.dk, cfg.dv
     dt = _DTYPES[cfg.dtype]
@@ -186,6 +198,7 @@ def linattn_inputs(cfg: LinAttnConfig, N: Optional[int] = None, ccq: bool = Fals
     v = torch.empty((B, H, N, dv), dtype=dt)
     gshape = (N, dk) if cfg.vector_gates else (N,)
     g = torch.empty((B, H) + gshape, dtype=torch.float32)
+    beta = torch.empty((B, H, N), dtype=torch.float32) if cfg.delta else None
     basis = None
     if cfg.lowrank_keys:
         r = cfg.lowrank_keys
@@ -196,6 +209,8 @@ def linattn_inputs(cfg: LinAttnConfig, N: Optional[int] = None, ccq: bool = Fals
         if cfg.lowrank_keys:
             z = _rng(cfg.cfg_id, T_COEF, b, h).standard_normal((N, cfg.lowrank_keys))
             ks = z @ basis[h].T + 0.1 * _rng(cfg.cfg_id, T_K, b, h).standard_normal((N, dk))
+            if cfg.delta:
+                ks = ks / np.linalg.norm(ks, axis=1, keepdims=True)
         else:
             z = _rng(cfg.cfg_id, T_K, b, h).standard_normal((N, dk))
             ks = z / np.linalg.norm(z, axis=1, keepdims=True)
@@ -208,9 +223,13 @@ def linattn_inputs(cfg: LinAttnConfig, N: Optional[int] = None, ccq: bool = Fals
         k[b, h] = _to(ks, cfg.dtype)
         v[b, h] = _to(vs, cfg.dtype)
         g[b, h] = _to(gs, "f32")
+        if cfg.delta:
+            beta[b, h] = _to(1.0 / (1.0 + np.exp(-_rng(cfg.cfg_id, T_BETA, b, h).standard_normal(N))), "f32")
 
     _per_slice(B, H, one)
     out = {"q": q, "k": k, "v": v, "g": g}
+    if cfg.delta:
+        out["beta"] = beta
     if ccq:
         w = np.stack([_rng(cfg.cfg_id, T_W, h).standard_normal(dk) / math.sqrt(dk) for h in range(H)])
         out["w_lambda"] = _to(w, "f32")

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_version_and_status_strings():
     L = binding.lib()
-    assert L.lm_abi_version() == 4
+    assert L.lm_abi_version() == 5
     for code, name in enumerate(["LM_OK", "LM_EINVAL", "LM_EUNSUPPORTED", "LM_EWORKSPACE", "LM_EHIP"]):
         assert L.lm_status_string(code).decode() == name
     assert L.lm_status_string(99).decode() == "LM_UNKNOWN"
@@ -120,6 +120,58 @@ def test_linattn_errors(fn, kw, code):
     st, msg = _lin(binding.lib(), fn, **kw)
     assert st == code, (st, msg)
     assert msg
+
+
+def _delta(L, fn, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30), beta=FAKE + (10 << 30),
+             w=FAKE + (4 << 30), b=FAKE + (5 << 30), out=FAKE + (6 << 30), B=1, H=2, N=100, dk=64, dv=64,
+             chunk=64, dt=binding.LM_BF16, seg=0, ws=FAKE + (7 << 30), wsb=None)
+    a.update(kw)
+    ccq = fn == "ccq_deltanet_forward"
+    if a["wsb"] is None:
+        wsf = L.ccq_deltanet_workspace_bytes if ccq else L.deltanet_workspace_bytes
+        a["wsb"] = wsf(a["B"], a["H"], a["N"], a["dk"], a["dv"], a["chunk"], a["dt"], a["seg"])
+    if ccq:
+        st = L.ccq_deltanet_forward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["w"], a["b"], a["out"], a["B"],
+                                    a["H"], a["N"], a["dk"], a["dv"], a["chunk"], a["dt"], a["seg"], a["ws"],
+                                    a["wsb"], None)
+    else:
+        st = L.deltanet_chunk_forward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["out"], a["B"], a["H"], a["N"],
+                                      a["dk"], a["dv"], a["chunk"], a["dt"], a["seg"], a["ws"], a["wsb"], None)
+    return st, L.lm_last_error().decode()
+
+
+@needs_lib
+@pytest.mark.parametrize("fn", ["deltanet_chunk_forward", "ccq_deltanet_forward"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(beta=None), binding.LM_EINVAL),
+    (dict(beta=FAKE + (10 << 30) + 2), binding.LM_EINVAL),  # misaligned
+    (dict(N=0), binding.LM_EINVAL),
+    (dict(chunk=32), binding.LM_EUNSUPPORTED),
+    (dict(dk=64, dv=128), binding.LM_EUNSUPPORTED),
+    (dict(dk=128, dv=128, dt=binding.LM_F32), binding.LM_EUNSUPPORTED),
+    (dict(out=FAKE + (10 << 30)), binding.LM_EINVAL),  # overlaps beta
+    (dict(B=256, H=256), binding.LM_EUNSUPPORTED),
+])
+def test_deltanet_errors(fn, kw, code):
+    st, msg = _delta(binding.lib(), fn, **kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+@needs_lib
+def test_deltanet_workspaces():
+    L = binding.lib()
+    # the plain read needs no workspace; the CCQ read holds the clean queries
+    assert L.deltanet_workspace_bytes(4, 16, 16384, 128, 128, 64, binding.LM_BF16, 0) == 0
+    n = L.ccq_deltanet_workspace_bytes(4, 16, 16384, 128, 128, 64, binding.LM_BF16, 0)
+    assert n >= 4 * 16 * 16384 * 128 * 2
+    st, _ = _delta(L, "ccq_deltanet_forward", wsb=16)
+    assert st == binding.LM_EWORKSPACE
+    st, _ = _delta(L, "ccq_deltanet_forward", ws=None)
+    assert st == binding.LM_EINVAL
+    st, _ = _delta(L, "ccq_deltanet_forward", w=None)
+    assert st == binding.LM_EINVAL
 
 
 @needs_lib
