@@ -27,8 +27,9 @@ The JSON line also holds:
   * parts: per-path rates;
   * secondary (--secondary): the bidirectional 16K GMA, the 8K-token GLA
     forward and backward, the per-feature-decay forward, the long-context GMA,
-    the causal GMA backward at the 16K GMA shapes and the CCQ backward at the
-    CCQ workload, each against 8 TB/s of
+    the causal GMA backward at the 16K GMA shapes, the CCQ backward at the
+    CCQ workload, the gated delta rule at the 8K-token GLA shape and the CCQ
+    read over it at the CCQ workload, each against 8 TB/s of
     its algorithmic bytes (and, for the long-context GMA, the bf16 MFMA peak);
   * decode (--decode): the one-token steps at the model shapes of the two
     workloads, batched so that the states (about 0.5 GB) exceed the cache,
@@ -279,7 +280,8 @@ def main():
         sec = {}
         for name, fn in (("gma_bidir_n16k", "bidir"), ("gla_bf16_n8k", "gla"), ("gla_backward_bf16_n8k", "glab"),
                          ("glv_bf16_n8k", "glv"), ("gma_bf16_n128k", "gma5"), ("gma_backward_bf16_n16k", "gmab"),
-                         ("ccq_backward_bf16_n16k", "ccqb")):
+                         ("ccq_backward_bf16_n16k", "ccqb"), ("deltanet_bf16_n8k", "gdn"),
+                         ("ccq_deltanet_bf16_n16k", "ccqgdn")):
             if fn == "bidir":
                 a = gset[0]
                 call = lambda: gma_forward(a["q"], a["k"], a["v"], a["mu"], a["log_var"], a["logit_pi"],
@@ -332,6 +334,22 @@ def main():
                 tok = c_tok
                 # read Q, K, V, dO (bf16) and g; write dQ, dK, dV (bf16) and dg (fp32)
                 byt = tok * (7 * ccfg.dk * 2 + 8)
+            elif fn in ("gdn", "ccqgdn"):
+                from linear_attention_gmm_amd import (ccq_deltanet_forward, ccq_deltanet_workspace_bytes,
+                                                      deltanet_chunk_forward)
+                cfg = inputs.CONFIGS["deltanet_bf16_n8k" if fn == "gdn" else "ccq_deltanet_bf16_n16k"]
+                xd = {k: v.to(dev) for k, v in inputs.linattn_inputs(cfg, ccq=fn == "ccqgdn").items()}
+                dout_ = torch.empty_like(xd["v"])
+                if fn == "gdn":
+                    call = lambda: deltanet_chunk_forward(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], out=dout_)
+                else:
+                    wsd = torch.empty(ccq_deltanet_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.dk, cfg.dv),
+                                      dtype=torch.uint8, device=dev)
+                    call = lambda: ccq_deltanet_forward(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"],
+                                                        xd["w_lambda"], xd["b_lambda"], out=dout_, workspace=wsd)
+                tok = cfg.B * cfg.H * cfg.N
+                # Q, K, V read and O written (bf16), decay and step size (fp32)
+                byt = tok * ((2 * cfg.dk + 2 * cfg.dv) * 2 + 8)
             else:
                 cfg = inputs.CONFIGS["gma_bf16_n128k"]
                 y = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inputs.gma_inputs(cfg).items()}

@@ -199,7 +199,8 @@ int ccq_forward(const void* q, const void* k, const void* v, const float* g,
  *   segments is accepted and has no effect: the state passes through every
  *         chunk of a sequence in order (the columns of S are what is split
  *         across workgroups: B*H*dv/32 of them).
- * Workspace: deltanet_workspace_bytes returns 0 (workspace may be NULL).
+ * Workspace (deltanet_workspace_bytes): W = T diag(beta gamma) K and
+ * T diag(beta) V of every chunk, B*H*N*(dk + dv) elements of dtype.
  * Implemented shapes: dk == dv in {32, 64, 128} for bf16, {32, 64} for
  * float32; any N >= 1.
  */
@@ -214,9 +215,10 @@ int deltanet_chunk_forward(const void* q, const void* k, const void* v, const fl
  * The CCQ read over the gated delta rule: o_t = S_t^T (q_t - lambda_t Sigma_t
  * q_t), with S_t as for deltanet_chunk_forward and lambda_t, Sigma_t as for
  * ccq_forward (w_lambda [H,dk], b_lambda [H], float32).
- * Workspace (ccq_deltanet_workspace_bytes): the clean queries (B*H*N*dk
- * elements of dtype) plus the running key sums of each segment of the
- * clean-query pass; segments (0 = automatic) splits that pass only.
+ * Workspace (ccq_deltanet_workspace_bytes): that of deltanet_chunk_forward,
+ * the clean queries (B*H*N*dk elements of dtype) and the running key sums of
+ * each segment of the clean-query pass; segments (0 = automatic) splits that
+ * pass only.
  * Implemented shapes: as for deltanet_chunk_forward.
  */
 size_t ccq_deltanet_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,

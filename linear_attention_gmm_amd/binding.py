@@ -264,20 +264,22 @@ def _beta(beta, shape) -> int:
 
 
 def deltanet_chunk_forward(q, k, v, g, beta, chunk: int = 64, segments: int = 0,
-                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Gated delta rule, plain read. beta [B,H,N] float32 step sizes."""
     dt = _dtype_code(q)
     (B, H, N, dk, dv), (pq, pk, pv, pg), out, po = _lin_common(q, k, v, g, out)
     pb = _beta(beta, (B, H, N))
-    st = lib().deltanet_chunk_forward(pq, pk, pv, pg, pb, po, B, H, N, dk, dv, chunk, dt, segments, None, 0,
-                                      _stream(q.device))
+    nbytes = deltanet_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace)
+    st = lib().deltanet_chunk_forward(pq, pk, pv, pg, pb, po, B, H, N, dk, dv, chunk, dt, segments, ws.data_ptr(),
+                                      nbytes, _stream(q.device))
     _check("deltanet_chunk_forward", st)
     return out
 
 
 def deltanet_forward_state(q, k, v, g, beta, state_in: Optional[torch.Tensor] = None, chunk: int = 64,
                            segments: int = 0, out: Optional[torch.Tensor] = None,
-                           state_out: Optional[torch.Tensor] = None):
+                           state_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Gated delta rule continuing from state_in [B,H,dk*dv]. Returns (out, state_out)."""
     dt = _dtype_code(q)
     (B, H, N, dk, dv), (pq, pk, pv, pg), out, po = _lin_common(q, k, v, g, out)
@@ -286,8 +288,10 @@ def deltanet_forward_state(q, k, v, g, beta, state_in: Optional[torch.Tensor] = 
     psi = _state(state_in, "state_in", shape, q.device)
     state_out = _state_out(state_out, shape, q.device)
     pso = _state(state_out, "state_out", shape, q.device)
+    nbytes = deltanet_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace)
     st = lib().deltanet_forward_state(pq, pk, pv, pg, pb, po, B, H, N, dk, dv, chunk, dt, segments, psi, pso,
-                                      None, 0, _stream(q.device))
+                                      ws.data_ptr(), nbytes, _stream(q.device))
     _check("deltanet_forward_state", st)
     return out, state_out
 

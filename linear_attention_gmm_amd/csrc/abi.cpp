@@ -240,17 +240,23 @@ int lin_forward(const char* fn, bool ccq, const void* q, const void* k, const vo
 // ----------------------------------------------------------------------------- gated delta rule
 
 struct DeltaLayout {
-  size_t qc, agg, total;  // total == 0: no workspace (plain read)
+  size_t w, u, qc, agg, total;
   Plan plan;
 };
 
-// CCQ: the clean queries (input dtype) and the clean-query pass's segment blocks.
-DeltaLayout delta_layout(int64_t B, int64_t H, int64_t N, int64_t dk, int dtype, bool ccq, int64_t segments) {
+// W and Ut of every chunk (input dtype, the shapes of K and V); for CCQ also
+// the clean queries (input dtype) and the clean-query pass's segment blocks.
+DeltaLayout delta_layout(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int dtype, bool ccq,
+                         int64_t segments) {
   DeltaLayout L{};
   L.plan = plan_segments(B * H, N, segments);
+  const size_t es = esize(dtype);
+  L.w = 0;
+  L.u = align_up((size_t)B * H * N * dk * es);
+  L.total = align_up(L.u + (size_t)B * H * N * dv * es);
   if (!ccq) return L;
-  L.qc = 0;
-  L.agg = align_up((size_t)B * H * N * dk * esize(dtype));
+  L.qc = L.total;
+  L.agg = align_up(L.qc + (size_t)B * H * N * dk * es);
   L.total = align_up(L.agg + (size_t)B * H * L.plan.P * lm::cq_state_floats(dk) * 4);
   return L;
 }
@@ -270,8 +276,8 @@ int delta_forward(const char* fn, bool ccq, const void* q, const void* k, const 
                   const float* state_in, float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
   int st = delta_check_shape(fn, B, H, N, dk, dv, chunk, dtype, segments);
   if (st != LM_OK) return st;
-  const DeltaLayout L = delta_layout(B, H, N, dk, dtype, ccq, segments);
-  if (!q || !k || !v || !g || !beta || !out || (L.total && !workspace) || (ccq && (!w_lambda || !b_lambda)))
+  const DeltaLayout L = delta_layout(B, H, N, dk, dv, dtype, ccq, segments);
+  if (!q || !k || !v || !g || !beta || !out || !workspace || (ccq && (!w_lambda || !b_lambda)))
     return fail(LM_EINVAL, "%s: null pointer argument", fn);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
       !aligned(g, 4) || !aligned(beta, 4) || (ccq && (!aligned(w_lambda, 4) || !aligned(b_lambda, 4))))
@@ -298,6 +304,8 @@ int delta_forward(const char* fn, bool ccq, const void* q, const void* k, const 
   La.w_lambda = w_lambda;
   La.b_lambda = b_lambda;
   La.out = out;
+  La.wbuf = static_cast<char*>(workspace) + L.w;
+  La.ubuf = static_cast<char*>(workspace) + L.u;
   La.qc = ccq ? static_cast<char*>(workspace) + L.qc : nullptr;
   La.agg = ccq ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.agg) : nullptr;
   La.B = B;
@@ -761,7 +769,7 @@ int ccq_decode_step(const void* q, const void* k, const void* v, const float* g,
 size_t deltanet_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
                                 int64_t segments) {
   if (delta_check_shape("deltanet_chunk_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
-  return delta_layout(B, H, N, dk, dtype, false, segments).total;
+  return delta_layout(B, H, N, dk, dv, dtype, false, segments).total;
 }
 
 int deltanet_chunk_forward(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -782,7 +790,7 @@ int deltanet_forward_state(const void* q, const void* k, const void* v, const fl
 size_t ccq_deltanet_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
                                     int dtype, int64_t segments) {
   if (delta_check_shape("ccq_deltanet_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
-  return delta_layout(B, H, N, dk, dtype, true, segments).total;
+  return delta_layout(B, H, N, dk, dv, dtype, true, segments).total;
 }
 
 int ccq_deltanet_forward(const void* q, const void* k, const void* v, const float* g, const float* beta,

@@ -34,19 +34,25 @@
 // drops terms of that (negligible) size.
 //
 // MI355X design
+//  * Two passes. The prepass forms T, W and Ut for every chunk at once (no
+//    chunk depends on another there) and writes W and Ut, rounded to the input
+//    type, in the layouts of K and V. The sequential pass then keeps only
+//    the state chain S_0 -> U -> S_C per chunk (two barriers), with the
+//    decayed Q K^T and the output hanging off it.
 //  * The rule acts on S from the key side only, so the value columns of S
-//    evolve independently: a workgroup of 8 waves owns 32 value columns of
-//    one (b, h) and walks every chunk in order. That is B*H*dv/32 workgroups
-//    (256 at B=4, H=16, dv=128) with no segment pass; the products that do
-//    not depend on S (K K^T, Q K^T, T, W) are recomputed by each column group
-//    (a segment pass for this rule would carry a dense dk x dk transition).
-//    The column groups of one (b, h) are launched gridDim/groups apart, which
-//    for B*H a multiple of 8 puts them on one XCD, sharing its L2 for Q, K.
+//    evolve independently: in the sequential pass a workgroup of 8 waves
+//    owns 32 value columns of one (b, h) and walks every chunk in order.
+//    That is B*H*dv/32 workgroups (256 at B=4, H=16, dv=128)
+//    with no segment pass (a segment pass for this rule would carry a dense
+//    dk x dk transition). The column groups of one (b, h) are launched
+//    gridDim/groups apart, which for B*H a multiple of 8 puts them on one
+//    XCD, sharing its L2 for Q, K and W.
 //  * Products are 16x16 MFMA tiles (bf16 operands, fp32 accumulation; or
 //    fp32), T in fp32 MFMA. S stays in fp32 registers and is rounded to the
 //    operand type once per chunk for the products that read it.
-//  * The next chunk's Q, K, V, g, beta are loaded into registers while the
-//    current chunk is computed.
+//  * Each pass loads the next chunk's rows into registers while the current
+//    chunk is computed (the sequential pass during its last phase only, which
+//    keeps its registers within 256 per lane without spills).
 #include "mfma.hpp"
 #include "launch.hpp"
 
@@ -127,236 +133,178 @@ __device__ __forceinline__ typename Mma<T>::frag ones_frag() {
   return f;
 }
 
-template <typename T, int D>
-struct Cfg {
+// 16-byte vectors of 64 rows of a [BH][N][width] tensor: loads into registers
+// (rows past `limit` read as zero) and stores into an LDS tile of pitch `pitch`.
+template <typename T, int W, int COLS>
+struct RowVecs {
   static constexpr int ES = (int)sizeof(T);
-  static constexpr int KS = Mma<T>::KS;
-  static constexpr int NKD = D / KS;  // k-steps over features
-  static constexpr int NKC = kC / KS;  // k-steps over a chunk's tokens
-  static constexpr int PAD = ES == 2 ? 8 : 4;
-  // pitches (elements)
-  static constexpr int PQ = D + PAD;    // Q, K, W rows
-  static constexpr int PV = kCG + PAD;  // V, S, U rows
-  static constexpr int PP = kC + PAD;   // P rows
-  static constexpr int PA = kC + 4;     // A, T rows (fp32)
-  // byte offsets
-  static constexpr int o_q = 0;
-  static constexpr int o_k = o_q + kC * PQ * ES;
-  static constexpr int o_w = o_k + kC * PQ * ES;
-  static constexpr int o_v = o_w + kC * PQ * ES;
-  static constexpr int o_s = o_v + kC * PV * ES;
-  static constexpr int o_u = o_s + D * PV * ES;
-  static constexpr int o_ud = o_u + kC * PV * ES;
-  static constexpr int o_p = o_ud + kC * PV * ES;
-  static constexpr int o_a = o_p + kC * PP * ES;
-  static constexpr int o_t = o_a + kC * PA * 4;
-  static constexpr int o_row = o_t + kC * PA * 4;  // [5][64] f32 per-token scalars
-  static constexpr int bytes = o_row + 5 * kC * 4;
-  static_assert(bytes <= 160 * 1024, "LDS budget");
-  static_assert(o_k % 16 == 0 && o_w % 16 == 0 && o_v % 16 == 0 && o_s % 16 == 0 && o_u % 16 == 0 &&
-                    o_ud % 16 == 0 && o_p % 16 == 0 && o_a % 16 == 0 && o_t % 16 == 0 && o_row % 16 == 0,
-                "16-byte aligned regions");
-  // 16-byte vectors per chunk of Q (or K), and per thread
-  static constexpr int VR = D * ES / 16;
-  static constexpr int NQ = (kC * VR + kNT - 1) / kNT;
-  static constexpr int VRV = kCG * ES / 16;
-  static constexpr int NVV = kC * VRV;  // V vectors per chunk (<= kNT)
-  static_assert(NVV <= kNT, "one V vector per thread");
-  // S tiles (16 x 16) of the column group and per wave
-  static constexpr int NST = 2 * D / 16;
-  static constexpr int SPW = (NST + kNW - 1) / kNW;
+  static constexpr int VR = COLS * ES / 16;          // vectors per row
+  static constexpr int NV = (kC * VR + kNT - 1) / kNT;  // per thread
+  uint4 x[NV];
+  // src: element (0, col0) of the (b, h) slice; width W elements per row
+  __device__ __forceinline__ void load(const T* src, int64_t c0, int64_t limit) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int p = threadIdx.x + i * kNT;
+      const int row = p / VR, cv = p % VR;
+      const bool ok = p < kC * VR && c0 + row < limit;
+      x[i] = ok ? *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src + (size_t)(c0 + row) * W) +
+                                                  cv * 16)
+                : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(T* dst, int pitch) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int p = threadIdx.x + i * kNT;
+      if (p < kC * VR) {
+        const int row = p / VR, cv = p % VR;
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst + row * pitch) + cv * 16) = x[i];
+      }
+    }
+  }
 };
 
-struct Args {
-  const void* q;
+// Per-token decay scalars of a chunk (wave 0, lane = token; g = 1 past the end):
+// l = running log2-decay, written with what the caller needs of it.
+__device__ __forceinline__ float chunk_log2_decay(float g) {
+  return wave_scan_incl(fmaxf(__builtin_amdgcn_logf(g), kMinLog2));
+}
+
+// ---------------------------------------------------------------------------
+// Prepass: for every chunk, T = (I + A)^{-1}, W = T diag(beta gamma) K and
+// Ut = T diag(beta) V, written to the workspace in the layouts of K and V.
+// Nothing here depends on the state, so every chunk is independent.
+
+template <typename T, int D>
+struct PCfg {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int KS = Mma<T>::KS;
+  static constexpr int NKD = D / KS;
+  static constexpr int PAD = ES == 2 ? 8 : 4;
+  static constexpr int PQ = D + PAD;  // K, V, and the W / Ut staging rows
+  static constexpr int PA = kC + 4;   // A, T rows (fp32)
+  static constexpr int o_k = 0;
+  static constexpr int o_v = o_k + kC * PQ * ES;
+  static constexpr int o_w = o_v + kC * PQ * ES;
+  static constexpr int o_u = o_w + kC * PQ * ES;
+  static constexpr int o_a = o_u + kC * PQ * ES;
+  static constexpr int o_t = o_a + kC * PA * 4;
+  static constexpr int o_row = o_t + kC * PA * 4;  // [3][64] f32: l, beta, beta gamma
+  static constexpr int bytes = o_row + 3 * kC * 4;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static_assert(o_v % 16 == 0 && o_w % 16 == 0 && o_u % 16 == 0 && o_a % 16 == 0 && o_t % 16 == 0 &&
+                    o_row % 16 == 0, "16-byte aligned regions");
+  static constexpr int FPW = D / 32;  // W (and Ut) column tiles per wave
+};
+
+struct PArgs {
   const void* k;
   const void* v;
   const float* g;
   const float* beta;
-  void* out;
-  const float* state_in;  // optional: S at state_in + bh * sstride
-  float* state_out;
-  int64_t sstride;
-  const float* mfinal;  // CCQ with state_out: running sums after the last token,
-                        // block P - 1 of the clean-query pass's workspace
-  int P, sfl;
+  void* w;   // [BH][N][D]
+  void* ut;  // [BH][N][dv]
   int64_t N;
-  int BH;
-  int dv;
-};
-
-// Registers holding one chunk's inputs between their load and their LDS store.
-template <typename T, int D>
-struct Pref {
-  typedef Cfg<T, D> C;
-  uint4 q[C::NQ], k[C::NQ], v;
-  float g, b;
-  __device__ __forceinline__ void load(const Args& a, int bh, int cg, int64_t c0) {
-    const int tid = threadIdx.x;
-    const char* qb = static_cast<const char*>(a.q) + (size_t)bh * a.N * D * C::ES;
-    const char* kb = static_cast<const char*>(a.k) + (size_t)bh * a.N * D * C::ES;
-#pragma unroll
-    for (int i = 0; i < C::NQ; ++i) {
-      const int p = tid + i * kNT;
-      const int row = p / C::VR, cv = p % C::VR;
-      const bool ok = p < kC * C::VR && c0 + row < a.N;
-      const size_t off = (size_t)(c0 + row) * D * C::ES + (size_t)cv * 16;
-      q[i] = ok ? *reinterpret_cast<const uint4*>(qb + off) : make_uint4(0, 0, 0, 0);
-      k[i] = ok ? *reinterpret_cast<const uint4*>(kb + off) : make_uint4(0, 0, 0, 0);
-    }
-    {
-      const int row = tid / C::VRV, cv = tid % C::VRV;
-      const bool ok = tid < C::NVV && c0 + row < a.N;
-      const char* vb = static_cast<const char*>(a.v) + ((size_t)bh * a.N + c0 + row) * a.dv * C::ES +
-                       (size_t)cg * kCG * C::ES + (size_t)cv * 16;
-      v = ok ? *reinterpret_cast<const uint4*>(vb) : make_uint4(0, 0, 0, 0);
-    }
-    const bool okt = tid < kC && c0 + tid < a.N;
-    g = okt ? a.g[(size_t)bh * a.N + c0 + tid] : 1.f;
-    b = okt ? a.beta[(size_t)bh * a.N + c0 + tid] : 0.f;
-  }
-  __device__ __forceinline__ void store(char* sm) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < C::NQ; ++i) {
-      const int p = tid + i * kNT;
-      if (p < kC * C::VR) {
-        const int row = p / C::VR, cv = p % C::VR;
-        *reinterpret_cast<uint4*>(sm + C::o_q + row * C::PQ * C::ES + cv * 16) = q[i];
-        *reinterpret_cast<uint4*>(sm + C::o_k + row * C::PQ * C::ES + cv * 16) = k[i];
-      }
-    }
-    if (tid < C::NVV) {
-      const int row = tid / C::VRV, cv = tid % C::VRV;
-      *reinterpret_cast<uint4*>(sm + C::o_v + row * C::PV * C::ES + cv * 16) = v;
-    }
-  }
+  int cpb;   // chunks per workgroup
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kNT) void gdn_kernel(Args a) {
-  typedef Cfg<T, D> C;
+__global__ __launch_bounds__(kNT) void gdn_prep_kernel(PArgs a) {
+  typedef PCfg<T, D> C;
   typedef Mma<T> M;
   __shared__ __attribute__((aligned(16))) char sm[C::bytes];
-  T* sQ = reinterpret_cast<T*>(sm + C::o_q);
   T* sK = reinterpret_cast<T*>(sm + C::o_k);
-  T* sW = reinterpret_cast<T*>(sm + C::o_w);
   T* sV = reinterpret_cast<T*>(sm + C::o_v);
-  T* sS = reinterpret_cast<T*>(sm + C::o_s);
+  T* sW = reinterpret_cast<T*>(sm + C::o_w);
   T* sU = reinterpret_cast<T*>(sm + C::o_u);
-  T* sUd = reinterpret_cast<T*>(sm + C::o_ud);
-  T* sP = reinterpret_cast<T*>(sm + C::o_p);
   float* sA = reinterpret_cast<float*>(sm + C::o_a);
   float* sT = reinterpret_cast<float*>(sm + C::o_t);
-  float* sL = reinterpret_cast<float*>(sm + C::o_row);  // running log2 decay
-  float* sBt = sL + kC;                                  // beta
-  float* sSw = sL + 2 * kC;                              // beta_j gamma_j
-  float* sDc = sL + 3 * kC;                              // gamma_C / gamma_j
-  float* sGm = sL + 4 * kC;                              // gamma_j
+  float* sL = reinterpret_cast<float*>(sm + C::o_row);
+  float* sBt = sL + kC;
+  float* sSw = sL + 2 * kC;
+  const int bh = blockIdx.y;
+  const int w = wave_id(), l = lane_id(), g = l >> 4, l16 = l & 15, tid = threadIdx.x;
+  const int64_t nch = (a.N + kC - 1) / kC;
+  const int64_t ch0 = (int64_t)blockIdx.x * a.cpb;
+  const int64_t ch1 = ch0 + a.cpb < nch ? ch0 + a.cpb : nch;
+  const T* kb = static_cast<const T*>(a.k) + (size_t)bh * a.N * D;
+  const T* vb = static_cast<const T*>(a.v) + (size_t)bh * a.N * D;
+  T* wb = static_cast<T*>(a.w) + (size_t)bh * a.N * D;
+  T* ub = static_cast<T*>(a.ut) + (size_t)bh * a.N * D;
+  const float* gb = a.g + (size_t)bh * a.N;
+  const float* bb = a.beta + (size_t)bh * a.N;
 
-  const int bh = blockIdx.x % a.BH, cg = blockIdx.x / a.BH;
-  const int w = wave_id(), l = lane_id(), g = l >> 4, l16 = l & 15;
-  const int tid = threadIdx.x;
-
-  // upper tiles of P and T stay zero (read by the k-steps that straddle the diagonal)
+  // upper tiles of T stay zero (read by the k-steps that straddle the diagonal)
   for (int i = tid; i < kC * kC; i += kNT) {
     const int r = i / kC, c = i % kC;
-    if ((c >> 4) > (r >> 4)) {
-      sP[r * C::PP + c] = cvt<T>(0.f);
-      sT[r * C::PA + c] = 0.f;
-    }
+    if ((c >> 4) > (r >> 4)) sT[r * C::PA + c] = 0.f;
   }
+  RowVecs<T, D, D> pk, pv;
+  float pg = 1.f, pb = 0.f;
+  auto fetch = [&](int64_t c0) {
+    pk.load(kb, c0, a.N);
+    pv.load(vb, c0, a.N);
+    const bool ok = tid < kC && c0 + tid < a.N;
+    pg = ok ? gb[c0 + tid] : 1.f;
+    pb = ok ? bb[c0 + tid] : 0.f;
+  };
+  if (ch0 < ch1) fetch(ch0 * kC);
 
-  // this wave's S tiles: t = w + kNW j, tile (a, c) = (t / 2, t % 2)
-  f32x4 St[C::SPW];
-#pragma unroll
-  for (int j = 0; j < C::SPW; ++j) {
-    St[j] = zero4();
-    const int t = w + kNW * j;
-    if (t < C::NST && a.state_in) {
-      const float* src = a.state_in + (size_t)bh * a.sstride;
-      const int ra = 16 * (t >> 1), col = cg * kCG + 16 * (t & 1) + l16;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) St[j][e] = src[(size_t)(ra + 4 * g + e) * a.dv + col];
-    }
-  }
-
-  Pref<T, D> pf;
-  pf.load(a, bh, cg, 0);
-  const int64_t nch = (a.N + kC - 1) / kC;
-  const int r_own = w >> 1, c_own = w & 1;  // the (row tile, column tile) of U and O this wave owns
-  T* outp = static_cast<T*>(a.out);
-
-  for (int64_t ch = 0; ch < nch; ++ch) {
+  for (int64_t ch = ch0; ch < ch1; ++ch) {
     const int64_t c0 = ch * kC;
-    // ---- inputs to LDS, the state to its operand copy, next chunk's loads
-    pf.store(sm);
-#pragma unroll
-    for (int j = 0; j < C::SPW; ++j) {
-      const int t = w + kNW * j;
-      if (t < C::NST) {
-        const int ra = 16 * (t >> 1), col = 16 * (t & 1) + l16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sS[(ra + 4 * g + e) * C::PV + col] = cvt<T>(St[j][e]);
-      }
-    }
+    pk.store(sK, C::PQ);
+    pv.store(sV, C::PQ);
     if (w == 0) {
-      const float lg = fmaxf(__builtin_amdgcn_logf(pf.g), kMinLog2);  // log2
-      const float lr = wave_scan_incl(lg);
-      const float lc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lr), 63));
-      const float gm = fast_exp2(lr);
+      const float lr = chunk_log2_decay(pg);
       sL[l] = lr;
-      sBt[l] = pf.b;
-      sSw[l] = pf.b * gm;
-      sDc[l] = fast_exp2(lc - lr);
-      sGm[l] = gm;
+      sBt[l] = pb;
+      sSw[l] = pb * fast_exp2(lr);
     }
-    if (ch + 1 < nch) pf.load(a, bh, cg, c0 + kC);
-    __syncthreads();
+    if (ch + 1 < ch1) fetch(c0 + kC);
+    lds_barrier();
 
-    // ---- score tiles: A = strictly lower beta-scaled decayed K K^T (fp32),
-    //      P = lower decayed Q K^T (operand type)
-    for (int t = w; t < 20; t += kNW) {
-      const bool kk = t < 10;
+    // A = strictly lower, beta-scaled, decayed K K^T (fp32)
+    for (int t = w; t < 10; t += kNW) {
       int it, jt;
-      tri_tile(kk ? t : t - 10, it, jt);
-      const T* lhs = kk ? sK : sQ;
+      tri_tile(t, it, jt);
       f32x4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < C::NKD; ++ks)
-        acc = M::mma(ld_kc_chain(lhs, C::PQ, 16 * it + l16, ks), ld_kc_chain(sK, C::PQ, 16 * jt + l16, ks), acc);
+        acc = M::mma(ld_kc_chain(sK, C::PQ, 16 * it + l16, ks), ld_kc_chain(sK, C::PQ, 16 * jt + l16, ks), acc);
       const int j = 16 * jt + l16;
       const float lj = sL[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * it + 4 * g + e;
-        const float f = fast_exp2(fminf(sL[i] - lj, 0.f));
-        if (kk)
-          sA[i * C::PA + j] = j < i ? sBt[i] * f * acc[e] : 0.f;
-        else
-          sP[i * C::PP + j] = cvt<T>(j <= i ? f * acc[e] : 0.f);
+        sA[i * C::PA + j] = j < i ? sBt[i] * fast_exp2(fminf(sL[i] - lj, 0.f)) * acc[e] : 0.f;
       }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- T: diagonal blocks by forward substitution (wave 0, lane group =
-    //      block, lane = column)
+    // T: diagonal blocks by forward substitution (wave 0: lane group = block,
+    // lane = column), two partial sums to halve the dependent chain
     if (w == 0) {
       const int b0 = 16 * g, c = l16;
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float acc = r == c ? 1.f : 0.f;
+        float s0 = r == c ? 1.f : 0.f, s1 = 0.f;
         const float* arow = sA + (b0 + r) * C::PA + b0;
 #pragma unroll
-        for (int i = 0; i < r; ++i) acc -= arow[i] * x[i];
-        x[r] = acc;
+        for (int i = 0; i < r; ++i) {
+          if (i & 1)
+            s1 -= arow[i] * x[i];
+          else
+            s0 -= arow[i] * x[i];
+        }
+        x[r] = s0 + s1;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sT[(b0 + r) * C::PA + b0 + c] = x[r];
     }
-    __syncthreads();
-    // ---- T: off-diagonal blocks, T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
+    lds_barrier();
+    // T: off-diagonal blocks, T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
 #pragma unroll
     for (int d = 1; d < 4; ++d) {
       if (w < 4 - d) {
@@ -370,18 +318,18 @@ __global__ __launch_bounds__(kNT) void gdn_kernel(Args a) {
         }
         f32x4 Y = zero4();
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) Y = Mma<float>::mma(ld_kc_chain(sT + 16 * bi, C::PA, 16 * bi + l16, ks), X[ks], Y);
+        for (int ks = 0; ks < 4; ++ks)
+          Y = Mma<float>::mma(ld_kc_chain(sT + 16 * bi, C::PA, 16 * bi + l16, ks), X[ks], Y);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sT[(16 * bi + 4 * g + e) * C::PA + 16 * bj + l16] = -Y[e];
       }
-      __syncthreads();
+      lds_barrier();
     }
 
-    // ---- W = T diag(beta gamma) K (all columns, shared out) and Ut = T
-    //      diag(beta) V (this wave's tile, kept in registers)
-    f32x4 ut = zero4();
+    // W = T diag(beta gamma) K and Ut = T diag(beta) V: wave w takes row tile
+    // w / 2 and half of the column tiles of each
     {
-      const int r = r_own;
+      const int r = w >> 1, h = w & 1;
       constexpr int NKT = tok_steps<T>(3);
       typename M::frag aw[NKT], au[NKT];
       const int nk = tok_steps<T>(r);
@@ -391,25 +339,196 @@ __global__ __launch_bounds__(kNT) void gdn_kernel(Args a) {
           aw[ks] = scaled_row<T>(sT, C::PA, 16 * r + l16, ks, sSw);
           au[ks] = scaled_row<T>(sT, C::PA, 16 * r + l16, ks, sBt);
         }
-      constexpr int FPW = D / 32;  // W column tiles per wave
 #pragma unroll
-      for (int fi = 0; fi < FPW; ++fi) {
-        const int f = c_own * FPW + fi;
-        f32x4 acc = zero4();
+      for (int fi = 0; fi < C::FPW; ++fi) {
+        const int f = h * C::FPW + fi;
+        f32x4 cw = zero4(), cu = zero4();
 #pragma unroll
         for (int ks = 0; ks < NKT; ++ks)
-          if (ks < nk) acc = M::mma(aw[ks], ld_km_chain(sK, C::PQ, 16 * f, ks), acc);
+          if (ks < nk) {
+            cw = M::mma(aw[ks], ld_km_chain(sK, C::PQ, 16 * f, ks), cw);
+            cu = M::mma(au[ks], ld_km_chain(sV, C::PQ, 16 * f, ks), cu);
+          }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sW[(16 * r + 4 * g + e) * C::PQ + 16 * f + l16] = cvt<T>(acc[e]);
+        for (int e = 0; e < 4; ++e) {
+          sW[(16 * r + 4 * g + e) * C::PQ + 16 * f + l16] = cvt<T>(cw[e]);
+          sU[(16 * r + 4 * g + e) * C::PQ + 16 * f + l16] = cvt<T>(cu[e]);
+        }
       }
-#pragma unroll
-      for (int ks = 0; ks < NKT; ++ks)
-        if (ks < nk) ut = M::mma(au[ks], ld_km_chain(sV, C::PV, 16 * c_own, ks), ut);
     }
-    __syncthreads();
+    lds_barrier();
+    // rows to the workspace, 16 bytes per lane
+    {
+      constexpr int VR = D * (int)sizeof(T) / 16;
+      for (int p = tid; p < kC * VR; p += kNT) {
+        const int row = p / VR, cv = p % VR;
+        if (c0 + row < a.N) {
+          const size_t off = (size_t)(c0 + row) * D * sizeof(T) + (size_t)cv * 16;
+          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(wb) + off) =
+              *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(sW + row * C::PQ) + cv * 16);
+          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(ub) + off) =
+              *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(sU + row * C::PQ) + cv * 16);
+        }
+      }
+    }
+  }
+}
 
-    // ---- U = Ut - W S_0 (this wave's tile), to LDS plainly and scaled by
-    //      gamma_C / gamma_j for the state update
+// ---------------------------------------------------------------------------
+// Sequential pass: per chunk, U = Ut - W S_0, O = diag(gamma) Q S_0 + P U with
+// P the decayed lower Q K^T, S_C = gamma_C S_0 + K^T diag(gamma_C / gamma) U.
+// The state chain per chunk is S_0 -> U -> S_C (two barriers); P and O hang
+// off it.
+
+template <typename T, int D>
+struct MCfg {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int KS = Mma<T>::KS;
+  static constexpr int NKD = D / KS;
+  static constexpr int NKC = kC / KS;
+  static constexpr int PQ = D + 4;                      // Q, K, W rows
+  static constexpr int PV = kCG + (ES == 2 ? 8 : 4);    // Ut, S, U rows
+  static constexpr int PP = kC + (ES == 2 ? 8 : 4);     // P rows
+  static constexpr int o_q = 0;
+  static constexpr int o_k = o_q + kC * PQ * ES;
+  static constexpr int o_w = o_k + kC * PQ * ES;
+  static constexpr int o_ut = o_w + kC * PQ * ES;
+  static constexpr int o_s = o_ut + kC * PV * ES;
+  static constexpr int o_u = o_s + D * PV * ES;
+  static constexpr int o_p = o_u + kC * PV * ES;
+  static constexpr int o_row = o_p + kC * PP * ES;  // [3][64] f32: l, gamma_C / gamma, gamma
+  static constexpr int bytes = o_row + 3 * kC * 4;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static_assert(o_k % 16 == 0 && o_w % 16 == 0 && o_ut % 16 == 0 && o_s % 16 == 0 && o_u % 16 == 0 &&
+                    o_p % 16 == 0 && o_row % 16 == 0, "16-byte aligned regions");
+  static constexpr int NST = 2 * D / 16;  // S tiles of the column group
+  static constexpr int SPW = (NST + kNW - 1) / kNW;
+};
+
+struct Args {
+  const void* q;
+  const void* k;
+  const void* w;   // prepass output [BH][N][D]
+  const void* ut;  // prepass output [BH][N][dv]
+  const float* g;
+  void* out;
+  const float* state_in;  // optional: S at state_in + bh * sstride
+  float* state_out;
+  int64_t sstride;
+  const float* mfinal;  // CCQ with state_out: running sums after the last token,
+                        // block P - 1 of the clean-query pass's workspace
+  int P, sfl;
+  int64_t N;
+  int BH;
+  int dv;
+};
+
+// A operand (CHAIN order) of K^T for feature tile a, token k-step ks, scaled per
+// token by sc[token].
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag scaled_kt(const T* sK, int pitch, int a, int ks, const float* sc) {
+  typename Mma<T>::frag f = ld_km_chain(sK, pitch, 16 * a, ks);
+  const int g = lane_id() >> 4;
+  if constexpr (sizeof(T) == 2) {
+    const int k0 = ks * 32 + 4 * g;
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sc + k0);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(sc + k0 + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = (bf16)((float)f[i] * s0[i]);
+      f[4 + i] = (bf16)((float)f[4 + i] * s1[i]);
+    }
+  } else {
+    f *= sc[16 * (ks >> 2) + 4 * g + (ks & 3)];
+  }
+  return f;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kNT, 2) void gdn_kernel(Args a) {
+  typedef MCfg<T, D> C;
+  typedef Mma<T> M;
+  __shared__ __attribute__((aligned(16))) char sm[C::bytes];
+  T* sQ = reinterpret_cast<T*>(sm + C::o_q);
+  T* sK = reinterpret_cast<T*>(sm + C::o_k);
+  T* sW = reinterpret_cast<T*>(sm + C::o_w);
+  T* sUt = reinterpret_cast<T*>(sm + C::o_ut);
+  T* sS = reinterpret_cast<T*>(sm + C::o_s);
+  T* sU = reinterpret_cast<T*>(sm + C::o_u);
+  T* sP = reinterpret_cast<T*>(sm + C::o_p);
+  float* sL = reinterpret_cast<float*>(sm + C::o_row);  // running log2 decay
+  float* sDc = sL + kC;                                  // gamma_C / gamma_j
+  float* sGm = sL + 2 * kC;                              // gamma_j
+
+  const int bh = blockIdx.x % a.BH, cg = blockIdx.x / a.BH;
+  const int w = wave_id(), l = lane_id(), g = l >> 4, l16 = l & 15;
+  const int tid = threadIdx.x;
+  const T* qb = static_cast<const T*>(a.q) + (size_t)bh * a.N * D;
+  const T* kb = static_cast<const T*>(a.k) + (size_t)bh * a.N * D;
+  const T* wb = static_cast<const T*>(a.w) + (size_t)bh * a.N * D;
+  const T* ub = static_cast<const T*>(a.ut) + (size_t)bh * a.N * a.dv + cg * kCG;
+  const float* gb = a.g + (size_t)bh * a.N;
+
+  for (int i = tid; i < kC * kC; i += kNT) {
+    const int r = i / kC, c = i % kC;
+    if ((c >> 4) > (r >> 4)) sP[r * C::PP + c] = cvt<T>(0.f);
+  }
+
+  // this wave's S tiles: t = w + kNW j, tile (t / 2, t % 2)
+  f32x4 St[C::SPW];
+#pragma unroll
+  for (int j = 0; j < C::SPW; ++j) {
+    St[j] = zero4();
+    const int t = w + kNW * j;
+    if (t < C::NST && a.state_in) {
+      const float* src = a.state_in + (size_t)bh * a.sstride;
+      const int ra = 16 * (t >> 1), col = cg * kCG + 16 * (t & 1) + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) St[j][e] = src[(size_t)(ra + 4 * g + e) * a.dv + col];
+    }
+  }
+
+  RowVecs<T, D, D> pq, pk, pw;
+  RowVecs<T, D, kCG> pu;  // this group's columns of rows of width dv (== D)
+  float pg = 1.f;
+  auto fetch = [&](int64_t c0) {
+    pq.load(qb, c0, a.N);
+    pk.load(kb, c0, a.N);
+    pw.load(wb, c0, a.N);
+    pu.load(ub, c0, a.N);
+    pg = tid < kC && c0 + tid < a.N ? gb[c0 + tid] : 1.f;
+  };
+  fetch(0);
+  const int64_t nch = (a.N + kC - 1) / kC;
+  const int r_own = w >> 1, c_own = w & 1;  // the (row tile, column tile) of U and O this wave owns
+  T* outp = static_cast<T*>(a.out);
+
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    const int64_t c0 = ch * kC;
+    // ---- inputs to LDS, the state to its operand copy, next chunk's loads
+    pq.store(sQ, C::PQ);
+    pk.store(sK, C::PQ);
+    pw.store(sW, C::PQ);
+    pu.store(sUt, C::PV);
+#pragma unroll
+    for (int j = 0; j < C::SPW; ++j) {
+      const int t = w + kNW * j;
+      if (t < C::NST) {
+        const int ra = 16 * (t >> 1), col = 16 * (t & 1) + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sS[(ra + 4 * g + e) * C::PV + col] = cvt<T>(St[j][e]);
+      }
+    }
+    if (w == 0) {
+      const float lr = chunk_log2_decay(pg);
+      const float lc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lr), 63));
+      sL[l] = lr;
+      sDc[l] = fast_exp2(lc - lr);
+      sGm[l] = fast_exp2(lr);
+    }
+    lds_barrier();
+
+    // ---- U = Ut - W S_0 (this wave's tile); P tiles
     {
       f32x4 acc = zero4();
 #pragma unroll
@@ -418,13 +537,44 @@ __global__ __launch_bounds__(kNT) void gdn_kernel(Args a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * r_own + 4 * g + e;
-        const float u = ut[e] - acc[e];
-        sU[i * C::PV + 16 * c_own + l16] = cvt<T>(u);
-        sUd[i * C::PV + 16 * c_own + l16] = cvt<T>(u * sDc[i]);
+        const int col = 16 * c_own + l16;
+        sU[i * C::PV + col] = cvt<T>(to_f32(sUt[i * C::PV + col]) - acc[e]);
       }
     }
-    __syncthreads();
+    for (int t = w; t < 10; t += kNW) {
+      int it, jt;
+      tri_tile(t, it, jt);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < C::NKD; ++ks)
+        acc = M::mma(ld_kc_chain(sQ, C::PQ, 16 * it + l16, ks), ld_kc_chain(sK, C::PQ, 16 * jt + l16, ks), acc);
+      const int j = 16 * jt + l16;
+      const float lj = sL[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * it + 4 * g + e;
+        sP[i * C::PP + j] = cvt<T>(j <= i ? fast_exp2(fminf(sL[i] - lj, 0.f)) * acc[e] : 0.f);
+      }
+    }
+    lds_barrier();
+    if (ch + 1 < nch) fetch(c0 + kC);  // held in registers through the last phase only
 
+    // ---- S_C = gamma_C S_0 + K^T diag(gamma_C / gamma_j) U (this wave's tiles)
+    {
+      const float gc = sGm[kC - 1];
+#pragma unroll
+      for (int j = 0; j < C::SPW; ++j) {
+        const int t = w + kNW * j;
+        if (t < C::NST) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int ks = 0; ks < C::NKC; ++ks)
+            acc = M::mma(scaled_kt<T>(sK, C::PQ, t >> 1, ks, sDc), ld_km_chain(sU, C::PV, 16 * (t & 1), ks), acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) St[j][e] = gc * St[j][e] + acc[e];
+        }
+      }
+    }
     // ---- O = diag(gamma) Q S_0 + P U (this wave's tile)
     {
       f32x4 acc = zero4(), acc2 = zero4();
@@ -441,23 +591,7 @@ __global__ __launch_bounds__(kNT) void gdn_kernel(Args a) {
           outp[((size_t)bh * a.N + c0 + i) * a.dv + cg * kCG + 16 * c_own + l16] = cvt<T>(acc[e] * sGm[i] + acc2[e]);
       }
     }
-    // ---- S_C = gamma_C S_0 + K^T diag(gamma_C / gamma_j) U (this wave's tiles)
-    {
-      const float gc = sGm[kC - 1];
-#pragma unroll
-      for (int j = 0; j < C::SPW; ++j) {
-        const int t = w + kNW * j;
-        if (t < C::NST) {
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int ks = 0; ks < C::NKC; ++ks)
-            acc = M::mma(ld_km_chain(sK, C::PQ, 16 * (t >> 1), ks), ld_km_chain(sUd, C::PV, 16 * (t & 1), ks), acc);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) St[j][e] = gc * St[j][e] + acc[e];
-        }
-      }
-    }
-    __syncthreads();
+    lds_barrier();
   }
 
   if (a.state_out) {
@@ -562,7 +696,7 @@ __global__ __launch_bounds__(kNT) void cq_agg_kernel(QArgs a) {
   float msum = 0.f;
   for (int64_t c0 = t0; c0 < t1; c0 += kC) {
     load_tile<T, D>(sm + C::o_k, a.k, bh, a.N, c0, t1);  // rows past the segment end read as zero
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < C::MPW; ++j) {
       const int t = w + kNW * j;
@@ -575,7 +709,7 @@ __global__ __launch_bounds__(kNT) void cq_agg_kernel(QArgs a) {
     }
     if (tid < D)
       for (int r = 0; r < kC; ++r) msum += to_f32(sK[r * C::PQ + tid]);
-    __syncthreads();
+    lds_barrier();
   }
   float* dst = a.agg + ((size_t)bh * a.P + s) * a.sfl;
 #pragma unroll
@@ -648,7 +782,7 @@ __global__ __launch_bounds__(kNT) void cq_kernel(QArgs a) {
     const int r = i / kC, c = i % kC;
     if ((c >> 4) > (r >> 4)) sP[r * C::PP + c] = cvt<T>(0.f);
   }
-  __syncthreads();
+  lds_barrier();
   if (owner && g == 0) {
     const T hi = cvt<T>(mv);
     sDot[2 * C::PQ + 16 * cw + l16] = hi;
@@ -660,7 +794,7 @@ __global__ __launch_bounds__(kNT) void cq_kernel(QArgs a) {
   for (int64_t c0 = t0; c0 < t1; c0 += kC) {
     load_tile<T, D>(sm + C::o_q, a.q, bh, a.N, c0, t1);
     load_tile<T, D>(sm + C::o_k, a.k, bh, a.N, c0, t1);
-    __syncthreads();
+    lds_barrier();
     // ---- raw scores (lower, rounded once) and the gate / key-sum dots
     for (int t = w; t < 14; t += kNW) {
       if (t < 10) {
@@ -688,7 +822,7 @@ __global__ __launch_bounds__(kNT) void cq_kernel(QArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- per-row gate and coefficients
     if (w == 0) {
       const int i = l;
@@ -703,7 +837,7 @@ __global__ __launch_bounds__(kNT) void cq_kernel(QArgs a) {
       sAl[i] = al;
       sBe[i] = ok ? al * (mq + rs) / tc : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     // ---- delta for this wave's feature tile, the clean query, the running sums
     if (owner) {
       typename M::frag mh[C::NKD], ml[C::NKD];
@@ -758,7 +892,7 @@ __global__ __launch_bounds__(kNT) void cq_kernel(QArgs a) {
       }
       mv += cs[0];
     }
-    __syncthreads();  // all reads of sQ, sK, sP and the key-sum row are done
+    lds_barrier();  // all reads of sQ, sK, sP and the key-sum row are done
     if (owner && g == 0) {
       const T hi = cvt<T>(mv);
       sDot[2 * C::PQ + 16 * cw + l16] = hi;
@@ -779,6 +913,7 @@ __global__ __launch_bounds__(kNT) void cq_kernel(QArgs a) {
 template <typename T, int D>
 hipError_t run(const DeltaLaunch& L, hipStream_t st) {
   const int BH = (int)(L.B * L.H);
+  const int64_t nch = (L.N + kC - 1) / kC;
   if (L.ccq) {
     QArgs q;
     q.q = L.q;
@@ -806,12 +941,30 @@ hipError_t run(const DeltaLaunch& L, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  {
+    PArgs p;
+    p.k = L.k;
+    p.v = L.v;
+    p.g = L.g;
+    p.beta = L.beta;
+    p.w = L.wbuf;
+    p.ut = L.ubuf;
+    p.N = L.N;
+    // about four workgroups per CU over the whole launch
+    int64_t per = (nch * BH + 1023) / 1024;
+    if (per < 1) per = 1;
+    p.cpb = (int)per;
+    const unsigned nb = (unsigned)((nch + per - 1) / per);
+    hipLaunchKernelGGL((gdn_prep_kernel<T, D>), dim3(nb, (unsigned)BH), dim3(kNT), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   Args a;
   a.q = L.ccq ? L.qc : L.q;
   a.k = L.k;
-  a.v = L.v;
+  a.w = L.wbuf;
+  a.ut = L.ubuf;
   a.g = L.g;
-  a.beta = L.beta;
   a.out = L.out;
   a.state_in = L.state_in;
   a.state_out = L.state_out;

@@ -67,9 +67,10 @@ struct CcqPipeLaunch {
 };
 hipError_t ccq_pipe_launch(const CcqPipeLaunch& L, hipStream_t st);
 
-// Gated delta rule with the plain or the CCQ read (deltanet.hip). For CCQ a
-// clean-query pass (segment sums, then one chunk pass per segment) writes q'
-// to qc, and the chunk pass reads with it.
+// Gated delta rule with the plain or the CCQ read (deltanet.hip): a prepass
+// writes W and Ut of every chunk, then a sequential pass carries the state.
+// For CCQ a clean-query pass (segment sums, then one chunk pass per segment)
+// first writes q' to qc, and the sequential pass reads with it.
 struct DeltaLaunch {
   const void* q;
   const void* k;
@@ -79,6 +80,8 @@ struct DeltaLaunch {
   const float* w_lambda;  // CCQ only
   const float* b_lambda;  // CCQ only
   void* out;
+  void* wbuf;  // workspace [B,H,N,D] of the input dtype: W of every chunk
+  void* ubuf;  // workspace [B,H,N,dv] of the input dtype: Ut of every chunk
   void* qc;    // CCQ: workspace [B,H,N,D] of the input dtype
   float* agg;  // CCQ: workspace [B*H][P][cq_state_floats(D)]
   int64_t B, H, N, D, dv;

@@ -162,14 +162,17 @@ def test_deltanet_errors(fn, kw, code):
 @needs_lib
 def test_deltanet_workspaces():
     L = binding.lib()
-    # the plain read needs no workspace; the CCQ read holds the clean queries
-    assert L.deltanet_workspace_bytes(4, 16, 16384, 128, 128, 64, binding.LM_BF16, 0) == 0
+    # W and Ut of every chunk (the shapes of K and V); the CCQ read also holds
+    # the clean queries
+    tensor = 4 * 16 * 16384 * 128 * 2
+    assert L.deltanet_workspace_bytes(4, 16, 16384, 128, 128, 64, binding.LM_BF16, 0) == 2 * tensor
     n = L.ccq_deltanet_workspace_bytes(4, 16, 16384, 128, 128, 64, binding.LM_BF16, 0)
-    assert n >= 4 * 16 * 16384 * 128 * 2
+    assert n >= 3 * tensor
     st, _ = _delta(L, "ccq_deltanet_forward", wsb=16)
     assert st == binding.LM_EWORKSPACE
-    st, _ = _delta(L, "ccq_deltanet_forward", ws=None)
-    assert st == binding.LM_EINVAL
+    for fn in ("deltanet_chunk_forward", "ccq_deltanet_forward"):
+        st, _ = _delta(L, fn, ws=None)
+        assert st == binding.LM_EINVAL
     st, _ = _delta(L, "ccq_deltanet_forward", w=None)
     assert st == binding.LM_EINVAL
 
