@@ -232,10 +232,9 @@ int ccq_deltanet_forward(const void* q, const void* k, const void* v, const floa
 /*
  * Decayed linear attention with one decay per key feature (chunkwise).
  *   q, k, v, out, chunk as for linattn_chunk_forward
- *   g     [B,H,N,dk] float32, expected in (0, 1]: S_t = diag(g_t) S_{t-1} + k_t v_t^T,
- *         o_t = S_t^T q_t, S_0 = 0. Decays below 2^-15 act as 2^-15 (per token
- *         and feature), which bounds the scaled operands of the intra-chunk
- *         products.
+ *   g     [B,H,N,dk] float32, expected in [0, 1]: S_t = diag(g_t) S_{t-1} + k_t v_t^T,
+ *         o_t = S_t^T q_t, S_0 = 0, for every such g (chunks that hold a decay
+ *         below 2^-15 run the recurrence token by token, which is slower).
  *   g must be 16-byte aligned (it is read in 16-byte transfers).
  * Source: allinfo.ai.kr post on linear attention, "Key messages" (decay gates,
  * forgetting rates that can differ per channel).

@@ -17,9 +17,13 @@
 //        update  S  <- diag(2^(E_t - P_t)) S + sum_{j in t} (k_j * 2^(E_t - L_j)) v_j^T
 //    Every exponent there is <= 0. The diagonal scores A_ij = sum_a q_ia k_ja
 //    2^(L_ia - L_ja) are one 16 x 16 product per sub-chunk with both operands
-//    scaled about the sub-chunk's middle token; with log2 g clamped at -15 per
-//    token and feature, no scaled operand exceeds 2^120, so the product stays
+//    scaled about the sub-chunk's middle token; with every log2 g of the chunk
+//    at or above -15, no scaled operand exceeds 2^120, so the product stays
 //    finite where it is kept (j <= i).
+//  * A chunk that holds a decay below 2^-15 (g = 0 included) runs the
+//    recurrence itself instead, token by token on the fp32 state (the
+//    one-token step's arithmetic), so every g in (0, 1] is honoured exactly;
+//    the other chunks are unaffected.
 //  * Long sequences are cut into segments: a segment pass computes the S and
 //    the decay (per feature) of every sub-segment (two per segment when the
 //    segment length allows), a fixed-order scan leaves the state at every
@@ -31,7 +35,7 @@ namespace lm {
 namespace vec {
 
 constexpr int kC = 64;
-constexpr float kMinLog2G = -15.f;
+constexpr float kMinLog2G = -15.f;  // below this a chunk takes the token-by-token path
 
 struct Args {
   const void* q;
@@ -120,6 +124,7 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) T sA[AGG ? 1 : C::H2][4][16][C::AP];
   __shared__ float sTot[NW][D];
   __shared__ float sLseg[D];
+  __shared__ int sTiny[2];  // per chunk parity: the chunk holds a decay below 2^kMinLog2G
 
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15, tid = threadIdx.x;
   const int bh = blockIdx.y, p = blockIdx.x;
@@ -171,6 +176,7 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
     }
   }
   if (tid < D) sLseg[tid] = 0.f;
+  if (tid < 2) sTiny[tid] = 0;
 
   float gA[GR], gB[C::NBUF == 2 ? GR : 1];
   if constexpr (C::NBUF == 2) {
@@ -179,6 +185,49 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
       load_g(gA, t_begin);
     }
   }
+  // The chunk as the plain recurrence, token by token, on the fp32 state this
+  // wave holds (rows a = 16 kt + 4 g + r, column cbase + c16):
+  //   S <- diag(g_i) S + k_i v_i^T,  o_i = S^T q_i.
+  // The decay tile sG is overwritten with the raw decays first.
+  auto exact_chunk = [&](int64_t t0, const char* Qt, const char* Kt, const char* Vt) {
+    for (int idx = tid; idx < kC * D; idx += NT) {
+      const int r = idx / D, f = idx - (idx / D) * D;
+      Lat<CPRG>(sG, r, f) = t0 + r < N ? Gg[(size_t)(t0 + r) * D + f] : 1.f;
+    }
+    lds_barrier();
+    const int nrow = (int)(N - t0 < kC ? N - t0 : kC);
+    for (int i = 0; i < nrow; ++i) {
+      const float vi = to_f32(*reinterpret_cast<const T*>(Vt + tile_off<CPR, sizeof(T)>(i, cbase + c16)));
+      float part = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < DT; ++kt) {
+        float gi[4];
+        load_l<CPRG, 1>(sG, i, 16 * kt + 4 * g, gi);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int f = 16 * kt + 4 * g + r;
+          const float ki = to_f32(*reinterpret_cast<const T*>(Kt + tile_off<CPR, sizeof(T)>(i, f)));
+          S[kt][r] = gi[r] * S[kt][r] + ki * vi;
+          if constexpr (!AGG) part += S[kt][r] * to_f32(*reinterpret_cast<const T*>(Qt + tile_off<CPR, sizeof(T)>(i, f)));
+        }
+        // keeps the loads of one feature tile from being hoisted over the
+        // others (this path is for correctness, not speed, and shares the
+        // kernel's registers with the chunk form)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (!AGG) {
+        part = group_sum(part);
+        if (g == 0) Og[(size_t)(t0 + i) * D + cbase + c16] = from_f32<T>(part);
+      }
+    }
+    if constexpr (AGG) {
+      if (tid < D) {
+        float ll = 0.f;
+        for (int i = 0; i < nrow; ++i) ll += __builtin_amdgcn_logf(Lat<CPRG>(sG, i, tid));
+        sLseg[tid] += ll;
+      }
+    }
+  };
   // One chunk; gc holds its decays, gn receives the next chunk's.
   auto body = [&](int64_t t0, int it, float* gc, float* gn) {
     char* buf = sBuf[C::NBUF == 2 ? (it & 1) : 0];
@@ -203,16 +252,20 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
     {
       // the block's prefix stays in registers (gc is reused for it) until the
       // offset of the earlier blocks is known
+      bool tiny = false;
 #pragma unroll
       for (int i = 0; i < FPL; ++i) {
         float run = 0.f;
 #pragma unroll
         for (int rr = 0; rr < TPW; ++rr) {
-          run += fmaxf(__builtin_amdgcn_logf(gc[rr * FPL + i]), kMinLog2G);
+          const float lg = __builtin_amdgcn_logf(gc[rr * FPL + i]);
+          tiny = tiny || !(lg >= kMinLog2G);
+          run += fmaxf(lg, kMinLog2G);
           gc[rr * FPL + i] = run;
         }
         if (l + 64 * i < D) sTot[w][l + 64 * i] = run;
       }
+      if (__any(tiny) && l == 0) sTiny[it & 1] = 1;
       lds_barrier();
 #pragma unroll
       for (int i = 0; i < FPL; ++i) {
@@ -227,6 +280,17 @@ __global__ __launch_bounds__(D / 16 * 64) void vec_kernel(Args a) {
         }
       }
       lds_barrier();
+    }
+    // the flag of the chunk before this one was read by every wave long before
+    // this point, so its slot is cleared for the next chunk here
+    const bool exact = sTiny[it & 1] != 0;
+    if (tid == 0) sTiny[(it + 1) & 1] = 0;
+    if (exact) {
+      exact_chunk(t0, Qt, Kt, Vt);
+      if constexpr (C::NBUF == 2) {
+        if (t0 + kC < t_end) load_g(gn, t0 + kC);
+      }
+      return;
     }
 
     // ---- 2a. diagonal scores of the four sub-chunks, scaled about token 16t + 8
