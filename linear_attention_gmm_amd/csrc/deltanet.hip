@@ -378,7 +378,9 @@ __global__ __launch_bounds__(kNT) void gdn_prep_kernel(PArgs a) {
 // Sequential pass: per chunk, U = Ut - W S_0, O = diag(gamma) Q S_0 + P U with
 // P the decayed lower Q K^T, S_C = gamma_C S_0 + K^T diag(gamma_C / gamma) U.
 // The state chain per chunk is S_0 -> U -> S_C (two barriers); P and O hang
-// off it.
+// off it. The operand copies of S and U sit in LDS transposed ([column][k]):
+// an accumulator tile's four rows of one column are then one 8-byte store,
+// and every product reads both operands as k-contiguous 16-byte fragments.
 
 template <typename T, int D>
 struct MCfg {
@@ -386,21 +388,26 @@ struct MCfg {
   static constexpr int KS = Mma<T>::KS;
   static constexpr int NKD = D / KS;
   static constexpr int NKC = kC / KS;
-  static constexpr int PQ = D + 4;                      // Q, K, W rows
-  static constexpr int PV = kCG + (ES == 2 ? 8 : 4);    // Ut, S, U rows
-  static constexpr int PP = kC + (ES == 2 ? 8 : 4);     // P rows
+  static constexpr int PAD = ES == 2 ? 8 : 4;
+  static constexpr int PQ = D + PAD;    // Q, K, W rows (token-major)
+  static constexpr int PV = kCG + PAD;  // Ut rows (token-major)
+  static constexpr int PS = D + PAD;    // S^T rows (column-major S: [column][feature])
+  static constexpr int PU = kC + PAD;   // U^T rows ([column][token]), P rows
   static constexpr int o_q = 0;
   static constexpr int o_k = o_q + kC * PQ * ES;
   static constexpr int o_w = o_k + kC * PQ * ES;
   static constexpr int o_ut = o_w + kC * PQ * ES;
   static constexpr int o_s = o_ut + kC * PV * ES;
-  static constexpr int o_u = o_s + D * PV * ES;
-  static constexpr int o_p = o_u + kC * PV * ES;
-  static constexpr int o_row = o_p + kC * PP * ES;  // [3][64] f32: l, gamma_C / gamma, gamma
+  static constexpr int o_u = o_s + kCG * PS * ES;
+  static constexpr int o_ud = o_u + kCG * PU * ES;
+  static constexpr int o_p = o_ud + kCG * PU * ES;
+  static constexpr int o_row = o_p + kC * PU * ES;  // [3][64] f32: l, gamma_C / gamma, gamma
   static constexpr int bytes = o_row + 3 * kC * 4;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(o_k % 16 == 0 && o_w % 16 == 0 && o_ut % 16 == 0 && o_s % 16 == 0 && o_u % 16 == 0 &&
-                    o_p % 16 == 0 && o_row % 16 == 0, "16-byte aligned regions");
+                    o_ud % 16 == 0 && o_p % 16 == 0 && o_row % 16 == 0 && (PQ * ES) % 16 == 0 &&
+                    (PS * ES) % 16 == 0 && (PU * ES) % 16 == 0,
+                "16-byte aligned regions and rows");
   static constexpr int NST = 2 * D / 16;  // S tiles of the column group
   static constexpr int SPW = (NST + kNW - 1) / kNW;
 };
@@ -423,25 +430,43 @@ struct Args {
   int dv;
 };
 
-// A operand (CHAIN order) of K^T for feature tile a, token k-step ks, scaled per
-// token by sc[token].
+// Four rows (r0 .. r0 + 3) of one column of an accumulator tile, stored as
+// four consecutive elements of a transposed LDS tile.
 template <typename T>
-__device__ __forceinline__ typename Mma<T>::frag scaled_kt(const T* sK, int pitch, int a, int ks, const float* sc) {
-  typename Mma<T>::frag f = ld_km_chain(sK, pitch, 16 * a, ks);
+__device__ __forceinline__ void put_col4(T* p, const f32x4& v) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+
+// NATURAL operand fragment with k along the rows of a token-major tile and the
+// operand's row/column = tile column c0 + lane % 16 (bf16: two transpose reads).
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag km_nat(const T* base, int pitch, int c0, int ks) {
   const int g = lane_id() >> 4;
   if constexpr (sizeof(T) == 2) {
-    const int k0 = ks * 32 + 4 * g;
-    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sc + k0);
-    const f32x4 s1 = *reinterpret_cast<const f32x4*>(sc + k0 + 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[i] = (bf16)((float)f[i] * s0[i]);
-      f[4 + i] = (bf16)((float)f[4 + i] * s1[i]);
-    }
+    const bf16x4 lo = tr16(base, pitch, c0, ks * 32 + 8 * g);
+    const bf16x4 hi = tr16(base, pitch, c0, ks * 32 + 8 * g + 4);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   } else {
-    f *= sc[16 * (ks >> 2) + 4 * g + (ks & 3)];
+    return base[(ks * 4 + g) * pitch + c0 + (lane_id() & 15)];
   }
-  return f;
+}
+
+// An accumulator-layout tile (rows r0 + 4 g .. + 3, column c0 + lane % 16) of a
+// token-major LDS tile.
+template <typename T>
+__device__ __forceinline__ f32x4 acc_tile(const T* base, int pitch, int r0, int c0) {
+  const int g = lane_id() >> 4, c = lane_id() & 15;
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 x = tr16(base, pitch, c0, r0 + 4 * g);
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+  } else {
+    return f32x4{base[(r0 + 4 * g) * pitch + c0 + c], base[(r0 + 4 * g + 1) * pitch + c0 + c],
+                 base[(r0 + 4 * g + 2) * pitch + c0 + c], base[(r0 + 4 * g + 3) * pitch + c0 + c]};
+  }
 }
 
 template <typename T, int D>
@@ -453,9 +478,10 @@ __global__ __launch_bounds__(kNT, 2) void gdn_kernel(Args a) {
   T* sK = reinterpret_cast<T*>(sm + C::o_k);
   T* sW = reinterpret_cast<T*>(sm + C::o_w);
   T* sUt = reinterpret_cast<T*>(sm + C::o_ut);
-  T* sS = reinterpret_cast<T*>(sm + C::o_s);
-  T* sU = reinterpret_cast<T*>(sm + C::o_u);
-  T* sP = reinterpret_cast<T*>(sm + C::o_p);
+  T* sS = reinterpret_cast<T*>(sm + C::o_s);    // S^T: [column][feature]
+  T* sU = reinterpret_cast<T*>(sm + C::o_u);    // U^T: [column][token]
+  T* sUd = reinterpret_cast<T*>(sm + C::o_ud);  // (diag(gamma_C / gamma) U)^T
+  T* sP = reinterpret_cast<T*>(sm + C::o_p);    // P: [query][key]
   float* sL = reinterpret_cast<float*>(sm + C::o_row);  // running log2 decay
   float* sDc = sL + kC;                                  // gamma_C / gamma_j
   float* sGm = sL + 2 * kC;                              // gamma_j
@@ -469,9 +495,10 @@ __global__ __launch_bounds__(kNT, 2) void gdn_kernel(Args a) {
   const T* ub = static_cast<const T*>(a.ut) + (size_t)bh * a.N * a.dv + cg * kCG;
   const float* gb = a.g + (size_t)bh * a.N;
 
+  // upper tiles of P stay zero (read by the k-steps that straddle the diagonal)
   for (int i = tid; i < kC * kC; i += kNT) {
     const int r = i / kC, c = i % kC;
-    if ((c >> 4) > (r >> 4)) sP[r * C::PP + c] = cvt<T>(0.f);
+    if ((c >> 4) > (r >> 4)) sP[r * C::PU + c] = cvt<T>(0.f);
   }
 
   // this wave's S tiles: t = w + kNW j, tile (t / 2, t % 2)
@@ -505,7 +532,7 @@ __global__ __launch_bounds__(kNT, 2) void gdn_kernel(Args a) {
 
   for (int64_t ch = 0; ch < nch; ++ch) {
     const int64_t c0 = ch * kC;
-    // ---- inputs to LDS, the state to its operand copy, next chunk's loads
+    // ---- inputs to LDS, the state to its operand copy
     pq.store(sQ, C::PQ);
     pk.store(sK, C::PQ);
     pw.store(sW, C::PQ);
@@ -513,11 +540,7 @@ __global__ __launch_bounds__(kNT, 2) void gdn_kernel(Args a) {
 #pragma unroll
     for (int j = 0; j < C::SPW; ++j) {
       const int t = w + kNW * j;
-      if (t < C::NST) {
-        const int ra = 16 * (t >> 1), col = 16 * (t & 1) + l16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sS[(ra + 4 * g + e) * C::PV + col] = cvt<T>(St[j][e]);
-      }
+      if (t < C::NST) put_col4(sS + (16 * (t & 1) + l16) * C::PS + 16 * (t >> 1) + 4 * g, St[j]);
     }
     if (w == 0) {
       const float lr = chunk_log2_decay(pg);
@@ -528,33 +551,43 @@ __global__ __launch_bounds__(kNT, 2) void gdn_kernel(Args a) {
     }
     lds_barrier();
 
-    // ---- U = Ut - W S_0 (this wave's tile); P tiles
+    // ---- U = Ut - W S_0 (this wave's tile), stored transposed, plainly and
+    //      scaled by gamma_C / gamma_j; the P tiles (as P^T tiles, so that a
+    //      lane's four entries are consecutive in a row of P)
     {
       f32x4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < C::NKD; ++ks)
-        acc = M::mma(ld_kc_chain(sW, C::PQ, 16 * r_own + l16, ks), ld_km_chain(sS, C::PV, 16 * c_own, ks), acc);
+        acc = M::mma(ld_kc_nat(sW, C::PQ, 16 * r_own + l16, ks), ld_kc_nat(sS, C::PS, 16 * c_own + l16, ks), acc);
+      const f32x4 ut = acc_tile(sUt, C::PV, 16 * r_own, 16 * c_own);
+      const f32x4 dc = *reinterpret_cast<const f32x4*>(sDc + 16 * r_own + 4 * g);
+      f32x4 u, ud;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * r_own + 4 * g + e;
-        const int col = 16 * c_own + l16;
-        sU[i * C::PV + col] = cvt<T>(to_f32(sUt[i * C::PV + col]) - acc[e]);
+        u[e] = ut[e] - acc[e];
+        ud[e] = u[e] * dc[e];
       }
+      const int off = (16 * c_own + l16) * C::PU + 16 * r_own + 4 * g;
+      put_col4(sU + off, u);
+      put_col4(sUd + off, ud);
     }
     for (int t = w; t < 10; t += kNW) {
       int it, jt;
       tri_tile(t, it, jt);
-      f32x4 acc = zero4();
+      f32x4 acc = zero4();  // element (key j = 16 jt + 4 g + e, query i = 16 it + l16)
 #pragma unroll
       for (int ks = 0; ks < C::NKD; ++ks)
-        acc = M::mma(ld_kc_chain(sQ, C::PQ, 16 * it + l16, ks), ld_kc_chain(sK, C::PQ, 16 * jt + l16, ks), acc);
-      const int j = 16 * jt + l16;
-      const float lj = sL[j];
+        acc = M::mma(ld_kc_nat(sK, C::PQ, 16 * jt + l16, ks), ld_kc_nat(sQ, C::PQ, 16 * it + l16, ks), acc);
+      const int i = 16 * it + l16;
+      const float li = sL[i];
+      const f32x4 lj = *reinterpret_cast<const f32x4*>(sL + 16 * jt + 4 * g);
+      f32x4 p;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * it + 4 * g + e;
-        sP[i * C::PP + j] = cvt<T>(j <= i ? fast_exp2(fminf(sL[i] - lj, 0.f)) * acc[e] : 0.f);
+        const int j = 16 * jt + 4 * g + e;
+        p[e] = j <= i ? fast_exp2(fminf(li - lj[e], 0.f)) * acc[e] : 0.f;
       }
+      put_col4(sP + i * C::PU + 16 * jt + 4 * g, p);
     }
     lds_barrier();
     if (ch + 1 < nch) fetch(c0 + kC);  // held in registers through the last phase only
@@ -569,7 +602,7 @@ __global__ __launch_bounds__(kNT, 2) void gdn_kernel(Args a) {
           f32x4 acc = zero4();
 #pragma unroll
           for (int ks = 0; ks < C::NKC; ++ks)
-            acc = M::mma(scaled_kt<T>(sK, C::PQ, t >> 1, ks, sDc), ld_km_chain(sU, C::PV, 16 * (t & 1), ks), acc);
+            acc = M::mma(km_nat(sK, C::PQ, 16 * (t >> 1), ks), ld_kc_nat(sUd, C::PU, 16 * (t & 1) + l16, ks), acc);
 #pragma unroll
           for (int e = 0; e < 4; ++e) St[j][e] = gc * St[j][e] + acc[e];
         }
@@ -580,15 +613,16 @@ __global__ __launch_bounds__(kNT, 2) void gdn_kernel(Args a) {
       f32x4 acc = zero4(), acc2 = zero4();
 #pragma unroll
       for (int ks = 0; ks < C::NKD; ++ks)
-        acc = M::mma(ld_kc_chain(sQ, C::PQ, 16 * r_own + l16, ks), ld_km_chain(sS, C::PV, 16 * c_own, ks), acc);
+        acc = M::mma(ld_kc_nat(sQ, C::PQ, 16 * r_own + l16, ks), ld_kc_nat(sS, C::PS, 16 * c_own + l16, ks), acc);
       const int nk = tok_steps<T>(r_own);
       for (int ks = 0; ks < nk; ++ks)
-        acc2 = M::mma(ld_kc_chain(sP, C::PP, 16 * r_own + l16, ks), ld_km_chain(sU, C::PV, 16 * c_own, ks), acc2);
+        acc2 = M::mma(ld_kc_nat(sP, C::PU, 16 * r_own + l16, ks), ld_kc_nat(sU, C::PU, 16 * c_own + l16, ks), acc2);
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(sGm + 16 * r_own + 4 * g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * r_own + 4 * g + e;
         if (c0 + i < a.N)
-          outp[((size_t)bh * a.N + c0 + i) * a.dv + cg * kCG + 16 * c_own + l16] = cvt<T>(acc[e] * sGm[i] + acc2[e]);
+          outp[((size_t)bh * a.N + c0 + i) * a.dv + cg * kCG + 16 * c_own + l16] = cvt<T>(acc[e] * gm[e] + acc2[e]);
       }
     }
     lds_barrier();
