@@ -171,6 +171,17 @@ __device__ __forceinline__ float chunk_log2_decay(float g) {
   return wave_scan_incl(fmaxf(__builtin_amdgcn_logf(g), kMinLog2));
 }
 
+// Four rows (r0 .. r0 + 3) of one column of an accumulator tile, stored as
+// four consecutive elements of a transposed LDS tile.
+template <typename T>
+__device__ __forceinline__ void put_col4(T* p, const f32x4& v) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Prepass: for every chunk, T = (I + A)^{-1}, W = T diag(beta gamma) K and
 // Ut = T diag(beta) V, written to the workspace in the layouts of K and V.
@@ -184,17 +195,18 @@ struct PCfg {
   static constexpr int PAD = ES == 2 ? 8 : 4;
   static constexpr int PQ = D + PAD;  // K, V, and the W / Ut staging rows
   static constexpr int PA = kC + 4;   // A, T rows (fp32)
+  // The W and Ut staging tiles reuse the A and T tiles once T is formed.
   static constexpr int o_k = 0;
   static constexpr int o_v = o_k + kC * PQ * ES;
-  static constexpr int o_w = o_v + kC * PQ * ES;
-  static constexpr int o_u = o_w + kC * PQ * ES;
-  static constexpr int o_a = o_u + kC * PQ * ES;
+  static constexpr int o_a = o_v + kC * PQ * ES;
   static constexpr int o_t = o_a + kC * PA * 4;
   static constexpr int o_row = o_t + kC * PA * 4;  // [3][64] f32: l, beta, beta gamma
+  static constexpr int o_w = o_a;
+  static constexpr int o_u = o_t;
   static constexpr int bytes = o_row + 3 * kC * 4;
-  static_assert(bytes <= 160 * 1024, "LDS budget");
-  static_assert(o_v % 16 == 0 && o_w % 16 == 0 && o_u % 16 == 0 && o_a % 16 == 0 && o_t % 16 == 0 &&
-                    o_row % 16 == 0, "16-byte aligned regions");
+  static_assert(PQ * ES <= PA * 4, "staging rows fit the A and T rows");
+  static_assert(bytes <= 80 * 1024, "two workgroups per CU");
+  static_assert(o_v % 16 == 0 && o_a % 16 == 0 && o_t % 16 == 0 && o_row % 16 == 0, "16-byte aligned regions");
   static constexpr int FPW = D / 32;  // W (and Ut) column tiles per wave
 };
 
@@ -210,7 +222,7 @@ struct PArgs {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kNT) void gdn_prep_kernel(PArgs a) {
+__global__ __launch_bounds__(kNT, sizeof(T) == 2 ? 4 : 2) void gdn_prep_kernel(PArgs a) {
   typedef PCfg<T, D> C;
   typedef Mma<T> M;
   __shared__ __attribute__((aligned(16))) char sm[C::bytes];
@@ -235,11 +247,6 @@ __global__ __launch_bounds__(kNT) void gdn_prep_kernel(PArgs a) {
   const float* gb = a.g + (size_t)bh * a.N;
   const float* bb = a.beta + (size_t)bh * a.N;
 
-  // upper tiles of T stay zero (read by the k-steps that straddle the diagonal)
-  for (int i = tid; i < kC * kC; i += kNT) {
-    const int r = i / kC, c = i % kC;
-    if ((c >> 4) > (r >> 4)) sT[r * C::PA + c] = 0.f;
-  }
   RowVecs<T, D, D> pk, pv;
   float pg = 1.f, pb = 0.f;
   auto fetch = [&](int64_t c0) {
@@ -261,29 +268,40 @@ __global__ __launch_bounds__(kNT) void gdn_prep_kernel(PArgs a) {
       sBt[l] = pb;
       sSw[l] = pb * fast_exp2(lr);
     }
-    if (ch + 1 < ch1) fetch(c0 + kC);
     lds_barrier();
 
-    // A = strictly lower, beta-scaled, decayed K K^T (fp32)
+    // A = strictly lower, beta-scaled, decayed K K^T (fp32), formed as A^T
+    // tiles so that a lane's four entries are consecutive in a row of A
     for (int t = w; t < 10; t += kNW) {
       int it, jt;
       tri_tile(t, it, jt);
-      f32x4 acc = zero4();
+      f32x4 acc = zero4();  // element (key j = 16 jt + 4 g + e, row i = 16 it + l16)
 #pragma unroll
       for (int ks = 0; ks < C::NKD; ++ks)
-        acc = M::mma(ld_kc_chain(sK, C::PQ, 16 * it + l16, ks), ld_kc_chain(sK, C::PQ, 16 * jt + l16, ks), acc);
-      const int j = 16 * jt + l16;
-      const float lj = sL[j];
+        acc = M::mma(ld_kc_nat(sK, C::PQ, 16 * jt + l16, ks), ld_kc_nat(sK, C::PQ, 16 * it + l16, ks), acc);
+      const int i = 16 * it + l16;
+      const float li = sL[i], bi = sBt[i];
+      const f32x4 lj = *reinterpret_cast<const f32x4*>(sL + 16 * jt + 4 * g);
+      f32x4 av;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * it + 4 * g + e;
-        sA[i * C::PA + j] = j < i ? sBt[i] * fast_exp2(fminf(sL[i] - lj, 0.f)) * acc[e] : 0.f;
+        const int j = 16 * jt + 4 * g + e;
+        av[e] = j < i ? bi * fast_exp2(fminf(li - lj[e], 0.f)) * acc[e] : 0.f;
       }
+      *reinterpret_cast<f32x4*>(sA + i * C::PA + 16 * jt + 4 * g) = av;
     }
     lds_barrier();
 
     // T: diagonal blocks by forward substitution (wave 0: lane group = block,
-    // lane = column), two partial sums to halve the dependent chain
+    // lane = column), two partial sums to halve the dependent chain. The other
+    // waves clear tiles (0, 1) and (2, 3), which the k-steps that straddle the
+    // diagonal read (the Ut staging of the previous chunk overwrote them).
+    if (w > 0) {
+      for (int i = tid - 64; i < 2 * 256; i += kNT - 64) {
+        const int t = i >> 8, e = i & 255;
+        sT[(32 * t + (e >> 4)) * C::PA + 32 * t + 16 + (e & 15)] = 0.f;
+      }
+    }
     if (w == 0) {
       const int b0 = 16 * g, c = l16;
       float x[16];
@@ -299,6 +317,7 @@ __global__ __launch_bounds__(kNT) void gdn_prep_kernel(PArgs a) {
             s0 -= arow[i] * x[i];
         }
         x[r] = s0 + s1;
+        __builtin_amdgcn_sched_barrier(0);  // one row's loads at a time (registers)
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sT[(b0 + r) * C::PA + b0 + c] = x[r];
@@ -339,24 +358,30 @@ __global__ __launch_bounds__(kNT) void gdn_prep_kernel(PArgs a) {
           aw[ks] = scaled_row<T>(sT, C::PA, 16 * r + l16, ks, sSw);
           au[ks] = scaled_row<T>(sT, C::PA, 16 * r + l16, ks, sBt);
         }
-#pragma unroll
+      lds_barrier();  // every wave holds its rows of T: the staging may overwrite A and T
+      // as W^T and Ut^T tiles (rows = features of column tile f, columns =
+      // tokens of row tile r), so that a lane's four entries are consecutive
+      // in a row of W (Ut)
+#pragma unroll 1
       for (int fi = 0; fi < C::FPW; ++fi) {
         const int f = h * C::FPW + fi;
         f32x4 cw = zero4(), cu = zero4();
 #pragma unroll
         for (int ks = 0; ks < NKT; ++ks)
           if (ks < nk) {
-            cw = M::mma(aw[ks], ld_km_chain(sK, C::PQ, 16 * f, ks), cw);
-            cu = M::mma(au[ks], ld_km_chain(sV, C::PQ, 16 * f, ks), cu);
+            cw = M::mma(ld_km_chain(sK, C::PQ, 16 * f, ks), aw[ks], cw);
+            cu = M::mma(ld_km_chain(sV, C::PQ, 16 * f, ks), au[ks], cu);
           }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sW[(16 * r + 4 * g + e) * C::PQ + 16 * f + l16] = cvt<T>(cw[e]);
-          sU[(16 * r + 4 * g + e) * C::PQ + 16 * f + l16] = cvt<T>(cu[e]);
-        }
+        const int off = (16 * r + l16) * C::PQ + 16 * f + 4 * g;
+        put_col4(sW + off, cw);
+        put_col4(sU + off, cu);
       }
     }
     lds_barrier();
+    // the next chunk's rows load while this one's are written out (issued this
+    // late so that they hold no registers during T and W; the other workgroup
+    // on the CU covers their latency)
+    if (ch + 1 < ch1) fetch(c0 + kC);
     // rows to the workspace, 16 bytes per lane
     {
       constexpr int VR = D * (int)sizeof(T) / 16;
@@ -429,17 +454,6 @@ struct Args {
   int BH;
   int dv;
 };
-
-// Four rows (r0 .. r0 + 3) of one column of an accumulator tile, stored as
-// four consecutive elements of a transposed LDS tile.
-template <typename T>
-__device__ __forceinline__ void put_col4(T* p, const f32x4& v) {
-  if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-  } else {
-    *reinterpret_cast<f32x4*>(p) = v;
-  }
-}
 
 // NATURAL operand fragment with k along the rows of a token-major tile and the
 // operand's row/column = tile column c0 + lane % 16 (bf16: two transpose reads).
