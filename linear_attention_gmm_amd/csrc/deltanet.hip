@@ -709,24 +709,6 @@ struct QArgs {
   int H, BH, P, sfl;
 };
 
-// Loads rows [c0, c0 + 64) of X [BH][N][D] into an LDS tile.
-// Rows at or past `limit` read as zero.
-template <typename T, int D>
-__device__ __forceinline__ void load_tile(char* dst, const void* src, int bh, int64_t N, int64_t c0, int64_t limit) {
-  typedef QCfg<T, D> C;
-  const char* base = static_cast<const char*>(src) + (size_t)bh * N * D * C::ES;
-#pragma unroll
-  for (int i = 0; i < C::NQ; ++i) {
-    const int p = threadIdx.x + i * kNT;
-    if (p < kC * C::VR) {
-      const int row = p / C::VR, cv = p % C::VR;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (c0 + row < limit) x = *reinterpret_cast<const uint4*>(base + (size_t)(c0 + row) * D * C::ES + (size_t)cv * 16);
-      *reinterpret_cast<uint4*>(dst + row * C::PQ * C::ES + cv * 16) = x;
-    }
-  }
-}
-
 // Segment pass: sums of k k^T and k over segment blockIdx.x of (b, h) blockIdx.y.
 template <typename T, int D>
 __global__ __launch_bounds__(kNT) void cq_agg_kernel(QArgs a) {
@@ -742,9 +724,13 @@ __global__ __launch_bounds__(kNT) void cq_agg_kernel(QArgs a) {
 #pragma unroll
   for (int j = 0; j < C::MPW; ++j) acc[j] = zero4();
   float msum = 0.f;
+  const T* kb = static_cast<const T*>(a.k) + (size_t)bh * a.N * D;
+  RowVecs<T, D, D> pk;  // the next chunk's keys (rows past the segment end read as zero)
+  pk.load(kb, t0, t1);
   for (int64_t c0 = t0; c0 < t1; c0 += kC) {
-    load_tile<T, D>(sm + C::o_k, a.k, bh, a.N, c0, t1);  // rows past the segment end read as zero
+    pk.store(sK, C::PQ);
     lds_barrier();
+    if (c0 + kC < t1) pk.load(kb, c0 + kC, t1);
 #pragma unroll
     for (int j = 0; j < C::MPW; ++j) {
       const int t = w + kNW * j;
@@ -839,10 +825,19 @@ __global__ __launch_bounds__(kNT) void cq_kernel(QArgs a) {
   const float bias = a.b_lambda[h];
   T* qcp = static_cast<T*>(a.qc);
 
+  const T* qb = static_cast<const T*>(a.q) + (size_t)bh * a.N * D;
+  const T* kb = static_cast<const T*>(a.k) + (size_t)bh * a.N * D;
+  RowVecs<T, D, D> pq, pk;  // the next chunk's rows (past the segment end: zero)
+  pq.load(qb, t0, t1);
+  pk.load(kb, t0, t1);
   for (int64_t c0 = t0; c0 < t1; c0 += kC) {
-    load_tile<T, D>(sm + C::o_q, a.q, bh, a.N, c0, t1);
-    load_tile<T, D>(sm + C::o_k, a.k, bh, a.N, c0, t1);
+    pq.store(sQ, C::PQ);
+    pk.store(sK, C::PQ);
     lds_barrier();
+    if (c0 + kC < t1) {
+      pq.load(qb, c0 + kC, t1);
+      pk.load(kb, c0 + kC, t1);
+    }
     // ---- raw scores (lower, rounded once) and the gate / key-sum dots
     for (int t = w; t < 14; t += kNW) {
       if (t < 10) {
@@ -875,7 +870,13 @@ __global__ __launch_bounds__(kNT) void cq_kernel(QArgs a) {
     if (w == 0) {
       const int i = l;
       float rs = 0.f;
-      for (int j = 0; j < kC; ++j) rs += to_f32(sP[i * C::PP + j]);
+      typedef typename Vec16<T>::type vec;
+#pragma unroll
+      for (int j = 0; j < kC; j += Vec16<T>::n) {
+        const vec x = *reinterpret_cast<const vec*>(sP + i * C::PP + j);
+#pragma unroll
+        for (int e = 0; e < Vec16<T>::n; ++e) rs += to_f32(x[e]);
+      }
       const float wq = sRd[i * 4 + 0] + sRd[i * 4 + 1];
       const float mq = sRd[i * 4 + 2] + sRd[i * 4 + 3];
       const float lam = 1.f / (1.f + __expf(-(wq + bias)));
