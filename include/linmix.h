@@ -78,6 +78,21 @@
  *    needs the number of tokens it holds, which the caller passes (t_in,
  *    t_prev); all (b, h) of one call hold the same number.
  *
+ * Feature widths. The forwards without a carried state (gma_forward,
+ * linattn_chunk_forward, ccq_forward, linattn_vec_forward,
+ * deltanet_chunk_forward, ccq_deltanet_forward) take feature widths d (dk)
+ * and dv in {16, 32, 64, 128}, equal or not. d == dv in {32, 64, 128} runs
+ * directly; any other pair runs on the kernels of width D, the smallest of
+ * 32, 64, 128 that holds both, after zero padding of the feature axis, which
+ * is exact (a routing feature with x = mu = 0 and log variance 0 adds the same
+ * constant to every component's log joint; a zero key or query feature adds
+ * nothing to any product, key covariance or norm; zero value columns give
+ * output columns that are dropped). Such a call needs, in its workspace, the
+ * padded Q, K, V and output (4 B*H*N*D elements of dtype), the padded
+ * per-head parameters and the workspace of the width-D call. Carried states,
+ * decode steps, backward passes and gma_forward_noalloc take d == dv in
+ * {32, 64, 128} only.
+ *
  * Conventions common to every entry point
  *  - Pointers named q, k, v, g, mu, ..., out, workspace are DEVICE pointers on
  *    the current HIP device. Tensors are dense and row-major in the layouts given
@@ -144,7 +159,7 @@ const char* lm_last_error(void);
  *   out      [B,H,N,dv]  O = Gamma_Q Vtil / (Gamma_Q Z + eps) (dtype)
  *   causal   1: row i reads the memory of keys j <= i; 0: of all keys
  *   eps      >= 0, added to the read normaliser
- * Implemented shapes: d and dv in {32, 64, 128} with d == dv, 1 <= K <= 256,
+ * Implemented shapes: d, dv in {16, 32, 64, 128} (see "Feature widths"), 1 <= K <= 256,
  * any N >= 1.
  */
 size_t gma_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv,
@@ -160,7 +175,7 @@ int gma_forward(const void* q, const void* k, const void* v, const float* mu,
  *   g     [B,H,N]    per-token, per-head decay (float32), expected in (0, 1]
  *   out   [B,H,N,dv] o_t = S_t^T q_t with S_t = g_t S_{t-1} + k_t v_t^T, S_0 = 0
  *   chunk tokens per chunk; 64 is implemented
- * Implemented shapes: dk == dv in {32, 64, 128}, any N >= 1.
+ * Implemented shapes: dk, dv in {16, 32, 64, 128} (see "Feature widths"), any N >= 1.
  */
 size_t linattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
                                int64_t chunk, int dtype, int64_t segments);
@@ -176,7 +191,7 @@ int linattn_chunk_forward(const void* q, const void* k, const void* v, const flo
  *            lambda_t = sigmoid(w_lambda[h] . q_t + b_lambda[h])
  *   out      o_t = S_t^T (q_t - lambda_t Sigma_t q_t), Sigma_t = (1/t) sum_{j<=t}
  *            k_j k_j^T - mu_t mu_t^T, mu_t = (1/t) sum_{j<=t} k_j (no decay)
- * Implemented shapes: dk == dv in {32, 64, 128}, any N >= 1.
+ * Implemented shapes: dk, dv in {16, 32, 64, 128} (see "Feature widths"), any N >= 1.
  */
 size_t ccq_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
                            int64_t chunk, int dtype, int64_t segments);
@@ -201,8 +216,9 @@ int ccq_forward(const void* q, const void* k, const void* v, const float* g,
  *         across workgroups: B*H*dv/32 of them).
  * Workspace (deltanet_workspace_bytes): W = T diag(beta gamma) K and
  * T diag(beta) V of every chunk, B*H*N*(dk + dv) elements of dtype.
- * Implemented shapes: dk == dv in {32, 64, 128} for bf16, {32, 64} for
- * float32; any N >= 1.
+ * Implemented shapes: dk, dv in {16, 32, 64, 128} (see "Feature widths")
+ * whose padded width is at most 128 for bf16 and at most 64 for float32; any
+ * N >= 1.
  */
 size_t deltanet_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
                                 int64_t chunk, int dtype, int64_t segments);
@@ -238,7 +254,8 @@ int ccq_deltanet_forward(const void* q, const void* k, const void* v, const floa
  *   g must be 16-byte aligned (it is read in 16-byte transfers).
  * Source: allinfo.ai.kr post on linear attention, "Key messages" (decay gates,
  * forgetting rates that can differ per channel).
- * Implemented shapes: dk == dv in {32, 64, 128}, chunk 64, any N >= 1.
+ * Implemented shapes: dk, dv in {16, 32, 64, 128} (see "Feature widths"), chunk 64,
+ * any N >= 1.
  */
 size_t linattn_vec_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
                                    int64_t chunk, int dtype, int64_t segments);

@@ -6,7 +6,9 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
+#include <utility>
 
 #include "../../include/linmix.h"
 #include "launch.hpp"
@@ -579,6 +581,215 @@ CcqBwdLayout ccq_bwd_layout(int64_t B, int64_t H, int64_t N, int64_t D, int dtyp
   return L;
 }
 
+// ----------------------------------------------------------------------------- padded shapes
+//
+// Feature widths of 16, and d != dv, run on the kernels of width D (the
+// smallest of 32, 64, 128 that holds both) after zero padding of the feature
+// axis (pad.hip; exact, see there). The padded tensors and the output sit in
+// the workspace ahead of the inner call's own workspace. Stateless forwards
+// only: carried states, decode steps, backward passes and the entry point that
+// allocates nothing take the native shapes (d == dv in {32, 64, 128}).
+
+bool width_ok(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool native_widths(int64_t d, int64_t dv) { return d == dv && d != 16; }
+int64_t pad_width(int64_t d, int64_t dv) {
+  const int64_t m = d > dv ? d : dv;
+  return m <= 32 ? 32 : m <= 64 ? 64 : 128;
+}
+
+int pad_check(const char* fn, int64_t d, int64_t dv) {
+  if (d < 1 || dv < 1) return fail(LM_EINVAL, "%s: sizes must be >= 1", fn);
+  if (!width_ok(d) || !width_ok(dv))
+    return fail(LM_EUNSUPPORTED, "%s implements feature widths in {16, 32, 64, 128} (got %lld and %lld)", fn,
+                (long long)d, (long long)dv);
+  return LM_OK;
+}
+
+struct PadLayout {
+  int64_t D;
+  size_t q, k, v, out, g, w, mu, lv, inner, total;
+};
+
+// q, k [.., d] -> [.., D]; v [.., dv] -> [.., D]; the output [.., D]; optional
+// per-feature decays [.., D] (vec), gate weights [H, D] (w) or routing
+// parameters [H, K, D] (mu, log_var; K > 0); then `inner` bytes.
+PadLayout pad_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, bool vec, bool w, int64_t K,
+                     size_t inner) {
+  PadLayout L{};
+  L.D = pad_width(d, dv);
+  const size_t rows = (size_t)B * H * N, es = esize(dtype), t = align_up(rows * L.D * es);
+  size_t off = 0;
+  L.q = off;
+  off += t;
+  L.k = off;
+  off += t;
+  L.v = off;
+  off += t;
+  L.out = off;
+  off += t;
+  L.g = off;
+  if (vec) off += align_up(rows * L.D * 4);
+  L.w = off;
+  if (w) off += align_up((size_t)H * L.D * 4);
+  L.mu = off;
+  if (K) off += align_up((size_t)H * K * L.D * 4);
+  L.lv = off;
+  if (K) off += align_up((size_t)H * K * L.D * 4);
+  L.inner = off;
+  L.total = align_up(off + inner);
+  return L;
+}
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// The caller's pointers of a padded call: null, alignment, and out against the
+// inputs and the workspace.
+int pad_args(const char* fn, std::initializer_list<const void*> need, const void* out, size_t nout,
+             std::initializer_list<std::pair<const void*, size_t>> inputs, const void* ws, size_t nws) {
+  for (const void* p : need)
+    if (!p) return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!out || !ws) return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned(out, 16) || !aligned(ws, 16)) return fail(LM_EINVAL, "%s: misaligned out or workspace", fn);
+  for (const auto& in : inputs) {
+    if (!aligned(in.first, 4)) return fail(LM_EINVAL, "%s: misaligned pointer", fn);
+    if (overlap(out, nout, in.first, in.second)) return fail(LM_EINVAL, "%s: out overlaps an input", fn);
+    if (overlap(ws, nws, in.first, in.second)) return fail(LM_EINVAL, "%s: an input overlaps the workspace", fn);
+  }
+  if (overlap(out, nout, ws, nws)) return fail(LM_EINVAL, "%s: out overlaps the workspace", fn);
+  return LM_OK;
+}
+
+int hip_fail(const char* fn, hipError_t e) { return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e)); }
+
+int gma_padded(const char* fn, const void* q, const void* k, const void* v, const float* mu, const float* log_var,
+               const float* logit_pi, void* out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv,
+               int causal, float eps, int dtype, int64_t segments, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  int st = pad_check(fn, d, dv);
+  if (st != LM_OK) return st;
+  const int64_t D = pad_width(d, dv);
+  if ((st = gma_check_shape(B, H, N, D, K, D, causal, dtype, segments)) != LM_OK) return st;
+  if (!(eps >= 0.f) || std::isinf(eps)) return fail(LM_EINVAL, "%s: eps must be finite and >= 0", fn);
+  const PadLayout L = pad_layout(B, H, N, d, dv, dtype, false, false, K,
+                                 gma_layout(B, H, N, D, K, D, dtype, segments, causal).total);
+  const size_t es = esize(dtype), rows = (size_t)B * H * N;
+  if ((st = pad_args(fn, {q, k, v, mu, log_var, logit_pi}, out, rows * dv * es,
+                     {{q, rows * d * es}, {k, rows * d * es}, {v, rows * dv * es}, {mu, (size_t)H * K * d * 4},
+                      {log_var, (size_t)H * K * d * 4}, {logit_pi, (size_t)H * K * 4}},
+                     workspace, L.total)) != LM_OK)
+    return st;
+  if (workspace_bytes < L.total)
+    return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = lm::pad_cols(q, at(workspace, L.q), rows, (int)d, (int)D, 0.f, (int)es, s)) != hipSuccess ||
+      (e = lm::pad_cols(k, at(workspace, L.k), rows, (int)d, (int)D, 0.f, (int)es, s)) != hipSuccess ||
+      (e = lm::pad_cols(v, at(workspace, L.v), rows, (int)dv, (int)D, 0.f, (int)es, s)) != hipSuccess ||
+      (e = lm::pad_cols(mu, at(workspace, L.mu), H * K, (int)d, (int)D, 0.f, 4, s)) != hipSuccess ||
+      (e = lm::pad_cols(log_var, at(workspace, L.lv), H * K, (int)d, (int)D, 0.f, 4, s)) != hipSuccess)
+    return hip_fail(fn, e);
+  if ((st = gma_impl(fn, at(workspace, L.q), at(workspace, L.k), at(workspace, L.v),
+                     reinterpret_cast<const float*>(at(workspace, L.mu)),
+                     reinterpret_cast<const float*>(at(workspace, L.lv)), logit_pi, at(workspace, L.out), B, H, N, D,
+                     K, D, causal, eps, dtype, segments, nullptr, nullptr, at(workspace, L.inner),
+                     L.total - L.inner, stream)) != LM_OK)
+    return st;
+  if ((e = lm::crop_cols(at(workspace, L.out), out, rows, (int)D, (int)dv, (int)es, s)) != hipSuccess)
+    return hip_fail(fn, e);
+  return ok();
+}
+
+// Linear attention, CCQ, the per-feature decay and the delta rule.
+enum class Lin { gla, ccq, vec, delta, ccq_delta };
+
+size_t lin_inner_bytes(Lin kind, int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int64_t segments) {
+  switch (kind) {
+    case Lin::gla: return lin_layout(B, H, N, D, false, segments).total;
+    case Lin::ccq: return lin_layout(B, H, N, D, true, segments).total;
+    case Lin::vec: return vec_layout(B, H, N, D, segments).total;
+    case Lin::delta: return delta_layout(B, H, N, D, D, dtype, false, segments).total;
+    case Lin::ccq_delta: return delta_layout(B, H, N, D, D, dtype, true, segments).total;
+  }
+  return 0;
+}
+
+int lin_pad_check(const char* fn, Lin kind, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
+                  int dtype, int64_t segments) {
+  int st = pad_check(fn, dk, dv);
+  if (st != LM_OK) return st;
+  const int64_t D = pad_width(dk, dv);
+  if (kind == Lin::delta || kind == Lin::ccq_delta) return delta_check_shape(fn, B, H, N, D, D, chunk, dtype, segments);
+  return lin_check_shape(fn, B, H, N, D, D, chunk, dtype, segments);
+}
+
+PadLayout lin_pad_layout(Lin kind, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int dtype,
+                         int64_t segments) {
+  const int64_t D = pad_width(dk, dv);
+  const bool w = kind == Lin::ccq || kind == Lin::ccq_delta;
+  return pad_layout(B, H, N, dk, dv, dtype, kind == Lin::vec, w, 0, lin_inner_bytes(kind, B, H, N, D, dtype, segments));
+}
+
+int lin_padded(const char* fn, Lin kind, const void* q, const void* k, const void* v, const float* g,
+               const float* beta, const float* w_lambda, const float* b_lambda, void* out, int64_t B, int64_t H,
+               int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  int st = lin_pad_check(fn, kind, B, H, N, dk, dv, chunk, dtype, segments);
+  if (st != LM_OK) return st;
+  const bool ccq = kind == Lin::ccq || kind == Lin::ccq_delta, delta = kind == Lin::delta || kind == Lin::ccq_delta;
+  const int64_t D = pad_width(dk, dv);
+  const PadLayout L = lin_pad_layout(kind, B, H, N, dk, dv, dtype, segments);
+  const size_t es = esize(dtype), rows = (size_t)B * H * N;
+  const size_t ng = kind == Lin::vec ? rows * dk * 4 : rows * 4;
+  if ((st = pad_args(fn, {q, k, v, g, delta ? beta : q, ccq ? w_lambda : q, ccq ? b_lambda : q}, out, rows * dv * es,
+                     {{q, rows * dk * es}, {k, rows * dk * es}, {v, rows * dv * es}, {g, ng},
+                      {delta ? beta : g, delta ? rows * 4 : 0}, {ccq ? w_lambda : g, ccq ? (size_t)H * dk * 4 : 0},
+                      {ccq ? b_lambda : g, ccq ? (size_t)H * 4 : 0}},
+                     workspace, L.total)) != LM_OK)
+    return st;
+  if (workspace_bytes < L.total)
+    return fail(LM_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = lm::pad_cols(q, at(workspace, L.q), rows, (int)dk, (int)D, 0.f, (int)es, s)) != hipSuccess ||
+      (e = lm::pad_cols(k, at(workspace, L.k), rows, (int)dk, (int)D, 0.f, (int)es, s)) != hipSuccess ||
+      (e = lm::pad_cols(v, at(workspace, L.v), rows, (int)dv, (int)D, 0.f, (int)es, s)) != hipSuccess)
+    return hip_fail(fn, e);
+  if (kind == Lin::vec && (e = lm::pad_cols(g, at(workspace, L.g), rows, (int)dk, (int)D, 1.f, 4, s)) != hipSuccess)
+    return hip_fail(fn, e);
+  if (ccq && (e = lm::pad_cols(w_lambda, at(workspace, L.w), H, (int)dk, (int)D, 0.f, 4, s)) != hipSuccess)
+    return hip_fail(fn, e);
+  const void *pq = at(workspace, L.q), *pk = at(workspace, L.k), *pv = at(workspace, L.v);
+  const float* pw = reinterpret_cast<const float*>(at(workspace, L.w));
+  void* po = at(workspace, L.out);
+  void* iw = at(workspace, L.inner);
+  const size_t nb = L.total - L.inner;
+  switch (kind) {
+    case Lin::gla:
+    case Lin::ccq:
+      st = lin_forward(fn, ccq, pq, pk, pv, g, ccq ? pw : nullptr, b_lambda, po, B, H, N, D, D, chunk, dtype, segments,
+                       0, nullptr, nullptr, iw, nb, stream);
+      break;
+    case Lin::vec:
+      st = vec_forward(fn, pq, pk, pv, reinterpret_cast<const float*>(at(workspace, L.g)), po, B, H, N, D, D, chunk,
+                       dtype, segments, nullptr, nullptr, iw, nb, stream);
+      break;
+    case Lin::delta:
+    case Lin::ccq_delta:
+      st = delta_forward(fn, ccq, pq, pk, pv, g, beta, ccq ? pw : nullptr, b_lambda, po, B, H, N, D, D, chunk, dtype,
+                         segments, 0, nullptr, nullptr, iw, nb, stream);
+      break;
+  }
+  if (st != LM_OK) return st;
+  if ((e = lm::crop_cols(po, out, rows, (int)D, (int)dv, (int)es, s)) != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+size_t lin_padded_bytes(const char* fn, Lin kind, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
+                        int64_t chunk, int dtype, int64_t segments) {
+  if (lin_pad_check(fn, kind, B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
+  return lin_pad_layout(kind, B, H, N, dk, dv, dtype, segments).total;
+}
+
 }  // namespace
 
 extern "C" {
@@ -600,6 +811,13 @@ const char* lm_last_error(void) { return g_err.c_str(); }
 
 size_t gma_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal,
                            int dtype, int64_t segments) {
+  if (!native_widths(d, dv)) {
+    if (pad_check("gma_forward", d, dv) != LM_OK) return 0;
+    const int64_t D = pad_width(d, dv);
+    if (gma_check_shape(B, H, N, D, K, D, causal, dtype, segments) != LM_OK) return 0;
+    return pad_layout(B, H, N, d, dv, dtype, false, false, K, gma_layout(B, H, N, D, K, D, dtype, segments, causal).total)
+        .total;
+  }
   if (gma_check_shape(B, H, N, d, K, dv, causal, dtype, segments) != LM_OK) return 0;
   return gma_layout(B, H, N, d, K, dv, dtype, segments, causal).total;
 }
@@ -608,6 +826,9 @@ int gma_forward(const void* q, const void* k, const void* v, const float* mu, co
                 const float* logit_pi, void* out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t K,
                 int64_t dv, int causal, float eps, int dtype, int64_t segments, void* workspace,
                 size_t workspace_bytes, void* stream) {
+  if (!native_widths(d, dv))
+    return gma_padded("gma_forward", q, k, v, mu, log_var, logit_pi, out, B, H, N, d, K, dv, causal, eps, dtype,
+                      segments, workspace, workspace_bytes, stream);
   return gma_impl("gma_forward", q, k, v, mu, log_var, logit_pi, out, B, H, N, d, K, dv, causal, eps, dtype,
                   segments, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
@@ -676,6 +897,8 @@ int gma_decode_step(const void* q, const void* k, const void* v, const float* mu
 
 size_t linattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
                                int64_t segments) {
+  if (!native_widths(dk, dv))
+    return lin_padded_bytes("linattn_chunk_forward", Lin::gla, B, H, N, dk, dv, chunk, dtype, segments);
   if (lin_check_shape("linattn_chunk_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
   return lin_layout(B, H, N, dk, false, segments).total;
 }
@@ -683,6 +906,9 @@ size_t linattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int6
 int linattn_chunk_forward(const void* q, const void* k, const void* v, const float* g, void* out, int64_t B,
                           int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!native_widths(dk, dv))
+    return lin_padded("linattn_chunk_forward", Lin::gla, q, k, v, g, nullptr, nullptr, nullptr, out, B, H, N, dk, dv,
+                      chunk, dtype, segments, workspace, workspace_bytes, stream);
   return lin_forward("linattn_chunk_forward", false, q, k, v, g, nullptr, nullptr, out, B, H, N, dk, dv, chunk,
                      dtype, segments, 0, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
@@ -718,6 +944,7 @@ int linattn_decode_step(const void* q, const void* k, const void* v, const float
 
 size_t ccq_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
                            int64_t segments) {
+  if (!native_widths(dk, dv)) return lin_padded_bytes("ccq_forward", Lin::ccq, B, H, N, dk, dv, chunk, dtype, segments);
   if (lin_check_shape("ccq_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
   return lin_layout(B, H, N, dk, true, segments).total;
 }
@@ -726,6 +953,9 @@ int ccq_forward(const void* q, const void* k, const void* v, const float* g, con
                 const float* b_lambda, void* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
                 int64_t chunk, int dtype, int64_t segments, void* workspace, size_t workspace_bytes,
                 void* stream) {
+  if (!native_widths(dk, dv))
+    return lin_padded("ccq_forward", Lin::ccq, q, k, v, g, nullptr, w_lambda, b_lambda, out, B, H, N, dk, dv, chunk,
+                      dtype, segments, workspace, workspace_bytes, stream);
   return lin_forward("ccq_forward", true, q, k, v, g, w_lambda, b_lambda, out, B, H, N, dk, dv, chunk, dtype,
                      segments, 0, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
@@ -768,6 +998,8 @@ int ccq_decode_step(const void* q, const void* k, const void* v, const float* g,
 
 size_t deltanet_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
                                 int64_t segments) {
+  if (!native_widths(dk, dv))
+    return lin_padded_bytes("deltanet_chunk_forward", Lin::delta, B, H, N, dk, dv, chunk, dtype, segments);
   if (delta_check_shape("deltanet_chunk_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
   return delta_layout(B, H, N, dk, dv, dtype, false, segments).total;
 }
@@ -775,6 +1007,9 @@ size_t deltanet_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int
 int deltanet_chunk_forward(const void* q, const void* k, const void* v, const float* g, const float* beta,
                            void* out, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
                            int dtype, int64_t segments, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!native_widths(dk, dv))
+    return lin_padded("deltanet_chunk_forward", Lin::delta, q, k, v, g, beta, nullptr, nullptr, out, B, H, N, dk, dv,
+                      chunk, dtype, segments, workspace, workspace_bytes, stream);
   return delta_forward("deltanet_chunk_forward", false, q, k, v, g, beta, nullptr, nullptr, out, B, H, N, dk, dv,
                        chunk, dtype, segments, 0, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
@@ -789,6 +1024,8 @@ int deltanet_forward_state(const void* q, const void* k, const void* v, const fl
 
 size_t ccq_deltanet_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
                                     int dtype, int64_t segments) {
+  if (!native_widths(dk, dv))
+    return lin_padded_bytes("ccq_deltanet_forward", Lin::ccq_delta, B, H, N, dk, dv, chunk, dtype, segments);
   if (delta_check_shape("ccq_deltanet_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
   return delta_layout(B, H, N, dk, dv, dtype, true, segments).total;
 }
@@ -797,6 +1034,9 @@ int ccq_deltanet_forward(const void* q, const void* k, const void* v, const floa
                          const float* w_lambda, const float* b_lambda, void* out, int64_t B, int64_t H, int64_t N,
                          int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments, void* workspace,
                          size_t workspace_bytes, void* stream) {
+  if (!native_widths(dk, dv))
+    return lin_padded("ccq_deltanet_forward", Lin::ccq_delta, q, k, v, g, beta, w_lambda, b_lambda, out, B, H, N, dk,
+                      dv, chunk, dtype, segments, workspace, workspace_bytes, stream);
   return delta_forward("ccq_deltanet_forward", true, q, k, v, g, beta, w_lambda, b_lambda, out, B, H, N, dk, dv,
                        chunk, dtype, segments, 0, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
@@ -812,6 +1052,8 @@ int ccq_deltanet_forward_state(const void* q, const void* k, const void* v, cons
 
 size_t linattn_vec_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
                                    int dtype, int64_t segments) {
+  if (!native_widths(dk, dv))
+    return lin_padded_bytes("linattn_vec_forward", Lin::vec, B, H, N, dk, dv, chunk, dtype, segments);
   if (lin_check_shape("linattn_vec_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
   return vec_layout(B, H, N, dk, segments).total;
 }
@@ -820,6 +1062,9 @@ size_t linattn_vec_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, 
 int linattn_vec_forward(const void* q, const void* k, const void* v, const float* g, void* out, int64_t B, int64_t H,
                         int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments,
                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!native_widths(dk, dv))
+    return lin_padded("linattn_vec_forward", Lin::vec, q, k, v, g, nullptr, nullptr, nullptr, out, B, H, N, dk, dv,
+                      chunk, dtype, segments, workspace, workspace_bytes, stream);
   return vec_forward("linattn_vec_forward", q, k, v, g, out, B, H, N, dk, dv, chunk, dtype, segments, nullptr,
                      nullptr, workspace, workspace_bytes, stream);
 }

@@ -261,6 +261,12 @@ struct GmaBwdLaunch {
 };
 hipError_t gma_backward_launch(const GmaBwdLaunch& L, hipStream_t st);
 
+// Feature-axis padding (pad.hip): rows of width sw to rows of width dw >= sw
+// with the new columns set to `fill`, and back (the first dw of sw columns).
+// esize is 2 (bf16) or 4 (float32).
+hipError_t pad_cols(const void* src, void* dst, int64_t rows, int sw, int dw, float fill, int esize, hipStream_t st);
+hipError_t crop_cols(const void* src, void* dst, int64_t rows, int sw, int dw, int esize, hipStream_t st);
+
 // Fixed device scratch of the entry point that allocates nothing (noalloc.hip):
 // its size, and its address on the current device (looked up once per device).
 constexpr size_t kNoallocScratchBytes = size_t(64) << 20;

@@ -70,8 +70,10 @@ def _gma(L, **kw):
     (dict(dt=7), binding.LM_EINVAL),
     (dict(seg=-1), binding.LM_EINVAL),
     (dict(d=48, dv=48), binding.LM_EUNSUPPORTED),
-    (dict(d=64, dv=32), binding.LM_EUNSUPPORTED),
+    (dict(d=64, dv=48), binding.LM_EUNSUPPORTED),
+    (dict(d=16, dv=8), binding.LM_EUNSUPPORTED),
     (dict(K=257), binding.LM_EUNSUPPORTED),
+    (dict(d=16, dv=128, K=200, dt=binding.LM_F32), binding.LM_EUNSUPPORTED),  # padded to d = 128
     (dict(d=128, dv=128, K=200, dt=binding.LM_F32), binding.LM_EUNSUPPORTED),
     (dict(wsb=16), binding.LM_EWORKSPACE),
     (dict(out=FAKE + 16), binding.LM_EINVAL),  # overlaps q
@@ -110,8 +112,11 @@ def _lin(L, fn, **kw):
     (dict(H=0), binding.LM_EINVAL),
     (dict(chunk=32), binding.LM_EUNSUPPORTED),
     (dict(dk=96, dv=96), binding.LM_EUNSUPPORTED),
-    (dict(dk=64, dv=128), binding.LM_EUNSUPPORTED),
+    (dict(dk=64, dv=96), binding.LM_EUNSUPPORTED),
     (dict(wsb=8), binding.LM_EWORKSPACE),
+    (dict(dk=16, dv=64, wsb=8), binding.LM_EWORKSPACE),  # padded shape
+    (dict(dk=16, dv=64, out=FAKE + (2 << 30) + 64), binding.LM_EINVAL),  # padded shape, out overlaps v
+    (dict(dk=32, dv=64, ws=FAKE + (3 << 30)), binding.LM_EINVAL),  # padded shape, g inside the workspace
     (dict(out=FAKE + (2 << 30) + 64), binding.LM_EINVAL),  # overlaps v
     (dict(N=(1 << 30) + 1), binding.LM_EUNSUPPORTED),  # beyond the largest sequence
     (dict(B=256, H=256), binding.LM_EUNSUPPORTED),  # beyond the largest B*H
@@ -148,8 +153,10 @@ def _delta(L, fn, **kw):
     (dict(beta=FAKE + (10 << 30) + 2), binding.LM_EINVAL),  # misaligned
     (dict(N=0), binding.LM_EINVAL),
     (dict(chunk=32), binding.LM_EUNSUPPORTED),
-    (dict(dk=64, dv=128), binding.LM_EUNSUPPORTED),
+    (dict(dk=64, dv=96), binding.LM_EUNSUPPORTED),
     (dict(dk=128, dv=128, dt=binding.LM_F32), binding.LM_EUNSUPPORTED),
+    (dict(dk=16, dv=128, dt=binding.LM_F32), binding.LM_EUNSUPPORTED),  # padded to 128 in float32
+    (dict(dk=16, dv=32, wsb=16), binding.LM_EWORKSPACE),
     (dict(out=FAKE + (10 << 30)), binding.LM_EINVAL),  # overlaps beta
     (dict(B=256, H=256), binding.LM_EUNSUPPORTED),
 ])
@@ -175,6 +182,27 @@ def test_deltanet_workspaces():
         assert st == binding.LM_EINVAL
     st, _ = _delta(L, "ccq_deltanet_forward", w=None)
     assert st == binding.LM_EINVAL
+
+
+@needs_lib
+def test_padded_shapes_workspace_and_native_only_entry_points():
+    L = binding.lib()
+    # d = 16 and d != dv run padded: the workspace holds the padded tensors too
+    assert L.linattn_workspace_bytes(2, 4, 1000, 16, 16, 64, binding.LM_BF16, 0) > \
+        L.linattn_workspace_bytes(2, 4, 1000, 32, 32, 64, binding.LM_BF16, 0)
+    assert L.gma_workspace_bytes(2, 4, 1000, 64, 16, 32, 1, binding.LM_BF16, 0) > \
+        L.gma_workspace_bytes(2, 4, 1000, 64, 16, 64, 1, binding.LM_BF16, 0)
+    for fn in ("ccq_workspace_bytes", "linattn_vec_workspace_bytes", "deltanet_workspace_bytes",
+               "ccq_deltanet_workspace_bytes"):
+        assert getattr(L, fn)(2, 4, 1000, 16, 64, 64, binding.LM_BF16, 0) > 0, fn
+        assert getattr(L, fn)(2, 4, 1000, 24, 64, 64, binding.LM_BF16, 0) == 0, fn
+    # the carried-state entry points and the backward take the native widths only
+    st, _ = _ccq_state(L, dk=16, dv=16)
+    assert st == binding.LM_EUNSUPPORTED
+    st, _ = _ccq_state(L, dk=32, dv=64)
+    assert st == binding.LM_EUNSUPPORTED
+    st, _ = _gma_state(L, d=16, dv=16)
+    assert st == binding.LM_EUNSUPPORTED
 
 
 @needs_lib
