@@ -163,3 +163,21 @@ def test_gma_deterministic():
     a = gma_forward(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"])
     b = gma_forward(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"])
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("N", [4096, 16384])
+def test_stored_key_responsibilities_are_bit_identical(N):
+    # the causal bf16 pass over several segments loads each chunk's key
+    # responsibilities stored by the segment pass; the entry point that
+    # allocates nothing routes the keys again in the causal pass, with the same
+    # segment plan: the outputs must agree bit for bit
+    import torch
+    from linear_attention_gmm_amd import binding
+    cfg = inputs.CONFIGS["gma_bf16_n16k"].replace(B=2, N=N)
+    x = cuda(inputs.gma_inputs(cfg))
+    a = binding.gma_forward(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"], causal=True, eps=cfg.eps)
+    b = binding.gma_forward_noalloc(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"], causal=True,
+                                    eps=cfg.eps)
+    torch.cuda.synchronize()
+    say("  stored vs routed key responsibilities, N=%d: max |diff| %.3e" % (N, float((a.float() - b.float()).abs().max())))
+    assert torch.equal(a, b)
