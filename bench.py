@@ -66,7 +66,7 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 # kernels launched by each entry point (name fragments as rocprofv3 reports them)
 ENTRY_KERNELS = {
     "gma_forward": ("gma4fast6kernel", "lm::gma::fast::kernel", "gma_kernel", "prep_kernel", "lm::gma::scan_kernel"),
-    "ccq_forward": ("lin_kernelIDF16bLi128ELb1", "lm::lin::scan_kernel"),
+    "ccq_forward": ("lin_kernelIDF16bLi128ELb1", "lm::lin::scan_kernel", "lm::ccqp::chunk_kernel"),
 }
 
 
@@ -74,7 +74,7 @@ ENTRY_KERNELS = {
 # ABI layer that plans their segments). The one-token steps and the
 # per-feature-decay kernel are not part of the measured step.
 DIGEST_SOURCES = ("abi.cpp", "launch.hpp", "mfma.hpp", "gma.hip", "gma.hpp", "gma_bf16.hip", "gma_generic.hpp",
-                  "gma_wide.hip", "linattn.hip")
+                  "gma_wide.hip", "linattn.hip", "ccq_pipe.hip")
 
 
 def sources_digest():
