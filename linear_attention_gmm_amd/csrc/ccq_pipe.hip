@@ -35,14 +35,16 @@
 //    of three: the consumer's, the producer's and the landing one). Each wave
 //    issues its share at a different point of the iteration, so that the
 //    transfers do not queue behind each other in the address unit.
-//  * Operand orders. Fragments chained from the fp32 state (M, S) carry their
-//    32 k-values in CHAIN order (rows 4g..4g+3 of two 16-row tiles), and the Q
-//    and q' operands they meet follow it. Everything that only meets LDS data
-//    uses the NATURAL order (k = 8g..8g+7 of a step: one 16-byte read).
-//  * The consumers' value columns are permuted within a wave (tile row x of
-//    column tile dt is column 8 (x / 4) + 4 dt + x % 4 of the wave's 32), so
-//    that each lane ends with eight adjacent outputs of one row: one 16-byte
-//    store per lane and query tile.
+//  * Operand orders. Every operand read from LDS along the feature axis is a
+//    NATURAL fragment (k = 8g..8g+7 of a step: one 16-byte read). Fragments
+//    chained from the fp32 state (M, S) carry rows 4g..4g+3 of two 16-row
+//    tiles, so the state's rows are labelled to match: row 4g + r of row
+//    tile bt holds feature 32 (bt / 2) + 8g + 4 (bt % 2) + r. The key
+//    operands that build the state (transposed reads of K) pick their 4-column
+//    groups in the same order, and so do the columns of M and of S (tile row x
+//    of column tile t is column 8 (x / 4) + 4 t + x % 4 of the wave's 32),
+//    which also gives each consumer lane eight adjacent outputs of one row:
+//    one 16-byte store per lane and query tile.
 #include "launch.hpp"
 #include "mfma.hpp"
 
@@ -54,7 +56,6 @@ constexpr int kD = 128;
 constexpr int kNW = 8;
 constexpr int kNT = kNW * 64;
 constexpr int TB = kC * kD * 2;  // bytes of one 64 x 128 bf16 tile
-constexpr int PP = kC + 8;       // pitch (elements) of the score tiles: 16-byte aligned rows
 constexpr int PDD = kD + 8;      // pitch of the gate / mean rows
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr float kLazy = 64.f;
@@ -64,9 +65,9 @@ constexpr int oK = 0;                    // K ring, 3 tiles
 constexpr int oQ = oK + 3 * TB;          // Q, 2 tiles
 constexpr int oV = oQ + 2 * TB;          // V, 2 tiles
 constexpr int oQc = oV + 2 * TB;         // cleaned queries as fragments [qt][ks][lane] x 16 B
-constexpr int oP = oQc + TB;             // raw masked scores [64 q][PP] bf16, keys in order
-constexpr int oPc = oP + kC * PP * 2;    // cleaned decayed scores [64 q][PP] bf16
-constexpr int oDot = oPc + kC * PP * 2;  // [4][PDD] bf16: w hi, w lo, m hi, m lo
+constexpr int oP = oQc + TB;             // raw masked scores, 64 x 64 bf16 (score layout below)
+constexpr int oPc = oP + kC * kC * 2;    // cleaned decayed scores, 64 x 64 bf16
+constexpr int oDot = oPc + kC * kC * 2;  // [4][PDD] bf16: w hi, w lo, m hi, m lo
 constexpr int oG = oDot + 4 * PDD * 2;   // decays, 2 x 64 fp32
 // per query: alpha, m_prev . q, and the row sums of P from the two slots; 16 spare
 constexpr int oQR = oG + 2 * kC * 4;     // [80] float4
@@ -96,28 +97,40 @@ struct Args {
 };
 
 // ----------------------------------------------------------------------------
-// Tile layout in LDS. A 64 x 128 bf16 tile is 64 rows of 16 pieces of 16
-// bytes. Row block rb = r / 16 holds 256 pieces; piece c of row r sits at slot
-//   rb * 256 + c * 16 + ((r % 16) ^ 4 (c % 2)).
-// Sixteen consecutive rows of one piece are 256 contiguous bytes (operand reads
-// of 16 rows touch every bank once), row blocks, pieces and k-steps are
-// constant offsets from a per-lane base, and the XOR keeps the two pieces of a
-// transposed read of 8 consecutive tokens in different banks. One DMA
-// instruction fills 64 slots: 16 rows x 4 pieces, i.e. 64-byte runs of 16
-// source rows.
+// LDS banking on gfx950 (measured with the bank-conflict counters): 64 banks
+// of 4 bytes for reads of 8 and 16 bytes per lane. A 16-byte read is served in
+// passes of 16 lanes: lanes {0-3, 12-15, 20-27} form one pass, {4-11, 16-19,
+// 28-31} another, and the same for lanes 32-63. An 8-byte read (plain or
+// transposed) is served in passes of 32 lanes. Writes of 8 bytes are served in
+// passes of 16 lanes over 128 bytes.
+//
+// Tile layout. A 64 x 128 bf16 tile is 64 rows of 16 pieces of 16 bytes. Row
+// block rb = r / 16 holds 256 pieces; piece c of row r sits at slot
+//   rb * 256 + c * 16 + ((r % 16) ^ h(c % 4)),  h = (0, 12, 4, 8).
+// An operand read (lane: row c16, piece 4 ks + g) lands on slot c16 ^ h(g) of
+// 16 (the 256 bytes of the 64 banks): distinct within each pass of a 16-byte
+// read. A transposed read takes one 8-byte half of 32 pieces per pass, two per
+// slot at best; the XOR spreads them over all 16 slots. Row blocks, pieces and
+// k-steps are constant offsets from a per-lane base. One DMA instruction fills
+// 64 slots: 16 rows x 4 pieces, i.e. 64-byte runs of 16 source rows.
+__device__ __forceinline__ constexpr int tile_xor(int c) { return ((0x84c0 >> (4 * (c & 3))) & 15); }
 __device__ __forceinline__ int slot_off(int rb, int r16, int c) {
-  return (rb * 256 + c * 16 + (r16 ^ ((c & 1) << 2))) * 16;
+  return (rb * 256 + c * 16 + (r16 ^ tile_xor(c))) * 16;
 }
+// Score tiles (64 queries x 64 keys, bf16): piece p (8 keys) of query row r at
+// 16-byte unit 8 r + (p ^ ((r / 2) % 8)). Operand reads (row c16, piece 4 s +
+// g) are conflict-free; the 8-byte stores of 16 rows take two cycles, the
+// least an 8-byte store of 16 lanes needs.
+__device__ __forceinline__ int sc_sigma(int c16) { return (c16 >> 1) & 7; }
 
 // The lane index, hidden from the optimiser once per chunk: the few per-lane
 // LDS bases derived from it are recomputed in the loop rather than held in
 // registers across it, next to the two state blocks.
 struct Lane {
   int l, g, c16;
-  int nat;    // NATURAL read of row c16 of a row block: piece 4 ks + g
-  int chain;  // CHAIN read of row c16: pieces 4 ks + g / 2 (+2), half g % 2
-  int tr, tr2;    // transposed read: rows 8 g + j / 4 (and + 4), piece pair (j % 4) / 2
-  int trp, trp2;  // the same for the permuted value columns: piece j % 4
+  int nat;        // NATURAL read of row c16 of a row block: piece 4 ks + g
+  int trp, trp2;  // transposed read: rows 8 g + j / 4 (and + 4), piece j % 4
+  int sc;         // score tiles: element offset of piece 4 s + g of row c16, s = 0
 };
 __device__ __forceinline__ Lane lane_opaque() {
   int x = (int)(threadIdx.x & 63);
@@ -128,37 +141,21 @@ __device__ __forceinline__ Lane lane_opaque() {
   L.c16 = x & 15;
   const int g = L.g, j = L.c16;
   L.nat = slot_off(0, j, g);
-  L.chain = slot_off(0, j, g >> 1) + (g & 1) * 8;
   // rows 8 g + j / 4: row block g / 2, row 8 (g % 2) + j / 4 in it
-  L.tr = slot_off(g >> 1, 8 * (g & 1) + (j >> 2), (j & 3) >> 1) + (j & 1) * 8;
-  L.tr2 = slot_off(g >> 1, 8 * (g & 1) + (j >> 2) + 4, (j & 3) >> 1) + (j & 1) * 8;
   L.trp = slot_off(g >> 1, 8 * (g & 1) + (j >> 2), j & 3);
   L.trp2 = slot_off(g >> 1, 8 * (g & 1) + (j >> 2) + 4, j & 3);
+  L.sc = j * kC + ((g ^ sc_sigma(j)) << 3);
   return L;
 }
 // NATURAL fragment: row 16 rb + c16, k = 32 ks + 8 g .. + 7.
 __device__ __forceinline__ bf16x8 nat_rd(const char* t, int rb, int ks, const Lane& L) {
   return *reinterpret_cast<const bf16x8*>(t + rb * 4096 + ks * 1024 + L.nat);
 }
-// CHAIN fragment: row 16 rb + c16, k = 32 ks + {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3}.
-__device__ __forceinline__ bf16x8 chain_rd(const char* t, int rb, int ks, const Lane& L) {
-  const char* p = t + rb * 4096 + ks * 1024 + L.chain;
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 512);
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
 // Transposed (k-major) NATURAL fragment: tokens 32 ks + 8 g .. + 7 of column
-// c0 + p for lane p of a 16-lane group (c0 a multiple of 16). Each lane of the
-// transpose read supplies one row and the 4 columns its group hands to lanes
+// base + 8 (p / 4) + 4 dt + p % 4 for lane p of a 16-lane group (base a
+// multiple of 32): the column order of the state. Each lane of the transpose
+// read supplies one row and the 4 columns its group hands to lanes
 // 4 (j % 4) .. + 3; the second read covers the next 4 rows.
-__device__ __forceinline__ bf16x8 tr_rd(const char* t, int ks, int c0, const Lane& L) {
-  const char* p = t + ks * 8192 + (c0 >> 3) * 256;
-  const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LM_LDS*)(p + L.tr)));
-  const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LM_LDS*)(p + L.tr2)));
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-// The same for the consumer's permuted value columns: lane p gets column
-// base + 8 (p / 4) + 4 dt + p % 4 (base a multiple of 32).
 __device__ __forceinline__ bf16x8 trp_rd(const char* t, int ks, int base, int dt, const Lane& L) {
   const char* p = t + ks * 8192 + (base >> 3) * 256 + dt * 8;
   const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LM_LDS*)(p + L.trp)));
@@ -169,12 +166,13 @@ __device__ __forceinline__ bf16x8 trp_rd(const char* t, int ks, int base, int dt
 __device__ __forceinline__ bf16x8 row_rd(const bf16* base, int pitch, int rc, int ks, int g) {
   return *reinterpret_cast<const bf16x8*>(base + rc * pitch + ks * 32 + 8 * g);
 }
-// CHAIN fragment of a plain row-major bf16 array: row rc, k = 32 ks + {4 g .., 16 + 4 g ..}.
-__device__ __forceinline__ bf16x8 row_chain_rd(const bf16* base, int pitch, int rc, int ks, int g) {
-  const bf16* p = base + rc * pitch + ks * 32 + 4 * g;
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+// Score tile operand: query row 16 qt + c16, keys 32 s + 8 g .. + 7.
+__device__ __forceinline__ bf16x8 sc_rd(const bf16* t, int qt, int s, const Lane& L) {
+  return *reinterpret_cast<const bf16x8*>(t + qt * 16 * kC + (L.sc ^ (s << 5)));
+}
+// Score tile element offset of query row r, keys k .. (k a multiple of 4).
+__device__ __forceinline__ int sc_off(int r, int k) {
+  return r * kC + ((((k >> 3) ^ sc_sigma(r & 15)) << 3) | (k & 7));
 }
 
 // Global->LDS transfer of 16 bytes per lane (buffer_load ... lds), issued as
@@ -203,7 +201,7 @@ struct Dma {
     for (int n = 0; n < 4; ++n) {
       const int i = 4 * q + n;
       const int c = (i & 3) * 4 + (l >> 4);
-      const int row = 16 * (i >> 2) + ((l & 15) ^ ((c & 1) << 2));
+      const int row = 16 * (i >> 2) + ((l & 15) ^ tile_xor(c));
       voff[n] = row * (kD * 2) + c * 16;
     }
   }
@@ -276,15 +274,16 @@ __device__ __forceinline__ bf16x4 pack4(const f32x4& v) {
   return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
 }
 
-// Writes m (this producer's 32 entries, rows 4 g + r of column tiles ct) as
-// the bf16 hi / lo rows 2 and 3 of the gate / mean operand.
+// Writes m (this producer's 32 entries: entry (ct, r) of lane group g is
+// feature 32 pw + 8 g + 4 ct + r) as the bf16 hi / lo rows 2 and 3 of the
+// gate / mean operand.
 __device__ __forceinline__ void put_m(bf16* sDot, const float (&m)[2][4], int pw, int g, int c16) {
   if (c16 == 0) {
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int a = 32 * pw + 16 * ct + 4 * g + r;
+        const int a = 32 * pw + 8 * g + 4 * ct + r;
         const bf16 hi = (bf16)m[ct][r];
         sDot[2 * PDD + a] = hi;
         sDot[3 * PDD + a] = (bf16)(m[ct][r] - (float)hi);
@@ -342,16 +341,16 @@ __device__ __forceinline__ void producer_first(const Ctx& x, int it, const f32x4
     x.issue_k(it + 1, PW);
   }
   struct Ops {
-    bf16x8 qc[4];      // Q, CHAIN, query tiles 0..3 (M_prev q, the gate and mean terms, the scores)
-    bf16x8 dot;        // gate / mean rows, CHAIN
-    bf16x8 kc[TL::n];  // K, CHAIN, the score list's key tiles
+    bf16x8 qc[4];      // Q, query tiles 0..3 (M_prev q, the gate and mean terms, the scores)
+    bf16x8 dot;        // gate / mean rows
+    bf16x8 kc[TL::n];  // K, the score list's key tiles
   };
   auto load = [&](int s, Ops& o) {
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) o.qc[qt] = chain_rd(Qt, qt, s, L);
-    o.dot = c16 < 4 ? row_chain_rd(sDot, PDD, c16, s, g) : zero8();
+    for (int qt = 0; qt < 4; ++qt) o.qc[qt] = nat_rd(Qt, qt, s, L);
+    o.dot = c16 < 4 ? row_rd(sDot, PDD, c16, s, g) : zero8();
 #pragma unroll
-    for (int n = 0; n < TL::n; ++n) o.kc[n] = chain_rd(Kt, TL::kt(n), s, L);
+    for (int n = 0; n < TL::n; ++n) o.kc[n] = nat_rd(Kt, TL::kt(n), s, L);
   };
   Ops ops[2];
   load(0, ops[0]);
@@ -397,7 +396,7 @@ __device__ __forceinline__ void producer_first(const Ctx& x, int it, const f32x4
         if (4 * g + r > c16) acc[n][r] = 0.f;
     }
     const bf16x4 p = pack4(acc[n]);
-    *reinterpret_cast<bf16x4*>(sP + (16 * qt + c16) * PP + 16 * kt + 4 * g) = p;
+    *reinterpret_cast<bf16x4*>(sP + sc_off(16 * qt + c16, 16 * kt + 4 * g)) = p;
     const float part = ((float)p[0] + (float)p[1]) + ((float)p[2] + (float)p[3]);
     if (qt == TL::qt(0)) rs0 += part; else rs1 += part;
   }
@@ -424,21 +423,23 @@ __device__ __forceinline__ void producer_second(const Ctx& x, int it, int pw, f3
   const bf16x8* sTri = reinterpret_cast<const bf16x8*>(x.smem + oTri);
   bf16* sDot = reinterpret_cast<bf16*>(x.smem + oDot);
   bf16x8* sQc = reinterpret_cast<bf16x8*>(x.smem + oQc);
-  // K columns of this wave (rows a = 32 pw + 16 ct + lane, k = tokens)
+  // K columns of this wave in the state's column order (lane p of column tile
+  // ct: feature 32 pw + 8 (p / 4) + 4 ct + p % 4; k = tokens)
   bf16x8 KC[2][2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) KC[ct][s] = tr_rd(Kt, s, 32 * pw + 16 * ct, L);
+    for (int s = 0; s < 2; ++s) KC[ct][s] = trp_rd(Kt, s, 32 * pw, ct, L);
+  // K columns of row tile bt in the state's row order
   bf16x8 kf[2][2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) kf[0][s] = tr_rd(Kt, s, 0, L);
+  for (int s = 0; s < 2; ++s) kf[0][s] = trp_rd(Kt, s, 0, 0, L);
   const float t_i0 = (float)x.t_tok0 + (float)(it * kC + c16 + 1);
 #pragma unroll
   for (int bt = 0; bt < 8; ++bt) {
     if (bt + 1 < 8) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) kf[(bt + 1) & 1][s] = tr_rd(Kt, s, 16 * (bt + 1), L);
+      for (int s = 0; s < 2; ++s) kf[(bt + 1) & 1][s] = trp_rd(Kt, s, 32 * ((bt + 1) >> 1), (bt + 1) & 1, L);
     }
     // M += K^T K[:, cols], row block bt
 #pragma unroll
@@ -461,7 +462,7 @@ __device__ __forceinline__ void producer_second(const Ctx& x, int it, int pw, f3
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (s == 1 && qt < 2) continue;  // keys 32..63 lie above the diagonal
-        const bf16x8 pf = row_rd(sP, PP, i, s, g);
+        const bf16x8 pf = sc_rd(sP, qt, s, L);
         // the query tile's diagonal k-step from the table, full steps below it
         const bf16x8 tf = s == (qt >> 1) ? sTri[qt * 64 + L.l] : ones8();
 #pragma unroll
@@ -470,7 +471,7 @@ __device__ __forceinline__ void producer_second(const Ctx& x, int it, int pw, f3
           kc[ct] = Mma<bf16>::mma(KC[ct][s], tf, kc[ct]);
         }
       }
-      const bf16x8 qv = chain_rd(Qt, qt, pw, L);
+      const bf16x8 qv = nat_rd(Qt, qt, pw, L);
       bf16x8 qc;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -526,14 +527,14 @@ __device__ __forceinline__ void consumer_first(const Ctx& x, int it, f32x4 (&St)
     if (PW == 0) x.issue_g(it);
   }
   struct Ops {
-    bf16x8 q[4];      // q', CHAIN, query tiles 0..3
-    bf16x8 k[TL::n];  // K, CHAIN, the score list's key tiles
+    bf16x8 q[4];      // q', query tiles 0..3
+    bf16x8 k[TL::n];  // K, the score list's key tiles
   };
   auto load = [&](int s, Ops& o) {
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) o.q[qt] = Qc[(qt * 4 + s) * 64 + l];
 #pragma unroll
-    for (int n = 0; n < TL::n; ++n) o.k[n] = chain_rd(Kt, TL::kt(n), s, L);
+    for (int n = 0; n < TL::n; ++n) o.k[n] = nat_rd(Kt, TL::kt(n), s, L);
   };
   Ops ops[2];
   load(0, ops[0]);
@@ -582,7 +583,7 @@ __device__ __forceinline__ void consumer_first(const Ctx& x, int it, f32x4 (&St)
   for (int n = 0; n < TL::n; ++n) {
     const int qt = TL::qt(n), kt = TL::kt(n);
     const f32x4 d = decay_tile(sLw, sLw[16 * qt + c16], kt, qt, g, c16);
-    *reinterpret_cast<bf16x4*>(sPc + (16 * qt + c16) * PP + 16 * kt + 4 * g) = pack4(acc[n] * d);
+    *reinterpret_cast<bf16x4*>(sPc + sc_off(16 * qt + c16, 16 * kt + 4 * g)) = pack4(acc[n] * d);
   }
   if (eager) {
     const float b = fast_exp2(ls_next);
@@ -625,12 +626,12 @@ __device__ __forceinline__ void consumer_second(const Ctx& x, int it, int pw, f3
   }
   bf16x8 kf[2][2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) kf[0][s] = tr_rd(Kt, s, 0, L);
+  for (int s = 0; s < 2; ++s) kf[0][s] = trp_rd(Kt, s, 0, 0, L);
 #pragma unroll
   for (int bt = 0; bt < 8; ++bt) {
     if (bt + 1 < 8) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) kf[(bt + 1) & 1][s] = tr_rd(Kt, s, 16 * (bt + 1), L);
+      for (int s = 0; s < 2; ++s) kf[(bt + 1) & 1][s] = trp_rd(Kt, s, 32 * ((bt + 1) >> 1), (bt + 1) & 1, L);
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -642,7 +643,7 @@ __device__ __forceinline__ void consumer_second(const Ctx& x, int it, int pw, f3
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (s == 1 && qt < 2) continue;
-        const bf16x8 pf = row_rd(sPc, PP, i, s, g);
+        const bf16x8 pf = sc_rd(sPc, qt, s, L);
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) acc[dt] = Mma<bf16>::mma(VF[dt][s], pf, acc[dt]);
       }
@@ -689,12 +690,13 @@ __global__ __launch_bounds__(kNT, 1) void chunk_kernel(Args a) {
   bf16* sP = reinterpret_cast<bf16*>(smem + oP);
   bf16* sDot = reinterpret_cast<bf16*>(smem + oDot);
 
-  // State: producers M[16 bt + 4 g + r][32 pw + 16 ct + c16] as St[bt][ct] and
-  // m; consumers S[16 bt + 4 g + r][value column of (dt, c16)] as St[bt][dt].
+  // State: producers M[frow(bt, r)][fcol(ct, c16)] as St[bt][ct] and m;
+  // consumers S[frow(bt, r)][fcol(dt, c16)] as St[bt][dt].
   f32x4 St[8][2];
   float mcol[2][4];
   Lazy lz{0.f, 0.f};  // consumers: S_true = 2^ls St
-  auto vcol = [&](int dt, int xx) { return 32 * pw + 8 * (xx >> 2) + 4 * dt + (xx & 3); };
+  auto frow = [&](int bt, int r) { return 32 * (bt >> 1) + 8 * g + 4 * (bt & 1) + r; };
+  auto fcol = [&](int t, int xx) { return 32 * pw + 8 * (xx >> 2) + 4 * t + (xx & 3); };
   {
     const float* blk = a.agg ? a.agg + ((size_t)bh * a.P + (size_t)a.R * seg) * a.sfl : nullptr;
 #pragma unroll
@@ -703,15 +705,15 @@ __global__ __launch_bounds__(kNT, 1) void chunk_kernel(Args a) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = 16 * bt + 4 * g + r;
+          const int row = frow(bt, r);
           float v = 0.f;
-          if (blk) v = producer ? blk[kD * kD + 1 + row * kD + 32 * pw + 16 * t + c16] : blk[row * kD + vcol(t, c16)];
+          if (blk) v = producer ? blk[kD * kD + 1 + row * kD + fcol(t, c16)] : blk[row * kD + fcol(t, c16)];
           St[bt][t][r] = v;
         }
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mcol[ct][r] = blk ? blk[2 * kD * kD + 1 + 32 * pw + 16 * ct + 4 * g + r] : 0.f;
+      for (int r = 0; r < 4; ++r) mcol[ct][r] = blk ? blk[2 * kD * kD + 1 + 32 * pw + 8 * g + 4 * ct + r] : 0.f;
   }
   // gate weights (rows 0 / 1, hi / lo), the zero score tiles above the
   // diagonal that the k-steps of 32 keys read, partial row sums slot 1
@@ -729,8 +731,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_kernel(Args a) {
     const int t = i >> 8, q = (i >> 4) & 15, j = i & 15;
     // tile (0, 1) and tile (2, 3) of both score buffers
     const int row = t == 0 ? q : 32 + q, col = t == 0 ? 16 + j : 48 + j;
-    sP[row * PP + col] = (bf16)0.f;
-    sPc[row * PP + col] = (bf16)0.f;
+    sP[sc_off(row, col & ~3) + (col & 3)] = (bf16)0.f;
+    sPc[sc_off(row, col & ~3) + (col & 3)] = (bf16)0.f;
   }
   for (int i = threadIdx.x; i < kC + 16; i += kNT) reinterpret_cast<float*>(smem + oQR)[4 * i + 3] = 0.f;
   if (producer) {
@@ -785,15 +787,15 @@ __global__ __launch_bounds__(kNT, 1) void chunk_kernel(Args a) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = 16 * bt + 4 * g + r;
-          if (producer) so[kD * kD + row * kD + 32 * pw + 16 * t + c16] = St[bt][t][r];
-          else so[row * kD + vcol(t, c16)] = St[bt][t][r] * sfin;
+          const int row = frow(bt, r);
+          if (producer) so[kD * kD + row * kD + fcol(t, c16)] = St[bt][t][r];
+          else so[row * kD + fcol(t, c16)] = St[bt][t][r] * sfin;
         }
     if (producer && c16 == 0) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) so[2 * kD * kD + 32 * pw + 16 * ct + 4 * g + r] = mcol[ct][r];
+        for (int r = 0; r < 4; ++r) so[2 * kD * kD + 32 * pw + 8 * g + 4 * ct + r] = mcol[ct][r];
     }
   }
 }
