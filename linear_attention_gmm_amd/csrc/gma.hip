@@ -185,6 +185,7 @@ static hipError_t generic(const GmaLaunch& L, const Args& a, int mode, int segme
 
 static hipError_t run(const GmaLaunch& L, const Args& a, int mode, int segments, hipStream_t st) {
   if (fast_supported(L)) return fast_launch(L, a, mode, segments, st);
+  if (long_supported(L)) return long_launch(a, mode, segments, (unsigned)(L.B * L.H), st);
   return L.bf16 ? generic<bf16>(L, a, mode, segments, st) : generic<float>(L, a, mode, segments, st);
 }
 

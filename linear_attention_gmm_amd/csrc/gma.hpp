@@ -46,6 +46,10 @@ struct Args {
 // General kernel for bf16, d = dv = 128, KP = 256 (gma_wide.hip).
 hipError_t wide_launch(const Args& a, int mode, int segments, unsigned BH, hipStream_t st);
 
+// bf16 kernel for d = dv = 128 and KP = 256 (gma_long.hip): modes AGG, CAUSAL, BIDIR.
+bool long_supported(const GmaLaunch& L);
+hipError_t long_launch(const Args& a, int mode, int segments, unsigned BH, hipStream_t st);
+
 // bf16 kernel (gma_bf16.hip) for d = dv in {32, 64} and KP in {64, 128}.
 bool fast_supported(const GmaLaunch& L);
 hipError_t fast_launch(const GmaLaunch& L, const Args& a, int mode, int segments, hipStream_t st);
