@@ -93,6 +93,8 @@ int check_states(const char* fn, const float* sin, float* sout, size_t nbytes, c
 // Components are padded to KP (padding has logit -inf). The bf16 kernel for
 // d <= 64 works on 64 or 128 components.
 bool gma_fast(int64_t d, int64_t K, int dtype) { return dtype == LM_BF16 && d <= 64 && K <= 128; }
+// The bf16 kernel for d = 128 and 129..256 components (256 padded).
+bool gma_long(int64_t d, int64_t K, int dtype) { return dtype == LM_BF16 && d == 128 && K > 128 && K <= 256; }
 
 int gma_kp(int64_t K, int64_t d, int dtype) {
   if (gma_fast(d, K, dtype)) return K <= 64 ? 64 : 128;
@@ -122,10 +124,10 @@ GmaLayout gma_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int6
   off = align_up(off + (size_t)B * H * L.plan.P * L.KP * dv * 4);
   L.aggz = off;
   off = align_up(off + (size_t)B * H * L.plan.P * L.KP * 4);
-  // causal bf16 kernel over several segments: the segment pass stores each
+  // causal bf16 kernels over several segments: the segment pass stores each
   // chunk's key responsibilities (64 x KP bf16) for the causal pass
   L.gk = 0;
-  if (store_gk && causal && gma_fast(d, K, dtype) && L.plan.P > 1) {
+  if (store_gk && causal && (gma_fast(d, K, dtype) || gma_long(d, K, dtype)) && L.plan.P > 1) {
     L.gk = off;
     off = align_up(off + (size_t)B * H * ((N + kChunk - 1) / kChunk) * kChunk * L.KP * 2);
   }

@@ -229,10 +229,10 @@ hipError_t gma_launch(const GmaLaunch& L, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int P = (int)L.P;
   if (L.causal) {
-    // With a key-responsibility buffer (bf16 kernel, several segments) the
+    // With a key-responsibility buffer (bf16 kernels, several segments) the
     // segment pass covers every segment and stores Gamma_K of each chunk; the
     // causal pass loads it instead of routing the keys a second time.
-    const bool reuse = L.gk != nullptr && fast_supported(L) && P > 1;
+    const bool reuse = L.gk != nullptr && (fast_supported(L) || long_supported(L)) && P > 1;
     // the memory after the last token needs the last segment's aggregate too
     const int nagg = reuse || L.state_out ? P : P - 1;
     if (nagg > 0 || L.state_in) {

@@ -19,7 +19,7 @@ constexpr float kPadLogit = -1.0e30f;
 
 // AGG: per-segment state [Vtil | Z] only. CAUSAL: outputs, starting from the
 // exclusive prefix of the earlier segments. BIDIR: outputs against the total.
-// AGG_G and CAUSAL_G (bf16 kernel only): AGG that also stores each chunk's key
+// AGG_G and CAUSAL_G (bf16 kernels only): AGG that also stores each chunk's key
 // responsibilities (the bf16 tile as it sits in LDS), and CAUSAL that loads
 // them instead of routing the keys again.
 enum Mode { AGG = 0, CAUSAL = 1, BIDIR = 2, AGG_G = 3, CAUSAL_G = 4 };
@@ -46,7 +46,7 @@ struct Args {
 // General kernel for bf16, d = dv = 128, KP = 256 (gma_wide.hip).
 hipError_t wide_launch(const Args& a, int mode, int segments, unsigned BH, hipStream_t st);
 
-// bf16 kernel for d = dv = 128 and KP = 256 (gma_long.hip): modes AGG, CAUSAL, BIDIR.
+// bf16 kernel for d = dv = 128 and KP = 256 (gma_long.hip): every mode.
 bool long_supported(const GmaLaunch& L);
 hipError_t long_launch(const Args& a, int mode, int segments, unsigned BH, hipStream_t st);
 

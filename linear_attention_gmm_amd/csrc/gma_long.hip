@@ -47,12 +47,9 @@ constexpr int GB = 64 * kKP * 2;  // of a Gamma tile
 constexpr int SB = kD * kKP * 2;  // of the bf16 state snapshot Vtil^T [dv][comp]
 constexpr int kInstr = XCPR * 64 * 16 / 1024 / kNW;  // DMA instructions per wave per x tile
 
-// LDS layout (bytes). The first 64 KB hold Q, K, Q*Q, K*K during routing and
-// Gamma_K, Gamma_Q after it.
-constexpr int oQ = 0, oK = XB, oQ2 = 2 * XB, oK2 = 3 * XB;
-constexpr int oGK = 0, oGQ = GB;
-constexpr int oV = 4 * XB;
-constexpr int oS = oV + XB;
+// LDS layout (bytes) of the passes with queries: the first 64 KB hold the
+// routing tiles (K, K*K, Q, Q*Q) and then Gamma_K, Gamma_Q; V; the snapshot.
+constexpr int oS = 5 * XB;
 constexpr int oStK = oS + SB;               // [8 waves][64 tokens] (max, sum)
 constexpr int oStQ = oStK + kNW * 64 * 8;   // [8 waves][64 tokens] (max, sum, Z-dot, -)
 constexpr int oZ = oStQ + kNW * 64 * 16;    // bf16 Z of the state before the chunk [KP]
@@ -142,12 +139,30 @@ __device__ __forceinline__ float pick(const float (&x)[4], int i) {
 // Component (relative to the wave's first) of row p of routing tile rt.
 __device__ __forceinline__ constexpr int route_comp(int rt, int p) { return 8 * (p >> 2) + 4 * rt + (p & 3); }
 
+// Modes: AGG (segment states), AGG_G (the same, storing each chunk's Gamma_K
+// tile as it sits in LDS), CAUSAL, CAUSAL_G (loading those tiles instead of
+// routing the keys), BIDIR.
 template <int MODE>
 struct Cfg {
-  static constexpr bool HK = MODE != BIDIR;   // keys: routing, update
-  static constexpr bool HQ = MODE != AGG;     // queries: routing, read
-  static constexpr bool CAUS = MODE == CAUSAL;
+  static constexpr bool IS_AGG = MODE == AGG || MODE == AGG_G;
+  static constexpr bool CAUS = MODE == CAUSAL || MODE == CAUSAL_G;
+  static constexpr bool HK = MODE != BIDIR;        // keys update the state
+  static constexpr bool GLOAD = MODE == CAUSAL_G;  // Gamma_K tiles loaded
+  static constexpr bool GSTORE = MODE == AGG_G;    // Gamma_K tiles stored
+  static constexpr bool RK = HK && !GLOAD;         // keys routed here
+  static constexpr bool HQ = !IS_AGG;              // queries: routing, read
+  // LDS. Segment passes (no queries, no snapshot) double-buffer their tiles:
+  // set s holds K and K*K (then Gamma_K) at s * 2 XB and V at 4 XB + s XB.
+  // The other passes hold Q and Q*Q at 2 XB, 3 XB (then Gamma_Q), K and K*K
+  // at 0, XB (then Gamma_K; or the loaded Gamma_K tile), V at 4 XB and the
+  // snapshot after it.
+  static constexpr int oA(int s) { return IS_AGG ? s * 2 * XB : 0; }
+  static constexpr int oVs(int s) { return IS_AGG ? 4 * XB + s * XB : 4 * XB; }
+  static constexpr int oQx = 2 * XB, oQ2x = 3 * XB;
+  static constexpr int oStK_ = IS_AGG ? 6 * XB : oStK;
+  static constexpr int lds = IS_AGG ? 6 * XB + kNW * 64 * 8 : kLds;
 };
+constexpr int GDMA = GB / 1024 / kNW;  // DMA instructions per wave for a Gamma_K tile
 
 // Logits (log2 units) of this wave's 64 components' two tiles for the 64
 // tokens of an x tile: L[ct][rt] = W_rt [x | x*x]^T (token tile ct) + c.
@@ -256,18 +271,25 @@ struct Dma {
   }
 };
 
+// Linear DMA of one stored Gamma_K tile (GB bytes, in its LDS layout).
+__device__ __forceinline__ void gdma_issue(char* dst, const char* src) {
+  const u32x4 d = buf_desc(src, (uint32_t)GB);
+  const unsigned base = lds_addr(dst) + (unsigned)(wave_id() * GDMA * 1024);
+#pragma unroll
+  for (int i = 0; i < GDMA; ++i)
+    lds_dma16(d, (wave_id() * GDMA + i) * 1024 + lane_id() * 16, base + (unsigned)(i * 1024));
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kNT, 1) void kernel(Args a) {
   typedef Cfg<MODE> C;
   typedef Mma<bf16> M;
-  __shared__ __attribute__((aligned(16))) char smem[kLds];
-  char* const sGK = smem + oGK;
-  char* const sGQ = smem + oGQ;
-  char* const sV = smem + oV;
-  char* const sS = smem + oS;
-  float2* const stK = reinterpret_cast<float2*>(smem + oStK);
+  __shared__ __attribute__((aligned(16))) char smem[C::lds];
+  float2* const stK = reinterpret_cast<float2*>(smem + C::oStK_);
   f32x4* const stQ = reinterpret_cast<f32x4*>(smem + oStQ);
   bf16* const sZ = reinterpret_cast<bf16*>(smem + oZ);
+  char* const sGQ = smem + C::oQx;
+  char* const sS = smem + oS;
 
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int bh = blockIdx.y, p = blockIdx.x;
@@ -282,6 +304,9 @@ __global__ __launch_bounds__(kNT, 1) void kernel(Args a) {
   const bf16* __restrict__ Wh = reinterpret_cast<const bf16*>(a.W) + (size_t)h * kKP * 2 * kD;
   const float* __restrict__ ch = a.c + (size_t)h * kKP;
   const int comp0 = w * kKPW;
+  // stored Gamma_K tiles of this sequence, one per chunk of 64 tokens
+  char* const gkh = C::GSTORE || C::GLOAD ? static_cast<char*>(a.gk) + (size_t)bh * ((N + kChunk - 1) / kChunk) * GB
+                                          : nullptr;
   // read split: query tile qt, value columns 64 dh .. 64 dh + 63; the two waves
   // of a SIMD (w, w + 4) take query tiles qt and 3 - qt
   const int qt = w < 4 ? w : 7 - w;
@@ -325,18 +350,29 @@ __global__ __launch_bounds__(kNT, 1) void kernel(Args a) {
     put_state(sS, sZ, S, Zt, comp0, g, c16);
   }
 
+  // The tiles of chunk c (set c % 2 in segment passes).
   Dma dma;
   dma.init();
+  auto issue = [&](int64_t t, int s) {
+    const int rows = (int)(t_end - t);
+    if constexpr (C::RK) dma.issue(smem + C::oA(s), Kg + (size_t)t * kD, rows);
+    if constexpr (C::GLOAD) gdma_issue(smem + C::oA(s), gkh + (size_t)(t / kChunk) * GB);
+    if constexpr (C::HK) dma.issue(smem + C::oVs(s), Vg + (size_t)t * kD, rows);
+    if constexpr (C::HQ) dma.issue(smem + C::oQx, Qg + (size_t)t * kD, rows);
+  };
+  auto square = [&](int s) {
+    if constexpr (C::RK) square_own(smem + C::oA(s), smem + C::oA(s) + XB);
+    if constexpr (C::HQ) square_own(smem + C::oQx, smem + C::oQ2x);
+  };
   if (t_begin < t_end) {
-    const int rows = (int)(t_end - t_begin);
-    if constexpr (C::HK) {
-      dma.issue(smem + oK, Kg + (size_t)t_begin * kD, rows);
-      dma.issue(sV, Vg + (size_t)t_begin * kD, rows);
+    issue(t_begin, 0);
+    if (C::IS_AGG && t_begin + kChunk < t_end) {
+      issue(t_begin + kChunk, 1);
+      LM_WAIT_VMEM(2 * kInstr);  // the first chunk's tiles
+    } else {
+      wait_vmem();
     }
-    if constexpr (C::HQ) dma.issue(smem + oQ, Qg + (size_t)t_begin * kD, rows);
-    wait_vmem();
-    if constexpr (C::HK) square_own(smem + oK, smem + oK2);
-    if constexpr (C::HQ) square_own(smem + oQ, smem + oQ2);
+    square(0);
   }
   lds_barrier();
 
@@ -344,18 +380,22 @@ __global__ __launch_bounds__(kNT, 1) void kernel(Args a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.f;
 
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kChunk) {
+  int it = 0;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kChunk, ++it) {
     const int nvalid = (int)((t_end - t0) < kChunk ? (t_end - t0) : kChunk);
     const bool more = t0 + kChunk < t_end;
     const int lo = lane_opaque();  // the lane index for LDS addressing in this chunk
     const int co = lo & 15;
+    const int cs = C::IS_AGG ? (it & 1) : 0;  // tile set of this chunk
+    char* const sGK = smem + C::oA(cs);
+    char* const sV = smem + C::oVs(cs);
 
     // ---- 1. routing and wave-local softmax statistics
     bf16x8 Ek[4], Eq[4];  // bf16 exponentials, k = the wave's components in order
     float mk[4], sk[4], mq[4], sq[4], dq[4];
-    if constexpr (C::HK) {
+    if constexpr (C::RK) {
       f32x4 L[4][2];
-      route(L, smem + oK, smem + oK2, Wf, cb, lo);
+      route(L, sGK, sGK + XB, Wf, cb, lo);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         Ek[ct] = local_exp(L[ct], mk[ct]);
@@ -365,7 +405,7 @@ __global__ __launch_bounds__(kNT, 1) void kernel(Args a) {
     }
     if constexpr (C::HQ) {
       f32x4 L[4][2];
-      route(L, smem + oQ, smem + oQ2, Wf, cb, lo);
+      route(L, smem + C::oQx, smem + C::oQ2x, Wf, cb, lo);
       // rows of A: even = 1, odd = Z of the wave's components (state before the chunk)
       const bf16x8 z = *reinterpret_cast<const bf16x8*>(sZ + comp0 + 8 * (lo >> 4));
       const bf16x8 az = (c16 & 1) ? z : ones;
@@ -383,7 +423,7 @@ __global__ __launch_bounds__(kNT, 1) void kernel(Args a) {
     // ---- 2. posterior responsibilities -> Gamma tiles. Lane l combines the
     // eight waves' statistics of token l; rows_all broadcasts them by tile.
     float den_inter = 0.f;
-    if constexpr (C::HK) {
+    if constexpr (C::RK) {
       float mm = stK[l].x;
 #pragma unroll
       for (int ww = 1; ww < kNW; ++ww) mm = vmax(mm, stK[ww * 64 + l].x);
@@ -422,6 +462,15 @@ __global__ __launch_bounds__(kNT, 1) void kernel(Args a) {
     lds_barrier();  // Gamma tiles complete
 
     // ---- 3. read (query tile qt, value columns of half dh) and update
+    if constexpr (C::GSTORE) {
+      // this chunk's Gamma_K tile, as it sits in LDS
+      char* gdst = gkh + (size_t)(t0 / kChunk) * GB;
+#pragma unroll
+      for (int j = 0; j < GB / 16 / kNT; ++j) {
+        const int i = (int)threadIdx.x + j * kNT;
+        *reinterpret_cast<u32x4*>(gdst + 16 * i) = *reinterpret_cast<const u32x4*>(sGK + 16 * i);
+      }
+    }
     if constexpr (C::HQ) {
       // one k-step (32 components) at a time: the Gamma_Q fragment serves the
       // snapshot read and the intra-chunk affinity
@@ -497,29 +546,28 @@ __global__ __launch_bounds__(kNT, 1) void kernel(Args a) {
         }
       }
     }
-    lds_barrier();  // Gamma tiles, the snapshot and V are dead
+    lds_barrier();  // this chunk's Gamma tiles, snapshot and V are dead
 
-    // ---- 4. next chunk's tiles, state snapshot, x*x
-    if (more) {
-      const int64_t t1 = t0 + kChunk;
-      const int rows = (int)(t_end - t1);
-      if constexpr (C::HK) {
-        dma.issue(smem + oK, Kg + (size_t)t1 * kD, rows);
-        dma.issue(sV, Vg + (size_t)t1 * kD, rows);
-      }
-      if constexpr (C::HQ) dma.issue(smem + oQ, Qg + (size_t)t1 * kD, rows);
-    }
-    if constexpr (C::CAUS) put_state(sS, sZ, S, Zt, comp0, lo >> 4, co);
-    if (more) {
+    // ---- 4. next tiles, state snapshot, x*x. Segment passes: the next
+    // chunk's tiles landed during this chunk; the tiles two chunks ahead go
+    // into the set just freed. Other passes: the next chunk's tiles now.
+    if constexpr (C::IS_AGG) {
       wait_vmem();
-      if constexpr (C::HK) square_own(smem + oK, smem + oK2);
-      if constexpr (C::HQ) square_own(smem + oQ, smem + oQ2);
+      if (t0 + 2 * kChunk < t_end) issue(t0 + 2 * kChunk, cs);
+      if (more) square(cs ^ 1);
+    } else {
+      if (more) issue(t0 + kChunk, 0);
+      if constexpr (C::CAUS) put_state(sS, sZ, S, Zt, comp0, lo >> 4, co);
+      if (more) {
+        wait_vmem();
+        square(0);
+      }
     }
     lds_barrier();
   }
-  wait_vmem();  // output stores
+  wait_vmem();  // output and tile stores
 
-  if constexpr (MODE == AGG) {
+  if constexpr (C::IS_AGG) {
     float* ag = a.agg + ((size_t)bh * a.P + p) * kKP * kD;
     float* az = a.aggz + ((size_t)bh * a.P + p) * kKP;
 #pragma unroll
@@ -544,6 +592,8 @@ hipError_t long_launch(const Args& a, int mode, int segments, unsigned BH, hipSt
     case AGG: hipLaunchKernelGGL(lng::kernel<AGG>, grid, block, 0, st, a); break;
     case CAUSAL: hipLaunchKernelGGL(lng::kernel<CAUSAL>, grid, block, 0, st, a); break;
     case BIDIR: hipLaunchKernelGGL(lng::kernel<BIDIR>, grid, block, 0, st, a); break;
+    case AGG_G: hipLaunchKernelGGL(lng::kernel<AGG_G>, grid, block, 0, st, a); break;
+    case CAUSAL_G: hipLaunchKernelGGL(lng::kernel<CAUSAL_G>, grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

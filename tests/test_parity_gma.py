@@ -165,15 +165,18 @@ def test_gma_deterministic():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("N", [4096, 16384])
-def test_stored_key_responsibilities_are_bit_identical(N):
+@pytest.mark.parametrize("name,N", [("gma_bf16_n16k", 4096), ("gma_bf16_n16k", 16384), ("gma_bf16_n128k", 8010),
+                                    ("gma_bf16_n128k", 32768)])
+def test_stored_key_responsibilities_are_bit_identical(name, N):
     # the causal bf16 pass over several segments loads each chunk's key
     # responsibilities stored by the segment pass; the entry point that
     # allocates nothing routes the keys again in the causal pass, with the same
-    # segment plan: the outputs must agree bit for bit
+    # segment plan: the outputs must agree bit for bit (d = 64 with 128
+    # components, and d = 128 with 256)
     import torch
     from linear_attention_gmm_amd import binding
-    cfg = inputs.CONFIGS["gma_bf16_n16k"].replace(B=2, N=N)
+    cfg = inputs.CONFIGS[name].replace(B=2, H=4, N=N) if name == "gma_bf16_n128k" else \
+        inputs.CONFIGS[name].replace(B=2, N=N)
     x = cuda(inputs.gma_inputs(cfg))
     a = binding.gma_forward(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"], causal=True, eps=cfg.eps)
     b = binding.gma_forward_noalloc(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"], causal=True,
