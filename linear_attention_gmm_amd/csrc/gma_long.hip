@@ -353,12 +353,14 @@ __global__ __launch_bounds__(kNT, 1) void kernel(Args a) {
   // The tiles of chunk c (set c % 2 in segment passes).
   Dma dma;
   dma.init();
+  // Q first: the loaded-Gamma_K pass waits for Q only before routing and for
+  // the Gamma_K and V transfers behind it just before the first barrier.
   auto issue = [&](int64_t t, int s) {
     const int rows = (int)(t_end - t);
+    if constexpr (C::HQ) dma.issue(smem + C::oQx, Qg + (size_t)t * kD, rows);
     if constexpr (C::RK) dma.issue(smem + C::oA(s), Kg + (size_t)t * kD, rows);
     if constexpr (C::GLOAD) gdma_issue(smem + C::oA(s), gkh + (size_t)(t / kChunk) * GB);
     if constexpr (C::HK) dma.issue(smem + C::oVs(s), Vg + (size_t)t * kD, rows);
-    if constexpr (C::HQ) dma.issue(smem + C::oQx, Qg + (size_t)t * kD, rows);
   };
   auto square = [&](int s) {
     if constexpr (C::RK) square_own(smem + C::oA(s), smem + C::oA(s) + XB);
@@ -418,6 +420,7 @@ __global__ __launch_bounds__(kNT, 1) void kernel(Args a) {
       }
       stQ[w * 64 + l] = f32x4{pick(mq, g), pick(sq, g), pick(dq, g), 0.f};
     }
+    if constexpr (C::GLOAD) wait_vmem();  // this chunk's Gamma_K and V transfers
     lds_barrier();  // statistics complete; the x and x*x tiles are dead
 
     // ---- 2. posterior responsibilities -> Gamma tiles. Lane l combines the
@@ -559,7 +562,8 @@ __global__ __launch_bounds__(kNT, 1) void kernel(Args a) {
       if (more) issue(t0 + kChunk, 0);
       if constexpr (C::CAUS) put_state(sS, sZ, S, Zt, comp0, lo >> 4, co);
       if (more) {
-        wait_vmem();
+        if constexpr (C::GLOAD) LM_WAIT_VMEM(GDMA + kInstr);  // Q (and everything before it)
+        else wait_vmem();
         square(0);
       }
     }
