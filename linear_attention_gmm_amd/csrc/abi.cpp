@@ -1101,9 +1101,17 @@ int linattn_vec_decode_step(const void* q, const void* k, const void* v, const f
   return dec_run(fn, false, false, La, dk, (size_t)dk * dv, stream);
 }
 
+// The dedicated bf16 backward kernel: d_k = d_v = 128, rows addressed with
+// 32-bit byte offsets within one (b, h) block.
+static bool lin_bwd_bf16(int64_t dk, int64_t dv, int64_t N, int dtype) {
+  return dtype == LM_BF16 && dk == 128 && dv == 128 && (N + 64) * 128 * 2 < ((int64_t)1 << 31);
+}
+
 size_t linattn_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
                                         int dtype, int64_t segments) {
   if (lin_check_shape("linattn_chunk_backward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
+  // bf16 with d = 128: k . dk per token only
+  if (lin_bwd_bf16(dk, dv, N, dtype)) return align_up((size_t)B * H * N * 4);
   // float32 tensors: 5 for the reversed passes, and for bf16 inputs 7 more
   // (float32 copies of q, k, v, do and the gradients before rounding)
   const size_t t = align_up((size_t)B * H * N * dk * 4);
@@ -1140,6 +1148,25 @@ int linattn_chunk_backward(const void* q, const void* k, const void* v, const fl
         return fail(LM_EINVAL, "%s: an output overlaps an input or the workspace", fn);
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], nout[i], outs[j], nout[j])) return fail(LM_EINVAL, "%s: outputs overlap", fn);
+  }
+  if (lin_bwd_bf16(dkk, dvv, N, dtype)) {
+    lm::BwdBf16Launch Lb;
+    Lb.q = q;
+    Lb.k = k;
+    Lb.v = v;
+    Lb.g = g;
+    Lb.dout = dout;
+    Lb.dq = dq;
+    Lb.dk = dk;
+    Lb.dv = dv;
+    Lb.dg = dg;
+    Lb.xk = static_cast<float*>(workspace);
+    Lb.B = B;
+    Lb.H = H;
+    Lb.N = N;
+    hipError_t e = lm::linattn_backward_bf16_launch(Lb, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
+    return ok();
   }
   char* ws = static_cast<char*>(workspace);
   const LinLayout LL = lin_layout(B, H, N, dkk, false, segments);

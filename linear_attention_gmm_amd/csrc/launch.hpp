@@ -178,6 +178,24 @@ struct BwdLaunch {
   bool bf16;
 };
 hipError_t linattn_backward_launch(const BwdLaunch& L, hipStream_t st);
+
+// Backward of decayed linear attention for bf16 inputs with d_k = d_v = 128:
+// one launch of forward-sweep (dq) and reverse-sweep (dk, dv) workgroups, then
+// the suffix sums of the gate gradient.
+struct BwdBf16Launch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* xk;  // workspace: B * H * N floats (k . dk per token)
+  int64_t B, H, N;
+};
+hipError_t linattn_backward_bf16_launch(const BwdBf16Launch& L, hipStream_t st);
 // The float32 passes of that backward on float32 tensors (gates: also dg).
 hipError_t linattn_backward_f32(const BwdLaunch& L, const float* q, const float* k, const float* v,
                                 const float* dout, float* dq, float* dk, float* dv, bool gates, hipStream_t st);

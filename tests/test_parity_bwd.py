@@ -69,3 +69,46 @@ def test_gla_backward_full_size_sampled():
     got, ref = _case(cfg, sl=[(5, 9)])
     for name, a, r in zip(("dq", "dk", "dv", "dg"), got, ref):
         assert_close(a, r, "bf16", "%s bf16 8K workload, slice (5,9)" % name)
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 200])
+def test_gla_backward_bf16_d128_ragged(N):
+    # bf16 with d = 128 (its own kernel): inside one chunk, whole chunks and a
+    # ragged last chunk
+    cfg = inputs.LinAttnConfig("gla_bwd128", 504, B=1, H=2, N=N, dk=128, dv=128, dtype="bf16")
+    got, ref = _case(cfg)
+    for name, a, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        assert_close(a, r, "bf16", "%s bf16 d=128 N=%d" % (name, N))
+    # the first token's gate gradient is rounding of q.dq - k.dk (see above)
+    scale = np.max(np.abs(got[0].astype(np.float32))) + 1e-30
+    assert np.max(np.abs(got[3][:, 0])) <= 1e-3 * scale * 128
+    if N > 1:
+        assert_close(got[3][:, 1:], ref[3][:, 1:], "bf16", "dg bf16 d=128 N=%d (tokens 1..)" % N)
+
+
+@pytest.mark.parametrize("g_logit_mean", [0.0, -1.0])
+def test_gla_backward_bf16_d128_strong_decay(g_logit_mean):
+    # gates around 0.5 and 0.27 per token: states forget within a few tokens
+    cfg = inputs.LinAttnConfig("gla_bwd128", 505, B=2, H=2, N=300, dk=128, dv=128, dtype="bf16",
+                               g_logit_mean=g_logit_mean)
+    got, ref = _case(cfg)
+    for name, a, r in zip(("dq", "dk", "dv", "dg"), got, ref):
+        assert_close(a, r, "bf16", "%s bf16 d=128 g logit mean %g" % (name, g_logit_mean))
+
+
+def test_gla_backward_full_size_last_slice():
+    # the 8K-token GLA workload, the last (b, h) block of the tensors
+    cfg = inputs.CONFIGS["gla_bf16_n8k"]
+    got, ref = _case(cfg, sl=[(7, 15)])
+    for name, a, r in zip(("dq", "dk", "dv", "dg"), got, ref):
+        assert_close(a, r, "bf16", "%s bf16 8K workload, slice (7,15)" % name)
+
+
+def test_gla_backward_bf16_deterministic():
+    cfg = inputs.LinAttnConfig("gla_bwd128", 506, B=2, H=3, N=777, dk=128, dv=128, dtype="bf16")
+    x = cuda(inputs.linattn_inputs(cfg))
+    do = torch.randn(x["v"].shape, generator=torch.Generator().manual_seed(7)).to(torch.bfloat16).cuda()
+    a = binding.linattn_chunk_backward(x["q"], x["k"], x["v"], x["g"], do)
+    b = binding.linattn_chunk_backward(x["q"], x["k"], x["v"], x["g"], do)
+    for s, t in zip(a, b):
+        assert torch.equal(s, t)
