@@ -174,7 +174,11 @@ int gma_forward(const void* q, const void* k, const void* v, const float* mu,
  *   q, k  [B,H,N,dk] (dtype);  v [B,H,N,dv] (dtype)
  *   g     [B,H,N]    per-token, per-head decay (float32), expected in (0, 1]
  *   out   [B,H,N,dv] o_t = S_t^T q_t with S_t = g_t S_{t-1} + k_t v_t^T, S_0 = 0
- *   chunk tokens per chunk; 64 is implemented
+ *   chunk tokens per chunk: 64 (the matrix-core kernels) or 32 (a float32
+ *         kernel with one workgroup per (b, h), segments not used). The
+ *         chunk length changes how the work is cut, not the result: the two
+ *         agree to float32 rounding. The same holds for ccq_forward and the
+ *         _state forms of both; the other chunked calls take 64.
  * Implemented shapes: dk, dv in {16, 32, 64, 128} (see "Feature widths"), any N >= 1.
  */
 size_t linattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,

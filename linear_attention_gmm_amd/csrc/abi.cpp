@@ -175,13 +175,17 @@ LinLayout lin_layout(int64_t B, int64_t H, int64_t N, int64_t dk, bool ccq, int6
   return L;
 }
 
+// allow32: the call also runs with chunks of 32 tokens (the plain and CCQ
+// forwards of decayed linear attention).
 int lin_check_shape(const char* fn, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
-                    int dtype, int64_t segments) {
+                    int dtype, int64_t segments, bool allow32 = false) {
   if (B < 1 || H < 1 || N < 1 || dk < 1 || dv < 1 || chunk < 1)
     return fail(LM_EINVAL, "%s: sizes must be >= 1", fn);
   if (dtype != LM_F32 && dtype != LM_BF16) return fail(LM_EINVAL, "%s: dtype %d is not LM_F32 or LM_BF16", fn, dtype);
   if (segments < 0) return fail(LM_EINVAL, "%s: segments must be >= 0", fn);
-  if (chunk != kChunk) return fail(LM_EUNSUPPORTED, "%s: chunk %lld; 64 is implemented", fn, (long long)chunk);
+  if (chunk != kChunk && !(allow32 && chunk == 32))
+    return fail(LM_EUNSUPPORTED, "%s: chunk %lld; %s implemented", fn, (long long)chunk,
+                allow32 ? "32 and 64 are" : "64 is");
   if (!(dk == 32 || dk == 64 || dk == 128) || dv != dk)
     return fail(LM_EUNSUPPORTED, "%s implements dk == dv in {32, 64, 128} (got dk=%lld dv=%lld)", fn,
                 (long long)dk, (long long)dv);
@@ -194,7 +198,7 @@ int lin_forward(const char* fn, bool ccq, const void* q, const void* k, const vo
                 const float* w_lambda, const float* b_lambda, void* out, int64_t B, int64_t H, int64_t N,
                 int64_t dk, int64_t dv, int64_t chunk, int dtype, int64_t segments, int64_t t_in,
                 const float* state_in, float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = lin_check_shape(fn, B, H, N, dk, dv, chunk, dtype, segments);
+  int st = lin_check_shape(fn, B, H, N, dk, dv, chunk, dtype, segments, true);
   if (st != LM_OK) return st;
   if (!q || !k || !v || !g || !out || !workspace || (ccq && (!w_lambda || !b_lambda)))
     return fail(LM_EINVAL, "%s: null pointer argument", fn);
@@ -236,6 +240,7 @@ int lin_forward(const char* fn, bool ccq, const void* q, const void* k, const vo
   La.state_in = state_in;
   La.state_out = state_out;
   La.t_in = t_in;
+  La.chunk = chunk;
   hipError_t e = lm::linattn_launch(La, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
   return ok();
@@ -721,7 +726,7 @@ int lin_pad_check(const char* fn, Lin kind, int64_t B, int64_t H, int64_t N, int
   if (st != LM_OK) return st;
   const int64_t D = pad_width(dk, dv);
   if (kind == Lin::delta || kind == Lin::ccq_delta) return delta_check_shape(fn, B, H, N, D, D, chunk, dtype, segments);
-  return lin_check_shape(fn, B, H, N, D, D, chunk, dtype, segments);
+  return lin_check_shape(fn, B, H, N, D, D, chunk, dtype, segments, kind == Lin::gla || kind == Lin::ccq);
 }
 
 PadLayout lin_pad_layout(Lin kind, int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int dtype,
@@ -901,7 +906,7 @@ size_t linattn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int6
                                int64_t segments) {
   if (!native_widths(dk, dv))
     return lin_padded_bytes("linattn_chunk_forward", Lin::gla, B, H, N, dk, dv, chunk, dtype, segments);
-  if (lin_check_shape("linattn_chunk_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
+  if (lin_check_shape("linattn_chunk_forward", B, H, N, dk, dv, chunk, dtype, segments, true) != LM_OK) return 0;
   return lin_layout(B, H, N, dk, false, segments).total;
 }
 
@@ -947,7 +952,7 @@ int linattn_decode_step(const void* q, const void* k, const void* v, const float
 size_t ccq_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk, int dtype,
                            int64_t segments) {
   if (!native_widths(dk, dv)) return lin_padded_bytes("ccq_forward", Lin::ccq, B, H, N, dk, dv, chunk, dtype, segments);
-  if (lin_check_shape("ccq_forward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
+  if (lin_check_shape("ccq_forward", B, H, N, dk, dv, chunk, dtype, segments, true) != LM_OK) return 0;
   return lin_layout(B, H, N, dk, true, segments).total;
 }
 

@@ -47,8 +47,11 @@ struct LinLaunch {
   const float* state_in;
   float* state_out;
   int64_t t_in;
+  int64_t chunk = 64;  // tokens per chunk: 64 (matrix-core kernels) or 32 (linattn_c32.hip)
 };
 hipError_t linattn_launch(const LinLaunch& L, hipStream_t st);
+// Chunks of 32 tokens (linattn_c32.hip): one workgroup per (b, h), no segments.
+hipError_t linattn_c32_launch(const LinLaunch& L, hipStream_t st);
 
 // Chunk pass of the CCQ read for bf16 inputs at dk = dv = 128 (ccq_pipe.hip):
 // one workgroup per (b, h, segment), starting from the segment's state block

@@ -1141,6 +1141,7 @@ static hipError_t launch_t(const LinLaunch& L, hipStream_t st) {
 }  // namespace lin
 
 hipError_t linattn_launch(const LinLaunch& L, hipStream_t st) {
+  if (L.chunk == 32) return linattn_c32_launch(L, st);
   if (L.bf16) return L.ccq ? lin::launch_t<bf16, true>(L, st) : lin::launch_t<bf16, false>(L, st);
   return L.ccq ? lin::launch_t<float, true>(L, st) : lin::launch_t<float, false>(L, st);
 }

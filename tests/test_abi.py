@@ -110,10 +110,12 @@ def _lin(L, fn, **kw):
     (dict(k=None), binding.LM_EINVAL),
     (dict(g=FAKE + (3 << 30) + 2), binding.LM_EINVAL),
     (dict(H=0), binding.LM_EINVAL),
-    (dict(chunk=32), binding.LM_EUNSUPPORTED),
+    (dict(chunk=48), binding.LM_EUNSUPPORTED),
+    (dict(chunk=128), binding.LM_EUNSUPPORTED),
     (dict(dk=96, dv=96), binding.LM_EUNSUPPORTED),
     (dict(dk=64, dv=96), binding.LM_EUNSUPPORTED),
     (dict(wsb=8), binding.LM_EWORKSPACE),
+    (dict(chunk=32, wsb=8), binding.LM_EWORKSPACE),  # chunk 32 runs (needs the same workspace)
     (dict(dk=16, dv=64, wsb=8), binding.LM_EWORKSPACE),  # padded shape
     (dict(dk=16, dv=64, out=FAKE + (2 << 30) + 64), binding.LM_EINVAL),  # padded shape, out overlaps v
     (dict(dk=32, dv=64, ws=FAKE + (3 << 30)), binding.LM_EINVAL),  # padded shape, g inside the workspace
@@ -445,3 +447,24 @@ def test_noalloc_checks_before_any_hip_call():
     assert call(p[:6] + [p[6] + 2], seg=1)[0] == binding.LM_EINVAL  # misaligned out
     assert call(p, seg=1, eps=-1.0)[0] == binding.LM_EINVAL
     assert call(p, d=48, seg=1)[0] == binding.LM_EUNSUPPORTED
+
+
+@needs_lib
+@pytest.mark.parametrize("fn", ["linattn_workspace_bytes", "ccq_workspace_bytes"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (16, 64), (128, 128)])
+def test_chunk32_accepted(fn, dk, dv):
+    # chunks of 32 tokens are implemented for the plain and CCQ forwards
+    L = binding.lib()
+    assert getattr(L, fn)(2, 3, 500, dk, dv, 32, binding.LM_F32, 0) > 0
+    assert getattr(L, fn)(2, 3, 500, dk, dv, 32, binding.LM_BF16, 0) > 0
+    assert getattr(L, fn)(2, 3, 500, dk, dv, 48, binding.LM_F32, 0) == 0
+
+
+@needs_lib
+@pytest.mark.parametrize("fn", ["deltanet_workspace_bytes", "ccq_deltanet_workspace_bytes",
+                                "linattn_vec_workspace_bytes", "linattn_backward_workspace_bytes"])
+def test_chunk32_not_elsewhere(fn):
+    # the other chunked calls run chunks of 64 only
+    L = binding.lib()
+    assert getattr(L, fn)(2, 3, 500, 64, 64, 64, binding.LM_F32, 0) > 0
+    assert getattr(L, fn)(2, 3, 500, 64, 64, 32, binding.LM_F32, 0) == 0
