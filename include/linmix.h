@@ -355,11 +355,12 @@ int ccq_backward(const void* q, const void* k, const void* v, const float* g,
  * Source: "Gaussian Mixture Attention", Method -> core mechanism (posterior
  * responsibilities), latent memory routing (write and read phases), variants
  * and training (trained end to end; softplus variances, softmax priors).
- * Implemented: causal 0 or 1, d == dv in {32, 64}, 1 <= K <= 128,
- * N <= 2^29. Outputs must not overlap each other, the inputs or the workspace
- * (of at least gma_backward_workspace_bytes; float32 rows of 64 or 128
- * entries per token, about 14 such tensors, twice as many rows when
- * bidirectional).
+ * Implemented: causal 0 or 1, d == dv in {32, 64, 128}, 1 <= K <= 256,
+ * N <= 2^29. With d = 128 or K > 128 the inner linear attention runs on
+ * blocks of 128 feature and value columns (once per pair of blocks, summed).
+ * Outputs must not overlap each other, the inputs or the workspace (of at
+ * least gma_backward_workspace_bytes; float32 rows of 64 to 256 entries per
+ * token, about 14 such tensors, twice as many rows when bidirectional).
  */
 size_t gma_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K,
                                     int64_t dv, int causal, int dtype);

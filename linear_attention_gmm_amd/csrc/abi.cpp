@@ -489,14 +489,22 @@ int64_t gma_bwd_width(int64_t K, int64_t dv) {
 }
 
 struct GmaBwdLayout {
-  size_t iv, cst, rows[8], ones, inner[5], rg, agg, part, sums, total;
+  size_t iv, cst, rows[8], ones, inner[5], rg, agg, part, sums, tmp[3], total;
   LinLayout lin;
   int64_t DL, nseg, seg_len, NN;
+  int64_t NF, NVB;  // wide shapes: blocks of 128 responsibility / value columns (1 otherwise)
+  bool wide;
 };
+
+// d = 128 or more than 128 components: the inner tensors in blocks of 128 columns.
+bool gma_bwd_wide(int64_t d, int64_t K) { return d > 64 || K > 128; }
 
 GmaBwdLayout gma_bwd_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal) {
   GmaBwdLayout L;
-  L.DL = gma_bwd_width(K, dv);
+  L.wide = gma_bwd_wide(d, K);
+  L.DL = L.wide ? 128 : gma_bwd_width(K, dv);
+  L.NF = L.wide ? (K + 127) / 128 : 1;
+  L.NVB = L.wide ? (dv + 128) / 128 : 1;
   L.NN = causal ? N : 2 * N;  // bidirectional: keys in rows [0, N), queries in [N, 2N)
   // token ranges of the routing and chain-rule kernels: about 1024 workgroups
   const int64_t want = (1024 + 2 * B * H - 1) / (2 * B * H);
@@ -505,7 +513,9 @@ GmaBwdLayout gma_bwd_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t 
   L.seg_len = len;
   L.nseg = (N + len - 1) / len;
   L.lin = lin_layout(B, H, L.NN, L.DL, false, 0);
-  const size_t rowt = align_up((size_t)B * H * L.NN * L.DL * 4), colt = align_up((size_t)B * H * L.NN * 4);
+  // wide: every row tensor holds two blocks (also B*H*N rows of 256 floats)
+  const size_t blk = align_up((size_t)B * H * L.NN * L.DL * 4);
+  const size_t rowt = L.wide ? 2 * blk : blk, colt = align_up((size_t)B * H * L.NN * 4);
   size_t off = 0;
   L.iv = off;
   off = align_up(off + (size_t)H * K * d * 4);
@@ -529,6 +539,10 @@ GmaBwdLayout gma_bwd_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t 
   off = align_up(off + (size_t)H * 2 * B * L.nseg * K * (2 * d + 1) * 4);
   L.sums = off;
   off = align_up(off + (size_t)H * K * (2 * d + 1) * 4);
+  for (int i = 0; i < 3; ++i) {
+    L.tmp[i] = off;
+    off += L.wide ? blk : 0;
+  }
   L.total = off;
   return L;
 }
@@ -539,10 +553,10 @@ int gma_bwd_check(const char* fn, int64_t B, int64_t H, int64_t N, int64_t d, in
   if (dtype != LM_F32 && dtype != LM_BF16) return fail(LM_EINVAL, "%s: dtype %d is not LM_F32 or LM_BF16", fn, dtype);
   if (causal != 0 && causal != 1) return fail(LM_EINVAL, "%s: causal must be 0 or 1 (got %d)", fn, causal);
   if (!(eps >= 0.f) || std::isinf(eps)) return fail(LM_EINVAL, "%s: eps must be finite and >= 0", fn);
-  if (!(d == 32 || d == 64) || dv != d)
-    return fail(LM_EUNSUPPORTED, "%s implements d == dv in {32, 64} (got d=%lld dv=%lld)", fn, (long long)d,
+  if (!(d == 32 || d == 64 || d == 128) || dv != d)
+    return fail(LM_EUNSUPPORTED, "%s implements d == dv in {32, 64, 128} (got d=%lld dv=%lld)", fn, (long long)d,
                 (long long)dv);
-  if (K > 128) return fail(LM_EUNSUPPORTED, "%s implements K <= 128 (got %lld)", fn, (long long)K);
+  if (K > 256) return fail(LM_EUNSUPPORTED, "%s implements K <= 256 (got %lld)", fn, (long long)K);
   if (N > (int64_t(1) << 29) || B * H > 65535) return fail(LM_EUNSUPPORTED, "%s: N <= 2^29 and B*H <= 65535", fn);
   return LM_OK;
 }
@@ -1324,6 +1338,14 @@ int gma_backward(const void* q, const void* k, const void* v, const float* mu, c
   La.nseg = L.nseg;
   La.seg_len = L.seg_len;
   La.NN = L.NN;
+  La.NF = L.NF;
+  La.NVB = L.NVB;
+  La.bstride = (size_t)B * H * L.NN * 128;
+  if (L.wide) {
+    La.tq = F(L.tmp[0]);
+    La.tk = F(L.tmp[1]);
+    La.tv = F(L.tmp[2]);
+  }
   La.causal = causal;
   La.eps = eps;
   La.bf16 = dtype == LM_BF16;

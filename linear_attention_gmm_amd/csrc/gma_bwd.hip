@@ -48,15 +48,16 @@ constexpr int kThr = 128; // threads per workgroup: one per component (K <= 128)
 
 // Per head: iv[k][d] = exp(-log_var), cst[k] = log pi_k - 1/2 sum_d log_var_kd
 // (log pi = log-softmax of the mixing logits).
-__global__ __launch_bounds__(kThr) void prep_kernel(const float* __restrict__ log_var,
-                                                    const float* __restrict__ logit_pi, float* __restrict__ iv,
-                                                    float* __restrict__ cst, int K, int D) {
-  __shared__ float red[kThr];
+template <int NT>
+__global__ __launch_bounds__(NT) void prep_kernel(const float* __restrict__ log_var,
+                                                  const float* __restrict__ logit_pi, float* __restrict__ iv,
+                                                  float* __restrict__ cst, int K, int D) {
+  __shared__ float red[NT];
   const int h = blockIdx.x, k = threadIdx.x;
   const float lp = k < K ? logit_pi[(size_t)h * K + k] : -INFINITY;
   red[k] = lp;
   __syncthreads();
-  for (int s = kThr / 2; s > 0; s >>= 1) {
+  for (int s = NT / 2; s > 0; s >>= 1) {
     if (k < s) red[k] = fmaxf(red[k], red[k + s]);
     __syncthreads();
   }
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(kThr) void prep_kernel(const float* __restrict__ lo
   __syncthreads();
   red[k] = k < K ? expf(lp - mx) : 0.f;
   __syncthreads();
-  for (int s = kThr / 2; s > 0; s >>= 1) {
+  for (int s = NT / 2; s > 0; s >>= 1) {
     if (k < s) red[k] += red[k + s];
     __syncthreads();
   }
@@ -393,11 +394,12 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
 
 // Parameter gradients per head from the summed partials S1, S2, S0:
 // dmu = iv * S1, dlog_var = -1/2 S0 + 1/2 iv * S2, dlogit_pi = S0 - pi * sum S0.
-__global__ __launch_bounds__(kThr) void params_kernel(const float* __restrict__ sums, const float* __restrict__ iv,
-                                                      const float* __restrict__ logit_pi, float* __restrict__ dmu,
-                                                      float* __restrict__ dlv, float* __restrict__ dlp, int K,
-                                                      int D) {
-  __shared__ float red[kThr];
+template <int NT>
+__global__ __launch_bounds__(NT) void params_kernel(const float* __restrict__ sums, const float* __restrict__ iv,
+                                                    const float* __restrict__ logit_pi, float* __restrict__ dmu,
+                                                    float* __restrict__ dlv, float* __restrict__ dlp, int K,
+                                                    int D) {
+  __shared__ float red[NT];
   const int h = blockIdx.x, c = threadIdx.x;
   const int F = 2 * D + 1;
   const float* base = sums + ((size_t)h * K + (c < K ? c : 0)) * F;
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(kThr) void params_kernel(const float* __restrict__ 
   const float lp = c < K ? logit_pi[(size_t)h * K + c] : -INFINITY;
   red[c] = lp;
   __syncthreads();
-  for (int s = kThr / 2; s > 0; s >>= 1) {
+  for (int s = NT / 2; s > 0; s >>= 1) {
     if (c < s) red[c] = fmaxf(red[c], red[c + s]);
     __syncthreads();
   }
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(kThr) void params_kernel(const float* __restrict__ 
   const float e = c < K ? expf(lp - mx) : 0.f;
   red[c] = e;
   __syncthreads();
-  for (int s = kThr / 2; s > 0; s >>= 1) {
+  for (int s = NT / 2; s > 0; s >>= 1) {
     if (c < s) red[c] += red[c + s];
     __syncthreads();
   }
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(kThr) void params_kernel(const float* __restrict__ 
   __syncthreads();
   red[c] = g0;
   __syncthreads();
-  for (int s = kThr / 2; s > 0; s >>= 1) {
+  for (int s = NT / 2; s > 0; s >>= 1) {
     if (c < s) red[c] += red[c + s];
     __syncthreads();
   }
@@ -463,7 +465,8 @@ static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
   const int K = (int)L.K, DL = (int)L.DL, H = (int)L.H;
   const int64_t N = L.N, NN = L.NN, qoff = L.causal ? 0 : N;
   hipError_t e;
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)H), dim3(kThr), 0, st, L.log_var, L.logit_pi, L.iv, L.cst, K, D);
+  hipLaunchKernelGGL(prep_kernel<kThr>, dim3((unsigned)H), dim3(kThr), 0, st, L.log_var, L.logit_pi, L.iv, L.cst, K,
+                     D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!L.causal) {
     // bidirectional: queries in rows [N, 2N), keys and values in [0, N)
@@ -526,7 +529,7 @@ static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((nred + 255) / 256)), dim3(256), 0, st, L.part, L.sums, nred, K,
                      NF, (int)(2 * L.B * L.nseg));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(params_kernel, dim3((unsigned)H), dim3(kThr), 0, st, L.sums, L.iv, L.logit_pi, L.dmu,
+  hipLaunchKernelGGL(params_kernel<kThr>, dim3((unsigned)H), dim3(kThr), 0, st, L.sums, L.iv, L.logit_pi, L.dmu,
                      L.dlog_var, L.dlogit_pi, K, D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if constexpr (sizeof(T) == 2)
@@ -538,10 +541,412 @@ static hipError_t run(const GmaBwdLaunch& L, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Wide shapes: d = 128 or more than 128 components (K <= 256). The inner
+// linear attention then has more than 128 features (K) or value columns
+// (d + 1), so its tensors are cut into blocks of 128 columns, each a dense
+// [B*H][NN][128] float32 tensor (block b at b * bstride floats): the
+// responsibilities and their gradients in NF = ceil(K / 128) blocks, the
+// values [v | 1 | 0 ...], the inner output and its gradient and the value
+// gradient in NVB = ceil((d + 1) / 128) blocks. The inner products are sums
+// over the feature blocks, so the inner forward and backward run once per
+// (feature block, value block) pair and the results are summed.
+constexpr int kWT = 256;  // threads of the routing and partial-sum kernels: one per component
+
+__device__ __forceinline__ size_t wcol(int c, size_t bstride) { return (size_t)(c >> 7) * bstride + (c & 127); }
+
+// Sums / maxima over the 256 threads (4 waves) of kTT values at once; red holds 4 kTT floats.
+template <bool MAX>
+__device__ __forceinline__ void block_red4(float (&x)[kTT], float* red) {
+#pragma unroll
+  for (int t = 0; t < kTT; ++t) {
+    float v = x[t];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float o = __shfl_xor(v, off);
+      v = MAX ? fmaxf(v, o) : v + o;
+    }
+    x[t] = v;
+  }
+  if (lane_id() == 0) {
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) red[wave_id() * kTT + t] = x[t];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < kTT; ++t) {
+    const float a = red[t], b = red[kTT + t], c = red[2 * kTT + t], d = red[3 * kTT + t];
+    x[t] = MAX ? fmaxf(fmaxf(a, b), fmaxf(c, d)) : (a + b) + (c + d);
+  }
+  __syncthreads();
+}
+
+// Responsibilities of q (blockIdx.z = 0) or k (1) in the block layout; thread =
+// component; the component's mu and 1/var pass through registers 32 features
+// at a time.
+template <typename T, int D>
+__global__ __launch_bounds__(kWT) void route_wide_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                         const float* __restrict__ mu, const float* __restrict__ iv,
+                                                         const float* __restrict__ cst, float* __restrict__ gq,
+                                                         float* __restrict__ gk, size_t bstride, int64_t N,
+                                                         int64_t NN, int64_t qoff, int H, int K, int NF, int64_t len) {
+  __shared__ float sx[kTT][D];
+  __shared__ float red[4 * kTT];
+  const int bh = blockIdx.y, h = bh % H, c = threadIdx.x;
+  const T* __restrict__ x = (blockIdx.z == 0 ? q : k) + (size_t)bh * N * D;
+  float* __restrict__ out = blockIdx.z == 0 ? gq + ((size_t)bh * NN + qoff) * 128 : gk + (size_t)bh * NN * 128;
+  const bool live = c < K;
+  const float* __restrict__ mr = mu + ((size_t)h * K + (live ? c : 0)) * D;
+  const float* __restrict__ ir = iv + ((size_t)h * K + (live ? c : 0)) * D;
+  const float ck = live ? cst[(size_t)h * K + c] : 0.f;
+  const int64_t t_begin = (int64_t)blockIdx.x * len;
+  const int64_t t_end = N < t_begin + len ? N : t_begin + len;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT) {
+    const int nv = (int)(t_end - t0 < kTT ? t_end - t0 : kTT);
+    for (int i = c; i < kTT * D; i += kWT) {
+      const int t = i / D, dd = i - t * D;
+      sx[t][dd] = t < nv ? to_f32(x[(size_t)(t0 + t) * D + dd]) : 0.f;
+    }
+    __syncthreads();
+    float acc[kTT];
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) acc[t] = 0.f;
+    if (live) {
+      for (int d0 = 0; d0 < D; d0 += 32) {
+        float m[32], w[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          m[i] = mr[d0 + i];
+          w[i] = ir[d0 + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+#pragma unroll
+          for (int t = 0; t < kTT; ++t) {
+            const float e = sx[t][d0 + i] - m[i];
+            acc[t] += e * e * w[i];
+          }
+      }
+    }
+    float l[kTT], mx[kTT];
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) mx[t] = l[t] = live ? ck - 0.5f * acc[t] : -INFINITY;
+    block_red4<true>(mx, red);
+    float e[kTT], sm[kTT];
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) sm[t] = e[t] = live ? expf(l[t] - mx[t]) : 0.f;
+    block_red4<false>(sm, red);
+    if (c < NF * 128) {
+      for (int t = 0; t < nv; ++t) out[(size_t)(t0 + t) * 128 + wcol(c, bstride)] = e[t] / sm[t];
+    }
+  }
+}
+
+// Values [v | 1 | 0 ...] of the inner linear attention in the block layout
+// (rows [0, N) of each sequence's NN rows).
+template <typename T>
+__global__ __launch_bounds__(256) void pack_wide_kernel(const T* __restrict__ v, float* __restrict__ vx,
+                                                        size_t bstride, int64_t N, int64_t NN, int64_t total, int DV,
+                                                        int NVB) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int W = NVB * 128;
+  const int64_t r = i / W;  // bh * N + t
+  const int c = (int)(i - r * W);
+  const int64_t bh = r / N, t = r - bh * N;
+  vx[((size_t)bh * NN + t) * 128 + wcol(c, bstride)] = c < DV ? to_f32(v[r * DV + c]) : (c == DV ? 1.f : 0.f);
+}
+
+// Output gradient [dN | dD | 0 ...] of the inner linear attention from its
+// output y = [N | D - eps | ...] and dO, one wave per token, block layout.
+template <typename T>
+__global__ __launch_bounds__(256) void out_grad_wide_kernel(const float* __restrict__ y, const T* __restrict__ dout,
+                                                            float* __restrict__ dy, size_t bstride, int64_t N,
+                                                            int64_t NN, int64_t qoff, int64_t rows, int DV, int NVB,
+                                                            float eps) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave_id();  // bh * N + t
+  if (r >= rows) return;
+  const int64_t bh = r / N, yr = bh * NN + qoff + (r - bh * N);
+  const int l = lane_id();
+  const float inv = 1.f / (y[yr * 128 + wcol(DV, bstride)] + eps);
+  float s = 0.f;
+  for (int c = l; c < DV; c += 64) s += to_f32(dout[r * DV + c]) * y[yr * 128 + wcol(c, bstride)] * inv;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  for (int c = l; c < NVB * 128; c += 64)
+    dy[yr * 128 + wcol(c, bstride)] = c < DV ? to_f32(dout[r * DV + c]) * inv : (c == DV ? -s * inv : 0.f);
+}
+
+// a[i] += b[i]
+__global__ __launch_bounds__(256) void add_kernel(float* __restrict__ a, const float* __restrict__ b, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) a[i] += b[i];
+}
+
+// Softmax backward per token of one side: dl_k = g_k (dg_k - sum_k' g_k' dg_k'),
+// written as rows of 256 floats (zero past K); one wave per token.
+__global__ __launch_bounds__(256) void dl_wide_kernel(const float* __restrict__ gx, const float* __restrict__ dgx,
+                                                      float* __restrict__ dl, size_t bstride, int64_t N, int64_t NN,
+                                                      int64_t off, int64_t rows, int K) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave_id();  // bh * N + t
+  if (r >= rows) return;
+  const int64_t bh = r / N, xr = bh * NN + off + (r - bh * N);
+  const int l = lane_id();
+  float g[4], dg[4], s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int c = l + 64 * m;
+    const bool ok = c < K;
+    g[m] = ok ? gx[xr * 128 + wcol(c, bstride)] : 0.f;
+    dg[m] = ok ? dgx[xr * 128 + wcol(c, bstride)] : 0.f;
+    s += g[m] * dg[m];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  // The component with the largest responsibility: where it holds almost all
+  // the mass, dg - s is a difference of two nearly equal numbers, so its dl is
+  // formed as g sum_k' g_k' (dg - dg_k') instead (the same value, as the
+  // responsibilities sum to 1), whose terms carry no cancellation.
+  float bv = g[0];
+  int bi = l;
+#pragma unroll
+  for (int m = 1; m < 4; ++m)
+    if (g[m] > bv) {
+      bv = g[m];
+      bi = l + 64 * m;
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  const int cs = __builtin_amdgcn_readfirstlane(bi);
+  const float own = cs < 64 ? dg[0] : cs < 128 ? dg[1] : cs < 192 ? dg[2] : dg[3];
+  const float dgs = __shfl(own, cs & 63);
+  float rr = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) rr += g[m] * (dgs - dg[m]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) rr += __shfl_xor(rr, o);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int c = l + 64 * m;
+    dl[r * 256 + c] = c == cs ? g[m] * rr : g[m] * (dg[m] - s);
+  }
+}
+
+// dx_d = sum_k dl_k mu_kd / var_kd - x_d sum_k dl_k / var_kd for kTT tokens of
+// one side per workgroup; thread = feature.
+template <typename T, int D>
+__global__ __launch_bounds__(D < 64 ? 64 : D) void dx_wide_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                                 const float* __restrict__ dlq,
+                                                                 const float* __restrict__ dlk,
+                                                                 const float* __restrict__ mu,
+                                                                 const float* __restrict__ iv, T* __restrict__ dq,
+                                                                 T* __restrict__ dk, int64_t N, int H, int K) {
+  __shared__ float sdl[kTT][256];
+  const int bh = blockIdx.y, h = bh % H, side = blockIdx.z, d = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * kTT;
+  const int nv = (int)(N - t0 < kTT ? N - t0 : kTT);
+  const float* __restrict__ dl = (side == 0 ? dlq : dlk) + ((size_t)bh * N + t0) * 256;
+  for (int i = threadIdx.x; i < kTT * 256; i += blockDim.x) sdl[i / 256][i % 256] = i / 256 < nv ? dl[i] : 0.f;
+  __syncthreads();
+  if (d >= D) return;
+  float s1[kTT], s2[kTT];
+#pragma unroll
+  for (int t = 0; t < kTT; ++t) s1[t] = s2[t] = 0.f;
+  for (int c = 0; c < K; ++c) {
+    const float w = iv[((size_t)h * K + c) * D + d];
+    const float a = mu[((size_t)h * K + c) * D + d] * w;
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) {
+      s1[t] += sdl[t][c] * a;
+      s2[t] += sdl[t][c] * w;
+    }
+  }
+  const T* __restrict__ x = (side == 0 ? q : k) + ((size_t)bh * N + t0) * D;
+  T* __restrict__ dx = (side == 0 ? dq : dk) + ((size_t)bh * N + t0) * D;
+  for (int t = 0; t < nv; ++t) dx[(size_t)t * D + d] = from_f32<T>(s1[t] - to_f32(x[(size_t)t * D + d]) * s2[t]);
+}
+
+// Parameter partial sums of one token range of one side and 32 features:
+//   part[h][slot][k] = [sum dl (x - mu) (D) | sum dl (x - mu)^2 (D) | sum dl]
+// (the features d0 .. d0 + 31 of the first two, and the last entry from the
+// first feature chunk), slot = (side * B + b) * nseg + range; thread = component.
+template <typename T, int D>
+__global__ __launch_bounds__(kWT) void partial_wide_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                           const float* __restrict__ dlq,
+                                                           const float* __restrict__ dlk,
+                                                           const float* __restrict__ mu, float* __restrict__ part,
+                                                           int64_t N, int B, int H, int K, int64_t len, int nseg) {
+  __shared__ float sx[kTT][32];
+  constexpr int NDC = D / 32;
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int side = blockIdx.z / NDC, d0 = 32 * (blockIdx.z % NDC), c = threadIdx.x;
+  const T* __restrict__ x = (side == 0 ? q : k) + (size_t)bh * N * D;
+  const float* __restrict__ dl = (side == 0 ? dlq : dlk) + (size_t)bh * N * 256;
+  const bool live = c < K;
+  float m[32], p1[32], p2[32], p0 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    m[i] = live ? mu[((size_t)h * K + c) * D + d0 + i] : 0.f;
+    p1[i] = p2[i] = 0.f;
+  }
+  const int64_t t_begin = (int64_t)blockIdx.x * len;
+  const int64_t t_end = N < t_begin + len ? N : t_begin + len;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT) {
+    const int nv = (int)(t_end - t0 < kTT ? t_end - t0 : kTT);
+    for (int i = c; i < kTT * 32; i += kWT) {
+      const int t = i / 32, dd = i % 32;
+      sx[t][dd] = t < nv ? to_f32(x[(size_t)(t0 + t) * D + d0 + dd]) : 0.f;
+    }
+    __syncthreads();
+    for (int t = 0; t < nv; ++t) {
+      const float g = dl[(size_t)(t0 + t) * 256 + c];
+      p0 += g;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float e = sx[t][i] - m[i];
+        const float a = g * e;
+        p1[i] += a;
+        p2[i] += a * e;
+      }
+    }
+    __syncthreads();
+  }
+  if (live) {
+    const int slot = (side * B + b) * nseg + (int)blockIdx.x;
+    float* dst = part + (((size_t)h * 2 * B * nseg + slot) * K + c) * (2 * D + 1);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      dst[d0 + i] = p1[i];
+      dst[D + d0 + i] = p2[i];
+    }
+    if (d0 == 0) dst[2 * D] = p0;
+  }
+}
+
+static hipError_t add_into(float* a, const float* b, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(add_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, b, n);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t run_wide(const GmaBwdLaunch& L, hipStream_t st) {
+  const int64_t BH = L.B * L.H, rows = BH * L.N;
+  const int K = (int)L.K, H = (int)L.H, NF = (int)L.NF, NVB = (int)L.NVB;
+  const int64_t N = L.N, NN = L.NN, qoff = L.causal ? 0 : N;
+  const size_t bs = L.bstride;  // floats per block tensor: B*H*NN*128
+  hipError_t e;
+  hipLaunchKernelGGL(prep_kernel<kWT>, dim3((unsigned)H), dim3(kWT), 0, st, L.log_var, L.logit_pi, L.iv, L.cst, K, D);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int b = 0; b < 2; ++b) {
+    if (!L.causal) {
+      // bidirectional: queries in rows [N, 2N), keys and values in [0, N)
+      if ((e = fill_rows(L.gq + b * bs, L, 0, N, 128, 0.f, st)) != hipSuccess) return e;
+      if ((e = fill_rows(L.gk + b * bs, L, N, N, 128, 0.f, st)) != hipSuccess) return e;
+      if ((e = fill_rows(L.vx + b * bs, L, N, N, 128, 0.f, st)) != hipSuccess) return e;
+      if ((e = fill_rows(L.dy + b * bs, L, 0, N, 128, 0.f, st)) != hipSuccess) return e;
+    }
+  }
+  if ((e = fill_rows(L.ones, L, 0, NN, 1, 1.f, st)) != hipSuccess) return e;
+  const dim3 grid((unsigned)L.nseg, (unsigned)BH, 2);
+  hipLaunchKernelGGL((route_wide_kernel<T, D>), grid, dim3(kWT), 0, st, static_cast<const T*>(L.q),
+                     static_cast<const T*>(L.k), L.mu, L.iv, L.cst, L.gq, L.gk, bs, N, NN, qoff, H, K, NF, L.seg_len);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t npk = rows * NVB * 128;
+  hipLaunchKernelGGL((pack_wide_kernel<T>), dim3((unsigned)((npk + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const T*>(L.v), L.vx, bs, N, NN, npk, D, NVB);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // inner forward, y_vb = sum_fb LA(gq_fb, gk_fb, vx_vb)
+  LinLaunch F = L.bwd.fwd;
+  F.g = L.ones;
+  F.bf16 = false;
+  F.ccq = false;
+  F.state_in = nullptr;
+  F.state_out = nullptr;
+  F.t_in = 0;
+  for (int vb = 0; vb < NVB; ++vb) {
+    for (int fb = 0; fb < NF; ++fb) {
+      F.q = L.gq + fb * bs;
+      F.k = L.gk + fb * bs;
+      F.v = L.vx + vb * bs;
+      F.out = fb == 0 ? L.y + vb * bs : L.tq;
+      if ((e = linattn_launch(F, st)) != hipSuccess) return e;
+      if (fb > 0 && (e = add_into(L.y + vb * bs, L.tq, (int64_t)bs, st)) != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL((out_grad_wide_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, L.y,
+                     static_cast<const T*>(L.dout), L.dy, bs, N, NN, qoff, rows, D, NVB, L.eps);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // inner backward per (feature block, value block), summed
+  BwdLaunch Bw = L.bwd;
+  Bw.g = L.ones;
+  for (int fb = 0; fb < NF; ++fb) {
+    for (int vb = 0; vb < NVB; ++vb) {
+      float* oq = vb == 0 ? L.dgq + fb * bs : L.tq;
+      float* ok = vb == 0 ? L.dgk + fb * bs : L.tk;
+      float* ov = fb == 0 ? L.dvx + vb * bs : L.tv;
+      if ((e = linattn_backward_f32(Bw, L.gq + fb * bs, L.gk + fb * bs, L.vx + vb * bs, L.dy + vb * bs, oq, ok, ov,
+                                    false, st)) != hipSuccess)
+        return e;
+      if (vb > 0 && (e = add_into(L.dgq + fb * bs, L.tq, (int64_t)bs, st)) != hipSuccess) return e;
+      if (vb > 0 && (e = add_into(L.dgk + fb * bs, L.tk, (int64_t)bs, st)) != hipSuccess) return e;
+      if (fb > 0 && (e = add_into(L.dvx + vb * bs, L.tv, (int64_t)bs, st)) != hipSuccess) return e;
+    }
+  }
+  // chain rule: softmax backward per token (into the dead inner output and its
+  // gradient: B*H*N rows of 256 floats each), dx, parameter partial sums
+  float* dlq = L.y;
+  float* dlk = L.dy;
+  hipLaunchKernelGGL(dl_wide_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, L.gq, L.dgq, dlq, bs, N, NN,
+                     qoff, rows, K);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(dl_wide_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, L.gk, L.dgk, dlk, bs, N, NN,
+                     (int64_t)0, rows, K);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((dx_wide_kernel<T, D>), dim3((unsigned)((N + kTT - 1) / kTT), (unsigned)BH, 2),
+                     dim3(D < 64 ? 64 : D), 0, st, static_cast<const T*>(L.q), static_cast<const T*>(L.k), dlq, dlk,
+                     L.mu, L.iv, static_cast<T*>(L.dq), static_cast<T*>(L.dk), N, H, K);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((partial_wide_kernel<T, D>), dim3((unsigned)L.nseg, (unsigned)BH, (unsigned)(2 * (D / 32))),
+                     dim3(kWT), 0, st, static_cast<const T*>(L.q), static_cast<const T*>(L.k), dlq, dlk, L.mu, L.part,
+                     N, (int)L.B, H, K, L.seg_len, (int)L.nseg);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int NFP = 2 * D + 1;
+  const int64_t nred = (int64_t)H * K * NFP;
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((nred + 255) / 256)), dim3(256), 0, st, L.part, L.sums, nred, K,
+                     NFP, (int)(2 * L.B * L.nseg));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(params_kernel<kWT>, dim3((unsigned)H), dim3(kWT), 0, st, L.sums, L.iv, L.logit_pi, L.dmu,
+                     L.dlog_var, L.dlogit_pi, K, D);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // dv: the first d columns of the value gradient (block 0)
+  hipLaunchKernelGGL((take_dv_kernel<T, float>), dim3((unsigned)((rows * D + 255) / 256)), dim3(256), 0, st, L.dvx,
+                     static_cast<T*>(L.dv), N, NN, rows, D, 128);
+  return hipGetLastError();
+}
+
 }  // namespace gbwd
 
 hipError_t gma_backward_launch(const GmaBwdLaunch& L, hipStream_t st) {
   using namespace gbwd;
+  if (L.NF > 1 || L.NVB > 1) {
+    if (L.bf16) {
+      if (L.D == 32) return run_wide<bf16, 32>(L, st);
+      if (L.D == 64) return run_wide<bf16, 64>(L, st);
+      if (L.D == 128) return run_wide<bf16, 128>(L, st);
+    } else {
+      if (L.D == 32) return run_wide<float, 32>(L, st);
+      if (L.D == 64) return run_wide<float, 64>(L, st);
+      if (L.D == 128) return run_wide<float, 128>(L, st);
+    }
+    return hipErrorInvalidValue;
+  }
   if (L.bf16) {
     if (L.D == 32) return run<bf16, 32>(L, st);
     if (L.D == 64) return run<bf16, 64>(L, st);

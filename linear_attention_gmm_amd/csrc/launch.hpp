@@ -276,6 +276,14 @@ struct GmaBwdLaunch {
   float* sums;  // the partials summed over the slots [H][K][2 D + 1]
   int64_t B, H, N, D, K, DL, nseg, seg_len;
   int64_t NN;  // inner rows per sequence: N (causal) or 2N (bidirectional)
+  // wide shapes (d = 128 or K > 128): the inner tensors above in blocks of 128
+  // columns, NF blocks of responsibilities, NVB of values, bstride floats apart;
+  // tq, tk, tv: one block each for the sums over the blocks
+  int64_t NF = 1, NVB = 1;
+  size_t bstride = 0;
+  float* tq = nullptr;
+  float* tk = nullptr;
+  float* tv = nullptr;
   int causal;
   float eps;
   bool bf16;

@@ -380,8 +380,11 @@ def test_gma_backward_errors():
     wsb = L.gma_backward_workspace_bytes(2, 2, 300, 64, 128, 64, 1, bf)
     assert wsb > 0
     assert L.gma_backward_workspace_bytes(2, 2, 300, 64, 128, 64, 0, bf) > wsb  # bidirectional: 2N inner rows
-    assert L.gma_backward_workspace_bytes(2, 2, 300, 128, 128, 128, 1, bf) == 0  # d = 128: not implemented
-    assert L.gma_backward_workspace_bytes(2, 2, 300, 64, 129, 64, 1, f32) == 0  # K > 128: not implemented
+    # d = 128 or K > 128: the inner tensors in two blocks of 128 columns
+    assert L.gma_backward_workspace_bytes(2, 2, 300, 128, 256, 128, 1, bf) > wsb
+    assert L.gma_backward_workspace_bytes(2, 2, 300, 64, 129, 64, 1, f32) > 0
+    assert L.gma_backward_workspace_bytes(2, 2, 300, 64, 257, 64, 1, f32) == 0  # K > 256: not implemented
+    assert L.gma_backward_workspace_bytes(2, 2, 300, 96, 64, 96, 1, f32) == 0  # d = 96: not implemented
     assert L.gma_backward_workspace_bytes(2, 2, 300, 32, 16, 32, 1, f32) > 0
 
     def call(**kw):
@@ -397,8 +400,8 @@ def test_gma_backward_errors():
     assert call(dq=None) == binding.LM_EINVAL
     assert call(eps=-1.0) == binding.LM_EINVAL
     assert call(causal=2) == binding.LM_EINVAL
-    assert call(d=128) == binding.LM_EUNSUPPORTED
-    assert call(K=200) == binding.LM_EUNSUPPORTED
+    assert call(d=16) == binding.LM_EUNSUPPORTED
+    assert call(K=300) == binding.LM_EUNSUPPORTED
     assert L.lm_last_error().decode()
 
 

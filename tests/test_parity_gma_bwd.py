@@ -115,3 +115,31 @@ def test_gma_backward_deterministic():
     b = binding.gma_backward(x["q"], x["k"], x["v"], x["mu"], x["log_var"], x["logit_pi"], do)
     for name, u, w in zip(NAMES, a, b):
         assert torch.equal(u, w), name
+
+
+@pytest.mark.parametrize("d,K,N", [(128, 64, 150), (64, 200, 130), (128, 256, 100), (32, 129, 70)])
+def test_gma_backward_wide_fp32(d, K, N):
+    # d = 128 or more than 128 components: the inner linear attention on blocks
+    # of 128 feature / value columns
+    cfg = inputs.GmaConfig("gma_bwd_wide", 708, B=2, H=2, N=N, d=d, K=K, dv=d, dtype="f32")
+    got, ref = _case(cfg)
+    for name, a, r in zip(NAMES, got, ref):
+        assert_close(a, r, "f32", "%s fp32 wide d=%d K=%d N=%d" % (name, d, K, N))
+
+
+def test_gma_backward_wide_bidirectional_fp32():
+    cfg = inputs.GmaConfig("gma_bwd_wide_bidir", 709, B=1, H=2, N=90, d=128, K=256, dv=128, dtype="f32")
+    got, ref = _case(cfg, causal=False)
+    for name, a, r in zip(NAMES, got, ref):
+        assert_close(a, r, "f32", "%s fp32 wide bidirectional" % name)
+
+
+@pytest.mark.parametrize("heads", [2, 16])
+def test_gma_backward_long_context_shape(heads):
+    # the long-context GMA shapes (d = dv = 128, K = 256, keys drawn from a
+    # 256-cluster mixture, bf16) on a short ragged sequence; all 16 heads in
+    # the second case
+    cfg = inputs.CONFIGS["gma_bf16_n128k"].replace(name="gma_bwd_long", cfg_id=710, B=1, H=heads, N=200)
+    got, ref = _case(cfg)
+    for name, a, r in zip(NAMES, got, ref):
+        assert_close(a, r, "bf16", "%s bf16 long-context shapes, %d heads, N=200" % (name, heads))
