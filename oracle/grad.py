@@ -22,27 +22,41 @@ def _t(x) -> torch.Tensor:
     return torch.as_tensor(np.asarray(x, dtype=np.float64))
 
 
-def gla_forward_torch(q, k, v, g) -> torch.Tensor:
-    """o [B,H,N,dv] of the recurrence, token by token (differentiable)."""
+def gla_forward_torch(q, k, v, g, state_in=None, return_state: bool = False):
+    """o [B,H,N,dv] of the recurrence, token by token (differentiable), from the
+    state state_in [B,H,dk,dv] (zero when None); with return_state also the
+    state after the last token."""
     B, H, N, dk = q.shape
     dv = v.shape[-1]
-    S = torch.zeros(B, H, dk, dv, dtype=q.dtype)
+    S = torch.zeros(B, H, dk, dv, dtype=q.dtype) if state_in is None else state_in
     outs = []
     for t in range(N):
         S = g[:, :, t, None, None] * S + k[:, :, t, :, None] * v[:, :, t, None, :]
         outs.append((S * q[:, :, t, :, None]).sum(dim=2))
-    return torch.stack(outs, dim=2)
+    o = torch.stack(outs, dim=2)
+    return (o, S) if return_state else o
 
 
-def gla_backward(q, k, v, g, do):
+def gla_backward(q, k, v, g, do, state_in=None, dstate_out=None):
     """Gradients (dq, dk, dv, dg) of sum(o * do) with o = gla_forward(q, k, v, g).
-    q, k [B,H,N,dk], v and do [B,H,N,dv], g [B,H,N]; returns numpy float64."""
+    q, k [B,H,N,dk], v and do [B,H,N,dv], g [B,H,N]; returns numpy float64.
+    With a carried state: the recurrence starts from state_in [B,H,dk,dv] (zero
+    when None), the loss adds sum(S_out * dstate_out) for the state S_out after
+    the last token, and the gradient of state_in is returned fifth."""
     q, k, v, g, do = map(_t, (q, k, v, g, do))
-    for x in (q, k, v, g):
+    with_state = state_in is not None or dstate_out is not None
+    B, H, _, dk = q.shape
+    dv = v.shape[-1]
+    s0 = _t(state_in) if state_in is not None else torch.zeros(B, H, dk, dv, dtype=torch.float64)
+    for x in (q, k, v, g, s0):
         x.requires_grad_(True)
-    o = gla_forward_torch(q, k, v, g)
-    o.backward(do)
-    return tuple(x.grad.numpy() for x in (q, k, v, g))
+    o, S = gla_forward_torch(q, k, v, g, state_in=s0, return_state=True)
+    loss = (o * do).sum()
+    if dstate_out is not None:
+        loss = loss + (S * _t(dstate_out)).sum()
+    loss.backward()
+    out = tuple(x.grad.numpy() for x in (q, k, v, g))
+    return out + (s0.grad.numpy(),) if with_state else out
 
 
 def gma_forward_torch(q, k, v, mu, log_var, logit_pi, eps, causal=True) -> torch.Tensor:

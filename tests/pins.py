@@ -479,6 +479,48 @@ def pin_gla_backward(orc):
         assert relerr(gx, num) < 1e-7, ("gradient", idx, relerr(gx, num))
 
 
+def pin_gla_backward_state(orc):
+    """Gradients of the decayed linear attention with a carried state: from a
+    state_in, with the loss sum(o * do) + sum(S_out * dS_out), every gradient
+    (q, k, v, the gates and state_in) equals central finite differences of
+    oracle.c's forward with a carried state."""
+    from oracle import grad
+    rng = _rng(605)
+    B, H, N, dk, dv = 1, 2, 5, 3, 2
+    q = rng.standard_normal((B, H, N, dk))
+    k = rng.standard_normal((B, H, N, dk))
+    v = rng.standard_normal((B, H, N, dv))
+    g = rng.uniform(0.3, 1.0, (B, H, N))
+    do = rng.standard_normal((B, H, N, dv))
+    s0 = rng.standard_normal((B, H, dk, dv))
+    dso = rng.standard_normal((B, H, dk, dv))
+    gs = grad.gla_backward(q, k, v, g, do, state_in=s0, dstate_out=dso)
+    assert len(gs) == 5
+
+    def loss(q_, k_, v_, g_, s_):
+        o, so = orc.gla_forward(q_, k_, v_, g_, state_in=s_.reshape(B, H, dk * dv), return_state=True)
+        return float(np.sum(o * do) + np.sum(so.reshape(B, H, dk, dv) * dso))
+
+    h = 1e-6
+    args = [q, k, v, g, s0]
+    for idx, gx in enumerate(gs):
+        x = args[idx]
+        num = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp = x.copy(); xp[pos] += h
+            xm = x.copy(); xm[pos] -= h
+            ap = list(args); ap[idx] = xp
+            am = list(args); am[idx] = xm
+            num[pos] = (loss(*ap) - loss(*am)) / (2 * h)
+        assert relerr(gx, num) < 1e-7, ("gradient", idx, relerr(gx, num))
+    # without the state terms the extra output is the plain state gradient and
+    # the others equal the stateless backward's
+    g0 = grad.gla_backward(q, k, v, g, do)
+    gz = grad.gla_backward(q, k, v, g, do, state_in=np.zeros_like(s0))
+    for a_, b_ in zip(g0, gz[:4]):
+        assert relerr(a_, b_) < 1e-12
+
+
 def pin_gma_backward(orc):
     """Gradients of GMA (causal and bidirectional): the autograd oracle's forward
     equals oracle.c's, and every gradient (q, k, v, mu, log_var, logit_pi)
@@ -741,7 +783,7 @@ ALL_PINS = [
     pin_gma_permutation, pin_gma_prefix, pin_gma_affinity_structure, pin_gma_golden,
     pin_gla_brute, pin_gla_chunkwise, pin_ccq_numpy_cov, pin_cov_is_logpartition_hessian,
     pin_ccq_reductions, pin_ccq_chunkwise, pin_ccq_golden, pin_gma_state, pin_gla_state,
-    pin_ccq_state, pin_glv, pin_gla_backward, pin_gma_backward, pin_ccq_backward,
+    pin_ccq_state, pin_glv, pin_gla_backward, pin_gla_backward_state, pin_gma_backward, pin_ccq_backward,
     pin_deltanet_gradient_step, pin_deltanet_orthogonal_keys, pin_deltanet_exact_recall,
     pin_deltanet_beta_zero, pin_deltanet_chunkwise, pin_deltanet_state, pin_ccq_deltanet_reductions,
 ]
