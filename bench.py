@@ -281,7 +281,7 @@ def main():
         for name, fn in (("gma_bidir_n16k", "bidir"), ("gla_bf16_n8k", "gla"), ("gla_backward_bf16_n8k", "glab"),
                          ("glv_bf16_n8k", "glv"), ("gma_bf16_n128k", "gma5"), ("gma_backward_bf16_n16k", "gmab"),
                          ("ccq_backward_bf16_n16k", "ccqb"), ("deltanet_bf16_n8k", "gdn"),
-                         ("ccq_deltanet_bf16_n16k", "ccqgdn")):
+                         ("ccq_deltanet_bf16_n16k", "ccqgdn"), ("gma_backward_bf16_n128k", "gmab5")):
             if fn == "bidir":
                 a = gset[0]
                 call = lambda: gma_forward(a["q"], a["k"], a["v"], a["mu"], a["log_var"], a["logit_pi"],
@@ -323,6 +323,18 @@ def main():
                 tok = g_tok
                 # read Q, K, V, dO and write dQ, dK, dV (bf16); parameters are negligible
                 byt = tok * 7 * gcfg.d * 2
+            elif fn == "gmab5":
+                from linear_attention_gmm_amd import gma_backward, gma_backward_workspace_bytes
+                cfg = inputs.CONFIGS["gma_bf16_n128k"]
+                y5 = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inputs.gma_inputs(cfg).items()}
+                g5do = torch.randn_like(y5["v"])
+                ws5 = torch.empty(gma_backward_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d, cfg.K, cfg.dv),
+                                  dtype=torch.uint8, device=dev)
+                call = lambda: gma_backward(y5["q"], y5["k"], y5["v"], y5["mu"], y5["log_var"], y5["logit_pi"], g5do,
+                                            eps=cfg.eps, workspace=ws5)
+                tok = cfg.B * cfg.H * cfg.N
+                # read Q, K, V, dO and write dQ, dK, dV (bf16); parameters are negligible
+                byt = tok * 7 * cfg.d * 2
             elif fn == "ccqb":
                 from linear_attention_gmm_amd import ccq_backward, ccq_backward_workspace_bytes
                 b_ = cset[0]

@@ -308,6 +308,28 @@ int linattn_chunk_backward(const void* q, const void* k, const void* v, const fl
                            int64_t segments, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same with a carried state (truncated backpropagation across calls): the
+ * forward ran from state_in [B,H,dk*dv] (float32, S[a][b] at a*dv + b; NULL =
+ * zero) and the loss also depends on the state after the last token through
+ * dstate_out [B,H,dk*dv] (its gradient; NULL = none). Writes dq, dk, dv, dg as
+ * above (dg then also holds the gates' effect on the carried states) and, when
+ * dstate_in is not NULL, the gradient of state_in [B,H,dk*dv] (float32).
+ * Chaining calls backwards (dstate_out of a call = dstate_in of the next)
+ * gives the gradients of the whole sequence.
+ * Source: allinfo.ai.kr post on linear attention, "Key messages" (the state is
+ * all that crosses from one part of the sequence to the next).
+ * Implemented: as linattn_chunk_backward; with a state pointer given, bf16 with
+ * dk = dv = 128 (LM_EUNSUPPORTED otherwise). State buffers 16-byte aligned;
+ * dstate_in must not overlap any other buffer. Same workspace.
+ */
+int linattn_chunk_backward_state(const void* q, const void* k, const void* v, const float* g,
+                                 const void* dout, const float* state_in, const float* dstate_out,
+                                 void* dq, void* dk, void* dv, float* dg, float* dstate_in,
+                                 int64_t B, int64_t H, int64_t N, int64_t dkk, int64_t dvv,
+                                 int64_t chunk, int dtype, int64_t segments, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * Backward pass of the CCQ read: given the output gradient dout [B,H,N,dv] of
  * ccq_forward(q, k, v, g, w_lambda, b_lambda), writes the gradients of
  * sum(out * dout):

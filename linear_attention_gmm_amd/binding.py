@@ -63,6 +63,8 @@ _SIGS = {
     "linattn_vec_decode_step": ([_P] * 6 + [_I64] * 4 + [ctypes.c_int, _P], ctypes.c_int),
     "linattn_backward_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, _I64], ctypes.c_size_t),
     "linattn_chunk_backward": ([_P] * 9 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "linattn_chunk_backward_state": ([_P] * 12 + [_I64] * 6 + [ctypes.c_int, _I64, _P, ctypes.c_size_t, _P],
+                                     ctypes.c_int),
     "gma_backward_workspace_bytes": ([_I64] * 6 + [ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
     "ccq_backward_workspace_bytes": ([_I64] * 6 + [ctypes.c_int], ctypes.c_size_t),
     "ccq_backward": ([_P] * 13 + [_I64] * 6 + [ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
@@ -578,6 +580,31 @@ def linattn_chunk_backward(q, k, v, g, dout, chunk: int = 64, segments: int = 0,
                                       ws.data_ptr() if ws is not None else None, nbytes, _stream(q.device))
     _check("linattn_chunk_backward", st)
     return dq, dkt, dvt, dg
+
+
+def linattn_chunk_backward_state(q, k, v, g, dout, state_in: Optional[torch.Tensor] = None,
+                                 dstate_out: Optional[torch.Tensor] = None, chunk: int = 64, segments: int = 0,
+                                 workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv, dg, dstate_in) of sum(out * dout) + sum(S_out *
+    dstate_out) for (out, S_out) = linattn_chunk_forward_state(q, k, v, g,
+    state_in); states [B,H,dk*dv] float32 (None = zero / no such term)."""
+    dt = _dtype_code(q)
+    (B, H, N, dk, dv), (pq, pk, pv, pg), _, _ = _lin_common(q, k, v, g, torch.empty_like(v))
+    pdo = _dev(dout, "dout", q.dtype, (B, H, N, dv))
+    shape = (B, H, linattn_state_size(dk, dv))
+    psi = _state(state_in, "state_in", shape, q.device)
+    pdso = _state(dstate_out, "dstate_out", shape, q.device)
+    dq, dkt, dvt = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dsi = torch.empty(shape, dtype=torch.float32, device=q.device)
+    nbytes = linattn_backward_workspace_bytes(B, H, N, dk, dv, chunk, q.dtype, segments)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    st = lib().linattn_chunk_backward_state(pq, pk, pv, pg, pdo, psi, pdso, dq.data_ptr(), dkt.data_ptr(),
+                                            dvt.data_ptr(), dg.data_ptr(), dsi.data_ptr(), B, H, N, dk, dv, chunk,
+                                            dt, segments, ws.data_ptr() if ws is not None else None, nbytes,
+                                            _stream(q.device))
+    _check("linattn_chunk_backward_state", st)
+    return dq, dkt, dvt, dg, dsi
 
 
 def gma_backward_workspace_bytes(B, H, N, d, K, dv, causal=True, dtype=torch.bfloat16) -> int:

@@ -1138,15 +1138,20 @@ size_t linattn_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t
          lin_layout(B, H, N, dk, false, segments).total;
 }
 
-int linattn_chunk_backward(const void* q, const void* k, const void* v, const float* g, const void* dout, void* dq,
-                           void* dk, void* dv, float* dg, int64_t B, int64_t H, int64_t N, int64_t dkk, int64_t dvv,
-                           int64_t chunk, int dtype, int64_t segments, void* workspace, size_t workspace_bytes,
-                           void* stream) {
-  const char* fn = "linattn_chunk_backward";
+static int lin_backward(const char* fn, const void* q, const void* k, const void* v, const float* g, const void* dout,
+                        const float* state_in, const float* dstate_out, void* dq, void* dk, void* dv, float* dg,
+                        float* dstate_in, int64_t B, int64_t H, int64_t N, int64_t dkk, int64_t dvv, int64_t chunk,
+                        int dtype, int64_t segments, void* workspace, size_t workspace_bytes, void* stream) {
   int st = lin_check_shape(fn, B, H, N, dkk, dvv, chunk, dtype, segments);
   if (st != LM_OK) return st;
   if (!q || !k || !v || !g || !dout || !dq || !dk || !dv || !dg || !workspace)
     return fail(LM_EINVAL, "%s: null pointer argument", fn);
+  const bool stateful = state_in || dstate_out || dstate_in;
+  if (stateful && !lin_bwd_bf16(dkk, dvv, N, dtype))
+    return fail(LM_EUNSUPPORTED, "%s: a carried state is implemented for bf16 with dk = dv = 128", fn);
+  const size_t ns = (size_t)B * H * dkk * dvv * 4;
+  for (const float* p : {state_in, dstate_out, static_cast<const float*>(dstate_in)})
+    if (p && !aligned(p, 16)) return fail(LM_EINVAL, "%s: misaligned state pointer (16 bytes needed)", fn);
   const void* ptrs16[] = {q, k, v, dout, dq, dk, dv, workspace};
   for (const void* p : ptrs16)
     if (!aligned(p, 16)) return fail(LM_EINVAL, "%s: misaligned pointer (tensors need 16 bytes)", fn);
@@ -1168,6 +1173,21 @@ int linattn_chunk_backward(const void* q, const void* k, const void* v, const fl
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], nout[i], outs[j], nout[j])) return fail(LM_EINVAL, "%s: outputs overlap", fn);
   }
+  // the states: inputs state_in, dstate_out; output dstate_in
+  for (const float* p : {state_in, dstate_out}) {
+    if (!p) continue;
+    for (int i = 0; i < 4; ++i)
+      if (overlap(outs[i], nout[i], p, ns)) return fail(LM_EINVAL, "%s: an output overlaps a state input", fn);
+    if (dstate_in && overlap(dstate_in, ns, p, ns))
+      return fail(LM_EINVAL, "%s: dstate_in overlaps a state input", fn);
+  }
+  if (dstate_in) {
+    for (int i = 0; i < 4; ++i)
+      if (overlap(outs[i], nout[i], dstate_in, ns)) return fail(LM_EINVAL, "%s: outputs overlap", fn);
+    for (int j = 0; j < 6; ++j)
+      if (overlap(dstate_in, ns, ins[j], nin[j]))
+        return fail(LM_EINVAL, "%s: dstate_in overlaps an input or the workspace", fn);
+  }
   if (lin_bwd_bf16(dkk, dvv, N, dtype)) {
     lm::BwdBf16Launch Lb;
     Lb.q = q;
@@ -1180,6 +1200,9 @@ int linattn_chunk_backward(const void* q, const void* k, const void* v, const fl
     Lb.dv = dv;
     Lb.dg = dg;
     Lb.xk = static_cast<float*>(workspace);
+    Lb.state_in = state_in;
+    Lb.dstate_out = dstate_out;
+    Lb.dstate_in = dstate_in;
     Lb.B = B;
     Lb.H = H;
     Lb.N = N;
@@ -1235,6 +1258,23 @@ int linattn_chunk_backward(const void* q, const void* k, const void* v, const fl
   hipError_t e = lm::linattn_backward_launch(La, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+int linattn_chunk_backward(const void* q, const void* k, const void* v, const float* g, const void* dout, void* dq,
+                           void* dk, void* dv, float* dg, int64_t B, int64_t H, int64_t N, int64_t dkk, int64_t dvv,
+                           int64_t chunk, int dtype, int64_t segments, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return lin_backward("linattn_chunk_backward", q, k, v, g, dout, nullptr, nullptr, dq, dk, dv, dg, nullptr, B, H, N,
+                      dkk, dvv, chunk, dtype, segments, workspace, workspace_bytes, stream);
+}
+
+int linattn_chunk_backward_state(const void* q, const void* k, const void* v, const float* g, const void* dout,
+                                 const float* state_in, const float* dstate_out, void* dq, void* dk, void* dv,
+                                 float* dg, float* dstate_in, int64_t B, int64_t H, int64_t N, int64_t dkk,
+                                 int64_t dvv, int64_t chunk, int dtype, int64_t segments, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return lin_backward("linattn_chunk_backward_state", q, k, v, g, dout, state_in, dstate_out, dq, dk, dv, dg,
+                      dstate_in, B, H, N, dkk, dvv, chunk, dtype, segments, workspace, workspace_bytes, stream);
 }
 
 size_t gma_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t K, int64_t dv, int causal,

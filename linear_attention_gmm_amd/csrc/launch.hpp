@@ -196,6 +196,10 @@ struct BwdBf16Launch {
   void* dv;
   float* dg;
   float* xk;  // workspace: B * H * N floats (k . dk per token)
+  // optional carried state, [B*H][128][128] float32 each
+  const float* state_in = nullptr;
+  const float* dstate_out = nullptr;
+  float* dstate_in = nullptr;
   int64_t B, H, N;
 };
 hipError_t linattn_backward_bf16_launch(const BwdBf16Launch& L, hipStream_t st);

@@ -67,7 +67,8 @@ constexpr int oAh = oT + 8 * TB;
 constexpr int oAl = oAh + SB;
 constexpr int oB = oAl + SB;
 constexpr int oX = oB + SB;
-constexpr int kLds = oX + kNW * kC * 4;
+constexpr int oXs = oX + kNW * kC * 4;  // per-wave <dS_out, S_out> partials
+constexpr int kLds = oXs + kNW * 4;
 static_assert(kLds <= 160 * 1024, "LDS budget");
 
 // The ten 16 x 16 tiles (query tile it >= key tile jt) of a chunk's scores.
@@ -87,6 +88,10 @@ struct Args {
   bf16* dv;
   float* xq;  // [BH][N]: q . dq (float32)
   float* xk;  // [BH][N]: k . dk (float32)
+  // optional carried state ([BH][128][128] float32, S[a][b] at a * 128 + b):
+  const float* state_in;    // the state before the first token
+  const float* dstate_out;  // the loss gradient of the state after the last token
+  float* dstate_in;         // output: the gradient of state_in
   int64_t N;
   int BH;
 };
@@ -182,12 +187,15 @@ __device__ __forceinline__ void store4(const f32x4& x, const rsrc_t& rs, int64_t
 }
 
 // Sum of the per-wave partials of the chunk at t0 (nw waves), one lane per
-// token, written to x[t0 + lane] for tokens inside the sequence.
-__device__ __forceinline__ void flush_dots(const char* smem, int nw, float* x, int64_t t0, int64_t N) {
+// token, written to x[t0 + lane] for tokens inside the sequence; `last` is
+// added to the sequence's last token.
+__device__ __forceinline__ void flush_dots(const char* smem, int nw, float* x, int64_t t0, int64_t N,
+                                           float last = 0.f) {
   const int l = lane_id();
   const float* sX = reinterpret_cast<const float*>(smem + oX);
   float s = 0.f;
   for (int u = 0; u < nw; ++u) s += sX[u * kC + l];
+  if (t0 + l == N - 1) s += last;
   if (t0 + l < N) x[t0 + l] = s;
 }
 
@@ -213,8 +221,11 @@ __device__ __forceinline__ void dq_sweep(const Args& a, char* smem, int bh) {
   float gnext = l < N ? G[l] : 1.f;
 
   f32x4 ST[8];  // S^T: tile bt holds rows b = 16 bt + 4g + r, column a = a0 + c16
+  const size_t sbase = (size_t)bh * kD * kD + (size_t)(a0 + c16) * kD;  // row a of this lane's S
 #pragma unroll
-  for (int bt = 0; bt < 8; ++bt) ST[bt] = zero4();
+  for (int bt = 0; bt < 8; ++bt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ST[bt][r] = a.state_in ? a.state_in[sbase + 16 * bt + 4 * g + r] : 0.f;
 
   for (int c = 0; c < nch; ++c) {
     const int set = c & 1;
@@ -312,8 +323,25 @@ __device__ __forceinline__ void dq_sweep(const Args& a, char* smem, int bh) {
       }
     }
   }
+  // with a gradient for the state after the last token, the gates also reach
+  // the loss through S_out: the last token's q . dq - k . dk gains <dS_out, S_out>
+  if (a.dstate_out) {
+    float p = 0.f;
+#pragma unroll
+    for (int bt = 0; bt < 8; ++bt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p += ST[bt][r] * a.dstate_out[sbase + 16 * bt + 4 * g + r];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+    if (l == 0) reinterpret_cast<float*>(smem + oXs)[w] = p;
+  }
   lds_barrier();
-  if (nch > 0 && w == kNW - 1) flush_dots(smem, kNW, xq, (int64_t)(nch - 1) * kC, N);
+  if (nch > 0 && w == kNW - 1) {
+    float last = 0.f;
+    if (a.dstate_out)
+      for (int u = 0; u < kNW; ++u) last += reinterpret_cast<const float*>(smem + oXs)[u];
+    flush_dots(smem, kNW, xq, (int64_t)(nch - 1) * kC, N, last);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -344,10 +372,17 @@ __device__ __forceinline__ void dkv_sweep(const Args& a, char* smem, int bh) {
   // dk waves: U^T, U[f][bt] rows b = 16 bt + 4g + r, column a = f0 + 16 f + c16.
   // dv waves: U, U[f][at] rows a = 16 at + 4g + r, column b = f0 + 16 f + c16.
   f32x4 U[2][8];
+  // U starts as the gradient of the state after the last token (zero without one)
+  const float* du = a.dstate_out ? a.dstate_out + (size_t)bh * kD * kD : nullptr;
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) U[f][t] = zero4();
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int x = f0 + 16 * f + c16, y = 16 * t + 4 * g + r;  // column, row of the tile
+        U[f][t][r] = du ? (kside ? du[(size_t)x * kD + y] : du[(size_t)y * kD + x]) : 0.f;
+      }
 
   for (int c = nch - 1; c >= 0; --c) {
     const int set = (nch - 1 - c) & 1;
@@ -516,6 +551,17 @@ __device__ __forceinline__ void dkv_sweep(const Args& a, char* smem, int bh) {
       }
     }
   }
+  // the gradient of the state before the first token is U after chunk 0 (the
+  // dk waves hold it to float32 accuracy, as U^T: row b, column a)
+  if (a.dstate_in && kside) {
+    float* ds = a.dstate_in + (size_t)bh * kD * kD;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ds[(size_t)(f0 + 16 * f + c16) * kD + 16 * t + 4 * g + r] = U[f][t][r];
+  }
   lds_barrier();
   if (nch > 0 && w == kNW - 1) flush_dots(smem, 4, xk, 0, N);
 }
@@ -563,6 +609,9 @@ hipError_t linattn_backward_bf16_launch(const BwdBf16Launch& L, hipStream_t st) 
   a.dv = static_cast<bf16*>(L.dv);
   a.xq = L.dg;  // q . dq lands in dg, which the suffix pass then overwrites
   a.xk = L.xk;
+  a.state_in = L.state_in;
+  a.dstate_out = L.dstate_out;
+  a.dstate_in = L.dstate_in;
   a.N = L.N;
   a.BH = (int)(L.B * L.H);
   hipLaunchKernelGGL(lbw::bwd_kernel, dim3((unsigned)(2 * a.BH)), dim3(lbw::kNT), 0, st, a);

@@ -471,3 +471,25 @@ def test_chunk32_not_elsewhere(fn):
     L = binding.lib()
     assert getattr(L, fn)(2, 3, 500, 64, 64, 64, binding.LM_F32, 0) > 0
     assert getattr(L, fn)(2, 3, 500, 64, 64, 32, binding.LM_F32, 0) == 0
+
+
+@needs_lib
+def test_backward_state_errors():
+    L = binding.lib()
+    (q, k, v, g, do, si, dso, dq, dk, dv, dg, dsi, ws) = (FAKE + (i << 30) for i in range(13))
+    bf, f32 = binding.LM_BF16, binding.LM_F32
+
+    def call(**kw):
+        a = dict(si=si, dso=dso, dq=dq, dsi=dsi, d=128, dt=bf, ws=ws, wsb=1 << 30)
+        a.update(kw)
+        return L.linattn_chunk_backward_state(q, k, v, g, do, a["si"], a["dso"], a["dq"], dk, dv, dg, a["dsi"], 2, 2,
+                                              300, a["d"], a["d"], 64, a["dt"], 0, a["ws"], a["wsb"], None)
+
+    assert call(d=64) == binding.LM_EUNSUPPORTED  # a carried state: bf16, d = 128 only
+    assert call(dt=f32) == binding.LM_EUNSUPPORTED
+    assert call(si=si + 4) == binding.LM_EINVAL  # misaligned
+    assert call(dsi=dq + 64) == binding.LM_EINVAL  # dstate_in overlaps dq
+    assert call(dsi=si) == binding.LM_EINVAL  # dstate_in overlaps state_in
+    assert call(dq=dso) == binding.LM_EINVAL  # an output overlaps a state input
+    assert call(wsb=8) == binding.LM_EWORKSPACE
+    assert L.lm_last_error().decode()

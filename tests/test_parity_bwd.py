@@ -112,3 +112,56 @@ def test_gla_backward_bf16_deterministic():
     b = binding.linattn_chunk_backward(x["q"], x["k"], x["v"], x["g"], do)
     for s, t in zip(a, b):
         assert torch.equal(s, t)
+
+
+def _state_case(cfg, x, do, st_in, dst_out):
+    d = cuda(x)
+    got = binding.linattn_chunk_backward_state(d["q"], d["k"], d["v"], d["g"], do.cuda(),
+                                               state_in=None if st_in is None else st_in.cuda(),
+                                               dstate_out=None if dst_out is None else dst_out.cuda())
+    B, H, D = cfg.B, cfg.H, cfg.dk
+    r4 = lambda t: None if t is None else t.reshape(B, H, D, D).double().numpy()
+    ref = grad.gla_backward(x["q"], x["k"], x["v"], x["g"], do, state_in=r4(st_in), dstate_out=r4(dst_out))
+    return [host(t) for t in got], ref
+
+
+@pytest.mark.parametrize("with_in,with_out", [(True, True), (True, False), (False, True)])
+def test_gla_backward_state_bf16(with_in, with_out):
+    # a carried state into the call and a gradient for the state after it;
+    # gates near 1 (g ~ sigmoid(N(6, 1))) so that both states reach every token
+    cfg = inputs.LinAttnConfig("gla_bwd_state", 507, B=2, H=2, N=200, dk=128, dv=128, dtype="bf16",
+                               g_logit_mean=6.0)
+    x = inputs.linattn_inputs(cfg)
+    rng = np.random.default_rng([cfg.cfg_id, 97])
+    do = torch.from_numpy(rng.standard_normal(x["v"].shape)).to(torch.bfloat16)
+    shape = (cfg.B, cfg.H, cfg.dk * cfg.dv)
+    st_in = torch.from_numpy(rng.standard_normal(shape) * 0.3).float() if with_in else None
+    dst_out = torch.from_numpy(rng.standard_normal(shape) * 0.3).float() if with_out else None
+    say("gla backward with state: in=%d out=%d" % (with_in, with_out))
+    got, ref = _state_case(cfg, x, do, st_in, dst_out)
+    for name, a, r in zip(("dq", "dk", "dv", "dg"), got[:4], ref[:4]):
+        assert_close(a, r, "bf16", "%s bf16 with state (in=%d out=%d)" % (name, with_in, with_out))
+    assert_close(got[4].reshape(ref[4].shape), ref[4], "f32" if not with_in and not with_out else "bf16",
+                 "dstate_in (in=%d out=%d)" % (with_in, with_out))
+
+
+def test_gla_backward_state_chaining():
+    # the gradients of a 300-token sequence from two calls: the second half
+    # from the state after the first (the forward's carried state), its
+    # dstate_in as the first half's dstate_out; against the oracle on the
+    # whole sequence
+    cfg = inputs.LinAttnConfig("gla_bwd_chain", 508, B=2, H=2, N=300, dk=128, dv=128, dtype="bf16")
+    x = inputs.linattn_inputs(cfg)
+    do = torch.from_numpy(np.random.default_rng([cfg.cfg_id, 96]).standard_normal(x["v"].shape)).to(torch.bfloat16)
+    d = cuda(x)
+    n1 = 130
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    _, s1 = binding.linattn_chunk_forward_state(*[sl(d[n], 0, n1) for n in "qkvg"])
+    g2 = binding.linattn_chunk_backward_state(*[sl(d[n], n1, cfg.N) for n in "qkvg"], sl(do.cuda(), n1, cfg.N),
+                                              state_in=s1)
+    g1 = binding.linattn_chunk_backward_state(*[sl(d[n], 0, n1) for n in "qkvg"], sl(do.cuda(), 0, n1),
+                                              dstate_out=g2[4])
+    ref = grad.gla_backward(x["q"], x["k"], x["v"], x["g"], do)
+    for i, name in enumerate(("dq", "dk", "dv", "dg")):
+        got = np.concatenate([host(g1[i]), host(g2[i])], axis=2)
+        assert_close(got, ref[i], "bf16", "%s of the whole sequence from two chained calls" % name)
