@@ -251,6 +251,8 @@ __device__ __forceinline__ void dq_sweep(const Args& a, char* smem, int bh) {
     score_tile(w, tv, to, dc, smem + oAh, smem + oAl);
     if (w < 2) score_tile(w + 8, tv, to, dc, smem + oAh, smem + oAl);
 
+    lds_barrier();
+
     // inter-chunk part: dq[a][i] = 2^(l_i) sum_b S[a][b] do_i[b]
     f32x4 acc[4];
 #pragma unroll
@@ -276,7 +278,6 @@ __device__ __forceinline__ void dq_sweep(const Args& a, char* smem, int bh) {
     bf16x8 kf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) kf[ks] = tl_kmaj<CPR>(tk, ks, a0);
-    lds_barrier();
 
     // intra-chunk part: dq[a][i] += sum_{j<=i} k_j[a] A_ij
 #pragma unroll
@@ -411,6 +412,8 @@ __device__ __forceinline__ void dkv_sweep(const Args& a, char* smem, int bh) {
       else score_tile(p, tk, tq, dc, smem + oB, nullptr);
     }
 
+    lds_barrier();
+
     // inter-chunk part, scaled by 2^(L - l_j) per key token j (the lane's column):
     //   dk[a][j] = sum_b U[a][b] v_j[b]   (split U)
     //   dv[b][j] = sum_a U[a][b] k_j[a]   (U hi)
@@ -463,7 +466,6 @@ __device__ __forceinline__ void dkv_sweep(const Args& a, char* smem, int bh) {
     for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) xf[f][ks] = tl_kmaj<CPR>(kside ? tq : to, ks, f0 + 16 * f);
-    lds_barrier();
 
     // intra-chunk part: dk[a][j] += sum_{i>=j} q_i[a] A_ij ; dv[b][j] += sum_{i>=j} do_i[b] B_ij
 #pragma unroll
