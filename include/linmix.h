@@ -128,7 +128,7 @@
 extern "C" {
 #endif
 
-#define LM_ABI_VERSION 5
+#define LM_ABI_VERSION 6
 
 typedef enum {
   LM_OK = 0,

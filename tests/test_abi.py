@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_version_and_status_strings():
     L = binding.lib()
-    assert L.lm_abi_version() == 5
+    assert L.lm_abi_version() == 6
     for code, name in enumerate(["LM_OK", "LM_EINVAL", "LM_EUNSUPPORTED", "LM_EWORKSPACE", "LM_EHIP"]):
         assert L.lm_status_string(code).decode() == name
     assert L.lm_status_string(99).decode() == "LM_UNKNOWN"
