@@ -290,11 +290,11 @@ int linattn_vec_decode_step(const void* q, const void* k, const void* v, const f
  * the gradients of sum(out * dout): dq_t = S_t dout_t; dk, dv from the state
  * gradient U_t = q_t dout_t^T + g_{t+1} U_{t+1}; and
  * dg_t = (1/g_t) sum_{m >= t} (q_m . dq_m - k_m . dk_m).
- * bf16 with dk = dv = 128: one launch of a forward sweep (dq) and a reverse
- * sweep (dk, dv) per (b, h), with dq and dk accurate to about 16 bits (split
- * bf16 operands), then the suffix sums; segments is not used. Other shapes:
- * three chunkwise passes of the forward kernel in float32 (dk, dv on the
- * time-reversed sequence).
+ * bf16 with dk = dv = 128 and B*H >= 32: one launch of a forward sweep (dq)
+ * and a reverse sweep (dk, dv) per (b, h), with dq and dk accurate to about 16
+ * bits (split bf16 operands), then the suffix sums; segments is not used.
+ * Other shapes: three chunkwise passes of the forward kernel in float32 (dk,
+ * dv on the time-reversed sequence), over segments of each sequence.
  * Source: allinfo.ai.kr post on linear attention, "Key messages" (matrix state
  * with decay gates; the chunkwise form is what makes training parallel).
  * Outputs must not overlap each other, the inputs or the workspace (of at least

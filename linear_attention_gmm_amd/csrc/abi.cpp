@@ -1125,12 +1125,20 @@ int linattn_vec_decode_step(const void* q, const void* k, const void* v, const f
 static bool lin_bwd_bf16(int64_t dk, int64_t dv, int64_t N, int dtype) {
   return dtype == LM_BF16 && dk == 128 && dv == 128 && (N + 64) * 128 * 2 < ((int64_t)1 << 31);
 }
+// It runs one sweep per (b, h) and direction with no segments (2 B H
+// workgroups, one per CU), so below about 32 sequences the chunk passes, which
+// cut each sequence into segments, are faster; a carried state takes it always.
+constexpr int64_t kBwdFusedMinBH = 32;
+static bool lin_bwd_fused(int64_t B, int64_t H, int64_t dk, int64_t dv, int64_t N, int dtype, bool stateful) {
+  return lin_bwd_bf16(dk, dv, N, dtype) && (stateful || B * H >= kBwdFusedMinBH);
+}
 
 size_t linattn_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
                                         int dtype, int64_t segments) {
   if (lin_check_shape("linattn_chunk_backward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
-  // bf16 with d = 128: k . dk per token only
-  if (lin_bwd_bf16(dk, dv, N, dtype)) return align_up((size_t)B * H * N * 4);
+  // the dedicated kernel: k . dk per token only (with fewer sequences the
+  // chunk passes' workspace, which also serves a call with a carried state)
+  if (lin_bwd_fused(B, H, dk, dv, N, dtype, false)) return align_up((size_t)B * H * N * 4);
   // float32 tensors: 5 for the reversed passes, and for bf16 inputs 7 more
   // (float32 copies of q, k, v, do and the gradients before rounding)
   const size_t t = align_up((size_t)B * H * N * dk * 4);
@@ -1188,7 +1196,7 @@ static int lin_backward(const char* fn, const void* q, const void* k, const void
       if (overlap(dstate_in, ns, ins[j], nin[j]))
         return fail(LM_EINVAL, "%s: dstate_in overlaps an input or the workspace", fn);
   }
-  if (lin_bwd_bf16(dkk, dvv, N, dtype)) {
+  if (lin_bwd_fused(B, H, dkk, dvv, N, dtype, stateful)) {
     lm::BwdBf16Launch Lb;
     Lb.q = q;
     Lb.k = k;

@@ -71,12 +71,17 @@ def test_gla_backward_full_size_sampled():
         assert_close(a, r, "bf16", "%s bf16 8K workload, slice (5,9)" % name)
 
 
+# the dedicated bf16 d = 128 kernel runs from 32 sequences on (B=2, H=16 here);
+# its cases are checked on four of the 32 slices, the last one included
+SL32 = [(0, 0), (0, 9), (1, 4), (1, 15)]
+
+
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 200])
 def test_gla_backward_bf16_d128_ragged(N):
     # bf16 with d = 128 (its own kernel): inside one chunk, whole chunks and a
     # ragged last chunk
-    cfg = inputs.LinAttnConfig("gla_bwd128", 504, B=1, H=2, N=N, dk=128, dv=128, dtype="bf16")
-    got, ref = _case(cfg)
+    cfg = inputs.LinAttnConfig("gla_bwd128", 504, B=2, H=16, N=N, dk=128, dv=128, dtype="bf16")
+    got, ref = _case(cfg, sl=SL32)
     for name, a, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
         assert_close(a, r, "bf16", "%s bf16 d=128 N=%d" % (name, N))
     # the first token's gate gradient is rounding of q.dq - k.dk (see above)
@@ -89,9 +94,9 @@ def test_gla_backward_bf16_d128_ragged(N):
 @pytest.mark.parametrize("g_logit_mean", [0.0, -1.0])
 def test_gla_backward_bf16_d128_strong_decay(g_logit_mean):
     # gates around 0.5 and 0.27 per token: states forget within a few tokens
-    cfg = inputs.LinAttnConfig("gla_bwd128", 505, B=2, H=2, N=300, dk=128, dv=128, dtype="bf16",
+    cfg = inputs.LinAttnConfig("gla_bwd128", 505, B=2, H=16, N=300, dk=128, dv=128, dtype="bf16",
                                g_logit_mean=g_logit_mean)
-    got, ref = _case(cfg)
+    got, ref = _case(cfg, sl=SL32)
     for name, a, r in zip(("dq", "dk", "dv", "dg"), got, ref):
         assert_close(a, r, "bf16", "%s bf16 d=128 g logit mean %g" % (name, g_logit_mean))
 
@@ -105,7 +110,7 @@ def test_gla_backward_full_size_last_slice():
 
 
 def test_gla_backward_bf16_deterministic():
-    cfg = inputs.LinAttnConfig("gla_bwd128", 506, B=2, H=3, N=777, dk=128, dv=128, dtype="bf16")
+    cfg = inputs.LinAttnConfig("gla_bwd128", 506, B=2, H=16, N=777, dk=128, dv=128, dtype="bf16")
     x = cuda(inputs.linattn_inputs(cfg))
     do = torch.randn(x["v"].shape, generator=torch.Generator().manual_seed(7)).to(torch.bfloat16).cuda()
     a = binding.linattn_chunk_backward(x["q"], x["k"], x["v"], x["g"], do)
@@ -165,3 +170,12 @@ def test_gla_backward_state_chaining():
     for i, name in enumerate(("dq", "dk", "dv", "dg")):
         got = np.concatenate([host(g1[i]), host(g2[i])], axis=2)
         assert_close(got, ref[i], "bf16", "%s of the whole sequence from two chained calls" % name)
+
+
+def test_gla_backward_bf16_d128_few_sequences():
+    # fewer than 32 sequences: the chunk passes over segments (the dedicated
+    # kernel would leave most CUs idle); the same gradients
+    cfg = inputs.LinAttnConfig("gla_bwd128_few", 509, B=1, H=4, N=700, dk=128, dv=128, dtype="bf16")
+    got, ref = _case(cfg, segments=4)
+    for name, a, r in zip(("dq", "dk", "dv", "dg"), got, ref):
+        assert_close(a, r, "bf16", "%s bf16 d=128, 4 sequences" % name)
