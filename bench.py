@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed steps before the warm-up steps (the GPU's clocks rise over the first "
+                         "tens of ms of sustained work; 0 times that rise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", action="store_true",
                     help="also time bidirectional GMA, GLA (forward and backward), per-feature decay and long GMA")
@@ -208,15 +211,26 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
+    # The GPU's clocks rise over the first tens of milliseconds of sustained
+    # work. Untimed steps for args.settle seconds first, so that the warm-up
+    # and the timed steps run at the steady clock (with 5 warm-up steps and no
+    # settle the timed steps caught the rise: about 0.66 against 0.59 ms per step).
+    n_settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(8):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
-        step(i)
+        step(n_settle + i)
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(n_settle + args.warmup + i, evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
@@ -263,6 +277,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle,
         "ms_per_step": wall * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
