@@ -343,7 +343,10 @@ int linattn_chunk_backward_state(const void* q, const void* k, const void* v, co
  * to dk_j (m_t the running key sum); dw, db sum -(u . Sigma q) lambda
  * (1 - lambda) q and its scalar over the batch and the tokens. Computed in
  * float32 with the chunk kernel (decayed and undecayed passes, some on the
- * time-reversed sequence); bf16 gradients are rounded once.
+ * time-reversed sequence); bf16 gradients are rounded once. For bf16 at
+ * dk = dv = 128 with B*H >= 32 the decayed read's gradients (u, dv, dg, the
+ * direct part of dk) come from the kernel of linattn_chunk_backward instead,
+ * with q_clean rounded once to bf16 as the forward's read takes it.
  * Source: "Don't Read Everything: A Curvature-Conditioned Query for Linear
  * Attention", section 2 Method (derivation, mechanism, integration).
  * Shapes as for ccq_forward (chunk 64, dk == dv in {32, 64, 128}); no carried

@@ -1498,6 +1498,7 @@ int ccq_backward(const void* q, const void* k, const void* v, const float* g, co
   La.clen = L.clen;
   La.nblk = L.nblk;
   La.blen = L.blen;
+  La.fused = lin_bwd_fused(B, H, dkk, dvv, N, dtype, false);
   La.bf16 = dtype == LM_BF16;
   hipError_t e = lm::ccq_backward_launch(La, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LM_EHIP, "%s: %s", fn, hipGetErrorString(e));

@@ -21,7 +21,10 @@
 // gradients are rounded once, except for bf16 inputs: there the undecayed
 // passes and the dv pass run on the bf16 chunk kernel (their results enter the
 // gradients as perturbations of the size of the bf16 rounding; the gradients
-// of the decayed read, whose gate gradient cancels, stay in float32).
+// of the decayed read, whose gate gradient cancels, stay in float32). At
+// D = 128 with enough sequences the decayed read's backward is the fused bf16
+// kernel of linattn_bwd_bf16.hip (dq and dk carried to about 16 bits there,
+// the gate gradient formed inside it), fed q_clean rounded once to bf16.
 #include "mfma.hpp"
 #include "launch.hpp"
 #include "bwd.hpp"
@@ -317,7 +320,39 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // backward of the decayed linear attention read with q_clean: u = dq_clean,
   // the direct part of dk, dv and dg
-  if constexpr (sizeof(T) == 2) {
+  T* mu16 = reinterpret_cast<T*>(L.mu);
+  T* u16 = sizeof(T) == 2 ? mu16 + n : nullptr;  // bf16: second half of the M u slot
+  bool fused = false;
+  if constexpr (sizeof(T) == 2 && D == 128) fused = L.fused;
+  if (fused) {
+    // the fused bf16 kernel, with q_clean rounded once to bf16 (as the
+    // forward's read takes it); dq lands in the bf16 u operand of the M u
+    // pass, dk in the slot of a later reversed sum, k . dk per token in dm
+    bf16* qc16 = reinterpret_cast<bf16*>(L.dvg);
+    bf16* dk16 = reinterpret_cast<bf16*>(L.r1);
+    hipLaunchKernelGGL((cvt_kernel<float, bf16>), dim3(nblocks(n / 4)), dim3(256), 0, st, L.qc, qc16, n);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    BwdBf16Launch F{};
+    F.q = qc16;
+    F.k = L.k;
+    F.v = L.v;
+    F.g = L.bwd.g;
+    F.dout = L.dout;
+    F.dq = u16;
+    F.dk = dk16;
+    F.dv = L.dv;
+    F.dg = L.bwd.dg;
+    F.xk = L.dm;
+    F.B = L.B;
+    F.H = L.H;
+    F.N = L.N;
+    if ((e = linattn_backward_bf16_launch(F, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL((cvt_kernel<bf16, float>), dim3(nblocks(n / 4)), dim3(256), 0, st,
+                       reinterpret_cast<const bf16*>(u16), L.u, n);
+    hipLaunchKernelGGL((cvt_kernel<bf16, float>), dim3(nblocks(n / 4)), dim3(256), 0, st,
+                       reinterpret_cast<const bf16*>(dk16), L.dkg, n);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else if constexpr (sizeof(T) == 2) {
     // dv (which dg does not use) on bf16 operands: reversed k, q_clean and
     // dout in the slots of the float32 dv and of the inner reversed k
     bf16* a16 = reinterpret_cast<bf16*>(L.dvg);
@@ -334,14 +369,14 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
       return e;
   }
   // Sigma u needs M u; then dq, the values of the reversed passes, dm, dw/db
-  T* mu16 = reinterpret_cast<T*>(L.mu);
   T* vr1 = reinterpret_cast<T*>(L.vr1);
   T* vr2 = reinterpret_cast<T*>(L.vr2);
   T* ru16 = sizeof(T) == 2 ? reinterpret_cast<T*>(L.vr1) + n : nullptr;  // bf16: second half of the vr1 slot
   if constexpr (sizeof(T) == 2) {
-    T* u16 = mu16 + n;  // second half of the M u slot
-    hipLaunchKernelGGL((cvt_kernel<float, T>), dim3(nblocks(n / 4)), dim3(256), 0, st, L.u, u16, n);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!fused) {
+      hipLaunchKernelGGL((cvt_kernel<float, T>), dim3(nblocks(n / 4)), dim3(256), 0, st, L.u, u16, n);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if ((e = la<T>(L, u16, static_cast<const T*>(L.k), static_cast<const T*>(L.k), mu16, st)) != hipSuccess)
       return e;
   } else {

@@ -238,6 +238,9 @@ struct CcqBwdLaunch {
   float *lam, *ones, *csum, *part;
   int64_t B, H, N, D, nch, clen, nblk, blen;
   bool bf16;
+  // bf16 at D = 128: the decayed read's gradients on the fused bf16 backward
+  // kernel (linattn_bwd_bf16.hip) instead of the float32 chunk passes
+  bool fused = false;
 };
 hipError_t ccq_backward_launch(const CcqBwdLaunch& L, hipStream_t st);
 

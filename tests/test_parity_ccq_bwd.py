@@ -100,6 +100,15 @@ def test_ccq_backward_workload_shape_sampled():
     _check(got, ref, "bf16", "bf16 CCQ workload shape N=2048, head 9")
 
 
+def test_ccq_backward_lowrank_many_heads():
+    # low-rank keys with gate bias +2 (a large covariance correction) at
+    # B*H = 32, a ragged length, dk = dv = 128 in bf16: the decayed read's
+    # gradients come from the fused bf16 backward kernel; two heads checked
+    cfg = inputs.CONFIGS["ccq_bf16_lowrank"].replace(name="ccq_bwd_lowrank_fused", cfg_id=806, B=2, H=16, N=1000)
+    got, ref = _case(cfg, heads=[3, 12])
+    _check(got, ref, "bf16", "bf16 low-rank keys B2 H16 N=1000, heads 3 and 12")
+
+
 def test_ccq_backward_deterministic():
     # fixed-order reductions: two calls give bit-identical gradients
     cfg = inputs.CONFIGS["ccq_bf16_lowrank"].replace(name="ccq_bwd_det", cfg_id=805, B=2, H=2, N=777)
