@@ -285,9 +285,13 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
     hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.q), L.fq, n);
     hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.k), L.fk, n);
-    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.v), L.fv, n);
-    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.dout),
-                       L.fdo, n);
+    if (!(D == 128 && L.fused)) {
+      // v and dout in float32 serve only the chunk passes of the decayed read
+      hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.v),
+                         L.fv, n);
+      hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st,
+                         static_cast<const T*>(L.dout), L.fdo, n);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     fq = L.fq;
     fk = L.fk;
