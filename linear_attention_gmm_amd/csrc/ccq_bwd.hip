@@ -32,44 +32,74 @@
 namespace lm {
 namespace cbwd {
 
+// Four consecutive features of a row as float32.
+template <typename TI>
+__device__ __forceinline__ f32x4 ld4(const TI* p) {
+  if constexpr (sizeof(TI) == 2) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  } else {
+    return *reinterpret_cast<const f32x4*>(p);
+  }
+}
+
 // Per (b, h, token range) feature sums: csum[bh][c][f] = sum_{t in range c} x[t][f].
-__global__ __launch_bounds__(128) void chunk_sum_kernel(const float* __restrict__ x, float* __restrict__ csum,
+// 256 threads: D / 4 quads of features times 256 / (D / 4) row groups (rows
+// t0 + group, t0 + group + groups, ...), then the groups' sums in a fixed order.
+template <typename TI>
+__global__ __launch_bounds__(256) void chunk_sum_kernel(const TI* __restrict__ x, float* __restrict__ csum,
                                                         int64_t N, int D, int64_t clen, int nch) {
-  const int c = blockIdx.x, bh = blockIdx.y, f = threadIdx.x;
-  if (f >= D) return;
+  __shared__ f32x4 red[256];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int nq = D / 4, ng = 256 / nq, fq = threadIdx.x % nq, rg = threadIdx.x / nq;
   const int64_t t0 = (int64_t)c * clen, t1 = N < t0 + clen ? N : t0 + clen;
-  const float* p = x + (size_t)bh * N * D + f;
-  float s = 0.f;
-  for (int64_t t = t0; t < t1; ++t) s += p[(size_t)t * D];
-  csum[((size_t)bh * nch + c) * D + f] = s;
+  const TI* p = x + (size_t)bh * N * D + 4 * fq;
+  f32x4 s = zero4();
+  for (int64_t t = t0 + rg; t < t1; t += ng) s += ld4(p + (size_t)t * D);
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (rg == 0) {
+    for (int r = 1; r < ng; ++r) s += red[r * nq + fq];
+    *reinterpret_cast<f32x4*>(csum + ((size_t)bh * nch + c) * D + 4 * fq) = s;
+  }
 }
 
 // Inclusive prefix (rev = 0) or suffix (rev = 1) sums over tokens of x, per
-// feature: the ranges before (after) this one from csum, then a running sum.
-__global__ __launch_bounds__(128) void scan_apply_kernel(const float* __restrict__ x, const float* __restrict__ csum,
-                                                         float* __restrict__ y, int64_t N, int D, int64_t clen,
-                                                         int nch, int rev) {
-  const int c = blockIdx.x, bh = blockIdx.y, f = threadIdx.x;
-  if (f >= D) return;
-  float off = 0.f;
-  const float* cs = csum + (size_t)bh * nch * D + f;
+// feature: the ranges before (after) this one from csum, then a running sum
+// over the range, eight rows of loads ahead. 64 threads: 64 / (D / 4) ranges
+// of D / 4 feature quads each.
+template <typename TI>
+__global__ __launch_bounds__(64) void scan_apply_kernel(const TI* __restrict__ x, const float* __restrict__ csum,
+                                                        float* __restrict__ y, int64_t N, int D, int64_t clen,
+                                                        int nch, int rev) {
+  const int nq = D / 4, fq = threadIdx.x % nq;
+  const int c = blockIdx.x * (64 / nq) + threadIdx.x / nq, bh = blockIdx.y;
+  if (c >= nch) return;
+  f32x4 off = zero4();
+  const float* cs = csum + (size_t)bh * nch * D + 4 * fq;
   if (!rev) {
-    for (int cc = 0; cc < c; ++cc) off += cs[(size_t)cc * D];
+    for (int cc = 0; cc < c; ++cc) off += *reinterpret_cast<const f32x4*>(cs + (size_t)cc * D);
   } else {
-    for (int cc = nch - 1; cc > c; --cc) off += cs[(size_t)cc * D];
+    for (int cc = nch - 1; cc > c; --cc) off += *reinterpret_cast<const f32x4*>(cs + (size_t)cc * D);
   }
   const int64_t t0 = (int64_t)c * clen, t1 = N < t0 + clen ? N : t0 + clen;
-  const float* p = x + (size_t)bh * N * D + f;
-  float* o = y + (size_t)bh * N * D + f;
-  if (!rev) {
-    for (int64_t t = t0; t < t1; ++t) {
-      off += p[(size_t)t * D];
-      o[(size_t)t * D] = off;
+  const TI* p = x + (size_t)bh * N * D + 4 * fq;
+  float* o = y + (size_t)bh * N * D + 4 * fq;
+  constexpr int U = 8;
+  for (int64_t i = 0; i < t1 - t0; i += U) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = rev ? t1 - 1 - (i + u) : t0 + i + u;
+      v[u] = i + u < t1 - t0 ? ld4(p + (size_t)t * D) : zero4();
     }
-  } else {
-    for (int64_t t = t1 - 1; t >= t0; --t) {
-      off += p[(size_t)t * D];
-      o[(size_t)t * D] = off;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i + u < t1 - t0) {
+        const int64_t t = rev ? t1 - 1 - (i + u) : t0 + i + u;
+        off += v[u];
+        *reinterpret_cast<f32x4*>(o + (size_t)t * D) = off;
+      }
     }
   }
 }
@@ -267,12 +297,15 @@ static hipError_t la(const CcqBwdLaunch& L, const T* q, const T* k, const T* v, 
   return linattn_launch(F, st);
 }
 
-static hipError_t scan(const CcqBwdLaunch& L, const float* x, float* y, int rev, hipStream_t st) {
-  const dim3 grid((unsigned)L.nch, (unsigned)(L.B * L.H));
-  hipLaunchKernelGGL(chunk_sum_kernel, grid, dim3(128), 0, st, x, L.csum, L.N, (int)L.D, L.clen, (int)L.nch);
+template <typename TI>
+static hipError_t scan(const CcqBwdLaunch& L, const TI* x, float* y, int rev, hipStream_t st) {
+  const unsigned BH = (unsigned)(L.B * L.H), per = (unsigned)(64 / (L.D / 4));
+  hipLaunchKernelGGL((chunk_sum_kernel<TI>), dim3((unsigned)L.nch, BH), dim3(256), 0, st, x, L.csum, L.N, (int)L.D,
+                     L.clen, (int)L.nch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_apply_kernel, grid, dim3(128), 0, st, x, L.csum, y, L.N, (int)L.D, L.clen, (int)L.nch, rev);
+  hipLaunchKernelGGL((scan_apply_kernel<TI>), dim3(((unsigned)L.nch + per - 1) / per, BH), dim3(64), 0, st, x, L.csum,
+                     y, L.N, (int)L.D, L.clen, (int)L.nch, rev);
   return hipGetLastError();
 }
 
@@ -284,9 +317,10 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   const float *fq, *fk, *fv, *fdo;
   if constexpr (sizeof(T) == 2) {
     hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.q), L.fq, n);
-    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.k), L.fk, n);
     if (!(D == 128 && L.fused)) {
-      // v and dout in float32 serve only the chunk passes of the decayed read
+      // k, v and dout in float32 serve only the chunk passes of the decayed read
+      hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.k),
+                         L.fk, n);
       hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.v),
                          L.fv, n);
       hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st,
@@ -310,7 +344,7 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   // run on the bf16 chunk kernel: their results enter q_clean, dq and dk as
   // perturbations of the size of the bf16 rounding, while the gradients of the
   // decayed read (with the gate gradient's cancellation) stay in float32.
-  if ((e = scan(L, fk, L.m, 0, st)) != hipSuccess) return e;
+  if ((e = scan<T>(L, static_cast<const T*>(L.k), L.m, 0, st)) != hipSuccess) return e;
   T* mq16 = reinterpret_cast<T*>(L.mq);  // the M q result in the input dtype
   if constexpr (sizeof(T) == 2) {
     if ((e = la<T>(L, static_cast<const T*>(L.q), static_cast<const T*>(L.k), static_cast<const T*>(L.k), mq16,
@@ -410,7 +444,7 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
     if ((e = la<float>(L, L.bwd.rk, L.bwd.rq, L.bwd.rdo, L.r1, st)) != hipSuccess) return e;
     if ((e = la<float>(L, L.bwd.rk, L.bwd.rv, L.bwd.rout, L.r2, st)) != hipSuccess) return e;
   }
-  if ((e = scan(L, L.dm, L.sdm, 1, st)) != hipSuccess) return e;
+  if ((e = scan<float>(L, L.dm, L.sdm, 1, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((dk_kernel<T>), dim3(nblocks(n)), dim3(256), 0, st, L.dkg, r1, r2, L.sdm,
                      static_cast<T*>(L.dk), L.N, D, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
