@@ -352,7 +352,7 @@ int linattn_chunk_backward_state(const void* q, const void* k, const void* v, co
  * Shapes as for ccq_forward (chunk 64, dk == dv in {32, 64, 128}); no carried
  * state. Outputs must not overlap each other, the inputs or the workspace (of
  * at least ccq_backward_workspace_bytes: about 18 float32 tensors of the
- * size of q, 23 for bf16 inputs).
+ * size of q, 22 for bf16 inputs).
  */
 size_t ccq_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv,
                                     int64_t chunk, int dtype);

@@ -580,8 +580,8 @@ CcqBwdLayout ccq_bwd_layout(int64_t B, int64_t H, int64_t N, int64_t D, int dtyp
   blen = blen < 4 ? 4 : (blen + 3) / 4 * 4;
   L.blen = blen;
   L.nblk = (N + blen - 1) / blen;
-  // 13 rows always, 4 input copies and dv for bf16, 5 reversal buffers
-  L.nrows = 13 + 5 + (dtype == LM_BF16 ? 5 : 0);
+  // 13 rows always, 3 input copies and dv for bf16, 5 reversal buffers
+  L.nrows = 13 + 5 + (dtype == LM_BF16 ? 4 : 0);
   const size_t rowt = align_up((size_t)B * H * N * D * 4), colt = align_up((size_t)B * H * N * 4);
   size_t off = 0;
   for (int i = 0; i < L.nrows; ++i) {
@@ -1468,7 +1468,6 @@ int ccq_backward(const void* q, const void* k, const void* v, const float* g, co
                     &La.r2, &Bw.rq, &Bw.rk, &Bw.rv, &Bw.rdo, &Bw.rout};
   for (float** p : rowp) *p = F(L.rows[r++]);
   if (dtype == LM_BF16) {
-    La.fq = F(L.rows[r++]);
     La.fk = F(L.rows[r++]);
     La.fv = F(L.rows[r++]);
     La.fdo = F(L.rows[r++]);

@@ -111,12 +111,14 @@ __device__ __forceinline__ float wsum(float x) {
   return x;
 }
 
-// Per token (one wave): lambda, s = Sigma q and q_clean.
-template <int D, typename TM>
-__global__ __launch_bounds__(256) void pre_kernel(const float* __restrict__ q, const float* __restrict__ m,
+// Per token (one wave): lambda, s = Sigma q and q_clean (q and M q in the
+// input dtype; q_clean in float32, or in bf16 where only its rounded value is
+// used).
+template <int D, typename TM, typename TC>
+__global__ __launch_bounds__(256) void pre_kernel(const TM* __restrict__ q, const float* __restrict__ m,
                                                   const TM* __restrict__ mq, const float* __restrict__ w,
                                                   const float* __restrict__ b, float* __restrict__ s,
-                                                  float* __restrict__ qc, float* __restrict__ lam, int64_t N, int H,
+                                                  TC* __restrict__ qc, float* __restrict__ lam, int64_t N, int H,
                                                   int64_t rows) {
   constexpr int PL = (D + 63) / 64;
   const int64_t r = (int64_t)blockIdx.x * 4 + wave_id();
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(256) void pre_kernel(const float* __restrict__ q, c
   for (int i = 0; i < PL; ++i) {
     const int f = l + 64 * i;
     const bool ok = f < D;
-    qv[i] = ok ? q[(size_t)r * D + f] : 0.f;
+    qv[i] = ok ? to_f32(q[(size_t)r * D + f]) : 0.f;
     mv[i] = ok ? m[(size_t)r * D + f] : 0.f;
     wv[i] = ok ? w[(size_t)h * D + f] : 0.f;
     wq += wv[i] * qv[i];
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(256) void pre_kernel(const float* __restrict__ q, c
     if (f < D) {
       const float sv = (to_f32(mq[(size_t)r * D + f]) - mv[i] * mqd / t) / t;
       s[(size_t)r * D + f] = sv;
-      qc[(size_t)r * D + f] = qv[i] - la * sv;
+      qc[(size_t)r * D + f] = from_f32<TC>(qv[i] - la * sv);
     }
   }
   if (l == 0) lam[r] = la;
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(256) void pre_kernel(const float* __restrict__ q, c
 // bf16, and the values and u written in bf16 at the time-reversed positions
 // (the operands of the reversed passes; ru receives u).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void post_kernel(const float* __restrict__ q, const float* __restrict__ m,
+__global__ __launch_bounds__(256) void post_kernel(const T* __restrict__ q, const float* __restrict__ m,
                                                    const float* __restrict__ s, const float* __restrict__ u,
                                                    const T* __restrict__ mu, const float* __restrict__ lam,
                                                    const float* __restrict__ w, T* __restrict__ dq,
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(256) void post_kernel(const float* __restrict__ q, 
     for (int i = 0; i < PL; ++i) {
       const int f = l + 64 * i;
       const bool ok = f < D;
-      qv[i] = ok ? q[r * D + f] : 0.f;
+      qv[i] = ok ? to_f32(q[r * D + f]) : 0.f;
       mv[i] = ok ? m[r * D + f] : 0.f;
       uv[i] = ok ? u[r * D + f] : 0.f;
       const float sv = ok ? s[r * D + f] : 0.f;
@@ -316,7 +318,6 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   hipError_t e;
   const float *fq, *fk, *fv, *fdo;
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.q), L.fq, n);
     if (!(D == 128 && L.fused)) {
       // k, v and dout in float32 serve only the chunk passes of the decayed read
       hipLaunchKernelGGL((cvt_kernel<T, float>), dim3(nblocks(n / 4)), dim3(256), 0, st, static_cast<const T*>(L.k),
@@ -327,7 +328,7 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
                          static_cast<const T*>(L.dout), L.fdo, n);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    fq = L.fq;
+    fq = nullptr;  // q is read in bf16
     fk = L.fk;
     fv = L.fv;
     fdo = L.fdo;
@@ -353,23 +354,27 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   } else {
     if ((e = la<float>(L, fq, fk, fk, L.mq, st)) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((pre_kernel<D, T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, fq, L.m, mq16, L.w,
-                     L.b, L.s, L.qc, L.lam, L.N, H, rows);
+  bool fused = false;
+  if constexpr (sizeof(T) == 2 && D == 128) fused = L.fused;
+  // the fused route takes q_clean rounded once to bf16 (as the forward's read
+  // takes it), written straight into a free slot
+  bf16* qc16 = reinterpret_cast<bf16*>(L.dvg);
+  const dim3 pgrid((unsigned)((rows + 3) / 4));
+  if (fused)
+    hipLaunchKernelGGL((pre_kernel<D, T, bf16>), pgrid, dim3(256), 0, st, static_cast<const T*>(L.q), L.m, mq16, L.w,
+                       L.b, L.s, qc16, L.lam, L.N, H, rows);
+  else
+    hipLaunchKernelGGL((pre_kernel<D, T, float>), pgrid, dim3(256), 0, st, static_cast<const T*>(L.q), L.m, mq16, L.w,
+                       L.b, L.s, L.qc, L.lam, L.N, H, rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // backward of the decayed linear attention read with q_clean: u = dq_clean,
   // the direct part of dk, dv and dg
   T* mu16 = reinterpret_cast<T*>(L.mu);
   T* u16 = sizeof(T) == 2 ? mu16 + n : nullptr;  // bf16: second half of the M u slot
-  bool fused = false;
-  if constexpr (sizeof(T) == 2 && D == 128) fused = L.fused;
   if (fused) {
-    // the fused bf16 kernel, with q_clean rounded once to bf16 (as the
-    // forward's read takes it); dq lands in the bf16 u operand of the M u
-    // pass, dk in the slot of a later reversed sum, k . dk per token in dm
-    bf16* qc16 = reinterpret_cast<bf16*>(L.dvg);
+    // the fused bf16 kernel: dq lands in the bf16 u operand of the M u pass,
+    // dk in the slot of a later reversed sum, k . dk per token in dm
     bf16* dk16 = reinterpret_cast<bf16*>(L.r1);
-    hipLaunchKernelGGL((cvt_kernel<float, bf16>), dim3(nblocks(n / 4)), dim3(256), 0, st, L.qc, qc16, n);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     BwdBf16Launch F{};
     F.q = qc16;
     F.k = L.k;
@@ -420,9 +425,9 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   } else {
     if ((e = la<float>(L, L.u, fk, fk, L.mu, st)) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((post_kernel<T, D>), dim3((unsigned)L.nblk, (unsigned)BH), dim3(256), 0, st, fq, L.m, L.s, L.u,
-                     mu16, L.lam, L.w, static_cast<T*>(L.dq), vr1, vr2, ru16, L.dm, L.part, L.N, (int)L.B, H, L.blen,
-                     (int)L.nblk);
+  hipLaunchKernelGGL((post_kernel<T, D>), dim3((unsigned)L.nblk, (unsigned)BH), dim3(256), 0, st,
+                     static_cast<const T*>(L.q), L.m, L.s, L.u, mu16, L.lam, L.w, static_cast<T*>(L.dq), vr1, vr2,
+                     ru16, L.dm, L.part, L.N, (int)L.B, H, L.blen, (int)L.nblk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // sum_{t>=j} (lambda_t/t) u_t (q_t . k_j) and (lambda_t/t) q_t (u_t . k_j): causal
   // passes over the reversed sequence (query rev k, keys rev q / rev u)

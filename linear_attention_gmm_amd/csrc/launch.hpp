@@ -229,7 +229,8 @@ struct CcqBwdLaunch {
   void* dv;
   float* dw;
   float* db;
-  // workspace (float32 rows [B*H][N][D]): copies of q, k, v, dout (bf16 inputs),
+  // workspace (float32 rows [B*H][N][D]): copies of k, v, dout (bf16 inputs;
+  // fq unused there, q is read in bf16),
   // m, M q, Sigma q, q_clean, u = dq_clean, the direct dk, dv (bf16), M u, the
   // values of the reversed passes, dm, its suffix sums, the two reversed sums;
   // [B*H][N]: lambda, unit gates; scan range sums [B*H][nch][D]; dw/db partials
