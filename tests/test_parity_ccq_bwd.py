@@ -91,6 +91,16 @@ def test_ccq_backward_bf16():
         _check(got, ref, "bf16", "bf16 %s N=300" % base)
 
 
+@pytest.mark.parametrize("dk", [32, 64])
+def test_ccq_backward_bf16_narrow(dk):
+    # bf16 at the narrower widths (the chunk passes of the decayed read, the
+    # scans reading bf16 keys), low-rank keys, a ragged length
+    cfg = inputs.CONFIGS["ccq_bf16_lowrank"].replace(name="ccq_bwd_bf16_narrow", cfg_id=807, B=2, H=2, N=333, dk=dk,
+                                                     dv=dk)
+    got, ref = _case(cfg)
+    _check(got, ref, "bf16", "bf16 low-rank keys dk=%d N=333" % dk)
+
+
 def test_ccq_backward_workload_shape_sampled():
     # the CCQ workload's shape (B=4, H=16, dk=dv=128, bf16) at N=2048 (the
     # autograd oracle keeps every step's state; at 16K tokens it would need
