@@ -1136,9 +1136,11 @@ static bool lin_bwd_fused(int64_t B, int64_t H, int64_t dk, int64_t dv, int64_t 
 size_t linattn_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t dk, int64_t dv, int64_t chunk,
                                         int dtype, int64_t segments) {
   if (lin_check_shape("linattn_chunk_backward", B, H, N, dk, dv, chunk, dtype, segments) != LM_OK) return 0;
-  // the dedicated kernel: k . dk per token only (with fewer sequences the
-  // chunk passes' workspace, which also serves a call with a carried state)
-  if (lin_bwd_fused(B, H, dk, dv, N, dtype, false)) return align_up((size_t)B * H * N * 4);
+  // the dedicated kernel: k . dk per token and the sums over slices of tokens
+  // (with fewer sequences the chunk passes' workspace, which also serves a
+  // call with a carried state)
+  if (lin_bwd_fused(B, H, dk, dv, N, dtype, false))
+    return align_up((size_t)B * H * N * 4) + align_up((size_t)B * H * lm::gate_slices(N) * 4);
   // float32 tensors: 5 for the reversed passes, and for bf16 inputs 7 more
   // (float32 copies of q, k, v, do and the gradients before rounding)
   const size_t t = align_up((size_t)B * H * N * dk * 4);
@@ -1208,6 +1210,7 @@ static int lin_backward(const char* fn, const void* q, const void* k, const void
     Lb.dv = dv;
     Lb.dg = dg;
     Lb.xk = static_cast<float*>(workspace);
+    Lb.tot = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)B * H * N * 4));
     Lb.state_in = state_in;
     Lb.dstate_out = dstate_out;
     Lb.dstate_in = dstate_in;

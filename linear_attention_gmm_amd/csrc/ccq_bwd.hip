@@ -373,7 +373,8 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   T* u16 = sizeof(T) == 2 ? mu16 + n : nullptr;  // bf16: second half of the M u slot
   if (fused) {
     // the fused bf16 kernel: dq lands in the bf16 u operand of the M u pass,
-    // dk in the slot of a later reversed sum, k . dk per token in dm
+    // dk in the slot of a later reversed sum, k . dk per token and the slice
+    // sums of the gate gradient in dm
     bf16* dk16 = reinterpret_cast<bf16*>(L.r1);
     BwdBf16Launch F{};
     F.q = qc16;
@@ -386,6 +387,7 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
     F.dv = L.dv;
     F.dg = L.bwd.dg;
     F.xk = L.dm;
+    F.tot = L.dm + BH * L.N;  // the dm rows hold D floats per token
     F.B = L.B;
     F.H = L.H;
     F.N = L.N;

@@ -185,6 +185,9 @@ hipError_t linattn_backward_launch(const BwdLaunch& L, hipStream_t st);
 // Backward of decayed linear attention for bf16 inputs with d_k = d_v = 128:
 // one launch of forward-sweep (dq) and reverse-sweep (dk, dv) workgroups, then
 // the suffix sums of the gate gradient.
+// Tokens per slice of the gate-gradient suffix sums of the bf16 backward.
+constexpr int kGateSlice = 1024;
+inline int64_t gate_slices(int64_t N) { return (N + kGateSlice - 1) / kGateSlice; }
 struct BwdBf16Launch {
   const void* q;
   const void* k;
@@ -195,7 +198,8 @@ struct BwdBf16Launch {
   void* dk;
   void* dv;
   float* dg;
-  float* xk;  // workspace: B * H * N floats (k . dk per token)
+  float* xk;   // workspace: B * H * N floats (k . dk per token)
+  float* tot;  // workspace: B * H * gate_slices(N) floats (sums over slices of tokens)
   // optional carried state, [B*H][128][128] float32 each
   const float* state_in = nullptr;
   const float* dstate_out = nullptr;

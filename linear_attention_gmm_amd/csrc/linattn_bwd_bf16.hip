@@ -575,25 +575,56 @@ __global__ __launch_bounds__(kNT, 1) void bwd_kernel(Args a) {
   else dkv_sweep(a, smem, b - a.BH);
 }
 
-// dg_t = (1 / g_t) sum_{m >= t} (xq_m - xk_m), one (b, h) per workgroup:
-// thread i owns tokens [i len, (i + 1) len); the totals of later ranges come
-// from LDS. dg may alias xq.
-__global__ __launch_bounds__(256) void gate_suffix(const float* __restrict__ g, const float* xq,
-                                                   const float* __restrict__ xk, float* dg, int64_t N) {
-  __shared__ float stot[256];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int64_t len = (N + 255) / 256;
-  const int64_t t0 = (int64_t)tid * len, t1 = t0 + len < N ? t0 + len : N;
+// dg_t = (1 / g_t) sum_{m >= t} (xq_m - xk_m) in slices of kGateSlice tokens:
+// gate_tot sums each slice, gate_apply adds the totals of the later slices and
+// walks its slice's tiles of 256 tokens from the last one back (thread = token:
+// a suffix sum inside each wave by lane shifts, the later waves' totals from
+// LDS). Every sum runs in a fixed order. dg may alias xq: gate_tot has read
+// all of xq before gate_apply runs, and there each token's xq is read before
+// its dg is written, by the same thread.
+__global__ __launch_bounds__(256) void gate_tot(const float* xq, const float* __restrict__ xk, float* __restrict__ tot,
+                                                int64_t N, int S) {
+  __shared__ float red[4];
+  const int sl = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, w = tid >> 6;
   const size_t base = (size_t)bh * N;
-  float tot = 0.f;
-  for (int64_t m = t0; m < t1; ++m) tot += xq[base + m] - xk[base + m];
-  stot[tid] = tot;
+  float x = 0.f;
+#pragma unroll
+  for (int j = 0; j < kGateSlice / 256; ++j) {
+    const int64_t t = (int64_t)sl * kGateSlice + j * 256 + tid;
+    if (t < N) x += xq[base + t] - xk[base + t];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  if (lane_id() == 0) red[w] = x;
   __syncthreads();
-  float run = 0.f;
-  for (int u = tid + 1; u < 256; ++u) run += stot[u];
-  for (int64_t m = t1 - 1; m >= t0; --m) {
-    run += xq[base + m] - xk[base + m];
-    dg[base + m] = run / g[base + m];
+  if (tid == 0) tot[(size_t)bh * S + sl] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(256) void gate_apply(const float* __restrict__ g, const float* xq,
+                                                  const float* __restrict__ xk, const float* __restrict__ tot,
+                                                  float* dg, int64_t N, int S) {
+  __shared__ float wtot[4];
+  const int sl = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, l = lane_id(), w = tid >> 6;
+  const size_t base = (size_t)bh * N;
+  float carry = 0.f;
+  for (int s2 = S - 1; s2 > sl; --s2) carry += tot[(size_t)bh * S + s2];
+  for (int j = kGateSlice / 256 - 1; j >= 0; --j) {
+    const int64_t t = (int64_t)sl * kGateSlice + j * 256 + tid;
+    const bool ok = t < N;
+    float s = ok ? xq[base + t] - xk[base + t] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_down(s, off);  // every lane takes part; the sum masks
+      if (l + off < 64) s += o;
+    }
+    if (l == 0) wtot[w] = s;  // lane 0 holds its wave's total
+    __syncthreads();
+    float after = carry;
+    for (int u = w + 1; u < 4; ++u) after += wtot[u];
+    const float tile = (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
+    if (ok) dg[base + t] = (s + after) / g[base + t];
+    carry += tile;
+    __syncthreads();  // wtot is rewritten by the next tile
   }
 }
 
@@ -619,7 +650,10 @@ hipError_t linattn_backward_bf16_launch(const BwdBf16Launch& L, hipStream_t st) 
   hipLaunchKernelGGL(lbw::bwd_kernel, dim3((unsigned)(2 * a.BH)), dim3(lbw::kNT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lbw::gate_suffix, dim3((unsigned)a.BH), dim3(256), 0, st, L.g, L.dg, L.xk, L.dg, L.N);
+  const int S = (int)gate_slices(L.N);
+  hipLaunchKernelGGL(lbw::gate_tot, dim3((unsigned)S, (unsigned)a.BH), dim3(256), 0, st, L.dg, L.xk, L.tot, L.N, S);
+  hipLaunchKernelGGL(lbw::gate_apply, dim3((unsigned)S, (unsigned)a.BH), dim3(256), 0, st, L.g, L.dg, L.xk, L.tot, L.dg,
+                     L.N, S);
   return hipGetLastError();
 }
 
