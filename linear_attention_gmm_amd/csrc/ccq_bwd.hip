@@ -160,9 +160,9 @@ __global__ __launch_bounds__(256) void pre_kernel(const TM* __restrict__ q, cons
 // inputs: M u and the values in float32, in time order. bf16 inputs: M u in
 // bf16, and the values and u written in bf16 at the time-reversed positions
 // (the operands of the reversed passes; ru receives u).
-template <typename T, int D>
+template <typename T, int D, typename TU>
 __global__ __launch_bounds__(256) void post_kernel(const T* __restrict__ q, const float* __restrict__ m,
-                                                   const float* __restrict__ s, const float* __restrict__ u,
+                                                   const float* __restrict__ s, const TU* __restrict__ u,
                                                    const T* __restrict__ mu, const float* __restrict__ lam,
                                                    const float* __restrict__ w, T* __restrict__ dq,
                                                    T* __restrict__ vr1, T* __restrict__ vr2, T* __restrict__ ru,
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void post_kernel(const T* __restrict__ q, cons
       const bool ok = f < D;
       qv[i] = ok ? to_f32(q[r * D + f]) : 0.f;
       mv[i] = ok ? m[r * D + f] : 0.f;
-      uv[i] = ok ? u[r * D + f] : 0.f;
+      uv[i] = ok ? to_f32(u[r * D + f]) : 0.f;
       const float sv = ok ? s[r * D + f] : 0.f;
       a += uv[i] * sv;
       um += uv[i] * mv[i];
@@ -236,9 +236,10 @@ __global__ __launch_bounds__(256) void post_kernel(const T* __restrict__ q, cons
   for (int f = threadIdx.x; f <= D; f += 256) dst[f] = sp[0][f] + sp[1][f] + sp[2][f] + sp[3][f];
 }
 
-// dk = (direct part) - R1 - R2 + suffix(dm); R1 and R2 come time-reversed.
-template <typename T>
-__global__ __launch_bounds__(256) void dk_kernel(const float* __restrict__ dkg, const T* __restrict__ r1,
+// dk = (direct part) - R1 - R2 + suffix(dm); R1 and R2 come time-reversed. The
+// direct part is float32, or bf16 where the fused kernel produced it.
+template <typename T, typename TD>
+__global__ __launch_bounds__(256) void dk_kernel(const TD* __restrict__ dkg, const T* __restrict__ r1,
                                                  const T* __restrict__ r2, const float* __restrict__ sdm,
                                                  T* __restrict__ dk, int64_t N, int D, int64_t total) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(256) void dk_kernel(const float* __restrict__ dkg, 
   const int f = (int)(i - row * D);
   const int64_t bh = row / N, t = row - bh * N;
   const size_t rr = ((size_t)bh * N + (N - 1 - t)) * D + f;
-  dk[i] = from_f32<T>(dkg[i] - to_f32(r1[rr]) - to_f32(r2[rr]) + sdm[i]);
+  dk[i] = from_f32<T>(to_f32(dkg[i]) - to_f32(r1[rr]) - to_f32(r2[rr]) + sdm[i]);
 }
 
 // dw, db per head: the block partials summed over (b, block) in a fixed order.
@@ -372,10 +373,10 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   T* mu16 = reinterpret_cast<T*>(L.mu);
   T* u16 = sizeof(T) == 2 ? mu16 + n : nullptr;  // bf16: second half of the M u slot
   if (fused) {
-    // the fused bf16 kernel: dq lands in the bf16 u operand of the M u pass,
-    // dk in the slot of a later reversed sum, k . dk per token and the slice
-    // sums of the gate gradient in dm
-    bf16* dk16 = reinterpret_cast<bf16*>(L.r1);
+    // the fused bf16 kernel: dq lands in the bf16 u operand of the M u pass
+    // (read as u by the later steps too), dk in the direct-dk slot (read in
+    // bf16), k . dk per token and the slice sums of the gate gradient in dm
+    bf16* dk16 = reinterpret_cast<bf16*>(L.dkg);
     BwdBf16Launch F{};
     F.q = qc16;
     F.k = L.k;
@@ -392,11 +393,6 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
     F.H = L.H;
     F.N = L.N;
     if ((e = linattn_backward_bf16_launch(F, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL((cvt_kernel<bf16, float>), dim3(nblocks(n / 4)), dim3(256), 0, st,
-                       reinterpret_cast<const bf16*>(u16), L.u, n);
-    hipLaunchKernelGGL((cvt_kernel<bf16, float>), dim3(nblocks(n / 4)), dim3(256), 0, st,
-                       reinterpret_cast<const bf16*>(dk16), L.dkg, n);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
   } else if constexpr (sizeof(T) == 2) {
     // dv (which dg does not use) on bf16 operands: reversed k, q_clean and
     // dout in the slots of the float32 dv and of the inner reversed k
@@ -427,9 +423,14 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
   } else {
     if ((e = la<float>(L, L.u, fk, fk, L.mu, st)) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((post_kernel<T, D>), dim3((unsigned)L.nblk, (unsigned)BH), dim3(256), 0, st,
-                     static_cast<const T*>(L.q), L.m, L.s, L.u, mu16, L.lam, L.w, static_cast<T*>(L.dq), vr1, vr2,
-                     ru16, L.dm, L.part, L.N, (int)L.B, H, L.blen, (int)L.nblk);
+  if (fused)
+    hipLaunchKernelGGL((post_kernel<T, D, bf16>), dim3((unsigned)L.nblk, (unsigned)BH), dim3(256), 0, st,
+                       static_cast<const T*>(L.q), L.m, L.s, reinterpret_cast<const bf16*>(u16), mu16, L.lam, L.w,
+                       static_cast<T*>(L.dq), vr1, vr2, ru16, L.dm, L.part, L.N, (int)L.B, H, L.blen, (int)L.nblk);
+  else
+    hipLaunchKernelGGL((post_kernel<T, D, float>), dim3((unsigned)L.nblk, (unsigned)BH), dim3(256), 0, st,
+                       static_cast<const T*>(L.q), L.m, L.s, L.u, mu16, L.lam, L.w, static_cast<T*>(L.dq), vr1, vr2,
+                       ru16, L.dm, L.part, L.N, (int)L.B, H, L.blen, (int)L.nblk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // sum_{t>=j} (lambda_t/t) u_t (q_t . k_j) and (lambda_t/t) q_t (u_t . k_j): causal
   // passes over the reversed sequence (query rev k, keys rev q / rev u)
@@ -452,8 +453,12 @@ static hipError_t run(const CcqBwdLaunch& L, hipStream_t st) {
     if ((e = la<float>(L, L.bwd.rk, L.bwd.rv, L.bwd.rout, L.r2, st)) != hipSuccess) return e;
   }
   if ((e = scan<float>(L, L.dm, L.sdm, 1, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((dk_kernel<T>), dim3(nblocks(n)), dim3(256), 0, st, L.dkg, r1, r2, L.sdm,
-                     static_cast<T*>(L.dk), L.N, D, n);
+  if (fused)
+    hipLaunchKernelGGL((dk_kernel<T, bf16>), dim3(nblocks(n)), dim3(256), 0, st, reinterpret_cast<const bf16*>(L.dkg),
+                       r1, r2, L.sdm, static_cast<T*>(L.dk), L.N, D, n);
+  else
+    hipLaunchKernelGGL((dk_kernel<T, float>), dim3(nblocks(n)), dim3(256), 0, st, L.dkg, r1, r2, L.sdm,
+                       static_cast<T*>(L.dk), L.N, D, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(param_kernel, dim3((unsigned)H), dim3(256), 0, st, L.part, L.dw, L.db, D,
                      (int)(L.B * L.nblk));
