@@ -91,6 +91,17 @@ def test_gla_backward_bf16_d128_ragged(N):
         assert_close(got[3][:, 1:], ref[3][:, 1:], "bf16", "dg bf16 d=128 N=%d (tokens 1..)" % N)
 
 
+@pytest.mark.parametrize("N", [1100, 2600])
+def test_gla_backward_bf16_d128_gate_slices(N):
+    # several 1024-token slices of the gate gradient's suffix sums, the last
+    # one ragged (2600 = 1024 + 1024 + 552, 1100 = 1024 + 76); dg on every token
+    cfg = inputs.LinAttnConfig("gla_bwd128", 510, B=2, H=16, N=N, dk=128, dv=128, dtype="bf16")
+    got, ref = _case(cfg, sl=[(0, 3), (1, 15)])
+    for name, a, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        assert_close(a, r, "bf16", "%s bf16 d=128 N=%d" % (name, N))
+    assert_close(got[3][:, 1:], ref[3][:, 1:], "bf16", "dg bf16 d=128 N=%d (tokens 1..)" % N)
+
+
 @pytest.mark.parametrize("g_logit_mean", [0.0, -1.0])
 def test_gla_backward_bf16_d128_strong_decay(g_logit_mean):
     # gates around 0.5 and 0.27 per token: states forget within a few tokens
